@@ -1,0 +1,342 @@
+"""fp64 CPU oracle for the row-typed associative-algebra projection Y = X *_{Q_q} W.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or link
+this module: only the tests, the smoke check and the bench's CPU-baseline leg
+use it.  It shares no code with the HIP library or its Python binding.
+
+Source: arXiv 2609.32814, "Change the Product, Keep the Parameters: Associative
+Algebra Layers for Transformers".  Every function names the passage it follows.
+
+What is computed, plainly:
+
+* The graph algebra Q_G (section 3.1, eq 9) has one basis element per vertex
+  slot (a, a) and per directed-edge slot (a, b).  Its only nonzero basis
+  products are  vertex*vertex = vertex,  vertex*edge = edge,  edge*vertex =
+  edge  when the inner indices agree; every other product is zero.
+  `structure_table` writes those structure constants out as a list of
+  (left slot, right slot, result slot) triples (eq 5 with c = 1 on each triple).
+* Lifted to matrix blocks, each triple is one block GEMM (section 1, "every
+  juxtaposition ... is one ordinary block GEMM").  `square_product` sums the
+  block GEMMs of every triple (eq 10-11, eq 13-14 for the complete graph Q_q).
+* The row-typed projection (section 4, eq 16-17; section 6.1, eq 27 and
+  Algorithm 1) gives each token row m the type i = tau[m]; the row uses the
+  triples whose left slot lies in block-row i.  `row_typed_forward` runs
+  Algorithm 1 with the support read off the table.
+* The vector-Jacobian products (appendix B, eq 31-35) are the same triples
+  with the GEMMs transposed: `row_typed_backward`.
+* `type_index` forms the row sets I_i = {m : tau[m] = i} (Algorithm 1, the
+  step that builds I_i), `type_schedule` the position-type schedule (section 4,
+  the cyclic tau; appendix D.5, the interval schedule of the pilot).
+* `mac_count` counts the multiply-accumulates the row-typed evaluator executes
+  (eq 18-19; eq 24 for equal groups).
+
+All arithmetic is float64; block products are numpy.matmul (a library
+primitive standing for one block GEMM).  The oracle itself rounds nothing.
+
+Readings where the pages leave a step open:
+* types are 0-based: the page's 1 + ((p-1) mod q) with 1-based p is the same
+  cycle as p mod q with 0-based p;
+* B(i, i) = {i} is a set: the j = i output group gets the single term x_i W_ii;
+* group widths default to equal (K/q, N/q); unequal widths are accepted;
+* a row whose tau lies outside [0, q) belongs to no type: it contributes to
+  nothing and its output row is zero (it is counted by `type_index`).
+
+Every function here is pinned by tests against closed forms or independent
+formulas from the pages (worked q=2 example, unit and associativity laws,
+product counts, appendix A's (d, n) form, masked-dense and brute-force forms,
+autograd of the masked-dense form for the VJPs).
+"""
+from __future__ import annotations
+
+from typing import Iterable, Sequence
+
+import numpy as np
+
+Slot = tuple[int, int]
+Triple = tuple[Slot, Slot, Slot]
+
+__all__ = [
+    "complete_graph_edges",
+    "graph_slots",
+    "structure_table",
+    "group_bounds",
+    "square_product",
+    "row_typed_forward",
+    "row_typed_backward",
+    "row_typed_forward_batched",
+    "type_index",
+    "type_schedule",
+    "mac_count",
+    "dense_equivalent_macs",
+]
+
+
+# ----------------------------------------------------------------------------
+# The algebra: section 3.1 (eq 9-11) and section 3.2 (eq 13-15)
+# ----------------------------------------------------------------------------
+
+def complete_graph_edges(q: int) -> list[Slot]:
+    """Directed edges of the complete graph on q vertices (section 3.2: Q_q)."""
+    return [(a, b) for a in range(q) for b in range(q) if a != b]
+
+
+def graph_slots(q: int, edges: Iterable[Slot] | None = None) -> list[Slot]:
+    """Slots of Q_G: vertices (a, a) and edges (a, b) (section 3.1).
+
+    `edges=None` means the complete graph, i.e. Q_q.
+    """
+    e = complete_graph_edges(q) if edges is None else [tuple(x) for x in edges]
+    for a, b in e:
+        if a == b or not (0 <= a < q and 0 <= b < q):
+            raise ValueError(f"bad edge {(a, b)} for q={q}")
+    return [(a, a) for a in range(q)] + sorted(set(e))
+
+
+def structure_table(q: int, edges: Iterable[Slot] | None = None) -> list[Triple]:
+    """Nonzero structure constants of Q_G as (left, right, result) slot triples.
+
+    Basis rule (eq 9): e_i e_i = e_i, e_i a_ij = a_ij, a_ij e_j = a_ij, and all
+    other basis products vanish.  In slot terms: (a, b) * (c, d) is nonzero only
+    when b == c and at least one factor is a vertex; the result is slot (a, d).
+    """
+    slots = graph_slots(q, edges)
+    slot_set = set(slots)
+    table: list[Triple] = []
+    for left in slots:
+        a, b = left
+        for right in slots:
+            c, d = right
+            if b != c:
+                continue                      # inner indices must meet
+            if a != b and c != d:
+                continue                      # edge * edge = 0
+            out = (a, d)
+            assert out in slot_set            # vertex*x and x*vertex return x
+            table.append((left, right, out))
+    return table
+
+
+# ----------------------------------------------------------------------------
+# Block bookkeeping
+# ----------------------------------------------------------------------------
+
+def group_bounds(total: int, q: int, widths: Sequence[int] | None = None) -> list[tuple[int, int]]:
+    """[start, end) of each feature group; equal widths total/q unless given (section 4)."""
+    if widths is None:
+        if total % q:
+            raise ValueError(f"q={q} does not divide width {total}")
+        widths = [total // q] * q
+    if len(widths) != q or sum(widths) != total or min(widths) < 0:
+        raise ValueError(f"widths {widths} do not partition {total} into {q} groups")
+    out, s = [], 0
+    for w in widths:
+        out.append((s, s + w))
+        s += w
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Square form: Z = X * W over block arrays (eq 10-11; eq 13-14; eq 3 at q = 2)
+# ----------------------------------------------------------------------------
+
+def square_product(X: np.ndarray, W: np.ndarray, q: int,
+                   row_heights: Sequence[int] | None = None,
+                   mid_widths: Sequence[int] | None = None,
+                   out_widths: Sequence[int] | None = None,
+                   edges: Iterable[Slot] | None = None) -> np.ndarray:
+    """Block-array product Z = X *_{Q_G} W.
+
+    X is split into q x q blocks (block-row heights `row_heights`, block-column
+    widths `mid_widths`), W into q x q blocks (heights `mid_widths`, widths
+    `out_widths`).  For every structure-constant triple (a,b)*(b,d) -> (a,d) the
+    block GEMM X_ab W_bd is added to Z_ad (eq 5 lifted to blocks).  Slots that
+    are not in the algebra (non-complete G) must hold zero blocks in X and W;
+    they are ignored.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    rb = group_bounds(X.shape[0], q, row_heights)
+    mb = group_bounds(X.shape[1], q, mid_widths)
+    if W.shape[0] != X.shape[1]:
+        raise ValueError("inner dimensions differ")
+    ob = group_bounds(W.shape[1], q, out_widths)
+    Z = np.zeros((X.shape[0], W.shape[1]), dtype=np.float64)
+    for (a, b), (_, d), (za, zd) in structure_table(q, edges):
+        xa = X[rb[a][0]:rb[a][1], mb[b][0]:mb[b][1]]
+        wb = W[mb[b][0]:mb[b][1], ob[d][0]:ob[d][1]]
+        Z[rb[za][0]:rb[za][1], ob[zd][0]:ob[zd][1]] += xa @ wb
+    return Z
+
+
+# ----------------------------------------------------------------------------
+# Type schedule and type index: section 4 (tau), Algorithm 1 (I_i), App D.5
+# ----------------------------------------------------------------------------
+
+def type_schedule(positions: np.ndarray, q: int, kind: str = "cyclic",
+                  period: int = 0) -> np.ndarray:
+    """Row types from absolute positions.
+
+    * "cyclic": tau(p) = p mod q (section 4, 0-based form of 1 + ((p-1) mod q)).
+    * "interval": tau(p) = floor((p mod period) / (period / q)) (appendix D.5,
+      the pilot's schedule floor((p mod 768) / 192) with period 768, q = 4).
+    """
+    p = np.asarray(positions, dtype=np.int64)
+    if kind == "cyclic":
+        return (p % q).astype(np.int32)
+    if kind == "interval":
+        if period <= 0 or period % q:
+            raise ValueError("interval schedule needs q | period > 0")
+        return ((p % period) // (period // q)).astype(np.int32)
+    raise ValueError(kind)
+
+
+def type_index(tau: np.ndarray, q: int):
+    """Row sets I_i = {m : tau[m] = i} (Algorithm 1).
+
+    Returns (counts[q], offsets[q+1], rows[sum counts], bad) where rows lists
+    the members of I_0, then I_1, ..., each in ascending row order, offsets are
+    the running sums of counts, and `bad` counts rows whose tau lies outside
+    [0, q) (they belong to no I_i).
+    """
+    tau = np.asarray(tau, dtype=np.int64)
+    counts = np.zeros(q, dtype=np.int64)
+    members: list[list[int]] = [[] for _ in range(q)]
+    bad = 0
+    for m, t in enumerate(tau.tolist()):
+        if 0 <= t < q:
+            members[t].append(m)
+            counts[t] += 1
+        else:
+            bad += 1
+    offsets = np.zeros(q + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    rows = np.array([m for grp in members for m in grp], dtype=np.int64)
+    return counts, offsets, rows, bad
+
+
+# ----------------------------------------------------------------------------
+# Row-typed projection: section 4 (eq 16-17), section 6.1 (eq 27, Algorithm 1)
+# ----------------------------------------------------------------------------
+
+def _row_sets(tau: np.ndarray, q: int) -> list[np.ndarray]:
+    counts, offsets, rows, _ = type_index(tau, q)
+    return [rows[offsets[i]:offsets[i + 1]] for i in range(q)]
+
+
+def row_typed_forward(X: np.ndarray, W: np.ndarray, tau: np.ndarray, q: int,
+                      in_widths: Sequence[int] | None = None,
+                      out_widths: Sequence[int] | None = None,
+                      edges: Iterable[Slot] | None = None) -> np.ndarray:
+    """Y = X *_{Q_G} W with row types tau (Algorithm 1).
+
+    Y <- 0; for each type i with rows I_i, for each structure-constant triple
+    (i, b) * (b, j) -> (i, j) whose left slot is in block-row i:
+        Y[I_i, g_j] += X[I_i, g_b] W[g_b, g_j].
+    For the complete graph that is y_i = x_i W_ii and y_j = x_i W_ij + x_j W_jj
+    (eq 16-17; support B(i, j) = {i, j} of eq 27).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    M, K = X.shape
+    if W.shape[0] != K:
+        raise ValueError("X and W inner widths differ")
+    N = W.shape[1]
+    kb = group_bounds(K, q, in_widths)
+    nb = group_bounds(N, q, out_widths)
+    table = structure_table(q, edges)
+    Y = np.zeros((M, N), dtype=np.float64)
+    for i, rows in enumerate(_row_sets(tau, q)):
+        if rows.size == 0:
+            continue
+        Xi = X[rows]
+        Yi = np.zeros((rows.size, N), dtype=np.float64)
+        for (xa, xb), (wa, wd), (ya, yd) in table:
+            if xa != i:
+                continue                      # the row of type i supplies slots (i, *)
+            assert ya == i
+            xs, xe = kb[xb]
+            ws, we = kb[wa]
+            ns, ne = nb[wd]
+            Yi[:, nb[yd][0]:nb[yd][1]] += Xi[:, xs:xe] @ W[ws:we, ns:ne]
+        Y[rows] = Yi
+    return Y
+
+
+def row_typed_backward(X: np.ndarray, W: np.ndarray, dY: np.ndarray, tau: np.ndarray, q: int,
+                       in_widths: Sequence[int] | None = None,
+                       out_widths: Sequence[int] | None = None,
+                       edges: Iterable[Slot] | None = None):
+    """(dX, dW) of Y = X *_{Q_G} W (appendix B, eq 31-35).
+
+    Each forward block GEMM Y[I_i, g_j] += X[I_i, g_b] W[g_b, g_j] contributes
+        dX[I_i, g_b] += dY[I_i, g_j] W[g_b, g_j]^T      (eq 31-32)
+        dW[g_b, g_j] += X[I_i, g_b]^T dY[I_i, g_j]      (eq 33-35)
+    summed over all types; blocks no type reaches stay zero.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    dY = np.asarray(dY, dtype=np.float64)
+    M, K = X.shape
+    N = W.shape[1]
+    if dY.shape != (M, N):
+        raise ValueError("dY shape")
+    kb = group_bounds(K, q, in_widths)
+    nb = group_bounds(N, q, out_widths)
+    table = structure_table(q, edges)
+    dX = np.zeros((M, K), dtype=np.float64)
+    dW = np.zeros((K, N), dtype=np.float64)
+    for i, rows in enumerate(_row_sets(tau, q)):
+        if rows.size == 0:
+            continue
+        Xi = X[rows]
+        dYi = dY[rows]
+        dXi = np.zeros((rows.size, K), dtype=np.float64)
+        for (xa, xb), (wa, wd), (ya, yd) in table:
+            if xa != i:
+                continue
+            assert ya == i
+            xs, xe = kb[xb]
+            ws, we = kb[wa]
+            ns, ne = nb[wd]
+            ys, ye = nb[yd]
+            dXi[:, xs:xe] += dYi[:, ys:ye] @ W[ws:we, ns:ne].T
+            dW[ws:we, ns:ne] += Xi[:, xs:xe].T @ dYi[:, ys:ye]
+        dX[rows] = dXi
+    return dX, dW
+
+
+def row_typed_forward_batched(X: np.ndarray, W: np.ndarray, tau: np.ndarray, q: int) -> np.ndarray:
+    """E independent projections (one weight bank per expert): X[E,M,K], W[E,K,N], tau[E,M]."""
+    return np.stack([row_typed_forward(X[e], W[e], tau[e], q) for e in range(X.shape[0])])
+
+
+# ----------------------------------------------------------------------------
+# Cost: eq 18-19 (rectangular cost), eq 21 / eq 24 (equal groups)
+# ----------------------------------------------------------------------------
+
+def mac_count(tau: np.ndarray, q: int, K: int, N: int,
+              in_widths: Sequence[int] | None = None,
+              out_widths: Sequence[int] | None = None,
+              edges: Iterable[Slot] | None = None) -> tuple[int, int]:
+    """(block GEMMs executed, MACs executed) by `row_typed_forward` on these types.
+
+    Counts, for every type i with M_i > 0, each triple with left slot in
+    block-row i as one block GEMM of M_i * s_b * r_j MACs.
+    """
+    kb = group_bounds(K, q, in_widths)
+    nb = group_bounds(N, q, out_widths)
+    counts, _, _, _ = type_index(tau, q)
+    gemms = 0
+    macs = 0
+    for (xa, _xb), (wa, wd), _out in structure_table(q, edges):
+        Mi = int(counts[xa])
+        if Mi == 0:
+            continue
+        gemms += 1
+        macs += Mi * (kb[wa][1] - kb[wa][0]) * (nb[wd][1] - nb[wd][0])
+    return gemms, macs
+
+
+def dense_equivalent_macs(M: int, K: int, N: int) -> int:
+    """MACs of the ordinary product X W (the dense control)."""
+    return M * K * N

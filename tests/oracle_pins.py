@@ -1,0 +1,522 @@
+"""Pins of the fp64 oracle against what the paper fixes, independent of the oracle's own code.
+
+Each `pin_*` function raises AssertionError when the oracle module `O` disagrees
+with a value, closed form or independent formula from arXiv 2609.32814.  They
+are run against the real oracle (test_oracle_pins.py) and against oracles with
+planted mistakes (test_oracle_mutations.py), which must each trip at least one pin.
+"""
+from __future__ import annotations
+
+import itertools
+import pathlib
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = pathlib.Path(__file__).resolve().parent / "golden"
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _ints(g, shape, lo=-4, hi=5):
+    return g.integers(lo, hi, size=shape).astype(np.float64)
+
+
+def _bounds(widths):
+    out, s = [], 0
+    for w in widths:
+        out.append((s, s + w))
+        s += w
+    return out
+
+
+# --------------------------------------------------------------------------
+# golden: the q = 2 law as printed (section 1, eq 1-3)
+# --------------------------------------------------------------------------
+
+def load_q2_products():
+    rows = []
+    for line in (GOLDEN / "q2_products.txt").read_text().splitlines():
+        if not line.strip() or line.startswith("#"):
+            continue
+        xs, ws, zs, _name = line.split()
+        rows.append(tuple(tuple(int(v) for v in t.split(",")) for t in (xs, ws, zs)))
+    return rows
+
+
+def load_q2_scalar():
+    vals = {}
+    for line in (GOLDEN / "q2_scalar_example.txt").read_text().splitlines():
+        if not line.strip() or line.startswith("#"):
+            continue
+        key, *nums = line.split()
+        vals[key] = np.array([float(v) for v in nums]).reshape(2, 2)
+    return vals
+
+
+def load_product_counts():
+    out = []
+    for line in (GOLDEN / "product_counts.txt").read_text().splitlines():
+        if not line.strip() or line.startswith("#"):
+            continue
+        out.append(tuple(int(v) for v in line.split()))
+    return out
+
+
+def pin_q2_table(O):
+    """The q=2 structure table is exactly the six products of eq (3)."""
+    assert sorted(O.structure_table(2)) == sorted(load_q2_products())
+
+
+def pin_q2_scalar_example(O):
+    """Hand evaluation of eq (3) at small integers, square and row-typed forms."""
+    v = load_q2_scalar()
+    Z = O.square_product(v["X"], v["W"], 2)
+    np.testing.assert_array_equal(Z, v["Q2"])
+    # each token row uses one row of the table (section 1 / section 4)
+    Y = O.row_typed_forward(v["X"], v["W"], np.array([0, 1]), 2)
+    np.testing.assert_array_equal(Y, v["Q2"])
+    # eq (2) differs exactly by the two removed cycle terms U W_v and V W_u
+    diff = v["DENSE"] - v["Q2"]
+    X, W = v["X"], v["W"]
+    np.testing.assert_array_equal(diff, np.array([[X[0, 1] * W[1, 0], 0], [0, X[1, 0] * W[0, 1]]]))
+
+
+def pin_eq3_rectangular_blocks(O, seed=11):
+    """eq (3) with random rectangular blocks of unequal sizes equals the table-driven square form."""
+    g = _rng(seed)
+    m0, m1, k0, k1, n0, n1 = 3, 5, 4, 2, 6, 3
+    A, U = g.standard_normal((m0, k0)), g.standard_normal((m0, k1))
+    V, D = g.standard_normal((m1, k0)), g.standard_normal((m1, k1))
+    Wa, Wu = g.standard_normal((k0, n0)), g.standard_normal((k0, n1))
+    Wv, Wd = g.standard_normal((k1, n0)), g.standard_normal((k1, n1))
+    X = np.block([[A, U], [V, D]])
+    W = np.block([[Wa, Wu], [Wv, Wd]])
+    want = np.block([[A @ Wa, A @ Wu + U @ Wd], [V @ Wa + D @ Wv, D @ Wd]])
+    Z = O.square_product(X, W, 2, row_heights=[m0, m1], mid_widths=[k0, k1], out_widths=[n0, n1])
+    np.testing.assert_allclose(Z, want, rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# eq 13-14 entry rule of Q_q; eq 15 counts; eq 12 for general graphs
+# --------------------------------------------------------------------------
+
+def pin_eq13_14(O, qs=(3, 4, 5), seed=12):
+    """(A*B)_ii = A_ii B_ii ; (A*B)_ij = A_ii B_ij + A_ij B_jj, blockwise with unequal widths."""
+    g = _rng(seed)
+    for q in qs:
+        hs = list(g.integers(1, 4, size=q))
+        ks = list(g.integers(1, 4, size=q))
+        ns = list(g.integers(1, 4, size=q))
+        A = g.standard_normal((sum(hs), sum(ks)))
+        B = g.standard_normal((sum(ks), sum(ns)))
+        hb, kb, nb = _bounds(hs), _bounds(ks), _bounds(ns)
+        Ab = lambda a, b: A[hb[a][0]:hb[a][1], kb[b][0]:kb[b][1]]
+        Bb = lambda a, b: B[kb[a][0]:kb[a][1], nb[b][0]:nb[b][1]]
+        want = np.zeros((sum(hs), sum(ns)))
+        for i in range(q):
+            for j in range(q):
+                blk = Ab(i, i) @ Bb(i, j) if i == j else Ab(i, i) @ Bb(i, j) + Ab(i, j) @ Bb(j, j)
+                want[hb[i][0]:hb[i][1], nb[j][0]:nb[j][1]] = blk
+        Z = O.square_product(A, B, q, row_heights=hs, mid_widths=ks, out_widths=ns)
+        np.testing.assert_allclose(Z, want, rtol=1e-12, atol=1e-12)
+
+
+def pin_product_counts(O):
+    """R(Q_q) = 2q^2 - q block GEMMs (eq 15), 2q - 1 per row, rho_q = (2q-1)/q^2 (eq 21)."""
+    for q, total, per_row, rn, rd in load_product_counts():
+        t = O.structure_table(q)
+        assert len(t) == total == 2 * q * q - q
+        for i in range(q):
+            assert sum(1 for (x, _w, _z) in t if x[0] == i) == per_row == 2 * q - 1
+        assert Fraction(per_row, q) / q == Fraction(rn, rd)
+        # every slot of the algebra is a result at least once and dim = q^2 (eq 15)
+        assert len({z for (_x, _w, z) in t}) == q * q
+        # each product pairs matching inner indices: a juxtaposition is one block GEMM
+        for x, w, z in t:
+            assert x[1] == w[0] and z == (x[0], w[1])
+
+
+def pin_graph_counts(O, seed=13):
+    """R(Q_G) = |V| + 2|E| explicit products for random digraphs (eq 12, section 3.1)."""
+    g = _rng(seed)
+    for q in (1, 2, 3, 5, 7):
+        all_e = [(a, b) for a in range(q) for b in range(q) if a != b]
+        for _ in range(4):
+            keep = [e for e in all_e if g.random() < 0.5]
+            t = O.structure_table(q, keep)
+            assert len(t) == q + 2 * len(keep)
+            # eq 10-11: vertex i gets x_i w_i; edge ij gets x_i w_ij + x_ij w_j
+            for (a, b) in keep:
+                terms = sorted((x, w) for (x, w, z) in t if z == (a, b))
+                assert terms == sorted([((a, a), (a, b)), ((a, b), (b, b))])
+            for a in range(q):
+                assert [(x, w) for (x, w, z) in t if z == (a, a)] == [((a, a), (a, a))]
+
+
+# --------------------------------------------------------------------------
+# appendix A (d, n) form; associativity; unit (eq 4, eq 6, eq 30, prop 3.1)
+# --------------------------------------------------------------------------
+
+def _scalar_square(O, d, n):
+    """Element (d, n) of Q_q as a q x q array with d on the diagonal."""
+    return np.diag(d) + n
+
+
+def pin_appendix_a(O, seed=14):
+    """(d,n)*(d',n') = (dd', dn' + nd') with (dn')_ij = d_i n'_ij, (nd')_ij = n_ij d'_j (eq 30)."""
+    g = _rng(seed)
+    for q in (1, 2, 3, 4, 5):
+        off = 1.0 - np.eye(q)
+        for _ in range(5):
+            d, d2 = _ints(g, q), _ints(g, q)
+            n, n2 = _ints(g, (q, q)) * off, _ints(g, (q, q)) * off
+            Z = O.square_product(_scalar_square(O, d, n), _scalar_square(O, d2, n2), q)
+            want_d = d * d2
+            want_n = d[:, None] * n2 + n * d2[None, :]
+            np.testing.assert_array_equal(np.diag(Z), want_d)
+            np.testing.assert_array_equal(Z * off, want_n)
+
+
+def _basis(q, slot):
+    e = np.zeros((q, q))
+    e[slot] = 1.0
+    return e
+
+
+def pin_associativity(O, seed=15):
+    """(x*y)*z = x*(y*z): every basis triple for q <= 4, random integer elements for q <= 5 (eq 4, eq 30)."""
+    for q in (1, 2, 3, 4):
+        slots = [(a, b) for a in range(q) for b in range(q)]
+        prod = {}
+        for s1 in slots:
+            for s2 in slots:
+                prod[s1, s2] = O.square_product(_basis(q, s1), _basis(q, s2), q)
+        for s1, s2, s3 in itertools.product(slots, repeat=3):
+            left = O.square_product(prod[s1, s2], _basis(q, s3), q)
+            right = O.square_product(_basis(q, s1), prod[s2, s3], q)
+            np.testing.assert_array_equal(left, right)
+    g = _rng(seed)
+    for q in (2, 3, 5):
+        for _ in range(3):
+            x, y, z = (_ints(g, (2 * q, 2 * q)) for _ in range(3))
+            np.testing.assert_array_equal(O.square_product(O.square_product(x, y, q), z, q),
+                                          O.square_product(x, O.square_product(y, z, q), q))
+
+
+def pin_row_typed_composition(O, seed=16):
+    """Phi_{W2}(Phi_{W1}(X)) = Phi_{W1 * W2}(X) for the row-typed maps (eq 4, eq 6; section 4)."""
+    g = _rng(seed)
+    for q in (1, 2, 3, 4):
+        s = 2
+        K = q * s
+        M = 7
+        X = _ints(g, (M, K))
+        W1, W2 = _ints(g, (K, K)), _ints(g, (K, K))
+        tau = g.integers(0, q, size=M)
+        lhs = O.row_typed_forward(O.row_typed_forward(X, W1, tau, q), W2, tau, q)
+        rhs = O.row_typed_forward(X, O.square_product(W1, W2, q), tau, q)
+        np.testing.assert_array_equal(lhs, rhs)
+
+
+def pin_unit_laws(O, seed=17):
+    """E = block identity: X*E = X and E*W = W (section 1, prop 3.1); row-typed identity bank (section 4)."""
+    g = _rng(seed)
+    for q in (1, 2, 3, 4, 6):
+        n = 2 * q
+        X, W = g.standard_normal((n, n)), g.standard_normal((n, n))
+        E = np.eye(n)
+        np.testing.assert_array_equal(O.square_product(X, E, q), X)
+        np.testing.assert_array_equal(O.square_product(E, W, q), W)
+        # row-typed: a diagonal bank of identity maps is the identity projection
+        M = 9
+        Xr = g.standard_normal((M, n))
+        tau = g.integers(0, q, size=M)
+        np.testing.assert_array_equal(O.row_typed_forward(Xr, E, tau, q), Xr)
+        # and feeding the identity's rows with interval types floor(m / s) returns W (Phi_w(1) = w)
+        s = n // q
+        tau_i = np.arange(n) // s
+        np.testing.assert_array_equal(O.row_typed_forward(E, W, tau_i, q), W)
+
+
+# --------------------------------------------------------------------------
+# row-typed form (section 4, eq 16-17; eq 27; Algorithm 1)
+# --------------------------------------------------------------------------
+
+def brute_force_row_typed(X, W, tau, q, kw, nw):
+    """Scalar loops over eq 16-17 directly: y_i = x_i W_ii, y_j = x_i W_ij + x_j W_jj."""
+    kb, nb = _bounds(kw), _bounds(nw)
+    M = X.shape[0]
+    Y = np.zeros((M, W.shape[1]))
+    for m in range(M):
+        i = int(tau[m])
+        if not 0 <= i < q:
+            continue
+        for j in range(q):
+            for c in range(nb[j][0], nb[j][1]):
+                acc = 0.0
+                for k in range(kb[i][0], kb[i][1]):
+                    acc += X[m, k] * W[k, c]
+                if j != i:
+                    for k in range(kb[j][0], kb[j][1]):
+                        acc += X[m, k] * W[k, c]
+                Y[m, c] = acc
+    return Y
+
+
+def pin_brute_force(O, seed=18):
+    """Table-driven Algorithm 1 equals scalar eq 16-17 (unequal widths, absent and invalid types)."""
+    g = _rng(seed)
+    for q in (1, 2, 3, 4):
+        kw = list(g.integers(1, 4, size=q))
+        nw = list(g.integers(1, 4, size=q))
+        M = 11
+        X = g.standard_normal((M, sum(kw)))
+        W = g.standard_normal((sum(kw), sum(nw)))
+        tau = g.integers(0, q, size=M)
+        tau[3] = q          # out of range: no type, zero row
+        tau[5] = -1
+        Y = O.row_typed_forward(X, W, tau, q, in_widths=kw, out_widths=nw)
+        np.testing.assert_allclose(Y, brute_force_row_typed(X, W, tau, q, kw, nw), rtol=1e-12, atol=1e-12)
+
+
+def masked_bank(W, i, q):
+    """T_i(W): W with every block (a, b), a != i and a != b, set to zero.
+
+    Generalises the slide deck's teaching matrix T_1(W) = [[W11, W12], [0, W22]]
+    (derived there from eq 16-17): a type-i row sees its own block row and the diagonal.
+    """
+    K, N = W.shape
+    s, r = K // q, N // q
+    T = W.copy()
+    for a in range(q):
+        for b in range(q):
+            if a != i and a != b:
+                T[a * s:(a + 1) * s, b * r:(b + 1) * r] = 0.0
+    return T
+
+
+def pin_teaching_matrix(O):
+    """q=2: T_1(W) = [[W11, W12], [0, W22]] and T_2(W) = [[W11, 0], [W21, W22]]."""
+    W = np.array([[5.0, 6.0], [7.0, 8.0]])
+    np.testing.assert_array_equal(masked_bank(W, 0, 2), [[5, 6], [0, 8]])
+    np.testing.assert_array_equal(masked_bank(W, 1, 2), [[5, 0], [7, 8]])
+    for i in range(2):
+        x = np.array([[1.0 + 2 * i, 2.0 + 2 * i]])
+        np.testing.assert_array_equal(O.row_typed_forward(x, W, np.array([i]), 2), x @ masked_bank(W, i, 2))
+
+
+def pin_masked_dense(O, seed=19):
+    """Y[I_i] = X[I_i] T_i(W) by plain matmul: an independent formula, like the paper's checks."""
+    g = _rng(seed)
+    for q, M, s, r in ((2, 10, 3, 4), (3, 13, 2, 5), (4, 17, 3, 2), (5, 9, 1, 1)):
+        X = g.standard_normal((M, q * s))
+        W = g.standard_normal((q * s, q * r))
+        tau = g.integers(0, q, size=M)
+        Y = O.row_typed_forward(X, W, tau, q)
+        for m in range(M):
+            want = X[m] @ masked_bank(W, int(tau[m]), q)
+            np.testing.assert_allclose(Y[m], want, rtol=1e-12, atol=1e-13)
+
+
+def pin_row_typed_is_square_rows(O, seed=20):
+    """Rows grouped by type form the square form's block rows (section 1: one row of the table per token)."""
+    g = _rng(seed)
+    for q, M in ((2, 9), (3, 14), (4, 6)):
+        s, r = 2, 3
+        X = g.standard_normal((M, q * s))
+        W = g.standard_normal((q * s, q * r))
+        tau = g.integers(0, q, size=M)
+        order = np.argsort(tau, kind="stable")
+        heights = [int((tau == i).sum()) for i in range(q)]
+        Z = O.square_product(X[order], W, q, row_heights=heights)
+        Y = np.empty_like(Z)
+        Y[order] = Z
+        np.testing.assert_allclose(O.row_typed_forward(X, W, tau, q), Y, rtol=1e-13, atol=1e-13)
+
+
+def pin_q1_is_matmul(O, seed=21):
+    """Q_1 is the ground field: one group, the projection is X W (eq 13 at q = 1)."""
+    g = _rng(seed)
+    X, W = g.standard_normal((7, 6)), g.standard_normal((6, 5))
+    np.testing.assert_allclose(O.row_typed_forward(X, W, np.zeros(7, np.int32), 1), X @ W, rtol=1e-14, atol=1e-14)
+
+
+def pin_block_diagonal(O, seed=22):
+    """With W_ij = 0 for i != j every type computes X W (eq 16-17 lose their cross terms)."""
+    g = _rng(seed)
+    q, s, r, M = 4, 3, 2, 15
+    X = g.standard_normal((M, q * s))
+    W = np.zeros((q * s, q * r))
+    for a in range(q):
+        W[a * s:(a + 1) * s, a * r:(a + 1) * r] = g.standard_normal((s, r))
+    tau = g.integers(0, q, size=M)
+    np.testing.assert_allclose(O.row_typed_forward(X, W, tau, q), X @ W, rtol=1e-13, atol=1e-14)
+
+
+def pin_coverage(O, seed=23):
+    """A weight in block (a, b) reaches rows of every type if a == b, else only type a, in group b only (section 4)."""
+    g = _rng(seed)
+    q, s, r, M = 3, 2, 2, 12
+    X = g.standard_normal((M, q * s)) + 3.0       # no zero entries
+    tau = np.arange(M) % q
+    for a in range(q):
+        for b in range(q):
+            W = np.zeros((q * s, q * r))
+            k0, c0 = a * s + 1, b * r + 1
+            W[k0, c0] = 1.0
+            Y = O.row_typed_forward(X, W, tau, q)
+            nz = Y != 0
+            want = np.zeros_like(nz)
+            for m in range(M):
+                if a == b or tau[m] == a:
+                    want[m, c0] = True
+            np.testing.assert_array_equal(nz, want)
+            np.testing.assert_array_equal(Y[want], X[want[:, c0], k0])
+
+
+# --------------------------------------------------------------------------
+# VJPs (appendix B, eq 31-35)
+# --------------------------------------------------------------------------
+
+def pin_vjp_scalar_eq31_35(O, seed=24):
+    """Per-token accumulation of eq 31-35 written out, versus the oracle's transposed table."""
+    g = _rng(seed)
+    for q, M, s, r in ((2, 5, 2, 3), (3, 7, 2, 2), (4, 9, 1, 2)):
+        X = g.standard_normal((M, q * s))
+        W = g.standard_normal((q * s, q * r))
+        dY = g.standard_normal((M, q * r))
+        tau = g.integers(0, q, size=M)
+        dX_w = np.zeros_like(X)
+        dW_w = np.zeros_like(W)
+        xs = lambda m, a: X[m, a * s:(a + 1) * s]
+        ys = lambda m, a: dY[m, a * r:(a + 1) * r]
+        Wb = lambda a, b: W[a * s:(a + 1) * s, b * r:(b + 1) * r]
+        for m in range(M):
+            i = int(tau[m])
+            dX_w[m, i * s:(i + 1) * s] += ys(m, i) @ Wb(i, i).T          # eq 31, first term
+            for j in range(q):
+                if j == i:
+                    continue
+                dX_w[m, i * s:(i + 1) * s] += ys(m, j) @ Wb(i, j).T      # eq 31, sum over j != i
+                dX_w[m, j * s:(j + 1) * s] += ys(m, j) @ Wb(j, j).T      # eq 32
+                dW_w[i * s:(i + 1) * s, j * r:(j + 1) * r] += np.outer(xs(m, i), ys(m, j))   # eq 34
+                dW_w[j * s:(j + 1) * s, j * r:(j + 1) * r] += np.outer(xs(m, j), ys(m, j))   # eq 35
+            dW_w[i * s:(i + 1) * s, i * r:(i + 1) * r] += np.outer(xs(m, i), ys(m, i))       # eq 33
+        dX, dW = O.row_typed_backward(X, W, dY, tau, q)
+        np.testing.assert_allclose(dX, dX_w, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dW, dW_w, rtol=1e-12, atol=1e-12)
+
+
+def pin_vjp_autograd(O, seed=25):
+    """float64 torch autograd of the masked-dense form equals the oracle's dX and dW."""
+    import torch
+    g = _rng(seed)
+    for q, M, s, r in ((2, 12, 3, 2), (3, 10, 2, 4), (5, 16, 2, 1)):
+        Xn = g.standard_normal((M, q * s))
+        Wn = g.standard_normal((q * s, q * r))
+        dYn = g.standard_normal((M, q * r))
+        tau = g.integers(0, q, size=M)
+        X = torch.tensor(Xn, requires_grad=True)
+        W = torch.tensor(Wn, requires_grad=True)
+        rows = []
+        for m in range(M):
+            i = int(tau[m])
+            mask = torch.tensor(masked_bank(np.ones_like(Wn), i, q))
+            rows.append(X[m:m + 1] @ (W * mask))
+        Y = torch.cat(rows)
+        (Y * torch.tensor(dYn)).sum().backward()
+        dX, dW = O.row_typed_backward(Xn, Wn, dYn, tau, q)
+        np.testing.assert_allclose(dX, X.grad.numpy(), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dW, W.grad.numpy(), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(O.row_typed_forward(Xn, Wn, tau, q), Y.detach().numpy(), rtol=1e-12, atol=1e-12)
+
+
+def pin_vjp_adjoint(O, seed=26):
+    """Bilinearity: <dY, Y> = <dX, X> = <dW, W>; dW blocks with no contributing rows are zero."""
+    g = _rng(seed)
+    q, M, s, r = 4, 6, 3, 2
+    X = g.standard_normal((M, q * s))
+    W = g.standard_normal((q * s, q * r))
+    dY = g.standard_normal((M, q * r))
+    tau = np.array([0, 0, 2, 2, 0, 2])          # types 1 and 3 absent
+    Y = O.row_typed_forward(X, W, tau, q)
+    dX, dW = O.row_typed_backward(X, W, dY, tau, q)
+    a = float((dY * Y).sum())
+    np.testing.assert_allclose(float((dX * X).sum()), a, rtol=1e-12)
+    np.testing.assert_allclose(float((dW * W).sum()), a, rtol=1e-12)
+    for b in range(q):
+        for j in range(q):
+            blk = dW[b * s:(b + 1) * s, j * r:(j + 1) * r]
+            if b != j and b in (1, 3):
+                assert not blk.any()                 # off-diagonal rows of absent types
+            else:
+                assert blk.any()
+
+
+# --------------------------------------------------------------------------
+# cost (eq 18-19, 21, 24) and index / schedule (section 4, Algorithm 1, App D.5)
+# --------------------------------------------------------------------------
+
+def pin_mac_count(O, seed=27):
+    """MACs = rho_q M K N for equal groups (eq 24); sum_i M_i C_i with C_i of eq 18 in general."""
+    g = _rng(seed)
+    for q in (1, 2, 3, 4, 8):
+        M, s, r = 37, 2 * q, 3
+        tau = g.integers(0, q, size=M)
+        gemms, macs = O.mac_count(tau, q, q * s, q * r)
+        assert Fraction(macs) == Fraction(2 * q - 1, q * q) * M * (q * s) * (q * r)
+        assert gemms == (2 * q - 1) * len(set(tau.tolist()))
+    q = 3
+    kw, nw = [2, 5, 1], [4, 1, 3]
+    K, N = sum(kw), sum(nw)
+    tau = np.array([0, 2, 2, 1, 0, 0, 2])
+    Ddiag = sum(a * b for a, b in zip(kw, nw))
+    want = sum(int((tau == i).sum()) * (Ddiag + kw[i] * (N - nw[i])) for i in range(q))
+    assert O.mac_count(tau, q, K, N, kw, nw)[1] == want
+
+
+def pin_type_index(O, seed=28):
+    """Cyclic types with any offset give arithmetic row progressions; arbitrary types a stable partition."""
+    for q in (1, 2, 3, 4, 8):
+        for M in (0, 1, 5, 16, 37):
+            for o in (0, 1, q - 1, 5):
+                tau = (np.arange(M) + o) % q
+                counts, offsets, rows, bad = O.type_index(tau, q)
+                assert bad == 0
+                for i in range(q):
+                    start = (i - o) % q
+                    cnt = max(0, -(-(M - start) // q))
+                    assert counts[i] == cnt
+                    np.testing.assert_array_equal(rows[offsets[i]:offsets[i + 1]], start + q * np.arange(cnt))
+    g = _rng(seed)
+    for q in (1, 3, 7):
+        tau = g.integers(-1, q + 1, size=50)
+        counts, offsets, rows, bad = O.type_index(tau, q)
+        assert bad == int(((tau < 0) | (tau >= q)).sum())
+        assert offsets[0] == 0 and offsets[-1] == 50 - bad
+        for i in range(q):
+            seg = rows[offsets[i]:offsets[i + 1]]
+            np.testing.assert_array_equal(seg, np.flatnonzero(tau == i))
+
+
+def pin_type_schedule(O):
+    """Section 4's 1 + ((p-1) mod q) with 1-based p is p mod q 0-based; App D.5's floor((p mod 768)/192)."""
+    p1 = np.arange(1, 200)
+    for q in (1, 2, 3, 8):
+        paper = 1 + ((p1 - 1) % q)
+        np.testing.assert_array_equal(O.type_schedule(p1 - 1, q) + 1, paper)
+    p = np.array([0, 191, 192, 383, 384, 575, 576, 767, 768, 959, 1535, 1536])
+    np.testing.assert_array_equal(O.type_schedule(p, 4, "interval", 768), [0, 0, 1, 1, 2, 2, 3, 3, 0, 0, 3, 0])
+
+
+ALL_PINS = [
+    pin_q2_table, pin_q2_scalar_example, pin_eq3_rectangular_blocks, pin_eq13_14,
+    pin_product_counts, pin_graph_counts, pin_appendix_a, pin_associativity,
+    pin_row_typed_composition, pin_unit_laws, pin_brute_force, pin_teaching_matrix,
+    pin_masked_dense, pin_row_typed_is_square_rows, pin_q1_is_matmul, pin_block_diagonal,
+    pin_coverage, pin_vjp_scalar_eq31_35, pin_vjp_autograd, pin_vjp_adjoint,
+    pin_mac_count, pin_type_index, pin_type_schedule,
+]

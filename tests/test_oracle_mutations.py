@@ -1,0 +1,158 @@
+"""Planted mistakes in the oracle (on the CPU) must each trip at least one pin.
+
+Each mutant replaces one oracle function with a plausibly wrong version (a
+dropped term, a wrong index, a transposed operand, a sign flip, an unstable
+index) for the duration of one test; the pins of oracle_pins.py then run and
+at least one of them has to fail.
+"""
+import numpy as np
+import pytest
+
+from oracle import qalg_oracle as O
+from oracle_pins import ALL_PINS
+
+_real_table = O.structure_table
+_real_fwd = O.row_typed_forward
+_real_bwd = O.row_typed_backward
+_real_index = O.type_index
+
+
+def table_with_edge_edge(q, edges=None):
+    """Mistake: keeps edge*edge products (this is ordinary block matmul)."""
+    t = list(_real_table(q, edges))
+    slots = O.graph_slots(q, edges)
+    for (a, b) in slots:
+        for (c, d) in slots:
+            if b == c and a != b and c != d and (a, d) in slots:
+                t.append(((a, b), (c, d), (a, d)))
+    return t
+
+
+def table_without_right_vertex(q, edges=None):
+    """Mistake: drops a_ij e_j (the x_ij W_jj term)."""
+    return [(x, w, z) for (x, w, z) in _real_table(q, edges) if not (x[0] != x[1] and w[0] == w[1])]
+
+
+def table_wrong_result(q, edges=None):
+    """Mistake: writes the product to the right factor's slot instead of (a, d)."""
+    return [(x, w, w) for (x, w, z) in _real_table(q, edges)]
+
+
+def table_transposed_weight(q, edges=None):
+    """Mistake: uses weight block (d, b) instead of (b, d)."""
+    return [(x, (w[1], w[0]), z) for (x, w, z) in _real_table(q, edges)]
+
+
+def fwd_sign_flip(X, W, tau, q, in_widths=None, out_widths=None, edges=None):
+    """Mistake: subtracts the off-diagonal endpoint product."""
+    Y = _real_fwd(X, W, tau, q, in_widths, out_widths, edges)
+    X = np.asarray(X, float)
+    W = np.asarray(W, float)
+    kb = O.group_bounds(X.shape[1], q, in_widths)
+    nb = O.group_bounds(W.shape[1], q, out_widths)
+    for m in range(X.shape[0]):
+        i = int(tau[m])
+        if not 0 <= i < q:
+            continue
+        for j in range(q):
+            if j != i:
+                Y[m, nb[j][0]:nb[j][1]] -= 2 * X[m, kb[i][0]:kb[i][1]] @ W[kb[i][0]:kb[i][1], nb[j][0]:nb[j][1]]
+    return Y
+
+
+def bwd_dw_all_rows(X, W, dY, tau, q, in_widths=None, out_widths=None, edges=None):
+    """Mistake: off-diagonal weight gradients summed over every row, not just type-i rows."""
+    dX, dW = _real_bwd(X, W, dY, tau, q, in_widths, out_widths, edges)
+    X = np.asarray(X, float)
+    dY = np.asarray(dY, float)
+    kb = O.group_bounds(X.shape[1], q, in_widths)
+    nb = O.group_bounds(dY.shape[1], q, out_widths)
+    for b in range(q):
+        for j in range(q):
+            if b != j:
+                dW[kb[b][0]:kb[b][1], nb[j][0]:nb[j][1]] = X[:, kb[b][0]:kb[b][1]].T @ dY[:, nb[j][0]:nb[j][1]]
+    return dX, dW
+
+
+def bwd_dx_drops_eq32(X, W, dY, tau, q, in_widths=None, out_widths=None, edges=None):
+    """Mistake: activation gradient keeps only the source-row terms (drops eq 32)."""
+    dX, dW = _real_bwd(X, W, dY, tau, q, in_widths, out_widths, edges)
+    X = np.asarray(X, float)
+    kb = O.group_bounds(X.shape[1], q, in_widths)
+    for m in range(X.shape[0]):
+        i = int(tau[m])
+        for a in range(q):
+            if a != i:
+                dX[m, kb[a][0]:kb[a][1]] = 0.0
+    return dX, dW
+
+
+def bwd_dx_untransposed(X, W, dY, tau, q, in_widths=None, out_widths=None, edges=None):
+    """Mistake: multiplies by W_bj instead of its transpose (square blocks, so shapes still fit)."""
+    X = np.asarray(X, float)
+    W = np.asarray(W, float)
+    dY = np.asarray(dY, float)
+    kb = O.group_bounds(X.shape[1], q, in_widths)
+    nb = O.group_bounds(W.shape[1], q, out_widths)
+    dX, dW = _real_bwd(X, W, dY, tau, q, in_widths, out_widths, edges)
+    dX[:] = 0.0
+    for m in range(X.shape[0]):
+        i = int(tau[m])
+        for (xa, xb), (wa, wd), (ya, yd) in O.structure_table(q, edges):
+            if xa != i:
+                continue
+            blk = W[kb[wa][0]:kb[wa][1], nb[wd][0]:nb[wd][1]]
+            if blk.shape[0] != blk.shape[1]:
+                blk = blk.T
+            dX[m, kb[xb][0]:kb[xb][1]] += dY[m, nb[yd][0]:nb[yd][1]] @ blk
+    return dX, dW
+
+
+def index_unstable(tau, q):
+    """Mistake: rows of each type listed in descending order."""
+    counts, offsets, rows, bad = _real_index(tau, q)
+    rows = rows.copy()
+    for i in range(q):
+        rows[offsets[i]:offsets[i + 1]] = rows[offsets[i]:offsets[i + 1]][::-1]
+    return counts, offsets, rows, bad
+
+
+def index_drops_bad_count(tau, q):
+    """Mistake: rows with out-of-range types are not counted."""
+    counts, offsets, rows, _bad = _real_index(tau, q)
+    return counts, offsets, rows, 0
+
+
+def schedule_one_based(positions, q, kind="cyclic", period=0):
+    """Mistake: keeps the page's 1-based types without shifting to 0-based."""
+    p = np.asarray(positions, dtype=np.int64)
+    if kind == "cyclic":
+        return (1 + ((p - 1) % q)).astype(np.int32)
+    return ((p % period) // (period // q)).astype(np.int32)
+
+
+MUTANTS = [
+    ("structure_table", table_with_edge_edge),
+    ("structure_table", table_without_right_vertex),
+    ("structure_table", table_wrong_result),
+    ("structure_table", table_transposed_weight),
+    ("row_typed_forward", fwd_sign_flip),
+    ("row_typed_backward", bwd_dw_all_rows),
+    ("row_typed_backward", bwd_dx_drops_eq32),
+    ("row_typed_backward", bwd_dx_untransposed),
+    ("type_index", index_unstable),
+    ("type_index", index_drops_bad_count),
+    ("type_schedule", schedule_one_based),
+]
+
+
+@pytest.mark.parametrize("name,mutant", MUTANTS, ids=[m.__name__ for _, m in MUTANTS])
+def test_planted_mistake_is_caught(monkeypatch, name, mutant):
+    monkeypatch.setattr(O, name, mutant)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(O)
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {mutant.__name__}"
