@@ -1,0 +1,257 @@
+"""Python binding of libqalg, the row-typed Q_q projection for MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of libqalg.so,
+called through its C ABI (include/qalg.h).  PyTorch supplies device memory and
+the current stream.  There is no CPU fallback: if libqalg.so is missing or a
+tensor is not on the GPU, the call raises.
+
+Functions carry the C names:
+    qalg_forward, qalg_backward_dx, qalg_backward_dw, qalg_forward_batched,
+    qalg_type_schedule, qalg_build_index, qalg_build_index_batched,
+    qalg_read_status, qalg_workspace_bytes, qalg_index_layout,
+    qalg_status_string, qalg_version.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+
+__all__ = [
+    "QalgError", "lib", "lib_path",
+    "QALG_F32", "QALG_BF16", "QALG_FLAG_INDEX_READY", "QALG_FLAG_FORCE_TILED",
+    "QALG_FLAG_FORCE_SMALL_M", "QALG_SCHEDULE_CYCLIC", "QALG_SCHEDULE_INTERVAL", "QALG_MAX_Q",
+    "qalg_version", "qalg_status_string", "qalg_workspace_bytes", "qalg_index_layout",
+    "qalg_type_schedule", "qalg_build_index", "qalg_build_index_batched",
+    "qalg_forward", "qalg_backward_dx", "qalg_backward_dw", "qalg_forward_batched",
+    "qalg_read_status", "workspace",
+]
+
+QALG_F32 = 0
+QALG_BF16 = 1
+QALG_FLAG_INDEX_READY = 1
+QALG_FLAG_FORCE_TILED = 2
+QALG_FLAG_FORCE_SMALL_M = 4
+QALG_SCHEDULE_CYCLIC = 0
+QALG_SCHEDULE_INTERVAL = 1
+QALG_MAX_Q = 512
+
+_PKG = pathlib.Path(__file__).resolve().parent
+lib_path = _PKG / "libqalg.so"
+_lib = None
+
+_c_size = ctypes.c_size_t
+_c_i32 = ctypes.c_int32
+_c_i64 = ctypes.c_int64
+_c_u32 = ctypes.c_uint32
+_vp = ctypes.c_void_p
+
+_SIGS = {
+    "qalg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "qalg_version": (ctypes.c_int, []),
+    "qalg_workspace_bytes": (_c_size, [_c_i32, _c_i64]),
+    "qalg_index_layout": (ctypes.c_int, [_c_i32, _c_i64, ctypes.POINTER(_c_i64)]),
+    "qalg_type_schedule": (ctypes.c_int, [_vp, _c_i64, _c_i32, _c_i32, _c_i64, _vp, _vp]),
+    "qalg_build_index": (ctypes.c_int, [_vp, _c_i32, _c_i64, _vp, _c_size, _vp]),
+    "qalg_build_index_batched": (ctypes.c_int, [_c_i32, _vp, _c_i32, _c_i64, _vp, _c_size, _vp]),
+    "qalg_forward": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
+    "qalg_backward_dx": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
+    "qalg_backward_dw": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
+    "qalg_forward_batched": (ctypes.c_int, [_c_i32, _vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
+    "qalg_read_status": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i64, _vp, ctypes.POINTER(_c_i64)]),
+}
+
+
+class QalgError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {qalg_status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libqalg.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not lib_path.exists():
+            raise RuntimeError(f"{lib_path} is missing: build it with `python -m gemm_qalg_forward_amd.build`")
+        handle = ctypes.CDLL(str(lib_path))
+        for name, (res, args) in _SIGS.items():
+            f = getattr(handle, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise QalgError(fn, status)
+
+
+def qalg_version() -> int:
+    return lib().qalg_version()
+
+
+def qalg_status_string(status: int) -> str:
+    return lib().qalg_status_string(status).decode()
+
+
+def qalg_workspace_bytes(q: int, M: int) -> int:
+    return lib().qalg_workspace_bytes(q, M)
+
+
+def qalg_index_layout(q: int, M: int) -> tuple[int, int, int, int]:
+    out = (_c_i64 * 4)()
+    _check("qalg_index_layout", lib().qalg_index_layout(q, M, out))
+    return tuple(out)
+
+
+# ---------------------------------------------------------------------------
+# tensor marshalling (torch is imported lazily: the CPU tests need only ctypes)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, name: str):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU (libqalg has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major, packed)")
+    return t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return QALG_BF16
+    if t.dtype == torch.float32:
+        return QALG_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def workspace(q: int, M: int, E: int = 1, device="cuda"):
+    """A device workspace of the size the projections need (uint8 tensor)."""
+    torch = _torch()
+    n = qalg_workspace_bytes(q, M) * E
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _tau_check(tau, M: int, E: int = 1):
+    torch = _torch()
+    if tau.dtype != torch.int32 or tau.numel() != M * E:
+        raise ValueError(f"tau must be int32 with {M * E} elements")
+
+
+def qalg_type_schedule(positions, q: int, kind: int = QALG_SCHEDULE_CYCLIC, period: int = 0,
+                       tau=None, stream=None):
+    """tau[m] = tau(positions[m]) on the device (int64 positions -> int32 types)."""
+    torch = _torch()
+    if positions.dtype != torch.int64:
+        raise TypeError("positions must be int64")
+    M = positions.numel()
+    if tau is None:
+        tau = torch.empty(M, dtype=torch.int32, device=positions.device)
+    _check("qalg_type_schedule", lib().qalg_type_schedule(
+        _dev_ptr(positions, "positions"), M, q, kind, period, _dev_ptr(tau, "tau"), _stream(stream)))
+    return tau
+
+
+def qalg_build_index(tau, q: int, ws=None, stream=None):
+    M = tau.numel()
+    if ws is None:
+        ws = workspace(q, M, device=tau.device)
+    _check("qalg_build_index", lib().qalg_build_index(
+        _dev_ptr(tau, "tau"), q, M, _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+    return ws
+
+
+def qalg_build_index_batched(tau, q: int, ws=None, stream=None):
+    E, M = tau.shape
+    if ws is None:
+        ws = workspace(q, M, E, device=tau.device)
+    _check("qalg_build_index_batched", lib().qalg_build_index_batched(
+        E, _dev_ptr(tau, "tau"), q, M, _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+    return ws
+
+
+def _proj(fn: str, A, B, tau, q: int, out, out_shape, ws, flags: int, stream, M: int, K: int, N: int):
+    torch = _torch()
+    if A.dtype != B.dtype:
+        raise TypeError("operands must share a dtype")
+    dt = _dtype_code(A)
+    _tau_check(tau, M)
+    if out is None:
+        out = torch.empty(out_shape, dtype=A.dtype, device=A.device)
+    if ws is None:
+        ws = workspace(q, M, device=A.device)
+    _check(fn, getattr(lib(), fn)(
+        _dev_ptr(A, "A"), _dev_ptr(B, "B"), _dev_ptr(tau, "tau"), q, M, K, N, _dev_ptr(out, "out"),
+        dt, _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags, _stream(stream)))
+    return out
+
+
+def qalg_forward(X, W, tau, q: int, Y=None, ws=None, flags: int = 0, stream=None):
+    """Y = X *_{Q_q} W: X [M, K], W [K, N], tau int32 [M] -> Y [M, N]."""
+    M, K = X.shape
+    K2, N = W.shape
+    if K2 != K:
+        raise ValueError("X and W inner sizes differ")
+    return _proj("qalg_forward", X, W, tau, q, Y, (M, N), ws, flags, stream, M, K, N)
+
+
+def qalg_backward_dx(dY, W, tau, q: int, dX=None, ws=None, flags: int = 0, stream=None):
+    """dX of the projection: dY [M, N], W [K, N] -> dX [M, K]."""
+    M, N = dY.shape
+    K, N2 = W.shape
+    if N2 != N:
+        raise ValueError("dY and W widths differ")
+    return _proj("qalg_backward_dx", dY, W, tau, q, dX, (M, K), ws, flags, stream, M, K, N)
+
+
+def qalg_backward_dw(X, dY, tau, q: int, dW=None, ws=None, flags: int = 0, stream=None):
+    """dW of the projection: X [M, K], dY [M, N] -> dW [K, N]."""
+    M, K = X.shape
+    M2, N = dY.shape
+    if M2 != M:
+        raise ValueError("X and dY row counts differ")
+    return _proj("qalg_backward_dw", X, dY, tau, q, dW, (K, N), ws, flags, stream, M, K, N)
+
+
+def qalg_forward_batched(X, W, tau, q: int, Y=None, ws=None, flags: int = 0, stream=None):
+    """E projections with their own weight banks: X [E, M, K], W [E, K, N], tau [E, M] -> Y [E, M, N]."""
+    torch = _torch()
+    E, M, K = X.shape
+    E2, K2, N = W.shape
+    if E2 != E or K2 != K:
+        raise ValueError("X and W shapes differ")
+    if X.dtype != W.dtype:
+        raise TypeError("operands must share a dtype")
+    _tau_check(tau, M, E)
+    if Y is None:
+        Y = torch.empty((E, M, N), dtype=X.dtype, device=X.device)
+    if ws is None:
+        ws = workspace(q, M, E, device=X.device)
+    _check("qalg_forward_batched", lib().qalg_forward_batched(
+        E, _dev_ptr(X, "X"), _dev_ptr(W, "W"), _dev_ptr(tau, "tau"), q, M, K, N, _dev_ptr(Y, "Y"),
+        _dtype_code(X), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags, _stream(stream)))
+    return Y
+
+
+def qalg_read_status(ws, q: int, M: int, E: int = 1, stream=None) -> int:
+    """Rows with an out-of-range type seen by the last index build in ws (synchronises)."""
+    out = _c_i64(0)
+    _check("qalg_read_status", lib().qalg_read_status(
+        _dev_ptr(ws, "ws"), E, q, M, _stream(stream), ctypes.byref(out)))
+    return out.value

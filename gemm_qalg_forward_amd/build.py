@@ -1,0 +1,62 @@
+"""Build libqalg.so (HIP for gfx950) in-tree with hipcc.
+
+Usage: python -m gemm_qalg_forward_amd.build  (or call build()).
+"""
+from __future__ import annotations
+
+import os
+import pathlib
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = pathlib.Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+OBJ = PKG / "_build"
+LIB = PKG / "libqalg.so"
+
+SOURCES = ["qalg_api.cpp", "qalg_index.hip", "qalg_tiled.hip", "qalg_small_m.hip"]
+
+HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
+    # packed-fp32 instructions stay off: the compiler emits none of them
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+    f"-I{ROOT / 'include'}", f"-I{CSRC}",
+]
+
+
+def _compile(src: str) -> pathlib.Path:
+    out = OBJ / (src + ".o")
+    cmd = [HIPCC, *COMMON, "-c", str(CSRC / src), "-o", str(out)]
+    if src.endswith(".cpp"):
+        cmd[1:1] = ["-x", "hip"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed on {src}")
+    return out
+
+
+def build(verbose: bool = False) -> pathlib.Path:
+    OBJ.mkdir(exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB.with_suffix(".so.tmp")
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *map(str, objs), "-o", str(tmp)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("link of libqalg.so failed")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,234 @@
+// C-ABI of libqalg: argument validation, path choice and launches.  See
+// include/qalg.h for the contract of every entry point.
+//
+// Nothing here waits on the device except qalg_read_status.  Every argument
+// error is detected before the first launch of a call.
+#include "qalg.h"
+
+#include <climits>
+#include <cstdint>
+
+#include "qalg_internal.h"
+
+namespace {
+
+using qalg::Op;
+using qalg::ProblemDesc;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+qalg_status hip_status(hipError_t e) { return e == hipSuccess ? QALG_OK : QALG_ERR_HIP; }
+
+// Shape, type and flag checks shared by the projection entry points.
+qalg_status check_shape(int32_t E, int32_t q, int64_t M, int64_t K, int64_t N, int32_t dtype,
+                        uint32_t flags) {
+  if (dtype != QALG_F32 && dtype != QALG_BF16) return QALG_ERR_DTYPE;
+  if (flags & ~uint32_t(QALG_FLAG_INDEX_READY | QALG_FLAG_FORCE_TILED | QALG_FLAG_FORCE_SMALL_M))
+    return QALG_ERR_ARG;
+  if ((flags & QALG_FLAG_FORCE_TILED) && (flags & QALG_FLAG_FORCE_SMALL_M)) return QALG_ERR_ARG;
+  if (E < 1 || M < 0 || K <= 0 || N <= 0) return QALG_ERR_DIM;
+  if (M > INT32_MAX / 2 || K > INT32_MAX / 2 || N > INT32_MAX / 2) return QALG_ERR_DIM;
+  if (q < 1 || q > QALG_MAX_Q || K % q || N % q) return QALG_ERR_Q;
+  if (dtype == QALG_BF16 && ((K / q) % 8 || (N / q) % 8)) return QALG_ERR_ALIGN;
+  if (dtype == QALG_F32 && ((K / q) % 4 || (N / q) % 4)) return QALG_ERR_ALIGN;
+  return QALG_OK;
+}
+
+qalg_status check_ws(int32_t E, int32_t q, int64_t M, const void* ws, size_t ws_bytes) {
+  if (ws == nullptr) return QALG_ERR_NULL;
+  if (!aligned16(ws)) return QALG_ERR_WORKSPACE;
+  const size_t need = size_t(E) * qalg_workspace_bytes(q, M);
+  if (ws_bytes < need) return QALG_ERR_WORKSPACE;
+  return QALG_OK;
+}
+
+int64_t ws_stride_ints(int32_t q, int64_t M) { return qalg::ws_layout(q, M).total_ints; }
+
+
+// Shared driver of qalg_forward / qalg_backward_dx / qalg_backward_dw / batched forward.
+qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const int32_t* tau,
+                           int32_t q, int64_t M, int64_t K, int64_t N, void* C, int32_t dtype,
+                           void* ws, size_t ws_bytes, uint32_t flags, void* stream) {
+  qalg_status st = check_shape(E, q, M, K, N, dtype, flags);
+  if (st != QALG_OK) return st;
+  if ((flags & QALG_FLAG_FORCE_SMALL_M) && (op != Op::Fwd || dtype != QALG_BF16)) return QALG_ERR_ARG;
+  // with no rows only dW's output is touched (it is zero-filled)
+  if (M > 0 && (A == nullptr || B == nullptr || C == nullptr || tau == nullptr)) return QALG_ERR_NULL;
+  if (M == 0 && op == Op::Dw && C == nullptr) return QALG_ERR_NULL;
+  if ((A && !aligned16(A)) || (B && !aligned16(B)) || (C && !aligned16(C)) ||
+      (tau && (reinterpret_cast<uintptr_t>(tau) & 3u)))
+    return QALG_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int elem = dtype == QALG_BF16 ? 2 : 4;
+
+  if (M == 0) {
+    if (op != Op::Dw) return QALG_OK;
+    // no rows: every weight-gradient block is zero
+    return hip_status(qalg::launch_fill_zero(C, size_t(E) * size_t(K) * size_t(N) * elem, s));
+  }
+
+  ProblemDesc p{};
+  p.op = op;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.tau = tau;
+  p.q = q;
+  p.M = M;
+  p.K = K;
+  p.N = N;
+  p.E = E;
+
+  // the workspace contract is the same on every path, used or not
+  st = check_ws(E, q, M, ws, ws_bytes);
+  if (st != QALG_OK) return st;
+
+  // small-M weight-streaming forward: reads the types directly, no index
+  const bool small_ok = dtype == QALG_BF16 && qalg::small_m_supported(p);
+  if (flags & QALG_FLAG_FORCE_SMALL_M) {
+    if (!small_ok) return QALG_ERR_ARG;
+  }
+  const bool use_small = small_ok && !(flags & QALG_FLAG_FORCE_TILED);
+  if (use_small) return hip_status(qalg::launch_small_m_bf16(p, s));
+  const int64_t stride = ws_stride_ints(q, M);
+  int32_t* wsi = static_cast<int32_t*>(ws);
+  p.ws = wsi;
+  p.ws_stride = stride;
+
+  // rows of an out-of-range type get zero Y / dX rows; dW ignores them
+  void* zero_out = op == Op::Dw ? nullptr : C;
+  const int64_t zero_ld = op == Op::Fwd ? N : K;
+  const int64_t zero_stride = M * zero_ld * elem;
+  hipError_t e;
+  if (!(flags & QALG_FLAG_INDEX_READY)) {
+    e = qalg::launch_build_index_zeroing(tau, q, M, E, wsi, stride, zero_out, zero_ld, elem,
+                                         zero_stride, s);
+  } else if (zero_out != nullptr) {
+    e = qalg::launch_zero_bad_rows(wsi, q, M, E, stride, zero_out, zero_ld, elem, zero_stride, s);
+  } else {
+    e = hipSuccess;
+  }
+  if (e != hipSuccess) return QALG_ERR_HIP;
+
+  e = dtype == QALG_BF16 ? qalg::launch_tiled_bf16(p, s) : qalg::launch_tiled_f32(p, s);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qalg_status_string(int status) {
+  switch (status) {
+    case QALG_OK: return "QALG_OK";
+    case QALG_ERR_NULL: return "QALG_ERR_NULL: a required pointer is NULL";
+    case QALG_ERR_DIM: return "QALG_ERR_DIM: a size is negative, zero or too large";
+    case QALG_ERR_Q: return "QALG_ERR_Q: q < 1, q > QALG_MAX_Q, or q does not divide K and N";
+    case QALG_ERR_ALIGN: return "QALG_ERR_ALIGN: pointer or group width misaligned";
+    case QALG_ERR_DTYPE: return "QALG_ERR_DTYPE: unknown element type";
+    case QALG_ERR_WORKSPACE: return "QALG_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case QALG_ERR_HIP: return "QALG_ERR_HIP: a HIP launch or copy failed";
+    case QALG_ERR_ARG: return "QALG_ERR_ARG: unknown flag, schedule or unsupported forced path";
+    default: return "unknown qalg status";
+  }
+}
+
+int qalg_version(void) { return QALG_VERSION; }
+
+size_t qalg_workspace_bytes(int32_t q, int64_t M) {
+  if (q < 1 || q > QALG_MAX_Q || M < 0 || M > INT32_MAX / 2) return 0;
+  return size_t(qalg::ws_layout(q, M).total_ints) * sizeof(int32_t);
+}
+
+qalg_status qalg_index_layout(int32_t q, int64_t M, int64_t out_offsets[4]) {
+  if (q < 1 || q > QALG_MAX_Q) return QALG_ERR_Q;
+  if (M < 0 || M > INT32_MAX / 2) return QALG_ERR_DIM;
+  if (out_offsets == nullptr) return QALG_ERR_NULL;
+  const qalg::WsLayout L = qalg::ws_layout(q, M);
+  out_offsets[0] = 0;
+  out_offsets[1] = L.counts;
+  out_offsets[2] = L.offsets;
+  out_offsets[3] = L.rows;
+  return QALG_OK;
+}
+
+qalg_status qalg_type_schedule(const int64_t* positions, int64_t M, int32_t q, int32_t kind,
+                               int64_t period, int32_t* tau, void* stream) {
+  if (q < 1 || q > QALG_MAX_Q) return QALG_ERR_Q;
+  if (M < 0 || M > INT32_MAX / 2) return QALG_ERR_DIM;
+  if (kind != QALG_SCHEDULE_CYCLIC && kind != QALG_SCHEDULE_INTERVAL) return QALG_ERR_ARG;
+  if (kind == QALG_SCHEDULE_INTERVAL && (period <= 0 || period % q)) return QALG_ERR_ARG;
+  if (M == 0) return QALG_OK;
+  if (positions == nullptr || tau == nullptr) return QALG_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(positions) & 7u) || (reinterpret_cast<uintptr_t>(tau) & 3u))
+    return QALG_ERR_ALIGN;
+  return hip_status(qalg::launch_type_schedule(positions, M, q, kind, period, tau,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+qalg_status qalg_build_index_batched(int32_t E, const int32_t* tau, int32_t q, int64_t M, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  if (E < 1) return QALG_ERR_DIM;
+  if (q < 1 || q > QALG_MAX_Q) return QALG_ERR_Q;
+  if (M < 0 || M > INT32_MAX / 2) return QALG_ERR_DIM;
+  if (M > 0 && tau == nullptr) return QALG_ERR_NULL;
+  if (tau && (reinterpret_cast<uintptr_t>(tau) & 3u)) return QALG_ERR_ALIGN;
+  const qalg_status st = check_ws(E, q, M, ws, ws_bytes);
+  if (st != QALG_OK) return st;
+  return hip_status(qalg::launch_build_index(tau, q, M, E, static_cast<int32_t*>(ws),
+                                             ws_stride_ints(q, M), static_cast<hipStream_t>(stream)));
+}
+
+qalg_status qalg_build_index(const int32_t* tau, int32_t q, int64_t M, void* ws, size_t ws_bytes,
+                             void* stream) {
+  return qalg_build_index_batched(1, tau, q, M, ws, ws_bytes, stream);
+}
+
+qalg_status qalg_forward(const void* X, const void* W, const int32_t* tau, int32_t q, int64_t M,
+                         int64_t K, int64_t N, void* Y, int32_t dtype, void* ws, size_t ws_bytes,
+                         uint32_t flags, void* stream) {
+  return run_projection(Op::Fwd, 1, X, W, tau, q, M, K, N, Y, dtype, ws, ws_bytes, flags, stream);
+}
+
+qalg_status qalg_backward_dx(const void* dY, const void* W, const int32_t* tau, int32_t q,
+                             int64_t M, int64_t K, int64_t N, void* dX, int32_t dtype, void* ws,
+                             size_t ws_bytes, uint32_t flags, void* stream) {
+  if (flags & QALG_FLAG_FORCE_SMALL_M) return QALG_ERR_ARG;
+  return run_projection(Op::Dx, 1, dY, W, tau, q, M, K, N, dX, dtype, ws, ws_bytes, flags, stream);
+}
+
+qalg_status qalg_backward_dw(const void* X, const void* dY, const int32_t* tau, int32_t q,
+                             int64_t M, int64_t K, int64_t N, void* dW, int32_t dtype, void* ws,
+                             size_t ws_bytes, uint32_t flags, void* stream) {
+  if (flags & QALG_FLAG_FORCE_SMALL_M) return QALG_ERR_ARG;
+  return run_projection(Op::Dw, 1, X, dY, tau, q, M, K, N, dW, dtype, ws, ws_bytes, flags, stream);
+}
+
+qalg_status qalg_forward_batched(int32_t E, const void* X, const void* W, const int32_t* tau,
+                                 int32_t q, int64_t M, int64_t K, int64_t N, void* Y,
+                                 int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags,
+                                 void* stream) {
+  return run_projection(Op::Fwd, E, X, W, tau, q, M, K, N, Y, dtype, ws, ws_bytes, flags, stream);
+}
+
+qalg_status qalg_read_status(const void* ws, int32_t E, int32_t q, int64_t M, void* stream,
+                             int64_t* bad_tau_rows) {
+  if (ws == nullptr || bad_tau_rows == nullptr) return QALG_ERR_NULL;
+  if (E < 1 || M < 0 || M > INT32_MAX / 2) return QALG_ERR_DIM;
+  if (q < 1 || q > QALG_MAX_Q) return QALG_ERR_Q;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t pitch = size_t(ws_stride_ints(q, M)) * sizeof(int32_t);
+  int64_t total = 0;
+  for (int32_t e = 0; e < E; ++e) {
+    int32_t v = 0;
+    if (hipMemcpyAsync(&v, static_cast<const char*>(ws) + e * pitch, sizeof(v),
+                       hipMemcpyDeviceToHost, s) != hipSuccess)
+      return QALG_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return QALG_ERR_HIP;
+    total += v;
+  }
+  *bad_tau_rows = total;
+  return QALG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Internal declarations shared by the libqalg translation units: the workspace
+// layout of the type index and the host-side launchers each kernel file exports.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qalg {
+
+// Row-tile heights the index precomputes prefix sums for (tiled kernels pick one).
+constexpr int kNumTileHeights = 5;
+constexpr int kTileHeights[kNumTileHeights] = {16, 32, 64, 128, 256};
+constexpr int tile_height_slot(int bm) {
+  return bm == 16 ? 0 : bm == 32 ? 1 : bm == 64 ? 2 : bm == 128 ? 3 : bm == 256 ? 4 : -1;
+}
+
+// Workspace of one problem, in int32 elements:
+//   [0]            rows with an out-of-range type
+//   [1]            magic (kIndexMagic) once an index was written
+//   [2], [3]       q and M of that index
+//   [16, 16+q)     counts[q]                 (M_i)
+//   [.., +q+1)     offsets[q+1]              (running sums of counts)
+//   [.., +5(q+1))  tile_off[5][q+1]          (running sums of ceil(M_i / BM))
+//   [rows, +M)     rows[M]                   (rows of type 0, 1, ..., then bad rows)
+constexpr int32_t kIndexMagic = 0x51414c47;  // "QALG"
+
+struct WsLayout {
+  int64_t counts, offsets, tile_off, rows, total_ints;
+};
+
+inline WsLayout ws_layout(int q, int64_t M) {
+  WsLayout L;
+  L.counts = 16;
+  L.offsets = L.counts + q;
+  L.tile_off = L.offsets + (q + 1);
+  int64_t end = L.tile_off + int64_t(kNumTileHeights) * (q + 1);
+  L.rows = (end + 15) / 16 * 16;
+  L.total_ints = (L.rows + M + 63) / 64 * 64;
+  return L;
+}
+
+// ---- launchers (return hipError_t of the launch) ----
+
+hipError_t launch_type_schedule(const int64_t* pos, int64_t M, int q, int kind, int64_t period,
+                                int32_t* tau, hipStream_t s);
+hipError_t launch_build_index(const int32_t* tau, int q, int64_t M, int E, int32_t* ws,
+                              int64_t ws_stride_ints, hipStream_t s);
+// Same, and zero the output rows (row length zero_ld elements of zero_elem_bytes)
+// whose type is out of range, in each problem's output (zero_stride_bytes apart).
+hipError_t launch_build_index_zeroing(const int32_t* tau, int q, int64_t M, int E, int32_t* ws,
+                                      int64_t ws_stride_ints, void* zero_out, int64_t zero_ld,
+                                      int zero_elem_bytes, int64_t zero_stride_bytes,
+                                      hipStream_t s);
+// Zero `bytes` bytes (a multiple of 4) at p with a kernel (no memset node in captured graphs).
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// Zero those rows from an index built earlier.
+hipError_t launch_zero_bad_rows(const int32_t* ws, int q, int64_t M, int E, int64_t ws_stride_ints,
+                                void* out, int64_t ld, int elem_bytes, int64_t stride_bytes,
+                                hipStream_t s);
+
+enum class Op { Fwd = 0, Dx = 1, Dw = 2 };
+
+struct ProblemDesc {
+  Op op;
+  const void* A;      // fwd: X;  dx: dY;  dw: X
+  const void* B;      // fwd: W;  dx: W;   dw: dY
+  void* C;            // fwd: Y;  dx: dX;  dw: dW
+  const int32_t* tau; // types of problem 0 (small-M path reads them directly)
+  const int32_t* ws;  // index of problem 0
+  int64_t ws_stride;  // int32 elements between the indices of consecutive problems
+  int q;
+  int64_t M, K, N;
+  int E;              // problems (experts); operands packed back to back
+};
+
+hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s);
+hipError_t launch_tiled_f32(const ProblemDesc& p, hipStream_t s);
+hipError_t launch_small_m_bf16(const ProblemDesc& p, hipStream_t s);
+bool small_m_supported(const ProblemDesc& p);
+
+}  // namespace qalg

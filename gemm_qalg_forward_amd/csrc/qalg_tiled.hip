@@ -1,0 +1,640 @@
+// Tiled matrix-core kernels of the row-typed Q_q projection (bf16 in, fp32
+// accumulate, bf16 out) for gfx950.
+//
+// Paper: arXiv 2609.32814.  Forward: section 4, eq 16-17, and Algorithm 1
+// (section 6.1): a row of type i gets y_i = x_i W_ii and y_j = x_i W_ij +
+// x_j W_jj.  Section 5.3 describes the fused schedule used here: one output
+// tile accumulates both endpoint products before it is written.  Gradients:
+// appendix B, eq 31-35, with one owner per output element (section 5.3).
+//
+// Every output tile is an ordinary GEMM tile whose contraction runs over at
+// most two segments of the feature axis:
+//   forward  Y[I_i, cols of group j]  : X[I_i, g_i] W[g_i, .] (+ X[I_i, g_j] W[g_j, .] if j != i)
+//   dX       dX[I_i, cols of group k] : dY[I_i, all N] W[g_i, :]^T if k == i,
+//                                       dY[I_i, group k] W[g_k, g_k]^T otherwise
+//   dW       dW[g_b, g_j]             : X[R, g_b]^T dY[R, g_j], R = all typed rows if b == j,
+//                                       else the rows of type b
+// Absent block products are never visited: they are simply not in a tile's
+// segment list.  Rows of a type are addressed through the index's row list
+// (a gather for arbitrary types; for a cyclic schedule the list is the
+// arithmetic progression start + k*q, i.e. strided rows).
+//
+// Data movement.  Operands go global -> registers -> LDS (double buffered,
+// one barrier per k-step) -> MFMA.  Both LDS tiles are stored
+// contraction-contiguous in 16-byte chunks so that each lane fetches one
+// 8-element MFMA operand with a single 128-bit LDS read; chunk positions are
+// XOR-swizzled by row to spread a wave's reads over the LDS banks.  Operands
+// whose contraction axis is the slow axis in memory (W in the forward, X and
+// dY in dW) are loaded as 8x8 blocks and transposed in registers on the way
+// into LDS.  The MFMA is v_mfma_f32_32x32x16_bf16 with the operands swapped
+// (the weight-side tile as the first operand) so that each lane ends with
+// four consecutive output columns of one row: one 8-byte store per group.
+#include "qalg_internal.h"
+
+namespace qalg {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
+  static constexpr int THREADS = 64 * WGM * WGN;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
+  static constexpr int FM = WTM / 32, FN = WTN / 32;    // 32x32 MFMA tiles per wave
+  static constexpr int KCH = BK / 8;                    // 16-byte chunks per LDS row
+  static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+  static_assert(BK == 32 || BK == 64 || BK == 128, "BK");
+  static constexpr int A_CHUNKS = BM * KCH;             // 16-byte chunks of a K-major A tile
+  static constexpr int B_CHUNKS = BN * KCH;
+  static constexpr int A_BLOCKS = (BM / 8) * KCH;       // 8x8 blocks of an MN-major tile
+  static constexpr int B_BLOCKS = (BN / 8) * KCH;
+  static constexpr int STAGE = (BM + BN) * BK;          // bf16 elements per LDS stage
+};
+
+struct Args {
+  const uint16_t* A;
+  const uint16_t* B;
+  uint16_t* C;
+  const int32_t* ws;
+  int64_t ws_stride;                 // int32 elements between problems' indices
+  int64_t strideA, strideB, strideC; // elements between problems' operands
+  int64_t off_offsets, off_tiles, off_rows;
+  int q, M, K, N, s, r;
+  int ct_per_group;                  // column tiles per output group
+  int n_ct;                          // all column tiles (q * ct_per_group)
+  int tm_dw, tn_dw;                  // dW: tiles per block along rows / columns
+};
+
+__device__ __forceinline__ int swz(int row, int chunk, int kch) {
+  return chunk ^ (((row & 7) ^ ((row >> 3) & 1)) & (kch - 1));
+}
+
+// 8x8 transpose of 16-bit elements held as 8 rows of 4 dwords: out[c] holds
+// column c of the input as 8 elements (pairs of consecutive rows per dword).
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int d = c >> 1;
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned lo = in[2 * e][d], hi = in[2 * e + 1][d];
+      o[e] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    out[c] = o;
+  }
+}
+
+__device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {
+  const bf16x2 lo = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  const bf16x2 hi = __builtin_convertvector((f32x2){c, d}, bf16x2);
+  return (u32x2){__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+}
+
+// Position of a row tile among the per-type row tiles: largest i with tile_off[i] <= rt.
+__device__ __forceinline__ int find_type(const int32_t* tile_off, int q, int rt) {
+  int lo = 0, hi = q;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tile_off[mid] <= rt)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+template <Op OP, class C>
+__global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, KCH = C::KCH, T = C::THREADS;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
+
+  const int e = blockIdx.y;
+  const int32_t* ws = a.ws + int64_t(e) * a.ws_stride;
+  const uint16_t* Ag = a.A + int64_t(e) * a.strideA;
+  const uint16_t* Bg = a.B + int64_t(e) * a.strideB;
+  uint16_t* Cg = a.C + int64_t(e) * a.strideC;
+  const int32_t* offsets = ws + a.off_offsets;
+  const int32_t* rows = ws + a.off_rows;
+  const int q = a.q;
+
+  // an index of another (q, M) is never trusted: no row id is read from it
+  if (ws[1] != kIndexMagic || ws[2] != q || ws[3] != a.M) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / C::WGN, wn = wid % C::WGN;
+
+  // ---------------- tile decode ----------------
+  int out_first;        // fwd/dx: first slot in `rows`;  dw: first output row
+  int m_cnt;            // valid output rows in the tile
+  int n0, n_cnt;        // output columns [n0, n0 + n_cnt)
+  int nseg, seg_len;    // contraction: nseg segments of seg_len each
+  int segA0 = 0, segA1 = 0, segB0 = 0, segB1 = 0;
+  const int32_t* krows = nullptr;  // dw: contraction rows
+
+  if constexpr (OP == Op::Dw) {
+    const int per_block = a.tm_dw * a.tn_dw;
+    const int bid = blockIdx.x / per_block;
+    const int t = blockIdx.x - bid * per_block;
+    int b, j;
+    if (bid < q) {
+      b = j = bid;                         // diagonal blocks first: longest contraction
+    } else {
+      const int x = bid - q;
+      b = x / (q - 1);
+      const int jj = x - b * (q - 1);
+      j = jj < b ? jj : jj + 1;
+    }
+    const int rm = t / a.tn_dw, rn = t - rm * a.tn_dw;
+    out_first = b * a.s + rm * BM;
+    m_cnt = min(BM, a.s - rm * BM);
+    n0 = j * a.r + rn * BN;
+    n_cnt = min(BN, a.r - rn * BN);
+    const int k_first = (b == j) ? 0 : offsets[b];
+    const int k_last = (b == j) ? offsets[q] : offsets[b + 1];
+    krows = rows + k_first;
+    nseg = 1;
+    seg_len = k_last - k_first;
+    segA0 = b * a.s + rm * BM;  // X column of output row 0
+    segB0 = n0;                 // dY column of output column 0
+  } else {
+    const int32_t* tile_off = ws + a.off_tiles + tile_height_slot(BM) * (q + 1);
+    const int rt = blockIdx.x / a.n_ct;
+    const int ct = blockIdx.x - rt * a.n_ct;
+    if (rt >= tile_off[q]) return;
+    const int i = find_type(tile_off, q, rt);
+    out_first = offsets[i] + (rt - tile_off[i]) * BM;
+    m_cnt = min(BM, offsets[i + 1] - out_first);
+    const int j = ct / a.ct_per_group, cc = ct - j * a.ct_per_group;
+    const int gw = (OP == Op::Fwd) ? a.r : a.s;
+    n0 = j * gw + cc * BN;
+    n_cnt = min(BN, gw - cc * BN);
+    if constexpr (OP == Op::Fwd) {
+      seg_len = a.s;
+      nseg = (j == i) ? 1 : 2;
+      segA0 = segB0 = i * a.s;   // X columns / W rows of group i
+      segA1 = segB1 = j * a.s;   // X columns / W rows of group j
+    } else {
+      nseg = 1;
+      seg_len = (j == i) ? a.N : a.r;
+      segA0 = (j == i) ? 0 : j * a.r;  // dY columns (= W columns) of the contraction
+    }
+  }
+  const int kts = (seg_len + BK - 1) / BK;  // k-steps per segment
+  const int nk = nseg * kts;
+
+  // ---------------- loaders ----------------
+  // A tile: BM output rows x BK contraction; B tile: BN output columns x BK.
+  constexpr bool A_KMAJOR = (OP != Op::Dw);
+  constexpr bool B_KMAJOR = (OP == Op::Dx);
+  constexpr int A_PER = A_KMAJOR ? (C::A_CHUNKS + T - 1) / T : (C::A_BLOCKS + T - 1) / T;
+  constexpr int B_PER = B_KMAJOR ? (C::B_CHUNKS + T - 1) / T : (C::B_BLOCKS + T - 1) / T;
+  constexpr int A_REGS = A_KMAJOR ? 1 : 8;
+  constexpr int B_REGS = B_KMAJOR ? 1 : 8;
+
+  const uint16_t* a_ptr[A_PER];  // K-major: row base (contraction offset added per step)
+  int a_kc[A_PER];               // K-major: chunk; MN-major: block's k-chunk
+  int a_mn[A_PER];               // K-major: local row; MN-major: local first column (x8)
+  bool a_on[A_PER];
+  const uint16_t* b_ptr[B_PER];
+  int b_kc[B_PER];
+  int b_mn[B_PER];
+  bool b_on[B_PER];
+
+#pragma unroll
+  for (int u = 0; u < A_PER; ++u) {
+    const int c = tid + u * T;
+    if constexpr (A_KMAJOR) {
+      a_on[u] = c < C::A_CHUNKS;
+      const int rl = c / KCH, kc = c % KCH;
+      a_mn[u] = rl;
+      a_kc[u] = kc;
+      const int slot = out_first + min(rl, m_cnt - 1);
+      const int grow = rows[slot];
+      const int64_t ld = (OP == Op::Fwd) ? a.K : a.N;
+      a_ptr[u] = Ag + int64_t(grow) * ld;  // + segment column + k offset per step
+    } else {
+      a_on[u] = c < C::A_BLOCKS;
+      const int kb = c % KCH, mb = c / KCH;
+      a_kc[u] = kb;
+      a_mn[u] = mb * 8;
+      a_ptr[u] = Ag + segA0 + mb * 8;  // row offset added per step (gathered)
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < B_PER; ++u) {
+    const int c = tid + u * T;
+    if constexpr (B_KMAJOR) {
+      b_on[u] = c < C::B_CHUNKS;
+      const int nl = c / KCH, kc = c % KCH;
+      b_mn[u] = nl;
+      b_kc[u] = kc;
+      b_ptr[u] = Bg + int64_t(n0 + min(nl, n_cnt - 1)) * a.N;  // W row = dX column
+    } else {
+      b_on[u] = c < C::B_BLOCKS;
+      const int kb = c % KCH, nb = c / KCH;
+      b_kc[u] = kb;
+      b_mn[u] = nb * 8;
+      b_ptr[u] = Bg + n0 + nb * 8;
+    }
+  }
+
+  u32x4 ra[A_PER][A_REGS];
+  u32x4 rb[B_PER][B_REGS];
+
+  auto load_step = [&](int kt) {
+    const int sg = kt >= kts ? 1 : 0;
+    const int k0 = (kt - sg * kts) * BK;  // offset inside the segment
+#pragma unroll
+    for (int u = 0; u < A_PER; ++u) {
+      if constexpr (A_KMAJOR) {
+        const int kk = k0 + a_kc[u] * 8;
+        const int col = (sg ? segA1 : segA0) + kk;
+        if (a_on[u] && kk < seg_len)
+          ra[u][0] = *reinterpret_cast<const u32x4*>(a_ptr[u] + col);
+        else
+          ra[u][0] = (u32x4){0u, 0u, 0u, 0u};
+      } else {  // dW: 8 gathered contraction rows x 8 output rows
+        const int kk = k0 + a_kc[u] * 8;
+        const bool on = a_on[u] && a_mn[u] < m_cnt;
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          if (on && kk + rr < seg_len) {
+            const int grow = krows[kk + rr];
+            ra[u][rr] = *reinterpret_cast<const u32x4*>(a_ptr[u] + int64_t(grow) * a.K);
+          } else {
+            ra[u][rr] = (u32x4){0u, 0u, 0u, 0u};
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < B_PER; ++u) {
+      if constexpr (B_KMAJOR) {  // dX: W row (output column), contraction along W's columns
+        const int kk = k0 + b_kc[u] * 8;
+        if (b_on[u] && kk < seg_len)
+          rb[u][0] = *reinterpret_cast<const u32x4*>(b_ptr[u] + segA0 + kk);
+        else
+          rb[u][0] = (u32x4){0u, 0u, 0u, 0u};
+      } else if constexpr (OP == Op::Fwd) {  // W rows of the segment, 8 output columns
+        const int kk = k0 + b_kc[u] * 8;
+        const int wrow = (sg ? segB1 : segB0) + kk;
+        const bool on = b_on[u] && b_mn[u] < n_cnt;
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          if (on && kk + rr < seg_len)
+            rb[u][rr] = *reinterpret_cast<const u32x4*>(b_ptr[u] + int64_t(wrow + rr) * a.N);
+          else
+            rb[u][rr] = (u32x4){0u, 0u, 0u, 0u};
+        }
+      } else {  // dW: dY rows gathered, 8 output columns
+        const int kk = k0 + b_kc[u] * 8;
+        const bool on = b_on[u] && b_mn[u] < n_cnt;
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          if (on && kk + rr < seg_len) {
+            const int grow = krows[kk + rr];
+            rb[u][rr] = *reinterpret_cast<const u32x4*>(b_ptr[u] + int64_t(grow) * a.N);
+          } else {
+            rb[u][rr] = (u32x4){0u, 0u, 0u, 0u};
+          }
+        }
+      }
+    }
+  };
+
+  auto store_step = [&](int stage) {
+    uint16_t* As = smem + stage * C::STAGE;
+    uint16_t* Bs = As + BM * BK;
+#pragma unroll
+    for (int u = 0; u < A_PER; ++u) {
+      if (!a_on[u]) continue;
+      if constexpr (A_KMAJOR) {
+        const int rl = a_mn[u];
+        *reinterpret_cast<u32x4*>(As + rl * BK + swz(rl, a_kc[u], KCH) * 8) = ra[u][0];
+      } else {
+        u32x4 t8[8];
+        transpose8x8(ra[u], t8);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int rl = a_mn[u] + c;
+          *reinterpret_cast<u32x4*>(As + rl * BK + swz(rl, a_kc[u], KCH) * 8) = t8[c];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < B_PER; ++u) {
+      if (!b_on[u]) continue;
+      if constexpr (B_KMAJOR) {
+        const int nl = b_mn[u];
+        *reinterpret_cast<u32x4*>(Bs + nl * BK + swz(nl, b_kc[u], KCH) * 8) = rb[u][0];
+      } else {
+        u32x4 t8[8];
+        transpose8x8(rb[u], t8);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int nl = b_mn[u] + c;
+          *reinterpret_cast<u32x4*>(Bs + nl * BK + swz(nl, b_kc[u], KCH) * 8) = t8[c];
+        }
+      }
+    }
+  };
+
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = (f32x16){};
+
+  const int l32 = lane & 31, lhi = lane >> 5;
+  auto compute_step = [&](int stage) {
+    const uint16_t* As = smem + stage * C::STAGE;
+    const uint16_t* Bs = As + BM * BK;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int ch = ks * 2 + lhi;
+      bf16x8 af[C::FM], bfr[C::FN];
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) {
+        const int rl = wm * C::WTM + fm * 32 + l32;
+        af[fm] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(As + rl * BK + swz(rl, ch, KCH) * 8));
+      }
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const int nl = wn * C::WTN + fn * 32 + l32;
+        bfr[fn] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Bs + nl * BK + swz(nl, ch, KCH) * 8));
+      }
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fn], af[fm], acc[fm][fn], 0, 0, 0);
+    }
+  };
+
+  // ---------------- main loop ----------------
+  if (nk > 0) {
+    load_step(0);
+    store_step(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool more = kt + 1 < nk;
+      if (more) load_step(kt + 1);
+      compute_step(kt & 1);
+      if (more) store_step((kt + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  // ---------------- epilogue: one RNE rounding per output ----------------
+  const int64_t ldc = (OP == Op::Fwd) ? a.N : (OP == Op::Dx ? a.K : a.N);
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) {
+    const int ml = wm * C::WTM + fm * 32 + l32;
+    if (ml >= m_cnt) continue;
+    int64_t grow;
+    if constexpr (OP == Op::Dw)
+      grow = out_first + ml;
+    else
+      grow = rows[out_first + ml];
+    uint16_t* crow = Cg + grow * ldc + n0;
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int nl = wn * C::WTN + fn * 32 + g * 8 + lhi * 4;
+        if (nl < n_cnt) {
+          const f32x16& v = acc[fm][fn];
+          *reinterpret_cast<u32x2*>(crow + nl) = pack4_bf16(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: the same tiles and segments, scalar FMA, 64x64 tiles.
+// ---------------------------------------------------------------------------
+constexpr int F_BM = 64, F_BN = 64, F_BK = 16, F_T = 256;
+
+template <Op OP>
+__global__ __launch_bounds__(F_T) void tiled_f32_kernel(Args a, const float* A32, const float* B32, float* C32) {
+  __shared__ float As[F_BK][F_BM + 4];
+  __shared__ float Bs[F_BK][F_BN + 4];
+  const int e = blockIdx.y;
+  const int32_t* ws = a.ws + int64_t(e) * a.ws_stride;
+  const float* Ag = A32 + int64_t(e) * a.strideA;
+  const float* Bg = B32 + int64_t(e) * a.strideB;
+  float* Cg = C32 + int64_t(e) * a.strideC;
+  const int32_t* offsets = ws + a.off_offsets;
+  const int32_t* rows = ws + a.off_rows;
+  const int q = a.q;
+  const int tid = threadIdx.x;
+  if (ws[1] != kIndexMagic || ws[2] != q || ws[3] != a.M) return;
+
+  int out_first, m_cnt, n0, n_cnt, nseg, seg_len;
+  int segA0 = 0, segA1 = 0, segB0 = 0, segB1 = 0;
+  const int32_t* krows = nullptr;
+  if constexpr (OP == Op::Dw) {
+    const int per_block = a.tm_dw * a.tn_dw;
+    const int bid = blockIdx.x / per_block;
+    const int t = blockIdx.x - bid * per_block;
+    int b, j;
+    if (bid < q) {
+      b = j = bid;
+    } else {
+      const int x = bid - q;
+      b = x / (q - 1);
+      const int jj = x - b * (q - 1);
+      j = jj < b ? jj : jj + 1;
+    }
+    const int rm = t / a.tn_dw, rn = t - rm * a.tn_dw;
+    out_first = b * a.s + rm * F_BM;
+    m_cnt = min(F_BM, a.s - rm * F_BM);
+    n0 = j * a.r + rn * F_BN;
+    n_cnt = min(F_BN, a.r - rn * F_BN);
+    const int k_first = (b == j) ? 0 : offsets[b];
+    const int k_last = (b == j) ? offsets[q] : offsets[b + 1];
+    krows = rows + k_first;
+    nseg = 1;
+    seg_len = k_last - k_first;
+  } else {
+    const int32_t* tile_off = ws + a.off_tiles + tile_height_slot(F_BM) * (q + 1);
+    const int rt = blockIdx.x / a.n_ct;
+    const int ct = blockIdx.x - rt * a.n_ct;
+    if (rt >= tile_off[q]) return;
+    const int i = find_type(tile_off, q, rt);
+    out_first = offsets[i] + (rt - tile_off[i]) * F_BM;
+    m_cnt = min(F_BM, offsets[i + 1] - out_first);
+    const int j = ct / a.ct_per_group, cc = ct - j * a.ct_per_group;
+    const int gw = (OP == Op::Fwd) ? a.r : a.s;
+    n0 = j * gw + cc * F_BN;
+    n_cnt = min(F_BN, gw - cc * F_BN);
+    if constexpr (OP == Op::Fwd) {
+      seg_len = a.s;
+      nseg = (j == i) ? 1 : 2;
+      segA0 = segB0 = i * a.s;
+      segA1 = segB1 = j * a.s;
+    } else {
+      nseg = 1;
+      seg_len = (j == i) ? a.N : a.r;
+      segA0 = (j == i) ? 0 : j * a.r;
+    }
+  }
+
+  const int tx = tid % 16, ty = tid / 16;  // thread owns rows ty*4.., columns tx*4..
+  float acc[4][4] = {};
+  for (int sg = 0; sg < nseg; ++sg) {
+    for (int k0 = 0; k0 < seg_len; k0 += F_BK) {
+      // A tile element (m, k): 64 x 16 = 1024 values, 4 per thread
+      for (int x = tid; x < F_BM * F_BK; x += F_T) {
+        int ml, kk;
+        if constexpr (OP == Op::Dw) { ml = x % F_BM; kk = x / F_BM; } else { kk = x % F_BK; ml = x / F_BK; }
+        const int k = k0 + kk;
+        float v = 0.f;
+        if (ml < m_cnt && k < seg_len) {
+          if constexpr (OP == Op::Fwd) v = Ag[int64_t(rows[out_first + ml]) * a.K + (sg ? segA1 : segA0) + k];
+          else if constexpr (OP == Op::Dx) v = Ag[int64_t(rows[out_first + ml]) * a.N + segA0 + k];
+          else v = Ag[int64_t(krows[k]) * a.K + out_first + ml];
+        }
+        As[kk][ml] = v;
+      }
+      for (int x = tid; x < F_BN * F_BK; x += F_T) {
+        int nl, kk;
+        if constexpr (OP == Op::Dx) { kk = x % F_BK; nl = x / F_BK; } else { nl = x % F_BN; kk = x / F_BN; }
+        const int k = k0 + kk;
+        float v = 0.f;
+        if (nl < n_cnt && k < seg_len) {
+          if constexpr (OP == Op::Fwd) v = Bg[int64_t((sg ? segB1 : segB0) + k) * a.N + n0 + nl];
+          else if constexpr (OP == Op::Dx) v = Bg[int64_t(n0 + nl) * a.N + segA0 + k];
+          else v = Bg[int64_t(krows[k]) * a.N + n0 + nl];
+        }
+        Bs[kk][nl] = v;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < F_BK; ++kk) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { av[u] = As[kk][ty * 4 + u]; bv[u] = Bs[kk][tx * 4 + u]; }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
+      }
+      __syncthreads();
+    }
+  }
+  const int64_t ldc = (OP == Op::Dx) ? a.K : a.N;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int ml = ty * 4 + u;
+    if (ml >= m_cnt) continue;
+    const int64_t grow = (OP == Op::Dw) ? int64_t(out_first + ml) : int64_t(rows[out_first + ml]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int nl = tx * 4 + v;
+      if (nl < n_cnt) Cg[grow * ldc + n0 + nl] = acc[u][v];
+    }
+  }
+}
+
+inline int cdiv(int64_t a, int64_t b) { return int((a + b - 1) / b); }
+
+Args make_args(const ProblemDesc& p, int bm, int bn) {
+  Args a{};
+  a.A = static_cast<const uint16_t*>(p.A);
+  a.B = static_cast<const uint16_t*>(p.B);
+  a.C = static_cast<uint16_t*>(p.C);
+  a.ws = p.ws;
+  a.ws_stride = p.ws_stride;
+  a.q = p.q;
+  a.M = int(p.M);
+  a.K = int(p.K);
+  a.N = int(p.N);
+  a.s = int(p.K / p.q);
+  a.r = int(p.N / p.q);
+  const WsLayout L = ws_layout(p.q, p.M);
+  a.off_offsets = L.offsets;
+  a.off_tiles = L.tile_off;
+  a.off_rows = L.rows;
+  if (p.op == Op::Fwd) {
+    a.strideA = p.M * p.K; a.strideB = p.K * p.N; a.strideC = p.M * p.N;
+    a.ct_per_group = cdiv(a.r, bn);
+  } else if (p.op == Op::Dx) {
+    a.strideA = p.M * p.N; a.strideB = p.K * p.N; a.strideC = p.M * p.K;
+    a.ct_per_group = cdiv(a.s, bn);
+  } else {
+    a.strideA = p.M * p.K; a.strideB = p.M * p.N; a.strideC = p.K * p.N;
+    a.ct_per_group = 0;
+    a.tm_dw = cdiv(a.s, bm);
+    a.tn_dw = cdiv(a.r, bn);
+  }
+  a.n_ct = p.q * a.ct_per_group;
+  return a;
+}
+
+dim3 grid_for(const ProblemDesc& p, const Args& a, int bm) {
+  if (p.op == Op::Dw) return dim3(unsigned(p.q * p.q * a.tm_dw * a.tn_dw), unsigned(p.E));
+  // worst case over all type splits: sum_i ceil(M_i / BM) <= ceil(M / BM) + q - 1
+  const int64_t rt = (p.M + bm - 1) / bm + p.q - 1;
+  return dim3(unsigned(rt * a.n_ct), unsigned(p.E));
+}
+
+template <Op OP, class C>
+hipError_t launch_cfg(const ProblemDesc& p, hipStream_t s) {
+  const Args a = make_args(p, C::BM, C::BN);
+  const dim3 g = grid_for(p, a, C::BM);
+  if (g.x == 0) return hipSuccess;
+  hipLaunchKernelGGL((tiled_bf16_kernel<OP, C>), g, dim3(C::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+using Cfg128 = TileCfg<128, 128, 64, 2, 2>;
+using Cfg64 = TileCfg<64, 64, 64, 2, 2>;
+using Cfg32 = TileCfg<32, 64, 64, 1, 2>;
+
+}  // namespace
+
+hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s) {
+  // Row-tile height from the rows per type (tiles never straddle types).
+  const int64_t per_type = p.op == Op::Dw ? p.K / p.q : (p.M + p.q - 1) / p.q;
+  switch (p.op) {
+    case Op::Fwd:
+      if (per_type >= 128) return launch_cfg<Op::Fwd, Cfg128>(p, s);
+      if (per_type >= 48) return launch_cfg<Op::Fwd, Cfg64>(p, s);
+      return launch_cfg<Op::Fwd, Cfg32>(p, s);
+    case Op::Dx:
+      if (per_type >= 128) return launch_cfg<Op::Dx, Cfg128>(p, s);
+      if (per_type >= 48) return launch_cfg<Op::Dx, Cfg64>(p, s);
+      return launch_cfg<Op::Dx, Cfg32>(p, s);
+    case Op::Dw:
+      if (per_type >= 128) return launch_cfg<Op::Dw, Cfg128>(p, s);
+      return launch_cfg<Op::Dw, Cfg64>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_tiled_f32(const ProblemDesc& p, hipStream_t s) {
+  const Args a = make_args(p, F_BM, F_BN);
+  const dim3 g = grid_for(p, a, F_BM);
+  if (g.x == 0) return hipSuccess;
+  const float* A = static_cast<const float*>(p.A);
+  const float* B = static_cast<const float*>(p.B);
+  float* Cp = static_cast<float*>(p.C);
+  switch (p.op) {
+    case Op::Fwd: hipLaunchKernelGGL((tiled_f32_kernel<Op::Fwd>), g, dim3(F_T), 0, s, a, A, B, Cp); break;
+    case Op::Dx: hipLaunchKernelGGL((tiled_f32_kernel<Op::Dx>), g, dim3(F_T), 0, s, a, A, B, Cp); break;
+    case Op::Dw: hipLaunchKernelGGL((tiled_f32_kernel<Op::Dw>), g, dim3(F_T), 0, s, a, A, B, Cp); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qalg

@@ -1,0 +1,206 @@
+/*
+ * libqalg: the row-typed associative-algebra projection Y = X *_{Q_q} W on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Source: arXiv 2609.32814, "Change the Product, Keep the Parameters:
+ * Associative Algebra Layers for Transformers".
+ *
+ * The operation (section 4, eq 16-17; section 6.1, eq 27 and Algorithm 1):
+ * X is M x K, W is K x N, both split into q equal feature groups (widths
+ * s = K/q and r = N/q; group g_j of X's columns / W's rows is
+ * [j*s, (j+1)*s), group g_j of W's and Y's columns is [j*r, (j+1)*r)).
+ * Token row m has type i = tau[m] in [0, q) and computes
+ *     y_i = x_i W_ii,      y_j = x_i W_ij + x_j W_jj   (j != i),
+ * i.e. one row of the Q_q interaction table: 2q-1 of the q^2 weight blocks,
+ * a fraction (2q-1)/q^2 of dense arithmetic (eq 21, eq 24).  The
+ * gradients are appendix B's vector-Jacobian products (eq 31-35).
+ *
+ * Conventions shared by every entry point below:
+ *  - Layout: row-major and packed.  X, dX: M x K (leading dimension K);
+ *    W, dW: K x N (leading dimension N); Y, dY: M x N (leading dimension N).
+ *    The weight bank is used exactly as stored (no repacking).  Batched
+ *    entry points take E such problems packed back to back.
+ *  - Element type (`dtype`): QALG_BF16 (bf16 in, bf16 out, fp32
+ *    accumulation, one round-to-nearest-even rounding of each output) or
+ *    QALG_F32 (fp32 throughout).
+ *  - tau: device int32[M], types in [0, q).  A row whose type lies outside
+ *    [0, q) belongs to no type: its Y / dX row is written as zero, it adds
+ *    nothing to dW, and it is counted (see qalg_read_status).
+ *  - Ownership: every pointer is device memory owned by the caller (for
+ *    example allocated by PyTorch).  The library allocates nothing, keeps no
+ *    pointer after a call returns, and holds no state: calls are reentrant,
+ *    but concurrent calls need separate workspaces.
+ *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    default stream) and the call returns without waiting.  Buffers must
+ *    stay valid until the stream has run the work.
+ *  - Workspace: `ws` is caller-owned device memory of at least
+ *    qalg_workspace_bytes(q, M) (per problem; batched: E times that), 256-byte
+ *    aligned.  It receives the type index of the call.
+ *  - Errors are returned synchronously, before anything is enqueued, for:
+ *    a NULL pointer that is needed (QALG_ERR_NULL), M < 0 or K, N <= 0 or a
+ *    size above the int32 index range (QALG_ERR_DIM), q < 1, q > QALG_MAX_Q
+ *    or q not dividing K and N (QALG_ERR_Q), a base pointer not 16-byte
+ *    aligned or (bf16) a group width not a multiple of 8 elements
+ *    (QALG_ERR_ALIGN), an unknown dtype (QALG_ERR_DTYPE), a workspace that
+ *    is too small or misaligned (QALG_ERR_WORKSPACE), an unknown flag or
+ *    schedule kind (QALG_ERR_ARG).  A failed launch returns QALG_ERR_HIP.
+ *    M = 0 returns QALG_OK and enqueues nothing, except that qalg_backward_dw
+ *    then zero-fills dW (only dW must be non-NULL in that case).
+ */
+#ifndef QALG_H
+#define QALG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QALG_VERSION 1
+#define QALG_MAX_Q 512
+
+typedef enum qalg_status {
+    QALG_OK = 0,
+    QALG_ERR_NULL = 1,
+    QALG_ERR_DIM = 2,
+    QALG_ERR_Q = 3,
+    QALG_ERR_ALIGN = 4,
+    QALG_ERR_DTYPE = 5,
+    QALG_ERR_WORKSPACE = 6,
+    QALG_ERR_HIP = 7,
+    QALG_ERR_ARG = 8
+} qalg_status;
+
+typedef enum qalg_dtype {
+    QALG_F32 = 0,
+    QALG_BF16 = 1
+} qalg_dtype;
+
+/* Flags for the projection entry points (bitwise or). */
+enum {
+    /* The workspace already holds the index of this (tau, q, M), written by
+     * qalg_build_index or by an earlier call on the same stream: skip
+     * rebuilding it.  Lets forward, dX and dW of one step share one index. */
+    QALG_FLAG_INDEX_READY = 1,
+    /* Force the tiled matrix-core path even for small M (testing). */
+    QALG_FLAG_FORCE_TILED = 2,
+    /* Force the small-M weight-streaming path (bf16 forward only; testing). */
+    QALG_FLAG_FORCE_SMALL_M = 4
+};
+
+/* Position-type schedules for qalg_type_schedule. */
+typedef enum qalg_schedule {
+    /* tau(p) = p mod q: section 4's cyclic schedule 1 + ((p-1) mod q) in 0-based form. */
+    QALG_SCHEDULE_CYCLIC = 0,
+    /* tau(p) = floor((p mod period) / (period / q)): appendix D.5's interval
+     * schedule, floor((p mod 768) / 192) for the pilot (period 768, q 4). */
+    QALG_SCHEDULE_INTERVAL = 1
+} qalg_schedule;
+
+/* Human-readable name of a status code (static string; never NULL). */
+const char* qalg_status_string(int status);
+
+/* Library version (QALG_VERSION of the build). */
+int qalg_version(void);
+
+/* Bytes of workspace one problem with q types and M rows needs (0 on bad
+ * arguments).  Batched calls need E times this. */
+size_t qalg_workspace_bytes(int32_t q, int64_t M);
+
+/*
+ * Type schedule (section 4: a token at position p selects row i = tau(p) by a
+ * fixed deterministic schedule; appendix D.5 for the interval form).
+ * positions: device int64[M], each >= 0 (a negative position yields type -1,
+ * which the projections treat as "no type").  tau: device int32[M], written.
+ * kind: a qalg_schedule; period is used by QALG_SCHEDULE_INTERVAL only and
+ * must be a positive multiple of q.
+ */
+qalg_status qalg_type_schedule(const int64_t* positions, int64_t M, int32_t q,
+                               int32_t kind, int64_t period, int32_t* tau,
+                               void* stream);
+
+/*
+ * Type index (Algorithm 1: I_i = {b : tau(p_b) = i}).  Reads tau (device
+ * int32[M]) and writes into ws the per-type row counts, their running
+ * offsets, the rows of each type in ascending order (type 0 first, rows with
+ * an out-of-range type last), the row-tile prefix sums the tiled kernels use
+ * and the count of out-of-range rows.  No sort: one counting pass and one
+ * stable scatter.  The projection entry points call this themselves unless
+ * QALG_FLAG_INDEX_READY is set.  Its layout is exposed for tests through
+ * qalg_index_layout.
+ */
+qalg_status qalg_build_index(const int32_t* tau, int32_t q, int64_t M,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Same, for E problems whose tau arrays are packed back to back (tau: E x M)
+ * into E workspaces of qalg_workspace_bytes(q, M) bytes each. */
+qalg_status qalg_build_index_batched(int32_t E, const int32_t* tau, int32_t q, int64_t M,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+/* Offsets, in int32 elements from the start of one problem's workspace, of the
+ * index arrays: [0] = out-of-range row count (1 int32), [1] = counts (q),
+ * [2] = offsets (q+1), [3] = rows (M).  Returns QALG_ERR_Q / QALG_ERR_DIM on bad
+ * arguments.  (Test hook: the index is internal data otherwise.) */
+qalg_status qalg_index_layout(int32_t q, int64_t M, int64_t out_offsets[4]);
+
+/*
+ * Forward projection Y = X *_{Q_q} W (eq 16-17, Algorithm 1).
+ * X: M x K, W: K x N, Y: M x N (overwritten; Algorithm 1 starts from Y = 0).
+ * Each output tile accumulates both endpoint products x_i W_ij and x_j W_jj
+ * in fp32 before its single rounded store (section 5.3's fused schedule).
+ * Small M (bf16) uses a weight-streaming kernel that reads each needed
+ * weight block once (section 5.2: decode needs a matrix-vector kernel).
+ */
+qalg_status qalg_forward(const void* X, const void* W, const int32_t* tau, int32_t q,
+                         int64_t M, int64_t K, int64_t N, void* Y,
+                         int32_t dtype, void* ws, size_t ws_bytes,
+                         uint32_t flags, void* stream);
+
+/*
+ * Activation gradient (appendix B, eq 31-32): for a row of type i,
+ *   dx_i = sum_j dy_j W_ij^T  and  dx_j = dy_j W_jj^T  (j != i).
+ * dY: M x N, W: K x N, dX: M x K (overwritten).
+ */
+qalg_status qalg_backward_dx(const void* dY, const void* W, const int32_t* tau, int32_t q,
+                             int64_t M, int64_t K, int64_t N, void* dX,
+                             int32_t dtype, void* ws, size_t ws_bytes,
+                             uint32_t flags, void* stream);
+
+/*
+ * Weight gradient (appendix B, eq 33-35), summed over all rows:
+ *   dW_jj = sum over every row of x_j^T dy_j,
+ *   dW_ij = sum over the rows of type i of x_i^T dy_j   (i != j).
+ * X: M x K, dY: M x N, dW: K x N (overwritten; a block no row reaches is
+ * written as zero).  Each dW element has one owner; the result does not
+ * depend on scheduling (bitwise reproducible).
+ */
+qalg_status qalg_backward_dw(const void* X, const void* dY, const int32_t* tau, int32_t q,
+                             int64_t M, int64_t K, int64_t N, void* dW,
+                             int32_t dtype, void* ws, size_t ws_bytes,
+                             uint32_t flags, void* stream);
+
+/*
+ * E independent forward projections, one weight bank each (the per-expert
+ * projections of a mixture-of-experts layer, section 7.1: an expert's M counts
+ * the tokens routed to it).  X: E x M x K, W: E x K x N, tau: E x M,
+ * Y: E x M x N, all packed; ws: E x qalg_workspace_bytes(q, M).
+ */
+qalg_status qalg_forward_batched(int32_t E, const void* X, const void* W, const int32_t* tau,
+                                 int32_t q, int64_t M, int64_t K, int64_t N, void* Y,
+                                 int32_t dtype, void* ws, size_t ws_bytes,
+                                 uint32_t flags, void* stream);
+
+/*
+ * Number of rows with an out-of-range type seen by the last index build in
+ * ws (summed over the E problems of a batched workspace; E = 1 otherwise).
+ * Synchronises `stream`.
+ */
+qalg_status qalg_read_status(const void* ws, int32_t E, int32_t q, int64_t M,
+                             void* stream, int64_t* bad_tau_rows);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QALG_H */

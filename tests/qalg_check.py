@@ -1,0 +1,41 @@
+"""Comparison helpers for parity tests: relative Frobenius error per output group.
+
+The bar (per output group, max over groups): 5e-3 for bf16 operands with fp32
+accumulation, 1e-5 for the fp32 path.  A group whose reference is exactly zero
+must be exactly zero.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BF16_TOL = 5e-3
+F32_TOL = 1e-5
+
+
+def _rel(got: np.ndarray, ref: np.ndarray) -> float:
+    den = float(np.linalg.norm(ref))
+    num = float(np.linalg.norm(got - ref))
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return num / den
+
+
+def rel_frob_col_groups(got: np.ndarray, ref: np.ndarray, q: int) -> list[float]:
+    """Per column group j: ||got[:, g_j] - ref[:, g_j]||_F / ||ref[:, g_j]||_F (rows: all)."""
+    assert got.shape == ref.shape
+    w = ref.shape[-1] // q
+    return [_rel(got[..., j * w:(j + 1) * w], ref[..., j * w:(j + 1) * w]) for j in range(q)]
+
+
+def rel_frob_blocks(got: np.ndarray, ref: np.ndarray, q: int) -> list[float]:
+    """Per (b, j) block of a K x N weight-shaped array."""
+    assert got.shape == ref.shape
+    s, r = ref.shape[0] // q, ref.shape[1] // q
+    return [_rel(got[b * s:(b + 1) * s, j * r:(j + 1) * r], ref[b * s:(b + 1) * s, j * r:(j + 1) * r])
+            for b in range(q) for j in range(q)]
+
+
+def assert_groups(errs: list[float], tol: float, what: str) -> float:
+    worst = max(errs) if errs else 0.0
+    assert worst <= tol, f"{what}: max relative Frobenius error {worst:.3e} > {tol:.1e} (per group: {np.round(errs, 6)})"
+    return worst

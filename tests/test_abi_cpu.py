@@ -1,0 +1,121 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+and rejects bad arguments before touching the device (no GPU calls here)."""
+import ctypes
+import pathlib
+import re
+
+import pytest
+
+import gemm_qalg_forward_amd as Q
+
+HEADER = pathlib.Path(__file__).resolve().parents[1] / "include" / "qalg.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qalg_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not Q.lib_path.exists():
+        pytest.skip("libqalg.so not built")
+    return Q.lib()
+
+
+def test_header_declares_the_projection_api():
+    names = declared_functions()
+    for n in ("qalg_forward", "qalg_backward_dx", "qalg_backward_dw", "qalg_build_index",
+              "qalg_type_schedule", "qalg_forward_batched", "qalg_workspace_bytes", "qalg_read_status"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(declared_functions()) == set(Q._SIGS), "binding and header disagree"
+
+
+def test_version_and_status_strings(lib):
+    assert Q.qalg_version() == 1
+    for code in range(9):
+        assert Q.qalg_status_string(code).startswith("QALG_")
+    assert "unknown" in Q.qalg_status_string(99)
+
+
+def test_workspace_layout(lib):
+    for q, M in ((1, 0), (2, 64), (8, 16384), (512, 1000)):
+        n = Q.qalg_workspace_bytes(q, M)
+        assert n % 256 == 0 and n >= 4 * (M + 2 * q)
+        lay = Q.qalg_index_layout(q, M)
+        assert lay[0] == 0 and lay[1] < lay[2] < lay[3] and lay[3] * 4 + 4 * M <= n
+    assert Q.qalg_workspace_bytes(0, 10) == 0
+    assert Q.qalg_workspace_bytes(513, 10) == 0
+    assert Q.qalg_workspace_bytes(4, -1) == 0
+
+
+FAKE = 0x10000  # 16-byte aligned non-null address; never dereferenced on these paths
+
+
+def call_fwd(lib, X=FAKE, W=FAKE, tau=FAKE, q=2, M=64, K=16, N=16, Y=FAKE, dt=1, ws=FAKE,
+             wsb=1 << 20, flags=0, fn="qalg_forward"):
+    return getattr(lib, fn)(X, W, tau, q, M, K, N, Y, dt, ws, wsb, flags, None)
+
+
+@pytest.mark.parametrize("fn", ["qalg_forward", "qalg_backward_dx", "qalg_backward_dw"])
+def test_argument_errors_are_synchronous(lib, fn):
+    assert call_fwd(lib, q=0, fn=fn) == 3
+    assert call_fwd(lib, q=3, fn=fn) == 3            # 3 does not divide 16
+    assert call_fwd(lib, q=513, K=513 * 8, N=513 * 8, fn=fn) == 3
+    assert call_fwd(lib, M=-1, fn=fn) == 2
+    assert call_fwd(lib, K=0, fn=fn) == 2
+    assert call_fwd(lib, N=-4, fn=fn) == 2
+    assert call_fwd(lib, dt=7, fn=fn) == 5
+    assert call_fwd(lib, X=None, fn=fn) == 1
+    assert call_fwd(lib, tau=None, fn=fn) == 1
+    assert call_fwd(lib, Y=None, fn=fn) == 1
+    assert call_fwd(lib, ws=None, fn=fn) == 1
+    assert call_fwd(lib, X=FAKE + 2, fn=fn) == 4     # misaligned operand
+    assert call_fwd(lib, q=4, K=16, N=16, fn=fn) == 4  # bf16 group width 4 < 8
+    assert call_fwd(lib, wsb=16, fn=fn) == 6         # workspace too small
+    assert call_fwd(lib, ws=FAKE + 4, fn=fn) == 6    # workspace misaligned
+    assert call_fwd(lib, flags=64, fn=fn) == 8       # unknown flag
+    assert call_fwd(lib, flags=2 | 4, fn=fn) == 8    # contradictory forced paths
+    if fn != "qalg_forward":
+        assert call_fwd(lib, M=4, flags=4, fn=fn) == 8   # small-M path is forward only
+    else:
+        assert call_fwd(lib, M=64, flags=4, fn=fn) == 8  # forced small-M path needs M <= 8
+        assert call_fwd(lib, M=4, ws=None, fn=fn) == 1   # the workspace is checked on every path
+
+
+def test_zero_rows_forward_is_a_no_op(lib):
+    # M = 0: nothing to compute; no pointer is touched
+    assert call_fwd(lib, M=0, X=None, tau=None, Y=None, ws=None) == 0
+    assert call_fwd(lib, M=0, X=None, tau=None, Y=None, ws=None, fn="qalg_backward_dx") == 0
+    # dW with M = 0 still needs its output (it is zero-filled)
+    assert call_fwd(lib, M=0, X=None, tau=None, Y=None, ws=None, fn="qalg_backward_dw") == 1
+
+
+def test_batched_and_index_errors(lib):
+    assert lib.qalg_forward_batched(0, FAKE, FAKE, FAKE, 2, 4, 16, 16, FAKE, 1, FAKE, 1 << 20, 0, None) == 2
+    assert lib.qalg_build_index(FAKE, 0, 4, FAKE, 1 << 20, None) == 3
+    assert lib.qalg_build_index(None, 2, 4, FAKE, 1 << 20, None) == 1
+    assert lib.qalg_build_index(FAKE, 2, 4, FAKE, 8, None) == 6
+    assert lib.qalg_build_index_batched(0, FAKE, 2, 4, FAKE, 1 << 20, None) == 2
+    assert lib.qalg_type_schedule(FAKE, 4, 2, 9, 0, FAKE, None) == 8
+    assert lib.qalg_type_schedule(FAKE, 4, 4, 1, 6, FAKE, None) == 8   # period not a multiple of q
+    assert lib.qalg_type_schedule(FAKE, -1, 4, 0, 0, FAKE, None) == 2
+    assert lib.qalg_type_schedule(None, 0, 4, 0, 0, None, None) == 0   # M = 0
+    out = (ctypes.c_int64 * 4)()
+    assert lib.qalg_index_layout(0, 4, out) == 3
+    assert lib.qalg_read_status(None, 1, 2, 4, None, None) == 1
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    X = torch.zeros(4, 16, dtype=torch.bfloat16)
+    W = torch.zeros(16, 16, dtype=torch.bfloat16)
+    tau = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        Q.qalg_forward(X, W, tau, 2, Y=torch.empty(4, 16, dtype=torch.bfloat16), ws=torch.empty(4096, dtype=torch.uint8))

@@ -1,0 +1,221 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on seeded inputs.
+
+Sizes here span several tiles and ragged tails and still let the oracle finish
+in seconds; full workload sizes are in test_gpu_workloads.py.
+"""
+import numpy as np
+import pytest
+
+import gemm_qalg_forward_amd as Q
+import synth
+from gpu_common import make_tau, say, tau_dev, to_dev, to_f64, torch_cuda
+from oracle import qalg_oracle as O
+from qalg_check import BF16_TOL, F32_TOL, assert_groups, rel_frob_blocks, rel_frob_col_groups
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    # M, K, N, q, tau kind, offset, bad rows
+    (64, 256, 256, 2, "cyclic", 0, 0),       # the fp32 workload's shape, in bf16
+    (1000, 512, 768, 4, "cyclic", 1, 0),     # r = 192: ragged column tiles
+    (3001, 384, 384, 3, "random", 0, 0),     # odd q, ragged row tiles
+    (777, 192, 320, 8, "random", 0, 13),     # s = 24, r = 40: groups narrower than a tile; bad types
+    (513, 1024, 512, 1, "zeros", 0, 0),      # q = 1: the dense product
+    (300, 128, 128, 16, "cyclic", 5, 0),     # s = r = 8
+    (2048, 256, 512, 4, "random", 0, 0),     # some types with many row tiles
+]
+
+
+def _inputs(M, K, N, dtype, seed):
+    X = synth.normal_operand(seed + 1, (M, K), 1.0, dtype)
+    W = synth.normal_operand(seed + 2, (K, N), K ** -0.5, dtype)
+    dY = synth.normal_operand(seed + 3, (M, N), 1.0, dtype)
+    return X, W, dY
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"M{s[0]}K{s[1]}N{s[2]}q{s[3]}{s[4]}" for s in SHAPES])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forward_dx_dw_match_oracle(shape, dtype):
+    torch = torch_cuda()
+    M, K, N, q, kind, off, bad = shape
+    if dtype == "f32" and (K // q) % 4:
+        pytest.skip("fp32 needs group widths that are multiples of 4")
+    say(f"[parity] {dtype} M={M} K={K} N={N} q={q} tau={kind} offset={off} bad={bad}")
+    X, W, dY = _inputs(M, K, N, dtype, 7000 + M)
+    tau = make_tau(kind, M, q, seed=M, offset=off, bad=bad)
+    Xd, Wd, dYd, td = to_dev(X), to_dev(W), to_dev(dY), tau_dev(tau)
+    ws = Q.workspace(q, M)
+    Y = Q.qalg_forward(Xd, Wd, td, q, ws=ws)
+    dX = Q.qalg_backward_dx(dYd, Wd, td, q, ws=ws, flags=Q.QALG_FLAG_INDEX_READY)
+    dW = Q.qalg_backward_dw(Xd, dYd, td, q, ws=ws, flags=Q.QALG_FLAG_INDEX_READY)
+    torch.cuda.synchronize()
+    assert Q.qalg_read_status(ws, q, M) == bad
+    Yr = O.row_typed_forward(X.f64, W.f64, tau, q)
+    dXr, dWr = O.row_typed_backward(X.f64, W.f64, dY.f64, tau, q)
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    ey = assert_groups(rel_frob_col_groups(to_f64(Y), Yr, q), tol, "Y")
+    ex = assert_groups(rel_frob_col_groups(to_f64(dX), dXr, q), tol, "dX")
+    ew = assert_groups(rel_frob_blocks(to_f64(dW), dWr, q), tol, "dW")
+    say(f"    max rel err  Y {ey:.2e}  dX {ex:.2e}  dW {ew:.2e}")
+    # rows of an out-of-range type are exactly zero in Y and dX
+    badrows = (tau < 0) | (tau >= q)
+    if badrows.any():
+        assert not to_f64(Y)[badrows].any() and not to_f64(dX)[badrows].any()
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("q,K,N", [(4, 512, 768), (8, 256, 768), (2, 1024, 64)])
+def test_small_m_paths_match_oracle(M, q, K, N):
+    """The weight-streaming path and the tiled path at decode sizes, both against the oracle."""
+    torch = torch_cuda()
+    X, W, _ = _inputs(M, K, N, "bf16", 9100 + M)
+    tau = make_tau("random", M, q, seed=M + q)
+    if M >= 3:
+        tau[1] = -5  # one row without a type
+    Xd, Wd, td = to_dev(X), to_dev(W), tau_dev(tau)
+    ws = Q.workspace(q, M)
+    Ys = Q.qalg_forward(Xd, Wd, td, q, ws=ws, flags=Q.QALG_FLAG_FORCE_SMALL_M)
+    Yt = Q.qalg_forward(Xd, Wd, td, q, ws=ws, flags=Q.QALG_FLAG_FORCE_TILED)
+    torch.cuda.synchronize()
+    Yr = O.row_typed_forward(X.f64, W.f64, tau, q)
+    assert_groups(rel_frob_col_groups(to_f64(Ys), Yr, q), BF16_TOL, "Y small-M")
+    assert_groups(rel_frob_col_groups(to_f64(Yt), Yr, q), BF16_TOL, "Y tiled")
+    Ys2 = Q.qalg_forward(Xd, Wd, td, q, ws=ws, flags=Q.QALG_FLAG_FORCE_SMALL_M)
+    torch.cuda.synchronize()
+    assert torch.equal(Ys, Ys2), "small-M path is not bitwise reproducible"
+
+
+@pytest.mark.parametrize("E,M,q,K,N", [(3, 1, 4, 512, 256), (4, 8, 8, 256, 768), (5, 64, 4, 512, 192), (2, 300, 8, 256, 256)])
+def test_batched_experts_match_oracle(E, M, q, K, N):
+    torch = torch_cuda()
+    Xs, Ws, taus = [], [], []
+    for e in range(E):
+        X, W, _ = _inputs(M, K, N, "bf16", 9500 + 10 * e)
+        Xs.append(X)
+        Ws.append(W)
+        taus.append(O.type_schedule(synth.random_positions(9900 + e, M), q))
+    Xd = torch.stack([to_dev(x) for x in Xs])
+    Wd = torch.stack([to_dev(w) for w in Ws])
+    td = tau_dev(np.stack(taus))
+    Y = Q.qalg_forward_batched(Xd, Wd, td, q)
+    torch.cuda.synchronize()
+    Yh = to_f64(Y)
+    for e in range(E):
+        Yr = O.row_typed_forward(Xs[e].f64, Ws[e].f64, taus[e], q)
+        assert_groups(rel_frob_col_groups(Yh[e], Yr, q), BF16_TOL, f"expert {e}")
+
+
+@pytest.mark.parametrize("kind,q,M,period", [("cyclic", 8, 16384, 0), ("cyclic", 3, 1001, 0),
+                                             ("interval", 4, 5000, 768), ("cyclic", 512, 7777, 0)])
+def test_type_schedule_and_index_bit_exact(kind, q, M, period):
+    torch = torch_cuda()
+    pos = synth.random_positions(77 + q, M, 1 << 20) if q % 2 else synth.cyclic_positions(M, 1024, 3)
+    code = Q.QALG_SCHEDULE_CYCLIC if kind == "cyclic" else Q.QALG_SCHEDULE_INTERVAL
+    tau = Q.qalg_type_schedule(torch.from_numpy(pos).to("cuda"), q, code, period)
+    want_tau = O.type_schedule(pos, q, kind, period)
+    np.testing.assert_array_equal(tau.cpu().numpy(), want_tau)
+    ws = Q.qalg_build_index(tau, q)
+    torch.cuda.synchronize()
+    _check_index(ws, want_tau, q)
+
+
+def _check_index(ws, tau, q):
+    M = tau.size
+    counts, offsets, rows, bad = O.type_index(tau, q)
+    lay = Q.qalg_index_layout(q, M)
+    w = ws.view(dtype=torch_cuda().int32).cpu().numpy()
+    assert w[lay[0]] == bad
+    np.testing.assert_array_equal(w[lay[1]:lay[1] + q], counts)
+    np.testing.assert_array_equal(w[lay[2]:lay[2] + q + 1], offsets)
+    np.testing.assert_array_equal(w[lay[3]:lay[3] + offsets[-1]], rows)
+    badrows = np.flatnonzero((tau < 0) | (tau >= q))
+    np.testing.assert_array_equal(w[lay[3] + offsets[-1]:lay[3] + M], badrows)
+
+
+@pytest.mark.parametrize("M,q,kind,bad", [(1, 1, "zeros", 0), (1, 4, "random", 1), (63, 2, "cyclic", 0),
+                                          (64, 4, "cyclic", 0), (65, 4, "random", 3), (4096, 8, "random", 0),
+                                          (20000, 7, "random", 111), (3000, 512, "random", 0)])
+def test_index_edge_cases_bit_exact(M, q, kind, bad):
+    torch = torch_cuda()
+    tau = make_tau(kind, M, q, seed=M, bad=bad)
+    ws = Q.qalg_build_index(tau_dev(tau), q)
+    torch.cuda.synchronize()
+    _check_index(ws, tau, q)
+    assert Q.qalg_read_status(ws, q, M) == bad
+
+
+def test_unit_law_is_bitwise():
+    """A diagonal bank of identity maps is the identity projection (section 4): Y == X exactly."""
+    torch = torch_cuda()
+    for q, K, M in ((4, 256, 1000), (8, 512, 3), (2, 128, 5)):
+        X = synth.normal_operand(11, (M, K), 1.0, "bf16")
+        Xd = to_dev(X)
+        I = torch.eye(K, dtype=torch.bfloat16, device="cuda")
+        tau = tau_dev(make_tau("random", M, q, seed=5))
+        for flags in (Q.QALG_FLAG_FORCE_TILED, 0):
+            Y = Q.qalg_forward(Xd, I, tau, q, flags=flags)
+            torch.cuda.synchronize()
+            assert torch.equal(Y, Xd)
+
+
+def test_block_diagonal_bank_is_type_independent():
+    """With W_ij = 0 off the diagonal every type computes X W: outputs for two schedules agree exactly."""
+    torch = torch_cuda()
+    q, K, N, M = 4, 512, 768, 999
+    X = synth.normal_operand(21, (M, K), 1.0, "bf16")
+    W = synth.normal_operand(22, (K, N), K ** -0.5, "bf16")
+    Wd = to_dev(W)
+    s, r = K // q, N // q
+    mask = torch.zeros(K, N, dtype=torch.bool, device="cuda")
+    for a in range(q):
+        mask[a * s:(a + 1) * s, a * r:(a + 1) * r] = True
+    Wd = torch.where(mask, Wd, torch.zeros_like(Wd))
+    Xd = to_dev(X)
+    Y1 = Q.qalg_forward(Xd, Wd, tau_dev(make_tau("cyclic", M, q)), q)
+    Y2 = Q.qalg_forward(Xd, Wd, tau_dev(make_tau("random", M, q, seed=3)), q)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
+
+
+def test_runs_are_bitwise_reproducible():
+    torch = torch_cuda()
+    q, K, N, M = 8, 1024, 2048, 4096
+    X, W, dY = _inputs(M, K, N, "bf16", 31)
+    Xd, Wd, dYd = to_dev(X), to_dev(W), to_dev(dY)
+    td = tau_dev(make_tau("random", M, q, seed=9))
+    outs = []
+    for _ in range(2):
+        ws = Q.workspace(q, M)
+        outs.append((Q.qalg_forward(Xd, Wd, td, q, ws=ws), Q.qalg_backward_dx(dYd, Wd, td, q, ws=ws),
+                     Q.qalg_backward_dw(Xd, dYd, td, q, ws=ws)))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_zero_rows_and_absent_types():
+    torch = torch_cuda()
+    q, K, N = 4, 256, 256
+    # M = 0: dW is all zero; forward / dX are no-ops
+    X = torch.empty(0, K, dtype=torch.bfloat16, device="cuda")
+    dY = torch.empty(0, N, dtype=torch.bfloat16, device="cuda")
+    t = torch.empty(0, dtype=torch.int32, device="cuda")
+    dW = torch.full((K, N), 3.0, dtype=torch.bfloat16, device="cuda")
+    Q.qalg_backward_dw(X, dY, t, q, dW=dW)
+    torch.cuda.synchronize()
+    assert not dW.any()
+    # every row has type 2: off-diagonal dW blocks of other source types are exactly zero
+    M = 100
+    Xo, _, dYo = _inputs(M, K, N, "bf16", 41)
+    tau = np.full(M, 2, np.int32)
+    dW = Q.qalg_backward_dw(to_dev(Xo), to_dev(dYo), tau_dev(tau), q)
+    torch.cuda.synchronize()
+    dWh = to_f64(dW)
+    _, dWr = O.row_typed_backward(Xo.f64, np.zeros((K, N)), dYo.f64, tau, q)
+    s, r = K // q, N // q
+    for b in range(q):
+        for j in range(q):
+            blk = dWh[b * s:(b + 1) * s, j * r:(j + 1) * r]
+            if b != j and b != 2:
+                assert not blk.any()
+    assert_groups(rel_frob_blocks(dWh, dWr, q), BF16_TOL, "dW")
