@@ -1,0 +1,327 @@
+"""Throughput of the row-typed Q_q projection (libqalg) on one MI355X.
+
+Workload (one step): the dense-model FFN shape (D, F) = (4096, 12288) in bf16
+with q = 8 (512 x 1536 weight blocks), M = 16384 token rows at positions
+0..M-1, types tau(p) = p mod 8:
+    type schedule (positions -> tau), type index, then the up projection
+    X_up [M, 4096] x W_up [4096, 12288] and the down projection
+    X_dn [M, 12288] x W_dn [12288, 4096], both forward, fp32 accumulation.
+Inputs are seeded synthetic N(0,1) activations and N(0,1/K) weights, resident
+in HBM before timing starts.
+
+Reported (one JSON line):
+  value            algebra TFLOP/s of the step: 2 * rho_q * M*K*N per projection
+                   (rho_q = (2q-1)/q^2, eq 21 and eq 24 of arXiv 2609.32814)
+  frac_peak        value / 2516.6 TFLOP/s (MI355X dense bf16 MFMA)
+  dense_equiv_tflops  2*M*K*N per projection / step time
+  speedup_vs_dense t(same kernel template at q = 1, i.e. a plain dense GEMM) / t(q)
+  roofline         the forward GEMM kernel against the bf16 MFMA peak, its
+                   launch time taken with HIP events on the launch stream
+  cpu_baseline     the fp64 CPU oracle on the host cores (a bounded sample)
+  extra            training leg (forward + dX + dW at the same shape) and the
+                   small-M decode leg (64 experts), each timed separately
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import pathlib
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+ROOT = pathlib.Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense)
+PEAK_HBM_GBS = 8000.0
+
+WORKLOAD = "ffn_up_down_D4096_F12288_q8_M16384_bf16_fwd"
+M, D, F, QQ = 16384, 4096, 12288, 8
+
+
+def rho(q: int) -> float:
+    return (2 * q - 1) / (q * q)
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="rows of each projection the CPU oracle leg evaluates")
+    ap.add_argument("--no-extra", action="store_true", help="skip the training and decode legs")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (scales HBM counters)")
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the row-typed projection is benchmarked on a single MI355X", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import gemm_qalg_forward_amd as Q
+    import synth
+
+    Q.lib()  # fails loudly without the HIP library
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ---------------- inputs (seeded, synthetic; generated in parallel per operand) ----------------
+    t0 = time.time()
+    c = 3
+    specs = {
+        "Xu": (1000 * c + 1, (M, D), 1.0),
+        "Wu": (1000 * c + 2, (D, F), D ** -0.5),
+        "Xd": (1000 * c + 11, (M, F), 1.0),
+        "Wd": (1000 * c + 12, (F, D), F ** -0.5),
+    }
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        futs = {k: ex.submit(synth.normal_operand, s, shp, std, "bf16") for k, (s, shp, std) in specs.items()}
+        host = {k: f.result() for k, f in futs.items()}
+
+    def to_dev(op):
+        return torch.from_numpy(op.bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    d = {k: to_dev(v) for k, v in host.items()}
+    pos = torch.from_numpy(synth.cyclic_positions(M)).to(dev)
+    tau = torch.empty(M, dtype=torch.int32, device=dev)
+    ws = Q.workspace(QQ, M, device=dev)
+    Yu = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+    Yd = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
+
+    ready = Q.QALG_FLAG_INDEX_READY
+
+    def step(q, tau_t, ws_t, ev=None):
+        Q.qalg_type_schedule(pos, q, Q.QALG_SCHEDULE_CYCLIC, 0, tau=tau_t, stream=stream)
+        Q.qalg_build_index(tau_t, q, ws=ws_t, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        Q.qalg_forward(d["Xu"], d["Wu"], tau_t, q, Y=Yu, ws=ws_t, flags=ready, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        Q.qalg_forward(d["Xd"], d["Wd"], tau_t, q, Y=Yd, ws=ws_t, flags=ready, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    def timed(q, tau_t, ws_t, steps, warmup):
+        for _ in range(warmup):
+            step(q, tau_t, ws_t)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(steps):
+            step(q, tau_t, ws_t, evs[k])
+        end.record(stream)
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(end)
+        up = [e[0].elapsed_time(e[1]) for e in evs]
+        dn = [e[1].elapsed_time(e[2]) for e in evs]
+        return total_ms, up, dn
+
+    # ---------------- the step at q = 8 ----------------
+    total_ms, up_ms, dn_ms = timed(QQ, tau, ws, args.steps, args.warmup)
+    ms_step = total_ms / args.steps
+    alg_flop_proj = 2.0 * rho(QQ) * M * D * F
+    dense_flop_proj = 2.0 * M * D * F
+    step_alg = 2 * alg_flop_proj
+    value = step_alg / (ms_step * 1e-3) / 1e12
+    fwd_launch_ms = (sum(up_ms) + sum(dn_ms)) / (len(up_ms) + len(dn_ms))
+    achieved = alg_flop_proj / (fwd_launch_ms * 1e-3) / 1e12
+    log(f"[bench] q=8 step {ms_step:.3f} ms; forward launch up {np.median(up_ms):.3f} ms "
+        f"down {np.median(dn_ms):.3f} ms; {value:.1f} algebra TFLOP/s")
+
+    # ---------------- dense control: the same kernel template at q = 1 ----------------
+    tau1 = torch.empty(M, dtype=torch.int32, device=dev)
+    ws1 = Q.workspace(1, M, device=dev)
+    dsteps = max(3, args.steps // 4)
+    dtotal, dup, ddn = timed(1, tau1, ws1, dsteps, 2)
+    dense_fwd_ms = (sum(dup) + sum(ddn)) / (len(dup) + len(ddn))
+    speedup = dense_fwd_ms / fwd_launch_ms
+    dense_tflops = dense_flop_proj / (dense_fwd_ms * 1e-3) / 1e12
+    log(f"[bench] q=1 dense template: forward launch {dense_fwd_ms:.3f} ms ({dense_tflops:.1f} TFLOP/s); "
+        f"speedup {speedup:.2f}x")
+
+    extra = {}
+    if not args.no_extra:
+        extra["training"] = training_leg(Q, torch, np, synth, dev, stream)
+        extra["decode"] = decode_leg(Q, torch, np, synth, dev, stream)
+
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {n} bytes read, {n} bytes written")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_leg(np, host, args.cpu_rows)
+
+    out = {
+        "metric": "algebra TFLOP/s + % bf16 MFMA peak; speedup vs same-shape dense GEMM",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "M": M, "D": D, "F": F, "q": QQ,
+                   "tau": "p mod 8, p = 0..M-1", "ops": ["type_schedule", "type_index",
+                                                        "forward up", "forward down"]},
+        "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "dense_equiv_tflops": round(2 * dense_flop_proj / (ms_step * 1e-3) / 1e12, 1),
+        "speedup_vs_dense": round(speedup, 3),
+        "dense_template_tflops": round(dense_tflops, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "tiled_bf16_kernel<Fwd> (forward GEMM)",
+                     "per_launch_flop": alg_flop_proj, "launch_ms": round(fwd_launch_ms, 4)},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def training_leg(Q, torch, np, synth, dev, stream):
+    """Forward + dX + dW at (4096, 12288), q = 8, M = 16384 (the up projection's shape)."""
+    c = 5
+    X = synth.normal_operand(1000 * c + 1, (M, D), 1.0, "bf16")
+    W = synth.normal_operand(1000 * c + 2, (D, F), D ** -0.5, "bf16")
+    dY = synth.normal_operand(1000 * c + 3, (M, F), 1.0, "bf16")
+    to = lambda op: torch.from_numpy(op.bits.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    Xd, Wd, dYd = to(X), to(W), to(dY)
+    tau = torch.from_numpy((np.arange(M) % QQ).astype(np.int32)).to(dev)
+    ws = Q.workspace(QQ, M, device=dev)
+    Y = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    dW = torch.empty(D, F, dtype=torch.bfloat16, device=dev)
+    Q.qalg_build_index(tau, QQ, ws=ws, stream=stream)
+    r = Q.QALG_FLAG_INDEX_READY
+    ops = {
+        "fwd": lambda: Q.qalg_forward(Xd, Wd, tau, QQ, Y=Y, ws=ws, flags=r, stream=stream),
+        "dx": lambda: Q.qalg_backward_dx(dYd, Wd, tau, QQ, dX=dX, ws=ws, flags=r, stream=stream),
+        "dw": lambda: Q.qalg_backward_dw(Xd, dYd, tau, QQ, dW=dW, ws=ws, flags=r, stream=stream),
+    }
+    flop = 2.0 * rho(QQ) * M * D * F
+    res = {"workload": "train_D4096_F12288_q8_M16384_bf16", "per_op_flop": flop}
+    tot = 0.0
+    for name, fn in ops.items():
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 5
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n
+        tot += ms
+        res[f"{name}_ms"] = round(ms, 4)
+        res[f"{name}_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+    res["step_ms"] = round(tot, 4)
+    res["step_tflops"] = round(3 * flop / (tot * 1e-3) / 1e12, 1)
+    log(f"[bench] training leg: {res}")
+    return res
+
+
+def decode_leg(Q, torch, np, synth, dev, stream):
+    """64 experts, one token row each (KV-cached decode), (7168 -> 2048) q = 4, weight-streaming path."""
+    c = 4
+    E, K, N, q, Mx = 64, 7168, 2048, 4, 1
+    Wb = np.stack([synth.normal_operand(1000 * c + 100 + e, (K, N), K ** -0.5, "bf16").bits for e in range(E)])
+    Xb = np.stack([synth.normal_operand(1000 * c + 300 + e, (Mx, K), 1.0, "bf16").bits for e in range(E)])
+    pos = np.stack([synth.random_positions(1000 * c + 200 + e, Mx) for e in range(E)])
+    taus = (pos % q).astype(np.int32)
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    W, X = to(Wb), to(Xb)
+    tau = torch.from_numpy(taus).to(dev)
+    Y = torch.empty(E, Mx, N, dtype=torch.bfloat16, device=dev)
+    ws = Q.workspace(q, Mx, E, device=dev)
+    fn = lambda: Q.qalg_forward_batched(X, W, tau, q, Y=Y, ws=ws, stream=stream)  # noqa: E731
+    s, r = K // q, N // q
+    # algorithmic bytes: every weight block some row needs, once, plus X and Y
+    wbytes = 0
+    for e in range(E):
+        present = set(int(t) for t in taus[e])
+        nblocks = q + sum(q - 1 for _ in present)  # all W_jj plus the strip W_i, off-diagonal, per present type
+        wbytes += nblocks * s * r * 2
+    byts = wbytes + E * Mx * (K + N) * 2
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    times = []
+    for k in range(12):
+        flush.fill_(k & 0xFF)  # evict L2 and the MALL between single launches
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(np.median(times[2:]))
+    res = {"workload": "decode_64experts_7168x2048_q4_M1_bf16", "ms": round(ms, 4),
+           "algorithmic_bytes": byts, "GBs": round(byts / (ms * 1e-3) / 1e9, 1),
+           "frac_hbm": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "protocol": "flushed (1 GiB)"}
+    log(f"[bench] decode leg: {res}")
+    return res
+
+
+def cpu_leg(np, host, rows):
+    """The fp64 oracle (NumPy/OpenBLAS) on the first `rows` rows of both projections."""
+    from oracle import qalg_oracle as O
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 0) for i in info if i.get("internal_api") in ("openblas", "mkl", "blis")] or [0])
+    except Exception:  # pragma: no cover - informational only
+        threads = 0
+    rows = min(rows, M)
+    tau = (np.arange(rows) % QQ).astype(np.int32)
+    Xu = host["Xu"].f64[:rows]
+    Xd = host["Xd"].f64[:rows]
+    Wu = host["Wu"].f64
+    Wd = host["Wd"].f64
+    t0 = time.perf_counter()
+    O.row_typed_forward(Xu, Wu, tau, QQ)
+    O.row_typed_forward(Xd, Wd, tau, QQ)
+    dt = time.perf_counter() - t0
+    flop = 2 * 2.0 * rho(QQ) * rows * D * F
+    res = {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads or len(os.sched_getaffinity(0)),
+           "kind": "oracle", "seconds": round(dt, 2),
+           "sample": f"first {rows} of {M} rows of the up and down projections (fp64 NumPy/OpenBLAS)"}
+    log(f"[bench] cpu oracle: {res}")
+    return res
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -38,13 +38,17 @@ __all__ = [
 def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 (round to nearest, ties to even); return uint16 bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
+    u = a.view(np.uint32)
+    # u + 0x7FFF + lsb cannot wrap for a non-NaN float32 (largest: -inf + 0x7FFF)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += u
+    r += np.uint32(0x7FFF)
+    r >>= np.uint32(16)
+    out = r.astype(np.uint16)
     nan = np.isnan(a)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
     if nan.any():
-        r[nan] = np.uint16(0x7FC0)
-    return r
+        out[nan] = np.uint16(0x7FC0)
+    return out
 
 
 def f64_from_bf16_bits(b: np.ndarray) -> np.ndarray:
@@ -56,16 +60,29 @@ def f64_from_bf16_bits(b: np.ndarray) -> np.ndarray:
 class Operand:
     """A synthetic operand: `bits` is what goes to the device, `f64` its exact value."""
 
-    __slots__ = ("bits", "f64", "dtype")
+    __slots__ = ("bits", "dtype", "_f64")
 
-    def __init__(self, bits: np.ndarray, f64: np.ndarray, dtype: str):
+    def __init__(self, bits: np.ndarray, dtype: str):
         self.bits = bits
-        self.f64 = f64
         self.dtype = dtype
+        self._f64 = None
+
+    @property
+    def f64(self) -> np.ndarray:
+        """Exact float64 value of the stored bits (computed on first use)."""
+        if self._f64 is None:
+            if self.dtype == "bf16":
+                self._f64 = f64_from_bf16_bits(self.bits)
+            else:
+                self._f64 = self.bits.astype(np.float64)
+        return self._f64
 
     @property
     def shape(self):
         return self.bits.shape
+
+
+_CHUNK = 1 << 23  # values drawn per step; the stream is the same as one big draw
 
 
 def normal_operand(seed: int, shape, std: float, dtype: str) -> Operand:
@@ -73,12 +90,16 @@ def normal_operand(seed: int, shape, std: float, dtype: str) -> Operand:
     if dtype not in ("f32", "bf16"):
         raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
     g = np.random.Generator(np.random.PCG64(seed))
-    v = g.standard_normal(size=shape) * std
-    f32 = v.astype(np.float32)
-    if dtype == "f32":
-        return Operand(f32, f32.astype(np.float64), dtype)
-    bits = bf16_bits_from_f32(f32)
-    return Operand(bits, f64_from_bf16_bits(bits), dtype)
+    shape = tuple(int(x) for x in np.atleast_1d(shape)) if not isinstance(shape, int) else (shape,)
+    n = int(np.prod(shape, dtype=np.int64))
+    bits = np.empty(n, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    for lo in range(0, n, _CHUNK):
+        hi = min(n, lo + _CHUNK)
+        v = g.standard_normal(size=hi - lo)
+        v *= std
+        f32 = v.astype(np.float32)
+        bits[lo:hi] = bf16_bits_from_f32(f32) if dtype == "bf16" else f32
+    return Operand(bits.reshape(shape), dtype)
 
 
 def cyclic_positions(M: int, seq_len: int | None = None, offset: int = 0) -> np.ndarray:
