@@ -95,11 +95,20 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
   p.ws = wsi;
   p.ws_stride = stride;
 
+  hipError_t e;
+  if (dtype == QALG_BF16 && qalg::fwd_persistent_supported(p)) {
+    // the persistent forward zeroes the rows of an out-of-range type itself
+    if (!(flags & QALG_FLAG_INDEX_READY)) {
+      e = qalg::launch_build_index(tau, q, M, E, wsi, stride, s);
+      if (e != hipSuccess) return QALG_ERR_HIP;
+    }
+    return hip_status(qalg::launch_fwd_persistent_bf16(p, s));
+  }
+
   // rows of an out-of-range type get zero Y / dX rows; dW ignores them
   void* zero_out = op == Op::Dw ? nullptr : C;
   const int64_t zero_ld = op == Op::Fwd ? N : K;
   const int64_t zero_stride = M * zero_ld * elem;
-  hipError_t e;
   if (!(flags & QALG_FLAG_INDEX_READY)) {
     e = qalg::launch_build_index_zeroing(tau, q, M, E, wsi, stride, zero_out, zero_ld, elem,
                                          zero_stride, s);

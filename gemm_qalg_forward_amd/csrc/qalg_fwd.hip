@@ -1,0 +1,536 @@
+// Persistent matrix-core forward of the row-typed Q_q projection (bf16 in,
+// fp32 accumulate, bf16 out) for gfx950.
+//
+// Paper: arXiv 2609.32814.  Section 4, eq 16-17: a token row of type i gets
+// y_i = x_i W_ii and y_j = x_i W_ij + x_j W_jj (j != i).  Section 6.1, eq 27
+// and Algorithm 1: the support of output group j for type i is B(i, j) =
+// {i, j}.  Section 5.3: the fused forward accumulates both endpoint products
+// before the output is written.
+//
+// Work decomposition.  The rows of each type (from the type index) are cut
+// into row tiles of BM rows that never straddle types; the N columns into
+// column tiles of BN columns that never straddle output groups.  Output tile
+// (row tile of type i, column tile in group j) is one GEMM tile whose
+// contraction runs over two K segments, X[rows, g_i] W[g_i, cols] and
+// X[rows, g_j] W[g_j, cols], or over the single segment g_i when j == i.  The
+// other q-2 weight blocks of that column tile never enter the tile: absent
+// block products are skipped at tile granularity.
+//
+// Schedule.  One workgroup per compute unit loops over its tiles (persistent).
+// The k-steps of all its tiles form one stream: operand loads for the next
+// k-step, and across a tile boundary for the next tile's first k-step, are in
+// flight while the current k-step runs on the matrix cores, so a tile costs
+// no pipeline fill.  Tiles are ordered in groups of up to 8 row tiles by all
+// column tiles (neighbouring tiles share operand rows or weight columns), the
+// order is cut into one contiguous chunk per XCD (workgroup w runs on XCD
+// w mod 8 when the grid is one workgroup per CU), and the workgroups of an XCD
+// take that chunk round robin, so concurrently running tiles of one XCD share
+// their operands in that XCD's L2.
+//
+// Data movement.  Operands go from global memory straight into LDS with the
+// gfx950 direct-to-LDS copy (global_load_lds_dwordx4: 16 bytes per lane, a
+// wave moves 1 KB per copy, no registers involved).  A k-step covers 32
+// contraction values; four LDS stages (32 KB each for 256x256 tiles) hold
+// k-steps step..step+3, so copies run three k-steps ahead of the matrix
+// cores.  The barrier that publishes the next stage sits in the middle of a
+// k-step: the first 16 contraction values' MFMAs cover it, and the next
+// k-step's first fragments are read while the second half's MFMAs run.
+//
+// LDS layouts (both bank-conflict free for the patterns used):
+//  * X tile: row r of the tile keeps its four 16-byte pieces (8 contraction
+//    values each) at piece c ^ ((r >> 1) & 3).  MFMA fragments are plain
+//    128-bit reads (lane: row l % 32, piece 2*ks + l / 32).
+//  * W tile: contraction row k keeps the tile's BN columns in 16-byte pieces
+//    at piece c ^ 2*(k & 3), i.e. the weight bank's own row-major layout.  The
+//    MFMA needs 8 consecutive contraction values per lane, so the fragment is
+//    read with two ds_read_b64_tr_b16 (gfx950 transposing LDS read): in a
+//    16-lane group, lane t's element e comes from element t % 4 of the
+//    8-byte read issued by lane 4e + t / 4, so lanes that read 4 rows x 4
+//    columns each receive one column x 4 rows.
+// The MFMA is v_mfma_f32_32x32x16_bf16 with the weight fragment as the first
+// operand, so each lane ends with four consecutive output columns of one row;
+// the wave tile is 128x128 (4x4 MFMA tiles, accumulators in AGPRs).
+//
+// Rows.  For a cyclic schedule (tau[m] = (o + m) mod q for all m, detected by
+// the index) the rows of type i are the arithmetic progression
+// (i - o) mod q + k q and are computed, never loaded; otherwise the index's
+// row list is read one tile ahead of its use.
+//
+// Rows whose type is out of range (listed after all typed rows by the index)
+// are written as zero by the same launch.
+#include "qalg.h"
+#include "qalg_internal.h"
+
+namespace qalg {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kBK = 32;       // contraction per k-step
+constexpr int kStages = 4;    // LDS stages: operands of 3 k-steps are in flight during a 4th
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM_, int BN_>
+struct FwdCfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = 2, WGN = 2;
+  static constexpr int THREADS = 256;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0 && FM >= 1 && FN >= 1, "wave tile");
+  // X tile: BM rows of 64 bytes (32 contraction values), 16-byte pieces swizzled
+  static constexpr int A_BYTES = BM * kBK * 2;
+  // W tile: 32 contraction rows of BN*2 bytes, 16-byte pieces swizzled
+  static constexpr int ROWB = BN * 2;
+  static constexpr int NCH = BN / 8;                // 16-byte pieces per W row
+  static constexpr int B_BYTES = kBK * ROWB;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = kStages * STAGE;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole 1 KB copies per wave");
+  static constexpr int A_DMA = A_BYTES / 4096;      // 1 KB direct-to-LDS copies per wave and k-step
+  static constexpr int B_DMA = B_BYTES / 4096;
+  static constexpr int DMA = A_DMA + B_DMA;
+  static_assert(2 * DMA < 64, "vmcnt range");
+};
+
+// One 16-byte piece per lane from global memory straight into LDS: lane l's
+// piece lands at lds_addr + 16 l (gfx950 global_load_lds_dwordx4; lds_addr must
+// be wave-uniform; M0 holds it, and one wait state must separate the M0 write
+// from the load).  Written as inline assembly so that the compiler does not
+// treat every later LDS read as possibly depending on the copy; completion is
+// tracked by hand with wait_vmcnt before the barrier that publishes a stage.
+__device__ __forceinline__ void copy16_to_lds(const char* gbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+// Workgroup barrier ordering LDS only (the stage copies are waited for
+// explicitly; global stores need no ordering here).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Piece swizzles (see the file comment): X row r keeps piece c at c ^ ((r >> 1) & 3);
+// W row k keeps piece c at c ^ 2 * (k & 3).
+__device__ __forceinline__ int swz_x(int row) { return (row >> 1) & 3; }
+__device__ __forceinline__ int swz_w(int k) { return 2 * (k & 3); }
+
+struct FwdArgs {
+  const char* X;
+  const char* W;
+  char* Y;
+  const int32_t* ws;
+  int64_t off_offsets, off_tiles, off_rows;
+  int q, M, K, N, s, r;
+  int cpg;     // column tiles per output group
+  int n_ct;    // column tiles in all (q * cpg)
+  int kts;     // k-steps per contraction segment (s / 32)
+};
+
+__device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {
+  const bf16x2 lo = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  const bf16x2 hi = __builtin_convertvector((f32x2){c, d}, bf16x2);
+  return (u32x2){__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+}
+
+__device__ __forceinline__ int find_group(const int32_t* tile_off, int q, int rt) {
+  int lo = 0, hi = q;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tile_off[mid] <= rt)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// One output tile, decoded from its position in the tile order.
+struct Tile {
+  int i;          // row type
+  int rank0;      // rank of the tile's first row among the rows of its type
+  int first;      // first slot of the tile's rows in the index's row list
+  int m_cnt;      // rows in the tile
+  int n0;         // first output column
+  int seg0, seg1; // K offsets of the contraction segments (group i, group j)
+  int nk;         // k-steps
+};
+
+template <class C>
+__device__ __forceinline__ Tile decode_tile(const FwdArgs& a, const int32_t* offsets,
+                                            const int32_t* tile_off, int n_rt, int L) {
+  // groups of up to 8 row tiles x all column tiles, row tile fastest
+  constexpr int G = 8;
+  const int span = G * a.n_ct;
+  const int g = L / span;
+  const int first_rt = g * G;
+  const int gm = min(n_rt - first_rt, G);
+  const int w = L - g * span;
+  const int rt = first_rt + w % gm;
+  const int ct = w / gm;
+  const int i = find_group(tile_off, a.q, rt);
+  Tile t;
+  t.i = i;
+  t.rank0 = (rt - tile_off[i]) * C::BM;
+  t.first = offsets[i] + t.rank0;
+  t.m_cnt = min(C::BM, offsets[i + 1] - t.first);
+  const int j = ct / a.cpg, cc = ct - j * a.cpg;
+  t.n0 = j * a.r + cc * C::BN;
+  t.seg0 = i * a.s;
+  t.seg1 = j * a.s;
+  t.nk = (j == i) ? a.kts : 2 * a.kts;
+  return t;
+}
+
+template <class C, bool CYC>
+__device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
+  constexpr int BM = C::BM, T = C::THREADS;
+  const int32_t* ws = a.ws;
+  const int32_t* rows = ws + a.off_rows;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // per-type row offsets and row-tile offsets, cached in LDS behind the stages
+  // (tile decoding then never waits on the vector-memory counter, which also
+  // counts the copies in flight)
+  int* s_off = reinterpret_cast<int*>(smem + C::LDS_BYTES);
+  int* s_toff = s_off + (a.q + 1);
+  {
+    const int32_t* offsets = ws + a.off_offsets;
+    const int32_t* tile_off = ws + a.off_tiles + tile_height_slot(BM) * (a.q + 1);
+    for (int x = tid; x <= a.q; x += T) {
+      s_off[x] = offsets[x];
+      s_toff[x] = tile_off[x];
+    }
+  }
+  __syncthreads();
+
+  // rows of an out-of-range type: zero output rows (rare)
+  {
+    const int typed = s_off[a.q];
+    const int nbad = a.M - typed;
+    const int row_u4 = a.N / 8;  // 16-byte pieces per output row
+    for (int b = blockIdx.x; b < nbad; b += gridDim.x) {
+      u32x4* yr = reinterpret_cast<u32x4*>(a.Y + int64_t(rows[typed + b]) * a.N * 2);
+      for (int x = tid; x < row_u4; x += T) yr[x] = (u32x4){0u, 0u, 0u, 0u};
+    }
+  }
+
+  // this workgroup's tiles: a contiguous chunk per XCD, round robin inside it
+  const int n_rt = s_toff[a.q];
+  const int total = n_rt * a.n_ct;
+  const int nx = gridDim.x >= 8 ? 8 : 1;
+  const int per_x = gridDim.x / nx;
+  const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx;
+  if (slot >= per_x) return;  // grid not a multiple of 8: the remainder idles
+  const int c_lo = int(int64_t(total) * xcd / nx), c_hi = int(int64_t(total) * (xcd + 1) / nx);
+  const int L_first = c_lo + slot;
+  if (L_first >= c_hi) return;
+
+  const uint32_t n_bytes = uint32_t(a.N) * 2u;
+  const uint32_t k_bytes = uint32_t(a.K) * 2u;
+  // cyclic schedule: the k-th row of type i is (i - cyc) mod q + k q, no row list needed
+  const int cyc = ws[4];
+  auto row_of = [&](const Tile& t, int r) -> int {
+    if constexpr (CYC) {
+      const int start = t.i >= cyc ? t.i - cyc : t.i - cyc + a.q;
+      return start + (t.rank0 + r) * a.q;
+    }
+    return rows[t.first + r];
+  };
+
+  // ---------------- copy cursor: direct global -> LDS copies, 3 k-steps ahead ----------------
+  // copy u of this wave moves 1 KB: lane l carries 16-byte slot (wid * DMA_x + u) * 64 + l
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(smem)));
+  uint32_t b_src[C::B_DMA];  // byte offset of the lane's W piece relative to (k-step row 0, n0)
+#pragma unroll
+  for (int u = 0; u < C::B_DMA; ++u) {
+    const int sl = (wid * C::B_DMA + u) * 64 + lane;
+    const int k = sl / C::NCH, p = sl - (sl / C::NCH) * C::NCH;
+    const int c = p ^ swz_w(k);
+    b_src[u] = uint32_t(k) * n_bytes + uint32_t(c) * 16u;
+  }
+  int a_row[C::A_DMA];   // tile-local row of each X copy slot, and its swizzled piece
+  uint32_t a_pc[C::A_DMA];
+#pragma unroll
+  for (int u = 0; u < C::A_DMA; ++u) {
+    const int sl = (wid * C::A_DMA + u) * 64 + lane;
+    a_row[u] = sl >> 2;
+    a_pc[u] = uint32_t((sl & 3) ^ swz_x(sl >> 2)) * 16u;
+  }
+  // row ids are fetched one tile ahead of their use (listed schedules only),
+  // so that the wait for them overlaps a whole tile
+  int pre_row[C::A_DMA];
+  auto prefetch_rows = [&](const Tile& t) {
+#pragma unroll
+    for (int u = 0; u < C::A_DMA; ++u) pre_row[u] = row_of(t, min(a_row[u], t.m_cnt - 1));
+  };
+  uint32_t a_src[C::A_DMA];
+  auto take_rows = [&]() {
+#pragma unroll
+    for (int u = 0; u < C::A_DMA; ++u) a_src[u] = uint32_t(pre_row[u]) * k_bytes + a_pc[u];
+  };
+
+  Tile lt = decode_tile<C>(a, s_off, s_toff, n_rt, L_first);
+  int lL = L_first, lk = 0;
+  prefetch_rows(lt);
+  take_rows();
+  if (lL + per_x < c_hi) prefetch_rows(decode_tile<C>(a, s_off, s_toff, n_rt, lL + per_x));
+  bool more = true;  // the copy cursor still has k-steps
+  auto issue_copies = [&](int stage) {
+    const int sg = lk >= a.kts ? 1 : 0;
+    const int kcol = (sg ? lt.seg1 : lt.seg0) + (lk - sg * a.kts) * kBK;
+    const uint32_t S = lds0 + uint32_t(stage * C::STAGE);
+#pragma unroll
+    for (int u = 0; u < C::A_DMA; ++u)
+      copy16_to_lds(a.X, a_src[u] + uint32_t(kcol) * 2u, S + uint32_t((wid * C::A_DMA + u) * 1024));
+    const uint32_t wbase = uint32_t(kcol) * n_bytes + uint32_t(lt.n0) * 2u;
+#pragma unroll
+    for (int u = 0; u < C::B_DMA; ++u)
+      copy16_to_lds(a.W, wbase + b_src[u], S + uint32_t(C::A_BYTES + (wid * C::B_DMA + u) * 1024));
+    if (++lk >= lt.nk) {
+      lL += per_x;
+      if (lL >= c_hi) {
+        more = false;
+      } else {
+        lt = decode_tile<C>(a, s_off, s_toff, n_rt, lL);
+        lk = 0;
+        take_rows();
+        if (lL + per_x < c_hi) prefetch_rows(decode_tile<C>(a, s_off, s_toff, n_rt, lL + per_x));
+      }
+    }
+  };
+
+  // ---------------- fragment reads ----------------
+  const int wm = wid / C::WGN, wn = wid % C::WGN;
+  const int l32 = lane & 31, lhi = lane >> 5;
+  // X fragment (32 rows x 16 contraction): lane reads row l32, piece 2*ks + lhi
+  int a_rd[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    a_rd[ks] = (wm * C::WTM + l32) * 64 + (((2 * ks + lhi) ^ swz_x(l32)) << 4);
+  // W fragment (32 columns x 16 contraction) as two transposing 8-byte reads per lane:
+  // in a 16-lane group (g = lane / 16, t = lane % 16) lane t reads row 8*(g/2) + t/4 (+4),
+  // columns 16*(g%2) + 4*(t%4) of the fragment; the transpose hands lane t column t, 4 rows.
+  int b_rd[2];  // by parity of the fragment's 32-column block index
+  {
+    const int g = lane >> 4, t = lane & 15;
+    const int k_l = 8 * (g >> 1) + (t >> 2);
+    const int f = swz_w(k_l);
+    const int r2 = 2 * (g & 1) + ((t & 3) >> 1);
+    const int lo = ((r2 ^ (f & 2)) << 4) + 8 * (t & 1) + k_l * C::ROWB;
+    const int dm = (f >> 2) ? 64 : 0;  // block-index bit flipped by the swizzle
+    b_rd[0] = C::A_BYTES + lo + dm;
+    b_rd[1] = C::A_BYTES + lo - dm;
+  }
+  const int m0 = wn * (C::WTN / 32);  // block index of the wave's first 32-column block
+
+  f32x16 acc[C::FM][C::FN];
+  // fragments of the two 16-wide halves of a k-step (registers double buffered)
+  bf16x8 fa0[C::FM], fb0[C::FN], fa1[C::FM], fb1[C::FN];
+  auto load_frags = [&](int stage, int ks, bf16x8 (&fa)[C::FM], bf16x8 (&fb)[C::FN]) {
+    const char* S = smem + stage * C::STAGE;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+      fa[fm] = *reinterpret_cast<const bf16x8*>(S + a_rd[ks] + fm * 32 * 64);
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int m = m0 + fn;
+      const char* p = S + b_rd[m & 1] + 64 * m + 16 * ks * C::ROWB;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * C::ROWB));
+      fb[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto mfmas = [&](const bf16x8 (&fa)[C::FM], const bf16x8 (&fb)[C::FN]) {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], acc[fm][fn], 0, 0, 0);
+  };
+
+  // ---------------- pipeline ----------------
+  // Copies run three k-steps ahead (stages step+1..step+3 in flight while step
+  // is computed).  The barrier that publishes stage step+1 sits in the middle
+  // of k-step `step`: the first half's MFMAs cover the wait, and after the
+  // barrier the next k-step's first fragments are read while the second half's
+  // MFMAs run, so the matrix cores never wait for a fragment read.
+  int issued = 0;  // k-steps whose copies were issued
+  for (int st = 0; st < kStages - 1 && more; ++st) {
+    issue_copies(st);
+    ++issued;
+  }
+  if (issued >= 3)
+    wait_vmcnt<2 * C::DMA>();
+  else if (issued == 2)
+    wait_vmcnt<C::DMA>();
+  else
+    wait_vmcnt<0>();
+  lds_barrier();
+  load_frags(0, 0, fa0, fb0);
+
+  Tile ct = decode_tile<C>(a, s_off, s_toff, n_rt, L_first);
+  int cL = L_first;
+  int step = 0;
+  for (;;) {
+    // output rows of this tile, loaded now and used after its last k-step
+    int out_row[C::FM];
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) out_row[fm] = row_of(ct, min(wm * C::WTM + fm * 32 + l32, ct.m_cnt - 1));
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = (f32x16){};
+
+    for (int ck = 0; ck < ct.nk; ++ck) {
+      const int stage = step & (kStages - 1);
+      load_frags(stage, 1, fa1, fb1);
+      mfmas(fa0, fb0);
+      // publish stage step+1: this wave's copies of it have landed (copies of
+      // later k-steps may still be in flight), then everyone's have
+      const int ahead = issued - step - 2;  // k-steps issued after step+1 (0..1)
+      if (ahead >= 1)
+        wait_vmcnt<C::DMA>();
+      else
+        wait_vmcnt<0>();
+      lds_barrier();
+      // every wave is past k-step step-1: its stage takes the copies of step+3
+      if (more) {
+        issue_copies((step + kStages - 1) & (kStages - 1));
+        ++issued;
+      }
+      if (step + 1 < issued) load_frags((step + 1) & (kStages - 1), 0, fa0, fb0);
+      mfmas(fa1, fb1);
+      ++step;
+    }
+
+    // epilogue: one rounding of each fp32 sum, 8-byte stores of 4 columns
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int ml = wm * C::WTM + fm * 32 + l32;
+      if (ml < ct.m_cnt) {
+        char* crow = a.Y + (uint32_t(out_row[fm]) * n_bytes + uint32_t(ct.n0 + wn * C::WTN + lhi * 4) * 2u);
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16& v = acc[fm][fn];
+            *reinterpret_cast<u32x2*>(crow + (fn * 32 + g * 8) * 2) =
+                pack4_bf16(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+          }
+        }
+      }
+    }
+    cL += per_x;
+    if (cL >= c_hi) break;
+    ct = decode_tile<C>(a, s_off, s_toff, n_rt, cL);
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS, 1) void fwd_persistent_kernel(FwdArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int32_t* ws = a.ws;
+  if (ws[1] != kIndexMagic || ws[2] != a.q || ws[3] != a.M) return;
+  // two instantiations: the cyclic one never reads the row list, so it has no
+  // global loads for the compiler to wait on inside the pipeline
+  if (ws[4] >= 0)
+    fwd_body<C, true>(a, smem);
+  else
+    fwd_body<C, false>(a, smem);
+}
+
+using Fwd256x256 = FwdCfg<256, 256>;
+using Fwd256x192 = FwdCfg<256, 192>;
+using Fwd256x128 = FwdCfg<256, 128>;
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+template <class C>
+hipError_t launch_fwd(const ProblemDesc& p, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_persistent_kernel<C>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             C::LDS_BYTES + int(sizeof(int)) * 2 * (QALG_MAX_Q + 1));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  FwdArgs a{};
+  a.X = static_cast<const char*>(p.A);
+  a.W = static_cast<const char*>(p.B);
+  a.Y = static_cast<char*>(p.C);
+  a.ws = p.ws;
+  const WsLayout L = ws_layout(p.q, p.M);
+  a.off_offsets = L.offsets;
+  a.off_tiles = L.tile_off;
+  a.off_rows = L.rows;
+  a.q = p.q;
+  a.M = int(p.M);
+  a.K = int(p.K);
+  a.N = int(p.N);
+  a.s = int(p.K / p.q);
+  a.r = int(p.N / p.q);
+  a.kts = a.s / kBK;
+  a.cpg = a.r / C::BN;
+  a.n_ct = p.q * a.cpg;
+  const int64_t max_tiles = ((p.M + C::BM - 1) / C::BM + p.q - 1) * int64_t(a.n_ct);
+  int grid = cu_count();
+  if (max_tiles < grid) grid = max_tiles < 8 ? int(max_tiles) : int(max_tiles / 8 * 8);
+  if (grid < 1) grid = 1;
+  const size_t lds = C::LDS_BYTES + sizeof(int) * 2 * (p.q + 1);
+  hipLaunchKernelGGL((fwd_persistent_kernel<C>), dim3(grid), dim3(C::THREADS), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool fwd_persistent_supported(const ProblemDesc& p) {
+  if (p.op != Op::Fwd || p.E != 1) return false;
+  const int64_t s = p.K / p.q, r = p.N / p.q;
+  // byte offsets of every operand fit in 32 bits
+  const int64_t lim = int64_t(1) << 31;
+  if (p.M * p.K >= lim || p.K * p.N >= lim || p.M * p.N >= lim) return false;
+  if (s % kBK != 0) return false;
+  if (r % 256 != 0 && r % 192 != 0 && r % 128 != 0) return false;
+  return (p.M + p.q - 1) / p.q >= 128;  // rows per type (cyclic estimate)
+}
+
+hipError_t launch_fwd_persistent_bf16(const ProblemDesc& p, hipStream_t s) {
+  const int64_t r = p.N / p.q;
+  if (r % 256 == 0) return launch_fwd<Fwd256x256>(p, s);
+  if (r % 192 == 0) return launch_fwd<Fwd256x192>(p, s);
+  return launch_fwd<Fwd256x128>(p, s);
+}
+
+}  // namespace qalg

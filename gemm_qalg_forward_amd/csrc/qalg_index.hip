@@ -19,6 +19,7 @@ namespace {
 
 constexpr int kIdxThreads = 1024;
 constexpr int kIdxWaves = kIdxThreads / 64;
+constexpr int kBatch = 8;  // 64-row steps whose types are loaded together
 
 __global__ void type_schedule_kernel(const int64_t* __restrict__ pos, int64_t M, int q, int kind,
                                      int64_t period, int32_t* __restrict__ tau) {
@@ -92,23 +93,42 @@ __global__ __launch_bounds__(kIdxThreads) void build_index_kernel(
   const int r0 = min(w * slice, M), r1 = min(r0 + slice, M);
   int* my = tab + w * Q1;
 
-  // pass 1: per-wave counts of each type in its slice
-  for (int base = r0; base < r1; base += 64) {
-    const int m = base + lane;
-    int t = -1;
-    if (m < r1) {
-      const int v = tau[m];
-      t = (v >= 0 && v < q) ? v : q;
+  // pass 1: per-wave counts of each type in its slice.  Types are loaded kBatch
+  // steps at a time so that the loads overlap; the same pass checks whether
+  // the schedule is cyclic, tau[m] = (tau[0] + m) mod q for every row.
+  __shared__ int s_cyclic;
+  const int t0 = M > 0 ? tau[0] : 0;
+  if (tid == 0) s_cyclic = (M > 0 && t0 >= 0 && t0 < q) ? 1 : 0;
+  __syncthreads();
+  bool cyc_ok = true;
+  for (int base = r0; base < r1; base += 64 * kBatch) {
+    int tv[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int m = base + b * 64 + lane;
+      tv[b] = (m < r1) ? tau[m] : 0;
     }
-    uint64_t left = __ballot(t >= 0);
-    while (left) {
-      const int leader = __builtin_ctzll(left);
-      const int tl = __shfl(t, leader, 64);
-      const uint64_t mask = __ballot(t == tl);
-      if (lane == leader) my[tl] += __popcll(mask);
-      left &= ~mask;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int m = base + b * 64 + lane;
+      if (base + b * 64 >= r1) break;
+      int t = -1;
+      if (m < r1) {
+        const int v = tv[b];
+        t = (v >= 0 && v < q) ? v : q;
+        cyc_ok = cyc_ok && v == int((int64_t(t0) + m) % q);
+      }
+      uint64_t left = __ballot(t >= 0);
+      while (left) {
+        const int leader = __builtin_ctzll(left);
+        const int tl = __shfl(t, leader, 64);
+        const uint64_t mask = __ballot(t == tl);
+        if (lane == leader) my[tl] += __popcll(mask);
+        left &= ~mask;
+      }
     }
   }
+  if (!cyc_ok) s_cyclic = 0;
   __syncthreads();
 
   // per type: exclusive prefix over waves (in place), total per type
@@ -165,28 +185,39 @@ __global__ __launch_bounds__(kIdxThreads) void build_index_kernel(
   __syncthreads();
 
   // pass 2: stable scatter of row ids
-  for (int base = r0; base < r1; base += 64) {
-    const int m = base + lane;
-    int t = -1;
-    if (m < r1) {
-      const int v = tau[m];
-      t = (v >= 0 && v < q) ? v : q;
+  for (int base = r0; base < r1; base += 64 * kBatch) {
+    int tv[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int m = base + b * 64 + lane;
+      tv[b] = (m < r1) ? tau[m] : 0;
     }
-    uint64_t left = __ballot(t >= 0);
-    const uint64_t below = (uint64_t(1) << lane) - 1;
-    while (left) {
-      const int leader = __builtin_ctzll(left);
-      const int tl = __shfl(t, leader, 64);
-      const uint64_t mask = __ballot(t == tl);
-      if (t == tl) rows[my[tl] + __popcll(mask & below)] = m;
-      if (lane == leader) my[tl] += __popcll(mask);
-      left &= ~mask;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int m = base + b * 64 + lane;
+      if (base + b * 64 >= r1) break;
+      int t = -1;
+      if (m < r1) {
+        const int v = tv[b];
+        t = (v >= 0 && v < q) ? v : q;
+      }
+      uint64_t left = __ballot(t >= 0);
+      const uint64_t below = (uint64_t(1) << lane) - 1;
+      while (left) {
+        const int leader = __builtin_ctzll(left);
+        const int tl = __shfl(t, leader, 64);
+        const uint64_t mask = __ballot(t == tl);
+        if (t == tl) rows[my[tl] + __popcll(mask & below)] = m;
+        if (lane == leader) my[tl] += __popcll(mask);
+        left &= ~mask;
+      }
     }
   }
 
   if (tid == 0) {
     ws[2] = q;
     ws[3] = M;
+    ws[4] = s_cyclic ? t0 : -1;  // cyclic schedule: rows of type i are (i - t0) mod q + k q
     ws[1] = kIndexMagic;
   }
 

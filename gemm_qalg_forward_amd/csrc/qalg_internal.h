@@ -19,6 +19,9 @@ constexpr int tile_height_slot(int bm) {
 //   [0]            rows with an out-of-range type
 //   [1]            magic (kIndexMagic) once an index was written
 //   [2], [3]       q and M of that index
+//   [4]            o >= 0 if the schedule is cyclic, tau[m] = (o + m) mod q for
+//                  every row (then the k-th row of type i is (i - o) mod q + k q);
+//                  -1 otherwise
 //   [16, 16+q)     counts[q]                 (M_i)
 //   [.., +q+1)     offsets[q+1]              (running sums of counts)
 //   [.., +5(q+1))  tile_off[5][q+1]          (running sums of ceil(M_i / BM))
@@ -78,5 +81,8 @@ hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s);
 hipError_t launch_tiled_f32(const ProblemDesc& p, hipStream_t s);
 hipError_t launch_small_m_bf16(const ProblemDesc& p, hipStream_t s);
 bool small_m_supported(const ProblemDesc& p);
+// Persistent 256x256-tile forward (bf16, one problem); zeroes rows of out-of-range type itself.
+bool fwd_persistent_supported(const ProblemDesc& p);
+hipError_t launch_fwd_persistent_bf16(const ProblemDesc& p, hipStream_t s);
 
 }  // namespace qalg

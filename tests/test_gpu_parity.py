@@ -23,6 +23,9 @@ SHAPES = [
     (513, 1024, 512, 1, "zeros", 0, 0),      # q = 1: the dense product
     (300, 128, 128, 16, "cyclic", 5, 0),     # s = r = 8
     (2048, 256, 512, 4, "random", 0, 0),     # some types with many row tiles
+    (5000, 512, 1024, 4, "random", 0, 37),   # persistent 256x256 path: ragged row tiles, bad types
+    (4099, 768, 768, 3, "cyclic", 2, 0),     # persistent path, odd q, type offset
+    (2600, 1024, 2304, 4, "cyclic", 0, 0),   # persistent 256x192 tiles (r = 576 = 3 x 192)
 ]
 
 

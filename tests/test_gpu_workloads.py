@@ -1,0 +1,172 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark times.
+
+Each workload's outputs are compared with the fp64 oracle on sampled rows (a
+row's output depends only on that row, so the oracle evaluates the sampled
+rows alone) or, where it finishes in seconds, on the whole output.  The bar is
+the relative Frobenius error per output group: 5e-3 for bf16, 1e-5 for fp32.
+
+Workloads:
+  * Q_2 row-typed forward in fp32, M=64, K=N=256 (whole output, dX and dW too)
+  * ~110M-LM FFN shapes, bf16, q=4: 768->3072 and 3072->768, M=8192
+  * dense FFN (4096, 12288), bf16, q=8, M=16384: up and down projections
+  * narrow expert shapes, bf16, 64 experts: (7168,2048) q=4, (2048,768) q=4 and q=8
+  * training gradients at (4096, 12288), q=8, M=16384: forward, dX and dW
+"""
+import numpy as np
+import pytest
+
+import gemm_qalg_forward_amd as Q
+import synth
+from gpu_common import say, tau_dev, to_dev, to_f64, torch_cuda
+from oracle import qalg_oracle as O
+from qalg_check import BF16_TOL, F32_TOL, assert_groups, rel_frob_blocks, rel_frob_col_groups
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(M, q, n, seed):
+    """n rows spread over all types, plus the first and last row."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    pick = g.choice(M, size=min(n, M), replace=False)
+    return np.unique(np.concatenate([pick, [0, M - 1]]))
+
+
+def _sampled_forward_check(X, W, tau, q, Yd, rows, what):
+    Yr = O.row_typed_forward(X.f64[rows], W.f64, tau[rows], q)
+    got = to_f64(Yd[rows])
+    return assert_groups(rel_frob_col_groups(got, Yr, q), BF16_TOL, what)
+
+
+def test_q2_fp32_whole_output():
+    torch = torch_cuda()
+    c, M, K, N, q = 1, 64, 256, 256, 2
+    say(f"[workload] Q_2 fp32 M={M} K={K} N={N}")
+    X = synth.normal_operand(synth.seed_for(c, "X"), (M, K), 1.0, "f32")
+    W = synth.normal_operand(synth.seed_for(c, "W"), (K, N), K ** -0.5, "f32")
+    dY = synth.normal_operand(synth.seed_for(c, "dY"), (M, N), 1.0, "f32")
+    tau = O.type_schedule(synth.cyclic_positions(M), q)
+    Xd, Wd, dYd, td = to_dev(X), to_dev(W), to_dev(dY), tau_dev(tau)
+    ws = Q.workspace(q, M)
+    Q.qalg_build_index(td, q, ws=ws)
+    r = Q.QALG_FLAG_INDEX_READY
+    Y = Q.qalg_forward(Xd, Wd, td, q, ws=ws, flags=r)
+    dX = Q.qalg_backward_dx(dYd, Wd, td, q, ws=ws, flags=r)
+    dW = Q.qalg_backward_dw(Xd, dYd, td, q, ws=ws, flags=r)
+    torch.cuda.synchronize()
+    Yr = O.row_typed_forward(X.f64, W.f64, tau, q)
+    dXr, dWr = O.row_typed_backward(X.f64, W.f64, dY.f64, tau, q)
+    assert_groups(rel_frob_col_groups(to_f64(Y), Yr, q), F32_TOL, "Y")
+    assert_groups(rel_frob_col_groups(to_f64(dX), dXr, q), F32_TOL, "dX")
+    assert_groups(rel_frob_blocks(to_f64(dW), dWr, q), F32_TOL, "dW")
+    # 6 of the 8 block products of the square form are used by the two row types
+    assert O.mac_count(tau, q, K, N)[0] == 6
+
+
+@pytest.mark.parametrize("K,N", [(768, 3072), (3072, 768)], ids=["up", "down"])
+def test_lm_ffn_q4_whole_output(K, N):
+    torch = torch_cuda()
+    c, M, q = 2, 8192, 4
+    say(f"[workload] 110M-LM FFN bf16 q=4 M={M} {K}->{N}")
+    X = synth.normal_operand(synth.seed_for(c, "X") + (10 if K > N else 0), (M, K), 1.0, "bf16")
+    W = synth.normal_operand(synth.seed_for(c, "W") + (10 if K > N else 0), (K, N), K ** -0.5, "bf16")
+    tau = O.type_schedule(synth.cyclic_positions(M, seq_len=1024), q)
+    Xd, Wd, td = to_dev(X), to_dev(W), tau_dev(tau)
+    ws = Q.workspace(q, M)
+    Q.qalg_build_index(td, q, ws=ws)
+    Y = Q.qalg_forward(Xd, Wd, td, q, ws=ws, flags=Q.QALG_FLAG_INDEX_READY)
+    torch.cuda.synchronize()
+    Yr = O.row_typed_forward(X.f64, W.f64, tau, q)
+    e = assert_groups(rel_frob_col_groups(to_f64(Y), Yr, q), BF16_TOL, "Y")
+    say(f"    max rel err {e:.2e}")
+
+
+@pytest.mark.parametrize("proj", ["up", "down"])
+def test_dense_ffn_q8_sampled(proj):
+    """The benchmark's workload: same seeds, same calls (schedule, index, forward with the index ready)."""
+    torch = torch_cuda()
+    c, M, D, F, q = 3, 16384, 4096, 12288, 8
+    K, N = (D, F) if proj == "up" else (F, D)
+    off = 0 if proj == "up" else 10
+    say(f"[workload] dense FFN bf16 q=8 M={M} {K}->{N}")
+    X = synth.normal_operand(1000 * c + 1 + off, (M, K), 1.0, "bf16")
+    W = synth.normal_operand(1000 * c + 2 + off, (K, N), K ** -0.5, "bf16")
+    pos = torch.from_numpy(synth.cyclic_positions(M)).to("cuda")
+    td = Q.qalg_type_schedule(pos, q)
+    ws = Q.workspace(q, M)
+    Q.qalg_build_index(td, q, ws=ws)
+    Xd, Wd = to_dev(X), to_dev(W)
+    Y = Q.qalg_forward(Xd, Wd, td, q, ws=ws, flags=Q.QALG_FLAG_INDEX_READY)
+    torch.cuda.synchronize()
+    tau = td.cpu().numpy()
+    np.testing.assert_array_equal(tau, np.arange(M) % q)
+    rows = _sample_rows(M, q, 768, 31 + off)
+    e = _sampled_forward_check(X, W, tau, q, Y, rows, f"Y {proj}")
+    say(f"    max rel err over {rows.size} sampled rows {e:.2e}")
+    # a second launch on the same inputs is bitwise identical
+    Y2 = Q.qalg_forward(Xd, Wd, td, q, ws=ws, flags=Q.QALG_FLAG_INDEX_READY)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)
+
+
+_EXPERT_BANKS = {}
+
+
+def _expert_banks(K, N, E, c=4):
+    """The E experts' weight banks (host operands and one device tensor), drawn once per shape."""
+    key = (K, N, E)
+    if key not in _EXPERT_BANKS:
+        from concurrent.futures import ThreadPoolExecutor
+        torch = torch_cuda()
+        with ThreadPoolExecutor(max_workers=8) as ex:
+            Ws = list(ex.map(lambda e: synth.normal_operand(1000 * c + 100 + e, (K, N), K ** -0.5, "bf16"), range(E)))
+        Wd = torch.empty((E, K, N), dtype=torch.bfloat16, device="cuda")
+        for e in range(E):
+            Wd[e].copy_(to_dev(Ws[e]))
+        _EXPERT_BANKS.clear()
+        _EXPERT_BANKS[key] = (Ws, Wd)
+    return _EXPERT_BANKS[key]
+
+
+@pytest.mark.parametrize("K,N,q", [(7168, 2048, 4), (2048, 768, 4), (2048, 768, 8)])
+@pytest.mark.parametrize("M", [1, 8, 64, 256, 1024])
+def test_experts_sampled(K, N, q, M):
+    torch = torch_cuda()
+    c, E = 4, 64
+    say(f"[workload] experts E={E} M={M} {K}->{N} q={q}")
+    Ws, Wd = _expert_banks(K, N, E, c)
+    Xs = [synth.normal_operand(1000 * c + 300 + e, (M, K), 1.0, "bf16") for e in range(E)]
+    taus = np.stack([O.type_schedule(synth.random_positions(1000 * c + 200 + e, M), q) for e in range(E)])
+    Xd = torch.stack([to_dev(x) for x in Xs])
+    Y = Q.qalg_forward_batched(Xd, Wd, tau_dev(taus), q)
+    torch.cuda.synchronize()
+    # oracle on a few experts, a sample of rows each
+    for e in (0, 17, 63):
+        rows = _sample_rows(M, q, 64, e)
+        _sampled_forward_check(Xs[e], Ws[e], taus[e], q, Y[e], rows, f"expert {e}")
+
+
+def test_training_grads_q8():
+    torch = torch_cuda()
+    c, M, K, N, q = 5, 16384, 4096, 12288, 8
+    say(f"[workload] training q=8 M={M} {K}->{N}: forward, dX, dW")
+    X = synth.normal_operand(synth.seed_for(c, "X"), (M, K), 1.0, "bf16")
+    W = synth.normal_operand(synth.seed_for(c, "W"), (K, N), K ** -0.5, "bf16")
+    dY = synth.normal_operand(synth.seed_for(c, "dY"), (M, N), 1.0, "bf16")
+    tau = (np.arange(M) % q).astype(np.int32)
+    Xd, Wd, dYd, td = to_dev(X), to_dev(W), to_dev(dY), tau_dev(tau)
+    ws = Q.workspace(q, M)
+    Q.qalg_build_index(td, q, ws=ws)
+    r = Q.QALG_FLAG_INDEX_READY
+    Y = Q.qalg_forward(Xd, Wd, td, q, ws=ws, flags=r)
+    dX = Q.qalg_backward_dx(dYd, Wd, td, q, ws=ws, flags=r)
+    dW = Q.qalg_backward_dw(Xd, dYd, td, q, ws=ws, flags=r)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M, q, 512, 5)
+    _sampled_forward_check(X, W, tau, q, Y, rows, "Y")
+    # dX rows depend on their own dY rows only
+    dXr_s, _ = O.row_typed_backward(X.f64[rows], W.f64, dY.f64[rows], tau[rows], q)
+    assert_groups(rel_frob_col_groups(to_f64(dX[rows]), dXr_s, q), BF16_TOL, "dX")
+    # dW is a sum over all rows: the whole oracle gradient (fp64 block GEMMs)
+    _, dWr = O.row_typed_backward(X.f64, W.f64, dY.f64, tau, q)
+    e = assert_groups(rel_frob_blocks(to_f64(dW), dWr, q), BF16_TOL, "dW")
+    say(f"    dW max rel err {e:.2e}")
