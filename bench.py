@@ -205,7 +205,7 @@ def main() -> int:
         "speedup_vs_dense": speedup,
         "dense_template_tflops": dense_tflops,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": profiled_traffic(),
                      "kernel": "fwd_persistent_kernel (forward GEMM, 256x256 tiles)",
                      "per_launch_flop": alg_flop_proj, "launch_ms": round(fwd_launch_ms, 4)},
         "cpu_baseline": cpu,
@@ -213,6 +213,28 @@ def main() -> int:
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+PROFILE = ROOT / "profiles" / "fwd_persistent_ffn_D4096_F12288_q8_M16384.md"
+
+
+def profiled_traffic():
+    """HBM bytes per forward launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE x2 + WRITE_SIZE x1, scaled against a plain 1 GiB copy), or None
+    when the kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        fields = {}
+        for line in PROFILE.read_text().splitlines():
+            if ":" in line and not line.startswith(("#", "|", " ")):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+        src = ROOT / fields["kernel_source"]
+        if hashlib.sha256(src.read_bytes()).hexdigest() != fields["kernel_source_sha256"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def training_leg(Q, torch, np, synth, dev, stream):
