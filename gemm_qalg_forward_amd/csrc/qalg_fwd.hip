@@ -20,7 +20,7 @@
 // The k-steps of all its tiles form one stream: operand loads for the next
 // k-step, and across a tile boundary for the next tile's first k-step, are in
 // flight while the current k-step runs on the matrix cores, so a tile costs
-// no pipeline fill.  Tiles are ordered in groups of up to 8 row tiles by all
+// no pipeline fill.  Tiles are ordered in groups of up to 4 row tiles by all
 // column tiles (neighbouring tiles share operand rows or weight columns), the
 // order is cut into one contiguous chunk per XCD (workgroup w runs on XCD
 // w mod 8 when the grid is one workgroup per CU), and the workgroups of an XCD
@@ -179,8 +179,9 @@ struct Tile {
 template <class C>
 __device__ __forceinline__ Tile decode_tile(const FwdArgs& a, const int32_t* offsets,
                                             const int32_t* tile_off, int n_rt, int L) {
-  // groups of up to 8 row tiles x all column tiles, row tile fastest
-  constexpr int G = 8;
+  // groups of up to 4 row tiles x all column tiles, row tile fastest (measured
+  // against 2, 8 and 16 row tiles: the least L2 refetch for 256x256 tiles)
+  constexpr int G = 4;
   const int span = G * a.n_ct;
   const int g = L / span;
   const int first_rt = g * G;

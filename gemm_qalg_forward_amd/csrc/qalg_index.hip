@@ -4,8 +4,11 @@
 // tau(p) (cyclic; appendix D.5 the pilot's interval form); Algorithm 1 forms
 // the row sets I_i = {b : tau(p_b) = i} that every later step works on.
 //
-// The index is built without a sort: one counting pass and one stable
-// scatter, inside a single workgroup per problem.  Each of the 16 waves owns a
+// The index is built without a sort, inside a single workgroup per problem.
+// A cyclic schedule (tau[m] = (o + m) mod q, the paper's position schedule at
+// any offset) is recognised by one parallel pass and its index written in
+// closed form.  Any other schedule takes one counting pass and one stable
+// scatter.  Each of the 16 waves owns a
 // contiguous slice of the rows; within a 64-row step a wave groups its lanes
 // by type with ballots (one round per distinct type present), so both passes
 // cost O(M / 64 * distinct types per step) wave instructions.  The scatter
@@ -93,15 +96,29 @@ __global__ __launch_bounds__(kIdxThreads) void build_index_kernel(
   const int r0 = min(w * slice, M), r1 = min(r0 + slice, M);
   int* my = tab + w * Q1;
 
-  // pass 1: per-wave counts of each type in its slice.  Types are loaded kBatch
-  // steps at a time so that the loads overlap; the same pass checks whether
-  // the schedule is cyclic, tau[m] = (tau[0] + m) mod q for every row.
+  // Cyclic schedules (tau[m] = (o + m) mod q for every row, o = tau[0]) have a
+  // closed-form index; checking for one is a fully parallel pass.
   __shared__ int s_cyclic;
   const int t0 = M > 0 ? tau[0] : 0;
   if (tid == 0) s_cyclic = (M > 0 && t0 >= 0 && t0 < q) ? 1 : 0;
   __syncthreads();
-  bool cyc_ok = true;
-  for (int base = r0; base < r1; base += 64 * kBatch) {
+  if (s_cyclic) {
+    const int step = kIdxThreads % q;
+    int want = (t0 + tid) % q;  // (t0 + m) mod q for m = tid + kIdxThreads k
+    bool ok = true;
+    for (int m = tid; m < M; m += kIdxThreads) {
+      ok = ok && tau[m] == want;
+      want += step;
+      if (want >= q) want -= q;
+    }
+    if (!ok) s_cyclic = 0;
+  }
+  __syncthreads();
+  const bool cyclic = s_cyclic != 0;
+
+  // pass 1 (listed schedules): per-wave counts of each type in its slice.  Types
+  // are loaded kBatch steps at a time so that the loads overlap.
+  for (int base = r0; base < r1 && !cyclic; base += 64 * kBatch) {
     int tv[kBatch];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
@@ -116,23 +133,27 @@ __global__ __launch_bounds__(kIdxThreads) void build_index_kernel(
       if (m < r1) {
         const int v = tv[b];
         t = (v >= 0 && v < q) ? v : q;
-        cyc_ok = cyc_ok && v == int((int64_t(t0) + m) % q);
       }
       uint64_t left = __ballot(t >= 0);
       while (left) {
         const int leader = __builtin_ctzll(left);
-        const int tl = __shfl(t, leader, 64);
+        const int tl = __builtin_amdgcn_readlane(t, leader);
         const uint64_t mask = __ballot(t == tl);
         if (lane == leader) my[tl] += __popcll(mask);
         left &= ~mask;
       }
     }
   }
-  if (!cyc_ok) s_cyclic = 0;
   __syncthreads();
 
   // per type: exclusive prefix over waves (in place), total per type
   for (int t = tid; t < Q1; t += kIdxThreads) {
+    if (cyclic) {
+      // rows of type t are (t - t0) mod q + k q
+      const int start = (t - t0 + q) % q;
+      tot[t] = (t < q && start < M) ? (M - 1 - start) / q + 1 : 0;
+      continue;
+    }
     int run = 0;
     for (int ww = 0; ww < kIdxWaves; ++ww) {
       const int c = tab[ww * Q1 + t];
@@ -184,8 +205,17 @@ __global__ __launch_bounds__(kIdxThreads) void build_index_kernel(
   for (int x = tid; x < kIdxWaves * Q1; x += kIdxThreads) tab[x] += tot[x % Q1];
   __syncthreads();
 
-  // pass 2: stable scatter of row ids
-  for (int base = r0; base < r1; base += 64 * kBatch) {
+  if (cyclic) {
+    // closed-form row list: slot offsets[i] + k holds (i - t0) mod q + k q
+    for (int t = 0; t < q; ++t) {
+      const int start = (t - t0 + q) % q;
+      const int first = tot[t], cnt = tot[t + 1] - tot[t];
+      for (int k = tid; k < cnt; k += kIdxThreads) rows[first + k] = start + k * q;
+    }
+  }
+
+  // pass 2 (listed schedules): stable scatter of row ids
+  for (int base = r0; base < r1 && !cyclic; base += 64 * kBatch) {
     int tv[kBatch];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
@@ -205,7 +235,7 @@ __global__ __launch_bounds__(kIdxThreads) void build_index_kernel(
       const uint64_t below = (uint64_t(1) << lane) - 1;
       while (left) {
         const int leader = __builtin_ctzll(left);
-        const int tl = __shfl(t, leader, 64);
+        const int tl = __builtin_amdgcn_readlane(t, leader);
         const uint64_t mask = __ballot(t == tl);
         if (t == tl) rows[my[tl] + __popcll(mask & below)] = m;
         if (lane == leader) my[tl] += __popcll(mask);
