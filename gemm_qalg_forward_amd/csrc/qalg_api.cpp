@@ -119,6 +119,13 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
   }
   if (e != hipSuccess) return QALG_ERR_HIP;
 
+  if (dtype == QALG_BF16 && qalg::grad_persistent_supported(p)) {
+    // which of the two runs depends on the index (cyclic schedule or not),
+    // known only on the device: both are enqueued, the other returns at once
+    e = qalg::launch_grad_persistent_bf16(p, s);
+    if (e != hipSuccess) return QALG_ERR_HIP;
+    return hip_status(qalg::launch_tiled_bf16(p, s, /*skip_cyclic=*/true));
+  }
   e = dtype == QALG_BF16 ? qalg::launch_tiled_bf16(p, s) : qalg::launch_tiled_f32(p, s);
   return hip_status(e);
 }

@@ -60,31 +60,16 @@
 // are written as zero by the same launch.
 #include "qalg.h"
 #include "qalg_internal.h"
+#include "qalg_device.h"
 
 namespace qalg {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-#define LDS_AS __attribute__((address_space(3)))
+using namespace dev;
 
 constexpr int kBK = 32;       // contraction per k-step
 constexpr int kStages = 4;    // LDS stages: operands of 3 k-steps are in flight during a 4th
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <int BM_, int BN_>
 struct FwdCfg {
@@ -109,32 +94,6 @@ struct FwdCfg {
   static_assert(2 * DMA < 64, "vmcnt range");
 };
 
-// One 16-byte piece per lane from global memory straight into LDS: lane l's
-// piece lands at lds_addr + 16 l (gfx950 global_load_lds_dwordx4; lds_addr must
-// be wave-uniform; M0 holds it, and one wait state must separate the M0 write
-// from the load).  Written as inline assembly so that the compiler does not
-// treat every later LDS read as possibly depending on the copy; completion is
-// tracked by hand with wait_vmcnt before the barrier that publishes a stage.
-__device__ __forceinline__ void copy16_to_lds(const char* gbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory", "m0");
-}
-
-// Workgroup barrier ordering LDS only (the stage copies are waited for
-// explicitly; global stores need no ordering here).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Piece swizzles (see the file comment): X row r keeps piece c at c ^ ((r >> 1) & 3);
-// W row k keeps piece c at c ^ 2 * (k & 3).
-__device__ __forceinline__ int swz_x(int row) { return (row >> 1) & 3; }
-__device__ __forceinline__ int swz_w(int k) { return 2 * (k & 3); }
-
 struct FwdArgs {
   const char* X;
   const char* W;
@@ -146,24 +105,6 @@ struct FwdArgs {
   int n_ct;    // column tiles in all (q * cpg)
   int kts;     // k-steps per contraction segment (s / 32)
 };
-
-__device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {
-  const bf16x2 lo = __builtin_convertvector((f32x2){a, b}, bf16x2);
-  const bf16x2 hi = __builtin_convertvector((f32x2){c, d}, bf16x2);
-  return (u32x2){__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
-}
-
-__device__ __forceinline__ int find_group(const int32_t* tile_off, int q, int rt) {
-  int lo = 0, hi = q;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (tile_off[mid] <= rt)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  return lo;
-}
 
 // One output tile, decoded from its position in the tile order.
 struct Tile {

@@ -1,0 +1,566 @@
+// Persistent matrix-core gradients of the row-typed Q_q projection (bf16 in,
+// fp32 accumulate, bf16 out) for gfx950, cyclic schedules.
+//
+// Paper: arXiv 2609.32814, appendix B (eq 31-35).  For a row of type i:
+//   dx_i = sum_j dy_j W_ij^T,   dx_k = dy_k W_kk^T (k != i)             (eq 31-32)
+//   dW_jj += x_j^T dy_j (every row),  dW_ij += x_i^T dy_j (rows of type i)  (eq 33-35)
+// Section 5.3: separate gradient kernels with one owner per output element,
+// so every dW / dX element is written once and the result does not depend on
+// scheduling.
+//
+// Output tiles are GEMM tiles of 256 x BN (BN = 256, 192 or 128):
+//   dX  tile (256 rows of type i, BN columns of input group k):
+//         k == i: dY[rows, :] W[cols, :]^T     (contraction N: a "long" tile)
+//         k != i: dY[rows, g_k] W[cols, g_k]^T (contraction r)
+//   dW  tile (256 features of group b, BN columns of output group j):
+//         b == j: X[:, f]^T dY[:, cols] over all M rows   ("long")
+//         b != j: the same over the rows of type b         (M / q rows)
+// The dX operands are both contraction-contiguous (dY rows; W rows, i.e. the
+// transpose of the weight block is read in place); the dW operands are both
+// row-major over the contraction (token rows of X and dY), read into LDS as is
+// and turned into MFMA fragments with the transposing LDS read.
+//
+// Pipeline (shared with the forward): one workgroup per CU, operands copied
+// global -> LDS directly (global_load_lds_dwordx4), four 32-deep stages so
+// that copies run three k-steps ahead, the publishing barrier in the middle of
+// a k-step, v_mfma_f32_32x32x16_bf16 on 128x128 wave tiles, one RNE rounding.
+//
+// Work balance.  Long tiles carry q times the contraction of short ones.  The
+// tiles of each XCD (a contiguous share of the long and of the short tiles)
+// are dealt to its workgroups round robin, longs first; workgroups that got
+// one long tile fewer then take up to q short tiles each before the remaining
+// short tiles are dealt round robin, so every workgroup ends with nearly the
+// same number of k-steps.
+//
+// Rows of type i are the arithmetic progression (i - o) mod q + k q of a
+// cyclic schedule (detected by the index); a launch on any other schedule
+// returns at once and the register-staged gradient kernels run instead.
+#include "qalg.h"
+#include "qalg_device.h"
+#include "qalg_internal.h"
+
+namespace qalg {
+
+namespace {
+
+using namespace dev;
+
+constexpr int kBK = 32;      // contraction per k-step
+constexpr int kStages = 4;   // LDS stages
+
+template <int BM_, int BN_, bool A_KM_, bool B_KM_>
+struct GradCfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = 2, WGN = 2;
+  static constexpr bool A_KM = A_KM_, B_KM = B_KM_;  // contraction-major (else row-major over it)
+  static constexpr int THREADS = 256;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0 && FM >= 1 && FN >= 1, "wave tile");
+  static constexpr int A_BYTES = BM * kBK * 2, B_BYTES = BN * kBK * 2;
+  static constexpr int A_ROWB = BM * 2, B_ROWB = BN * 2;  // row-major layout: bytes per contraction row
+  static constexpr int A_NCH = BM / 8, B_NCH = BN / 8;    // 16-byte pieces per such row
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = kStages * STAGE;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole 1 KB copies per wave");
+  static constexpr int A_DMA = A_BYTES / 4096, B_DMA = B_BYTES / 4096;
+  static constexpr int DMA = A_DMA + B_DMA;
+  static_assert(2 * DMA < 64, "vmcnt range");
+};
+
+struct GradArgs {
+  const char* A;   // dX: dY;  dW: X
+  const char* B;   // dX: W;   dW: dY
+  char* C;         // dX: dX;  dW: dW
+  const int32_t* ws;
+  int64_t off_offsets, off_tiles;
+  int q, M, K, N, s, r;
+  int n_rt;        // dX: row tiles over all types (from the index; read on device)
+  int cpg;         // dX: column tiles per input group (s / BN); dW: per output group (r / BN)
+  int rpb;         // dW: row tiles per feature group (s / BM)
+};
+
+// One output tile.
+struct GTile {
+  int out_row0;    // dX: rank of the first row within its type;  dW: first feature
+  int type;        // dX: row type;  dW: type whose rows are contracted (-1: all rows)
+  int m_cnt;       // valid output rows (dX ragged row tiles)
+  int n0;          // first output column
+  int c0;          // dX: first contraction column (in N)
+  int nk;          // k-steps
+};
+
+// Tile list of a workgroup: a contiguous share of the long and of the short
+// tiles per XCD, dealt so that the k-steps per workgroup are balanced.
+struct TileDeal {
+  int lx0, lx1, sx0, sx1;   // this XCD's long and short tile ranges
+  int g, G;                 // slot inside the XCD, workgroups per XCD
+  int light, lg, G_light, E, base;
+  int phase, k;
+  __device__ void init(int n_long, int n_short, int t_long, int t_short, int xcd, int nx, int slot, int per_x) {
+    lx0 = int(int64_t(n_long) * xcd / nx);
+    lx1 = int(int64_t(n_long) * (xcd + 1) / nx);
+    sx0 = int(int64_t(n_short) * xcd / nx);
+    sx1 = int(int64_t(n_short) * (xcd + 1) / nx);
+    g = slot;
+    G = per_x;
+    const int nl = lx1 - lx0, ns = sx1 - sx0;
+    const int rem = nl % G;
+    light = rem != 0 && g >= rem;
+    G_light = rem != 0 ? G - rem : 0;
+    lg = g - rem;
+    const int e = t_short > 0 ? t_long / t_short : 0;
+    E = (rem != 0) ? min(e, ns / G_light) : 0;
+    base = G_light * E;
+    phase = 0;
+    k = 0;
+  }
+  // next tile: returns false at the end; *is_long and *idx (global class index) otherwise
+  __device__ bool next(bool* is_long, int* idx) {
+    if (phase == 0) {
+      const int i = lx0 + g + k * G;
+      if (i < lx1) {
+        ++k;
+        *is_long = true;
+        *idx = i;
+        return true;
+      }
+      phase = 1;
+      k = 0;
+    }
+    if (phase == 1) {
+      if (light && k < E) {
+        *is_long = false;
+        *idx = sx0 + lg + k * G_light;
+        ++k;
+        return true;
+      }
+      phase = 2;
+      k = 0;
+    }
+    const int i = sx0 + base + g + k * G;
+    if (i < sx1) {
+      ++k;
+      *is_long = false;
+      *idx = i;
+      return true;
+    }
+    return false;
+  }
+};
+
+__device__ __forceinline__ int find_group(const int* tile_off, int q, int rt) {
+  int lo = 0, hi = q;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tile_off[mid] <= rt)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// Tile decode.  dX long tiles: (row tile, column tile of the row's own group);
+// short: (row tile, other group, column tile); both in groups of 4 row tiles
+// by all columns, row tile fastest.  dW long tiles: (block b == j, row tile,
+// column tile); short: (b, j != b, row tile, column tile), b slowest.
+template <class C, Op OP>
+__device__ __forceinline__ GTile decode(const GradArgs& a, const int* s_off, const int* s_toff,
+                                        bool is_long, int idx) {
+  GTile t;
+  if constexpr (OP == Op::Dx) {
+    constexpr int G = 4;
+    const int ncol = is_long ? a.cpg : (a.q - 1) * a.cpg;
+    const int span = G * ncol;
+    const int grp = idx / span, w = idx - grp * span;
+    const int first_rt = grp * G;
+    const int gm = min(a.n_rt - first_rt, G);
+    const int rt = first_rt + w % gm, ct = w / gm;
+    const int i = find_group(s_toff, a.q, rt);
+    t.type = i;
+    t.out_row0 = (rt - s_toff[i]) * C::BM;
+    t.m_cnt = min(C::BM, (s_off[i + 1] - s_off[i]) - t.out_row0);
+    int k, cc;
+    if (is_long) {
+      k = i;
+      cc = ct;
+    } else {
+      const int kk = ct / a.cpg;
+      cc = ct - kk * a.cpg;
+      k = kk < i ? kk : kk + 1;
+    }
+    t.n0 = k * a.s + cc * C::BN;
+    t.c0 = is_long ? 0 : k * a.r;
+    t.nk = (is_long ? a.N : a.r) / kBK;
+  } else {
+    const int tpb = a.rpb * a.cpg;
+    const int blk = idx / tpb, w = idx - blk * tpb;
+    int b, j;
+    if (is_long) {
+      b = j = blk;
+    } else {
+      b = blk / (a.q - 1);
+      const int jj = blk - b * (a.q - 1);
+      j = jj < b ? jj : jj + 1;
+    }
+    const int rt = w % a.rpb, ct = w / a.rpb;
+    t.out_row0 = b * a.s + rt * C::BM;
+    t.m_cnt = C::BM;
+    t.n0 = j * a.r + ct * C::BN;
+    t.type = is_long ? -1 : b;
+    t.c0 = 0;
+    t.nk = (is_long ? a.M : a.M / a.q) / kBK;
+  }
+  return t;
+}
+
+template <class C, Op OP>
+__global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs a) {
+  constexpr int T = C::THREADS;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int32_t* ws = a.ws;
+  if (ws[1] != kIndexMagic || ws[2] != a.q || ws[3] != a.M) return;
+  const int cyc = ws[4];
+  if (cyc < 0) return;  // listed schedule: the register-staged kernel handles it
+  const int q = a.q;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  int* s_off = reinterpret_cast<int*>(smem + C::LDS_BYTES);
+  int* s_toff = s_off + (q + 1);
+  {
+    const int32_t* offsets = ws + a.off_offsets;
+    const int32_t* tile_off = ws + a.off_tiles + tile_height_slot(C::BM) * (q + 1);
+    for (int x = tid; x <= q; x += T) {
+      s_off[x] = offsets[x];
+      s_toff[x] = tile_off[x];
+    }
+  }
+  __syncthreads();
+  // first row of each type in the cyclic schedule
+  auto type_start = [&](int i) { return i >= cyc ? i - cyc : i - cyc + q; };
+
+  GradArgs g = a;
+  int n_long, n_short, t_long, t_short;
+  if constexpr (OP == Op::Dx) {
+    g.n_rt = s_toff[q];
+    n_long = g.n_rt * g.cpg;
+    n_short = g.n_rt * (q - 1) * g.cpg;
+    t_long = g.N / kBK;
+    t_short = g.r / kBK;
+  } else {
+    const int tpb = g.rpb * g.cpg;
+    n_long = q * tpb;
+    n_short = q * (q - 1) * tpb;
+    t_long = g.M / kBK;
+    t_short = g.M / q / kBK;
+  }
+
+  const int nx = gridDim.x >= 8 ? 8 : 1;
+  const int per_x = gridDim.x / nx;
+  const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx;
+  if (slot >= per_x) return;
+
+  const uint32_t a_ld = uint32_t(OP == Op::Dx ? g.N : g.K) * 2u;   // bytes per row of A
+  const uint32_t b_ld = uint32_t(g.N) * 2u;                         // bytes per row of B (W or dY)
+  const uint32_t c_ld = uint32_t(OP == Op::Dx ? g.K : g.N) * 2u;    // bytes per row of C
+
+  // ---------------- copy cursor ----------------
+  TileDeal dcopy;
+  dcopy.init(n_long, n_short, t_long, t_short, xcd, nx, slot, per_x);
+  bool l_long;
+  int l_idx;
+  if (!dcopy.next(&l_long, &l_idx)) return;
+  GTile lt = decode<C, OP>(g, s_off, s_toff, l_long, l_idx);
+  int lk = 0;
+  bool more = true;
+
+  // per-lane copy slots: KM operand -> (tile row, swizzled piece); RM operand -> (contraction row, piece)
+  int a_r[C::A_DMA], a_c[C::A_DMA], b_r[C::B_DMA], b_c[C::B_DMA];
+#pragma unroll
+  for (int u = 0; u < C::A_DMA; ++u) {
+    const int sl = (wid * C::A_DMA + u) * 64 + lane;
+    if constexpr (C::A_KM) {
+      a_r[u] = sl >> 2;
+      a_c[u] = (sl & 3) ^ swz_x(sl >> 2);
+    } else {
+      a_r[u] = sl / C::A_NCH;
+      a_c[u] = (sl - (sl / C::A_NCH) * C::A_NCH) ^ swz_w(sl / C::A_NCH);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < C::B_DMA; ++u) {
+    const int sl = (wid * C::B_DMA + u) * 64 + lane;
+    if constexpr (C::B_KM) {
+      b_r[u] = sl >> 2;
+      b_c[u] = (sl & 3) ^ swz_x(sl >> 2);
+    } else {
+      b_r[u] = sl / C::B_NCH;
+      b_c[u] = (sl - (sl / C::B_NCH) * C::B_NCH) ^ swz_w(sl / C::B_NCH);
+    }
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(smem)));
+
+  auto issue_copies = [&](int stage) {
+    const uint32_t S = lds0 + uint32_t(stage * C::STAGE);
+    if constexpr (OP == Op::Dx) {
+      // A = dY rows of type lt.type (tile rows), B = W rows n0.. (tile rows); contraction columns kc..
+      const int kc = lt.c0 + lk * kBK;
+      const int start = type_start(lt.type);
+#pragma unroll
+      for (int u = 0; u < C::A_DMA; ++u) {
+        const int row = start + (lt.out_row0 + min(a_r[u], lt.m_cnt - 1)) * q;
+        copy16_to_lds(g.A, uint32_t(row) * a_ld + uint32_t(kc + a_c[u] * 8) * 2u,
+                      S + uint32_t((wid * C::A_DMA + u) * 1024));
+      }
+#pragma unroll
+      for (int u = 0; u < C::B_DMA; ++u)
+        copy16_to_lds(g.B, uint32_t(lt.n0 + b_r[u]) * b_ld + uint32_t(kc + b_c[u] * 8) * 2u,
+                      S + uint32_t(C::A_BYTES + (wid * C::B_DMA + u) * 1024));
+    } else {
+      // contraction rows: all rows (long tiles) or the rows of type lt.type
+      const int k0 = lk * kBK;
+      const int rbase = lt.type < 0 ? k0 : type_start(lt.type) + k0 * q;
+      const int rstep = lt.type < 0 ? 1 : q;
+#pragma unroll
+      for (int u = 0; u < C::A_DMA; ++u) {
+        const int row = rbase + a_r[u] * rstep;
+        copy16_to_lds(g.A, uint32_t(row) * a_ld + uint32_t(lt.out_row0 + a_c[u] * 8) * 2u,
+                      S + uint32_t((wid * C::A_DMA + u) * 1024));
+      }
+#pragma unroll
+      for (int u = 0; u < C::B_DMA; ++u) {
+        const int row = rbase + b_r[u] * rstep;
+        copy16_to_lds(g.B, uint32_t(row) * b_ld + uint32_t(lt.n0 + b_c[u] * 8) * 2u,
+                      S + uint32_t(C::A_BYTES + (wid * C::B_DMA + u) * 1024));
+      }
+    }
+    if (++lk >= lt.nk) {
+      if (dcopy.next(&l_long, &l_idx)) {
+        lt = decode<C, OP>(g, s_off, s_toff, l_long, l_idx);
+        lk = 0;
+      } else {
+        more = false;
+      }
+    }
+  };
+
+  // ---------------- fragment reads ----------------
+  const int wm = wid / C::WGN, wn = wid % C::WGN;
+  const int l32 = lane & 31, lhi = lane >> 5;
+  // contraction-major operand: 128-bit read of row l32, piece 2*ks + lhi
+  auto km_rd = [&](int w0, int ks) { return (w0 + l32) * 64 + (((2 * ks + lhi) ^ swz_x(l32)) << 4); };
+  // row-major operand with rows of rowb bytes: per-lane offsets of the two
+  // transposing reads, by parity of the fragment's 32-column block index
+  auto rm_rd = [&](int rowb, int par) {
+    const int gq = lane >> 4, t = lane & 15;
+    const int k_l = 8 * (gq >> 1) + (t >> 2);
+    const int f = swz_w(k_l);
+    const int r2 = 2 * (gq & 1) + ((t & 3) >> 1);
+    const int lo = ((r2 ^ (f & 2)) << 4) + 8 * (t & 1) + k_l * rowb;
+    const int dm = (f >> 2) ? 64 : 0;
+    return par == 0 ? lo + dm : lo - dm;
+  };
+  int a_rd[2], b_rd[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    a_rd[x] = C::A_KM ? km_rd(wm * C::WTM, x) : rm_rd(C::A_ROWB, x);
+    b_rd[x] = C::A_BYTES + (C::B_KM ? km_rd(wn * C::WTN, x) : rm_rd(C::B_ROWB, x));
+  }
+  const int am0 = wm * (C::WTM / 32), bm0 = wn * (C::WTN / 32);
+
+  f32x16 acc[C::FM][C::FN];
+  bf16x8 fa0[C::FM], fb0[C::FN], fa1[C::FM], fb1[C::FN];
+  auto load_frags = [&](int stage, int ks, bf16x8 (&fa)[C::FM], bf16x8 (&fb)[C::FN]) {
+    const char* S = smem + stage * C::STAGE;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      if constexpr (C::A_KM) {
+        fa[fm] = *reinterpret_cast<const bf16x8*>(S + a_rd[ks] + fm * 32 * 64);
+      } else {
+        const int m = am0 + fm;
+        const char* p = S + a_rd[m & 1] + 64 * m + 16 * ks * C::A_ROWB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * C::A_ROWB));
+        fa[fm] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      if constexpr (C::B_KM) {
+        fb[fn] = *reinterpret_cast<const bf16x8*>(S + b_rd[ks] + fn * 32 * 64);
+      } else {
+        const int m = bm0 + fn;
+        const char* p = S + b_rd[m & 1] + 64 * m + 16 * ks * C::B_ROWB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * C::B_ROWB));
+        fb[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+  };
+  auto mfmas = [&](const bf16x8 (&fa)[C::FM], const bf16x8 (&fb)[C::FN]) {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], acc[fm][fn], 0, 0, 0);
+  };
+
+  // ---------------- pipeline (as in the forward) ----------------
+  int issued = 0;
+  for (int st = 0; st < kStages - 1 && more; ++st) {
+    issue_copies(st);
+    ++issued;
+  }
+  if (issued >= 3)
+    wait_vmcnt<2 * C::DMA>();
+  else if (issued == 2)
+    wait_vmcnt<C::DMA>();
+  else
+    wait_vmcnt<0>();
+  lds_barrier();
+  load_frags(0, 0, fa0, fb0);
+
+  TileDeal dcomp;
+  dcomp.init(n_long, n_short, t_long, t_short, xcd, nx, slot, per_x);
+  bool c_long;
+  int c_idx;
+  dcomp.next(&c_long, &c_idx);
+  GTile ct = decode<C, OP>(g, s_off, s_toff, c_long, c_idx);
+  int step = 0;
+  for (;;) {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = (f32x16){};
+
+    for (int ck = 0; ck < ct.nk; ++ck) {
+      const int stage = step & (kStages - 1);
+      load_frags(stage, 1, fa1, fb1);
+      mfmas(fa0, fb0);
+      const int ahead = issued - step - 2;
+      if (ahead >= 1)
+        wait_vmcnt<C::DMA>();
+      else
+        wait_vmcnt<0>();
+      lds_barrier();
+      if (more) {
+        issue_copies((step + kStages - 1) & (kStages - 1));
+        ++issued;
+      }
+      if (step + 1 < issued) load_frags((step + 1) & (kStages - 1), 0, fa0, fb0);
+      mfmas(fa1, fb1);
+      ++step;
+    }
+
+    // epilogue: one rounding of each fp32 sum, 8-byte stores of 4 columns
+    const int ostart = OP == Op::Dx ? type_start(ct.type) : 0;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int ml = wm * C::WTM + fm * 32 + l32;
+      if (ml < ct.m_cnt) {
+        const int orow = OP == Op::Dx ? ostart + (ct.out_row0 + ml) * q : ct.out_row0 + ml;
+        char* crow = g.C + (uint32_t(orow) * c_ld + uint32_t(ct.n0 + wn * C::WTN + lhi * 4) * 2u);
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            const f32x16& v = acc[fm][fn];
+            *reinterpret_cast<u32x2*>(crow + (fn * 32 + gg * 8) * 2) =
+                pack4_bf16(v[4 * gg], v[4 * gg + 1], v[4 * gg + 2], v[4 * gg + 3]);
+          }
+        }
+      }
+    }
+    if (!dcomp.next(&c_long, &c_idx)) break;
+    ct = decode<C, OP>(g, s_off, s_toff, c_long, c_idx);
+  }
+}
+
+template <int BN>
+using DxCfg = GradCfg<256, BN, true, true>;
+template <int BN>
+using DwCfg = GradCfg<256, BN, false, false>;
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+template <class C, Op OP>
+hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
+  static bool attr_set = false;
+  const int lds = C::LDS_BYTES + int(sizeof(int)) * 2 * (QALG_MAX_Q + 1);
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grad_persistent_kernel<C, OP>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  GradArgs a{};
+  a.A = static_cast<const char*>(p.A);
+  a.B = static_cast<const char*>(p.B);
+  a.C = static_cast<char*>(p.C);
+  a.ws = p.ws;
+  const WsLayout L = ws_layout(p.q, p.M);
+  a.off_offsets = L.offsets;
+  a.off_tiles = L.tile_off;
+  a.q = p.q;
+  a.M = int(p.M);
+  a.K = int(p.K);
+  a.N = int(p.N);
+  a.s = int(p.K / p.q);
+  a.r = int(p.N / p.q);
+  if (OP == Op::Dx) {
+    a.cpg = a.s / C::BN;
+    a.rpb = 0;
+  } else {
+    a.cpg = a.r / C::BN;
+    a.rpb = a.s / C::BM;
+  }
+  int grid = cu_count();
+  grid = grid >= 8 ? grid / 8 * 8 : grid;
+  const size_t shm = C::LDS_BYTES + sizeof(int) * 2 * (p.q + 1);
+  hipLaunchKernelGGL((grad_persistent_kernel<C, OP>), dim3(grid), dim3(C::THREADS), shm, s, a);
+  return hipGetLastError();
+}
+
+int pick_bn(int64_t w) { return w % 256 == 0 ? 256 : w % 192 == 0 ? 192 : w % 128 == 0 ? 128 : 0; }
+
+}  // namespace
+
+bool grad_persistent_supported(const ProblemDesc& p) {
+  if (p.E != 1 || (p.op != Op::Dx && p.op != Op::Dw)) return false;
+  const int64_t s = p.K / p.q, r = p.N / p.q;
+  const int64_t lim = int64_t(1) << 31;
+  if (p.M * p.K >= lim || p.K * p.N >= lim || p.M * p.N >= lim) return false;
+  if (p.op == Op::Dx) {
+    // rows of a type in 256-row tiles; columns of an input group in BN tiles;
+    // contraction lengths N and r in whole k-steps
+    return (p.M + p.q - 1) / p.q >= 128 && pick_bn(s) != 0 && r % kBK == 0;
+  }
+  // features of a group in 256-row tiles, output group columns in BN tiles,
+  // every type's rows (M / q of a cyclic schedule) in whole k-steps
+  return s % 256 == 0 && pick_bn(r) != 0 && p.M % (int64_t(kBK) * p.q) == 0 && p.M >= int64_t(kBK) * p.q;
+}
+
+hipError_t launch_grad_persistent_bf16(const ProblemDesc& p, hipStream_t s) {
+  const int bn = pick_bn(p.op == Op::Dx ? p.K / p.q : p.N / p.q);
+  if (p.op == Op::Dx) {
+    if (bn == 256) return launch_grad<DxCfg<256>, Op::Dx>(p, s);
+    if (bn == 192) return launch_grad<DxCfg<192>, Op::Dx>(p, s);
+    return launch_grad<DxCfg<128>, Op::Dx>(p, s);
+  }
+  if (bn == 256) return launch_grad<DwCfg<256>, Op::Dw>(p, s);
+  if (bn == 192) return launch_grad<DwCfg<192>, Op::Dw>(p, s);
+  return launch_grad<DwCfg<128>, Op::Dw>(p, s);
+}
+
+}  // namespace qalg

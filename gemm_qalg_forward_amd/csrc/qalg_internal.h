@@ -77,12 +77,18 @@ struct ProblemDesc {
   int E;              // problems (experts); operands packed back to back
 };
 
-hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s);
+// skip_cyclic: the kernel returns at once when the index says the schedule is
+// cyclic (a persistent kernel launched beside it covers that case).
+hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s, bool skip_cyclic = false);
 hipError_t launch_tiled_f32(const ProblemDesc& p, hipStream_t s);
 hipError_t launch_small_m_bf16(const ProblemDesc& p, hipStream_t s);
 bool small_m_supported(const ProblemDesc& p);
 // Persistent 256x256-tile forward (bf16, one problem); zeroes rows of out-of-range type itself.
 bool fwd_persistent_supported(const ProblemDesc& p);
 hipError_t launch_fwd_persistent_bf16(const ProblemDesc& p, hipStream_t s);
+// Persistent 256-row-tile dX / dW (bf16, one problem) for cyclic schedules; a
+// launch on any other schedule returns at once.
+bool grad_persistent_supported(const ProblemDesc& p);
+hipError_t launch_grad_persistent_bf16(const ProblemDesc& p, hipStream_t s);
 
 }  // namespace qalg

@@ -70,6 +70,7 @@ struct Args {
   int ct_per_group;                  // column tiles per output group
   int n_ct;                          // all column tiles (q * ct_per_group)
   int tm_dw, tn_dw;                  // dW: tiles per block along rows / columns
+  int skip_cyclic;                   // return at once when the index says the schedule is cyclic
 };
 
 __device__ __forceinline__ int swz(int row, int chunk, int kch) {
@@ -127,6 +128,8 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
 
   // an index of another (q, M) is never trusted: no row id is read from it
   if (ws[1] != kIndexMagic || ws[2] != q || ws[3] != a.M) return;
+  // cyclic schedules are handled by the persistent kernel launched beside this one
+  if (a.skip_cyclic && ws[4] >= 0) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / C::WGN, wn = wid % C::WGN;
@@ -589,8 +592,9 @@ dim3 grid_for(const ProblemDesc& p, const Args& a, int bm) {
 }
 
 template <Op OP, class C>
-hipError_t launch_cfg(const ProblemDesc& p, hipStream_t s) {
-  const Args a = make_args(p, C::BM, C::BN);
+hipError_t launch_cfg(const ProblemDesc& p, hipStream_t s, bool skip_cyclic) {
+  Args a = make_args(p, C::BM, C::BN);
+  a.skip_cyclic = skip_cyclic ? 1 : 0;
   const dim3 g = grid_for(p, a, C::BM);
   if (g.x == 0) return hipSuccess;
   hipLaunchKernelGGL((tiled_bf16_kernel<OP, C>), g, dim3(C::THREADS), 0, s, a);
@@ -603,21 +607,21 @@ using Cfg32 = TileCfg<32, 64, 64, 1, 2>;
 
 }  // namespace
 
-hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s) {
+hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s, bool skip_cyclic) {
   // Row-tile height from the rows per type (tiles never straddle types).
   const int64_t per_type = p.op == Op::Dw ? p.K / p.q : (p.M + p.q - 1) / p.q;
   switch (p.op) {
     case Op::Fwd:
-      if (per_type >= 128) return launch_cfg<Op::Fwd, Cfg128>(p, s);
-      if (per_type >= 48) return launch_cfg<Op::Fwd, Cfg64>(p, s);
-      return launch_cfg<Op::Fwd, Cfg32>(p, s);
+      if (per_type >= 128) return launch_cfg<Op::Fwd, Cfg128>(p, s, skip_cyclic);
+      if (per_type >= 48) return launch_cfg<Op::Fwd, Cfg64>(p, s, skip_cyclic);
+      return launch_cfg<Op::Fwd, Cfg32>(p, s, skip_cyclic);
     case Op::Dx:
-      if (per_type >= 128) return launch_cfg<Op::Dx, Cfg128>(p, s);
-      if (per_type >= 48) return launch_cfg<Op::Dx, Cfg64>(p, s);
-      return launch_cfg<Op::Dx, Cfg32>(p, s);
+      if (per_type >= 128) return launch_cfg<Op::Dx, Cfg128>(p, s, skip_cyclic);
+      if (per_type >= 48) return launch_cfg<Op::Dx, Cfg64>(p, s, skip_cyclic);
+      return launch_cfg<Op::Dx, Cfg32>(p, s, skip_cyclic);
     case Op::Dw:
-      if (per_type >= 128) return launch_cfg<Op::Dw, Cfg128>(p, s);
-      return launch_cfg<Op::Dw, Cfg64>(p, s);
+      if (per_type >= 128) return launch_cfg<Op::Dw, Cfg128>(p, s, skip_cyclic);
+      return launch_cfg<Op::Dw, Cfg64>(p, s, skip_cyclic);
   }
   return hipErrorInvalidValue;
 }

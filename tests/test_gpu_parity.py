@@ -26,6 +26,8 @@ SHAPES = [
     (5000, 512, 1024, 4, "random", 0, 37),   # persistent 256x256 path: ragged row tiles, bad types
     (4099, 768, 768, 3, "cyclic", 2, 0),     # persistent path, odd q, type offset
     (2600, 1024, 2304, 4, "cyclic", 0, 0),   # persistent 256x192 tiles (r = 576 = 3 x 192)
+    (2048, 1024, 1536, 4, "cyclic", 1, 0),   # persistent dX and dW (dW tiles 256x192)
+    (4096, 2048, 2048, 8, "cyclic", 3, 0),   # persistent dX and dW (256x256), long/short balance
 ]
 
 
@@ -180,12 +182,14 @@ def test_block_diagonal_bank_is_type_independent():
     assert torch.equal(Y1, Y2)
 
 
-def test_runs_are_bitwise_reproducible():
+@pytest.mark.parametrize("kind", ["random", "cyclic"])
+def test_runs_are_bitwise_reproducible(kind):
+    """Every output element has one owner: repeated runs are bitwise equal (both kernel families)."""
     torch = torch_cuda()
-    q, K, N, M = 8, 1024, 2048, 4096
+    q, K, N, M = 8, 2048, 2048, 4096
     X, W, dY = _inputs(M, K, N, "bf16", 31)
     Xd, Wd, dYd = to_dev(X), to_dev(W), to_dev(dY)
-    td = tau_dev(make_tau("random", M, q, seed=9))
+    td = tau_dev(make_tau(kind, M, q, seed=9, offset=5))
     outs = []
     for _ in range(2):
         ws = Q.workspace(q, M)
