@@ -34,7 +34,10 @@
 // k-steps step..step+3, so copies run three k-steps ahead of the matrix
 // cores.  The barrier that publishes the next stage sits in the middle of a
 // k-step: the first 16 contraction values' MFMAs cover it, and the next
-// k-step's first fragments are read while the second half's MFMAs run.
+// k-step's first fragments are read while the second half's MFMAs run.  Inside
+// each half the 16 MFMAs are interleaved one by one with the fragment reads and
+// the copies (pinned by scheduling barriers), so that the matrix cores see a
+// steady stream instead of bursts of other instructions.
 //
 // LDS layouts (both bank-conflict free for the patterns used):
 //  * X tile: row r of the tile keeps its four 16-byte pieces (8 contraction
@@ -239,17 +242,22 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   take_rows();
   if (lL + per_x < c_hi) prefetch_rows(decode_tile<C>(a, s_off, s_toff, n_rt, lL + per_x));
   bool more = true;  // the copy cursor still has k-steps
-  auto issue_copies = [&](int stage) {
+  // copy cursor split in three so that the copies can be interleaved with MFMAs
+  uint32_t cp_x = 0, cp_w = 0;  // per-step byte offsets of the X and W pieces
+  auto prep_copies = [&]() {
     const int sg = lk >= a.kts ? 1 : 0;
     const int kcol = (sg ? lt.seg1 : lt.seg0) + (lk - sg * a.kts) * kBK;
+    cp_x = uint32_t(kcol) * 2u;
+    cp_w = uint32_t(kcol) * n_bytes + uint32_t(lt.n0) * 2u;
+  };
+  auto copy_u = [&](int stage, int u) {
     const uint32_t S = lds0 + uint32_t(stage * C::STAGE);
-#pragma unroll
-    for (int u = 0; u < C::A_DMA; ++u)
-      copy16_to_lds(a.X, a_src[u] + uint32_t(kcol) * 2u, S + uint32_t((wid * C::A_DMA + u) * 1024));
-    const uint32_t wbase = uint32_t(kcol) * n_bytes + uint32_t(lt.n0) * 2u;
-#pragma unroll
-    for (int u = 0; u < C::B_DMA; ++u)
-      copy16_to_lds(a.W, wbase + b_src[u], S + uint32_t(C::A_BYTES + (wid * C::B_DMA + u) * 1024));
+    if (u < C::A_DMA)
+      copy16_to_lds(a.X, a_src[u] + cp_x, S + uint32_t((wid * C::A_DMA + u) * 1024));
+    else
+      copy16_to_lds(a.W, cp_w + b_src[u - C::A_DMA], S + uint32_t(C::A_BYTES + (wid * C::B_DMA + (u - C::A_DMA)) * 1024));
+  };
+  auto advance_copies = [&]() {
     if (++lk >= lt.nk) {
       lL += per_x;
       if (lL >= c_hi) {
@@ -261,6 +269,12 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
         if (lL + per_x < c_hi) prefetch_rows(decode_tile<C>(a, s_off, s_toff, n_rt, lL + per_x));
       }
     }
+  };
+  auto issue_copies = [&](int stage) {
+    prep_copies();
+#pragma unroll
+    for (int u = 0; u < C::DMA; ++u) copy_u(stage, u);
+    advance_copies();
   };
 
   // ---------------- fragment reads ----------------
@@ -290,6 +304,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   f32x16 acc[C::FM][C::FN];
   // fragments of the two 16-wide halves of a k-step (registers double buffered)
   bf16x8 fa0[C::FM], fb0[C::FN], fa1[C::FM], fb1[C::FN];
+  auto read_a = [&](int stage, int ks, int fm) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(smem + stage * C::STAGE + a_rd[ks] + fm * 32 * 64);
+  };
+  auto read_b = [&](int stage, int ks, int fn) -> bf16x8 {
+    const int m = m0 + fn;
+    const char* p = smem + stage * C::STAGE + b_rd[m & 1] + 64 * m + 16 * ks * C::ROWB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * C::ROWB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   auto load_frags = [&](int stage, int ks, bf16x8 (&fa)[C::FM], bf16x8 (&fb)[C::FN]) {
     const char* S = smem + stage * C::STAGE;
 #pragma unroll
@@ -347,23 +371,51 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
 
     for (int ck = 0; ck < ct.nk; ++ck) {
       const int stage = step & (kStages - 1);
-      load_frags(stage, 1, fa1, fb1);
-      mfmas(fa0, fb0);
-      // publish stage step+1: this wave's copies of it have landed (copies of
-      // later k-steps may still be in flight), then everyone's have
-      const int ahead = issued - step - 2;  // k-steps issued after step+1 (0..1)
+      // first half: MFMAs on fragments 0 interleaved with the reads of fragments 1
+      static_assert(C::FM + C::FN <= C::FM * C::FN, "fragment reads fit the first half");
+#pragma unroll
+      for (int x = 0; x < C::FM * C::FN; ++x) {
+        const int fm = x / C::FN, fn = x % C::FN;
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[fn], fa0[fm], acc[fm][fn], 0, 0, 0);
+        if (x < C::FM) fa1[x] = read_a(stage, 1, x);
+        else if (x < C::FM + C::FN) fb1[x - C::FM] = read_b(stage, 1, x - C::FM);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int ahead = issued - step - 2;
       if (ahead >= 1)
         wait_vmcnt<C::DMA>();
       else
         wait_vmcnt<0>();
       lds_barrier();
-      // every wave is past k-step step-1: its stage takes the copies of step+3
-      if (more) {
-        issue_copies((step + kStages - 1) & (kStages - 1));
+      const bool cp = more;
+      const int cstage = (step + kStages - 1) & (kStages - 1);
+      if (cp) prep_copies();
+      const bool rd = step + 1 < issued + (cp ? 1 : 0);
+      const int nstage = (step + 1) & (kStages - 1);
+      // second half: MFMAs on fragments 1 interleaved with the copies of k-step
+      // step+3 and the reads of the next k-step's fragments 0
+      // (narrow tiles have fewer MFMAs than copies and reads: the slots past
+      // the last MFMA carry the rest)
+      constexpr int kSlots = C::FM * C::FN > C::DMA + C::FM + C::FN ? C::FM * C::FN : C::DMA + C::FM + C::FN;
+#pragma unroll
+      for (int x = 0; x < kSlots; ++x) {
+        if (x < C::FM * C::FN) {
+          const int fm = x / C::FN, fn = x % C::FN;
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[fn], fa1[fm], acc[fm][fn], 0, 0, 0);
+        }
+        if (x < C::DMA) {
+          if (cp) copy_u(cstage, x);
+        } else if (x - C::DMA < C::FM) {
+          if (rd) fa0[x - C::DMA] = read_a(nstage, 0, x - C::DMA);
+        } else if (x - C::DMA - C::FM < C::FN) {
+          if (rd) fb0[x - C::DMA - C::FM] = read_b(nstage, 0, x - C::DMA - C::FM);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (cp) {
+        advance_copies();
         ++issued;
       }
-      if (step + 1 < issued) load_frags((step + 1) & (kStages - 1), 0, fa0, fb0);
-      mfmas(fa1, fb1);
       ++step;
     }
 

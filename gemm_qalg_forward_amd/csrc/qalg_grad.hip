@@ -23,7 +23,8 @@
 // Pipeline (shared with the forward): one workgroup per CU, operands copied
 // global -> LDS directly (global_load_lds_dwordx4), four 32-deep stages so
 // that copies run three k-steps ahead, the publishing barrier in the middle of
-// a k-step, v_mfma_f32_32x32x16_bf16 on 128x128 wave tiles, one RNE rounding.
+// a k-step, MFMAs interleaved one by one with fragment reads and copies,
+// v_mfma_f32_32x32x16_bf16 on 128x128 wave tiles, one RNE rounding.
 //
 // Work balance.  Long tiles carry q times the contraction of short ones.  The
 // tiles of each XCD (a contiguous share of the long and of the short tiles)
@@ -302,40 +303,48 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(smem)));
 
-  auto issue_copies = [&](int stage) {
+  // copy cursor in three parts (per-step offsets, one copy, advance) so that
+  // the copies can be interleaved with MFMAs
+  int cp_kc = 0, cp_start = 0, cp_rbase = 0, cp_rstep = 1;
+  auto prep_copies = [&]() {
+    if constexpr (OP == Op::Dx) {
+      cp_kc = lt.c0 + lk * kBK;
+      cp_start = type_start(lt.type);
+    } else {
+      const int k0 = lk * kBK;
+      cp_rbase = lt.type < 0 ? k0 : type_start(lt.type) + k0 * q;
+      cp_rstep = lt.type < 0 ? 1 : q;
+    }
+  };
+  auto copy_u = [&](int stage, int u) {
     const uint32_t S = lds0 + uint32_t(stage * C::STAGE);
     if constexpr (OP == Op::Dx) {
-      // A = dY rows of type lt.type (tile rows), B = W rows n0.. (tile rows); contraction columns kc..
-      const int kc = lt.c0 + lk * kBK;
-      const int start = type_start(lt.type);
-#pragma unroll
-      for (int u = 0; u < C::A_DMA; ++u) {
-        const int row = start + (lt.out_row0 + min(a_r[u], lt.m_cnt - 1)) * q;
-        copy16_to_lds(g.A, uint32_t(row) * a_ld + uint32_t(kc + a_c[u] * 8) * 2u,
+      // A = dY rows of type lt.type (tile rows), B = W rows n0.. (tile rows);
+      // contraction columns cp_kc..
+      if (u < C::A_DMA) {
+        const int row = cp_start + (lt.out_row0 + min(a_r[u], lt.m_cnt - 1)) * q;
+        copy16_to_lds(g.A, uint32_t(row) * a_ld + uint32_t(cp_kc + a_c[u] * 8) * 2u,
                       S + uint32_t((wid * C::A_DMA + u) * 1024));
+      } else {
+        const int v = u - C::A_DMA;
+        copy16_to_lds(g.B, uint32_t(lt.n0 + b_r[v]) * b_ld + uint32_t(cp_kc + b_c[v] * 8) * 2u,
+                      S + uint32_t(C::A_BYTES + (wid * C::B_DMA + v) * 1024));
       }
-#pragma unroll
-      for (int u = 0; u < C::B_DMA; ++u)
-        copy16_to_lds(g.B, uint32_t(lt.n0 + b_r[u]) * b_ld + uint32_t(kc + b_c[u] * 8) * 2u,
-                      S + uint32_t(C::A_BYTES + (wid * C::B_DMA + u) * 1024));
     } else {
       // contraction rows: all rows (long tiles) or the rows of type lt.type
-      const int k0 = lk * kBK;
-      const int rbase = lt.type < 0 ? k0 : type_start(lt.type) + k0 * q;
-      const int rstep = lt.type < 0 ? 1 : q;
-#pragma unroll
-      for (int u = 0; u < C::A_DMA; ++u) {
-        const int row = rbase + a_r[u] * rstep;
+      if (u < C::A_DMA) {
+        const int row = cp_rbase + a_r[u] * cp_rstep;
         copy16_to_lds(g.A, uint32_t(row) * a_ld + uint32_t(lt.out_row0 + a_c[u] * 8) * 2u,
                       S + uint32_t((wid * C::A_DMA + u) * 1024));
-      }
-#pragma unroll
-      for (int u = 0; u < C::B_DMA; ++u) {
-        const int row = rbase + b_r[u] * rstep;
-        copy16_to_lds(g.B, uint32_t(row) * b_ld + uint32_t(lt.n0 + b_c[u] * 8) * 2u,
-                      S + uint32_t(C::A_BYTES + (wid * C::B_DMA + u) * 1024));
+      } else {
+        const int v = u - C::A_DMA;
+        const int row = cp_rbase + b_r[v] * cp_rstep;
+        copy16_to_lds(g.B, uint32_t(row) * b_ld + uint32_t(lt.n0 + b_c[v] * 8) * 2u,
+                      S + uint32_t(C::A_BYTES + (wid * C::B_DMA + v) * 1024));
       }
     }
+  };
+  auto advance_copies = [&]() {
     if (++lk >= lt.nk) {
       if (dcopy.next(&l_long, &l_idx)) {
         lt = decode<C, OP>(g, s_off, s_toff, l_long, l_idx);
@@ -344,6 +353,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
         more = false;
       }
     }
+  };
+  auto issue_copies = [&](int stage) {
+    prep_copies();
+#pragma unroll
+    for (int u = 0; u < C::DMA; ++u) copy_u(stage, u);
+    advance_copies();
   };
 
   // ---------------- fragment reads ----------------
@@ -372,32 +387,35 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
 
   f32x16 acc[C::FM][C::FN];
   bf16x8 fa0[C::FM], fb0[C::FN], fa1[C::FM], fb1[C::FN];
-  auto load_frags = [&](int stage, int ks, bf16x8 (&fa)[C::FM], bf16x8 (&fb)[C::FN]) {
+  auto read_a = [&](int stage, int ks, int fm) -> bf16x8 {
     const char* S = smem + stage * C::STAGE;
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-      if constexpr (C::A_KM) {
-        fa[fm] = *reinterpret_cast<const bf16x8*>(S + a_rd[ks] + fm * 32 * 64);
-      } else {
-        const int m = am0 + fm;
-        const char* p = S + a_rd[m & 1] + 64 * m + 16 * ks * C::A_ROWB;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * C::A_ROWB));
-        fa[fm] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
+    if constexpr (C::A_KM) {
+      return *reinterpret_cast<const bf16x8*>(S + a_rd[ks] + fm * 32 * 64);
+    } else {
+      const int m = am0 + fm;
+      const char* p = S + a_rd[m & 1] + 64 * m + 16 * ks * C::A_ROWB;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * C::A_ROWB));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn) {
-      if constexpr (C::B_KM) {
-        fb[fn] = *reinterpret_cast<const bf16x8*>(S + b_rd[ks] + fn * 32 * 64);
-      } else {
-        const int m = bm0 + fn;
-        const char* p = S + b_rd[m & 1] + 64 * m + 16 * ks * C::B_ROWB;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * C::B_ROWB));
-        fb[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
+  };
+  auto read_b = [&](int stage, int ks, int fn) -> bf16x8 {
+    const char* S = smem + stage * C::STAGE;
+    if constexpr (C::B_KM) {
+      return *reinterpret_cast<const bf16x8*>(S + b_rd[ks] + fn * 32 * 64);
+    } else {
+      const int m = bm0 + fn;
+      const char* p = S + b_rd[m & 1] + 64 * m + 16 * ks * C::B_ROWB;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * C::B_ROWB));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
+  };
+  auto load_frags = [&](int stage, int ks, bf16x8 (&fa)[C::FM], bf16x8 (&fb)[C::FN]) {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) fa[fm] = read_a(stage, ks, fm);
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) fb[fn] = read_b(stage, ks, fn);
   };
   auto mfmas = [&](const bf16x8 (&fa)[C::FM], const bf16x8 (&fb)[C::FN]) {
 #pragma unroll
@@ -437,20 +455,51 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
 
     for (int ck = 0; ck < ct.nk; ++ck) {
       const int stage = step & (kStages - 1);
-      load_frags(stage, 1, fa1, fb1);
-      mfmas(fa0, fb0);
+      // first half: MFMAs on fragments 0 interleaved with the reads of fragments 1
+      static_assert(C::FM + C::FN <= C::FM * C::FN, "fragment reads fit the first half");
+#pragma unroll
+      for (int x = 0; x < C::FM * C::FN; ++x) {
+        const int fm = x / C::FN, fn = x % C::FN;
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[fn], fa0[fm], acc[fm][fn], 0, 0, 0);
+        if (x < C::FM) fa1[x] = read_a(stage, 1, x);
+        else if (x < C::FM + C::FN) fb1[x - C::FM] = read_b(stage, 1, x - C::FM);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const int ahead = issued - step - 2;
       if (ahead >= 1)
         wait_vmcnt<C::DMA>();
       else
         wait_vmcnt<0>();
       lds_barrier();
-      if (more) {
-        issue_copies((step + kStages - 1) & (kStages - 1));
+      const bool cp = more;
+      const int cstage = (step + kStages - 1) & (kStages - 1);
+      if (cp) prep_copies();
+      const bool rd = step + 1 < issued + (cp ? 1 : 0);
+      const int nstage = (step + 1) & (kStages - 1);
+      // second half: MFMAs on fragments 1 interleaved with the copies of k-step
+      // step+3 and the reads of the next k-step's fragments 0
+      // (narrow tiles have fewer MFMAs than copies and reads: the slots past
+      // the last MFMA carry the rest)
+      constexpr int kSlots = C::FM * C::FN > C::DMA + C::FM + C::FN ? C::FM * C::FN : C::DMA + C::FM + C::FN;
+#pragma unroll
+      for (int x = 0; x < kSlots; ++x) {
+        if (x < C::FM * C::FN) {
+          const int fm = x / C::FN, fn = x % C::FN;
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[fn], fa1[fm], acc[fm][fn], 0, 0, 0);
+        }
+        if (x < C::DMA) {
+          if (cp) copy_u(cstage, x);
+        } else if (x - C::DMA < C::FM) {
+          if (rd) fa0[x - C::DMA] = read_a(nstage, 0, x - C::DMA);
+        } else if (x - C::DMA - C::FM < C::FN) {
+          if (rd) fb0[x - C::DMA - C::FM] = read_b(nstage, 0, x - C::DMA - C::FM);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (cp) {
+        advance_copies();
         ++issued;
       }
-      if (step + 1 < issued) load_frags((step + 1) & (kStages - 1), 0, fa0, fb0);
-      mfmas(fa1, fb1);
       ++step;
     }
 
