@@ -95,6 +95,13 @@ struct FwdCfg {
   static constexpr int B_DMA = B_BYTES / 4096;
   static constexpr int DMA = A_DMA + B_DMA;
   static_assert(2 * DMA < 64, "vmcnt range");
+  // epilogue: each wave restages 32 rows x WTN columns of bf16 at a time in
+  // its share of the stage its tile's last k-step used
+  static constexpr int E_PITCH = WTN * 2;          // bytes per restaged row
+  static constexpr int E_NP = WTN / 8;             // 16-byte pieces per row
+  static constexpr int E_BYTES = 32 * E_PITCH;
+  static constexpr int E_MASK = E_NP == 12 ? 3 : E_NP - 1;  // piece swizzle: p ^ (row & E_MASK)
+  static_assert(4 * E_BYTES <= STAGE && E_NP % 2 == 0 && (E_NP == 12 || (E_NP & E_MASK) == 0), "epilogue buffer");
 };
 
 struct FwdArgs {
@@ -136,14 +143,14 @@ __device__ __forceinline__ Tile decode_tile(const FwdArgs& a, const int32_t* off
   const int i = find_group(tile_off, a.q, rt);
   Tile t;
   t.i = i;
-  t.rank0 = (rt - tile_off[i]) * C::BM;
-  t.first = offsets[i] + t.rank0;
-  t.m_cnt = min(C::BM, offsets[i + 1] - t.first);
+  t.rank0 = (rt - uni(tile_off[i])) * C::BM;
+  t.first = uni(offsets[i]) + t.rank0;
+  t.m_cnt = min(C::BM, uni(offsets[i + 1]) - t.first);
   const int j = ct / a.cpg, cc = ct - j * a.cpg;
   t.n0 = j * a.r + cc * C::BN;
   t.seg0 = i * a.s;
   t.seg1 = j * a.s;
-  t.nk = (j == i) ? a.kts : 2 * a.kts;
+  t.nk = uni((j == i) ? a.kts : 2 * a.kts);
   return t;
 }
 
@@ -241,7 +248,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   prefetch_rows(lt);
   take_rows();
   if (lL + per_x < c_hi) prefetch_rows(decode_tile<C>(a, s_off, s_toff, n_rt, lL + per_x));
-  bool more = true;  // the copy cursor still has k-steps
+  bool more = true;  // the copy cursor has not passed the last k-step
   // copy cursor split in three so that the copies can be interleaved with MFMAs
   uint32_t cp_x = 0, cp_w = 0;  // per-step byte offsets of the X and W pieces
   auto prep_copies = [&]() {
@@ -257,12 +264,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
     else
       copy16_to_lds(a.W, cp_w + b_src[u - C::A_DMA], S + uint32_t(C::A_BYTES + (wid * C::B_DMA + (u - C::A_DMA)) * 1024));
   };
+  // After the last k-step the cursor stays on it: the copies issued for the
+  // three k-steps past the end repeat it into stages that are never read, so
+  // that the pipeline needs no conditions (they are drained before exit).
   auto advance_copies = [&]() {
-    if (++lk >= lt.nk) {
-      lL += per_x;
-      if (lL >= c_hi) {
+    if (more && (lk = uni(lk + 1)) >= lt.nk) {
+      if (lL + per_x >= c_hi) {
         more = false;
+        lk = uni(lt.nk - 1);
       } else {
+        lL = uni(lL + per_x);
         lt = decode_tile<C>(a, s_off, s_toff, n_rt, lL);
         lk = 0;
         take_rows();
@@ -342,17 +353,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   // of k-step `step`: the first half's MFMAs cover the wait, and after the
   // barrier the next k-step's first fragments are read while the second half's
   // MFMAs run, so the matrix cores never wait for a fragment read.
-  int issued = 0;  // k-steps whose copies were issued
-  for (int st = 0; st < kStages - 1 && more; ++st) {
-    issue_copies(st);
-    ++issued;
-  }
-  if (issued >= 3)
-    wait_vmcnt<2 * C::DMA>();
-  else if (issued == 2)
-    wait_vmcnt<C::DMA>();
-  else
-    wait_vmcnt<0>();
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st) issue_copies(st);
+  wait_vmcnt<2 * C::DMA>();
   lds_barrier();
   load_frags(0, 0, fa0, fb0);
 
@@ -362,8 +365,10 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   for (;;) {
     // output rows of this tile, loaded now and used after its last k-step
     int out_row[C::FM];
+    if constexpr (!CYC) {
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) out_row[fm] = row_of(ct, min(wm * C::WTM + fm * 32 + l32, ct.m_cnt - 1));
+      for (int fm = 0; fm < C::FM; ++fm) out_row[fm] = row_of(ct, min(wm * C::WTM + fm * 32 + l32, ct.m_cnt - 1));
+    }
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
@@ -381,16 +386,12 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
         else if (x < C::FM + C::FN) fb1[x - C::FM] = read_b(stage, 1, x - C::FM);
         __builtin_amdgcn_sched_barrier(0);
       }
-      const int ahead = issued - step - 2;
-      if (ahead >= 1)
-        wait_vmcnt<C::DMA>();
-      else
-        wait_vmcnt<0>();
+      // the copies of k-step step+1 are complete when at most one k-step's
+      // copies (step+2) are still in flight
+      wait_vmcnt<C::DMA>();
       lds_barrier();
-      const bool cp = more;
       const int cstage = (step + kStages - 1) & (kStages - 1);
-      if (cp) prep_copies();
-      const bool rd = step + 1 < issued + (cp ? 1 : 0);
+      prep_copies();
       const int nstage = (step + 1) & (kStages - 1);
       // second half: MFMAs on fragments 1 interleaved with the copies of k-step
       // step+3 and the reads of the next k-step's fragments 0
@@ -403,43 +404,66 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
           const int fm = x / C::FN, fn = x % C::FN;
           acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[fn], fa1[fm], acc[fm][fn], 0, 0, 0);
         }
-        if (x < C::DMA) {
-          if (cp) copy_u(cstage, x);
-        } else if (x - C::DMA < C::FM) {
-          if (rd) fa0[x - C::DMA] = read_a(nstage, 0, x - C::DMA);
-        } else if (x - C::DMA - C::FM < C::FN) {
-          if (rd) fb0[x - C::DMA - C::FM] = read_b(nstage, 0, x - C::DMA - C::FM);
-        }
+        // (past the last k-step these reads fetch stale fragments that are never used)
+        if (x < C::DMA)
+          copy_u(cstage, x);
+        else if (x - C::DMA < C::FM)
+          fa0[x - C::DMA] = read_a(nstage, 0, x - C::DMA);
+        else if (x - C::DMA - C::FM < C::FN)
+          fb0[x - C::DMA - C::FM] = read_b(nstage, 0, x - C::DMA - C::FM);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (cp) {
-        advance_copies();
-        ++issued;
-      }
-      ++step;
+      advance_copies();
+      step = uni(step + 1);
     }
 
-    // epilogue: one rounding of each fp32 sum, 8-byte stores of 4 columns
+    // epilogue: one rounding of each fp32 sum.  The MFMA layout leaves each
+    // lane with pieces of one row, so a direct store would touch 32 rows per
+    // instruction; instead each 32-row slice of the wave tile is written to
+    // LDS (the stage of the tile's last k-step: every wave has read it before
+    // that k-step's barrier, and the next copy into it comes after the next
+    // barrier) and read back row-contiguous, so that a store instruction
+    // writes whole rows of 16-byte pieces.
+    {
+      char* ebuf = smem + ((step - 1) & (kStages - 1)) * C::STAGE + wid * C::E_BYTES;
+      const uint32_t col0 = uint32_t(ct.n0 + wn * C::WTN) * 2u;
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-      const int ml = wm * C::WTM + fm * 32 + l32;
-      if (ml < ct.m_cnt) {
-        char* crow = a.Y + (uint32_t(out_row[fm]) * n_bytes + uint32_t(ct.n0 + wn * C::WTN + lhi * 4) * 2u);
+      for (int fm = 0; fm < C::FM; ++fm) {
+        // lane (l32, lhi) holds row l32, columns fn*32 + g*8 + lhi*4 .. +3
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const f32x16& v = acc[fm][fn];
-            *reinterpret_cast<u32x2*>(crow + (fn * 32 + g * 8) * 2) =
+            const int pc = (fn * 4 + g) ^ (l32 & C::E_MASK);
+            *reinterpret_cast<u32x2*>(ebuf + l32 * C::E_PITCH + pc * 16 + lhi * 8) =
                 pack4_bf16(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
           }
         }
+        // read back: 64 lanes take 64 consecutive (row, piece) slots per instruction
+#pragma unroll
+        for (int it = 0; it < C::E_NP / 2; ++it) {
+          const int sl = it * 64 + lane;
+          const int row = sl / C::E_NP, pc = sl - row * C::E_NP;
+          const u32x4 val = *reinterpret_cast<const u32x4*>(ebuf + row * C::E_PITCH + ((pc ^ (row & C::E_MASK)) << 4));
+          const int ml = wm * C::WTM + fm * 32 + row;
+          int orow;
+          if constexpr (CYC)
+            orow = row_of(ct, ml);
+          else
+            orow = __shfl(out_row[fm], row);
+          if (ml < ct.m_cnt)
+            *reinterpret_cast<u32x4*>(a.Y + (uint32_t(orow) * n_bytes + col0 + uint32_t(pc) * 16u)) = val;
+        }
       }
     }
-    cL += per_x;
+    cL = uni(cL + per_x);
     if (cL >= c_hi) break;
     ct = decode_tile<C>(a, s_off, s_toff, n_rt, cL);
   }
+  // the repeated copies past the last k-step land in LDS: drain them before
+  // the workgroup's LDS can be handed to another workgroup
+  wait_vmcnt<0>();
 }
 
 template <class C>
