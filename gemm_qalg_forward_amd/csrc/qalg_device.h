@@ -63,13 +63,20 @@ __device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) 
   return (u32x2){__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
 }
 
+// Read-only global data addressed uniformly: loads through this pointer type
+// go through the scalar data cache (s_load), which the lgkm counter tracks,
+// so they never wait behind the vector-memory counter.
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+__device__ __forceinline__ cint_ptr to_const(const int32_t* p) { return (cint_ptr)(p); }
+
 // A value the caller knows to be the same in every lane, moved to a scalar
 // register so that comparisons and branches on it stay on the scalar unit.
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Group g with tile_off[g] <= rt < tile_off[g + 1] (binary search over q + 1
 // non-decreasing offsets; rt and the offsets are wave-uniform).
-__device__ __forceinline__ int find_group(const int32_t* tile_off, int q, int rt) {
+template <class P>
+__device__ __forceinline__ int find_group(P tile_off, int q, int rt) {
   int lo = 0, hi = q;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;

@@ -94,7 +94,7 @@ struct FwdCfg {
   static constexpr int A_DMA = A_BYTES / 4096;      // 1 KB direct-to-LDS copies per wave and k-step
   static constexpr int B_DMA = B_BYTES / 4096;
   static constexpr int DMA = A_DMA + B_DMA;
-  static_assert(2 * DMA < 64, "vmcnt range");
+  static_assert((kStages - 1) * DMA < 64, "vmcnt range");
   // epilogue: each wave restages 32 rows x WTN columns of bf16 at a time in
   // its share of the stage its tile's last k-step used
   static constexpr int E_PITCH = WTN * 2;          // bytes per restaged row
@@ -128,8 +128,7 @@ struct Tile {
 };
 
 template <class C>
-__device__ __forceinline__ Tile decode_tile(const FwdArgs& a, const int32_t* offsets,
-                                            const int32_t* tile_off, int n_rt, int L) {
+__device__ __forceinline__ Tile decode_tile(const FwdArgs& a, cint_ptr offsets, cint_ptr tile_off, int n_rt, int L) {
   // groups of up to 4 row tiles x all column tiles, row tile fastest (measured
   // against 2, 8 and 16 row tiles: the least L2 refetch for 256x256 tiles)
   constexpr int G = 4;
@@ -162,24 +161,15 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // per-type row offsets and row-tile offsets, cached in LDS behind the stages
-  // (tile decoding then never waits on the vector-memory counter, which also
-  // counts the copies in flight)
-  int* s_off = reinterpret_cast<int*>(smem + C::LDS_BYTES);
-  int* s_toff = s_off + (a.q + 1);
-  {
-    const int32_t* offsets = ws + a.off_offsets;
-    const int32_t* tile_off = ws + a.off_tiles + tile_height_slot(BM) * (a.q + 1);
-    for (int x = tid; x <= a.q; x += T) {
-      s_off[x] = offsets[x];
-      s_toff[x] = tile_off[x];
-    }
-  }
-  __syncthreads();
+  // per-type row offsets and row-tile offsets, read through the scalar data
+  // cache (tile decoding then never waits on the vector-memory counter, which
+  // also counts the copies in flight, and the LDS is left to the stages)
+  const cint_ptr s_off = to_const(ws + a.off_offsets);
+  const cint_ptr s_toff = to_const(ws + a.off_tiles + tile_height_slot(BM) * (a.q + 1));
 
   // rows of an out-of-range type: zero output rows (rare)
   {
-    const int typed = s_off[a.q];
+    const int typed = uni(s_off[a.q]);
     const int nbad = a.M - typed;
     const int row_u4 = a.N / 8;  // 16-byte pieces per output row
     for (int b = blockIdx.x; b < nbad; b += gridDim.x) {
@@ -189,7 +179,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   }
 
   // this workgroup's tiles: a contiguous chunk per XCD, round robin inside it
-  const int n_rt = s_toff[a.q];
+  const int n_rt = uni(s_toff[a.q]);
   const int total = n_rt * a.n_ct;
   const int nx = gridDim.x >= 8 ? 8 : 1;
   const int per_x = gridDim.x / nx;
@@ -325,6 +315,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * C::ROWB));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
+  // fragment read j of a half k-step, in the order the MFMAs (x = fm * FN + fn)
+  // first need them: a[0], b[0..FN-1], a[1..FM-1]
+  auto read_slot = [&](int j, int stage, int ks, bf16x8 (&fa)[C::FM], bf16x8 (&fb)[C::FN]) {
+    if (j == 0)
+      fa[0] = read_a(stage, ks, 0);
+    else if (j <= C::FN)
+      fb[j - 1] = read_b(stage, ks, j - 1);
+    else
+      fa[j - C::FN] = read_a(stage, ks, j - C::FN);
+  };
   auto load_frags = [&](int stage, int ks, bf16x8 (&fa)[C::FM], bf16x8 (&fb)[C::FN]) {
     const char* S = smem + stage * C::STAGE;
 #pragma unroll
@@ -355,13 +355,13 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   // MFMAs run, so the matrix cores never wait for a fragment read.
 #pragma unroll
   for (int st = 0; st < kStages - 1; ++st) issue_copies(st);
-  wait_vmcnt<2 * C::DMA>();
+  wait_vmcnt<(kStages - 2) * C::DMA>();
   lds_barrier();
   load_frags(0, 0, fa0, fb0);
 
   Tile ct = decode_tile<C>(a, s_off, s_toff, n_rt, L_first);
   int cL = L_first;
-  int step = 0;
+  int stage = 0;  // LDS stage of the current k-step (k-step mod kStages)
   for (;;) {
     // output rows of this tile, loaded now and used after its last k-step
     int out_row[C::FM];
@@ -375,26 +375,24 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
       for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = (f32x16){};
 
     for (int ck = 0; ck < ct.nk; ++ck) {
-      const int stage = step & (kStages - 1);
       // first half: MFMAs on fragments 0 interleaved with the reads of fragments 1
       static_assert(C::FM + C::FN <= C::FM * C::FN, "fragment reads fit the first half");
 #pragma unroll
       for (int x = 0; x < C::FM * C::FN; ++x) {
         const int fm = x / C::FN, fn = x % C::FN;
         acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[fn], fa0[fm], acc[fm][fn], 0, 0, 0);
-        if (x < C::FM) fa1[x] = read_a(stage, 1, x);
-        else if (x < C::FM + C::FN) fb1[x - C::FM] = read_b(stage, 1, x - C::FM);
+        if (x < C::FM + C::FN) read_slot(x, stage, 1, fa1, fb1);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // the copies of k-step step+1 are complete when at most one k-step's
-      // copies (step+2) are still in flight
-      wait_vmcnt<C::DMA>();
+      // the copies of k-step step+1 are complete when at most those of
+      // k-steps step+2 .. step+kStages-2 are still in flight
+      wait_vmcnt<(kStages - 3) * C::DMA>();
       lds_barrier();
-      const int cstage = (step + kStages - 1) & (kStages - 1);
+      const int cstage = stage == 0 ? kStages - 1 : stage - 1;  // consumed by k-step step-1
       prep_copies();
-      const int nstage = (step + 1) & (kStages - 1);
-      // second half: MFMAs on fragments 1 interleaved with the copies of k-step
-      // step+3 and the reads of the next k-step's fragments 0
+      const int nstage = stage == kStages - 1 ? 0 : stage + 1;
+      // second half: MFMAs on fragments 1 interleaved with the reads of the next
+      // k-step's fragments 0 and the copies of k-step step+kStages-1
       // (narrow tiles have fewer MFMAs than copies and reads: the slots past
       // the last MFMA carry the rest)
       constexpr int kSlots = C::FM * C::FN > C::DMA + C::FM + C::FN ? C::FM * C::FN : C::DMA + C::FM + C::FN;
@@ -404,17 +402,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
           const int fm = x / C::FN, fn = x % C::FN;
           acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[fn], fa1[fm], acc[fm][fn], 0, 0, 0);
         }
-        // (past the last k-step these reads fetch stale fragments that are never used)
-        if (x < C::DMA)
-          copy_u(cstage, x);
-        else if (x - C::DMA < C::FM)
-          fa0[x - C::DMA] = read_a(nstage, 0, x - C::DMA);
-        else if (x - C::DMA - C::FM < C::FN)
-          fb0[x - C::DMA - C::FM] = read_b(nstage, 0, x - C::DMA - C::FM);
+        // the next k-step's first fragments first, then the copies (past the
+        // last k-step these reads fetch stale fragments that are never used)
+        if (x < C::FM + C::FN)
+          read_slot(x, nstage, 0, fa0, fb0);
+        else if (x - (C::FM + C::FN) < C::DMA)
+          copy_u(cstage, x - (C::FM + C::FN));
         __builtin_amdgcn_sched_barrier(0);
       }
       advance_copies();
-      step = uni(step + 1);
+      stage = uni(nstage);
     }
 
     // epilogue: one rounding of each fp32 sum.  The MFMA layout leaves each
@@ -425,7 +422,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
     // barrier) and read back row-contiguous, so that a store instruction
     // writes whole rows of 16-byte pieces.
     {
-      char* ebuf = smem + ((step - 1) & (kStages - 1)) * C::STAGE + wid * C::E_BYTES;
+      char* ebuf = smem + (stage == 0 ? kStages - 1 : stage - 1) * C::STAGE + wid * C::E_BYTES;
       const uint32_t col0 = uint32_t(ct.n0 + wn * C::WTN) * 2u;
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm) {
@@ -500,7 +497,7 @@ hipError_t launch_fwd(const ProblemDesc& p, hipStream_t s) {
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_persistent_kernel<C>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             C::LDS_BYTES + int(sizeof(int)) * 2 * (QALG_MAX_Q + 1));
+                                             C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -526,7 +523,7 @@ hipError_t launch_fwd(const ProblemDesc& p, hipStream_t s) {
   int grid = cu_count();
   if (max_tiles < grid) grid = max_tiles < 8 ? int(max_tiles) : int(max_tiles / 8 * 8);
   if (grid < 1) grid = 1;
-  const size_t lds = C::LDS_BYTES + sizeof(int) * 2 * (p.q + 1);
+  const size_t lds = C::LDS_BYTES;
   hipLaunchKernelGGL((fwd_persistent_kernel<C>), dim3(grid), dim3(C::THREADS), lds, s, a);
   return hipGetLastError();
 }
