@@ -23,8 +23,9 @@
 // Pipeline (shared with the forward): one workgroup per CU, operands copied
 // global -> LDS directly (global_load_lds_dwordx4), four 32-deep stages so
 // that copies run three k-steps ahead, the publishing barrier in the middle of
-// a k-step, MFMAs interleaved one by one with fragment reads and copies,
-// v_mfma_f32_32x32x16_bf16 on 128x128 wave tiles, one RNE rounding.
+// a k-step, MFMAs interleaved one by one with fragment reads (in the order
+// the MFMAs use them) and copies, v_mfma_f32_32x32x16_bf16 on 128x128 wave
+// tiles, one RNE rounding, output restaged through LDS into whole pieces.
 //
 // Work balance.  Long tiles carry q times the contraction of short ones.  The
 // tiles of each XCD (a contiguous share of the long and of the short tiles)
@@ -66,7 +67,14 @@ struct GradCfg {
   static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole 1 KB copies per wave");
   static constexpr int A_DMA = A_BYTES / 4096, B_DMA = B_BYTES / 4096;
   static constexpr int DMA = A_DMA + B_DMA;
-  static_assert(2 * DMA < 64, "vmcnt range");
+  static_assert((kStages - 1) * DMA < 64, "vmcnt range");
+  // epilogue: each wave restages 32 rows x WTN columns of bf16 at a time in
+  // its share of the stage its tile's last k-step used
+  static constexpr int E_PITCH = WTN * 2;          // bytes per restaged row
+  static constexpr int E_NP = WTN / 8;             // 16-byte pieces per row
+  static constexpr int E_BYTES = 32 * E_PITCH;
+  static constexpr int E_MASK = E_NP == 12 ? 3 : E_NP - 1;  // piece swizzle: p ^ (row & E_MASK)
+  static_assert(4 * E_BYTES <= STAGE && E_NP % 2 == 0 && (E_NP == 12 || (E_NP & E_MASK) == 0), "epilogue buffer");
 };
 
 struct GradArgs {
@@ -150,24 +158,12 @@ struct TileDeal {
   }
 };
 
-__device__ __forceinline__ int find_group(const int* tile_off, int q, int rt) {
-  int lo = 0, hi = q;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (tile_off[mid] <= rt)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  return lo;
-}
-
 // Tile decode.  dX long tiles: (row tile, column tile of the row's own group);
 // short: (row tile, other group, column tile); both in groups of 4 row tiles
 // by all columns, row tile fastest.  dW long tiles: (block b == j, row tile,
 // column tile); short: (b, j != b, row tile, column tile), b slowest.
 template <class C, Op OP>
-__device__ __forceinline__ GTile decode(const GradArgs& a, const int* s_off, const int* s_toff,
+__device__ __forceinline__ GTile decode(const GradArgs& a, cint_ptr s_off, cint_ptr s_toff,
                                         bool is_long, int idx) {
   GTile t;
   if constexpr (OP == Op::Dx) {
@@ -180,8 +176,8 @@ __device__ __forceinline__ GTile decode(const GradArgs& a, const int* s_off, con
     const int rt = first_rt + w % gm, ct = w / gm;
     const int i = find_group(s_toff, a.q, rt);
     t.type = i;
-    t.out_row0 = (rt - s_toff[i]) * C::BM;
-    t.m_cnt = min(C::BM, (s_off[i + 1] - s_off[i]) - t.out_row0);
+    t.out_row0 = (rt - uni(s_toff[i])) * C::BM;
+    t.m_cnt = min(C::BM, (uni(s_off[i + 1]) - uni(s_off[i])) - t.out_row0);
     int k, cc;
     if (is_long) {
       k = i;
@@ -193,7 +189,7 @@ __device__ __forceinline__ GTile decode(const GradArgs& a, const int* s_off, con
     }
     t.n0 = k * a.s + cc * C::BN;
     t.c0 = is_long ? 0 : k * a.r;
-    t.nk = (is_long ? a.N : a.r) / kBK;
+    t.nk = uni((is_long ? a.N : a.r) / kBK);
   } else {
     const int tpb = a.rpb * a.cpg;
     const int blk = idx / tpb, w = idx - blk * tpb;
@@ -211,14 +207,13 @@ __device__ __forceinline__ GTile decode(const GradArgs& a, const int* s_off, con
     t.n0 = j * a.r + ct * C::BN;
     t.type = is_long ? -1 : b;
     t.c0 = 0;
-    t.nk = (is_long ? a.M : a.M / a.q) / kBK;
+    t.nk = uni((is_long ? a.M : a.M / a.q) / kBK);
   }
   return t;
 }
 
 template <class C, Op OP>
 __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs a) {
-  constexpr int T = C::THREADS;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int32_t* ws = a.ws;
   if (ws[1] != kIndexMagic || ws[2] != a.q || ws[3] != a.M) return;
@@ -228,24 +223,16 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  int* s_off = reinterpret_cast<int*>(smem + C::LDS_BYTES);
-  int* s_toff = s_off + (q + 1);
-  {
-    const int32_t* offsets = ws + a.off_offsets;
-    const int32_t* tile_off = ws + a.off_tiles + tile_height_slot(C::BM) * (q + 1);
-    for (int x = tid; x <= q; x += T) {
-      s_off[x] = offsets[x];
-      s_toff[x] = tile_off[x];
-    }
-  }
-  __syncthreads();
+  // per-type row offsets and row-tile offsets through the scalar data cache
+  const cint_ptr s_off = to_const(ws + a.off_offsets);
+  const cint_ptr s_toff = to_const(ws + a.off_tiles + tile_height_slot(C::BM) * (q + 1));
   // first row of each type in the cyclic schedule
   auto type_start = [&](int i) { return i >= cyc ? i - cyc : i - cyc + q; };
 
   GradArgs g = a;
   int n_long, n_short, t_long, t_short;
   if constexpr (OP == Op::Dx) {
-    g.n_rt = s_toff[q];
+    g.n_rt = uni(s_toff[q]);
     n_long = g.n_rt * g.cpg;
     n_short = g.n_rt * (q - 1) * g.cpg;
     t_long = g.N / kBK;
@@ -275,7 +262,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   if (!dcopy.next(&l_long, &l_idx)) return;
   GTile lt = decode<C, OP>(g, s_off, s_toff, l_long, l_idx);
   int lk = 0;
-  bool more = true;
+  bool more = true;  // the copy cursor has not passed the last k-step
 
   // per-lane copy slots: KM operand -> (tile row, swizzled piece); RM operand -> (contraction row, piece)
   int a_r[C::A_DMA], a_c[C::A_DMA], b_r[C::B_DMA], b_c[C::B_DMA];
@@ -344,13 +331,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
       }
     }
   };
+  // After the last k-step the cursor stays on it: the copies issued for the
+  // k-steps past the end repeat it into stages that are never read (drained
+  // before exit), so that the pipeline needs no conditions.
   auto advance_copies = [&]() {
-    if (++lk >= lt.nk) {
+    if (more && (lk = uni(lk + 1)) >= lt.nk) {
       if (dcopy.next(&l_long, &l_idx)) {
-        lt = decode<C, OP>(g, s_off, s_toff, l_long, l_idx);
+        lt = decode<C, OP>(g, s_off, s_toff, l_long, uni(l_idx));
         lk = 0;
       } else {
         more = false;
+        lk = uni(lt.nk - 1);
       }
     }
   };
@@ -417,26 +408,21 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) fb[fn] = read_b(stage, ks, fn);
   };
-  auto mfmas = [&](const bf16x8 (&fa)[C::FM], const bf16x8 (&fb)[C::FN]) {
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], acc[fm][fn], 0, 0, 0);
+  // fragment read j of a half k-step, in the order the MFMAs (x = fm * FN + fn)
+  // first need them: a[0], b[0..FN-1], a[1..FM-1]
+  auto read_slot = [&](int j, int stage, int ks, bf16x8 (&fa)[C::FM], bf16x8 (&fb)[C::FN]) {
+    if (j == 0)
+      fa[0] = read_a(stage, ks, 0);
+    else if (j <= C::FN)
+      fb[j - 1] = read_b(stage, ks, j - 1);
+    else
+      fa[j - C::FN] = read_a(stage, ks, j - C::FN);
   };
 
   // ---------------- pipeline (as in the forward) ----------------
-  int issued = 0;
-  for (int st = 0; st < kStages - 1 && more; ++st) {
-    issue_copies(st);
-    ++issued;
-  }
-  if (issued >= 3)
-    wait_vmcnt<2 * C::DMA>();
-  else if (issued == 2)
-    wait_vmcnt<C::DMA>();
-  else
-    wait_vmcnt<0>();
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st) issue_copies(st);
+  wait_vmcnt<(kStages - 2) * C::DMA>();
   lds_barrier();
   load_frags(0, 0, fa0, fb0);
 
@@ -445,8 +431,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   bool c_long;
   int c_idx;
   dcomp.next(&c_long, &c_idx);
-  GTile ct = decode<C, OP>(g, s_off, s_toff, c_long, c_idx);
-  int step = 0;
+  GTile ct = decode<C, OP>(g, s_off, s_toff, c_long, uni(c_idx));
+  int stage = 0;  // LDS stage of the current k-step
   for (;;) {
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
@@ -454,32 +440,26 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
       for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = (f32x16){};
 
     for (int ck = 0; ck < ct.nk; ++ck) {
-      const int stage = step & (kStages - 1);
       // first half: MFMAs on fragments 0 interleaved with the reads of fragments 1
       static_assert(C::FM + C::FN <= C::FM * C::FN, "fragment reads fit the first half");
 #pragma unroll
       for (int x = 0; x < C::FM * C::FN; ++x) {
         const int fm = x / C::FN, fn = x % C::FN;
         acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[fn], fa0[fm], acc[fm][fn], 0, 0, 0);
-        if (x < C::FM) fa1[x] = read_a(stage, 1, x);
-        else if (x < C::FM + C::FN) fb1[x - C::FM] = read_b(stage, 1, x - C::FM);
+        if (x < C::FM + C::FN) read_slot(x, stage, 1, fa1, fb1);
         __builtin_amdgcn_sched_barrier(0);
       }
-      const int ahead = issued - step - 2;
-      if (ahead >= 1)
-        wait_vmcnt<C::DMA>();
-      else
-        wait_vmcnt<0>();
+      // the copies of the next k-step are complete when at most those of the
+      // kStages-3 k-steps after it are still in flight
+      wait_vmcnt<(kStages - 3) * C::DMA>();
       lds_barrier();
-      const bool cp = more;
-      const int cstage = (step + kStages - 1) & (kStages - 1);
-      if (cp) prep_copies();
-      const bool rd = step + 1 < issued + (cp ? 1 : 0);
-      const int nstage = (step + 1) & (kStages - 1);
-      // second half: MFMAs on fragments 1 interleaved with the copies of k-step
-      // step+3 and the reads of the next k-step's fragments 0
-      // (narrow tiles have fewer MFMAs than copies and reads: the slots past
-      // the last MFMA carry the rest)
+      const int cstage = stage == 0 ? kStages - 1 : stage - 1;  // consumed by the previous k-step
+      prep_copies();
+      const int nstage = stage == kStages - 1 ? 0 : stage + 1;
+      // second half: MFMAs on fragments 1 interleaved with the reads of the next
+      // k-step's fragments 0 (stale past the last k-step, never used) and the
+      // copies of the k-step kStages-1 ahead; narrow tiles have fewer MFMAs
+      // than reads and copies, the slots past the last MFMA carry the rest
       constexpr int kSlots = C::FM * C::FN > C::DMA + C::FM + C::FN ? C::FM * C::FN : C::DMA + C::FM + C::FN;
 #pragma unroll
       for (int x = 0; x < kSlots; ++x) {
@@ -487,44 +467,55 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
           const int fm = x / C::FN, fn = x % C::FN;
           acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[fn], fa1[fm], acc[fm][fn], 0, 0, 0);
         }
-        if (x < C::DMA) {
-          if (cp) copy_u(cstage, x);
-        } else if (x - C::DMA < C::FM) {
-          if (rd) fa0[x - C::DMA] = read_a(nstage, 0, x - C::DMA);
-        } else if (x - C::DMA - C::FM < C::FN) {
-          if (rd) fb0[x - C::DMA - C::FM] = read_b(nstage, 0, x - C::DMA - C::FM);
-        }
+        if (x < C::FM + C::FN)
+          read_slot(x, nstage, 0, fa0, fb0);
+        else if (x - (C::FM + C::FN) < C::DMA)
+          copy_u(cstage, x - (C::FM + C::FN));
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (cp) {
-        advance_copies();
-        ++issued;
-      }
-      ++step;
+      advance_copies();
+      stage = uni(nstage);
     }
 
-    // epilogue: one rounding of each fp32 sum, 8-byte stores of 4 columns
-    const int ostart = OP == Op::Dx ? type_start(ct.type) : 0;
+    // epilogue: one rounding of each fp32 sum, restaged through LDS (the stage
+    // of the tile's last k-step, free until the next k-step's barrier) so that
+    // each store instruction writes whole 16-byte pieces of a few rows
+    {
+      char* ebuf = smem + (stage == 0 ? kStages - 1 : stage - 1) * C::STAGE + wid * C::E_BYTES;
+      const uint32_t col0 = uint32_t(ct.n0 + wn * C::WTN) * 2u;
+      const int ostart = OP == Op::Dx ? type_start(ct.type) : 0;
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-      const int ml = wm * C::WTM + fm * 32 + l32;
-      if (ml < ct.m_cnt) {
-        const int orow = OP == Op::Dx ? ostart + (ct.out_row0 + ml) * q : ct.out_row0 + ml;
-        char* crow = g.C + (uint32_t(orow) * c_ld + uint32_t(ct.n0 + wn * C::WTN + lhi * 4) * 2u);
+      for (int fm = 0; fm < C::FM; ++fm) {
+        // lane (l32, lhi) holds row l32, columns fn*32 + g*8 + lhi*4 .. +3
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) {
 #pragma unroll
           for (int gg = 0; gg < 4; ++gg) {
             const f32x16& v = acc[fm][fn];
-            *reinterpret_cast<u32x2*>(crow + (fn * 32 + gg * 8) * 2) =
+            const int pc = (fn * 4 + gg) ^ (l32 & C::E_MASK);
+            *reinterpret_cast<u32x2*>(ebuf + l32 * C::E_PITCH + pc * 16 + lhi * 8) =
                 pack4_bf16(v[4 * gg], v[4 * gg + 1], v[4 * gg + 2], v[4 * gg + 3]);
           }
+        }
+        // read back: 64 lanes take 64 consecutive (row, piece) slots per instruction
+#pragma unroll
+        for (int it = 0; it < C::E_NP / 2; ++it) {
+          const int sl = it * 64 + lane;
+          const int row = sl / C::E_NP, pc = sl - row * C::E_NP;
+          const u32x4 val = *reinterpret_cast<const u32x4*>(ebuf + row * C::E_PITCH + ((pc ^ (row & C::E_MASK)) << 4));
+          const int ml = wm * C::WTM + fm * 32 + row;
+          const int orow = OP == Op::Dx ? ostart + (ct.out_row0 + ml) * q : ct.out_row0 + ml;
+          if (ml < ct.m_cnt)
+            *reinterpret_cast<u32x4*>(g.C + (uint32_t(orow) * c_ld + col0 + uint32_t(pc) * 16u)) = val;
         }
       }
     }
     if (!dcomp.next(&c_long, &c_idx)) break;
-    ct = decode<C, OP>(g, s_off, s_toff, c_long, c_idx);
+    ct = decode<C, OP>(g, s_off, s_toff, c_long, uni(c_idx));
   }
+  // the repeated copies past the last k-step land in LDS: drain them before
+  // the workgroup's LDS can be handed to another workgroup
+  wait_vmcnt<0>();
 }
 
 template <int BN>
@@ -546,7 +537,7 @@ int cu_count() {
 template <class C, Op OP>
 hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
   static bool attr_set = false;
-  const int lds = C::LDS_BYTES + int(sizeof(int)) * 2 * (QALG_MAX_Q + 1);
+  const int lds = C::LDS_BYTES;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grad_persistent_kernel<C, OP>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -576,7 +567,7 @@ hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
   }
   int grid = cu_count();
   grid = grid >= 8 ? grid / 8 * 8 : grid;
-  const size_t shm = C::LDS_BYTES + sizeof(int) * 2 * (p.q + 1);
+  const size_t shm = C::LDS_BYTES;
   hipLaunchKernelGGL((grad_persistent_kernel<C, OP>), dim3(grid), dim3(C::THREADS), shm, s, a);
   return hipGetLastError();
 }
