@@ -29,20 +29,23 @@
 //
 // Data movement.  Operands go from global memory straight into LDS with the
 // gfx950 direct-to-LDS copy (global_load_lds_dwordx4: 16 bytes per lane, a
-// wave moves 1 KB per copy, no registers involved).  A k-step covers 32
-// contraction values; four LDS stages (32 KB each for 256x256 tiles) hold
-// k-steps step..step+3, so copies run three k-steps ahead of the matrix
-// cores.  The barrier that publishes the next stage sits in the middle of a
-// k-step: the first 16 contraction values' MFMAs cover it, and the next
-// k-step's first fragments are read while the second half's MFMAs run.  Inside
-// each half the 16 MFMAs are interleaved one by one with the fragment reads and
-// the copies (pinned by scheduling barriers), so that the matrix cores see a
-// steady stream instead of bursts of other instructions.
+// wave moves 1 KB per copy, no registers involved).  A k-step covers 64
+// contraction values, so each X row contributes one whole 128-byte line per
+// k-step (32 values, half a line, measured 8-12 % slower).  Two LDS stages
+// (64 KB each for 256x256 tiles): the copies of k-step step+1 run while
+// k-step step is computed, four quarter steps of 16 contraction values.  The
+// barrier that publishes the next stage sits after the third quarter, whose
+// MFMAs cover the wait; the fourth quarter reads the next k-step's first
+// fragments and issues the copies of k-step step+2 into the stage just
+// consumed.  Inside each quarter the 16 MFMAs are interleaved one by one with
+// the fragment reads and the copies (pinned by scheduling barriers), so that
+// the matrix cores see a steady stream instead of bursts of other
+// instructions.
 //
 // LDS layouts (both bank-conflict free for the patterns used):
-//  * X tile: row r of the tile keeps its four 16-byte pieces (8 contraction
-//    values each) at piece c ^ ((r >> 1) & 3).  MFMA fragments are plain
-//    128-bit reads (lane: row l % 32, piece 2*ks + l / 32).
+//  * X tile: row r of the tile keeps its eight 16-byte pieces (8 contraction
+//    values each) at piece c ^ ((r >> 1) & 7).  MFMA fragments are plain
+//    128-bit reads (lane: row l % 32, piece 2*ks + l / 32 for quarter ks).
 //  * W tile: contraction row k keeps the tile's BN columns in 16-byte pieces
 //    at piece c ^ 2*(k & 3), i.e. the weight bank's own row-major layout.  The
 //    MFMA needs 8 consecutive contraction values per lane, so the fragment is
@@ -71,8 +74,9 @@ namespace {
 
 using namespace dev;
 
-constexpr int kBK = 32;       // contraction per k-step
-constexpr int kStages = 4;    // LDS stages: operands of 3 k-steps are in flight during a 4th
+constexpr int kBK = 64;       // contraction per k-step (128-byte X row segments)
+constexpr int kStages = 2;    // LDS stages: the next k-step's operands arrive while one is computed
+constexpr int kQ = kBK / 16;  // MFMA quarter steps per k-step
 
 template <int BM_, int BN_>
 struct FwdCfg {
@@ -81,28 +85,35 @@ struct FwdCfg {
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0 && FM >= 1 && FN >= 1, "wave tile");
-  // X tile: BM rows of 64 bytes (32 contraction values), 16-byte pieces swizzled
+  // X tile: BM rows of 128 bytes (64 contraction values), 16-byte pieces swizzled
   static constexpr int A_BYTES = BM * kBK * 2;
-  // W tile: 32 contraction rows of BN*2 bytes, 16-byte pieces swizzled
+  static constexpr int AROWB = kBK * 2;
+  // W tile: 64 contraction rows of BN*2 bytes, 16-byte pieces swizzled
   static constexpr int ROWB = BN * 2;
   static constexpr int NCH = BN / 8;                // 16-byte pieces per W row
   static constexpr int B_BYTES = kBK * ROWB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = kStages * STAGE;
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole 1 KB copies per wave");
   static constexpr int A_DMA = A_BYTES / 4096;      // 1 KB direct-to-LDS copies per wave and k-step
   static constexpr int B_DMA = B_BYTES / 4096;
   static constexpr int DMA = A_DMA + B_DMA;
-  static_assert((kStages - 1) * DMA < 64, "vmcnt range");
+  static_assert(kStages * DMA < 64, "vmcnt range");
   // epilogue: each wave restages 32 rows x WTN columns of bf16 at a time in
-  // its share of the stage its tile's last k-step used
+  // its own share of a buffer behind the stages
   static constexpr int E_PITCH = WTN * 2;          // bytes per restaged row
   static constexpr int E_NP = WTN / 8;             // 16-byte pieces per row
   static constexpr int E_BYTES = 32 * E_PITCH;
   static constexpr int E_MASK = E_NP == 12 ? 3 : E_NP - 1;  // piece swizzle: p ^ (row & E_MASK)
-  static_assert(4 * E_BYTES <= STAGE && E_NP % 2 == 0 && (E_NP == 12 || (E_NP & E_MASK) == 0), "epilogue buffer");
+  static_assert(E_NP % 2 == 0 && (E_NP == 12 || (E_NP & E_MASK) == 0), "epilogue buffer");
+  static constexpr int E_OFF = kStages * STAGE;
+  static constexpr int LDS_BYTES = E_OFF + 4 * E_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
+
+// X tile swizzle: row r keeps its 16-byte piece c (8 contraction values) at
+// c ^ ((r >> 1) & 7), so that the 16 rows a quarter-wave reads, and the 8 rows
+// a 1 KB copy writes, fall in distinct bank groups.
+__device__ __forceinline__ int swz_a(int row) { return (row >> 1) & 7; }
 
 struct FwdArgs {
   const char* X;
@@ -217,8 +228,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
 #pragma unroll
   for (int u = 0; u < C::A_DMA; ++u) {
     const int sl = (wid * C::A_DMA + u) * 64 + lane;
-    a_row[u] = sl >> 2;
-    a_pc[u] = uint32_t((sl & 3) ^ swz_x(sl >> 2)) * 16u;
+    a_row[u] = sl >> 3;
+    a_pc[u] = uint32_t((sl & 7) ^ swz_a(sl >> 3)) * 16u;
   }
   // row ids are fetched one tile ahead of their use (listed schedules only),
   // so that the wait for them overlaps a whole tile
@@ -255,7 +266,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
       copy16_to_lds(a.W, cp_w + b_src[u - C::A_DMA], S + uint32_t(C::A_BYTES + (wid * C::B_DMA + (u - C::A_DMA)) * 1024));
   };
   // After the last k-step the cursor stays on it: the copies issued for the
-  // three k-steps past the end repeat it into stages that are never read, so
+  // k-steps past the end repeat it into a stage that is never read, so
   // that the pipeline needs no conditions (they are drained before exit).
   auto advance_copies = [&]() {
     if (more && (lk = uni(lk + 1)) >= lt.nk) {
@@ -282,10 +293,10 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   const int wm = wid / C::WGN, wn = wid % C::WGN;
   const int l32 = lane & 31, lhi = lane >> 5;
   // X fragment (32 rows x 16 contraction): lane reads row l32, piece 2*ks + lhi
-  int a_rd[2];
+  int a_rd[kQ];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-    a_rd[ks] = (wm * C::WTM + l32) * 64 + (((2 * ks + lhi) ^ swz_x(l32)) << 4);
+  for (int ks = 0; ks < kQ; ++ks)
+    a_rd[ks] = (wm * C::WTM + l32) * C::AROWB + (((2 * ks + lhi) ^ swz_a(l32)) << 4);
   // W fragment (32 columns x 16 contraction) as two transposing 8-byte reads per lane:
   // in a 16-lane group (g = lane / 16, t = lane % 16) lane t reads row 8*(g/2) + t/4 (+4),
   // columns 16*(g%2) + 4*(t%4) of the fragment; the transpose hands lane t column t, 4 rows.
@@ -306,7 +317,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   // fragments of the two 16-wide halves of a k-step (registers double buffered)
   bf16x8 fa0[C::FM], fb0[C::FN], fa1[C::FM], fb1[C::FN];
   auto read_a = [&](int stage, int ks, int fm) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(smem + stage * C::STAGE + a_rd[ks] + fm * 32 * 64);
+    return *reinterpret_cast<const bf16x8*>(smem + stage * C::STAGE + a_rd[ks] + fm * 32 * C::AROWB);
   };
   auto read_b = [&](int stage, int ks, int fn) -> bf16x8 {
     const int m = m0 + fn;
@@ -329,7 +340,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
     const char* S = smem + stage * C::STAGE;
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
-      fa[fm] = *reinterpret_cast<const bf16x8*>(S + a_rd[ks] + fm * 32 * 64);
+      fa[fm] = *reinterpret_cast<const bf16x8*>(S + a_rd[ks] + fm * 32 * C::AROWB);
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
       const int m = m0 + fn;
@@ -348,20 +359,36 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   };
 
   // ---------------- pipeline ----------------
-  // Copies run three k-steps ahead (stages step+1..step+3 in flight while step
-  // is computed).  The barrier that publishes stage step+1 sits in the middle
-  // of k-step `step`: the first half's MFMAs cover the wait, and after the
-  // barrier the next k-step's first fragments are read while the second half's
-  // MFMAs run, so the matrix cores never wait for a fragment read.
-#pragma unroll
-  for (int st = 0; st < kStages - 1; ++st) issue_copies(st);
-  wait_vmcnt<(kStages - 2) * C::DMA>();
+  // Two stages: while k-step `step` is computed from one, the copies of
+  // k-step step+1 land in the other.  A k-step is four quarter steps of 16
+  // contraction values; fragments are double buffered in registers, each
+  // quarter's MFMAs interleaved with the reads of the next quarter's
+  // fragments.  The barrier sits after the third quarter: by then every wave
+  // has issued (and the barrier's fence completed) all its reads of the
+  // current stage, so the fourth quarter reads the next k-step's first
+  // fragments from the other stage and copies k-step step+2 into this one.
+  issue_copies(0);
+  issue_copies(1);
+  wait_vmcnt<C::DMA>();
   lds_barrier();
   load_frags(0, 0, fa0, fb0);
 
   Tile ct = decode_tile<C>(a, s_off, s_toff, n_rt, L_first);
   int cL = L_first;
-  int stage = 0;  // LDS stage of the current k-step (k-step mod kStages)
+  int stage = 0;  // LDS stage of the current k-step (k-step mod 2)
+  static_assert(C::FM + C::FN <= C::FM * C::FN, "fragment reads fit a quarter step");
+  // one quarter step: MFMAs on fragments (fa, fb) of quarter ks, each followed
+  // by one read of quarter ks + 1's fragments into (ga, gb)
+  auto quarter = [&](int ks, const bf16x8 (&fa)[C::FM], const bf16x8 (&fb)[C::FN], bf16x8 (&ga)[C::FM],
+                     bf16x8 (&gb)[C::FN]) {
+#pragma unroll
+    for (int x = 0; x < C::FM * C::FN; ++x) {
+      const int fm = x / C::FN, fn = x % C::FN;
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], acc[fm][fn], 0, 0, 0);
+      if (x < C::FM + C::FN) read_slot(x, stage, ks + 1, ga, gb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   for (;;) {
     // output rows of this tile, loaded now and used after its last k-step
     int out_row[C::FM];
@@ -375,39 +402,27 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
       for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = (f32x16){};
 
     for (int ck = 0; ck < ct.nk; ++ck) {
-      // first half: MFMAs on fragments 0 interleaved with the reads of fragments 1
-      static_assert(C::FM + C::FN <= C::FM * C::FN, "fragment reads fit the first half");
-#pragma unroll
-      for (int x = 0; x < C::FM * C::FN; ++x) {
-        const int fm = x / C::FN, fn = x % C::FN;
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[fn], fa0[fm], acc[fm][fn], 0, 0, 0);
-        if (x < C::FM + C::FN) read_slot(x, stage, 1, fa1, fb1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // the copies of k-step step+1 are complete when at most those of
-      // k-steps step+2 .. step+kStages-2 are still in flight
-      wait_vmcnt<(kStages - 3) * C::DMA>();
+      quarter(0, fa0, fb0, fa1, fb1);
+      quarter(1, fa1, fb1, fa0, fb0);
+      quarter(2, fa0, fb0, fa1, fb1);
+      // the copies of k-step step+1 (the only ones in flight) are complete
+      wait_vmcnt<0>();
       lds_barrier();
-      const int cstage = stage == 0 ? kStages - 1 : stage - 1;  // consumed by k-step step-1
       prep_copies();
-      const int nstage = stage == kStages - 1 ? 0 : stage + 1;
-      // second half: MFMAs on fragments 1 interleaved with the reads of the next
-      // k-step's fragments 0 and the copies of k-step step+kStages-1
-      // (narrow tiles have fewer MFMAs than copies and reads: the slots past
-      // the last MFMA carry the rest)
-      constexpr int kSlots = C::FM * C::FN > C::DMA + C::FM + C::FN ? C::FM * C::FN : C::DMA + C::FM + C::FN;
+      const int nstage = stage ^ 1;
+      // last quarter: MFMAs on fragments 1 interleaved with the reads of the
+      // next k-step's first fragments (stale past the last k-step, never used)
+      // and the copies of k-step step+2 into this k-step's stage; narrow tiles
+      // have fewer MFMAs than copies, the slots past the last MFMA carry the rest
+      constexpr int kSlots = C::FM * C::FN > C::DMA ? C::FM * C::FN : C::DMA;
 #pragma unroll
       for (int x = 0; x < kSlots; ++x) {
         if (x < C::FM * C::FN) {
           const int fm = x / C::FN, fn = x % C::FN;
           acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[fn], fa1[fm], acc[fm][fn], 0, 0, 0);
         }
-        // the next k-step's first fragments first, then the copies (past the
-        // last k-step these reads fetch stale fragments that are never used)
-        if (x < C::FM + C::FN)
-          read_slot(x, nstage, 0, fa0, fb0);
-        else if (x - (C::FM + C::FN) < C::DMA)
-          copy_u(cstage, x - (C::FM + C::FN));
+        if (x < C::FM + C::FN) read_slot(x, nstage, 0, fa0, fb0);
+        if (x < C::DMA) copy_u(stage, x);
         __builtin_amdgcn_sched_barrier(0);
       }
       advance_copies();
@@ -417,12 +432,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
     // epilogue: one rounding of each fp32 sum.  The MFMA layout leaves each
     // lane with pieces of one row, so a direct store would touch 32 rows per
     // instruction; instead each 32-row slice of the wave tile is written to
-    // LDS (the stage of the tile's last k-step: every wave has read it before
-    // that k-step's barrier, and the next copy into it comes after the next
-    // barrier) and read back row-contiguous, so that a store instruction
-    // writes whole rows of 16-byte pieces.
+    // the wave's share of the LDS behind the stages and read back
+    // row-contiguous, so that a store instruction writes whole rows of
+    // 16-byte pieces.
     {
-      char* ebuf = smem + (stage == 0 ? kStages - 1 : stage - 1) * C::STAGE + wid * C::E_BYTES;
+      char* ebuf = smem + C::E_OFF + wid * C::E_BYTES;
       const uint32_t col0 = uint32_t(ct.n0 + wn * C::WTN) * 2u;
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm) {
