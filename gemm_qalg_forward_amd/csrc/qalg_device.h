@@ -55,6 +55,11 @@ __device__ __forceinline__ void lds_barrier() {
 // c ^ 2 (k & 3).  Both make 8 consecutive lanes of the fragment reads and of
 // the 1 KB direct-to-LDS copies touch distinct bank groups.
 __device__ __forceinline__ int swz_x(int row) { return (row >> 1) & 3; }
+// Contraction-major tile with rows of 64 contraction values (128 bytes): row
+// r keeps its piece c at c ^ ((r >> 1) & 7), so that the 16 rows a
+// quarter-wave reads, and the 8 rows a 1 KB copy writes, fall in distinct
+// bank groups.
+__device__ __forceinline__ int swz_x128(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz_w(int k) { return 2 * (k & 3); }
 
 __device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {

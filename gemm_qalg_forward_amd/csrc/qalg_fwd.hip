@@ -110,10 +110,6 @@ struct FwdCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
-// X tile swizzle: row r keeps its 16-byte piece c (8 contraction values) at
-// c ^ ((r >> 1) & 7), so that the 16 rows a quarter-wave reads, and the 8 rows
-// a 1 KB copy writes, fall in distinct bank groups.
-__device__ __forceinline__ int swz_a(int row) { return (row >> 1) & 7; }
 
 struct FwdArgs {
   const char* X;
@@ -229,7 +225,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   for (int u = 0; u < C::A_DMA; ++u) {
     const int sl = (wid * C::A_DMA + u) * 64 + lane;
     a_row[u] = sl >> 3;
-    a_pc[u] = uint32_t((sl & 7) ^ swz_a(sl >> 3)) * 16u;
+    a_pc[u] = uint32_t((sl & 7) ^ swz_x128(sl >> 3)) * 16u;
   }
   // row ids are fetched one tile ahead of their use (listed schedules only),
   // so that the wait for them overlaps a whole tile
@@ -296,7 +292,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   int a_rd[kQ];
 #pragma unroll
   for (int ks = 0; ks < kQ; ++ks)
-    a_rd[ks] = (wm * C::WTM + l32) * C::AROWB + (((2 * ks + lhi) ^ swz_a(l32)) << 4);
+    a_rd[ks] = (wm * C::WTM + l32) * C::AROWB + (((2 * ks + lhi) ^ swz_x128(l32)) << 4);
   // W fragment (32 columns x 16 contraction) as two transposing 8-byte reads per lane:
   // in a 16-lane group (g = lane / 16, t = lane % 16) lane t reads row 8*(g/2) + t/4 (+4),
   // columns 16*(g%2) + 4*(t%4) of the fragment; the transpose hands lane t column t, 4 rows.

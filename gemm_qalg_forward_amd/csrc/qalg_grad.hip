@@ -20,12 +20,13 @@
 // row-major over the contraction (token rows of X and dY), read into LDS as is
 // and turned into MFMA fragments with the transposing LDS read.
 //
-// Pipeline (shared with the forward): one workgroup per CU, operands copied
-// global -> LDS directly (global_load_lds_dwordx4), four 32-deep stages so
-// that copies run three k-steps ahead, the publishing barrier in the middle of
-// a k-step, MFMAs interleaved one by one with fragment reads (in the order
-// the MFMAs use them) and copies, v_mfma_f32_32x32x16_bf16 on 128x128 wave
-// tiles, one RNE rounding, output restaged through LDS into whole pieces.
+// Pipeline (as in the forward): one workgroup per CU, operands copied
+// global -> LDS directly (global_load_lds_dwordx4); dX in two 64-deep stages
+// (contraction-major rows are whole 128-byte lines; the publishing barrier
+// after the third of four MFMA quarter steps), dW in four 32-deep stages
+// (copies three k-steps ahead; the barrier mid-step); MFMAs interleaved one by one with fragment reads (in the
+// order the MFMAs use them) and copies, v_mfma_f32_32x32x16_bf16 on 128x128
+// wave tiles, one RNE rounding, output restaged through LDS into whole pieces.
 //
 // Work balance.  Long tiles carry q times the contraction of short ones.  The
 // tiles of each XCD (a contiguous share of the long and of the short tiles)
@@ -47,35 +48,49 @@ namespace {
 
 using namespace dev;
 
-constexpr int kBK = 32;      // contraction per k-step
-constexpr int kStages = 4;   // LDS stages
+// Pipeline depth per operation: dX reads both operands contraction-major, so
+// 64-deep k-steps make every row copy a whole 128-byte line (two stages);
+// dW reads token rows that are whole lines already, and keeps 32-deep
+// k-steps in four stages (copies three k-steps ahead), measured faster there.
+constexpr int kBKDx = 64, kBKDw = 32;
 
-template <int BM_, int BN_, bool A_KM_, bool B_KM_>
+template <int BM_, int BN_, bool A_KM_, bool B_KM_, int BK_, int STAGES_>
 struct GradCfg {
+  static constexpr int BK = BK_;          // contraction per k-step
+  static constexpr int STAGES = STAGES_;  // LDS stages
+  static constexpr int Q = BK / 16;       // MFMA quarter steps per k-step
+  static_assert((BK == 64 && STAGES == 2) || (BK == 32 && STAGES == 4), "pipeline shapes");
   static constexpr int BM = BM_, BN = BN_, WGM = 2, WGN = 2;
   static constexpr bool A_KM = A_KM_, B_KM = B_KM_;  // contraction-major (else row-major over it)
   static constexpr int THREADS = 256;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0 && FM >= 1 && FN >= 1, "wave tile");
-  static constexpr int A_BYTES = BM * kBK * 2, B_BYTES = BN * kBK * 2;
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int KROWB = BK * 2;                    // contraction-major layout: bytes per tile row
+  static constexpr int KPC = BK / 8;                      // its 16-byte pieces per row
   static constexpr int A_ROWB = BM * 2, B_ROWB = BN * 2;  // row-major layout: bytes per contraction row
   static constexpr int A_NCH = BM / 8, B_NCH = BN / 8;    // 16-byte pieces per such row
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = kStages * STAGE;
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole 1 KB copies per wave");
   static constexpr int A_DMA = A_BYTES / 4096, B_DMA = B_BYTES / 4096;
   static constexpr int DMA = A_DMA + B_DMA;
-  static_assert((kStages - 1) * DMA < 64, "vmcnt range");
+  static_assert(STAGES * DMA < 64, "vmcnt range");
   // epilogue: each wave restages 32 rows x WTN columns of bf16 at a time in
-  // its share of the stage its tile's last k-step used
+  // its own share of a buffer behind the stages
   static constexpr int E_PITCH = WTN * 2;          // bytes per restaged row
   static constexpr int E_NP = WTN / 8;             // 16-byte pieces per row
   static constexpr int E_BYTES = 32 * E_PITCH;
   static constexpr int E_MASK = E_NP == 12 ? 3 : E_NP - 1;  // piece swizzle: p ^ (row & E_MASK)
-  static_assert(4 * E_BYTES <= STAGE && E_NP % 2 == 0 && (E_NP == 12 || (E_NP & E_MASK) == 0), "epilogue buffer");
+  static_assert(E_NP % 2 == 0 && (E_NP == 12 || (E_NP & E_MASK) == 0), "epilogue buffer");
+  static constexpr int E_OFF = STAGES * STAGE;
+  static constexpr int LDS_BYTES = E_OFF + 4 * E_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
+
+// piece swizzle of a contraction-major tile with rows of BK contraction values
+template <int BK>
+__device__ __forceinline__ int swz_km(int row) { return BK == 64 ? swz_x128(row) : swz_x(row); }
 
 struct GradArgs {
   const char* A;   // dX: dY;  dW: X
@@ -189,7 +204,7 @@ __device__ __forceinline__ GTile decode(const GradArgs& a, cint_ptr s_off, cint_
     }
     t.n0 = k * a.s + cc * C::BN;
     t.c0 = is_long ? 0 : k * a.r;
-    t.nk = uni((is_long ? a.N : a.r) / kBK);
+    t.nk = uni((is_long ? a.N : a.r) / C::BK);
   } else {
     const int tpb = a.rpb * a.cpg;
     const int blk = idx / tpb, w = idx - blk * tpb;
@@ -207,7 +222,7 @@ __device__ __forceinline__ GTile decode(const GradArgs& a, cint_ptr s_off, cint_
     t.n0 = j * a.r + ct * C::BN;
     t.type = is_long ? -1 : b;
     t.c0 = 0;
-    t.nk = uni((is_long ? a.M : a.M / a.q) / kBK);
+    t.nk = uni((is_long ? a.M : a.M / a.q) / C::BK);
   }
   return t;
 }
@@ -235,14 +250,14 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
     g.n_rt = uni(s_toff[q]);
     n_long = g.n_rt * g.cpg;
     n_short = g.n_rt * (q - 1) * g.cpg;
-    t_long = g.N / kBK;
-    t_short = g.r / kBK;
+    t_long = g.N / C::BK;
+    t_short = g.r / C::BK;
   } else {
     const int tpb = g.rpb * g.cpg;
     n_long = q * tpb;
     n_short = q * (q - 1) * tpb;
-    t_long = g.M / kBK;
-    t_short = g.M / q / kBK;
+    t_long = g.M / C::BK;
+    t_short = g.M / q / C::BK;
   }
 
   const int nx = gridDim.x >= 8 ? 8 : 1;
@@ -270,8 +285,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   for (int u = 0; u < C::A_DMA; ++u) {
     const int sl = (wid * C::A_DMA + u) * 64 + lane;
     if constexpr (C::A_KM) {
-      a_r[u] = sl >> 2;
-      a_c[u] = (sl & 3) ^ swz_x(sl >> 2);
+      a_r[u] = sl / C::KPC;
+      a_c[u] = (sl % C::KPC) ^ swz_km<C::BK>(sl / C::KPC);
     } else {
       a_r[u] = sl / C::A_NCH;
       a_c[u] = (sl - (sl / C::A_NCH) * C::A_NCH) ^ swz_w(sl / C::A_NCH);
@@ -281,8 +296,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   for (int u = 0; u < C::B_DMA; ++u) {
     const int sl = (wid * C::B_DMA + u) * 64 + lane;
     if constexpr (C::B_KM) {
-      b_r[u] = sl >> 2;
-      b_c[u] = (sl & 3) ^ swz_x(sl >> 2);
+      b_r[u] = sl / C::KPC;
+      b_c[u] = (sl % C::KPC) ^ swz_km<C::BK>(sl / C::KPC);
     } else {
       b_r[u] = sl / C::B_NCH;
       b_c[u] = (sl - (sl / C::B_NCH) * C::B_NCH) ^ swz_w(sl / C::B_NCH);
@@ -295,10 +310,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   int cp_kc = 0, cp_start = 0, cp_rbase = 0, cp_rstep = 1;
   auto prep_copies = [&]() {
     if constexpr (OP == Op::Dx) {
-      cp_kc = lt.c0 + lk * kBK;
+      cp_kc = lt.c0 + lk * C::BK;
       cp_start = type_start(lt.type);
     } else {
-      const int k0 = lk * kBK;
+      const int k0 = lk * C::BK;
       cp_rbase = lt.type < 0 ? k0 : type_start(lt.type) + k0 * q;
       cp_rstep = lt.type < 0 ? 1 : q;
     }
@@ -356,7 +371,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   const int wm = wid / C::WGN, wn = wid % C::WGN;
   const int l32 = lane & 31, lhi = lane >> 5;
   // contraction-major operand: 128-bit read of row l32, piece 2*ks + lhi
-  auto km_rd = [&](int w0, int ks) { return (w0 + l32) * 64 + (((2 * ks + lhi) ^ swz_x(l32)) << 4); };
+  auto km_rd = [&](int w0, int ks) { return (w0 + l32) * C::KROWB + (((2 * ks + lhi) ^ swz_km<C::BK>(l32)) << 4); };
   // row-major operand with rows of rowb bytes: per-lane offsets of the two
   // transposing reads, by parity of the fragment's 32-column block index
   auto rm_rd = [&](int rowb, int par) {
@@ -368,11 +383,13 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
     const int dm = (f >> 2) ? 64 : 0;
     return par == 0 ? lo + dm : lo - dm;
   };
-  int a_rd[2], b_rd[2];
+  // contraction-major: one offset per quarter step; row-major: one per
+  // parity of the 32-column block index (entries 2, 3 unused)
+  int a_rd[C::Q], b_rd[C::Q];
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    a_rd[x] = C::A_KM ? km_rd(wm * C::WTM, x) : rm_rd(C::A_ROWB, x);
-    b_rd[x] = C::A_BYTES + (C::B_KM ? km_rd(wn * C::WTN, x) : rm_rd(C::B_ROWB, x));
+  for (int x = 0; x < C::Q; ++x) {
+    a_rd[x] = C::A_KM ? km_rd(wm * C::WTM, x) : rm_rd(C::A_ROWB, x & 1);
+    b_rd[x] = C::A_BYTES + (C::B_KM ? km_rd(wn * C::WTN, x) : rm_rd(C::B_ROWB, x & 1));
   }
   const int am0 = wm * (C::WTM / 32), bm0 = wn * (C::WTN / 32);
 
@@ -381,7 +398,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   auto read_a = [&](int stage, int ks, int fm) -> bf16x8 {
     const char* S = smem + stage * C::STAGE;
     if constexpr (C::A_KM) {
-      return *reinterpret_cast<const bf16x8*>(S + a_rd[ks] + fm * 32 * 64);
+      return *reinterpret_cast<const bf16x8*>(S + a_rd[ks] + fm * 32 * C::KROWB);
     } else {
       const int m = am0 + fm;
       const char* p = S + a_rd[m & 1] + 64 * m + 16 * ks * C::A_ROWB;
@@ -393,7 +410,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   auto read_b = [&](int stage, int ks, int fn) -> bf16x8 {
     const char* S = smem + stage * C::STAGE;
     if constexpr (C::B_KM) {
-      return *reinterpret_cast<const bf16x8*>(S + b_rd[ks] + fn * 32 * 64);
+      return *reinterpret_cast<const bf16x8*>(S + b_rd[ks] + fn * 32 * C::KROWB);
     } else {
       const int m = bm0 + fn;
       const char* p = S + b_rd[m & 1] + 64 * m + 16 * ks * C::B_ROWB;
@@ -420,9 +437,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   };
 
   // ---------------- pipeline (as in the forward) ----------------
+  static_assert(C::FM + C::FN <= C::FM * C::FN, "fragment reads fit a quarter step");
+  constexpr int S = C::STAGES;
 #pragma unroll
-  for (int st = 0; st < kStages - 1; ++st) issue_copies(st);
-  wait_vmcnt<(kStages - 2) * C::DMA>();
+  for (int st = 0; st < S - 1 + (S == 2 ? 1 : 0); ++st) issue_copies(st);
+  // two stages: step 1 may be in flight; four: steps 1 and 2
+  wait_vmcnt<(S == 2 ? 1 : 2) * C::DMA>();
   lds_barrier();
   load_frags(0, 0, fa0, fb0);
 
@@ -433,6 +453,39 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   dcomp.next(&c_long, &c_idx);
   GTile ct = decode<C, OP>(g, s_off, s_toff, c_long, uni(c_idx));
   int stage = 0;  // LDS stage of the current k-step
+  // one quarter step: MFMAs on fragments (fa, fb) of quarter ks, each followed
+  // by one read of quarter ks + 1's fragments into (ga, gb)
+  auto quarter = [&](int ks, const bf16x8 (&fa)[C::FM], const bf16x8 (&fb)[C::FN], bf16x8 (&ga)[C::FM],
+                     bf16x8 (&gb)[C::FN]) {
+#pragma unroll
+    for (int x = 0; x < C::FM * C::FN; ++x) {
+      const int fm = x / C::FN, fn = x % C::FN;
+      acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], acc[fm][fn], 0, 0, 0);
+      if (x < C::FM + C::FN) read_slot(x, stage, ks + 1, ga, gb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // last quarter: MFMAs on fragments 1 interleaved with the reads of the next
+  // k-step's first fragments from stage nstage (stale past the last k-step,
+  // never used) and the copies into stage cstage.  With two stages the copies
+  // start with the reads (one of each per MFMA); with four they follow the
+  // reads.  Narrow tiles have fewer MFMAs than reads and copies, the slots
+  // past the last MFMA carry the rest.
+  auto last_quarter = [&](int nstage, int cstage) {
+    constexpr int R = C::FM + C::FN;
+    constexpr int C0 = S == 2 ? 0 : R;  // slot of the first copy
+    constexpr int kSlots = C::FM * C::FN > C0 + C::DMA ? C::FM * C::FN : C0 + C::DMA;
+#pragma unroll
+    for (int x = 0; x < kSlots; ++x) {
+      if (x < C::FM * C::FN) {
+        const int fm = x / C::FN, fn = x % C::FN;
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[fn], fa1[fm], acc[fm][fn], 0, 0, 0);
+      }
+      if (x < R) read_slot(x, nstage, 0, fa0, fb0);
+      if (x >= C0 && x - C0 < C::DMA) copy_u(cstage, x - C0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   for (;;) {
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
@@ -440,48 +493,38 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
       for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = (f32x16){};
 
     for (int ck = 0; ck < ct.nk; ++ck) {
-      // first half: MFMAs on fragments 0 interleaved with the reads of fragments 1
-      static_assert(C::FM + C::FN <= C::FM * C::FN, "fragment reads fit the first half");
-#pragma unroll
-      for (int x = 0; x < C::FM * C::FN; ++x) {
-        const int fm = x / C::FN, fn = x % C::FN;
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[fn], fa0[fm], acc[fm][fn], 0, 0, 0);
-        if (x < C::FM + C::FN) read_slot(x, stage, 1, fa1, fb1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // the copies of the next k-step are complete when at most those of the
-      // kStages-3 k-steps after it are still in flight
-      wait_vmcnt<(kStages - 3) * C::DMA>();
-      lds_barrier();
-      const int cstage = stage == 0 ? kStages - 1 : stage - 1;  // consumed by the previous k-step
-      prep_copies();
-      const int nstage = stage == kStages - 1 ? 0 : stage + 1;
-      // second half: MFMAs on fragments 1 interleaved with the reads of the next
-      // k-step's fragments 0 (stale past the last k-step, never used) and the
-      // copies of the k-step kStages-1 ahead; narrow tiles have fewer MFMAs
-      // than reads and copies, the slots past the last MFMA carry the rest
-      constexpr int kSlots = C::FM * C::FN > C::DMA + C::FM + C::FN ? C::FM * C::FN : C::DMA + C::FM + C::FN;
-#pragma unroll
-      for (int x = 0; x < kSlots; ++x) {
-        if (x < C::FM * C::FN) {
-          const int fm = x / C::FN, fn = x % C::FN;
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[fn], fa1[fm], acc[fm][fn], 0, 0, 0);
-        }
-        if (x < C::FM + C::FN)
-          read_slot(x, nstage, 0, fa0, fb0);
-        else if (x - (C::FM + C::FN) < C::DMA)
-          copy_u(cstage, x - (C::FM + C::FN));
-        __builtin_amdgcn_sched_barrier(0);
+      if constexpr (S == 2) {
+        // 64-deep k-step: the barrier after the third quarter publishes the
+        // next stage (the only copies in flight) and frees this one, which the
+        // last quarter refills with the k-step after next
+        quarter(0, fa0, fb0, fa1, fb1);
+        quarter(1, fa1, fb1, fa0, fb0);
+        quarter(2, fa0, fb0, fa1, fb1);
+        wait_vmcnt<0>();
+        lds_barrier();
+        prep_copies();
+        last_quarter(stage ^ 1, stage);
+        stage = uni(stage ^ 1);
+      } else {
+        // 32-deep k-step: the barrier in the middle publishes the next stage
+        // (at most the copies of the k-step after it still in flight); the
+        // second half refills the stage consumed by the previous k-step
+        quarter(0, fa0, fb0, fa1, fb1);
+        wait_vmcnt<C::DMA>();
+        lds_barrier();
+        prep_copies();
+        const int nstage = (stage + 1) & 3;
+        last_quarter(nstage, (stage + 3) & 3);
+        stage = uni(nstage);
       }
       advance_copies();
-      stage = uni(nstage);
     }
 
-    // epilogue: one rounding of each fp32 sum, restaged through LDS (the stage
-    // of the tile's last k-step, free until the next k-step's barrier) so that
-    // each store instruction writes whole 16-byte pieces of a few rows
+    // epilogue: one rounding of each fp32 sum, restaged through the wave's
+    // share of the LDS behind the stages so that each store instruction
+    // writes whole 16-byte pieces of a few rows
     {
-      char* ebuf = smem + (stage == 0 ? kStages - 1 : stage - 1) * C::STAGE + wid * C::E_BYTES;
+      char* ebuf = smem + C::E_OFF + wid * C::E_BYTES;
       const uint32_t col0 = uint32_t(ct.n0 + wn * C::WTN) * 2u;
       const int ostart = OP == Op::Dx ? type_start(ct.type) : 0;
 #pragma unroll
@@ -519,9 +562,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
 }
 
 template <int BN>
-using DxCfg = GradCfg<256, BN, true, true>;
+using DxCfg = GradCfg<256, BN, true, true, kBKDx, 2>;
 template <int BN>
-using DwCfg = GradCfg<256, BN, false, false>;
+using DwCfg = GradCfg<256, BN, false, false, kBKDw, 4>;
 
 int cu_count() {
   static int n = 0;
@@ -584,11 +627,11 @@ bool grad_persistent_supported(const ProblemDesc& p) {
   if (p.op == Op::Dx) {
     // rows of a type in 256-row tiles; columns of an input group in BN tiles;
     // contraction lengths N and r in whole k-steps
-    return (p.M + p.q - 1) / p.q >= 128 && pick_bn(s) != 0 && r % kBK == 0;
+    return (p.M + p.q - 1) / p.q >= 128 && pick_bn(s) != 0 && r % kBKDx == 0;
   }
   // features of a group in 256-row tiles, output group columns in BN tiles,
   // every type's rows (M / q of a cyclic schedule) in whole k-steps
-  return s % 256 == 0 && pick_bn(r) != 0 && p.M % (int64_t(kBK) * p.q) == 0 && p.M >= int64_t(kBK) * p.q;
+  return s % 256 == 0 && pick_bn(r) != 0 && p.M % (int64_t(kBKDw) * p.q) == 0 && p.M >= int64_t(kBKDw) * p.q;
 }
 
 hipError_t launch_grad_persistent_bf16(const ProblemDesc& p, hipStream_t s) {
