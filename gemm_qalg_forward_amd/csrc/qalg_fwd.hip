@@ -20,12 +20,13 @@
 // The k-steps of all its tiles form one stream: operand loads for the next
 // k-step, and across a tile boundary for the next tile's first k-step, are in
 // flight while the current k-step runs on the matrix cores, so a tile costs
-// no pipeline fill.  Tiles are ordered in groups of up to 4 row tiles by all
-// column tiles (neighbouring tiles share operand rows or weight columns), the
-// order is cut into one contiguous chunk per XCD (workgroup w runs on XCD
+// no pipeline fill.  Long tiles (two contraction segments) and short ones
+// (one) are ordered separately in groups of up to 4 row tiles by the class's
+// column tiles (neighbouring tiles share operand rows or weight columns); each
+// order is cut into one contiguous share per XCD (workgroup w runs on XCD
 // w mod 8 when the grid is one workgroup per CU), and the workgroups of an XCD
-// take that chunk round robin, so concurrently running tiles of one XCD share
-// their operands in that XCD's L2.
+// are dealt the longs round robin, then the shorts, balanced in k-steps, so
+// concurrently running tiles of one XCD share their operands in its L2.
 //
 // Data movement.  Operands go from global memory straight into LDS with the
 // gfx950 direct-to-LDS copy (global_load_lds_dwordx4: 16 bytes per lane, a
@@ -134,19 +135,31 @@ struct Tile {
   int nk;         // k-steps
 };
 
+// Tiles come in two lengths: "long" tiles (output group j != row type i, two
+// contraction segments) and "short" ones (j == i, one segment).  Each class is
+// ordered in groups of up to 4 row tiles x the class's column tiles, row tile
+// fastest (measured against 2, 8 and 16 row tiles: the least L2 refetch for
+// 256x256 tiles); idx is the tile's position in its class.
 template <class C>
-__device__ __forceinline__ Tile decode_tile(const FwdArgs& a, cint_ptr offsets, cint_ptr tile_off, int n_rt, int L) {
-  // groups of up to 4 row tiles x all column tiles, row tile fastest (measured
-  // against 2, 8 and 16 row tiles: the least L2 refetch for 256x256 tiles)
+__device__ __forceinline__ Tile decode_tile(const FwdArgs& a, cint_ptr offsets, cint_ptr tile_off, int n_rt,
+                                            bool is_long, int idx) {
   constexpr int G = 4;
-  const int span = G * a.n_ct;
-  const int g = L / span;
+  const int ncol = is_long ? (a.q - 1) * a.cpg : a.cpg;  // column tiles of the class per row tile
+  const int span = G * ncol;
+  const int g = idx / span;
   const int first_rt = g * G;
   const int gm = min(n_rt - first_rt, G);
-  const int w = L - g * span;
+  const int w = idx - g * span;
   const int rt = first_rt + w % gm;
-  const int ct = w / gm;
+  const int c2 = w / gm;
   const int i = find_group(tile_off, a.q, rt);
+  int ct;
+  if (is_long) {
+    const int jj = c2 / a.cpg, cc = c2 - jj * a.cpg;
+    ct = (jj < i ? jj : jj + 1) * a.cpg + cc;  // output groups other than i
+  } else {
+    ct = i * a.cpg + c2;
+  }
   Tile t;
   t.i = i;
   t.rank0 = (rt - uni(tile_off[i])) * C::BM;
@@ -185,16 +198,21 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
     }
   }
 
-  // this workgroup's tiles: a contiguous chunk per XCD, round robin inside it
+  // this workgroup's tiles: contiguous shares of the long and of the short
+  // tiles per XCD (workgroup w runs on XCD w mod 8 when the grid is one
+  // workgroup per CU), dealt so that k-steps per workgroup are balanced
   const int n_rt = uni(s_toff[a.q]);
-  const int total = n_rt * a.n_ct;
+  const int n_long = n_rt * (a.q - 1) * a.cpg, n_short = n_rt * a.cpg;
   const int nx = gridDim.x >= 8 ? 8 : 1;
   const int per_x = gridDim.x / nx;
   const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx;
   if (slot >= per_x) return;  // grid not a multiple of 8: the remainder idles
-  const int c_lo = int(int64_t(total) * xcd / nx), c_hi = int(int64_t(total) * (xcd + 1) / nx);
-  const int L_first = c_lo + slot;
-  if (L_first >= c_hi) return;
+  TileDeal dcopy, dcomp;
+  dcopy.init(n_long, n_short, 2 * a.kts, a.kts, xcd, nx, slot, per_x);
+  dcomp = dcopy;
+  bool l_long;
+  int l_idx;
+  if (!dcopy.next(&l_long, &l_idx)) return;
 
   const uint32_t n_bytes = uint32_t(a.N) * 2u;
   const uint32_t k_bytes = uint32_t(a.K) * 2u;
@@ -240,11 +258,15 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
     for (int u = 0; u < C::A_DMA; ++u) a_src[u] = uint32_t(pre_row[u]) * k_bytes + a_pc[u];
   };
 
-  Tile lt = decode_tile<C>(a, s_off, s_toff, n_rt, L_first);
-  int lL = L_first, lk = 0;
+  // copy cursor: tile lt at k-step lk; the tile after it is decoded ahead so
+  // that a listed schedule's row ids are fetched a whole tile before use
+  Tile lt = decode_tile<C>(a, s_off, s_toff, n_rt, l_long, uni(l_idx));
+  int lk = 0;
+  bool have_next = dcopy.next(&l_long, &l_idx);
+  Tile nt = have_next ? decode_tile<C>(a, s_off, s_toff, n_rt, l_long, uni(l_idx)) : lt;
   prefetch_rows(lt);
   take_rows();
-  if (lL + per_x < c_hi) prefetch_rows(decode_tile<C>(a, s_off, s_toff, n_rt, lL + per_x));
+  if (have_next) prefetch_rows(nt);
   bool more = true;  // the copy cursor has not passed the last k-step
   // copy cursor split in three so that the copies can be interleaved with MFMAs
   uint32_t cp_x = 0, cp_w = 0;  // per-step byte offsets of the X and W pieces
@@ -266,15 +288,18 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   // that the pipeline needs no conditions (they are drained before exit).
   auto advance_copies = [&]() {
     if (more && (lk = uni(lk + 1)) >= lt.nk) {
-      if (lL + per_x >= c_hi) {
+      if (!have_next) {
         more = false;
         lk = uni(lt.nk - 1);
       } else {
-        lL = uni(lL + per_x);
-        lt = decode_tile<C>(a, s_off, s_toff, n_rt, lL);
+        lt = nt;
         lk = 0;
         take_rows();
-        if (lL + per_x < c_hi) prefetch_rows(decode_tile<C>(a, s_off, s_toff, n_rt, lL + per_x));
+        have_next = dcopy.next(&l_long, &l_idx);
+        if (have_next) {
+          nt = decode_tile<C>(a, s_off, s_toff, n_rt, l_long, uni(l_idx));
+          prefetch_rows(nt);
+        }
       }
     }
   };
@@ -369,8 +394,10 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   lds_barrier();
   load_frags(0, 0, fa0, fb0);
 
-  Tile ct = decode_tile<C>(a, s_off, s_toff, n_rt, L_first);
-  int cL = L_first;
+  bool c_long;
+  int c_idx;
+  dcomp.next(&c_long, &c_idx);
+  Tile ct = decode_tile<C>(a, s_off, s_toff, n_rt, c_long, uni(c_idx));
   int stage = 0;  // LDS stage of the current k-step (k-step mod 2)
   static_assert(C::FM + C::FN <= C::FM * C::FN, "fragment reads fit a quarter step");
   // one quarter step: MFMAs on fragments (fa, fb) of quarter ks, each followed
@@ -464,9 +491,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
         }
       }
     }
-    cL = uni(cL + per_x);
-    if (cL >= c_hi) break;
-    ct = decode_tile<C>(a, s_off, s_toff, n_rt, cL);
+    if (!dcomp.next(&c_long, &c_idx)) break;
+    ct = decode_tile<C>(a, s_off, s_toff, n_rt, c_long, uni(c_idx));
   }
   // the repeated copies past the last k-step land in LDS: drain them before
   // the workgroup's LDS can be handed to another workgroup

@@ -114,64 +114,6 @@ struct GTile {
   int nk;          // k-steps
 };
 
-// Tile list of a workgroup: a contiguous share of the long and of the short
-// tiles per XCD, dealt so that the k-steps per workgroup are balanced.
-struct TileDeal {
-  int lx0, lx1, sx0, sx1;   // this XCD's long and short tile ranges
-  int g, G;                 // slot inside the XCD, workgroups per XCD
-  int light, lg, G_light, E, base;
-  int phase, k;
-  __device__ void init(int n_long, int n_short, int t_long, int t_short, int xcd, int nx, int slot, int per_x) {
-    lx0 = int(int64_t(n_long) * xcd / nx);
-    lx1 = int(int64_t(n_long) * (xcd + 1) / nx);
-    sx0 = int(int64_t(n_short) * xcd / nx);
-    sx1 = int(int64_t(n_short) * (xcd + 1) / nx);
-    g = slot;
-    G = per_x;
-    const int nl = lx1 - lx0, ns = sx1 - sx0;
-    const int rem = nl % G;
-    light = rem != 0 && g >= rem;
-    G_light = rem != 0 ? G - rem : 0;
-    lg = g - rem;
-    const int e = t_short > 0 ? t_long / t_short : 0;
-    E = (rem != 0) ? min(e, ns / G_light) : 0;
-    base = G_light * E;
-    phase = 0;
-    k = 0;
-  }
-  // next tile: returns false at the end; *is_long and *idx (global class index) otherwise
-  __device__ bool next(bool* is_long, int* idx) {
-    if (phase == 0) {
-      const int i = lx0 + g + k * G;
-      if (i < lx1) {
-        ++k;
-        *is_long = true;
-        *idx = i;
-        return true;
-      }
-      phase = 1;
-      k = 0;
-    }
-    if (phase == 1) {
-      if (light && k < E) {
-        *is_long = false;
-        *idx = sx0 + lg + k * G_light;
-        ++k;
-        return true;
-      }
-      phase = 2;
-      k = 0;
-    }
-    const int i = sx0 + base + g + k * G;
-    if (i < sx1) {
-      ++k;
-      *is_long = false;
-      *idx = i;
-      return true;
-    }
-    return false;
-  }
-};
 
 // Tile decode.  dX long tiles: (row tile, column tile of the row's own group);
 // short: (row tile, other group, column tile); both in groups of 4 row tiles
