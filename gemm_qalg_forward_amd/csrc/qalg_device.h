@@ -93,6 +93,59 @@ __device__ __forceinline__ int find_group(P tile_off, int q, int rt) {
   return lo;
 }
 
+// Type index of a cyclic schedule (tau[m] = (o + m) mod q for every row m),
+// in closed form: type i has M / q rows, plus one when (i - o) mod q <
+// M mod q; row tiles are tile_h rows of one type.  Decoding a tile then needs
+// no memory access (the workspace's tables hold the same numbers).
+struct CycIndex {
+  int q, o, base, rem, tile_h, per_type, uniform;
+  __device__ static CycIndex make(int q, int o, int M, int tile_h) {
+    CycIndex c;
+    c.q = q;
+    c.o = o;
+    c.base = M / q;
+    c.rem = M - c.base * q;
+    c.tile_h = tile_h;
+    // every type has the same tile count unless an extra row opens a tile
+    c.uniform = c.rem == 0 || c.base % tile_h != 0;
+    c.per_type = c.uniform ? (c.base + tile_h - 1) / tile_h : c.base / tile_h;
+    return c;
+  }
+  // types j < i among the cyclic interval [o, o + rem) of types with an extra row
+  __device__ int extra_before(int i) const {
+    if (rem == 0) return 0;
+    const int end = o + rem;
+    int c = max(0, min(i, end) - o);
+    if (end > q) c += min(i, end - q);
+    return c;
+  }
+  __device__ int count(int i) const { return base + (extra_before(i + 1) - extra_before(i)); }
+  __device__ int offset(int i) const { return i * base + extra_before(i); }  // first slot of type i
+  __device__ int tiles_before(int i) const { return i * per_type + (uniform ? 0 : extra_before(i)); }
+  __device__ int group_of_tile(int rt) const {
+    if (uniform) return per_type > 0 ? min(rt / per_type, q - 1) : 0;
+    int lo = 0, hi = q;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tiles_before(mid) <= rt)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    return lo;
+  }
+};
+
+// The same queries answered from the index workspace's tables (any schedule).
+struct MemIndex {
+  cint_ptr offsets, tile_off;
+  int q;
+  __device__ int count(int i) const { return uni(offsets[i + 1]) - uni(offsets[i]); }
+  __device__ int offset(int i) const { return uni(offsets[i]); }
+  __device__ int tiles_before(int i) const { return uni(tile_off[i]); }
+  __device__ int group_of_tile(int rt) const { return find_group(tile_off, q, rt); }
+};
+
 // Tile list of a workgroup in a persistent grid whose tiles come in two
 // lengths (t_long and t_short k-steps).  Each XCD takes a contiguous share of
 // the long and of the short tiles; its workgroups are dealt the longs round

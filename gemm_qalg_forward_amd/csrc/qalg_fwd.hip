@@ -65,6 +65,8 @@
 //
 // Rows whose type is out of range (listed after all typed rows by the index)
 // are written as zero by the same launch.
+#include <type_traits>
+
 #include "qalg.h"
 #include "qalg_internal.h"
 #include "qalg_device.h"
@@ -140,9 +142,8 @@ struct Tile {
 // ordered in groups of up to 4 row tiles x the class's column tiles, row tile
 // fastest (measured against 2, 8 and 16 row tiles: the least L2 refetch for
 // 256x256 tiles); idx is the tile's position in its class.
-template <class C>
-__device__ __forceinline__ Tile decode_tile(const FwdArgs& a, cint_ptr offsets, cint_ptr tile_off, int n_rt,
-                                            bool is_long, int idx) {
+template <class C, class IX>
+__device__ __forceinline__ Tile decode_tile(const FwdArgs& a, const IX& ix, int n_rt, bool is_long, int idx) {
   constexpr int G = 4;
   const int ncol = is_long ? (a.q - 1) * a.cpg : a.cpg;  // column tiles of the class per row tile
   const int span = G * ncol;
@@ -152,7 +153,7 @@ __device__ __forceinline__ Tile decode_tile(const FwdArgs& a, cint_ptr offsets, 
   const int w = idx - g * span;
   const int rt = first_rt + w % gm;
   const int c2 = w / gm;
-  const int i = find_group(tile_off, a.q, rt);
+  const int i = ix.group_of_tile(rt);
   int ct;
   if (is_long) {
     const int jj = c2 / a.cpg, cc = c2 - jj * a.cpg;
@@ -162,9 +163,9 @@ __device__ __forceinline__ Tile decode_tile(const FwdArgs& a, cint_ptr offsets, 
   }
   Tile t;
   t.i = i;
-  t.rank0 = (rt - uni(tile_off[i])) * C::BM;
-  t.first = uni(offsets[i]) + t.rank0;
-  t.m_cnt = min(C::BM, uni(offsets[i + 1]) - t.first);
+  t.rank0 = (rt - ix.tiles_before(i)) * C::BM;
+  t.first = ix.offset(i) + t.rank0;
+  t.m_cnt = min(C::BM, ix.count(i) - t.rank0);
   const int j = ct / a.cpg, cc = ct - j * a.cpg;
   t.n0 = j * a.r + cc * C::BN;
   t.seg0 = i * a.s;
@@ -186,6 +187,14 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   // also counts the copies in flight, and the LDS is left to the stages)
   const cint_ptr s_off = to_const(ws + a.off_offsets);
   const cint_ptr s_toff = to_const(ws + a.off_tiles + tile_height_slot(BM) * (a.q + 1));
+  // tile decoding: closed form for a cyclic schedule (no memory access on the
+  // way to the next tile), the index tables otherwise
+  using IX = std::conditional_t<CYC, CycIndex, MemIndex>;
+  IX ix;
+  if constexpr (CYC)
+    ix = CycIndex::make(a.q, uni(ws[4]), a.M, BM);
+  else
+    ix = MemIndex{s_off, s_toff, a.q};
 
   // rows of an out-of-range type: zero output rows (rare)
   {
@@ -201,7 +210,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   // this workgroup's tiles: contiguous shares of the long and of the short
   // tiles per XCD (workgroup w runs on XCD w mod 8 when the grid is one
   // workgroup per CU), dealt so that k-steps per workgroup are balanced
-  const int n_rt = uni(s_toff[a.q]);
+  const int n_rt = ix.tiles_before(a.q);
   const int n_long = n_rt * (a.q - 1) * a.cpg, n_short = n_rt * a.cpg;
   const int nx = gridDim.x >= 8 ? 8 : 1;
   const int per_x = gridDim.x / nx;
@@ -260,10 +269,10 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
 
   // copy cursor: tile lt at k-step lk; the tile after it is decoded ahead so
   // that a listed schedule's row ids are fetched a whole tile before use
-  Tile lt = decode_tile<C>(a, s_off, s_toff, n_rt, l_long, uni(l_idx));
+  Tile lt = decode_tile<C>(a, ix, n_rt, l_long, uni(l_idx));
   int lk = 0;
   bool have_next = dcopy.next(&l_long, &l_idx);
-  Tile nt = have_next ? decode_tile<C>(a, s_off, s_toff, n_rt, l_long, uni(l_idx)) : lt;
+  Tile nt = have_next ? decode_tile<C>(a, ix, n_rt, l_long, uni(l_idx)) : lt;
   prefetch_rows(lt);
   take_rows();
   if (have_next) prefetch_rows(nt);
@@ -297,7 +306,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
         take_rows();
         have_next = dcopy.next(&l_long, &l_idx);
         if (have_next) {
-          nt = decode_tile<C>(a, s_off, s_toff, n_rt, l_long, uni(l_idx));
+          nt = decode_tile<C>(a, ix, n_rt, l_long, uni(l_idx));
           prefetch_rows(nt);
         }
       }
@@ -397,7 +406,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   bool c_long;
   int c_idx;
   dcomp.next(&c_long, &c_idx);
-  Tile ct = decode_tile<C>(a, s_off, s_toff, n_rt, c_long, uni(c_idx));
+  Tile ct = decode_tile<C>(a, ix, n_rt, c_long, uni(c_idx));
   int stage = 0;  // LDS stage of the current k-step (k-step mod 2)
   static_assert(C::FM + C::FN <= C::FM * C::FN, "fragment reads fit a quarter step");
   // one quarter step: MFMAs on fragments (fa, fb) of quarter ks, each followed
@@ -492,7 +501,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
       }
     }
     if (!dcomp.next(&c_long, &c_idx)) break;
-    ct = decode_tile<C>(a, s_off, s_toff, n_rt, c_long, uni(c_idx));
+    ct = decode_tile<C>(a, ix, n_rt, c_long, uni(c_idx));
   }
   // the repeated copies past the last k-step land in LDS: drain them before
   // the workgroup's LDS can be handed to another workgroup

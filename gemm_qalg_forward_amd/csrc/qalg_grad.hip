@@ -120,8 +120,7 @@ struct GTile {
 // by all columns, row tile fastest.  dW long tiles: (block b == j, row tile,
 // column tile); short: (b, j != b, row tile, column tile), b slowest.
 template <class C, Op OP>
-__device__ __forceinline__ GTile decode(const GradArgs& a, cint_ptr s_off, cint_ptr s_toff,
-                                        bool is_long, int idx) {
+__device__ __forceinline__ GTile decode(const GradArgs& a, const CycIndex& ix, bool is_long, int idx) {
   GTile t;
   if constexpr (OP == Op::Dx) {
     constexpr int G = 4;
@@ -131,10 +130,10 @@ __device__ __forceinline__ GTile decode(const GradArgs& a, cint_ptr s_off, cint_
     const int first_rt = grp * G;
     const int gm = min(a.n_rt - first_rt, G);
     const int rt = first_rt + w % gm, ct = w / gm;
-    const int i = find_group(s_toff, a.q, rt);
+    const int i = ix.group_of_tile(rt);
     t.type = i;
-    t.out_row0 = (rt - uni(s_toff[i])) * C::BM;
-    t.m_cnt = min(C::BM, (uni(s_off[i + 1]) - uni(s_off[i])) - t.out_row0);
+    t.out_row0 = (rt - ix.tiles_before(i)) * C::BM;
+    t.m_cnt = min(C::BM, ix.count(i) - t.out_row0);
     int k, cc;
     if (is_long) {
       k = i;
@@ -180,16 +179,15 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // per-type row offsets and row-tile offsets through the scalar data cache
-  const cint_ptr s_off = to_const(ws + a.off_offsets);
-  const cint_ptr s_toff = to_const(ws + a.off_tiles + tile_height_slot(C::BM) * (q + 1));
+  // the type index of the cyclic schedule, in closed form
+  const CycIndex ix = CycIndex::make(q, uni(cyc), a.M, C::BM);
   // first row of each type in the cyclic schedule
   auto type_start = [&](int i) { return i >= cyc ? i - cyc : i - cyc + q; };
 
   GradArgs g = a;
   int n_long, n_short, t_long, t_short;
   if constexpr (OP == Op::Dx) {
-    g.n_rt = uni(s_toff[q]);
+    g.n_rt = ix.tiles_before(q);
     n_long = g.n_rt * g.cpg;
     n_short = g.n_rt * (q - 1) * g.cpg;
     t_long = g.N / C::BK;
@@ -217,7 +215,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   bool l_long;
   int l_idx;
   if (!dcopy.next(&l_long, &l_idx)) return;
-  GTile lt = decode<C, OP>(g, s_off, s_toff, l_long, l_idx);
+  GTile lt = decode<C, OP>(g, ix, l_long, l_idx);
   int lk = 0;
   bool more = true;  // the copy cursor has not passed the last k-step
 
@@ -294,7 +292,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   auto advance_copies = [&]() {
     if (more && (lk = uni(lk + 1)) >= lt.nk) {
       if (dcopy.next(&l_long, &l_idx)) {
-        lt = decode<C, OP>(g, s_off, s_toff, l_long, uni(l_idx));
+        lt = decode<C, OP>(g, ix, l_long, uni(l_idx));
         lk = 0;
       } else {
         more = false;
@@ -393,7 +391,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   bool c_long;
   int c_idx;
   dcomp.next(&c_long, &c_idx);
-  GTile ct = decode<C, OP>(g, s_off, s_toff, c_long, uni(c_idx));
+  GTile ct = decode<C, OP>(g, ix, c_long, uni(c_idx));
   int stage = 0;  // LDS stage of the current k-step
   // one quarter step: MFMAs on fragments (fa, fb) of quarter ks, each followed
   // by one read of quarter ks + 1's fragments into (ga, gb)
@@ -496,7 +494,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
       }
     }
     if (!dcomp.next(&c_long, &c_idx)) break;
-    ct = decode<C, OP>(g, s_off, s_toff, c_long, uni(c_idx));
+    ct = decode<C, OP>(g, ix, c_long, uni(c_idx));
   }
   // the repeated copies past the last k-step land in LDS: drain them before
   // the workgroup's LDS can be handed to another workgroup

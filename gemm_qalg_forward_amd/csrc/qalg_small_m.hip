@@ -28,10 +28,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kSmThreads = 256;
-constexpr int kSmCols = 64;            // output columns per workgroup
-constexpr int kSmKLanes = kSmThreads / (kSmCols / 8);  // 32 weight rows in flight per step
+
 constexpr int kSmMaxRows = 8;
-constexpr int kSmUnroll = 4;
+constexpr int kSmUnroll = 8;          // weight loads per thread per batch; two batches in flight
 constexpr int kSmMaxXs = 16384;        // bf16 elements of staged activations (32 KB)
 
 struct SmallArgs {
@@ -46,8 +45,15 @@ struct SmallArgs {
 __device__ __forceinline__ float lo_bf16(unsigned u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_bf16(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
 
-template <int R>
+// COLS output columns per workgroup: each weight row is read as COLS * 2
+// contiguous bytes, 16 per lane (wider rows stream better; narrower ones give
+// more workgroups)
+template <int R, int COLS>
 __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
+  constexpr int kSmCols = COLS;
+  constexpr int kSmColLanes = kSmCols / 8;             // lanes per weight row (16 bytes each)
+  constexpr int kSmKLanes = kSmThreads / kSmColLanes;  // weight rows in flight per step
+  static_assert(kSmColLanes <= 64 && 64 % kSmColLanes == 0, "a weight row within one wave");
   extern __shared__ __attribute__((aligned(16))) unsigned char sm_raw[];
   uint16_t* xs = reinterpret_cast<uint16_t*>(sm_raw);               // [s][R]
   float* red = reinterpret_cast<float*>(sm_raw + size_t(a.s) * R * 2 + 16);  // [4][R][64]
@@ -91,7 +97,7 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
   }
   __syncthreads();
 
-  const int l8 = tid & 7, kr = tid >> 3;
+  const int l8 = tid % kSmColLanes, kr = tid / kSmColLanes;
   const bool col_on = l8 * 8 < ncol;
   float acc[R][8];
 #pragma unroll
@@ -102,26 +108,39 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
   const int nblk = s_nblk;
   for (int bi = 0; bi < nblk; ++bi) {
     const int b = s_blocks[bi];
-    // stage x[m, g_b] transposed (xs[k][m]); zero for rows that do not use block (b, j)
-    for (int x = tid; x < s * R; x += kSmThreads) {
-      const int k = x / R, m = x - (x / R) * R;
+    // stage x[m, g_b] transposed (xs[k][m]), 8 contraction values (16 bytes)
+    // per load; zero for rows that do not use block (b, j)
+    const int s8 = s >> 3;
+    for (int x = tid; x < s8 * R; x += kSmThreads) {
+      const int m = x / s8, k8 = x - m * s8;
       const int t = s_type[m];
       const bool need = t >= 0 && (b == j || t == b);
-      xs[x] = need ? X[int64_t(m) * K + int64_t(b) * s + k] : uint16_t(0);
+      const u32x4 v = need ? *reinterpret_cast<const u32x4*>(X + int64_t(m) * K + int64_t(b) * s + k8 * 8)
+                           : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        xs[(k8 * 8 + 2 * d) * R + m] = uint16_t(v[d] & 0xffffu);
+        xs[(k8 * 8 + 2 * d + 1) * R + m] = uint16_t(v[d] >> 16);
+      }
     }
     __syncthreads();
+    // weight rows of the block: batches of kSmUnroll rows per thread, the next
+    // batch's loads issued before the current batch is applied, so that two
+    // batches (2 x 8 x 16 bytes per thread) are in flight
     const uint16_t* wp = W + int64_t(b) * s * N + col0 + l8 * 8;
-    for (int k = kr; k < s; k += kSmKLanes * kSmUnroll) {
-      u32x4 wv[kSmUnroll];
+    constexpr int kStep = kSmKLanes * kSmUnroll;
+    auto load_batch = [&](int k0, u32x4 (&wv)[kSmUnroll]) {
 #pragma unroll
       for (int u = 0; u < kSmUnroll; ++u) {
-        const int kk = k + u * kSmKLanes;
+        const int kk = k0 + u * kSmKLanes;
         wv[u] = (kk < s && col_on) ? *reinterpret_cast<const u32x4*>(wp + int64_t(kk) * N)
                                    : (u32x4){0u, 0u, 0u, 0u};
       }
+    };
+    auto apply_batch = [&](int k0, const u32x4 (&wv)[kSmUnroll]) {
 #pragma unroll
       for (int u = 0; u < kSmUnroll; ++u) {
-        const int kk = k + u * kSmKLanes;
+        const int kk = k0 + u * kSmKLanes;
         if (kk >= s) break;
         float w8[8];
 #pragma unroll
@@ -137,23 +156,31 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
           for (int c = 0; c < 8; ++c) acc[m][c] = fmaf(xv, w8[c], acc[m][c]);
         }
       }
+    };
+    u32x4 wa[kSmUnroll], wb[kSmUnroll];
+    load_batch(kr, wa);
+    for (int k = kr; k < s; k += 2 * kStep) {
+      load_batch(k + kStep, wb);
+      apply_batch(k, wa);
+      load_batch(k + 2 * kStep, wa);
+      apply_batch(k + kStep, wb);
     }
     __syncthreads();  // xs is restaged for the next block
   }
 
-  // reduce the 32 weight-row lanes: 8 per wave by a fixed shuffle tree, then 4 waves
+  // reduce the weight-row lanes: those of a wave by a fixed shuffle tree, then
+  // the 4 waves in a fixed order
   const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
   for (int m = 0; m < R; ++m)
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float v = acc[m][c];
-      v += __shfl_xor(v, 8, 64);
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
+#pragma unroll
+      for (int o = kSmColLanes; o < 64; o *= 2) v += __shfl_xor(v, o, 64);
       acc[m][c] = v;
     }
-  if (lane < 8) {
+  if (lane < kSmColLanes) {
 #pragma unroll
     for (int m = 0; m < R; ++m)
 #pragma unroll
@@ -170,12 +197,34 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
   }
 }
 
+template <int R, int COLS>
+hipError_t launch_rc(SmallArgs a, int E, hipStream_t st) {
+  a.chunks_per_group = (a.r + COLS - 1) / COLS;
+  const dim3 grid(unsigned(a.q * a.chunks_per_group), unsigned(E));
+  const size_t shm = size_t(a.s) * R * 2 + 16 + sizeof(float) * 4 * R * COLS;
+  static bool attr_set = false;  // allow more than the default 64 KB of dynamic LDS
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&small_m_kernel<R, COLS>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             int(kSmMaxXs * 2 + 16 + sizeof(float) * 4 * R * COLS));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((small_m_kernel<R, COLS>), grid, dim3(kSmThreads), shm, st, a);
+  return hipGetLastError();
+}
+
+// the widest chunk that the group width fills and that still gives about two
+// workgroups per CU (measured on 64 experts, 7168 -> 2048, q = 4: 64 columns
+// 4.8 TB/s, 256 columns 6.0 TB/s)
 template <int R>
 hipError_t launch_r(const SmallArgs& a, int E, hipStream_t st) {
-  const dim3 grid(unsigned(a.q * a.chunks_per_group), unsigned(E));
-  const size_t shm = size_t(a.s) * R * 2 + 16 + sizeof(float) * 4 * R * kSmCols;
-  hipLaunchKernelGGL((small_m_kernel<R>), grid, dim3(kSmThreads), shm, st, a);
-  return hipGetLastError();
+  const int64_t want = 512;
+  auto fits = [&](int cols) { return a.r >= cols && int64_t(E) * a.q * ((a.r + cols - 1) / cols) >= want; };
+  if (fits(512)) return launch_rc<R, 512>(a, E, st);
+  if (fits(256)) return launch_rc<R, 256>(a, E, st);
+  if (fits(128)) return launch_rc<R, 128>(a, E, st);
+  return launch_rc<R, 64>(a, E, st);
 }
 
 }  // namespace
@@ -199,7 +248,6 @@ hipError_t launch_small_m_bf16(const ProblemDesc& p, hipStream_t st) {
   a.N = int(p.N);
   a.s = int(p.K / p.q);
   a.r = int(p.N / p.q);
-  a.chunks_per_group = (a.r + kSmCols - 1) / kSmCols;
   if (p.M <= 1) return launch_r<1>(a, p.E, st);
   if (p.M <= 2) return launch_r<2>(a, p.E, st);
   if (p.M <= 4) return launch_r<4>(a, p.E, st);
