@@ -488,8 +488,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
           const u32x4 val = *reinterpret_cast<const u32x4*>(ebuf + row * C::E_PITCH + ((pc ^ (row & C::E_MASK)) << 4));
           const int ml = wm * C::WTM + fm * 32 + row;
           const int orow = OP == Op::Dx ? ostart + (ct.out_row0 + ml) * q : ct.out_row0 + ml;
+          // non-temporal whole-line stores keep the output out of L2 (as in the forward)
           if (ml < ct.m_cnt)
-            *reinterpret_cast<u32x4*>(g.C + (uint32_t(orow) * c_ld + col0 + uint32_t(pc) * 16u)) = val;
+            __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(g.C + (uint32_t(orow) * c_ld + col0 + uint32_t(pc) * 16u)));
         }
       }
     }
