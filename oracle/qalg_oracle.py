@@ -29,6 +29,12 @@ What is computed, plainly:
   the cyclic tau; appendix D.5, the interval schedule of the pilot).
 * `mac_count` counts the multiply-accumulates the row-typed evaluator executes
   (eq 18-19; eq 24 for equal groups).
+* `gated_forward` is the gate/up half of a gated (SwiGLU) FFN: both D x F
+  projections follow the same row law (section 2: "the same row law applies
+  to each shape"; gates and pointwise activations keep their usual
+  definitions), combined as silu(X *_{Q_q} W_gate) * (X *_{Q_q} W_up), silu
+  being x * sigmoid(x) (the pilot's bias-free SwiGLU, appendix D; SwiGLU
+  x * sigma(beta x) with beta = 1).
 
 All arithmetic is float64; block products are numpy.matmul (a library
 primitive standing for one block GEMM).  The oracle itself rounds nothing.
@@ -68,6 +74,8 @@ __all__ = [
     "type_schedule",
     "mac_count",
     "dense_equivalent_macs",
+    "silu",
+    "gated_forward",
 ]
 
 
@@ -340,3 +348,26 @@ def mac_count(tau: np.ndarray, q: int, K: int, N: int,
 def dense_equivalent_macs(M: int, K: int, N: int) -> int:
     """MACs of the ordinary product X W (the dense control)."""
     return M * K * N
+
+
+# ----------------------------------------------------------------------------
+# Gated FFN: section 2 (gated FFN shapes, the same row law for each
+# projection), the pilot's bias-free SwiGLU (appendix D), table 9
+# ----------------------------------------------------------------------------
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """x * sigmoid(x) (SwiGLU's swish with beta = 1), evaluated in float64."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def gated_forward(X: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, tau: np.ndarray, q: int) -> np.ndarray:
+    """H = silu(X *_{Q_q} W_gate) * (X *_{Q_q} W_up), both products row-typed with the same tau.
+
+    The activation applies to the gate product, elementwise, after both
+    endpoint sums of each product are complete (the same Algorithm 1 for
+    both D x F weights).
+    """
+    G = row_typed_forward(X, Wg, tau, q)
+    U = row_typed_forward(X, Wu, tau, q)
+    return silu(G) * U

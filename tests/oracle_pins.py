@@ -11,6 +11,8 @@ import itertools
 import pathlib
 from fractions import Fraction
 
+import math
+
 import numpy as np
 
 GOLDEN = pathlib.Path(__file__).resolve().parent / "golden"
@@ -512,11 +514,44 @@ def pin_type_schedule(O):
     np.testing.assert_array_equal(O.type_schedule(p, 4, "interval", 768), [0, 0, 1, 1, 2, 2, 3, 3, 0, 0, 3, 0])
 
 
+# --------------------------------------------------------------------------
+# gated FFN (section 2; appendix D's SwiGLU)
+# --------------------------------------------------------------------------
+
+def pin_silu_values(O):
+    """silu(0) = 0, silu(x) - silu(-x) = x (sigmoid(x) + sigmoid(-x) = 1), silu(x) -> x and -> 0 at the tails,
+    and silu(1) = 1 / (1 + 1/e) written out."""
+    x = np.linspace(-30.0, 30.0, 121)
+    np.testing.assert_allclose(O.silu(x) - O.silu(-x), x, rtol=1e-14, atol=1e-14)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(O.silu(np.array([40.0])), [40.0], rtol=1e-15)
+    assert abs(O.silu(np.array([-40.0]))[0]) < 1e-15
+    np.testing.assert_allclose(O.silu(np.array([1.0])), [1.0 / (1.0 + np.exp(-1.0))], rtol=1e-15)
+
+
+def pin_gated_masked_dense(O, seed=31):
+    """Each gated row is silu(x T_i(W_gate)) * (x T_i(W_up)) with the masked banks, scalar silu per element."""
+    g = _rng(seed)
+    for q, M, s, r in ((2, 7, 3, 2), (3, 9, 2, 3), (1, 5, 4, 3)):
+        X = g.standard_normal((M, q * s))
+        Wg = g.standard_normal((q * s, q * r))
+        Wu = g.standard_normal((q * s, q * r))
+        tau = g.integers(0, q, size=M)
+        H = O.gated_forward(X, Wg, Wu, tau, q)
+        for m in range(M):
+            i = int(tau[m])
+            gv = X[m] @ masked_bank(Wg, i, q)
+            uv = X[m] @ masked_bank(Wu, i, q)
+            for n in range(q * r):
+                want = gv[n] / (1.0 + math.exp(-gv[n])) * uv[n]
+                assert abs(H[m, n] - want) <= 1e-12 * (1.0 + abs(want)), (q, m, n)
+
+
 ALL_PINS = [
     pin_q2_table, pin_q2_scalar_example, pin_eq3_rectangular_blocks, pin_eq13_14,
     pin_product_counts, pin_graph_counts, pin_appendix_a, pin_associativity,
     pin_row_typed_composition, pin_unit_laws, pin_brute_force, pin_teaching_matrix,
     pin_masked_dense, pin_row_typed_is_square_rows, pin_q1_is_matmul, pin_block_diagonal,
     pin_coverage, pin_vjp_scalar_eq31_35, pin_vjp_autograd, pin_vjp_adjoint,
-    pin_mac_count, pin_type_index, pin_type_schedule,
+    pin_mac_count, pin_type_index, pin_type_schedule, pin_silu_values, pin_gated_masked_dense,
 ]

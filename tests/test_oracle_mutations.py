@@ -15,6 +15,8 @@ _real_table = O.structure_table
 _real_fwd = O.row_typed_forward
 _real_bwd = O.row_typed_backward
 _real_index = O.type_index
+_real_silu = O.silu
+_real_gated = O.gated_forward
 
 
 def table_with_edge_edge(q, edges=None):
@@ -131,6 +133,22 @@ def schedule_one_based(positions, q, kind="cyclic", period=0):
     return ((p % period) // (period // q)).astype(np.int32)
 
 
+def silu_wrong_sign(z):
+    """Mistake: x * sigmoid(-x)."""
+    z = np.asarray(z, float)
+    return z / (1.0 + np.exp(z))
+
+
+def gated_swapped(X, Wg, Wu, tau, q):
+    """Mistake: the activation applied to the up product instead of the gate."""
+    return O.row_typed_forward(X, Wg, tau, q) * _real_silu(O.row_typed_forward(X, Wu, tau, q))
+
+
+def gated_dense_gate(X, Wg, Wu, tau, q):
+    """Mistake: the gate product ignores the row types (plain X W_gate)."""
+    return _real_silu(np.asarray(X, float) @ np.asarray(Wg, float)) * O.row_typed_forward(X, Wu, tau, q)
+
+
 MUTANTS = [
     ("structure_table", table_with_edge_edge),
     ("structure_table", table_without_right_vertex),
@@ -143,6 +161,9 @@ MUTANTS = [
     ("type_index", index_unstable),
     ("type_index", index_drops_bad_count),
     ("type_schedule", schedule_one_based),
+    ("silu", silu_wrong_sign),
+    ("gated_forward", gated_swapped),
+    ("gated_forward", gated_dense_gate),
 ]
 
 
