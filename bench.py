@@ -170,6 +170,7 @@ def main() -> int:
     if not args.no_extra:
         extra["training"] = training_leg(Q, torch, np, synth, dev, stream)
         extra["decode"] = decode_leg(Q, torch, np, synth, dev, stream)
+        extra["gated_ffn"] = gated_leg(Q, torch, np, synth, dev, stream)
 
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib << 20
@@ -278,6 +279,48 @@ def training_leg(Q, torch, np, synth, dev, stream):
     res["step_ms"] = round(tot, 4)
     res["step_tflops"] = round(3 * flop / (tot * 1e-3) / 1e12, 1)
     log(f"[bench] training leg: {res}")
+    return res
+
+
+def gated_leg(Q, torch, np, synth, dev, stream):
+    """Gated (SwiGLU) FFN at (4096, 12288), q = 8, M = 16384: fused gate/up (silu(x W_g) * x W_u) + down."""
+    c = 6
+    X = synth.normal_operand(1000 * c + 1, (M, D), 1.0, "bf16")
+    Wg = synth.normal_operand(1000 * c + 2, (D, F), D ** -0.5, "bf16")
+    Wu = synth.normal_operand(1000 * c + 3, (D, F), D ** -0.5, "bf16")
+    Wd = synth.normal_operand(1000 * c + 4, (F, D), F ** -0.5, "bf16")
+    to = lambda op: torch.from_numpy(op.bits.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    Xd, Wdd = to(X), to(Wd)
+    Wgu = Q.qalg_merge_gate_up(to(Wg), to(Wu), QQ, stream=stream)  # weight layout, once
+    tau = torch.from_numpy((np.arange(M) % QQ).astype(np.int32)).to(dev)
+    ws = Q.workspace(QQ, M, device=dev)
+    H = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+    Y = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    Q.qalg_build_index(tau, QQ, ws=ws, stream=stream)
+    r = Q.QALG_FLAG_INDEX_READY
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    for _ in range(3):
+        Q.qalg_gated_forward(Xd, Wgu, tau, QQ, H=H, ws=ws, flags=r, stream=stream)
+        Q.qalg_forward(H, Wdd, tau, QQ, Y=Y, ws=ws, flags=r, stream=stream)
+    torch.cuda.synchronize()
+    n = 10
+    a, b, cc = ev(), ev(), ev()
+    tg = td = 0.0
+    for _ in range(n):
+        a.record(stream)
+        Q.qalg_gated_forward(Xd, Wgu, tau, QQ, H=H, ws=ws, flags=r, stream=stream)
+        b.record(stream)
+        Q.qalg_forward(H, Wdd, tau, QQ, Y=Y, ws=ws, flags=r, stream=stream)
+        cc.record(stream)
+        torch.cuda.synchronize()
+        tg += a.elapsed_time(b)
+        td += b.elapsed_time(cc)
+    tg, td = tg / n, td / n
+    flop = 2.0 * rho(QQ) * M * D * F  # per projection (gate, up and down each)
+    res = {"workload": "gated_ffn_D4096_F12288_q8_M16384_bf16", "gate_up_ms": round(tg, 4),
+           "gate_up_tflops": round(2 * flop / (tg * 1e-3) / 1e12, 1), "down_ms": round(td, 4),
+           "step_ms": round(tg + td, 4), "step_tflops": round(3 * flop / ((tg + td) * 1e-3) / 1e12, 1)}
+    log(f"[bench] gated FFN leg: {res}")
     return res
 
 

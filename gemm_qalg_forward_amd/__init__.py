@@ -7,7 +7,7 @@ tensor is not on the GPU, the call raises.
 
 Functions carry the C names:
     qalg_forward, qalg_backward_dx, qalg_backward_dw, qalg_forward_batched,
-    qalg_type_schedule, qalg_build_index, qalg_build_index_batched,
+    qalg_gated_forward, qalg_merge_gate_up, qalg_type_schedule, qalg_build_index, qalg_build_index_batched,
     qalg_read_status, qalg_workspace_bytes, qalg_index_layout,
     qalg_status_string, qalg_version.
 """
@@ -23,6 +23,7 @@ __all__ = [
     "qalg_version", "qalg_status_string", "qalg_workspace_bytes", "qalg_index_layout",
     "qalg_type_schedule", "qalg_build_index", "qalg_build_index_batched",
     "qalg_forward", "qalg_backward_dx", "qalg_backward_dw", "qalg_forward_batched",
+    "qalg_gated_forward", "qalg_merge_gate_up",
     "qalg_read_status", "workspace",
 ]
 
@@ -57,6 +58,8 @@ _SIGS = {
     "qalg_backward_dx": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
     "qalg_backward_dw": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
     "qalg_forward_batched": (ctypes.c_int, [_c_i32, _vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
+    "qalg_gated_forward": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
+    "qalg_merge_gate_up": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i64, _vp, _c_i32, _vp]),
     "qalg_read_status": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i64, _vp, ctypes.POINTER(_c_i64)]),
 }
 
@@ -227,6 +230,28 @@ def qalg_backward_dw(X, dY, tau, q: int, dW=None, ws=None, flags: int = 0, strea
     if M2 != M:
         raise ValueError("X and dY row counts differ")
     return _proj("qalg_backward_dw", X, dY, tau, q, dW, (K, N), ws, flags, stream, M, K, N)
+
+
+def qalg_merge_gate_up(Wg, Wu, q: int, Wgu=None, stream=None):
+    """Merged gate/up bank (layout in include/qalg.h): Wg, Wu [K, F] -> Wgu [K, 2F]."""
+    torch = _torch()
+    K, F = Wg.shape
+    if tuple(Wu.shape) != (K, F) or Wu.dtype != Wg.dtype:
+        raise ValueError("gate and up weights must have the same shape and dtype")
+    if Wgu is None:
+        Wgu = torch.empty((K, 2 * F), dtype=Wg.dtype, device=Wg.device)
+    _check("qalg_merge_gate_up", lib().qalg_merge_gate_up(
+        _dev_ptr(Wg, "Wg"), _dev_ptr(Wu, "Wu"), q, K, F, _dev_ptr(Wgu, "Wgu"), _dtype_code(Wg), _stream(stream)))
+    return Wgu
+
+
+def qalg_gated_forward(X, Wgu, tau, q: int, H=None, ws=None, flags: int = 0, stream=None):
+    """H = silu(X *_{Q_q} W_gate) * (X *_{Q_q} W_up): X [M, K], merged Wgu [K, 2F] -> H [M, F]."""
+    M, K = X.shape
+    K2, F2 = Wgu.shape
+    if K2 != K or F2 % 2:
+        raise ValueError("X and Wgu shapes differ (Wgu is K x 2F)")
+    return _proj("qalg_gated_forward", X, Wgu, tau, q, H, (M, F2 // 2), ws, flags, stream, M, K, F2 // 2)
 
 
 def qalg_forward_batched(X, W, tau, q: int, Y=None, ws=None, flags: int = 0, stream=None):

@@ -227,6 +227,55 @@ qalg_status qalg_forward_batched(int32_t E, const void* X, const void* W, const 
   return run_projection(Op::Fwd, E, X, W, tau, q, M, K, N, Y, dtype, ws, ws_bytes, flags, stream);
 }
 
+qalg_status qalg_gated_forward(const void* X, const void* Wgu, const int32_t* tau, int32_t q, int64_t M,
+                               int64_t K, int64_t F, void* H, int32_t dtype, void* ws, size_t ws_bytes,
+                               uint32_t flags, void* stream) {
+  if (dtype != QALG_BF16) return QALG_ERR_DTYPE;
+  if (flags & ~uint32_t(QALG_FLAG_INDEX_READY)) return QALG_ERR_ARG;
+  if (M < 0 || K <= 0 || F <= 0 || M > INT32_MAX / 2 || K > INT32_MAX / 2 || F > INT32_MAX / 4)
+    return QALG_ERR_DIM;
+  if (q < 1 || q > QALG_MAX_Q || K % q || F % q) return QALG_ERR_Q;
+  if ((F / q) % 128 || (K / q) % 64) return QALG_ERR_ALIGN;
+  if (M == 0) return QALG_OK;
+  if (X == nullptr || Wgu == nullptr || tau == nullptr || H == nullptr) return QALG_ERR_NULL;
+  if (!aligned16(X) || !aligned16(Wgu) || !aligned16(H) || (reinterpret_cast<uintptr_t>(tau) & 3u))
+    return QALG_ERR_ALIGN;
+  qalg_status st = check_ws(1, q, M, ws, ws_bytes);
+  if (st != QALG_OK) return st;
+  ProblemDesc p{};
+  p.op = Op::Fwd;
+  p.A = X;
+  p.B = Wgu;
+  p.C = H;
+  p.tau = tau;
+  p.q = q;
+  p.M = M;
+  p.K = K;
+  p.N = 2 * F;  // the merged bank's width
+  p.E = 1;
+  if (!qalg::fwd_gated_supported(p)) return QALG_ERR_DIM;
+  int32_t* wsi = static_cast<int32_t*>(ws);
+  p.ws = wsi;
+  p.ws_stride = ws_stride_ints(q, M);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!(flags & QALG_FLAG_INDEX_READY)) {
+    const hipError_t e = qalg::launch_build_index(tau, q, M, 1, wsi, p.ws_stride, s);
+    if (e != hipSuccess) return QALG_ERR_HIP;
+  }
+  return hip_status(qalg::launch_fwd_gated_bf16(p, s));
+}
+
+qalg_status qalg_merge_gate_up(const void* Wg, const void* Wu, int32_t q, int64_t K, int64_t F, void* Wgu,
+                               int32_t dtype, void* stream) {
+  if (dtype != QALG_BF16) return QALG_ERR_DTYPE;
+  if (K <= 0 || F <= 0 || K > INT32_MAX / 2 || F > INT32_MAX / 4) return QALG_ERR_DIM;
+  if (q < 1 || q > QALG_MAX_Q || F % q) return QALG_ERR_Q;
+  if ((F / q) % 128) return QALG_ERR_ALIGN;
+  if (Wg == nullptr || Wu == nullptr || Wgu == nullptr) return QALG_ERR_NULL;
+  if (!aligned16(Wg) || !aligned16(Wu) || !aligned16(Wgu)) return QALG_ERR_ALIGN;
+  return hip_status(qalg::launch_merge_gate_up_bf16(Wg, Wu, Wgu, K, F, q, static_cast<hipStream_t>(stream)));
+}
+
 qalg_status qalg_read_status(const void* ws, int32_t E, int32_t q, int64_t M, void* stream,
                              int64_t* bad_tau_rows) {
   if (ws == nullptr || bad_tau_rows == nullptr) return QALG_ERR_NULL;

@@ -81,9 +81,13 @@ constexpr int kBK = 64;       // contraction per k-step (128-byte X row segments
 constexpr int kStages = 2;    // LDS stages: the next k-step's operands arrive while one is computed
 constexpr int kQ = kBK / 16;  // MFMA quarter steps per k-step
 
-template <int BM_, int BN_>
+// GATED: the gate/up half of a gated FFN over a merged weight bank (see the
+// gated entry point below): each wave's 128 accumulator columns are 64 gate
+// and the matching 64 up columns, and the epilogue writes silu(gate) * up.
+template <int BM_, int BN_, bool GATED_ = false>
 struct FwdCfg {
   static constexpr int BM = BM_, BN = BN_, WGM = 2, WGN = 2;
+  static constexpr bool GATED = GATED_;
   static constexpr int THREADS = 256;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -103,8 +107,10 @@ struct FwdCfg {
   static_assert(kStages * DMA < 64, "vmcnt range");
   // epilogue: each wave restages 32 rows x WTN columns of bf16 at a time in
   // its own share of a buffer behind the stages
-  static constexpr int E_PITCH = WTN * 2;          // bytes per restaged row
-  static constexpr int E_NP = WTN / 8;             // 16-byte pieces per row
+  static constexpr int OUT_WTN = GATED ? WTN / 2 : WTN;  // output columns per wave tile
+  static_assert(!GATED || FN % 2 == 0, "gate and up halves of a wave tile");
+  static constexpr int E_PITCH = OUT_WTN * 2;      // bytes per restaged row
+  static constexpr int E_NP = OUT_WTN / 8;         // 16-byte pieces per row
   static constexpr int E_BYTES = 32 * E_PITCH;
   static constexpr int E_MASK = E_NP == 12 ? 3 : E_NP - 1;  // piece swizzle: p ^ (row & E_MASK)
   static_assert(E_NP % 2 == 0 && (E_NP == 12 || (E_NP & E_MASK) == 0), "epilogue buffer");
@@ -123,7 +129,8 @@ struct FwdArgs {
   int q, M, K, N, s, r;
   int cpg;     // column tiles per output group
   int n_ct;    // column tiles in all (q * cpg)
-  int kts;     // k-steps per contraction segment (s / 32)
+  int kts;     // k-steps per contraction segment (s / kBK)
+  int out_n;   // columns of an output row (N; N / 2 for the gated epilogue)
 };
 
 // One output tile, decoded from its position in the tile order.
@@ -200,9 +207,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   {
     const int typed = uni(s_off[a.q]);
     const int nbad = a.M - typed;
-    const int row_u4 = a.N / 8;  // 16-byte pieces per output row
+    const int row_u4 = a.out_n / 8;  // 16-byte pieces per output row
     for (int b = blockIdx.x; b < nbad; b += gridDim.x) {
-      u32x4* yr = reinterpret_cast<u32x4*>(a.Y + int64_t(rows[typed + b]) * a.N * 2);
+      u32x4* yr = reinterpret_cast<u32x4*>(a.Y + int64_t(rows[typed + b]) * a.out_n * 2);
       for (int x = tid; x < row_u4; x += T) yr[x] = (u32x4){0u, 0u, 0u, 0u};
     }
   }
@@ -223,7 +230,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   int l_idx;
   if (!dcopy.next(&l_long, &l_idx)) return;
 
-  const uint32_t n_bytes = uint32_t(a.N) * 2u;
+  const uint32_t n_bytes = uint32_t(a.N) * 2u;      // bytes per weight row
+  const uint32_t y_bytes = uint32_t(a.out_n) * 2u;  // bytes per output row
   const uint32_t k_bytes = uint32_t(a.K) * 2u;
   // cyclic schedule: the k-th row of type i is (i - cyc) mod q + k q, no row list needed
   const int cyc = ws[4];
@@ -469,18 +477,40 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
     // 16-byte pieces.
     {
       char* ebuf = smem + C::E_OFF + wid * C::E_BYTES;
-      const uint32_t col0 = uint32_t(ct.n0 + wn * C::WTN) * 2u;
+      // first output column of the wave (gated: the tile's 256 merged columns
+      // hold 128 output columns, 64 per wave)
+      const uint32_t col0 = uint32_t((C::GATED ? ct.n0 / 2 : ct.n0) + wn * C::OUT_WTN) * 2u;
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm) {
         // lane (l32, lhi) holds row l32, columns fn*32 + g*8 + lhi*4 .. +3
+        constexpr int FO = C::GATED ? C::FN / 2 : C::FN;  // 32-column output blocks per wave
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) {
+        for (int fn = 0; fn < FO; ++fn) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const f32x16& v = acc[fm][fn];
             const int pc = (fn * 4 + g) ^ (l32 & C::E_MASK);
-            *reinterpret_cast<u32x2*>(ebuf + l32 * C::E_PITCH + pc * 16 + lhi * 8) =
-                pack4_bf16(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+            u32x2 packed;
+            if constexpr (C::GATED) {
+              // gate column c sits in block fn, its up column in block fn + FN/2,
+              // same lane and register: h = silu(gate) * up in fp32, one rounding
+              const f32x16& u = acc[fm][fn + C::FN / 2];
+              float h[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float gv = v[4 * g + e];
+                // sigmoid through the hardware reciprocal (about 1 ulp; the
+                // result is rounded to bf16 next)
+                h[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * u[4 * g + e];
+              }
+              packed = pack4_bf16(h[0], h[1], h[2], h[3]);
+            } else {
+              packed = pack4_bf16(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+            }
+            *reinterpret_cast<u32x2*>(ebuf + l32 * C::E_PITCH + pc * 16 + lhi * 8) = packed;
+            // gated: keep one group's values live at a time (else the
+            // activation work of a whole block is interleaved and spills)
+            if constexpr (C::GATED) __builtin_amdgcn_sched_barrier(0);
           }
         }
         // read back: 64 lanes take 64 consecutive (row, piece) slots per instruction
@@ -499,7 +529,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
           // of L2 leaves the cache to the operand tiles (measured 11 % on the
           // 4096 -> 12288 projection against plain stores)
           if (ml < ct.m_cnt)
-            __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(a.Y + (uint32_t(orow) * n_bytes + col0 + uint32_t(pc) * 16u)));
+            __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(a.Y + (uint32_t(orow) * y_bytes + col0 + uint32_t(pc) * 16u)));
         }
       }
     }
@@ -525,6 +555,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void fwd_persistent_kernel(FwdArgs a
 }
 
 using Fwd256x256 = FwdCfg<256, 256>;
+using Fwd256x256Gated = FwdCfg<256, 256, true>;
 using Fwd256x192 = FwdCfg<256, 192>;
 using Fwd256x128 = FwdCfg<256, 128>;
 
@@ -565,6 +596,7 @@ hipError_t launch_fwd(const ProblemDesc& p, hipStream_t s) {
   a.s = int(p.K / p.q);
   a.r = int(p.N / p.q);
   a.kts = a.s / kBK;
+  a.out_n = C::GATED ? a.N / 2 : a.N;
   a.cpg = a.r / C::BN;
   a.n_ct = p.q * a.cpg;
   const int64_t max_tiles = ((p.M + C::BM - 1) / C::BM + p.q - 1) * int64_t(a.n_ct);
@@ -587,6 +619,54 @@ bool fwd_persistent_supported(const ProblemDesc& p) {
   if (s % kBK != 0) return false;
   if (r % 256 != 0 && r % 192 != 0 && r % 128 != 0) return false;
   return (p.M + p.q - 1) / p.q >= 128;  // rows per type (cyclic estimate)
+}
+
+// Gated: N is the merged bank's width 2F.  Output group j's 2r merged columns
+// come in 256-column pieces, each [gate 64 | up 64 | gate 64 | up 64] of 128
+// consecutive output columns, so r = F / q must be a multiple of 128.
+bool fwd_gated_supported(const ProblemDesc& p) {
+  if (p.op != Op::Fwd || p.E != 1) return false;
+  const int64_t s = p.K / p.q, r2 = p.N / p.q;
+  const int64_t lim = int64_t(1) << 31;
+  if (p.M * p.K >= lim || p.K * p.N >= lim || p.M * p.N >= lim) return false;
+  return s % kBK == 0 && r2 % 256 == 0;
+}
+
+hipError_t launch_fwd_gated_bf16(const ProblemDesc& p, hipStream_t s) { return launch_fwd<Fwd256x256Gated>(p, s); }
+
+namespace {
+
+// Merged gate/up bank: for output group j and its piece t (output columns
+// j r + 128 t .. +127), merged columns j 2r + 256 t + [0, 256) hold gate
+// columns +0..63, up +0..63, gate +64..127, up +64..127.  One thread per
+// 16-byte piece (8 columns) of the merged bank.
+__global__ void merge_gate_up_kernel(const uint16_t* Wg, const uint16_t* Wu, uint16_t* Wgu, int64_t K, int F,
+                                     int r) {
+  const int64_t pieces_per_row = int64_t(2) * F / 8;
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= K * pieces_per_row) return;
+  const int64_t k = i / pieces_per_row;
+  const int c = int(i - k * pieces_per_row) * 8;  // merged column of the piece
+  const int j = c / (2 * r), w = c - j * 2 * r;
+  const int t = w / 256, x = w - t * 256;
+  const int blk = x / 64;
+  const int h = j * r + t * 128 + (blk >> 1) * 64 + (x & 63);
+  const uint16_t* src = (blk & 1) ? Wu : Wg;
+  *reinterpret_cast<uint4*>(Wgu + k * 2 * F + c) = *reinterpret_cast<const uint4*>(src + k * F + h);
+}
+
+}  // namespace
+
+hipError_t launch_merge_gate_up_bf16(const void* Wg, const void* Wu, void* Wgu, int64_t K, int64_t F, int q,
+                                     hipStream_t s) {
+  const int64_t n = K * (2 * F / 8);
+  if (n == 0) return hipSuccess;
+  const int threads = 256;
+  const int64_t blocks = (n + threads - 1) / threads;
+  hipLaunchKernelGGL(merge_gate_up_kernel, dim3(unsigned(blocks)), dim3(threads), 0, s,
+                     static_cast<const uint16_t*>(Wg), static_cast<const uint16_t*>(Wu), static_cast<uint16_t*>(Wgu),
+                     K, int(F), int(F / q));
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd_persistent_bf16(const ProblemDesc& p, hipStream_t s) {

@@ -86,6 +86,11 @@ bool small_m_supported(const ProblemDesc& p);
 // Persistent 256x256-tile forward (bf16, one problem); zeroes rows of out-of-range type itself.
 bool fwd_persistent_supported(const ProblemDesc& p);
 hipError_t launch_fwd_persistent_bf16(const ProblemDesc& p, hipStream_t s);
+// Gated (SwiGLU gate/up) forward over a merged bank; p.N is the merged width 2F.
+bool fwd_gated_supported(const ProblemDesc& p);
+hipError_t launch_fwd_gated_bf16(const ProblemDesc& p, hipStream_t s);
+hipError_t launch_merge_gate_up_bf16(const void* Wg, const void* Wu, void* Wgu, int64_t K, int64_t F, int q,
+                                     hipStream_t s);
 // Persistent 256-row-tile dX / dW (bf16, one problem) for cyclic schedules; a
 // launch on any other schedule returns at once.
 bool grad_persistent_supported(const ProblemDesc& p);

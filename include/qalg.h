@@ -192,6 +192,36 @@ qalg_status qalg_forward_batched(int32_t E, const void* X, const void* W, const 
                                  uint32_t flags, void* stream);
 
 /*
+ * Gate/up half of a gated (SwiGLU) FFN, fused: H = silu(X *_{Q_q} W_gate) *
+ * (X *_{Q_q} W_up) elementwise, silu(z) = z * sigmoid(z).  Section 2: a gated
+ * FFN has two D x F weights that follow the same row law as any projection
+ * (gates and pointwise activations keep their usual definitions); the pilot's
+ * FFN is a bias-free SwiGLU (appendix D); table 9 merges gate and up.
+ * Both products accumulate in fp32; the activation is applied in fp32 and H is
+ * rounded once (RNE).  bf16 only.
+ * X: M x K.  Wgu: K x 2F, the merged bank built by qalg_merge_gate_up.  H: M x F
+ * (overwritten; rows of an out-of-range type are written as zero).
+ * Requires F / q to be a multiple of 128 and K / q a multiple of 64
+ * (QALG_ERR_ALIGN otherwise), and M*K, K*2F, M*2F below 2^31 (QALG_ERR_DIM).
+ * Flags: QALG_FLAG_INDEX_READY only.
+ */
+qalg_status qalg_gated_forward(const void* X, const void* Wgu, const int32_t* tau, int32_t q,
+                               int64_t M, int64_t K, int64_t F, void* H,
+                               int32_t dtype, void* ws, size_t ws_bytes,
+                               uint32_t flags, void* stream);
+
+/*
+ * Merged gate/up bank for qalg_gated_forward (a layout copy, done once per
+ * weight update): Wg, Wu: K x F; Wgu: K x 2F.  Output group j's columns
+ * j*2r .. j*2r + 2r - 1 (r = F / q) come in pieces of 256: piece t holds, for
+ * output columns c0 = j*r + 128 t .. c0 + 127, the gate columns c0 .. c0+63,
+ * the up columns c0 .. c0+63, the gate columns c0+64 .. c0+127, then the up
+ * columns c0+64 .. c0+127.  bf16 only; F / q must be a multiple of 128.
+ */
+qalg_status qalg_merge_gate_up(const void* Wg, const void* Wu, int32_t q, int64_t K, int64_t F,
+                               void* Wgu, int32_t dtype, void* stream);
+
+/*
  * Number of rows with an out-of-range type seen by the last index build in
  * ws (summed over the E problems of a batched workspace; E = 1 otherwise).
  * Synchronises `stream`.

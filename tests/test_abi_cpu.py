@@ -119,3 +119,35 @@ def test_binding_refuses_cpu_tensors(lib):
     tau = torch.zeros(4, dtype=torch.int32)
     with pytest.raises(ValueError, match="GPU"):
         Q.qalg_forward(X, W, tau, 2, Y=torch.empty(4, 16, dtype=torch.bfloat16), ws=torch.empty(4096, dtype=torch.uint8))
+
+
+def call_gated(lib, X=FAKE, W=FAKE, tau=FAKE, q=2, M=64, K=256, F=512, H=FAKE, dt=1, ws=FAKE,
+               wsb=1 << 20, flags=0):
+    return lib.qalg_gated_forward(X, W, tau, q, M, K, F, H, dt, ws, wsb, flags, None)
+
+
+def test_gated_argument_errors_are_synchronous(lib):
+    assert call_gated(lib, dt=0) == 5                 # bf16 only
+    assert call_gated(lib, flags=2) == 8              # only QALG_FLAG_INDEX_READY
+    assert call_gated(lib, q=0) == 3
+    assert call_gated(lib, q=3) == 3                  # 3 does not divide 256
+    assert call_gated(lib, F=384) == 4                # F / q = 192: not a multiple of 128
+    assert call_gated(lib, K=128, q=4) == 4           # K / q = 32: not a multiple of 64
+    assert call_gated(lib, M=-1) == 2
+    assert call_gated(lib, X=None) == 1
+    assert call_gated(lib, H=None) == 1
+    assert call_gated(lib, ws=None) == 1
+    assert call_gated(lib, X=FAKE + 2) == 4
+    assert call_gated(lib, wsb=16) == 6               # workspace too small
+    assert call_gated(lib, M=0, X=None, H=None) == 0  # no rows: nothing to do, no launch
+
+
+def test_merge_argument_errors_are_synchronous(lib):
+    m = lambda **k: lib.qalg_merge_gate_up(k.get("Wg", FAKE), k.get("Wu", FAKE), k.get("q", 2), k.get("K", 64),  # noqa: E731
+                                           k.get("F", 512), k.get("Wgu", FAKE), k.get("dt", 1), None)
+    assert m(dt=0) == 5
+    assert m(F=384) == 4
+    assert m(q=3) == 3
+    assert m(K=0) == 2
+    assert m(Wu=None) == 1
+    assert m(Wgu=FAKE + 4) == 4

@@ -229,3 +229,68 @@ def test_zero_rows_and_absent_types():
             if b != j and b != 2:
                 assert not blk.any()
     assert_groups(rel_frob_blocks(dWh, dWr, q), BF16_TOL, "dW")
+
+
+# ---------------------------------------------------------------------------
+# gated (SwiGLU) gate/up forward over the merged bank
+# ---------------------------------------------------------------------------
+
+def _merged_reference(Wg_bits, Wu_bits, q):
+    """The merged gate/up layout as include/qalg.h states it, built column by column."""
+    K, F = Wg_bits.shape
+    r = F // q
+    out = np.empty((K, 2 * F), dtype=Wg_bits.dtype)
+    for j in range(q):
+        for t in range(r // 128):
+            c0 = j * r + 128 * t
+            base = j * 2 * r + 256 * t
+            out[:, base:base + 64] = Wg_bits[:, c0:c0 + 64]
+            out[:, base + 64:base + 128] = Wu_bits[:, c0:c0 + 64]
+            out[:, base + 128:base + 192] = Wg_bits[:, c0 + 64:c0 + 128]
+            out[:, base + 192:base + 256] = Wu_bits[:, c0 + 64:c0 + 128]
+    return out
+
+
+@pytest.mark.parametrize("q,K,F", [(4, 64, 1024), (1, 32, 384), (3, 16, 768)])
+def test_merge_gate_up_layout_bit_exact(q, K, F):
+    torch = torch_cuda()
+    Wg = synth.normal_operand(9700 + q, (K, F), 1.0, "bf16")
+    Wu = synth.normal_operand(9800 + q, (K, F), 1.0, "bf16")
+    Wgu = Q.qalg_merge_gate_up(to_dev(Wg), to_dev(Wu), q)
+    torch.cuda.synchronize()
+    got = Wgu.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, _merged_reference(Wg.bits.view(np.uint16), Wu.bits.view(np.uint16), q))
+
+
+GATED_SHAPES = [
+    # M, K, F, q, tau kind, offset, bad rows
+    (2048, 512, 1024, 4, "cyclic", 0, 0),     # r = 256: two 128-column pieces per group
+    (1000, 768, 3072, 4, "cyclic", 3, 0),     # the 110M-LM FFN widths, type offset, ragged rows
+    (700, 256, 256, 2, "random", 0, 9),       # listed schedule, out-of-range types
+    (777, 256, 512, 1, "zeros", 0, 0),        # q = 1: a dense SwiGLU gate/up
+    (4096, 1024, 2048, 8, "cyclic", 5, 0),    # q = 8, r = 256
+]
+
+
+@pytest.mark.parametrize("shape", GATED_SHAPES, ids=[f"M{s[0]}K{s[1]}F{s[2]}q{s[3]}{s[4]}" for s in GATED_SHAPES])
+def test_gated_forward_matches_oracle(shape):
+    torch = torch_cuda()
+    M, K, F, q, kind, off, bad = shape
+    say(f"[gated] M={M} K={K} F={F} q={q} tau={kind} offset={off} bad={bad}")
+    X = synth.normal_operand(9100 + M, (M, K), 1.0, "bf16")
+    Wg = synth.normal_operand(9200 + M, (K, F), K ** -0.5, "bf16")
+    Wu = synth.normal_operand(9300 + M, (K, F), K ** -0.5, "bf16")
+    tau = make_tau(kind, M, q, seed=M + 1, offset=off, bad=bad)
+    Xd, td = to_dev(X), tau_dev(tau)
+    Wgu = Q.qalg_merge_gate_up(to_dev(Wg), to_dev(Wu), q)
+    ws = Q.workspace(q, M)
+    H = Q.qalg_gated_forward(Xd, Wgu, td, q, ws=ws)
+    H2 = Q.qalg_gated_forward(Xd, Wgu, td, q, ws=ws, flags=Q.QALG_FLAG_INDEX_READY)
+    torch.cuda.synchronize()
+    assert Q.qalg_read_status(ws, q, M) == bad
+    assert torch.equal(H, H2), "gated forward is not bitwise reproducible"
+    Hr = O.gated_forward(X.f64, Wg.f64, Wu.f64, tau, q)
+    assert_groups(rel_frob_col_groups(to_f64(H), Hr, q), BF16_TOL, "H")
+    if bad:
+        rows = np.where((tau < 0) | (tau >= q))[0]
+        assert np.all(to_f64(H)[rows] == 0.0)

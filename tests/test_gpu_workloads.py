@@ -170,3 +170,31 @@ def test_training_grads_q8():
     _, dWr = O.row_typed_backward(X.f64, W.f64, dY.f64, tau, q)
     e = assert_groups(rel_frob_blocks(to_f64(dW), dWr, q), BF16_TOL, "dW")
     say(f"    dW max rel err {e:.2e}")
+
+
+def test_gated_ffn_q8_sampled():
+    """The benchmark's gated FFN leg: same seeds and calls (merge once, gated gate/up, down)."""
+    torch = torch_cuda()
+    c, M, D, F, q = 6, 16384, 4096, 12288, 8
+    say(f"[workload] gated FFN bf16 q=8 M={M} {D}->{F}->{D}")
+    X = synth.normal_operand(1000 * c + 1, (M, D), 1.0, "bf16")
+    Wg = synth.normal_operand(1000 * c + 2, (D, F), D ** -0.5, "bf16")
+    Wu = synth.normal_operand(1000 * c + 3, (D, F), D ** -0.5, "bf16")
+    Wd = synth.normal_operand(1000 * c + 4, (F, D), F ** -0.5, "bf16")
+    pos = torch.from_numpy(synth.cyclic_positions(M)).to("cuda")
+    td = Q.qalg_type_schedule(pos, q)
+    ws = Q.workspace(q, M)
+    Q.qalg_build_index(td, q, ws=ws)
+    Wgu = Q.qalg_merge_gate_up(to_dev(Wg), to_dev(Wu), q)
+    r = Q.QALG_FLAG_INDEX_READY
+    H = Q.qalg_gated_forward(to_dev(X), Wgu, td, q, ws=ws, flags=r)
+    Y = Q.qalg_forward(H, to_dev(Wd), td, q, ws=ws, flags=r)
+    torch.cuda.synchronize()
+    tau = td.cpu().numpy()
+    rows = _sample_rows(M, q, 512, 61)
+    Hr = O.gated_forward(X.f64[rows], Wg.f64, Wu.f64, tau[rows], q)
+    e1 = assert_groups(rel_frob_col_groups(to_f64(H[rows]), Hr, q), BF16_TOL, "H")
+    # the down projection consumes the GPU's bf16 H; the reference uses the exact H
+    Yr = O.row_typed_forward(Hr, Wd.f64, tau[rows], q)
+    e2 = assert_groups(rel_frob_col_groups(to_f64(Y[rows]), Yr, q), BF16_TOL, "Y")
+    say(f"    max rel err over {rows.size} sampled rows: H {e1:.2e}, Y {e2:.2e}")
