@@ -4,8 +4,8 @@
 // Paper: arXiv 2609.32814.  Section 4, eq 16-17: a token row of type i gets
 // y_i = x_i W_ii and y_j = x_i W_ij + x_j W_jj (j != i).  Section 6.1, eq 27
 // and Algorithm 1: the support of output group j for type i is B(i, j) =
-// {i, j}.  Section 5.3: the fused forward accumulates both endpoint products
-// before the output is written.
+// {i, j}.  Section 5.3: in the fused forward the two endpoint products of an
+// output are summed in registers and the output is stored once.
 //
 // Work decomposition.  The rows of each type (from the type index) are cut
 // into row tiles of BM rows that never straddle types; the N columns into

@@ -3,8 +3,8 @@
 //
 // Paper: arXiv 2609.32814.  Forward: section 4, eq 16-17, and Algorithm 1
 // (section 6.1): a row of type i gets y_i = x_i W_ii and y_j = x_i W_ij +
-// x_j W_jj.  Section 5.3 describes the fused schedule used here: one output
-// tile accumulates both endpoint products before it is written.  Gradients:
+// x_j W_jj.  Section 5.3 describes the fused schedule used here: an output
+// tile sums both endpoint products in registers and is stored once.  Gradients:
 // appendix B, eq 31-35, with one owner per output element (section 5.3).
 //
 // Every output tile is an ordinary GEMM tile whose contraction runs over at

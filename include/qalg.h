@@ -147,8 +147,8 @@ qalg_status qalg_index_layout(int32_t q, int64_t M, int64_t out_offsets[4]);
 /*
  * Forward projection Y = X *_{Q_q} W (eq 16-17, Algorithm 1).
  * X: M x K, W: K x N, Y: M x N (overwritten; Algorithm 1 starts from Y = 0).
- * Each output tile accumulates both endpoint products x_i W_ij and x_j W_jj
- * in fp32 before its single rounded store (section 5.3's fused schedule).
+ * Each output tile sums both endpoint products x_i W_ij and x_j W_jj in fp32
+ * registers and is rounded and stored once (section 5.3's fused schedule).
  * Small M (bf16) uses a weight-streaming kernel that reads each needed
  * weight block once (section 5.2: decode needs a matrix-vector kernel).
  */
@@ -193,7 +193,7 @@ qalg_status qalg_forward_batched(int32_t E, const void* X, const void* W, const 
 
 /*
  * Gate/up half of a gated (SwiGLU) FFN, fused: H = silu(X *_{Q_q} W_gate) *
- * (X *_{Q_q} W_up) elementwise, silu(z) = z * sigmoid(z).  Section 2: a gated
+ * (X *_{Q_q} W_up) elementwise, silu(z) = z * sigmoid(z).  Section 4: a gated
  * FFN has two D x F weights that follow the same row law as any projection
  * (gates and pointwise activations keep their usual definitions); the pilot's
  * FFN is a bias-free SwiGLU (appendix D); table 9 merges gate and up.

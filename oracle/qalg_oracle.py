@@ -15,8 +15,8 @@ What is computed, plainly:
   edge  when the inner indices agree; every other product is zero.
   `structure_table` writes those structure constants out as a list of
   (left slot, right slot, result slot) triples (eq 5 with c = 1 on each triple).
-* Lifted to matrix blocks, each triple is one block GEMM (section 1, "every
-  juxtaposition ... is one ordinary block GEMM").  `square_product` sums the
+* Lifted to matrix blocks, each triple is one block GEMM (section 1: a
+  product of two blocks in the table is an ordinary GEMM).  `square_product` sums the
   block GEMMs of every triple (eq 10-11, eq 13-14 for the complete graph Q_q).
 * The row-typed projection (section 4, eq 16-17; section 6.1, eq 27 and
   Algorithm 1) gives each token row m the type i = tau[m]; the row uses the
@@ -30,11 +30,14 @@ What is computed, plainly:
 * `mac_count` counts the multiply-accumulates the row-typed evaluator executes
   (eq 18-19; eq 24 for equal groups).
 * `gated_forward` is the gate/up half of a gated (SwiGLU) FFN: both D x F
-  projections follow the same row law (section 2: "the same row law applies
-  to each shape"; gates and pointwise activations keep their usual
-  definitions), combined as silu(X *_{Q_q} W_gate) * (X *_{Q_q} W_up), silu
+  projections are row-typed exactly like any other projection, while gates
+  and pointwise activations are left as they are (section 4), combined as silu(X *_{Q_q} W_gate) * (X *_{Q_q} W_up), silu
   being x * sigmoid(x) (the pilot's bias-free SwiGLU, appendix D; SwiGLU
   x * sigma(beta x) with beta = 1).
+* `gated_ffn_forward` / `gated_ffn_backward` are the whole gated FFN
+  (gate, up, down; section 4) and its training step: the projections' VJPs
+  from appendix B and the chain rule through silu(G) * U
+  (`swiglu_backward`, with silu' = sigmoid (1 + x (1 - sigmoid))).
 
 All arithmetic is float64; block products are numpy.matmul (a library
 primitive standing for one block GEMM).  The oracle itself rounds nothing.
@@ -351,7 +354,7 @@ def dense_equivalent_macs(M: int, K: int, N: int) -> int:
 
 
 # ----------------------------------------------------------------------------
-# Gated FFN: section 2 (gated FFN shapes, the same row law for each
+# Gated FFN: section 4 (gated FFN shapes, the same row law for each
 # projection), the pilot's bias-free SwiGLU (appendix D), table 9
 # ----------------------------------------------------------------------------
 
@@ -371,3 +374,49 @@ def gated_forward(X: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, tau: np.ndarray
     G = row_typed_forward(X, Wg, tau, q)
     U = row_typed_forward(X, Wu, tau, q)
     return silu(G) * U
+
+
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d silu / dz = sigmoid(z) (1 + z (1 - sigmoid(z))), evaluated in float64."""
+    z = np.asarray(z, dtype=np.float64)
+    sg = 1.0 / (1.0 + np.exp(-z))
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+def swiglu(G: np.ndarray, U: np.ndarray) -> np.ndarray:
+    """The pointwise gate of a SwiGLU FFN: silu(G) * U (appendix D; beta = 1)."""
+    return silu(G) * np.asarray(U, dtype=np.float64)
+
+
+def swiglu_backward(G: np.ndarray, U: np.ndarray, dH: np.ndarray):
+    """(dG, dU) of H = silu(G) * U: dG = dH * U * silu'(G), dU = dH * silu(G)."""
+    dH = np.asarray(dH, dtype=np.float64)
+    return dH * np.asarray(U, dtype=np.float64) * silu_grad(G), dH * silu(G)
+
+
+def gated_ffn_forward(X, Wg, Wu, Wd, tau, q):
+    """Y = (silu(X *_Q W_gate) * (X *_Q W_up)) *_Q W_down, each projection row-typed with the
+    same tau (section 4: all three gated-FFN weights are row-typed projections).
+
+    Returns Y and the intermediates (G, U, H) that the backward pass uses.
+    """
+    G = row_typed_forward(X, Wg, tau, q)
+    U = row_typed_forward(X, Wu, tau, q)
+    H = swiglu(G, U)
+    return row_typed_forward(H, Wd, tau, q), (G, U, H)
+
+
+def gated_ffn_backward(X, Wg, Wu, Wd, dY, tau, q):
+    """(dX, dW_gate, dW_up, dW_down) of `gated_ffn_forward`.
+
+    Each projection's VJP is appendix B's (eq 31-35) with the same support as
+    its forward; the activation's is the chain rule of silu(G) * U.  Six
+    projection-shaped products against the forward's three: the 9 B D F ->
+    9 rho B D F training count of section 6.2.
+    """
+    _, (G, U, H) = gated_ffn_forward(X, Wg, Wu, Wd, tau, q)
+    dH, dWd = row_typed_backward(H, Wd, dY, tau, q)
+    dG, dU = swiglu_backward(G, U, dH)
+    dXg, dWg = row_typed_backward(X, Wg, dG, tau, q)
+    dXu, dWu = row_typed_backward(X, Wu, dU, tau, q)
+    return dXg + dXu, dWg, dWu, dWd

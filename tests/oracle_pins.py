@@ -515,7 +515,7 @@ def pin_type_schedule(O):
 
 
 # --------------------------------------------------------------------------
-# gated FFN (section 2; appendix D's SwiGLU)
+# gated FFN (section 4; appendix D's SwiGLU)
 # --------------------------------------------------------------------------
 
 def pin_silu_values(O):
@@ -547,6 +547,46 @@ def pin_gated_masked_dense(O, seed=31):
                 assert abs(H[m, n] - want) <= 1e-12 * (1.0 + abs(want)), (q, m, n)
 
 
+def pin_silu_grad(O):
+    """silu' from central differences of silu (error O(h^2)), silu'(0) = 1/2, and
+    silu'(x) + silu'(-x) = 1 (the derivative of silu(x) - silu(-x) = x)."""
+    x = np.linspace(-12.0, 12.0, 97)
+    h = 1e-5
+    fd = (O.silu(x + h) - O.silu(x - h)) / (2 * h)
+    np.testing.assert_allclose(O.silu_grad(x), fd, rtol=1e-8, atol=1e-9)
+    assert O.silu_grad(np.array([0.0]))[0] == 0.5
+    np.testing.assert_allclose(O.silu_grad(x) + O.silu_grad(-x), np.ones_like(x), rtol=1e-14, atol=1e-14)
+
+
+def pin_gated_ffn_autograd(O, seed=33):
+    """float64 torch autograd of the masked-dense gated FFN, silu(x T_i(W_g)) * (x T_i(W_u)) then
+    T_i(W_d), equals the oracle's forward and its (dX, dW_gate, dW_up, dW_down)."""
+    import torch
+    g = _rng(seed)
+    for q, M, s, r in ((2, 9, 3, 2), (3, 8, 2, 3), (4, 11, 1, 2)):
+        D, F = q * s, q * r
+        Xn = g.standard_normal((M, D))
+        Wgn = g.standard_normal((D, F))
+        Wun = g.standard_normal((D, F))
+        Wdn = g.standard_normal((F, D))
+        dYn = g.standard_normal((M, D))
+        tau = g.integers(0, q, size=M)
+        X, Wg, Wu, Wd = (torch.tensor(a, requires_grad=True) for a in (Xn, Wgn, Wun, Wdn))
+        rows = []
+        for m in range(M):
+            i = int(tau[m])
+            mk = lambda W: torch.tensor(masked_bank(np.ones(W.shape), i, q))  # noqa: E731
+            h = torch.nn.functional.silu(X[m:m + 1] @ (Wg * mk(Wgn))) * (X[m:m + 1] @ (Wu * mk(Wun)))
+            rows.append(h @ (Wd * mk(Wdn)))
+        Y = torch.cat(rows)
+        (Y * torch.tensor(dYn)).sum().backward()
+        Yo, _ = O.gated_ffn_forward(Xn, Wgn, Wun, Wdn, tau, q)
+        np.testing.assert_allclose(Yo, Y.detach().numpy(), rtol=1e-12, atol=1e-12)
+        got = O.gated_ffn_backward(Xn, Wgn, Wun, Wdn, dYn, tau, q)
+        for a, t in zip(got, (X, Wg, Wu, Wd)):
+            np.testing.assert_allclose(a, t.grad.numpy(), rtol=1e-11, atol=1e-11)
+
+
 ALL_PINS = [
     pin_q2_table, pin_q2_scalar_example, pin_eq3_rectangular_blocks, pin_eq13_14,
     pin_product_counts, pin_graph_counts, pin_appendix_a, pin_associativity,
@@ -554,4 +594,5 @@ ALL_PINS = [
     pin_masked_dense, pin_row_typed_is_square_rows, pin_q1_is_matmul, pin_block_diagonal,
     pin_coverage, pin_vjp_scalar_eq31_35, pin_vjp_autograd, pin_vjp_adjoint,
     pin_mac_count, pin_type_index, pin_type_schedule, pin_silu_values, pin_gated_masked_dense,
+    pin_silu_grad, pin_gated_ffn_autograd,
 ]

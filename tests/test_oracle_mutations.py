@@ -17,6 +17,8 @@ _real_bwd = O.row_typed_backward
 _real_index = O.type_index
 _real_silu = O.silu
 _real_gated = O.gated_forward
+_real_silu_grad = O.silu_grad
+_real_swiglu_bwd = O.swiglu_backward
 
 
 def table_with_edge_edge(q, edges=None):
@@ -149,6 +151,24 @@ def gated_dense_gate(X, Wg, Wu, tau, q):
     return _real_silu(np.asarray(X, float) @ np.asarray(Wg, float)) * O.row_typed_forward(X, Wu, tau, q)
 
 
+def silu_grad_drops_term(z):
+    """Mistake: silu' taken as sigmoid(z) alone (the product rule's second term dropped)."""
+    z = np.asarray(z, float)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def swiglu_bwd_swapped(G, U, dH):
+    """Mistake: the gate and up gradients exchanged."""
+    dG, dU = _real_swiglu_bwd(G, U, dH)
+    return dU, dG
+
+
+def swiglu_bwd_no_up(G, U, dH):
+    """Mistake: the gate gradient misses the factor U."""
+    dH = np.asarray(dH, float)
+    return dH * _real_silu_grad(G), dH * _real_silu(G)
+
+
 MUTANTS = [
     ("structure_table", table_with_edge_edge),
     ("structure_table", table_without_right_vertex),
@@ -164,6 +184,9 @@ MUTANTS = [
     ("silu", silu_wrong_sign),
     ("gated_forward", gated_swapped),
     ("gated_forward", gated_dense_gate),
+    ("silu_grad", silu_grad_drops_term),
+    ("swiglu_backward", swiglu_bwd_swapped),
+    ("swiglu_backward", swiglu_bwd_no_up),
 ]
 
 
