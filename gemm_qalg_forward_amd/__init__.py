@@ -7,7 +7,8 @@ tensor is not on the GPU, the call raises.
 
 Functions carry the C names:
     qalg_forward, qalg_backward_dx, qalg_backward_dw, qalg_forward_batched,
-    qalg_gated_forward, qalg_merge_gate_up, qalg_type_schedule, qalg_build_index, qalg_build_index_batched,
+    qalg_gated_forward, qalg_merge_gate_up, qalg_split_gate_up, qalg_swiglu_forward, qalg_swiglu_backward,
+    qalg_type_schedule, qalg_build_index, qalg_build_index_batched,
     qalg_read_status, qalg_workspace_bytes, qalg_index_layout,
     qalg_status_string, qalg_version.
 """
@@ -23,8 +24,8 @@ __all__ = [
     "qalg_version", "qalg_status_string", "qalg_workspace_bytes", "qalg_index_layout",
     "qalg_type_schedule", "qalg_build_index", "qalg_build_index_batched",
     "qalg_forward", "qalg_backward_dx", "qalg_backward_dw", "qalg_forward_batched",
-    "qalg_gated_forward", "qalg_merge_gate_up",
-    "qalg_read_status", "workspace",
+    "qalg_gated_forward", "qalg_merge_gate_up", "qalg_split_gate_up", "qalg_swiglu_forward",
+    "qalg_swiglu_backward", "qalg_read_status", "workspace",
 ]
 
 QALG_F32 = 0
@@ -60,6 +61,9 @@ _SIGS = {
     "qalg_forward_batched": (ctypes.c_int, [_c_i32, _vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
     "qalg_gated_forward": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
     "qalg_merge_gate_up": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i64, _vp, _c_i32, _vp]),
+    "qalg_split_gate_up": (ctypes.c_int, [_vp, _c_i32, _c_i64, _c_i64, _vp, _vp, _c_i32, _vp]),
+    "qalg_swiglu_forward": (ctypes.c_int, [_vp, _c_i32, _c_i64, _c_i64, _vp, _c_i32, _vp]),
+    "qalg_swiglu_backward": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i64, _vp, _c_i32, _vp]),
     "qalg_read_status": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i64, _vp, ctypes.POINTER(_c_i64)]),
 }
 
@@ -243,6 +247,53 @@ def qalg_merge_gate_up(Wg, Wu, q: int, Wgu=None, stream=None):
     _check("qalg_merge_gate_up", lib().qalg_merge_gate_up(
         _dev_ptr(Wg, "Wg"), _dev_ptr(Wu, "Wu"), q, K, F, _dev_ptr(Wgu, "Wgu"), _dtype_code(Wg), _stream(stream)))
     return Wgu
+
+
+def qalg_split_gate_up(Wgu, q: int, Wg=None, Wu=None, stream=None):
+    """Inverse of the merge: Wgu [K, 2F] -> (Wg, Wu), each [K, F]."""
+    torch = _torch()
+    K, F2 = Wgu.shape
+    if F2 % 2:
+        raise ValueError("Wgu must have an even number of columns")
+    F = F2 // 2
+    if Wg is None:
+        Wg = torch.empty((K, F), dtype=Wgu.dtype, device=Wgu.device)
+    if Wu is None:
+        Wu = torch.empty((K, F), dtype=Wgu.dtype, device=Wgu.device)
+    _check("qalg_split_gate_up", lib().qalg_split_gate_up(
+        _dev_ptr(Wgu, "Wgu"), q, K, F, _dev_ptr(Wg, "Wg"), _dev_ptr(Wu, "Wu"), _dtype_code(Wgu), _stream(stream)))
+    return Wg, Wu
+
+
+def qalg_swiglu_forward(GU, q: int, H=None, stream=None):
+    """H = silu(gate) * up on merged pre-activations: GU [M, 2F] -> H [M, F]."""
+    torch = _torch()
+    M, F2 = GU.shape
+    if F2 % 2:
+        raise ValueError("GU must have an even number of columns")
+    if H is None:
+        H = torch.empty((M, F2 // 2), dtype=GU.dtype, device=GU.device)
+    elif tuple(H.shape) != (M, F2 // 2) or H.dtype != GU.dtype:
+        raise ValueError("H must be [M, F] with the dtype of GU")
+    _check("qalg_swiglu_forward", lib().qalg_swiglu_forward(
+        _dev_ptr(GU, "GU"), q, M, F2 // 2, _dev_ptr(H, "H"), _dtype_code(GU), _stream(stream)))
+    return H
+
+
+def qalg_swiglu_backward(GU, dH, q: int, dGU=None, stream=None):
+    """(dgate, dup) of H = silu(gate) * up, merged: GU [M, 2F], dH [M, F] -> dGU [M, 2F]."""
+    torch = _torch()
+    M, F2 = GU.shape
+    if F2 % 2 or tuple(dH.shape) != (M, F2 // 2) or dH.dtype != GU.dtype:
+        raise ValueError("GU must be [M, 2F] and dH [M, F] of the same dtype")
+    if dGU is None:
+        dGU = torch.empty((M, F2), dtype=GU.dtype, device=GU.device)
+    elif tuple(dGU.shape) != (M, F2) or dGU.dtype != GU.dtype:
+        raise ValueError("dGU must be [M, 2F] with the dtype of GU")
+    _check("qalg_swiglu_backward", lib().qalg_swiglu_backward(
+        _dev_ptr(GU, "GU"), _dev_ptr(dH, "dH"), q, M, F2 // 2, _dev_ptr(dGU, "dGU"), _dtype_code(GU),
+        _stream(stream)))
+    return dGU
 
 
 def qalg_gated_forward(X, Wgu, tau, q: int, H=None, ws=None, flags: int = 0, stream=None):

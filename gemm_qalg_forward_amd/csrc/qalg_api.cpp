@@ -276,6 +276,44 @@ qalg_status qalg_merge_gate_up(const void* Wg, const void* Wu, int32_t q, int64_
   return hip_status(qalg::launch_merge_gate_up_bf16(Wg, Wu, Wgu, K, F, q, static_cast<hipStream_t>(stream)));
 }
 
+qalg_status qalg_split_gate_up(const void* Wgu, int32_t q, int64_t K, int64_t F, void* Wg, void* Wu,
+                               int32_t dtype, void* stream) {
+  if (dtype != QALG_BF16) return QALG_ERR_DTYPE;
+  if (K <= 0 || F <= 0 || K > INT32_MAX / 2 || F > INT32_MAX / 4) return QALG_ERR_DIM;
+  if (q < 1 || q > QALG_MAX_Q || F % q) return QALG_ERR_Q;
+  if ((F / q) % 128) return QALG_ERR_ALIGN;
+  if (Wgu == nullptr || Wg == nullptr || Wu == nullptr) return QALG_ERR_NULL;
+  if (!aligned16(Wgu) || !aligned16(Wg) || !aligned16(Wu)) return QALG_ERR_ALIGN;
+  return hip_status(qalg::launch_split_gate_up_bf16(Wgu, Wg, Wu, K, F, q, static_cast<hipStream_t>(stream)));
+}
+
+// shared checks of the two pointwise SwiGLU entry points
+static qalg_status check_swiglu(int32_t q, int64_t M, int64_t F, int32_t dtype) {
+  if (dtype != QALG_BF16) return QALG_ERR_DTYPE;
+  if (M < 0 || F <= 0 || F > INT32_MAX / 4) return QALG_ERR_DIM;
+  if (q < 1 || q > QALG_MAX_Q || F % q) return QALG_ERR_Q;
+  if ((F / q) % 128) return QALG_ERR_ALIGN;
+  return QALG_OK;
+}
+
+qalg_status qalg_swiglu_forward(const void* GU, int32_t q, int64_t M, int64_t F, void* H, int32_t dtype,
+                                void* stream) {
+  if (qalg_status st = check_swiglu(q, M, F, dtype)) return st;
+  if (M == 0) return QALG_OK;
+  if (GU == nullptr || H == nullptr) return QALG_ERR_NULL;
+  if (!aligned16(GU) || !aligned16(H)) return QALG_ERR_ALIGN;
+  return hip_status(qalg::launch_swiglu_fwd_bf16(GU, H, M, F, q, static_cast<hipStream_t>(stream)));
+}
+
+qalg_status qalg_swiglu_backward(const void* GU, const void* dH, int32_t q, int64_t M, int64_t F, void* dGU,
+                                 int32_t dtype, void* stream) {
+  if (qalg_status st = check_swiglu(q, M, F, dtype)) return st;
+  if (M == 0) return QALG_OK;
+  if (GU == nullptr || dH == nullptr || dGU == nullptr) return QALG_ERR_NULL;
+  if (!aligned16(GU) || !aligned16(dH) || !aligned16(dGU)) return QALG_ERR_ALIGN;
+  return hip_status(qalg::launch_swiglu_bwd_bf16(GU, dH, dGU, M, F, q, static_cast<hipStream_t>(stream)));
+}
+
 qalg_status qalg_read_status(const void* ws, int32_t E, int32_t q, int64_t M, void* stream,
                              int64_t* bad_tau_rows) {
   if (ws == nullptr || bad_tau_rows == nullptr) return QALG_ERR_NULL;

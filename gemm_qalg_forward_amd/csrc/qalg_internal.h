@@ -91,6 +91,12 @@ bool fwd_gated_supported(const ProblemDesc& p);
 hipError_t launch_fwd_gated_bf16(const ProblemDesc& p, hipStream_t s);
 hipError_t launch_merge_gate_up_bf16(const void* Wg, const void* Wu, void* Wgu, int64_t K, int64_t F, int q,
                                      hipStream_t s);
+// pointwise SwiGLU pieces on the merged gate/up layout (qalg_act.hip)
+hipError_t launch_swiglu_fwd_bf16(const void* GU, void* H, int64_t M, int64_t F, int q, hipStream_t s);
+hipError_t launch_swiglu_bwd_bf16(const void* GU, const void* dH, void* dGU, int64_t M, int64_t F, int q,
+                                  hipStream_t s);
+hipError_t launch_split_gate_up_bf16(const void* Wgu, void* Wg, void* Wu, int64_t K, int64_t F, int q,
+                                     hipStream_t s);
 // Persistent 256-row-tile dX / dW (bf16, one problem) for cyclic schedules; a
 // launch on any other schedule returns at once.
 bool grad_persistent_supported(const ProblemDesc& p);

@@ -222,6 +222,40 @@ qalg_status qalg_merge_gate_up(const void* Wg, const void* Wu, int32_t q, int64_
                                void* Wgu, int32_t dtype, void* stream);
 
 /*
+ * Inverse of qalg_merge_gate_up: Wgu (K x 2F, merged) -> Wg, Wu (K x F each),
+ * e.g. to read the merged gradient from qalg_backward_dw as two banks.  Same
+ * requirements and errors as the merge.
+ */
+qalg_status qalg_split_gate_up(const void* Wgu, int32_t q, int64_t K, int64_t F, void* Wg, void* Wu,
+                               int32_t dtype, void* stream);
+
+/*
+ * Pointwise SwiGLU gate on merged pre-activations, for the training step of a
+ * gated FFN (section 4: gates and pointwise activations keep their usual
+ * definitions; appendix D: bias-free SwiGLU, silu(z) = z * sigmoid(z)).
+ * GU: M x 2F, the merged [gate | up] pre-activations, i.e. qalg_forward of X
+ * with the merged bank Wgu and N = 2F (merging permutes columns within each
+ * output group, so that product is the merged pair of row-typed products).
+ * H: M x F (overwritten), H = silu(gate) * up, computed in fp32 and rounded
+ * once (RNE).  bf16 only; F / q must be a multiple of 128 (QALG_ERR_ALIGN);
+ * M = 0 returns QALG_OK without a launch.
+ */
+qalg_status qalg_swiglu_forward(const void* GU, int32_t q, int64_t M, int64_t F, void* H,
+                                int32_t dtype, void* stream);
+
+/*
+ * Its vector-Jacobian product (chain rule through silu(gate) * up):
+ * dgate = dH * up * silu'(gate), dup = dH * silu(gate), silu'(z) =
+ * sigmoid(z) (1 + z (1 - sigmoid(z))).  GU: M x 2F merged (as above), dH:
+ * M x F, dGU: M x 2F (overwritten, merged layout: the input of
+ * qalg_backward_dx / qalg_backward_dw with the merged bank and N = 2F, which
+ * give dX and the merged dWgu, App B eq 31-35).  fp32 arithmetic, one RNE
+ * rounding per output.  Same requirements as qalg_swiglu_forward.
+ */
+qalg_status qalg_swiglu_backward(const void* GU, const void* dH, int32_t q, int64_t M, int64_t F,
+                                 void* dGU, int32_t dtype, void* stream);
+
+/*
  * Number of rows with an out-of-range type seen by the last index build in
  * ws (summed over the E problems of a batched workspace; E = 1 otherwise).
  * Synchronises `stream`.

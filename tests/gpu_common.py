@@ -51,3 +51,18 @@ def make_tau(kind: str, M: int, q: int, seed: int = 0, offset: int = 0, bad: int
 def say(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+def merge_perm(F: int, q: int) -> np.ndarray:
+    """Column map of the merged gate/up layout (include/qalg.h): merged column k holds column
+    perm[k] of the concatenation [gate | up] (up columns offset by F)."""
+    r = F // q
+    perm = np.empty(2 * F, dtype=np.int64)
+    for j in range(q):
+        for t in range(r // 128):
+            c0, base = j * r + 128 * t, j * 2 * r + 256 * t
+            perm[base:base + 64] = np.arange(c0, c0 + 64)
+            perm[base + 64:base + 128] = F + np.arange(c0, c0 + 64)
+            perm[base + 128:base + 192] = np.arange(c0 + 64, c0 + 128)
+            perm[base + 192:base + 256] = F + np.arange(c0 + 64, c0 + 128)
+    return perm

@@ -151,3 +151,34 @@ def test_merge_argument_errors_are_synchronous(lib):
     assert m(K=0) == 2
     assert m(Wu=None) == 1
     assert m(Wgu=FAKE + 4) == 4
+
+
+def test_split_argument_errors_are_synchronous(lib):
+    sp = lambda **k: lib.qalg_split_gate_up(k.get("Wgu", FAKE), k.get("q", 2), k.get("K", 64), k.get("F", 512),  # noqa: E731
+                                            k.get("Wg", FAKE), k.get("Wu", FAKE), k.get("dt", 1), None)
+    assert sp(dt=0) == 5
+    assert sp(F=384) == 4
+    assert sp(q=3) == 3
+    assert sp(K=0) == 2
+    assert sp(Wg=None) == 1
+    assert sp(Wu=FAKE + 8) == 4
+
+
+def test_swiglu_argument_errors_are_synchronous(lib):
+    fw = lambda **k: lib.qalg_swiglu_forward(k.get("GU", FAKE), k.get("q", 2), k.get("M", 64), k.get("F", 512),  # noqa: E731
+                                             k.get("H", FAKE), k.get("dt", 1), None)
+    bw = lambda **k: lib.qalg_swiglu_backward(k.get("GU", FAKE), k.get("dH", FAKE), k.get("q", 2),  # noqa: E731
+                                              k.get("M", 64), k.get("F", 512), k.get("dGU", FAKE), k.get("dt", 1), None)
+    for f in (fw, bw):
+        assert f(dt=0) == 5                 # bf16 only
+        assert f(M=-1) == 2
+        assert f(F=0) == 2
+        assert f(q=0) == 3
+        assert f(q=3) == 3                  # 3 does not divide 512
+        assert f(F=384) == 4                # F / q = 192: not a multiple of 128
+        assert f(GU=None) == 1
+        assert f(GU=FAKE + 2) == 4
+        assert f(M=0, GU=None) == 0         # no rows: nothing to do, no launch
+    assert fw(H=None) == 1
+    assert bw(dH=None) == 1
+    assert bw(dGU=FAKE + 4) == 4
