@@ -320,8 +320,56 @@ def gated_leg(Q, torch, np, synth, dev, stream):
     res = {"workload": "gated_ffn_D4096_F12288_q8_M16384_bf16", "gate_up_ms": round(tg, 4),
            "gate_up_tflops": round(2 * flop / (tg * 1e-3) / 1e12, 1), "down_ms": round(td, 4),
            "step_ms": round(tg + td, 4), "step_tflops": round(3 * flop / ((tg + td) * 1e-3) / 1e12, 1)}
+    res["training"] = gated_train(Q, torch, np, synth, dev, stream, Xd, Wgu, Wdd, tau, ws, H, Y, flop)
     log(f"[bench] gated FFN leg: {res}")
     return res
+
+
+def gated_train(Q, torch, np, synth, dev, stream, Xd, Wgu, Wdd, tau, ws, H, Y, flop):
+    """Training step of the gated FFN on the merged layout: merged forward, pointwise SwiGLU, down
+    forward; down dX and dW, pointwise SwiGLU VJP, merged dX and dW.  9 projections (section 6.2)."""
+    r = Q.QALG_FLAG_INDEX_READY
+    dY = torch.from_numpy(synth.normal_operand(6005, (M, D), 1.0, "bf16").bits.view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    GU = torch.empty(M, 2 * F, dtype=torch.bfloat16, device=dev)
+    dGU = torch.empty_like(GU)
+    dH = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    dWd = torch.empty(F, D, dtype=torch.bfloat16, device=dev)
+    dWgu = torch.empty(D, 2 * F, dtype=torch.bfloat16, device=dev)
+    ops = [
+        ("fwd_gate_up", lambda: Q.qalg_forward(Xd, Wgu, tau, QQ, Y=GU, ws=ws, flags=r, stream=stream)),
+        ("swiglu_fwd", lambda: Q.qalg_swiglu_forward(GU, QQ, H=H, stream=stream)),
+        ("fwd_down", lambda: Q.qalg_forward(H, Wdd, tau, QQ, Y=Y, ws=ws, flags=r, stream=stream)),
+        ("dx_down", lambda: Q.qalg_backward_dx(dY, Wdd, tau, QQ, dX=dH, ws=ws, flags=r, stream=stream)),
+        ("dw_down", lambda: Q.qalg_backward_dw(H, dY, tau, QQ, dW=dWd, ws=ws, flags=r, stream=stream)),
+        ("swiglu_bwd", lambda: Q.qalg_swiglu_backward(GU, dH, QQ, dGU=dGU, stream=stream)),
+        ("dx_gate_up", lambda: Q.qalg_backward_dx(dGU, Wgu, tau, QQ, dX=dX, ws=ws, flags=r, stream=stream)),
+        ("dw_gate_up", lambda: Q.qalg_backward_dw(Xd, dGU, tau, QQ, dW=dWgu, ws=ws, flags=r, stream=stream)),
+    ]
+    for _ in range(2):
+        for _, f in ops:
+            f()
+    torch.cuda.synchronize()
+    n = 5
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)]
+    tot = [0.0] * len(ops)
+    for _ in range(n):
+        ev[0].record(stream)
+        for k, (_, f) in enumerate(ops):
+            f()
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        for k in range(len(ops)):
+            tot[k] += ev[k].elapsed_time(ev[k + 1])
+    ms = {name: t / n for (name, _), t in zip(ops, tot)}
+    step = sum(ms.values())
+    out = {f"{k}_ms": round(v, 4) for k, v in ms.items()}
+    out["step_ms"] = round(step, 4)
+    out["step_tflops"] = round(9 * flop / (step * 1e-3) / 1e12, 1)  # 9 projection-shaped products
+    out["swiglu_fwd_GBs"] = round(6.0 * M * F / (ms["swiglu_fwd"] * 1e-3) / 1e9, 1)   # gate, up in; H out
+    out["swiglu_bwd_GBs"] = round(10.0 * M * F / (ms["swiglu_bwd"] * 1e-3) / 1e9, 1)  # gate, up, dH in; 2 out
+    return out
 
 
 def decode_leg(Q, torch, np, synth, dev, stream):

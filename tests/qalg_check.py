@@ -11,6 +11,13 @@ import numpy as np
 BF16_TOL = 5e-3
 F32_TOL = 1e-5
 
+# The gated FFN's composed training step rounds to bf16 up to five times along
+# the path of any output (GU, H or dH, dGU, the output itself), each rounding
+# adding about 1.5e-3 relative error (the level one projection shows): about
+# sqrt(5) x 1.5e-3 = 3.4e-3 expected, 3.4-3.6e-3 measured.  Its bar is 1e-2 per
+# group, about 3x that; each projection given its bf16 inputs meets BF16_TOL.
+GATED_STEP_TOL = 1e-2
+
 
 def _rel(got: np.ndarray, ref: np.ndarray) -> float:
     den = float(np.linalg.norm(ref))

@@ -19,7 +19,7 @@ import gemm_qalg_forward_amd as Q
 import synth
 from gpu_common import say, tau_dev, to_dev, to_f64, torch_cuda
 from oracle import qalg_oracle as O
-from qalg_check import BF16_TOL, F32_TOL, assert_groups, rel_frob_blocks, rel_frob_col_groups
+from qalg_check import BF16_TOL, F32_TOL, GATED_STEP_TOL as STEP_TOL, assert_groups, rel_frob_blocks, rel_frob_col_groups
 
 pytestmark = pytest.mark.gpu
 
@@ -198,3 +198,57 @@ def test_gated_ffn_q8_sampled():
     Yr = O.row_typed_forward(Hr, Wd.f64, tau[rows], q)
     e2 = assert_groups(rel_frob_col_groups(to_f64(Y[rows]), Yr, q), BF16_TOL, "Y")
     say(f"    max rel err over {rows.size} sampled rows: H {e1:.2e}, Y {e2:.2e}")
+
+
+def test_gated_ffn_training_q8_sampled():
+    """The benchmark's gated FFN training step at full size (same seeds and calls).  Y and dX on
+    sampled rows (row-local in the oracle); dW on one column per group (q columns keep the group
+    structure, so the oracle's table-driven VJP on the column subset is the subset of the full VJP)."""
+    torch = torch_cuda()
+    c, M, D, F, q = 6, 16384, 4096, 12288, 8
+    say(f"[workload] gated FFN training bf16 q=8 M={M} {D}->{F}->{D}")
+    X = synth.normal_operand(1000 * c + 1, (M, D), 1.0, "bf16")
+    Wg = synth.normal_operand(1000 * c + 2, (D, F), D ** -0.5, "bf16")
+    Wu = synth.normal_operand(1000 * c + 3, (D, F), D ** -0.5, "bf16")
+    Wd = synth.normal_operand(1000 * c + 4, (F, D), F ** -0.5, "bf16")
+    dY = synth.normal_operand(1000 * c + 5, (M, D), 1.0, "bf16")
+    pos = torch.from_numpy(synth.cyclic_positions(M)).to("cuda")
+    td = Q.qalg_type_schedule(pos, q)
+    ws = Q.workspace(q, M)
+    Q.qalg_build_index(td, q, ws=ws)
+    r = Q.QALG_FLAG_INDEX_READY
+    Xd, Wdd, dYd = to_dev(X), to_dev(Wd), to_dev(dY)
+    Wgu = Q.qalg_merge_gate_up(to_dev(Wg), to_dev(Wu), q)
+    GU = Q.qalg_forward(Xd, Wgu, td, q, ws=ws, flags=r)
+    H = Q.qalg_swiglu_forward(GU, q)
+    Y = Q.qalg_forward(H, Wdd, td, q, ws=ws, flags=r)
+    dH = Q.qalg_backward_dx(dYd, Wdd, td, q, ws=ws, flags=r)
+    dWd = Q.qalg_backward_dw(H, dYd, td, q, ws=ws, flags=r)
+    dGU = Q.qalg_swiglu_backward(GU, dH, q)
+    dX = Q.qalg_backward_dx(dGU, Wgu, td, q, ws=ws, flags=r)
+    dWgu = Q.qalg_backward_dw(Xd, dGU, td, q, ws=ws, flags=r)
+    dWg, dWu = Q.qalg_split_gate_up(dWgu, q)
+    torch.cuda.synchronize()
+    tau = td.cpu().numpy()
+    # rows: Y and dX
+    rows = _sample_rows(M, q, 256, 67)
+    Yr, _ = O.gated_ffn_forward(X.f64[rows], Wg.f64, Wu.f64, Wd.f64, tau[rows], q)
+    e = {"Y": assert_groups(rel_frob_col_groups(to_f64(Y[rows]), Yr, q), STEP_TOL, "Y")}
+    dXr = O.gated_ffn_backward(X.f64[rows], Wg.f64, Wu.f64, Wd.f64, dY.f64[rows], tau[rows], q)[0]
+    e["dX"] = assert_groups(rel_frob_col_groups(to_f64(dX[rows]), dXr, q), STEP_TOL, "dX")
+    # columns: one per output group of each bank
+    cf = np.array([j * (F // q) + 37 for j in range(q)])   # F-side columns (gate/up outputs, down inputs)
+    cd = np.array([j * (D // q) + 5 for j in range(q)])    # D-side columns (down outputs)
+    G_all = O.row_typed_forward(X.f64, Wg.f64, tau, q)
+    U_all = O.row_typed_forward(X.f64, Wu.f64, tau, q)
+    H_all = O.swiglu(G_all, U_all)
+    dWd_r = O.row_typed_backward(H_all, Wd.f64[:, cd], dY.f64[:, cd], tau, q)[1]
+    e["dW_down"] = assert_groups(rel_frob_blocks(to_f64(dWd[:, cd]), dWd_r, q), STEP_TOL, "dW_down")
+    # dH on the down projection's input columns cf (all rows), then the SwiGLU VJP there
+    dH_cf = O.row_typed_backward(H_all[:, cf], Wd.f64[cf], dY.f64, tau, q)[0]
+    dG_cf, dU_cf = O.swiglu_backward(G_all[:, cf], U_all[:, cf], dH_cf)
+    dWg_r = O.row_typed_backward(X.f64, Wg.f64[:, cf], dG_cf, tau, q)[1]
+    dWu_r = O.row_typed_backward(X.f64, Wu.f64[:, cf], dU_cf, tau, q)[1]
+    e["dW_gate"] = assert_groups(rel_frob_blocks(to_f64(dWg[:, cf]), dWg_r, q), STEP_TOL, "dW_gate")
+    e["dW_up"] = assert_groups(rel_frob_blocks(to_f64(dWu[:, cf]), dWu_r, q), STEP_TOL, "dW_up")
+    say("    " + ", ".join(f"{k} {v:.2e}" for k, v in e.items()))
