@@ -29,6 +29,11 @@ What is computed, plainly:
   the cyclic tau; appendix D.5, the interval schedule of the pilot).
 * `mac_count` counts the multiply-accumulates the row-typed evaluator executes
   (eq 18-19; eq 24 for equal groups).
+* `tensor_power_table` lists the triples of the recursive law Q_2^{(x)L}
+  (appendix C): bit-string slots, one Q_2 triple per level, 6^L triples; the
+  evaluators take any law's triples through their `table` argument, so a row
+  of type alpha sums x_beta W_beta,delta over the beta whose bits each come
+  from alpha or delta (eq 36's support; section 6.1's B(i, j) for this law).
 * `gated_forward` is the gate/up half of a gated (SwiGLU) FFN: both D x F
   projections are row-typed exactly like any other projection, while gates
   and pointwise activations are left as they are (section 4), combined as silu(X *_{Q_q} W_gate) * (X *_{Q_q} W_up), silu
@@ -68,6 +73,7 @@ __all__ = [
     "complete_graph_edges",
     "graph_slots",
     "structure_table",
+    "tensor_power_table",
     "group_bounds",
     "square_product",
     "row_typed_forward",
@@ -127,6 +133,27 @@ def structure_table(q: int, edges: Iterable[Slot] | None = None) -> list[Triple]
     return table
 
 
+def tensor_power_table(L: int) -> list[Triple]:
+    """Nonzero structure constants of the recursive law Q_2^{(x)L} (appendix C).
+
+    Basis elements of a tensor product are tensors of basis elements, and
+    their product is the tensor of the factors' products, so a triple of the
+    L-fold power is one Q_2 triple per level.  Slots are pairs of L-bit
+    strings (a, b); level 1 is the most significant bit (the first split of
+    the recursion).  L = 1 is Q_2 itself.
+    """
+    if L < 1:
+        raise ValueError("L >= 1")
+    base = structure_table(2)
+    table = base
+    for _ in range(L - 1):
+        table = [((2 * l[0] + l2[0], 2 * l[1] + l2[1]),
+                  (2 * r[0] + r2[0], 2 * r[1] + r2[1]),
+                  (2 * o[0] + o2[0], 2 * o[1] + o2[1]))
+                 for (l, r, o) in table for (l2, r2, o2) in base]
+    return table
+
+
 # ----------------------------------------------------------------------------
 # Block bookkeeping
 # ----------------------------------------------------------------------------
@@ -154,8 +181,9 @@ def square_product(X: np.ndarray, W: np.ndarray, q: int,
                    row_heights: Sequence[int] | None = None,
                    mid_widths: Sequence[int] | None = None,
                    out_widths: Sequence[int] | None = None,
-                   edges: Iterable[Slot] | None = None) -> np.ndarray:
-    """Block-array product Z = X *_{Q_G} W.
+                   edges: Iterable[Slot] | None = None,
+                   table: Sequence[Triple] | None = None) -> np.ndarray:
+    """Block-array product Z = X *_{Q_G} W (or of the law whose triples `table` lists).
 
     X is split into q x q blocks (block-row heights `row_heights`, block-column
     widths `mid_widths`), W into q x q blocks (heights `mid_widths`, widths
@@ -172,7 +200,7 @@ def square_product(X: np.ndarray, W: np.ndarray, q: int,
         raise ValueError("inner dimensions differ")
     ob = group_bounds(W.shape[1], q, out_widths)
     Z = np.zeros((X.shape[0], W.shape[1]), dtype=np.float64)
-    for (a, b), (_, d), (za, zd) in structure_table(q, edges):
+    for (a, b), (_, d), (za, zd) in (structure_table(q, edges) if table is None else table):
         xa = X[rb[a][0]:rb[a][1], mb[b][0]:mb[b][1]]
         wb = W[mb[b][0]:mb[b][1], ob[d][0]:ob[d][1]]
         Z[rb[za][0]:rb[za][1], ob[zd][0]:ob[zd][1]] += xa @ wb
@@ -237,8 +265,9 @@ def _row_sets(tau: np.ndarray, q: int) -> list[np.ndarray]:
 def row_typed_forward(X: np.ndarray, W: np.ndarray, tau: np.ndarray, q: int,
                       in_widths: Sequence[int] | None = None,
                       out_widths: Sequence[int] | None = None,
-                      edges: Iterable[Slot] | None = None) -> np.ndarray:
-    """Y = X *_{Q_G} W with row types tau (Algorithm 1).
+                      edges: Iterable[Slot] | None = None,
+                      table: Sequence[Triple] | None = None) -> np.ndarray:
+    """Y = X *_{Q_G} W with row types tau (Algorithm 1); `table` gives another law's triples.
 
     Y <- 0; for each type i with rows I_i, for each structure-constant triple
     (i, b) * (b, j) -> (i, j) whose left slot is in block-row i:
@@ -254,7 +283,8 @@ def row_typed_forward(X: np.ndarray, W: np.ndarray, tau: np.ndarray, q: int,
     N = W.shape[1]
     kb = group_bounds(K, q, in_widths)
     nb = group_bounds(N, q, out_widths)
-    table = structure_table(q, edges)
+    if table is None:
+        table = structure_table(q, edges)
     Y = np.zeros((M, N), dtype=np.float64)
     for i, rows in enumerate(_row_sets(tau, q)):
         if rows.size == 0:
@@ -276,8 +306,9 @@ def row_typed_forward(X: np.ndarray, W: np.ndarray, tau: np.ndarray, q: int,
 def row_typed_backward(X: np.ndarray, W: np.ndarray, dY: np.ndarray, tau: np.ndarray, q: int,
                        in_widths: Sequence[int] | None = None,
                        out_widths: Sequence[int] | None = None,
-                       edges: Iterable[Slot] | None = None):
-    """(dX, dW) of Y = X *_{Q_G} W (appendix B, eq 31-35).
+                       edges: Iterable[Slot] | None = None,
+                       table: Sequence[Triple] | None = None):
+    """(dX, dW) of Y = X *_{Q_G} W (appendix B, eq 31-35); `table` as in the forward.
 
     Each forward block GEMM Y[I_i, g_j] += X[I_i, g_b] W[g_b, g_j] contributes
         dX[I_i, g_b] += dY[I_i, g_j] W[g_b, g_j]^T      (eq 31-32)
@@ -293,7 +324,8 @@ def row_typed_backward(X: np.ndarray, W: np.ndarray, dY: np.ndarray, tau: np.nda
         raise ValueError("dY shape")
     kb = group_bounds(K, q, in_widths)
     nb = group_bounds(N, q, out_widths)
-    table = structure_table(q, edges)
+    if table is None:
+        table = structure_table(q, edges)
     dX = np.zeros((M, K), dtype=np.float64)
     dW = np.zeros((K, N), dtype=np.float64)
     for i, rows in enumerate(_row_sets(tau, q)):
@@ -328,7 +360,8 @@ def row_typed_forward_batched(X: np.ndarray, W: np.ndarray, tau: np.ndarray, q: 
 def mac_count(tau: np.ndarray, q: int, K: int, N: int,
               in_widths: Sequence[int] | None = None,
               out_widths: Sequence[int] | None = None,
-              edges: Iterable[Slot] | None = None) -> tuple[int, int]:
+              edges: Iterable[Slot] | None = None,
+              table: Sequence[Triple] | None = None) -> tuple[int, int]:
     """(block GEMMs executed, MACs executed) by `row_typed_forward` on these types.
 
     Counts, for every type i with M_i > 0, each triple with left slot in
@@ -339,7 +372,7 @@ def mac_count(tau: np.ndarray, q: int, K: int, N: int,
     counts, _, _, _ = type_index(tau, q)
     gemms = 0
     macs = 0
-    for (xa, _xb), (wa, wd), _out in structure_table(q, edges):
+    for (xa, _xb), (wa, wd), _out in (structure_table(q, edges) if table is None else table):
         Mi = int(counts[xa])
         if Mi == 0:
             continue
@@ -364,15 +397,16 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def gated_forward(X: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, tau: np.ndarray, q: int) -> np.ndarray:
+def gated_forward(X: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, tau: np.ndarray, q: int,
+                  table: Sequence[Triple] | None = None) -> np.ndarray:
     """H = silu(X *_{Q_q} W_gate) * (X *_{Q_q} W_up), both products row-typed with the same tau.
 
     The activation applies to the gate product, elementwise, after both
     endpoint sums of each product are complete (the same Algorithm 1 for
     both D x F weights).
     """
-    G = row_typed_forward(X, Wg, tau, q)
-    U = row_typed_forward(X, Wu, tau, q)
+    G = row_typed_forward(X, Wg, tau, q, table=table)
+    U = row_typed_forward(X, Wu, tau, q, table=table)
     return silu(G) * U
 
 

@@ -587,6 +587,139 @@ def pin_gated_ffn_autograd(O, seed=33):
             np.testing.assert_allclose(a, t.grad.numpy(), rtol=1e-11, atol=1e-11)
 
 
+# --------------------------------------------------------------------------
+# the recursive law Q_2^{(x)L} (appendix C; section 6.1's B(i, j) for it)
+# --------------------------------------------------------------------------
+
+def _bits_support(a, d, L):
+    """eq 36's index set: the beta whose every bit equals alpha's or delta's bit."""
+    return {b for b in range(2 ** L) if all(((b >> k) & 1) in (((a >> k) & 1), ((d >> k) & 1)) for k in range(L))}
+
+
+def tensor_masked_bank(W, a, L):
+    """W with block (beta, delta) zeroed unless beta's bits each come from alpha or delta."""
+    q = 2 ** L
+    K, N = W.shape
+    s, r = K // q, N // q
+    T = W.copy()
+    for b in range(q):
+        for d in range(q):
+            if b not in _bits_support(a, d, L):
+                T[b * s:(b + 1) * s, d * r:(d + 1) * r] = 0.0
+    return T
+
+
+def pin_tensor_counts(O):
+    """6^L triples (the recursive algorithm's 6^L products, appendix C.1); L = 1 is Q_2; at L = 2 the
+    4 * 1 + 8 * 2 + 4 * 4 = 36 split by Hamming distance of the endpoints."""
+    for L in (1, 2, 3):
+        assert len(O.tensor_power_table(L)) == 6 ** L
+    assert sorted(O.tensor_power_table(1)) == sorted(O.structure_table(2))
+    per_pair = {}
+    for (a, b), (_, d), out in O.tensor_power_table(2):
+        assert out == (a, d)
+        per_pair[(a, d)] = per_pair.get((a, d), 0) + 1
+    hist = {}
+    for (a, d), n in per_pair.items():
+        h = bin(a ^ d).count("1")
+        assert n == 2 ** h
+        hist[h] = hist.get(h, 0) + 1
+    assert hist == {0: 4, 1: 8, 2: 4}
+
+
+def pin_tensor_support(O):
+    """For every (alpha, delta), the intermediate groups of the table are eq 36's set."""
+    for L in (1, 2, 3):
+        got = {}
+        for (a, b), (b2, d), _ in O.tensor_power_table(L):
+            assert b == b2
+            got.setdefault((a, d), set()).add(b)
+        for a in range(2 ** L):
+            for d in range(2 ** L):
+                assert got.get((a, d), set()) == _bits_support(a, d, L), (L, a, d)
+
+
+def pin_tensor_associativity(O):
+    """The tensor power is associative (all basis triples at L = 2), and unlike Q_4 its radical (slots
+    with a != b) does not square to zero (appendix C: J (x) J is nonzero)."""
+    L = 2
+    prod = {}
+    for x, y, z in O.tensor_power_table(L):
+        prod[(x, y)] = z
+    slots = [(a, b) for a in range(4) for b in range(4)]
+
+    def mul(x, y):
+        return None if x is None or y is None else prod.get((x, y))
+
+    for x in slots:
+        for y in slots:
+            for z in slots:
+                assert mul(mul(x, y), z) == mul(x, mul(y, z)), (x, y, z)
+    rad = [x for x in slots if x[0] != x[1]]
+    assert any(mul(x, y) is not None for x in rad for y in rad)
+    q4 = {(x, y) for x, y, _ in O.structure_table(4)}
+    assert not any((x, y) in q4 for x in rad for y in rad)
+
+
+def pin_tensor_masked_dense(O, seed=41):
+    """Row-typed evaluation with the tensor table equals x T_alpha(W) with the bit-rule mask."""
+    g = _rng(seed)
+    for L, M, s, r in ((1, 7, 2, 3), (2, 12, 2, 2), (3, 10, 1, 2)):
+        q = 2 ** L
+        X = g.standard_normal((M, q * s))
+        W = g.standard_normal((q * s, q * r))
+        tau = g.integers(0, q, size=M)
+        Y = O.row_typed_forward(X, W, tau, q, table=O.tensor_power_table(L))
+        for m in range(M):
+            want = X[m] @ tensor_masked_bank(W, int(tau[m]), L)
+            np.testing.assert_allclose(Y[m], want, rtol=1e-12, atol=1e-12)
+
+
+def pin_tensor_cost(O, seed=42):
+    """eq 36 per type on unequal widths; equal widths and uniform types give (3/4)^L of dense (C.1)."""
+    g = _rng(seed)
+    L = 2
+    q = 4
+    sw = [3, 1, 4, 2]
+    rw = [2, 5, 1, 3]
+    tau = np.array([0, 1, 1, 2, 3, 3, 3])
+    _, macs = O.mac_count(tau, q, sum(sw), sum(rw), sw, rw, table=O.tensor_power_table(L))
+    want = 0
+    for a in range(q):
+        Ma = int(np.sum(tau == a))
+        for d in range(q):
+            for b in _bits_support(a, d, L):
+                want += Ma * sw[b] * rw[d]
+    assert macs == want
+    for L in (1, 2, 3):
+        q = 2 ** L
+        tau = np.repeat(np.arange(q), 3)
+        K, N = 2 * q, 3 * q
+        _, macs = O.mac_count(tau, q, K, N, table=O.tensor_power_table(L))
+        assert macs * 4 ** L == 3 ** L * tau.size * K * N
+    del g
+
+
+def pin_tensor_vjp_autograd(O, seed=43):
+    """float64 torch autograd of the tensor law's masked-dense form equals the table-driven VJPs."""
+    import torch
+    g = _rng(seed)
+    for L, M, s, r in ((2, 11, 2, 3), (3, 9, 1, 1)):
+        q = 2 ** L
+        Xn = g.standard_normal((M, q * s))
+        Wn = g.standard_normal((q * s, q * r))
+        dYn = g.standard_normal((M, q * r))
+        tau = g.integers(0, q, size=M)
+        X = torch.tensor(Xn, requires_grad=True)
+        W = torch.tensor(Wn, requires_grad=True)
+        rows = [X[m:m + 1] @ (W * torch.tensor(tensor_masked_bank(np.ones_like(Wn), int(tau[m]), L)))
+                for m in range(M)]
+        (torch.cat(rows) * torch.tensor(dYn)).sum().backward()
+        dX, dW = O.row_typed_backward(Xn, Wn, dYn, tau, q, table=O.tensor_power_table(L))
+        np.testing.assert_allclose(dX, X.grad.numpy(), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dW, W.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [
     pin_q2_table, pin_q2_scalar_example, pin_eq3_rectangular_blocks, pin_eq13_14,
     pin_product_counts, pin_graph_counts, pin_appendix_a, pin_associativity,
@@ -594,5 +727,6 @@ ALL_PINS = [
     pin_masked_dense, pin_row_typed_is_square_rows, pin_q1_is_matmul, pin_block_diagonal,
     pin_coverage, pin_vjp_scalar_eq31_35, pin_vjp_autograd, pin_vjp_adjoint,
     pin_mac_count, pin_type_index, pin_type_schedule, pin_silu_values, pin_gated_masked_dense,
-    pin_silu_grad, pin_gated_ffn_autograd,
+    pin_silu_grad, pin_gated_ffn_autograd, pin_tensor_counts, pin_tensor_support,
+    pin_tensor_associativity, pin_tensor_masked_dense, pin_tensor_cost, pin_tensor_vjp_autograd,
 ]

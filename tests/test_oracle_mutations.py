@@ -18,6 +18,7 @@ _real_index = O.type_index
 _real_silu = O.silu
 _real_gated = O.gated_forward
 _real_silu_grad = O.silu_grad
+_real_tensor = O.tensor_power_table
 _real_swiglu_bwd = O.swiglu_backward
 
 
@@ -47,9 +48,9 @@ def table_transposed_weight(q, edges=None):
     return [(x, (w[1], w[0]), z) for (x, w, z) in _real_table(q, edges)]
 
 
-def fwd_sign_flip(X, W, tau, q, in_widths=None, out_widths=None, edges=None):
+def fwd_sign_flip(X, W, tau, q, in_widths=None, out_widths=None, edges=None, table=None):
     """Mistake: subtracts the off-diagonal endpoint product."""
-    Y = _real_fwd(X, W, tau, q, in_widths, out_widths, edges)
+    Y = _real_fwd(X, W, tau, q, in_widths, out_widths, edges, table)
     X = np.asarray(X, float)
     W = np.asarray(W, float)
     kb = O.group_bounds(X.shape[1], q, in_widths)
@@ -64,9 +65,9 @@ def fwd_sign_flip(X, W, tau, q, in_widths=None, out_widths=None, edges=None):
     return Y
 
 
-def bwd_dw_all_rows(X, W, dY, tau, q, in_widths=None, out_widths=None, edges=None):
+def bwd_dw_all_rows(X, W, dY, tau, q, in_widths=None, out_widths=None, edges=None, table=None):
     """Mistake: off-diagonal weight gradients summed over every row, not just type-i rows."""
-    dX, dW = _real_bwd(X, W, dY, tau, q, in_widths, out_widths, edges)
+    dX, dW = _real_bwd(X, W, dY, tau, q, in_widths, out_widths, edges, table)
     X = np.asarray(X, float)
     dY = np.asarray(dY, float)
     kb = O.group_bounds(X.shape[1], q, in_widths)
@@ -78,9 +79,9 @@ def bwd_dw_all_rows(X, W, dY, tau, q, in_widths=None, out_widths=None, edges=Non
     return dX, dW
 
 
-def bwd_dx_drops_eq32(X, W, dY, tau, q, in_widths=None, out_widths=None, edges=None):
+def bwd_dx_drops_eq32(X, W, dY, tau, q, in_widths=None, out_widths=None, edges=None, table=None):
     """Mistake: activation gradient keeps only the source-row terms (drops eq 32)."""
-    dX, dW = _real_bwd(X, W, dY, tau, q, in_widths, out_widths, edges)
+    dX, dW = _real_bwd(X, W, dY, tau, q, in_widths, out_widths, edges, table)
     X = np.asarray(X, float)
     kb = O.group_bounds(X.shape[1], q, in_widths)
     for m in range(X.shape[0]):
@@ -91,18 +92,18 @@ def bwd_dx_drops_eq32(X, W, dY, tau, q, in_widths=None, out_widths=None, edges=N
     return dX, dW
 
 
-def bwd_dx_untransposed(X, W, dY, tau, q, in_widths=None, out_widths=None, edges=None):
+def bwd_dx_untransposed(X, W, dY, tau, q, in_widths=None, out_widths=None, edges=None, table=None):
     """Mistake: multiplies by W_bj instead of its transpose (square blocks, so shapes still fit)."""
     X = np.asarray(X, float)
     W = np.asarray(W, float)
     dY = np.asarray(dY, float)
     kb = O.group_bounds(X.shape[1], q, in_widths)
     nb = O.group_bounds(W.shape[1], q, out_widths)
-    dX, dW = _real_bwd(X, W, dY, tau, q, in_widths, out_widths, edges)
+    dX, dW = _real_bwd(X, W, dY, tau, q, in_widths, out_widths, edges, table)
     dX[:] = 0.0
     for m in range(X.shape[0]):
         i = int(tau[m])
-        for (xa, xb), (wa, wd), (ya, yd) in O.structure_table(q, edges):
+        for (xa, xb), (wa, wd), (ya, yd) in (O.structure_table(q, edges) if table is None else table):
             if xa != i:
                 continue
             blk = W[kb[wa][0]:kb[wa][1], nb[wd][0]:nb[wd][1]]
@@ -169,6 +170,35 @@ def swiglu_bwd_no_up(G, U, dH):
     return dH * _real_silu_grad(G), dH * _real_silu(G)
 
 
+def tensor_msb_lsb_mixed(L):
+    """Mistake: the levels combined with inconsistent bit order for the two factors' slots."""
+    t = _real_tensor(L)
+    if L < 2:
+        return t
+    def swap(v):
+        return ((v & 1) << 1) | ((v >> 1) & 1) if L == 2 else v
+    return [((swap(x[0]), x[1]), (w[0], w[1]), (swap(z[0]), z[1])) for (x, w, z) in t]
+
+
+def tensor_drops_far_terms(L):
+    """Mistake: only one intermediate group per level pair (the Q_q-like {alpha, delta} support)."""
+    return [(x, w, z) for (x, w, z) in _real_tensor(L) if w[0] in (x[0], z[1])]
+
+
+def tensor_edge_edge(L):
+    """Mistake: a level keeps edge * edge (plain block matmul on that level)."""
+    t = list(_real_tensor(L))
+    q = 2 ** L
+    have = {(x, w) for x, w, _ in t}
+    for a in range(q):
+        for b in range(q):
+            for d in range(q):
+                if ((a, b), (b, d)) not in have:
+                    t.append(((a, b), (b, d), (a, d)))
+                    return t
+    return t
+
+
 MUTANTS = [
     ("structure_table", table_with_edge_edge),
     ("structure_table", table_without_right_vertex),
@@ -187,6 +217,9 @@ MUTANTS = [
     ("silu_grad", silu_grad_drops_term),
     ("swiglu_backward", swiglu_bwd_swapped),
     ("swiglu_backward", swiglu_bwd_no_up),
+    ("tensor_power_table", tensor_msb_lsb_mixed),
+    ("tensor_power_table", tensor_drops_far_terms),
+    ("tensor_power_table", tensor_edge_edge),
 ]
 
 
