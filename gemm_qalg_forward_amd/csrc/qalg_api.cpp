@@ -23,7 +23,8 @@ qalg_status hip_status(hipError_t e) { return e == hipSuccess ? QALG_OK : QALG_E
 qalg_status check_shape(int32_t E, int32_t q, int64_t M, int64_t K, int64_t N, int32_t dtype,
                         uint32_t flags) {
   if (dtype != QALG_F32 && dtype != QALG_BF16) return QALG_ERR_DTYPE;
-  if (flags & ~uint32_t(QALG_FLAG_INDEX_READY | QALG_FLAG_FORCE_TILED | QALG_FLAG_FORCE_SMALL_M))
+  if (flags & ~uint32_t(QALG_FLAG_INDEX_READY | QALG_FLAG_FORCE_TILED | QALG_FLAG_FORCE_SMALL_M |
+                       QALG_FLAG_LAW_TENSOR))
     return QALG_ERR_ARG;
   if ((flags & QALG_FLAG_FORCE_TILED) && (flags & QALG_FLAG_FORCE_SMALL_M)) return QALG_ERR_ARG;
   if (E < 1 || M < 0 || K <= 0 || N <= 0) return QALG_ERR_DIM;
@@ -44,6 +45,14 @@ qalg_status check_ws(int32_t E, int32_t q, int64_t M, const void* ws, size_t ws_
 
 int64_t ws_stride_ints(int32_t q, int64_t M) { return qalg::ws_layout(q, M).total_ints; }
 
+// L of the recursive law Q_2^(x)L for q = 2^L, or -1 when q is not a power of two.
+int tensor_levels(int32_t q) {
+  if (q < 1 || (q & (q - 1))) return -1;
+  int L = 0;
+  while ((1 << L) < q) ++L;
+  return L;
+}
+
 
 // Shared driver of qalg_forward / qalg_backward_dx / qalg_backward_dw / batched forward.
 qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const int32_t* tau,
@@ -52,6 +61,13 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
   qalg_status st = check_shape(E, q, M, K, N, dtype, flags);
   if (st != QALG_OK) return st;
   if ((flags & QALG_FLAG_FORCE_SMALL_M) && (op != Op::Fwd || dtype != QALG_BF16)) return QALG_ERR_ARG;
+  const bool tensor = (flags & QALG_FLAG_LAW_TENSOR) != 0;
+  if (tensor) {
+    // the recursive law runs on the persistent forward only
+    if (op != Op::Fwd || E != 1 || dtype != QALG_BF16 || (flags & (QALG_FLAG_FORCE_TILED | QALG_FLAG_FORCE_SMALL_M)))
+      return QALG_ERR_ARG;
+    if (tensor_levels(q) < 0) return QALG_ERR_Q;
+  }
   // with no rows only dW's output is touched (it is zero-filled)
   if (M > 0 && (A == nullptr || B == nullptr || C == nullptr || tau == nullptr)) return QALG_ERR_NULL;
   if (M == 0 && op == Op::Dw && C == nullptr) return QALG_ERR_NULL;
@@ -78,10 +94,25 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
   p.K = K;
   p.N = N;
   p.E = E;
+  p.law_L = tensor ? tensor_levels(q) : 0;
 
   // the workspace contract is the same on every path, used or not
   st = check_ws(E, q, M, ws, ws_bytes);
   if (st != QALG_OK) return st;
+
+  if (p.law_L > 0) {
+    if (!qalg::fwd_persistent_shape_ok(p)) {
+      const int64_t lim = int64_t(1) << 31;
+      return (M * K >= lim || K * N >= lim || M * N >= lim) ? QALG_ERR_DIM : QALG_ERR_ALIGN;
+    }
+    int32_t* wsl = static_cast<int32_t*>(ws);
+    p.ws = wsl;
+    p.ws_stride = ws_stride_ints(q, M);
+    if (!(flags & QALG_FLAG_INDEX_READY)) {
+      if (qalg::launch_build_index(tau, q, M, 1, wsl, p.ws_stride, s) != hipSuccess) return QALG_ERR_HIP;
+    }
+    return hip_status(qalg::launch_fwd_persistent_bf16(p, s));
+  }
 
   // small-M weight-streaming forward: reads the types directly, no index
   const bool small_ok = dtype == QALG_BF16 && qalg::small_m_supported(p);
@@ -231,10 +262,11 @@ qalg_status qalg_gated_forward(const void* X, const void* Wgu, const int32_t* ta
                                int64_t K, int64_t F, void* H, int32_t dtype, void* ws, size_t ws_bytes,
                                uint32_t flags, void* stream) {
   if (dtype != QALG_BF16) return QALG_ERR_DTYPE;
-  if (flags & ~uint32_t(QALG_FLAG_INDEX_READY)) return QALG_ERR_ARG;
+  if (flags & ~uint32_t(QALG_FLAG_INDEX_READY | QALG_FLAG_LAW_TENSOR)) return QALG_ERR_ARG;
   if (M < 0 || K <= 0 || F <= 0 || M > INT32_MAX / 2 || K > INT32_MAX / 2 || F > INT32_MAX / 4)
     return QALG_ERR_DIM;
   if (q < 1 || q > QALG_MAX_Q || K % q || F % q) return QALG_ERR_Q;
+  if ((flags & QALG_FLAG_LAW_TENSOR) && tensor_levels(q) < 0) return QALG_ERR_Q;
   if ((F / q) % 128 || (K / q) % 64) return QALG_ERR_ALIGN;
   if (M == 0) return QALG_OK;
   if (X == nullptr || Wgu == nullptr || tau == nullptr || H == nullptr) return QALG_ERR_NULL;
@@ -253,6 +285,7 @@ qalg_status qalg_gated_forward(const void* X, const void* Wgu, const int32_t* ta
   p.K = K;
   p.N = 2 * F;  // the merged bank's width
   p.E = 1;
+  p.law_L = (flags & QALG_FLAG_LAW_TENSOR) ? tensor_levels(q) : 0;
   if (!qalg::fwd_gated_supported(p)) return QALG_ERR_DIM;
   int32_t* wsi = static_cast<int32_t*>(ws);
   p.ws = wsi;

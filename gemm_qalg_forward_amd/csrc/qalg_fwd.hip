@@ -131,6 +131,7 @@ struct FwdArgs {
   int n_ct;    // column tiles in all (q * cpg)
   int kts;     // k-steps per contraction segment (s / kBK)
   int out_n;   // columns of an output row (N; N / 2 for the gated epilogue)
+  int L;       // 0: the complete-graph law Q_q; L >= 1: the recursive law Q_2^(x)L (q = 2^L)
 };
 
 // One output tile, decoded from its position in the tile order.
@@ -142,6 +143,78 @@ struct Tile {
   int n0;         // first output column
   int seg0, seg1; // K offsets of the contraction segments (group i, group j)
   int nk;         // k-steps
+  int fmask;      // recursive law: bits where i and j differ (free bits of the segments)
+  int fbase;      // recursive law: i's bits elsewhere (segment n is fbase | pdep(n, fmask))
+};
+
+// The recursive law Q_2^(x)L (appendix C): types and groups are L-bit strings,
+// and output group j of a type-i row sums x_b W_bj over every b whose bits each
+// equal i's or j's (eq 36), i.e. b = (i & ~m) | (any subset of m), m = i ^ j:
+// 2^popcount(m) segments.  Tiles fall in L + 1 classes by d = popcount(m), with
+// C(L, d) output groups per type and 2^d segments each.
+__device__ __forceinline__ int binom_small(int L, int d) {
+  int c = 1;
+  for (int k = 0; k < d; ++k) c = c * (L - k) / (k + 1);
+  return c;
+}
+// the jj-th L-bit mask (ascending) with d bits set
+__device__ __forceinline__ int unrank_mask(int jj, int d, int L) {
+  for (int m = 0; m < (1 << L); ++m)
+    if (__builtin_popcount(m) == d && jj-- == 0) return m;
+  return 0;
+}
+// scatter the low bits of n into the set bits of m
+__device__ __forceinline__ int deposit_bits(int n, int m, int L) {
+  int b = 0;
+  for (int k = 0; k < L; ++k)
+    if ((m >> k) & 1) {
+      if (n & 1) b |= 1 << k;
+      n >>= 1;
+    }
+  return b;
+}
+
+// Tile list of a workgroup for the recursive law: each XCD takes a contiguous
+// share of every class; its workgroups are dealt the concatenation of those
+// shares, longest class first, round robin, so k-steps per workgroup end within
+// one tile of each other.
+struct ClassDeal {
+  int L, n_rt, cpg, xcd, nx, g, G, k;
+  __device__ void init(int L_, int n_rt_, int cpg_, int xcd_, int nx_, int slot, int per_x) {
+    L = L_;
+    n_rt = n_rt_;
+    cpg = cpg_;
+    xcd = xcd_;
+    nx = nx_;
+    g = slot;
+    G = per_x;
+    k = 0;
+  }
+  __device__ bool next(int* cls, int* idx) {
+    int p = uni(g + k * G);
+    k = uni(k + 1);
+    for (int d = L; d >= 0; --d) {
+      const int T = n_rt * binom_small(L, d) * cpg;
+      const int x0 = T * xcd / nx, x1 = T * (xcd + 1) / nx;
+      if (p < x1 - x0) {
+        *cls = d;
+        *idx = x0 + p;
+        return true;
+      }
+      p -= x1 - x0;
+    }
+    return false;
+  }
+};
+
+// the two-class deal of the complete law, with the class as an int (1: long)
+struct TileDeal2 : TileDeal {
+  __device__ bool next(int* cls, int* idx) {
+    bool lg;
+    const bool ok = TileDeal::next(&lg, idx);
+    *cls = lg ? 1 : 0;
+    return ok;
+  }
 };
 
 // Tiles come in two lengths: "long" tiles (output group j != row type i, two
@@ -149,10 +222,14 @@ struct Tile {
 // ordered in groups of up to 4 row tiles x the class's column tiles, row tile
 // fastest (measured against 2, 8 and 16 row tiles: the least L2 refetch for
 // 256x256 tiles); idx is the tile's position in its class.
-template <class C, class IX>
-__device__ __forceinline__ Tile decode_tile(const FwdArgs& a, const IX& ix, int n_rt, bool is_long, int idx) {
+// Complete law: cls 1 is the long class, 0 the short one.  Recursive law: cls
+// is d, the Hamming distance between row type and output group.
+template <class C, bool TENSOR, class IX>
+__device__ __forceinline__ Tile decode_tile(const FwdArgs& a, const IX& ix, int n_rt, int cls, int idx) {
   constexpr int G = 4;
-  const int ncol = is_long ? (a.q - 1) * a.cpg : a.cpg;  // column tiles of the class per row tile
+  const bool is_long = cls != 0;
+  const int ngrp = TENSOR ? binom_small(a.L, cls) : (is_long ? a.q - 1 : 1);
+  const int ncol = ngrp * a.cpg;  // column tiles of the class per row tile
   const int span = G * ncol;
   const int g = idx / span;
   const int first_rt = g * G;
@@ -162,26 +239,40 @@ __device__ __forceinline__ Tile decode_tile(const FwdArgs& a, const IX& ix, int 
   const int c2 = w / gm;
   const int i = ix.group_of_tile(rt);
   int ct;
-  if (is_long) {
+  Tile t;
+  if constexpr (TENSOR) {
+    const int jj = c2 / a.cpg, cc = c2 - jj * a.cpg;
+    const int m = unrank_mask(jj, cls, a.L);
+    ct = (i ^ m) * a.cpg + cc;
+    t.fmask = m;
+    t.fbase = i & ~m;
+  } else if (is_long) {
     const int jj = c2 / a.cpg, cc = c2 - jj * a.cpg;
     ct = (jj < i ? jj : jj + 1) * a.cpg + cc;  // output groups other than i
+    t.fmask = t.fbase = 0;
   } else {
     ct = i * a.cpg + c2;
+    t.fmask = t.fbase = 0;
   }
-  Tile t;
   t.i = i;
   t.rank0 = (rt - ix.tiles_before(i)) * C::BM;
   t.first = ix.offset(i) + t.rank0;
   t.m_cnt = min(C::BM, ix.count(i) - t.rank0);
   const int j = ct / a.cpg, cc = ct - j * a.cpg;
   t.n0 = j * a.r + cc * C::BN;
-  t.seg0 = i * a.s;
-  t.seg1 = j * a.s;
-  t.nk = uni((j == i) ? a.kts : 2 * a.kts);
+  if constexpr (TENSOR) {
+    t.seg0 = t.fbase * a.s;  // segment 0: no free bit set
+    t.seg1 = 0;
+    t.nk = uni(a.kts << cls);
+  } else {
+    t.seg0 = i * a.s;
+    t.seg1 = j * a.s;
+    t.nk = uni((j == i) ? a.kts : 2 * a.kts);
+  }
   return t;
 }
 
-template <class C, bool CYC>
+template <class C, bool CYC, bool TENSOR>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   constexpr int BM = C::BM, T = C::THREADS;
   const int32_t* ws = a.ws;
@@ -223,10 +314,14 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   const int per_x = gridDim.x / nx;
   const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx;
   if (slot >= per_x) return;  // grid not a multiple of 8: the remainder idles
-  TileDeal dcopy, dcomp;
-  dcopy.init(n_long, n_short, 2 * a.kts, a.kts, xcd, nx, slot, per_x);
+  using Deal = std::conditional_t<TENSOR, ClassDeal, TileDeal2>;
+  Deal dcopy, dcomp;
+  if constexpr (TENSOR)
+    dcopy.init(a.L, n_rt, a.cpg, xcd, nx, slot, per_x);
+  else
+    dcopy.init(n_long, n_short, 2 * a.kts, a.kts, xcd, nx, slot, per_x);
   dcomp = dcopy;
-  bool l_long;
+  int l_long;  // class of the copy cursor's next tile
   int l_idx;
   if (!dcopy.next(&l_long, &l_idx)) return;
 
@@ -277,19 +372,26 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
 
   // copy cursor: tile lt at k-step lk; the tile after it is decoded ahead so
   // that a listed schedule's row ids are fetched a whole tile before use
-  Tile lt = decode_tile<C>(a, ix, n_rt, l_long, uni(l_idx));
+  Tile lt = decode_tile<C, TENSOR>(a, ix, n_rt, l_long, uni(l_idx));
   int lk = 0;
   bool have_next = dcopy.next(&l_long, &l_idx);
-  Tile nt = have_next ? decode_tile<C>(a, ix, n_rt, l_long, uni(l_idx)) : lt;
+  Tile nt = have_next ? decode_tile<C, TENSOR>(a, ix, n_rt, l_long, uni(l_idx)) : lt;
   prefetch_rows(lt);
   take_rows();
   if (have_next) prefetch_rows(nt);
   bool more = true;  // the copy cursor has not passed the last k-step
   // copy cursor split in three so that the copies can be interleaved with MFMAs
   uint32_t cp_x = 0, cp_w = 0;  // per-step byte offsets of the X and W pieces
+  // recursive law: k-step within the current segment, segment number, its K offset
+  int lks = 0, lseg = 0, lcol = lt.seg0;
   auto prep_copies = [&]() {
-    const int sg = lk >= a.kts ? 1 : 0;
-    const int kcol = (sg ? lt.seg1 : lt.seg0) + (lk - sg * a.kts) * kBK;
+    int kcol;
+    if constexpr (TENSOR) {
+      kcol = lcol + lks * kBK;
+    } else {
+      const int sg = lk >= a.kts ? 1 : 0;
+      kcol = (sg ? lt.seg1 : lt.seg0) + (lk - sg * a.kts) * kBK;
+    }
     cp_x = uint32_t(kcol) * 2u;
     cp_w = uint32_t(kcol) * n_bytes + uint32_t(lt.n0) * 2u;
   };
@@ -304,6 +406,36 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   // k-steps past the end repeat it into a stage that is never read, so
   // that the pipeline needs no conditions (they are drained before exit).
   auto advance_copies = [&]() {
+    if constexpr (TENSOR) {
+      if (!more) return;
+      if (uni(lk + 1) < lt.nk) {
+        lk = uni(lk + 1);
+        if (uni(lks + 1) == a.kts) {
+          lks = 0;
+          lseg = uni(lseg + 1);
+          lcol = uni((lt.fbase | deposit_bits(lseg, lt.fmask, a.L)) * a.s);
+        } else {
+          lks = uni(lks + 1);
+        }
+        return;
+      }
+      if (!have_next) {
+        more = false;  // the cursor stays on the last k-step
+        return;
+      }
+      lt = nt;
+      lk = 0;
+      lks = 0;
+      lseg = 0;
+      lcol = lt.seg0;
+      take_rows();
+      have_next = dcopy.next(&l_long, &l_idx);
+      if (have_next) {
+        nt = decode_tile<C, TENSOR>(a, ix, n_rt, l_long, uni(l_idx));
+        prefetch_rows(nt);
+      }
+      return;
+    }
     if (more && (lk = uni(lk + 1)) >= lt.nk) {
       if (!have_next) {
         more = false;
@@ -314,7 +446,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
         take_rows();
         have_next = dcopy.next(&l_long, &l_idx);
         if (have_next) {
-          nt = decode_tile<C>(a, ix, n_rt, l_long, uni(l_idx));
+          nt = decode_tile<C, TENSOR>(a, ix, n_rt, l_long, uni(l_idx));
           prefetch_rows(nt);
         }
       }
@@ -411,10 +543,10 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   lds_barrier();
   load_frags(0, 0, fa0, fb0);
 
-  bool c_long;
+  int c_long;
   int c_idx;
   dcomp.next(&c_long, &c_idx);
-  Tile ct = decode_tile<C>(a, ix, n_rt, c_long, uni(c_idx));
+  Tile ct = decode_tile<C, TENSOR>(a, ix, n_rt, c_long, uni(c_idx));
   int stage = 0;  // LDS stage of the current k-step (k-step mod 2)
   static_assert(C::FM + C::FN <= C::FM * C::FN, "fragment reads fit a quarter step");
   // one quarter step: MFMAs on fragments (fa, fb) of quarter ks, each followed
@@ -534,14 +666,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
       }
     }
     if (!dcomp.next(&c_long, &c_idx)) break;
-    ct = decode_tile<C>(a, ix, n_rt, c_long, uni(c_idx));
+    ct = decode_tile<C, TENSOR>(a, ix, n_rt, c_long, uni(c_idx));
   }
   // the repeated copies past the last k-step land in LDS: drain them before
   // the workgroup's LDS can be handed to another workgroup
   wait_vmcnt<0>();
 }
 
-template <class C>
+// one kernel per law: the recursive law's cursor state stays out of the
+// complete law's register allocation
+template <class C, bool TENSOR>
 __global__ __launch_bounds__(C::THREADS, 1) void fwd_persistent_kernel(FwdArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int32_t* ws = a.ws;
@@ -549,9 +683,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void fwd_persistent_kernel(FwdArgs a
   // two instantiations: the cyclic one never reads the row list, so it has no
   // global loads for the compiler to wait on inside the pipeline
   if (ws[4] >= 0)
-    fwd_body<C, true>(a, smem);
+    fwd_body<C, true, TENSOR>(a, smem);
   else
-    fwd_body<C, false>(a, smem);
+    fwd_body<C, false, TENSOR>(a, smem);
 }
 
 using Fwd256x256 = FwdCfg<256, 256>;
@@ -570,16 +704,23 @@ int cu_count() {
   return n;
 }
 
-template <class C>
-hipError_t launch_fwd(const ProblemDesc& p, hipStream_t s) {
+template <class C, bool TENSOR>
+hipError_t set_lds_limit() {
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_persistent_kernel<C>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             C::LDS_BYTES);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_persistent_kernel<C, TENSOR>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  return hipSuccess;
+}
+
+template <class C>
+hipError_t launch_fwd(const ProblemDesc& p, hipStream_t s) {
+  const bool tensor = p.law_L > 0;
+  const hipError_t e = tensor ? set_lds_limit<C, true>() : set_lds_limit<C, false>();
+  if (e != hipSuccess) return e;
   FwdArgs a{};
   a.X = static_cast<const char*>(p.A);
   a.W = static_cast<const char*>(p.B);
@@ -597,6 +738,7 @@ hipError_t launch_fwd(const ProblemDesc& p, hipStream_t s) {
   a.r = int(p.N / p.q);
   a.kts = a.s / kBK;
   a.out_n = C::GATED ? a.N / 2 : a.N;
+  a.L = p.law_L;
   a.cpg = a.r / C::BN;
   a.n_ct = p.q * a.cpg;
   const int64_t max_tiles = ((p.M + C::BM - 1) / C::BM + p.q - 1) * int64_t(a.n_ct);
@@ -604,21 +746,28 @@ hipError_t launch_fwd(const ProblemDesc& p, hipStream_t s) {
   if (max_tiles < grid) grid = max_tiles < 8 ? int(max_tiles) : int(max_tiles / 8 * 8);
   if (grid < 1) grid = 1;
   const size_t lds = C::LDS_BYTES;
-  hipLaunchKernelGGL((fwd_persistent_kernel<C>), dim3(grid), dim3(C::THREADS), lds, s, a);
+  if (tensor)
+    hipLaunchKernelGGL((fwd_persistent_kernel<C, true>), dim3(grid), dim3(C::THREADS), lds, s, a);
+  else
+    hipLaunchKernelGGL((fwd_persistent_kernel<C, false>), dim3(grid), dim3(C::THREADS), lds, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool fwd_persistent_supported(const ProblemDesc& p) {
+bool fwd_persistent_shape_ok(const ProblemDesc& p) {
   if (p.op != Op::Fwd || p.E != 1) return false;
   const int64_t s = p.K / p.q, r = p.N / p.q;
   // byte offsets of every operand fit in 32 bits
   const int64_t lim = int64_t(1) << 31;
   if (p.M * p.K >= lim || p.K * p.N >= lim || p.M * p.N >= lim) return false;
   if (s % kBK != 0) return false;
-  if (r % 256 != 0 && r % 192 != 0 && r % 128 != 0) return false;
-  return (p.M + p.q - 1) / p.q >= 128;  // rows per type (cyclic estimate)
+  return r % 256 == 0 || r % 192 == 0 || r % 128 == 0;
+}
+
+bool fwd_persistent_supported(const ProblemDesc& p) {
+  // below about 128 rows per type the register-staged kernel's 128-row tiles waste less
+  return fwd_persistent_shape_ok(p) && (p.M + p.q - 1) / p.q >= 128;
 }
 
 // Gated: N is the merged bank's width 2F.  Output group j's 2r merged columns

@@ -75,6 +75,7 @@ struct ProblemDesc {
   int q;
   int64_t M, K, N;
   int E;              // problems (experts); operands packed back to back
+  int law_L = 0;      // 0: the complete-graph law Q_q; L >= 1: the recursive law Q_2^(x)L, q = 2^L
 };
 
 // skip_cyclic: the kernel returns at once when the index says the schedule is
@@ -85,6 +86,8 @@ hipError_t launch_small_m_bf16(const ProblemDesc& p, hipStream_t s);
 bool small_m_supported(const ProblemDesc& p);
 // Persistent 256x256-tile forward (bf16, one problem); zeroes rows of out-of-range type itself.
 bool fwd_persistent_supported(const ProblemDesc& p);
+// the shapes the persistent forward can run at all (the only path of the recursive law)
+bool fwd_persistent_shape_ok(const ProblemDesc& p);
 hipError_t launch_fwd_persistent_bf16(const ProblemDesc& p, hipStream_t s);
 // Gated (SwiGLU gate/up) forward over a merged bank; p.N is the merged width 2F.
 bool fwd_gated_supported(const ProblemDesc& p);

@@ -86,7 +86,20 @@ enum {
     /* Force the tiled matrix-core path even for small M (testing). */
     QALG_FLAG_FORCE_TILED = 2,
     /* Force the small-M weight-streaming path (bf16 forward only; testing). */
-    QALG_FLAG_FORCE_SMALL_M = 4
+    QALG_FLAG_FORCE_SMALL_M = 4,
+    /* Use the recursive law Q_2^(x)L of appendix C instead of Q_q (the law of
+     * the paper's pretraining pilot): q = 2^L types and feature groups are
+     * L-bit strings (bit L-1, the most significant, is the first level of
+     * the recursion) and output group j of a type-i row sums x_b W_bj over
+     * every group b whose bits each equal i's or j's (eq 36; section 6.1's
+     * B(i, j) for this law), 2^popcount(i xor j) terms; (3/4)^L of the
+     * dense MACs with equal groups.  q must be a power of two
+     * (QALG_ERR_Q); q = 2 is Q_2 itself and q = 1 the plain product.
+     * Accepted by qalg_forward and qalg_gated_forward, bf16, on shapes whose
+     * K / q is a multiple of 64 and N / q of 128 (QALG_ERR_ALIGN otherwise;
+     * byte offsets below 2^31, QALG_ERR_DIM); other entry points return
+     * QALG_ERR_ARG. */
+    QALG_FLAG_LAW_TENSOR = 8
 };
 
 /* Position-type schedules for qalg_type_schedule. */
@@ -203,7 +216,7 @@ qalg_status qalg_forward_batched(int32_t E, const void* X, const void* W, const 
  * (overwritten; rows of an out-of-range type are written as zero).
  * Requires F / q to be a multiple of 128 and K / q a multiple of 64
  * (QALG_ERR_ALIGN otherwise), and M*K, K*2F, M*2F below 2^31 (QALG_ERR_DIM).
- * Flags: QALG_FLAG_INDEX_READY only.
+ * Flags: QALG_FLAG_INDEX_READY and QALG_FLAG_LAW_TENSOR.
  */
 qalg_status qalg_gated_forward(const void* X, const void* Wgu, const int32_t* tau, int32_t q,
                                int64_t M, int64_t K, int64_t F, void* H,

@@ -182,3 +182,22 @@ def test_swiglu_argument_errors_are_synchronous(lib):
     assert fw(H=None) == 1
     assert bw(dH=None) == 1
     assert bw(dGU=FAKE + 4) == 4
+
+
+def test_tensor_law_flag_errors_are_synchronous(lib):
+    T = Q.QALG_FLAG_LAW_TENSOR
+    fwd = lambda **k: lib.qalg_forward(FAKE, FAKE, FAKE, k.get("q", 4), k.get("M", 64), k.get("K", 256),  # noqa: E731
+                                       k.get("N", 512), FAKE, k.get("dt", 1), FAKE, 1 << 20, k.get("flags", T), None)
+    assert fwd(q=3, K=192, N=384) == 3            # not a power of two
+    assert fwd(q=6, K=384, N=768) == 3
+    assert fwd(dt=0) == 8                          # bf16 only
+    assert fwd(flags=T | Q.QALG_FLAG_FORCE_TILED) == 8
+    assert fwd(flags=T | Q.QALG_FLAG_FORCE_SMALL_M) == 8
+    assert fwd(K=128) == 4                         # K / q = 32: not a multiple of 64
+    assert fwd(N=320) == 4                         # N / q = 80: no tile width divides it
+    assert fwd(flags=16) == 8                      # unknown flag
+    dx = lib.qalg_backward_dx(FAKE, FAKE, FAKE, 4, 64, 256, 512, FAKE, 1, FAKE, 1 << 20, T, None)
+    dw = lib.qalg_backward_dw(FAKE, FAKE, FAKE, 4, 64, 256, 512, FAKE, 1, FAKE, 1 << 20, T, None)
+    bt = lib.qalg_forward_batched(2, FAKE, FAKE, FAKE, 4, 64, 256, 512, FAKE, 1, FAKE, 1 << 20, T, None)
+    assert dx == dw == bt == 8                     # the recursive law runs on the forward only
+    assert call_gated(lib, q=3, K=192, F=384, flags=T) == 3
