@@ -20,7 +20,8 @@ import pathlib
 __all__ = [
     "QalgError", "lib", "lib_path",
     "QALG_F32", "QALG_BF16", "QALG_FLAG_INDEX_READY", "QALG_FLAG_FORCE_TILED",
-    "QALG_FLAG_FORCE_SMALL_M", "QALG_FLAG_LAW_TENSOR", "QALG_SCHEDULE_CYCLIC", "QALG_SCHEDULE_INTERVAL", "QALG_MAX_Q",
+    "QALG_FLAG_FORCE_SMALL_M", "QALG_FLAG_LAW_TENSOR",
+    "QALG_FLAG_TILE_M64", "QALG_FLAG_TILE_M128", "QALG_FLAG_TILE_M256", "QALG_SCHEDULE_CYCLIC", "QALG_SCHEDULE_INTERVAL", "QALG_MAX_Q",
     "qalg_version", "qalg_status_string", "qalg_workspace_bytes", "qalg_index_layout",
     "qalg_type_schedule", "qalg_build_index", "qalg_build_index_batched",
     "qalg_forward", "qalg_backward_dx", "qalg_backward_dw", "qalg_forward_batched",
@@ -34,6 +35,9 @@ QALG_FLAG_INDEX_READY = 1
 QALG_FLAG_FORCE_TILED = 2
 QALG_FLAG_FORCE_SMALL_M = 4
 QALG_FLAG_LAW_TENSOR = 8
+QALG_FLAG_TILE_M64 = 16
+QALG_FLAG_TILE_M128 = 32
+QALG_FLAG_TILE_M256 = 64
 QALG_SCHEDULE_CYCLIC = 0
 QALG_SCHEDULE_INTERVAL = 1
 QALG_MAX_Q = 512

@@ -19,12 +19,24 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 qalg_status hip_status(hipError_t e) { return e == hipSuccess ? QALG_OK : QALG_ERR_HIP; }
 
+constexpr uint32_t kTileFlags = QALG_FLAG_TILE_M64 | QALG_FLAG_TILE_M128 | QALG_FLAG_TILE_M256;
+
+// forced tile height of the persistent forward: 0 (none), 64, 128, 256, or -1 (several flags)
+int forced_tile_height(uint32_t flags) {
+  const uint32_t t = flags & kTileFlags;
+  if (t == 0) return 0;
+  if (t == QALG_FLAG_TILE_M64) return 64;
+  if (t == QALG_FLAG_TILE_M128) return 128;
+  if (t == QALG_FLAG_TILE_M256) return 256;
+  return -1;
+}
+
 // Shape, type and flag checks shared by the projection entry points.
 qalg_status check_shape(int32_t E, int32_t q, int64_t M, int64_t K, int64_t N, int32_t dtype,
                         uint32_t flags) {
   if (dtype != QALG_F32 && dtype != QALG_BF16) return QALG_ERR_DTYPE;
   if (flags & ~uint32_t(QALG_FLAG_INDEX_READY | QALG_FLAG_FORCE_TILED | QALG_FLAG_FORCE_SMALL_M |
-                       QALG_FLAG_LAW_TENSOR))
+                       QALG_FLAG_LAW_TENSOR | kTileFlags))
     return QALG_ERR_ARG;
   if ((flags & QALG_FLAG_FORCE_TILED) && (flags & QALG_FLAG_FORCE_SMALL_M)) return QALG_ERR_ARG;
   if (E < 1 || M < 0 || K <= 0 || N <= 0) return QALG_ERR_DIM;
@@ -61,6 +73,12 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
   qalg_status st = check_shape(E, q, M, K, N, dtype, flags);
   if (st != QALG_OK) return st;
   if ((flags & QALG_FLAG_FORCE_SMALL_M) && (op != Op::Fwd || dtype != QALG_BF16)) return QALG_ERR_ARG;
+  const int forced_bm = forced_tile_height(flags);
+  if (forced_bm != 0) {
+    if (forced_bm < 0 || op != Op::Fwd || E != 1 || dtype != QALG_BF16 ||
+        (flags & (QALG_FLAG_FORCE_TILED | QALG_FLAG_FORCE_SMALL_M)))
+      return QALG_ERR_ARG;
+  }
   const bool tensor = (flags & QALG_FLAG_LAW_TENSOR) != 0;
   if (tensor) {
     // the recursive law runs on the persistent forward only
@@ -100,18 +118,20 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
   st = check_ws(E, q, M, ws, ws_bytes);
   if (st != QALG_OK) return st;
 
-  if (p.law_L > 0) {
+  if (p.law_L > 0 || forced_bm != 0) {
     if (!qalg::fwd_persistent_shape_ok(p)) {
       const int64_t lim = int64_t(1) << 31;
-      return (M * K >= lim || K * N >= lim || M * N >= lim) ? QALG_ERR_DIM : QALG_ERR_ALIGN;
+      if (M * K >= lim || K * N >= lim || M * N >= lim) return QALG_ERR_DIM;
+      return forced_bm ? QALG_ERR_ARG : QALG_ERR_ALIGN;
     }
+    if (forced_bm != 0 && qalg::fwd_tile_height(p, forced_bm) == 0) return QALG_ERR_ARG;
     int32_t* wsl = static_cast<int32_t*>(ws);
     p.ws = wsl;
     p.ws_stride = ws_stride_ints(q, M);
     if (!(flags & QALG_FLAG_INDEX_READY)) {
       if (qalg::launch_build_index(tau, q, M, 1, wsl, p.ws_stride, s) != hipSuccess) return QALG_ERR_HIP;
     }
-    return hip_status(qalg::launch_fwd_persistent_bf16(p, s));
+    return hip_status(qalg::launch_fwd_persistent_bf16(p, s, forced_bm));
   }
 
   // small-M weight-streaming forward: reads the types directly, no index
@@ -127,7 +147,7 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
   p.ws_stride = stride;
 
   hipError_t e;
-  if (dtype == QALG_BF16 && qalg::fwd_persistent_supported(p)) {
+  if (dtype == QALG_BF16 && !(flags & QALG_FLAG_FORCE_TILED) && qalg::fwd_persistent_supported(p)) {
     // the persistent forward zeroes the rows of an out-of-range type itself
     if (!(flags & QALG_FLAG_INDEX_READY)) {
       e = qalg::launch_build_index(tau, q, M, E, wsi, stride, s);

@@ -84,9 +84,12 @@ constexpr int kQ = kBK / 16;  // MFMA quarter steps per k-step
 // GATED: the gate/up half of a gated FFN over a merged weight bank (see the
 // gated entry point below): each wave's 128 accumulator columns are 64 gate
 // and the matching 64 up columns, and the epilogue writes silu(gate) * up.
-template <int BM_, int BN_, bool GATED_ = false>
+// WGM x WGN waves per workgroup; the low tile heights (for few rows per type)
+// use 1 x 4 or 2 x 2 so that every wave still has at least 2 x 2 MFMA blocks.
+template <int BM_, int BN_, bool GATED_ = false, int WGM_ = 2, int WGN_ = 2>
 struct FwdCfg {
-  static constexpr int BM = BM_, BN = BN_, WGM = 2, WGN = 2;
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static_assert(WGM * WGN == 4, "four waves");
   static constexpr bool GATED = GATED_;
   static constexpr int THREADS = 256;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -692,6 +695,10 @@ using Fwd256x256 = FwdCfg<256, 256>;
 using Fwd256x256Gated = FwdCfg<256, 256, true>;
 using Fwd256x192 = FwdCfg<256, 192>;
 using Fwd256x128 = FwdCfg<256, 128>;
+// few rows per type: 128- and 64-row tiles (64 x 64 and 64 x 128 wave tiles)
+using Fwd128x256 = FwdCfg<128, 256>;
+using Fwd128x128 = FwdCfg<128, 128>;
+using Fwd64x256 = FwdCfg<64, 256, false, 1, 4>;
 
 int cu_count() {
   static int n = 0;
@@ -766,8 +773,10 @@ bool fwd_persistent_shape_ok(const ProblemDesc& p) {
 }
 
 bool fwd_persistent_supported(const ProblemDesc& p) {
-  // below about 128 rows per type the register-staged kernel's 128-row tiles waste less
-  return fwd_persistent_shape_ok(p) && (p.M + p.q - 1) / p.q >= 128;
+  // with only 256-row tiles available, below about 128 rows per type the
+  // register-staged kernel's 128-row tiles waste less
+  if (!fwd_persistent_shape_ok(p)) return false;
+  return fwd_tile_height(p, 0) < 256 || (p.M + p.q - 1) / p.q >= 128;
 }
 
 // Gated: N is the merged bank's width 2F.  Output group j's 2r merged columns
@@ -818,8 +827,46 @@ hipError_t launch_merge_gate_up_bf16(const void* Wg, const void* Wu, void* Wgu, 
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_persistent_bf16(const ProblemDesc& p, hipStream_t s) {
+// Tile height from a cost model calibrated with the sweep of calibrate.py on
+// 4096 <-> 12288 at M = 2048 .. 16384, q = 8 .. 64: (waves of tiles over the
+// CUs) x (tile area) / (relative per-area efficiency of the height: 1, 0.85
+// and 0.6 for 256, 128 and 64 rows).  Few rows per type favour low tiles (a
+// 256-row tile of a 64-row type is 3/4 padding); few tiles in all favour low
+// tiles too (more workgroups busy); many rows favour the most efficient tile.
+int fwd_tile_height(const ProblemDesc& p, int forced) {
   const int64_t r = p.N / p.q;
+  const bool ok64 = r % 256 == 0, ok128 = r % 128 == 0;
+  if (forced) {
+    if (forced == 256) return 256;
+    if (forced == 128 && ok128) return 128;
+    if (forced == 64 && ok64) return 64;
+    return 0;
+  }
+  const int64_t rows = (p.M + p.q - 1) / p.q;  // per type (cyclic estimate)
+  const int64_t cus = cu_count();
+  auto cost = [&](int bm, int bn, double eff) {
+    const int64_t tiles = int64_t(p.q) * ((rows + bm - 1) / bm) * (p.N / bn);
+    return double((tiles + cus - 1) / cus) * bm * bn / eff;
+  };
+  int best = 256;
+  double c_best = cost(256, r % 256 == 0 ? 256 : (r % 192 == 0 ? 192 : 128), 1.0);
+  if (ok128) {
+    const double c = cost(128, ok64 ? 256 : 128, 0.85);
+    if (c < c_best) best = 128, c_best = c;
+  }
+  if (ok64) {
+    const double c = cost(64, 256, 0.6);
+    if (c < c_best) best = 64, c_best = c;
+  }
+  return best;
+}
+
+hipError_t launch_fwd_persistent_bf16(const ProblemDesc& p, hipStream_t s, int forced_bm) {
+  const int64_t r = p.N / p.q;
+  const int bm = fwd_tile_height(p, forced_bm);
+  if (bm == 64) return launch_fwd<Fwd64x256>(p, s);
+  if (bm == 128) return r % 256 == 0 ? launch_fwd<Fwd128x256>(p, s) : launch_fwd<Fwd128x128>(p, s);
+  if (bm != 256) return hipErrorInvalidValue;
   if (r % 256 == 0) return launch_fwd<Fwd256x256>(p, s);
   if (r % 192 == 0) return launch_fwd<Fwd256x192>(p, s);
   return launch_fwd<Fwd256x128>(p, s);

@@ -88,7 +88,10 @@ bool small_m_supported(const ProblemDesc& p);
 bool fwd_persistent_supported(const ProblemDesc& p);
 // the shapes the persistent forward can run at all (the only path of the recursive law)
 bool fwd_persistent_shape_ok(const ProblemDesc& p);
-hipError_t launch_fwd_persistent_bf16(const ProblemDesc& p, hipStream_t s);
+// forced_bm: 0 picks the tile height from the rows per type; 256, 128 or 64 forces it
+hipError_t launch_fwd_persistent_bf16(const ProblemDesc& p, hipStream_t s, int forced_bm = 0);
+// tile height the persistent forward uses (forced_bm as above); 0 if the forced one cannot run
+int fwd_tile_height(const ProblemDesc& p, int forced_bm);
 // Gated (SwiGLU gate/up) forward over a merged bank; p.N is the merged width 2F.
 bool fwd_gated_supported(const ProblemDesc& p);
 hipError_t launch_fwd_gated_bf16(const ProblemDesc& p, hipStream_t s);

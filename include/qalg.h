@@ -83,7 +83,8 @@ enum {
      * qalg_build_index or by an earlier call on the same stream: skip
      * rebuilding it.  Lets forward, dX and dW of one step share one index. */
     QALG_FLAG_INDEX_READY = 1,
-    /* Force the tiled matrix-core path even for small M (testing). */
+    /* Force the register-staged tiled matrix-core kernels (neither the
+     * small-M path nor the persistent forward; testing and calibration). */
     QALG_FLAG_FORCE_TILED = 2,
     /* Force the small-M weight-streaming path (bf16 forward only; testing). */
     QALG_FLAG_FORCE_SMALL_M = 4,
@@ -99,7 +100,15 @@ enum {
      * K / q is a multiple of 64 and N / q of 128 (QALG_ERR_ALIGN otherwise;
      * byte offsets below 2^31, QALG_ERR_DIM); other entry points return
      * QALG_ERR_ARG. */
-    QALG_FLAG_LAW_TENSOR = 8
+    QALG_FLAG_LAW_TENSOR = 8,
+    /* Tile calibration (qalg_forward, bf16, one bank): run the persistent
+     * forward with 64-, 128- or 256-row output tiles instead of the height
+     * chosen from the rows per type (at most one; QALG_ERR_ARG if the shape
+     * cannot use it: 64 needs N / q a multiple of 256, 128 a multiple of 128,
+     * and every persistent shape K / q a multiple of 64). */
+    QALG_FLAG_TILE_M64 = 16,
+    QALG_FLAG_TILE_M128 = 32,
+    QALG_FLAG_TILE_M256 = 64
 };
 
 /* Position-type schedules for qalg_type_schedule. */

@@ -195,9 +195,23 @@ def test_tensor_law_flag_errors_are_synchronous(lib):
     assert fwd(flags=T | Q.QALG_FLAG_FORCE_SMALL_M) == 8
     assert fwd(K=128) == 4                         # K / q = 32: not a multiple of 64
     assert fwd(N=320) == 4                         # N / q = 80: no tile width divides it
-    assert fwd(flags=16) == 8                      # unknown flag
+    assert fwd(flags=128) == 8                     # unknown flag
     dx = lib.qalg_backward_dx(FAKE, FAKE, FAKE, 4, 64, 256, 512, FAKE, 1, FAKE, 1 << 20, T, None)
     dw = lib.qalg_backward_dw(FAKE, FAKE, FAKE, 4, 64, 256, 512, FAKE, 1, FAKE, 1 << 20, T, None)
     bt = lib.qalg_forward_batched(2, FAKE, FAKE, FAKE, 4, 64, 256, 512, FAKE, 1, FAKE, 1 << 20, T, None)
     assert dx == dw == bt == 8                     # the recursive law runs on the forward only
     assert call_gated(lib, q=3, K=192, F=384, flags=T) == 3
+
+
+def test_tile_flags_errors_are_synchronous(lib):
+    fwd = lambda **k: lib.qalg_forward(FAKE, FAKE, FAKE, k.get("q", 4), k.get("M", 64), k.get("K", 256),  # noqa: E731
+                                       k.get("N", 1024), FAKE, k.get("dt", 1), FAKE, 1 << 20, k.get("flags", 0), None)
+    assert fwd(flags=Q.QALG_FLAG_TILE_M64 | Q.QALG_FLAG_TILE_M128) == 8    # one height at most
+    assert fwd(flags=Q.QALG_FLAG_TILE_M64, dt=0) == 8                      # bf16 only
+    assert fwd(flags=Q.QALG_FLAG_TILE_M64 | Q.QALG_FLAG_FORCE_TILED) == 8
+    assert fwd(flags=Q.QALG_FLAG_TILE_M64, N=512) == 8                     # N / q = 128: no 64-row tiles
+    assert fwd(flags=Q.QALG_FLAG_TILE_M128, N=640) == 8                    # N / q = 160
+    assert fwd(flags=Q.QALG_FLAG_TILE_M256, K=128) == 8                    # K / q = 32
+    dx = lib.qalg_backward_dx(FAKE, FAKE, FAKE, 4, 64, 256, 1024, FAKE, 1, FAKE, 1 << 20, Q.QALG_FLAG_TILE_M64, None)
+    assert dx == 8
+    assert fwd(flags=Q.QALG_FLAG_TILE_M64, M=0) == 0                       # no rows: nothing to do
