@@ -171,6 +171,8 @@ def main() -> int:
         extra["training"] = training_leg(Q, torch, np, synth, dev, stream)
         extra["decode"] = decode_leg(Q, torch, np, synth, dev, stream)
         extra["gated_ffn"] = gated_leg(Q, torch, np, synth, dev, stream)
+        extra["pilot_ffn"] = pilot_leg(Q, torch, np, synth, dev, stream)
+        extra["few_rows"] = few_rows_leg(Q, torch, np, synth, dev, stream)
 
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib << 20
@@ -369,6 +371,88 @@ def gated_train(Q, torch, np, synth, dev, stream, Xd, Wgu, Wdd, tau, ws, H, Y, f
     out["step_tflops"] = round(9 * flop / (step * 1e-3) / 1e12, 1)  # 9 projection-shaped products
     out["swiglu_fwd_GBs"] = round(6.0 * M * F / (ms["swiglu_fwd"] * 1e-3) / 1e9, 1)   # gate, up in; H out
     out["swiglu_bwd_GBs"] = round(10.0 * M * F / (ms["swiglu_bwd"] * 1e-3) / 1e9, 1)  # gate, up, dH in; 2 out
+    return out
+
+
+def pilot_leg(Q, torch, np, synth, dev, stream):
+    """The pretraining pilot's FFN law (appendix D): Q_2^(x)2 on a bias-free SwiGLU FFN, D = 768,
+    F = 1536, one 40 x 1536-position batch (M = 61440), the interval schedule floor((p mod 768) / 192).
+    Timed: fused gate/up + down forwards under the recursive law, under Q_4 and at q = 1 (dense)."""
+    c, Mp, Dp, Fp, qp = 7, 61440, 768, 1536, 4
+    to = lambda op: torch.from_numpy(op.bits.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    X = to(synth.normal_operand(1000 * c + 1, (Mp, Dp), 1.0, "bf16"))
+    Wg = to(synth.normal_operand(1000 * c + 2, (Dp, Fp), Dp ** -0.5, "bf16"))
+    Wu = to(synth.normal_operand(1000 * c + 3, (Dp, Fp), Dp ** -0.5, "bf16"))
+    Wd = to(synth.normal_operand(1000 * c + 4, (Fp, Dp), Fp ** -0.5, "bf16"))
+    pos = torch.from_numpy(synth.cyclic_positions(Mp, 1536)).to(dev)
+    H = torch.empty(Mp, Fp, dtype=torch.bfloat16, device=dev)
+    Y = torch.empty(Mp, Dp, dtype=torch.bfloat16, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    out = {"workload": "pilot_swiglu_ffn_D768_F1536_M61440_interval", "M": Mp, "D": Dp, "F": Fp}
+    for name, q, law, frac in (("tensor_q4", qp, Q.QALG_FLAG_LAW_TENSOR, 9 / 16), ("complete_q4", qp, 0, 7 / 16),
+                               ("dense_q1", 1, 0, 1.0)):
+        tau = Q.qalg_type_schedule(pos, q, Q.QALG_SCHEDULE_INTERVAL, 768 if q > 1 else 1, stream=stream)
+        ws = Q.workspace(q, Mp, device=dev)
+        Q.qalg_build_index(tau, q, ws=ws, stream=stream)
+        Wgu = Q.qalg_merge_gate_up(Wg, Wu, q, stream=stream)
+        fl = law | Q.QALG_FLAG_INDEX_READY
+        step = lambda: (Q.qalg_gated_forward(X, Wgu, tau, q, H=H, ws=ws, flags=fl, stream=stream),  # noqa: E731
+                        Q.qalg_forward(H, Wd, tau, q, Y=Y, ws=ws, flags=fl, stream=stream))
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        n = 20
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(n):
+            step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n
+        flop = 3 * 2.0 * frac * Mp * Dp * Fp
+        out[name] = {"step_ms": round(ms, 4), "algebra_tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+    out["speedup_tensor_vs_dense"] = round(out["dense_q1"]["step_ms"] / out["tensor_q4"]["step_ms"], 3)
+    out["speedup_complete_vs_dense"] = round(out["dense_q1"]["step_ms"] / out["complete_q4"]["step_ms"], 3)
+    log(f"[bench] pilot FFN leg: {out}")
+    return out
+
+
+def few_rows_leg(Q, torch, np, synth, dev, stream):
+    """Few rows per type (appendix E's q = 32 projections at M = 2048, 64 rows per type): the
+    Qwen3-8B and Qwen3-1.7B FFN shapes, up and down, at q = 32 and with the same kernels at q = 1."""
+    c, Mf, q = 8, 2048, 32
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    out = {"workload": "q32_M2048_projections", "M": Mf, "q": q}
+    for name, D, F in (("qwen3_8b", 4096, 12288), ("qwen3_1_7b", 2048, 6144)):
+        for direction, K, N in (("up", D, F), ("down", F, D)):
+            X = torch.from_numpy(synth.normal_operand(1000 * c + 1, (Mf, K), 1.0, "bf16").bits.view(np.int16)).view(
+                torch.bfloat16).to(dev)
+            W = torch.from_numpy(synth.normal_operand(1000 * c + 2, (K, N), K ** -0.5, "bf16").bits.view(
+                np.int16)).view(torch.bfloat16).to(dev)
+            Y = torch.empty(Mf, N, dtype=torch.bfloat16, device=dev)
+            res = {}
+            for qq in (q, 1):
+                tau = torch.from_numpy((np.arange(Mf) % qq).astype(np.int32)).to(dev)
+                ws = Q.workspace(qq, Mf, device=dev)
+                Q.qalg_build_index(tau, qq, ws=ws, stream=stream)
+                fl = Q.QALG_FLAG_INDEX_READY
+                for _ in range(5):
+                    Q.qalg_forward(X, W, tau, qq, Y=Y, ws=ws, flags=fl, stream=stream)
+                torch.cuda.synchronize()
+                n = 40
+                a, b = ev(), ev()
+                a.record(stream)
+                for _ in range(n):
+                    Q.qalg_forward(X, W, tau, qq, Y=Y, ws=ws, flags=fl, stream=stream)
+                b.record(stream)
+                torch.cuda.synchronize()
+                res[qq] = a.elapsed_time(b) / n
+            flop = 2.0 * rho(q) * Mf * K * N
+            out[f"{name}_{direction}"] = {"K": K, "N": N, "q32_us": round(res[q] * 1e3, 1),
+                                          "q32_algebra_tflops": round(flop / (res[q] * 1e-3) / 1e12, 1),
+                                          "q1_us": round(res[1] * 1e3, 1),
+                                          "speedup_vs_q1": round(res[1] / res[q], 2)}
+    log(f"[bench] few-rows leg: {out}")
     return out
 
 

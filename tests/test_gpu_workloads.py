@@ -252,3 +252,51 @@ def test_gated_ffn_training_q8_sampled():
     e["dW_gate"] = assert_groups(rel_frob_blocks(to_f64(dWg[:, cf]), dWg_r, q), STEP_TOL, "dW_gate")
     e["dW_up"] = assert_groups(rel_frob_blocks(to_f64(dWu[:, cf]), dWu_r, q), STEP_TOL, "dW_up")
     say("    " + ", ".join(f"{k} {v:.2e}" for k, v in e.items()))
+
+
+def test_pilot_law_ffn_sampled():
+    """The benchmark's pilot FFN leg under Q_2^(x)2 (same seeds, schedule and calls): fused gate/up
+    then down, both with the recursive law; H and Y checked on sampled rows."""
+    torch = torch_cuda()
+    c, M, D, F, q, L = 7, 61440, 768, 1536, 4, 2
+    say(f"[workload] pilot FFN Q_2^2 bf16 M={M} {D}->{F}->{D}, interval schedule")
+    X = synth.normal_operand(1000 * c + 1, (M, D), 1.0, "bf16")
+    Wg = synth.normal_operand(1000 * c + 2, (D, F), D ** -0.5, "bf16")
+    Wu = synth.normal_operand(1000 * c + 3, (D, F), D ** -0.5, "bf16")
+    Wd = synth.normal_operand(1000 * c + 4, (F, D), F ** -0.5, "bf16")
+    positions = synth.cyclic_positions(M, 1536)
+    td = Q.qalg_type_schedule(torch.from_numpy(positions).to("cuda"), q, Q.QALG_SCHEDULE_INTERVAL, 768)
+    ws = Q.workspace(q, M)
+    Q.qalg_build_index(td, q, ws=ws)
+    fl = Q.QALG_FLAG_LAW_TENSOR | Q.QALG_FLAG_INDEX_READY
+    Wgu = Q.qalg_merge_gate_up(to_dev(Wg), to_dev(Wu), q)
+    H = Q.qalg_gated_forward(to_dev(X), Wgu, td, q, ws=ws, flags=fl)
+    Y = Q.qalg_forward(H, to_dev(Wd), td, q, ws=ws, flags=fl)
+    torch.cuda.synchronize()
+    tau = td.cpu().numpy()
+    np.testing.assert_array_equal(tau, O.type_schedule(positions, q, "interval", 768))
+    table = O.tensor_power_table(L)
+    rows = _sample_rows(M, q, 512, 71)
+    Hr = O.gated_forward(X.f64[rows], Wg.f64, Wu.f64, tau[rows], q, table=table)
+    e1 = assert_groups(rel_frob_col_groups(to_f64(H[rows]), Hr, q), BF16_TOL, "H")
+    Yr = O.row_typed_forward(Hr, Wd.f64, tau[rows], q, table=table)
+    e2 = assert_groups(rel_frob_col_groups(to_f64(Y[rows]), Yr, q), BF16_TOL, "Y")
+    say(f"    max rel err over {rows.size} sampled rows: H {e1:.2e}, Y {e2:.2e}")
+
+
+@pytest.mark.parametrize("direction", ["up", "down"])
+def test_few_rows_q32_sampled(direction):
+    """The benchmark's few-rows leg at the Qwen3-8B shape (q = 32, M = 2048, 64 rows per type;
+    same seeds): the default (calibrated) tile choice on sampled rows."""
+    torch = torch_cuda()
+    c, M, q = 8, 2048, 32
+    K, N = (4096, 12288) if direction == "up" else (12288, 4096)
+    say(f"[workload] few rows per type: bf16 q={q} M={M} {K}->{N}")
+    X = synth.normal_operand(1000 * c + 1, (M, K), 1.0, "bf16")
+    W = synth.normal_operand(1000 * c + 2, (K, N), K ** -0.5, "bf16")
+    tau = (np.arange(M) % q).astype(np.int32)
+    Y = Q.qalg_forward(to_dev(X), to_dev(W), tau_dev(tau), q)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M, q, 256, 73)
+    e = _sampled_forward_check(X, W, tau, q, Y, rows, "Y")
+    say(f"    max rel err over {rows.size} sampled rows: {e:.2e}")
