@@ -34,6 +34,11 @@ What is computed, plainly:
   evaluators take any law's triples through their `table` argument, so a row
   of type alpha sums x_beta W_beta,delta over the beta whose bits each come
   from alpha or delta (eq 36's support; section 6.1's B(i, j) for this law).
+* `algebraic_attention` is appendix G's causal attention with the algebraic
+  score: a query of type i and a key of type j compare only the feature groups
+  F(i, j) ({i} or {i, j}, eq 38; eq 42 for the recursive law), scaled by
+  1 / sqrt(|F| m) (eq 41), then the causal softmax and a dense PV (eq 43-44);
+  `attention_score_macs` counts its score and value MACs (eq 45).
 * `gated_forward` is the gate/up half of a gated (SwiGLU) FFN: both D x F
   projections are row-typed exactly like any other projection, while gates
   and pointwise activations are left as they are (section 4), combined as silu(X *_{Q_q} W_gate) * (X *_{Q_q} W_up), silu
@@ -85,6 +90,9 @@ __all__ = [
     "dense_equivalent_macs",
     "silu",
     "gated_forward",
+    "score_support",
+    "algebraic_attention",
+    "attention_score_macs",
 ]
 
 
@@ -454,3 +462,81 @@ def gated_ffn_backward(X, Wg, Wu, Wd, dY, tau, q):
     dXg, dWg = row_typed_backward(X, Wg, dG, tau, q)
     dXu, dWu = row_typed_backward(X, Wu, dU, tau, q)
     return dXg + dXu, dWg, dWu, dWd
+
+
+# ----------------------------------------------------------------------------
+# Algebraic attention scores: appendix G (eq 38-46), Algorithm 2
+# ----------------------------------------------------------------------------
+
+def score_support(i: int, j: int, q: int, L: int = 0) -> list[int]:
+    """Feature groups a query of type i and a key of type j compare (eq 38 for Q_q: {i} or
+    {i, j}; eq 42 for the recursive law Q_2^(x)L, L >= 1: every b whose bits each come from i or j)."""
+    if L == 0:
+        return [i] if i == j else [i, j]
+    return [b for b in range(q) if all(((b >> k) & 1) in (((i >> k) & 1), ((j >> k) & 1)) for k in range(L))]
+
+
+def algebraic_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, tau: np.ndarray, q: int,
+                        L: int = 0, positions: np.ndarray | None = None) -> np.ndarray:
+    """Causal attention with the algebraic score (appendix G, Algorithm 2, steps 3-7).
+
+    Q: [Hq, S, d], K and V: [Hkv, S, d] with Hkv dividing Hq (query head h uses key/value head
+    h // (Hq / Hkv), the GQA convention of appendix G); tau: [S] types of the S positions;
+    positions: [S] absolute positions for the causal mask (default 0..S-1).  Each head's d
+    features form q groups of width m = d / q.  For a query at p (type i) and a key at u (type j):
+        r_pu = sum over a in F(i, j) of <Q_p^(a), K_u^(a)>          (eq 39)
+        s_pu = r_pu / sqrt(|F(i, j)| m)                              (eq 40-41)
+        P_p  = softmax over u with position(u) <= position(p)        (eq 43-44)
+        O_p  = sum_u P_pu V_u                                         (dense PV)
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    Hq, S, d = Q.shape
+    Hkv = K.shape[0]
+    if d % q or Hq % Hkv or K.shape[1:] != (S, d) or V.shape != K.shape:
+        raise ValueError("shapes")
+    m = d // q
+    tau = np.asarray(tau)
+    pos = np.arange(S) if positions is None else np.asarray(positions)
+    allowed = pos[None, :] <= pos[:, None]                       # [p, u]
+    # selection of group a for each (p, u) pair and the support size k_ij = |F| m
+    sel = np.zeros((q, S, S), dtype=bool)
+    for i in range(q):
+        for j in range(q):
+            pi = tau == i
+            uj = tau == j
+            for a in score_support(i, j, q, L):
+                sel[a][np.ix_(pi, uj)] = True
+    k_pair = sel.sum(axis=0) * m
+    O = np.zeros((Hq, S, d))
+    for h in range(Hq):
+        kv = h // (Hq // Hkv)
+        r = np.zeros((S, S))
+        for a in range(q):
+            g = Q[h][:, a * m:(a + 1) * m] @ K[kv][:, a * m:(a + 1) * m].T
+            r += np.where(sel[a], g, 0.0)
+        s = np.where(allowed, r / np.sqrt(np.maximum(k_pair, 1)), -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        P = np.exp(s)
+        P /= P.sum(axis=1, keepdims=True)
+        O[h] = P @ V[kv]
+    return O
+
+
+def attention_score_macs(tau: np.ndarray, q: int, d: int, L: int = 0,
+                         positions: np.ndarray | None = None) -> tuple[int, int]:
+    """(score MACs, value MACs) of one head over the allowed pairs: sum of |F(i, j)| m per pair
+    for the structured QK^T, d per pair for the dense PV (appendix G, eq 45)."""
+    tau = np.asarray(tau)
+    S = tau.size
+    pos = np.arange(S) if positions is None else np.asarray(positions)
+    m = d // q
+    score = 0
+    pairs = 0
+    for p in range(S):
+        for u in range(S):
+            if pos[u] <= pos[p]:
+                pairs += 1
+                score += len(score_support(int(tau[p]), int(tau[u]), q, L)) * m
+    return score, pairs * d

@@ -720,6 +720,112 @@ def pin_tensor_vjp_autograd(O, seed=43):
         np.testing.assert_allclose(dW, W.grad.numpy(), rtol=1e-12, atol=1e-12)
 
 
+# --------------------------------------------------------------------------
+# algebraic attention scores (appendix G)
+# --------------------------------------------------------------------------
+
+def pin_attention_q1_is_sdpa(O, seed=51):
+    """q = 1 is ordinary causal attention with 1/sqrt(d): fp64 torch scaled_dot_product_attention."""
+    import torch
+    g = _rng(seed)
+    Q = g.standard_normal((4, 13, 8))
+    K = g.standard_normal((2, 13, 8))
+    V = g.standard_normal((2, 13, 8))
+    got = O.algebraic_attention(Q, K, V, np.zeros(13, int), 1)
+    Kx = torch.tensor(np.repeat(K, 2, axis=0))
+    Vx = torch.tensor(np.repeat(V, 2, axis=0))
+    want = torch.nn.functional.scaled_dot_product_attention(torch.tensor(Q), Kx, Vx, is_causal=True).numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def _softmax_rows(s):
+    s = s - s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def pin_attention_scores_are_typed_product(O, seed=52):
+    """Before normalisation the score matrix is Q *_{Q_q} K^T with keys grouped by type (appendix G:
+    the block S_ij = Q_ii K_ji^T + Q_ij K_jj^T): the row-typed projection of Q with the bank K^T
+    (columns sorted by key type), scaled per pair by 1/sqrt(|F| m), then the causal softmax and PV."""
+    g = _rng(seed)
+    for q, S, d in ((4, 12, 8), (2, 10, 6), (3, 9, 6)):
+        Q = g.standard_normal((1, S, d))
+        K = g.standard_normal((1, S, d))
+        V = g.standard_normal((1, S, d))
+        tau = np.arange(S) % q
+        perm = np.argsort(tau, kind="stable")
+        Z = O.row_typed_forward(Q[0], K[0][perm].T, tau, q)
+        r = np.empty_like(Z)
+        r[:, perm] = Z
+        m = d // q
+        k = np.where(tau[:, None] == tau[None, :], m, 2 * m)
+        s = np.where(np.tri(S, dtype=bool), r / np.sqrt(k), -np.inf)
+        want = _softmax_rows(s) @ V[0]
+        np.testing.assert_allclose(O.algebraic_attention(Q, K, V, tau, q)[0], want, rtol=1e-12, atol=1e-12)
+
+
+def pin_attention_scale_and_mask(O):
+    """With all-ones Q and K the score is sqrt(|F| m) (eq 41); V = I reads P back: P_pu is
+    proportional to exp(sqrt(m)) for equal types and exp(sqrt(2m)) otherwise, zero for u > p."""
+    q, S = 4, 8
+    d = S
+    m = d // q
+    tau = np.arange(S) % q
+    P = O.algebraic_attention(np.ones((1, S, d)), np.ones((1, S, d)), np.eye(S)[None], tau, q)[0]
+    for p in range(S):
+        w = np.array([np.exp(np.sqrt(m if tau[u] == tau[p] else 2 * m)) if u <= p else 0.0 for u in range(S)])
+        np.testing.assert_allclose(P[p], w / w.sum(), rtol=1e-13, atol=1e-15)
+
+
+def pin_attention_causality(O, seed=53):
+    """Proposition G.1: keys and values after position p do not change O_p."""
+    g = _rng(seed)
+    Q = g.standard_normal((2, 16, 8))
+    K = g.standard_normal((2, 16, 8))
+    V = g.standard_normal((2, 16, 8))
+    tau = np.arange(16) % 4
+    a = O.algebraic_attention(Q, K, V, tau, 4)
+    K2, V2 = K.copy(), V.copy()
+    K2[:, 9:] += 5.0
+    V2[:, 9:] -= 3.0
+    b = O.algebraic_attention(Q, K2, V2, tau, 4)
+    assert np.array_equal(a[:, :9], b[:, :9])
+    assert not np.allclose(a[:, 9:], b[:, 9:])
+
+
+def pin_attention_gqa(O, seed=54):
+    """Query head h uses key/value head h // (Hq / Hkv): the same as repeating each K/V head."""
+    g = _rng(seed)
+    Q = g.standard_normal((6, 10, 8))
+    K = g.standard_normal((2, 10, 8))
+    V = g.standard_normal((2, 10, 8))
+    tau = np.arange(10) % 2
+    a = O.algebraic_attention(Q, K, V, tau, 2)
+    b = O.algebraic_attention(Q, np.repeat(K, 3, axis=0), np.repeat(V, 3, axis=0), tau, 2)
+    np.testing.assert_allclose(a, b, rtol=0, atol=0)
+
+
+def pin_attention_laws_and_counts(O):
+    """eq 38 and eq 42 supports; L = 1 is Q_2; score MACs are (2M - M_eq) m (eq 45) over the allowed
+    pairs, value MACs M d."""
+    assert O.score_support(2, 2, 4) == [2] and O.score_support(3, 1, 4) == [3, 1]
+    for L in (1, 2, 3):
+        q = 2 ** L
+        for i in range(q):
+            for j in range(q):
+                assert set(O.score_support(i, j, q, L)) == _bits_support(i, j, L)
+    for i in range(2):
+        for j in range(2):
+            assert sorted(O.score_support(i, j, 2, 1)) == sorted(O.score_support(i, j, 2))
+    for q, S, d in ((4, 37, 8), (3, 20, 6), (1, 9, 4)):
+        tau = np.arange(S) % q
+        sm, vm = O.attention_score_macs(tau, q, d)
+        Mp = S * (S + 1) // 2
+        Meq = sum(1 for p in range(S) for u in range(p + 1) if tau[u] == tau[p])
+        assert sm == (2 * Mp - Meq) * (d // q) and vm == Mp * d
+
+
 ALL_PINS = [
     pin_q2_table, pin_q2_scalar_example, pin_eq3_rectangular_blocks, pin_eq13_14,
     pin_product_counts, pin_graph_counts, pin_appendix_a, pin_associativity,
@@ -729,4 +835,6 @@ ALL_PINS = [
     pin_mac_count, pin_type_index, pin_type_schedule, pin_silu_values, pin_gated_masked_dense,
     pin_silu_grad, pin_gated_ffn_autograd, pin_tensor_counts, pin_tensor_support,
     pin_tensor_associativity, pin_tensor_masked_dense, pin_tensor_cost, pin_tensor_vjp_autograd,
+    pin_attention_q1_is_sdpa, pin_attention_scores_are_typed_product, pin_attention_scale_and_mask,
+    pin_attention_causality, pin_attention_gqa, pin_attention_laws_and_counts,
 ]

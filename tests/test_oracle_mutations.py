@@ -19,6 +19,8 @@ _real_silu = O.silu
 _real_gated = O.gated_forward
 _real_silu_grad = O.silu_grad
 _real_tensor = O.tensor_power_table
+_real_attn = O.algebraic_attention
+_real_support = O.score_support
 _real_swiglu_bwd = O.swiglu_backward
 
 
@@ -199,6 +201,35 @@ def tensor_edge_edge(L):
     return t
 
 
+def attn_dense_scale(Q, K, V, tau, q, L=0, positions=None):
+    """Mistake: the dense scale: queries shrunk by sqrt(m / d), so that an equal-type pair is
+    scaled by 1/sqrt(d) as in ordinary attention instead of 1/sqrt(m)."""
+    d = np.asarray(Q).shape[2]
+    return _real_attn(np.asarray(Q, float) * np.sqrt((d // q) / d), K, V, tau, q, L, positions)
+
+
+def support_own_group_only(i, j, q, L=0):
+    """Mistake: a pair compares only the query's own group."""
+    return [i]
+
+
+def attn_kv_head_modulo(Q, K, V, tau, q, L=0, positions=None):
+    """Mistake: query head h uses key/value head h mod Hkv."""
+    Q = np.asarray(Q, float)
+    K = np.asarray(K, float)
+    V = np.asarray(V, float)
+    Hq, Hkv = Q.shape[0], K.shape[0]
+    idx = [h % Hkv for h in range(Hq)]
+    return _real_attn(Q, K[idx], V[idx], tau, q, L, positions)
+
+
+def attn_anticausal(Q, K, V, tau, q, L=0, positions=None):
+    """Mistake: the mask admits keys at or after the query."""
+    S = np.asarray(Q).shape[1]
+    pos = np.arange(S) if positions is None else np.asarray(positions)
+    return _real_attn(Q, K, V, tau, q, L, -pos)
+
+
 MUTANTS = [
     ("structure_table", table_with_edge_edge),
     ("structure_table", table_without_right_vertex),
@@ -220,6 +251,10 @@ MUTANTS = [
     ("tensor_power_table", tensor_msb_lsb_mixed),
     ("tensor_power_table", tensor_drops_far_terms),
     ("tensor_power_table", tensor_edge_edge),
+    ("algebraic_attention", attn_dense_scale),
+    ("score_support", support_own_group_only),
+    ("algebraic_attention", attn_kv_head_modulo),
+    ("algebraic_attention", attn_anticausal),
 ]
 
 
