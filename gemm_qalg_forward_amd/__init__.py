@@ -8,6 +8,7 @@ tensor is not on the GPU, the call raises.
 Functions carry the C names:
     qalg_forward, qalg_backward_dx, qalg_backward_dw, qalg_forward_batched,
     qalg_gated_forward, qalg_merge_gate_up, qalg_split_gate_up, qalg_swiglu_forward, qalg_swiglu_backward,
+    qalg_attention_forward,
     qalg_type_schedule, qalg_build_index, qalg_build_index_batched,
     qalg_read_status, qalg_workspace_bytes, qalg_index_layout,
     qalg_status_string, qalg_version.
@@ -26,7 +27,7 @@ __all__ = [
     "qalg_type_schedule", "qalg_build_index", "qalg_build_index_batched",
     "qalg_forward", "qalg_backward_dx", "qalg_backward_dw", "qalg_forward_batched",
     "qalg_gated_forward", "qalg_merge_gate_up", "qalg_split_gate_up", "qalg_swiglu_forward",
-    "qalg_swiglu_backward", "qalg_read_status", "workspace",
+    "qalg_swiglu_backward", "qalg_attention_forward", "qalg_read_status", "workspace",
 ]
 
 QALG_F32 = 0
@@ -69,6 +70,8 @@ _SIGS = {
     "qalg_split_gate_up": (ctypes.c_int, [_vp, _c_i32, _c_i64, _c_i64, _vp, _vp, _c_i32, _vp]),
     "qalg_swiglu_forward": (ctypes.c_int, [_vp, _c_i32, _c_i64, _c_i64, _vp, _c_i32, _vp]),
     "qalg_swiglu_backward": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i64, _vp, _c_i32, _vp]),
+    "qalg_attention_forward": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _vp, _c_i32,
+                                              _c_u32, _vp]),
     "qalg_read_status": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i64, _vp, ctypes.POINTER(_c_i64)]),
 }
 
@@ -299,6 +302,23 @@ def qalg_swiglu_backward(GU, dH, q: int, dGU=None, stream=None):
         _dev_ptr(GU, "GU"), _dev_ptr(dH, "dH"), q, M, F2 // 2, _dev_ptr(dGU, "dGU"), _dtype_code(GU),
         _stream(stream)))
     return dGU
+
+
+def qalg_attention_forward(Qh, Kh, Vh, q: int, O=None, flags: int = 0, stream=None):
+    """Causal attention with the algebraic score: Q [Hq, S, d], K and V [Hkv, S, d] -> O [Hq, S, d]."""
+    torch = _torch()
+    Hq, S, d = Qh.shape
+    Hkv = Kh.shape[0]
+    if tuple(Kh.shape) != (Hkv, S, d) or tuple(Vh.shape) != (Hkv, S, d):
+        raise ValueError("K and V must be [Hkv, S, d] with the S and d of Q")
+    if Kh.dtype != Qh.dtype or Vh.dtype != Qh.dtype:
+        raise TypeError("Q, K and V must share a dtype")
+    if O is None:
+        O = torch.empty_like(Qh)
+    _check("qalg_attention_forward", lib().qalg_attention_forward(
+        _dev_ptr(Qh, "Q"), _dev_ptr(Kh, "K"), _dev_ptr(Vh, "V"), Hq, Hkv, S, d, q, _dev_ptr(O, "O"),
+        _dtype_code(Qh), flags, _stream(stream)))
+    return O
 
 
 def qalg_gated_forward(X, Wgu, tau, q: int, H=None, ws=None, flags: int = 0, stream=None):

@@ -367,6 +367,22 @@ qalg_status qalg_swiglu_backward(const void* GU, const void* dH, int32_t q, int6
   return hip_status(qalg::launch_swiglu_bwd_bf16(GU, dH, dGU, M, F, q, static_cast<hipStream_t>(stream)));
 }
 
+qalg_status qalg_attention_forward(const void* Q, const void* K, const void* V, int32_t Hq, int32_t Hkv,
+                                   int64_t S, int32_t d, int32_t q, void* O, int32_t dtype, uint32_t flags,
+                                   void* stream) {
+  if (dtype != QALG_BF16) return QALG_ERR_DTYPE;
+  if (flags & ~uint32_t(QALG_FLAG_LAW_TENSOR)) return QALG_ERR_ARG;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv || S < 0 || S > INT32_MAX / 4 || (d != 64 && d != 128)) return QALG_ERR_DIM;
+  if (q < 1 || q > QALG_MAX_Q || d % q) return QALG_ERR_Q;
+  const int L = (flags & QALG_FLAG_LAW_TENSOR) ? tensor_levels(q) : 0;
+  if (L < 0) return QALG_ERR_Q;
+  if (!qalg::attn_supported(d, q)) return QALG_ERR_ALIGN;
+  if (S == 0) return QALG_OK;
+  if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr) return QALG_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return QALG_ERR_ALIGN;
+  return hip_status(qalg::launch_attn_fwd_bf16(Q, K, V, O, Hq, Hkv, S, d, q, L, static_cast<hipStream_t>(stream)));
+}
+
 qalg_status qalg_read_status(const void* ws, int32_t E, int32_t q, int64_t M, void* stream,
                              int64_t* bad_tau_rows) {
   if (ws == nullptr || bad_tau_rows == nullptr) return QALG_ERR_NULL;

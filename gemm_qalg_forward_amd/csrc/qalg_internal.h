@@ -103,6 +103,11 @@ hipError_t launch_swiglu_bwd_bf16(const void* GU, const void* dH, void* dGU, int
                                   hipStream_t s);
 hipError_t launch_split_gate_up_bf16(const void* Wgu, void* Wg, void* Wu, int64_t K, int64_t F, int q,
                                      hipStream_t s);
+
+// causal attention with the algebraic score, forward (qalg_attn.hip)
+bool attn_supported(int d, int q);
+hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, void* O, int Hq, int Hkv, int64_t S,
+                                int d, int q, int L, hipStream_t s);
 // Persistent 256-row-tile dX / dW (bf16, one problem) for cyclic schedules; a
 // launch on any other schedule returns at once.
 bool grad_persistent_supported(const ProblemDesc& p);

@@ -278,6 +278,27 @@ qalg_status qalg_swiglu_backward(const void* GU, const void* dH, int32_t q, int6
                                  void* dGU, int32_t dtype, void* stream);
 
 /*
+ * Causal attention with the algebraic score, forward (appendix G, Algorithm 2
+ * steps 3-7; one sequence per head, positions 0 .. S-1, types p mod q).  A
+ * query of type i and a key of type j compare only the feature groups F(i, j)
+ * of the head ({i} if i == j, else {i, j}, eq 38; with QALG_FLAG_LAW_TENSOR the
+ * recursive law's groups, eq 42): r = sum over F of <Q^(a), K^(a)> (eq 39),
+ * scaled by 1 / sqrt(|F| d / q) (eq 41), masked to keys at or before the query
+ * (eq 43), softmaxed, O = P V over all d features (eq 44).
+ * Q, O: Hq x S x d; K, V: Hkv x S x d (Hkv divides Hq; query head h uses
+ * key/value head h / (Hq / Hkv), the GQA convention); all bf16, packed,
+ * 16-byte aligned, caller-owned device memory.  fp32 scores, softmax
+ * statistics and accumulation; P is rounded to bf16 for the value product and
+ * O once at the end.  d must be 64 or 128 (QALG_ERR_DIM), q must divide d
+ * (QALG_ERR_Q) with d / q a multiple of 16 (QALG_ERR_ALIGN); the recursive law
+ * needs q = 2^L (QALG_ERR_Q).  Flags: QALG_FLAG_LAW_TENSOR only.  S = 0 returns
+ * QALG_OK without a launch.
+ */
+qalg_status qalg_attention_forward(const void* Q, const void* K, const void* V, int32_t Hq, int32_t Hkv,
+                                   int64_t S, int32_t d, int32_t q, void* O, int32_t dtype, uint32_t flags,
+                                   void* stream);
+
+/*
  * Number of rows with an out-of-range type seen by the last index build in
  * ws (summed over the E problems of a batched workspace; E = 1 otherwise).
  * Synchronises `stream`.

@@ -215,3 +215,19 @@ def test_tile_flags_errors_are_synchronous(lib):
     dx = lib.qalg_backward_dx(FAKE, FAKE, FAKE, 4, 64, 256, 1024, FAKE, 1, FAKE, 1 << 20, Q.QALG_FLAG_TILE_M64, None)
     assert dx == 8
     assert fwd(flags=Q.QALG_FLAG_TILE_M64, M=0) == 0                       # no rows: nothing to do
+
+
+def test_attention_argument_errors_are_synchronous(lib):
+    at = lambda **k: lib.qalg_attention_forward(k.get("Qp", FAKE), FAKE, FAKE, k.get("Hq", 4), k.get("Hkv", 2),  # noqa: E731
+                                                k.get("S", 64), k.get("d", 128), k.get("q", 4), k.get("O", FAKE),
+                                                k.get("dt", 1), k.get("flags", 0), None)
+    assert at(dt=0) == 5
+    assert at(flags=2) == 8
+    assert at(Hkv=3) == 2          # Hkv must divide Hq
+    assert at(d=96) == 2           # d is 64 or 128
+    assert at(q=3) == 3            # q divides d
+    assert at(q=16) == 4           # d / q = 8: not a multiple of 16
+    assert at(q=8, d=64) == 4
+    assert at(Qp=None) == 1
+    assert at(O=FAKE + 4) == 4
+    assert at(S=0, Qp=None) == 0   # no positions: nothing to do
