@@ -173,6 +173,7 @@ def main() -> int:
         extra["gated_ffn"] = gated_leg(Q, torch, np, synth, dev, stream)
         extra["pilot_ffn"] = pilot_leg(Q, torch, np, synth, dev, stream)
         extra["few_rows"] = few_rows_leg(Q, torch, np, synth, dev, stream)
+        extra["attention"] = attention_leg(Q, torch, np, synth, dev, stream)
 
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib << 20
@@ -453,6 +454,57 @@ def few_rows_leg(Q, torch, np, synth, dev, stream):
                                           "q1_us": round(res[1] * 1e3, 1),
                                           "speedup_vs_q1": round(res[1] / res[q], 2)}
     log(f"[bench] few-rows leg: {out}")
+    return out
+
+
+def attention_leg(Q, torch, np, synth, dev, stream):
+    """Causal attention with the algebraic score (appendix G): 32 query heads, 8 key/value heads,
+    d = 128, S = 4096 (one sequence), q = 4 under Q_4 and under Q_2^(x)2, and the same kernel at
+    q = 1 (ordinary attention).  FLOP: 2 |F| m per allowed pair for QK^T plus 2 d for PV."""
+    c, Hq, Hkv, S, d, q = 9, 32, 8, 4096, 128, 4
+    to = lambda op: torch.from_numpy(op.bits.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    Qd = to(synth.normal_operand(1000 * c + 1, (Hq, S, d), 1.0, "bf16"))
+    Kd = to(synth.normal_operand(1000 * c + 2, (Hkv, S, d), 1.0, "bf16"))
+    Vd = to(synth.normal_operand(1000 * c + 3, (Hkv, S, d), 1.0, "bf16"))
+    Od = torch.empty_like(Qd)
+    pairs = S * (S + 1) // 2
+    same = {}  # allowed pairs with equal types, per q (cyclic types)
+    for qq in (1, q):
+        n = [(S - i + qq - 1) // qq for i in range(qq)]
+        same[qq] = sum(k * (k + 1) // 2 for k in n)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    out = {"workload": "causal_attention_Hq32_Hkv8_S4096_d128", "Hq": Hq, "Hkv": Hkv, "S": S, "d": d}
+    for name, qq, fl in (("complete_q4", q, 0), ("tensor_q4", q, Q.QALG_FLAG_LAW_TENSOR), ("dense_q1", 1, 0)):
+        run = lambda: Q.qalg_attention_forward(Qd, Kd, Vd, qq, O=Od, flags=fl, stream=stream)  # noqa: E731
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        n = 10
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(n):
+            run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n
+        m = d // qq
+        if fl:   # recursive law at L = 2: |F| = 2^popcount(i ^ j); mean over cyclic pairs, exact below
+            score = 0
+            for i in range(qq):
+                for j in range(qq):
+                    ni = (S - i + qq - 1) // qq
+                    cnt = sum(max(0, (i + qq * t - j) // qq + 1) for t in range(ni))  # keys j + q t' <= i + q t
+                    score += cnt * (1 << bin(i ^ j).count("1")) * m
+        else:
+            score = (2 * pairs - same[qq]) * m if qq > 1 else pairs * d
+        flop = 2.0 * Hq * (score + pairs * d)
+        out[name] = {"ms": round(ms, 4), "algebra_tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+                     "score_fraction": round(score / (pairs * d), 4)}
+    for name in ("complete_q4", "tensor_q4"):
+        out[name]["speedup_vs_q1"] = round(out["dense_q1"]["ms"] / out[name]["ms"], 3)
+        rho = out[name]["score_fraction"]
+        out[name]["ceiling"] = round(2 / (1 + rho), 3)   # eq 46
+    log(f"[bench] attention leg: {out}")
     return out
 
 

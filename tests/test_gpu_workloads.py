@@ -300,3 +300,26 @@ def test_few_rows_q32_sampled(direction):
     rows = _sample_rows(M, q, 256, 73)
     e = _sampled_forward_check(X, W, tau, q, Y, rows, "Y")
     say(f"    max rel err over {rows.size} sampled rows: {e:.2e}")
+
+
+@pytest.mark.parametrize("law", [0, 2])
+def test_attention_bench_shape_sampled_heads(law):
+    """The benchmark's attention leg (32 query heads over 8 key/value heads, S = 4096, d = 128,
+    q = 4; same seeds): three query heads against the oracle, whole sequences."""
+    torch = torch_cuda()
+    c, Hq, Hkv, S, d, q = 9, 32, 8, 4096, 128, 4
+    say(f"[workload] attention Hq={Hq} Hkv={Hkv} S={S} d={d} q={q} L={law}")
+    Qo = synth.normal_operand(1000 * c + 1, (Hq, S, d), 1.0, "bf16")
+    Ko = synth.normal_operand(1000 * c + 2, (Hkv, S, d), 1.0, "bf16")
+    Vo = synth.normal_operand(1000 * c + 3, (Hkv, S, d), 1.0, "bf16")
+    flags = Q.QALG_FLAG_LAW_TENSOR if law else 0
+    Og = Q.qalg_attention_forward(to_dev(Qo), to_dev(Ko), to_dev(Vo), q, flags=flags)
+    torch.cuda.synchronize()
+    tau = np.arange(S) % q
+    heads = [0, 13, 31]
+    got = to_f64(Og[heads])
+    kv = [h // (Hq // Hkv) for h in heads]
+    Or = O.algebraic_attention(Qo.f64[heads], Ko.f64[kv], Vo.f64[kv], tau, q, law)
+    errs = [float(np.linalg.norm(got[k] - Or[k]) / np.linalg.norm(Or[k])) for k in range(len(heads))]
+    say(f"    max rel err over heads {heads}: {max(errs):.2e}")
+    assert max(errs) <= BF16_TOL, errs
