@@ -372,7 +372,8 @@ qalg_status qalg_attention_forward(const void* Q, const void* K, const void* V, 
                                    void* stream) {
   if (dtype != QALG_BF16) return QALG_ERR_DTYPE;
   if (flags & ~uint32_t(QALG_FLAG_LAW_TENSOR)) return QALG_ERR_ARG;
-  if (Hq < 1 || Hkv < 1 || Hq % Hkv || S < 0 || S > INT32_MAX / 4 || (d != 64 && d != 128)) return QALG_ERR_DIM;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv || S < 0 || (d != 64 && d != 128)) return QALG_ERR_DIM;
+  if (S * int64_t(d) * 2 >= (int64_t(1) << 31)) return QALG_ERR_DIM;  // a head's rows: 32-bit byte offsets
   if (q < 1 || q > QALG_MAX_Q || d % q) return QALG_ERR_Q;
   const int L = (flags & QALG_FLAG_LAW_TENSOR) ? tensor_levels(q) : 0;
   if (L < 0) return QALG_ERR_Q;

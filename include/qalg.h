@@ -289,7 +289,8 @@ qalg_status qalg_swiglu_backward(const void* GU, const void* dH, int32_t q, int6
  * key/value head h / (Hq / Hkv), the GQA convention); all bf16, packed,
  * 16-byte aligned, caller-owned device memory.  fp32 scores, softmax
  * statistics and accumulation; P is rounded to bf16 for the value product and
- * O once at the end.  d must be 64 or 128 (QALG_ERR_DIM), q must divide d
+ * O once at the end.  d must be 64 or 128 and S * d * 2 below 2^31
+ * (QALG_ERR_DIM), q must divide d
  * (QALG_ERR_Q) with d / q a multiple of 16 (QALG_ERR_ALIGN); the recursive law
  * needs q = 2^L (QALG_ERR_Q).  Flags: QALG_FLAG_LAW_TENSOR only.  S = 0 returns
  * QALG_OK without a launch.
