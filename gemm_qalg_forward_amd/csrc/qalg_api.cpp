@@ -81,8 +81,8 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
   }
   const bool tensor = (flags & QALG_FLAG_LAW_TENSOR) != 0;
   if (tensor) {
-    // the recursive law runs on the persistent forward only
-    if (op != Op::Fwd || E != 1 || dtype != QALG_BF16 || (flags & (QALG_FLAG_FORCE_TILED | QALG_FLAG_FORCE_SMALL_M)))
+    // the recursive law: persistent forward, register-staged dX and dW, one bank, bf16
+    if (E != 1 || dtype != QALG_BF16 || (flags & (QALG_FLAG_FORCE_TILED | QALG_FLAG_FORCE_SMALL_M)))
       return QALG_ERR_ARG;
     if (tensor_levels(q) < 0) return QALG_ERR_Q;
   }
@@ -118,7 +118,7 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
   st = check_ws(E, q, M, ws, ws_bytes);
   if (st != QALG_OK) return st;
 
-  if (p.law_L > 0 || forced_bm != 0) {
+  if ((p.law_L > 0 && op == Op::Fwd) || forced_bm != 0) {
     if (!qalg::fwd_persistent_shape_ok(p)) {
       const int64_t lim = int64_t(1) << 31;
       if (M * K >= lim || K * N >= lim || M * N >= lim) return QALG_ERR_DIM;
@@ -170,7 +170,7 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
   }
   if (e != hipSuccess) return QALG_ERR_HIP;
 
-  if (dtype == QALG_BF16 && qalg::grad_persistent_supported(p)) {
+  if (dtype == QALG_BF16 && p.law_L == 0 && qalg::grad_persistent_supported(p)) {
     // which of the two runs depends on the index (cyclic schedule or not),
     // known only on the device: both are enqueued, the other returns at once
     e = qalg::launch_grad_persistent_bf16(p, s);

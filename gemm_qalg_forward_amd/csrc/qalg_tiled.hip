@@ -71,7 +71,26 @@ struct Args {
   int n_ct;                          // all column tiles (q * ct_per_group)
   int tm_dw, tn_dw;                  // dW: tiles per block along rows / columns
   int skip_cyclic;                   // return at once when the index says the schedule is cyclic
+  int L;                             // recursive law Q_2^(x)L (TENSOR kernels); 0 otherwise
 };
+
+// Recursive law Q_2^(x)L (appendix C, eq 36): b is in the support of (i, j)
+// when every bit of b equals i's or j's.  Hence, transposed for the VJPs:
+//   dX[I_i, g_b] sums over the output groups j that agree with b wherever b
+//     differs from i (2^(L - |i ^ b|) groups);
+//   dW[g_b, g_j] sums over the rows of the types i that agree with b wherever
+//     b differs from j (2^(L - |b ^ j|) types).
+// In both, segment n fixes the free bits (the bits where the two given indices
+// agree) to n's bits in order.
+__device__ __forceinline__ int law_member(int fixed_from, int fixed_mask, int n, int L) {
+  int g = fixed_from & fixed_mask;
+  for (int k = 0; k < L; ++k)
+    if (!((fixed_mask >> k) & 1)) {
+      if (n & 1) g |= 1 << k;
+      n >>= 1;
+    }
+  return g;
+}
 
 __device__ __forceinline__ int swz(int row, int chunk, int kch) {
   return chunk ^ (((row & 7) ^ ((row >> 3) & 1)) & (kch - 1));
@@ -112,7 +131,7 @@ __device__ __forceinline__ int find_type(const int32_t* tile_off, int q, int rt)
   return lo;
 }
 
-template <Op OP, class C>
+template <Op OP, class C, bool TENSOR = false>
 __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, KCH = C::KCH, T = C::THREADS;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
@@ -140,6 +159,7 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
   int n0, n_cnt;        // output columns [n0, n0 + n_cnt)
   int nseg, seg_len;    // contraction: nseg segments of seg_len each
   int segA0 = 0, segA1 = 0, segB0 = 0, segB1 = 0;
+  int tb_b = 0, tb_j = 0;  // recursive law: the tile's (dX: column group, row type; dW: b, j)
   const int32_t* krows = nullptr;  // dw: contraction rows
 
   if constexpr (OP == Op::Dw) {
@@ -167,6 +187,10 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
     seg_len = k_last - k_first;
     segA0 = b * a.s + rm * BM;  // X column of output row 0
     segB0 = n0;                 // dY column of output column 0
+    if constexpr (TENSOR) {
+      tb_b = b;
+      tb_j = j;
+    }
   } else {
     const int32_t* tile_off = ws + a.off_tiles + tile_height_slot(BM) * (q + 1);
     const int rt = blockIdx.x / a.n_ct;
@@ -184,6 +208,13 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
       nseg = (j == i) ? 1 : 2;
       segA0 = segB0 = i * a.s;   // X columns / W rows of group i
       segA1 = segB1 = j * a.s;   // X columns / W rows of group j
+    } else if constexpr (TENSOR) {
+      // dX column group j of a type-i row: contraction over the output groups
+      // agreeing with j where j differs from i, r columns each
+      nseg = 1 << (a.L - __builtin_popcount(i ^ j));
+      seg_len = a.r;
+      tb_b = j;
+      tb_j = i;
     } else {
       nseg = 1;
       seg_len = (j == i) ? a.N : a.r;
@@ -191,7 +222,18 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
     }
   }
   const int kts = (seg_len + BK - 1) / BK;  // k-steps per segment
-  const int nk = nseg * kts;
+  const int this_seg_len = seg_len;
+  int nk = nseg * kts;
+  if constexpr (TENSOR && OP == Op::Dw) {
+    // dW block (b, j): the rows of each type agreeing with b where b differs from j
+    const int fm_ = tb_b ^ tb_j;
+    nseg = 1 << (a.L - __builtin_popcount(fm_));
+    nk = 0;
+    for (int n = 0; n < nseg; ++n) {
+      const int t = law_member(tb_b, fm_, n, a.L);
+      nk += (offsets[t + 1] - offsets[t] + BK - 1) / BK;
+    }
+  }
 
   // ---------------- loaders ----------------
   // A tile: BM output rows x BK contraction; B tile: BN output columns x BK.
@@ -253,13 +295,39 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
   u32x4 rb[B_PER][B_REGS];
 
   auto load_step = [&](int kt) {
-    const int sg = kt >= kts ? 1 : 0;
-    const int k0 = (kt - sg * kts) * BK;  // offset inside the segment
+    int sg = kt >= kts ? 1 : 0;
+    int k0 = (kt - sg * kts) * BK;  // offset inside the segment
+    int seg_len = this_seg_len;     // this segment's length
+    const int32_t* krows_s = krows;
+    int segA0_s = segA0;
+    if constexpr (TENSOR) {
+      if constexpr (OP == Op::Dx) {
+        const int n = kt / kts;
+        k0 = (kt - n * kts) * BK;
+        segA0_s = law_member(tb_b, tb_b ^ tb_j, n, a.L) * a.r;
+        sg = 0;
+      } else {  // Dw: walk the types' row ranges
+        const int fm_ = tb_b ^ tb_j;
+        int rem = kt;
+        for (int n = 0; n < nseg; ++n) {
+          const int t = law_member(tb_b, fm_, n, a.L);
+          const int lo = offsets[t], len = offsets[t + 1] - lo;
+          const int kn = (len + BK - 1) / BK;
+          if (rem < kn) {
+            krows_s = rows + lo;
+            seg_len = len;
+            k0 = rem * BK;
+            break;
+          }
+          rem -= kn;
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < A_PER; ++u) {
       if constexpr (A_KMAJOR) {
         const int kk = k0 + a_kc[u] * 8;
-        const int col = (sg ? segA1 : segA0) + kk;
+        const int col = (sg ? segA1 : segA0_s) + kk;
         if (a_on[u] && kk < seg_len)
           ra[u][0] = *reinterpret_cast<const u32x4*>(a_ptr[u] + col);
         else
@@ -270,7 +338,7 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
           if (on && kk + rr < seg_len) {
-            const int grow = krows[kk + rr];
+            const int grow = krows_s[kk + rr];
             ra[u][rr] = *reinterpret_cast<const u32x4*>(a_ptr[u] + int64_t(grow) * a.K);
           } else {
             ra[u][rr] = (u32x4){0u, 0u, 0u, 0u};
@@ -283,7 +351,7 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
       if constexpr (B_KMAJOR) {  // dX: W row (output column), contraction along W's columns
         const int kk = k0 + b_kc[u] * 8;
         if (b_on[u] && kk < seg_len)
-          rb[u][0] = *reinterpret_cast<const u32x4*>(b_ptr[u] + segA0 + kk);
+          rb[u][0] = *reinterpret_cast<const u32x4*>(b_ptr[u] + segA0_s + kk);
         else
           rb[u][0] = (u32x4){0u, 0u, 0u, 0u};
       } else if constexpr (OP == Op::Fwd) {  // W rows of the segment, 8 output columns
@@ -303,7 +371,7 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
           if (on && kk + rr < seg_len) {
-            const int grow = krows[kk + rr];
+            const int grow = krows_s[kk + rr];
             rb[u][rr] = *reinterpret_cast<const u32x4*>(b_ptr[u] + int64_t(grow) * a.N);
           } else {
             rb[u][rr] = (u32x4){0u, 0u, 0u, 0u};
@@ -595,8 +663,15 @@ template <Op OP, class C>
 hipError_t launch_cfg(const ProblemDesc& p, hipStream_t s, bool skip_cyclic) {
   Args a = make_args(p, C::BM, C::BN);
   a.skip_cyclic = skip_cyclic ? 1 : 0;
+  a.L = p.law_L;
   const dim3 g = grid_for(p, a, C::BM);
   if (g.x == 0) return hipSuccess;
+  if constexpr (OP != Op::Fwd) {
+    if (p.law_L > 0) {
+      hipLaunchKernelGGL((tiled_bf16_kernel<OP, C, true>), g, dim3(C::THREADS), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((tiled_bf16_kernel<OP, C>), g, dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }

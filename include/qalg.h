@@ -96,10 +96,12 @@ enum {
      * B(i, j) for this law), 2^popcount(i xor j) terms; (3/4)^L of the
      * dense MACs with equal groups.  q must be a power of two
      * (QALG_ERR_Q); q = 2 is Q_2 itself and q = 1 the plain product.
-     * Accepted by qalg_forward and qalg_gated_forward, bf16, on shapes whose
-     * K / q is a multiple of 64 and N / q of 128 (QALG_ERR_ALIGN otherwise;
-     * byte offsets below 2^31, QALG_ERR_DIM); other entry points return
-     * QALG_ERR_ARG. */
+     * Accepted by qalg_forward and qalg_gated_forward (bf16; K / q a
+     * multiple of 64 and N / q of 128, QALG_ERR_ALIGN otherwise; byte offsets
+     * below 2^31, QALG_ERR_DIM), by qalg_backward_dx and qalg_backward_dw
+     * (bf16, any shape the projection accepts: the VJPs of App B with the
+     * law's supports transposed) and by qalg_attention_forward; the batched
+     * forward, fp32 and the forced paths return QALG_ERR_ARG. */
     QALG_FLAG_LAW_TENSOR = 8,
     /* Tile calibration (qalg_forward, bf16, one bank): run the persistent
      * forward with 64-, 128- or 256-row output tiles instead of the height

@@ -436,19 +436,19 @@ def swiglu_backward(G: np.ndarray, U: np.ndarray, dH: np.ndarray):
     return dH * np.asarray(U, dtype=np.float64) * silu_grad(G), dH * silu(G)
 
 
-def gated_ffn_forward(X, Wg, Wu, Wd, tau, q):
+def gated_ffn_forward(X, Wg, Wu, Wd, tau, q, table=None):
     """Y = (silu(X *_Q W_gate) * (X *_Q W_up)) *_Q W_down, each projection row-typed with the
     same tau (section 4: all three gated-FFN weights are row-typed projections).
 
     Returns Y and the intermediates (G, U, H) that the backward pass uses.
     """
-    G = row_typed_forward(X, Wg, tau, q)
-    U = row_typed_forward(X, Wu, tau, q)
+    G = row_typed_forward(X, Wg, tau, q, table=table)
+    U = row_typed_forward(X, Wu, tau, q, table=table)
     H = swiglu(G, U)
-    return row_typed_forward(H, Wd, tau, q), (G, U, H)
+    return row_typed_forward(H, Wd, tau, q, table=table), (G, U, H)
 
 
-def gated_ffn_backward(X, Wg, Wu, Wd, dY, tau, q):
+def gated_ffn_backward(X, Wg, Wu, Wd, dY, tau, q, table=None):
     """(dX, dW_gate, dW_up, dW_down) of `gated_ffn_forward`.
 
     Each projection's VJP is appendix B's (eq 31-35) with the same support as
@@ -456,11 +456,11 @@ def gated_ffn_backward(X, Wg, Wu, Wd, dY, tau, q):
     projection-shaped products against the forward's three: the 9 B D F ->
     9 rho B D F training count of section 6.2.
     """
-    _, (G, U, H) = gated_ffn_forward(X, Wg, Wu, Wd, tau, q)
-    dH, dWd = row_typed_backward(H, Wd, dY, tau, q)
+    _, (G, U, H) = gated_ffn_forward(X, Wg, Wu, Wd, tau, q, table)
+    dH, dWd = row_typed_backward(H, Wd, dY, tau, q, table=table)
     dG, dU = swiglu_backward(G, U, dH)
-    dXg, dWg = row_typed_backward(X, Wg, dG, tau, q)
-    dXu, dWu = row_typed_backward(X, Wu, dU, tau, q)
+    dXg, dWg = row_typed_backward(X, Wg, dG, tau, q, table=table)
+    dXu, dWu = row_typed_backward(X, Wu, dU, tau, q, table=table)
     return dXg + dXu, dWg, dWu, dWd
 
 

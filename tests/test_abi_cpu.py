@@ -196,10 +196,11 @@ def test_tensor_law_flag_errors_are_synchronous(lib):
     assert fwd(K=128) == 4                         # K / q = 32: not a multiple of 64
     assert fwd(N=320) == 4                         # N / q = 80: no tile width divides it
     assert fwd(flags=128) == 8                     # unknown flag
-    dx = lib.qalg_backward_dx(FAKE, FAKE, FAKE, 4, 64, 256, 512, FAKE, 1, FAKE, 1 << 20, T, None)
-    dw = lib.qalg_backward_dw(FAKE, FAKE, FAKE, 4, 64, 256, 512, FAKE, 1, FAKE, 1 << 20, T, None)
+    # dX and dW accept the law (bf16, one bank); the checks still come first
+    dx = lib.qalg_backward_dx(FAKE, FAKE, FAKE, 6, 64, 384, 768, FAKE, 1, FAKE, 1 << 20, T, None)
+    dw = lib.qalg_backward_dw(FAKE, FAKE, FAKE, 4, 64, 256, 512, FAKE, 0, FAKE, 1 << 20, T, None)
     bt = lib.qalg_forward_batched(2, FAKE, FAKE, FAKE, 4, 64, 256, 512, FAKE, 1, FAKE, 1 << 20, T, None)
-    assert dx == dw == bt == 8                     # the recursive law runs on the forward only
+    assert dx == 3 and dw == 8 and bt == 8         # q = 6 not 2^L; fp32; several banks
     assert call_gated(lib, q=3, K=192, F=384, flags=T) == 3
 
 

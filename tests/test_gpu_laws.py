@@ -1,8 +1,8 @@
 """The recursive law Q_2^(x)L (appendix C) on the GPU against the oracle's tensor-power table.
 
-qalg_forward and qalg_gated_forward with QALG_FLAG_LAW_TENSOR run the
-persistent forward with eq 36's supports; the oracle evaluates the same rows
-from tensor_power_table(L).  Types come from the cyclic schedule, from the
+qalg_forward, qalg_gated_forward, qalg_backward_dx and qalg_backward_dw with
+QALG_FLAG_LAW_TENSOR use eq 36's supports (transposed for the VJPs); the oracle
+evaluates the same products from tensor_power_table(L).  Types come from the cyclic schedule, from the
 pilot's interval schedule floor((p mod 768) / 192) (appendix D.5), or are
 random (with out-of-range rows).
 """
@@ -13,7 +13,7 @@ import gemm_qalg_forward_amd as Q
 import synth
 from gpu_common import make_tau, say, tau_dev, to_dev, to_f64, torch_cuda
 from oracle import qalg_oracle as O
-from qalg_check import BF16_TOL, assert_groups, rel_frob_col_groups
+from qalg_check import BF16_TOL, assert_groups, rel_frob_blocks, rel_frob_col_groups
 
 pytestmark = pytest.mark.gpu
 
@@ -114,3 +114,84 @@ def test_tensor_law_gated_forward_matches_oracle(shape):
     Hr = O.gated_forward(X.f64, Wg.f64, Wu.f64, tau, q, table=O.tensor_power_table(L))
     e = assert_groups(rel_frob_col_groups(to_f64(H), Hr, q), BF16_TOL, "H")
     say(f"    max rel err {e:.2e}")
+
+
+LAW_GRAD_SHAPES = [
+    # M, K, N, L, tau kind, bad rows
+    (3072, 768, 1536, 2, "interval", 0),    # the pilot's up projection
+    (3072, 1536, 768, 2, "interval", 0),    # and down
+    (1000, 512, 1024, 2, "random", 9),      # listed types, out-of-range rows
+    (512, 256, 512, 3, "cyclic", 0),
+    (777, 256, 512, 1, "cyclic", 0),        # L = 1 is Q_2
+]
+
+
+@pytest.mark.parametrize("shape", LAW_GRAD_SHAPES, ids=[f"M{s[0]}K{s[1]}N{s[2]}L{s[3]}{s[4]}" for s in LAW_GRAD_SHAPES])
+def test_tensor_law_gradients_match_oracle(shape):
+    """dX and dW under Q_2^(x)L (App B's VJPs with the law's supports) against the oracle."""
+    torch = torch_cuda()
+    M, K, N, L, kind, bad = shape
+    q = 2 ** L
+    say(f"[law grads] Q_2^{L}: M={M} K={K} N={N} tau={kind} bad={bad}")
+    X = synth.normal_operand(9310 + M + L, (M, K), 1.0, "bf16")
+    W = synth.normal_operand(9410 + M + L, (K, N), K ** -0.5, "bf16")
+    dY = synth.normal_operand(9510 + M + L, (M, N), 1.0, "bf16")
+    if kind == "interval":
+        td, tau = _interval_tau(M)
+    else:
+        tau = make_tau(kind, M, q, seed=M + 13, bad=bad)
+        td = tau_dev(tau)
+    Xd, Wd, dYd = to_dev(X), to_dev(W), to_dev(dY)
+    ws = Q.workspace(q, M)
+    Q.qalg_build_index(td, q, ws=ws)
+    fl = T | Q.QALG_FLAG_INDEX_READY
+    dX = Q.qalg_backward_dx(dYd, Wd, td, q, ws=ws, flags=fl)
+    dW = Q.qalg_backward_dw(Xd, dYd, td, q, ws=ws, flags=fl)
+    dX2 = Q.qalg_backward_dx(dYd, Wd, td, q, ws=ws, flags=fl)
+    dW2 = Q.qalg_backward_dw(Xd, dYd, td, q, ws=ws, flags=fl)
+    torch.cuda.synchronize()
+    assert torch.equal(dX, dX2) and torch.equal(dW, dW2), "not bitwise reproducible"
+    dXr, dWr = O.row_typed_backward(X.f64, W.f64, dY.f64, tau, q, table=O.tensor_power_table(L))
+    e1 = assert_groups(rel_frob_col_groups(to_f64(dX), dXr, q), BF16_TOL, "dX")
+    e2 = assert_groups(rel_frob_blocks(to_f64(dW), dWr, q), BF16_TOL, "dW")
+    say(f"    max rel err dX {e1:.2e}, dW {e2:.2e}")
+    if bad:
+        rows = np.where((tau < 0) | (tau >= q))[0]
+        assert np.all(to_f64(dX)[rows] == 0.0)
+
+
+def test_pilot_gated_training_step_matches_oracle():
+    """The pilot's SwiGLU FFN training step under Q_2^(x)2 with its interval schedule (D = 768,
+    F = 1536, two 1536-position sequences): merged forward, SwiGLU, down, then all VJPs."""
+    from qalg_check import GATED_STEP_TOL
+    torch = torch_cuda()
+    M, D, F, q, L = 3072, 768, 1536, 4, 2
+    say(f"[law train] pilot FFN Q_2^2 M={M} D={D} F={F}")
+    X = synth.normal_operand(9601, (M, D), 1.0, "bf16")
+    Wg = synth.normal_operand(9602, (D, F), D ** -0.5, "bf16")
+    Wu = synth.normal_operand(9603, (D, F), D ** -0.5, "bf16")
+    Wdn = synth.normal_operand(9604, (F, D), F ** -0.5, "bf16")
+    dY = synth.normal_operand(9605, (M, D), 1.0, "bf16")
+    td, tau = _interval_tau(M)
+    ws = Q.workspace(q, M)
+    Q.qalg_build_index(td, q, ws=ws)
+    fl = T | Q.QALG_FLAG_INDEX_READY
+    Xd, Wdd, dYd = to_dev(X), to_dev(Wdn), to_dev(dY)
+    Wgu = Q.qalg_merge_gate_up(to_dev(Wg), to_dev(Wu), q)
+    GU = Q.qalg_forward(Xd, Wgu, td, q, ws=ws, flags=fl)
+    H = Q.qalg_swiglu_forward(GU, q)
+    Y = Q.qalg_forward(H, Wdd, td, q, ws=ws, flags=fl)
+    dH = Q.qalg_backward_dx(dYd, Wdd, td, q, ws=ws, flags=fl)
+    dWd = Q.qalg_backward_dw(H, dYd, td, q, ws=ws, flags=fl)
+    dGU = Q.qalg_swiglu_backward(GU, dH, q)
+    dX = Q.qalg_backward_dx(dGU, Wgu, td, q, ws=ws, flags=fl)
+    dWg, dWu = Q.qalg_split_gate_up(Q.qalg_backward_dw(Xd, dGU, td, q, ws=ws, flags=fl), q)
+    torch.cuda.synchronize()
+    table = O.tensor_power_table(L)
+    Yr, _ = O.gated_ffn_forward(X.f64, Wg.f64, Wu.f64, Wdn.f64, tau, q, table)
+    dXr, dWgr, dWur, dWdr = O.gated_ffn_backward(X.f64, Wg.f64, Wu.f64, Wdn.f64, dY.f64, tau, q, table)
+    e = {"Y": assert_groups(rel_frob_col_groups(to_f64(Y), Yr, q), GATED_STEP_TOL, "Y"),
+         "dX": assert_groups(rel_frob_col_groups(to_f64(dX), dXr, q), GATED_STEP_TOL, "dX")}
+    for name, got, ref in (("dW_gate", dWg, dWgr), ("dW_up", dWu, dWur), ("dW_down", dWd, dWdr)):
+        e[name] = assert_groups(rel_frob_blocks(to_f64(got), ref, q), GATED_STEP_TOL, name)
+    say("    " + ", ".join(f"{k} {v:.2e}" for k, v in e.items()))
