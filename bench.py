@@ -412,6 +412,47 @@ def pilot_leg(Q, torch, np, synth, dev, stream):
         ms = a.elapsed_time(b) / n
         flop = 3 * 2.0 * frac * Mp * Dp * Fp
         out[name] = {"step_ms": round(ms, 4), "algebra_tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+    # the training step (merged forward, SwiGLU, down; down dX and dW, SwiGLU VJP, merged dX and dW)
+    dY = to(synth.normal_operand(1000 * c + 5, (Mp, Dp), 1.0, "bf16"))
+    GU = torch.empty(Mp, 2 * Fp, dtype=torch.bfloat16, device=dev)
+    dGU = torch.empty_like(GU)
+    dH = torch.empty(Mp, Fp, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(Mp, Dp, dtype=torch.bfloat16, device=dev)
+    dWd = torch.empty(Fp, Dp, dtype=torch.bfloat16, device=dev)
+    dWgu = torch.empty(Dp, 2 * Fp, dtype=torch.bfloat16, device=dev)
+    for name, q, law, frac in (("tensor_q4", qp, Q.QALG_FLAG_LAW_TENSOR, 9 / 16), ("complete_q4", qp, 0, 7 / 16),
+                               ("dense_q1", 1, 0, 1.0)):
+        tau = Q.qalg_type_schedule(pos, q, Q.QALG_SCHEDULE_INTERVAL, 768 if q > 1 else 1, stream=stream)
+        ws = Q.workspace(q, Mp, device=dev)
+        Q.qalg_build_index(tau, q, ws=ws, stream=stream)
+        Wgu = Q.qalg_merge_gate_up(Wg, Wu, q, stream=stream)
+        fl = law | Q.QALG_FLAG_INDEX_READY
+
+        def train():
+            Q.qalg_forward(X, Wgu, tau, q, Y=GU, ws=ws, flags=fl, stream=stream)
+            Q.qalg_swiglu_forward(GU, q, H=H, stream=stream)
+            Q.qalg_forward(H, Wd, tau, q, Y=Y, ws=ws, flags=fl, stream=stream)
+            Q.qalg_backward_dx(dY, Wd, tau, q, dX=dH, ws=ws, flags=fl, stream=stream)
+            Q.qalg_backward_dw(H, dY, tau, q, dW=dWd, ws=ws, flags=fl, stream=stream)
+            Q.qalg_swiglu_backward(GU, dH, q, dGU=dGU, stream=stream)
+            Q.qalg_backward_dx(dGU, Wgu, tau, q, dX=dX, ws=ws, flags=fl, stream=stream)
+            Q.qalg_backward_dw(X, dGU, tau, q, dW=dWgu, ws=ws, flags=fl, stream=stream)
+
+        for _ in range(2):
+            train()
+        torch.cuda.synchronize()
+        n = 10
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(n):
+            train()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n
+        flop = 9 * 2.0 * frac * Mp * Dp * Fp
+        out[name]["train_step_ms"] = round(ms, 4)
+        out[name]["train_algebra_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+    out["train_speedup_tensor_vs_dense"] = round(out["dense_q1"]["train_step_ms"] / out["tensor_q4"]["train_step_ms"], 3)
     out["speedup_tensor_vs_dense"] = round(out["dense_q1"]["step_ms"] / out["tensor_q4"]["step_ms"], 3)
     out["speedup_complete_vs_dense"] = round(out["dense_q1"]["step_ms"] / out["complete_q4"]["step_ms"], 3)
     log(f"[bench] pilot FFN leg: {out}")
