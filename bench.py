@@ -423,7 +423,8 @@ def pilot_leg(Q, torch, np, synth, dev, stream):
     for name, q, law, frac in (("tensor_q4", qp, Q.QALG_FLAG_LAW_TENSOR, 9 / 16), ("complete_q4", qp, 0, 7 / 16),
                                ("dense_q1", 1, 0, 1.0)):
         tau = Q.qalg_type_schedule(pos, q, Q.QALG_SCHEDULE_INTERVAL, 768 if q > 1 else 1, stream=stream)
-        ws = Q.workspace(q, Mp, device=dev)
+        # a workspace that lets dW split its contraction (the largest dW: D x 2F)
+        ws = Q.workspace(q, Mp, device=dev, dw_shape=(Dp, 2 * Fp))
         Q.qalg_build_index(tau, q, ws=ws, stream=stream)
         Wgu = Q.qalg_merge_gate_up(Wg, Wu, q, stream=stream)
         fl = law | Q.QALG_FLAG_INDEX_READY

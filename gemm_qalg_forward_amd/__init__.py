@@ -23,7 +23,7 @@ __all__ = [
     "QALG_F32", "QALG_BF16", "QALG_FLAG_INDEX_READY", "QALG_FLAG_FORCE_TILED",
     "QALG_FLAG_FORCE_SMALL_M", "QALG_FLAG_LAW_TENSOR",
     "QALG_FLAG_TILE_M64", "QALG_FLAG_TILE_M128", "QALG_FLAG_TILE_M256", "QALG_SCHEDULE_CYCLIC", "QALG_SCHEDULE_INTERVAL", "QALG_MAX_Q",
-    "qalg_version", "qalg_status_string", "qalg_workspace_bytes", "qalg_index_layout",
+    "qalg_version", "qalg_status_string", "qalg_workspace_bytes", "qalg_workspace_bytes_dw", "qalg_index_layout",
     "qalg_type_schedule", "qalg_build_index", "qalg_build_index_batched",
     "qalg_forward", "qalg_backward_dx", "qalg_backward_dw", "qalg_forward_batched",
     "qalg_gated_forward", "qalg_merge_gate_up", "qalg_split_gate_up", "qalg_swiglu_forward",
@@ -57,6 +57,7 @@ _SIGS = {
     "qalg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qalg_version": (ctypes.c_int, []),
     "qalg_workspace_bytes": (_c_size, [_c_i32, _c_i64]),
+    "qalg_workspace_bytes_dw": (_c_size, [_c_i32, _c_i64, _c_i64, _c_i64]),
     "qalg_index_layout": (ctypes.c_int, [_c_i32, _c_i64, ctypes.POINTER(_c_i64)]),
     "qalg_type_schedule": (ctypes.c_int, [_vp, _c_i64, _c_i32, _c_i32, _c_i64, _vp, _vp]),
     "qalg_build_index": (ctypes.c_int, [_vp, _c_i32, _c_i64, _vp, _c_size, _vp]),
@@ -114,6 +115,10 @@ def qalg_workspace_bytes(q: int, M: int) -> int:
     return lib().qalg_workspace_bytes(q, M)
 
 
+def qalg_workspace_bytes_dw(q: int, M: int, K: int, N: int) -> int:
+    return lib().qalg_workspace_bytes_dw(q, M, K, N)
+
+
 def qalg_index_layout(q: int, M: int) -> tuple[int, int, int, int]:
     out = (_c_i64 * 4)()
     _check("qalg_index_layout", lib().qalg_index_layout(q, M, out))
@@ -156,10 +161,14 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def workspace(q: int, M: int, E: int = 1, device="cuda"):
-    """A device workspace of the size the projections need (uint8 tensor)."""
+def workspace(q: int, M: int, E: int = 1, device="cuda", dw_shape=None):
+    """A device workspace of the size the projections need (uint8 tensor); with dw_shape = (K, N)
+    large enough for qalg_backward_dw to split its contraction (qalg_workspace_bytes_dw)."""
     torch = _torch()
-    n = qalg_workspace_bytes(q, M) * E
+    if dw_shape is not None and E == 1:
+        n = qalg_workspace_bytes_dw(q, M, dw_shape[0], dw_shape[1])
+    else:
+        n = qalg_workspace_bytes(q, M) * E
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 

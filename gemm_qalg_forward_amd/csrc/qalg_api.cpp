@@ -113,6 +113,9 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
   p.N = N;
   p.E = E;
   p.law_L = tensor ? tensor_levels(q) : 0;
+  // dW: a workspace of qalg_workspace_bytes_dw lets the register-staged path split its contraction
+  if (op == Op::Dw && E == 1 && ws != nullptr && ws_bytes >= qalg_workspace_bytes_dw(q, M, K, N))
+    p.dw_part = static_cast<char*>(ws) + qalg_workspace_bytes(q, M);
 
   // the workspace contract is the same on every path, used or not
   st = check_ws(E, q, M, ws, ws_bytes);
@@ -205,6 +208,12 @@ int qalg_version(void) { return QALG_VERSION; }
 size_t qalg_workspace_bytes(int32_t q, int64_t M) {
   if (q < 1 || q > QALG_MAX_Q || M < 0 || M > INT32_MAX / 2) return 0;
   return size_t(qalg::ws_layout(q, M).total_ints) * sizeof(int32_t);
+}
+
+size_t qalg_workspace_bytes_dw(int32_t q, int64_t M, int64_t K, int64_t N) {
+  const size_t base = qalg_workspace_bytes(q, M);
+  if (base == 0 || K <= 0 || N <= 0 || K > INT32_MAX / 2 || N > INT32_MAX / 2) return 0;
+  return base + size_t(qalg::kDwMaxSplits) * size_t(K) * size_t(N) * sizeof(float);
 }
 
 qalg_status qalg_index_layout(int32_t q, int64_t M, int64_t out_offsets[4]) {

@@ -76,7 +76,11 @@ struct ProblemDesc {
   int64_t M, K, N;
   int E;              // problems (experts); operands packed back to back
   int law_L = 0;      // 0: the complete-graph law Q_q; L >= 1: the recursive law Q_2^(x)L, q = 2^L
+  void* dw_part = nullptr;  // dW on the register-staged path: fp32 scratch for a split contraction
 };
+
+// dW's split contraction (register-staged path): at most this many partial tiles per output tile
+constexpr int kDwMaxSplits = 16;
 
 // skip_cyclic: the kernel returns at once when the index says the schedule is
 // cyclic (a persistent kernel launched beside it covers that case).

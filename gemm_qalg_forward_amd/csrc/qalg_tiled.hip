@@ -72,6 +72,8 @@ struct Args {
   int tm_dw, tn_dw;                  // dW: tiles per block along rows / columns
   int skip_cyclic;                   // return at once when the index says the schedule is cyclic
   int L;                             // recursive law Q_2^(x)L (TENSOR kernels); 0 otherwise
+  float* part;                       // dW split contraction: fp32 partial tiles [splits][K][N]
+  int splits;                        // dW: workgroups per output tile (1: no split)
 };
 
 // Recursive law Q_2^(x)L (appendix C, eq 36): b is in the support of (i, j)
@@ -162,10 +164,13 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
   int tb_b = 0, tb_j = 0;  // recursive law: the tile's (dX: column group, row type; dW: b, j)
   const int32_t* krows = nullptr;  // dw: contraction rows
 
+  int split = 0;  // dW: this workgroup's share of the tile's contraction
   if constexpr (OP == Op::Dw) {
     const int per_block = a.tm_dw * a.tn_dw;
-    const int bid = blockIdx.x / per_block;
-    const int t = blockIdx.x - bid * per_block;
+    const int tix = blockIdx.x / a.splits;
+    split = blockIdx.x - tix * a.splits;
+    const int bid = tix / per_block;
+    const int t = tix - bid * per_block;
     int b, j;
     if (bid < q) {
       b = j = bid;                         // diagonal blocks first: longest contraction
@@ -224,6 +229,9 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
   const int kts = (seg_len + BK - 1) / BK;  // k-steps per segment
   const int this_seg_len = seg_len;
   int nk = nseg * kts;
+  // recursive-law dW: the segment (type) the copy steps are in, its first
+  // k-step, row range and k-steps (loads call it with increasing k-steps)
+  int w_n = 0, w_k0 = 0, w_lo = 0, w_len = 0, w_kn = 0;
   if constexpr (TENSOR && OP == Op::Dw) {
     // dW block (b, j): the rows of each type agreeing with b where b differs from j
     const int fm_ = tb_b ^ tb_j;
@@ -233,6 +241,10 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
       const int t = law_member(tb_b, fm_, n, a.L);
       nk += (offsets[t + 1] - offsets[t] + BK - 1) / BK;
     }
+    const int t0 = law_member(tb_b, fm_, 0, a.L);
+    w_lo = offsets[t0];
+    w_len = offsets[t0 + 1] - w_lo;
+    w_kn = (w_len + BK - 1) / BK;
   }
 
   // ---------------- loaders ----------------
@@ -306,21 +318,18 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
         k0 = (kt - n * kts) * BK;
         segA0_s = law_member(tb_b, tb_b ^ tb_j, n, a.L) * a.r;
         sg = 0;
-      } else {  // Dw: walk the types' row ranges
-        const int fm_ = tb_b ^ tb_j;
-        int rem = kt;
-        for (int n = 0; n < nseg; ++n) {
-          const int t = law_member(tb_b, fm_, n, a.L);
-          const int lo = offsets[t], len = offsets[t + 1] - lo;
-          const int kn = (len + BK - 1) / BK;
-          if (rem < kn) {
-            krows_s = rows + lo;
-            seg_len = len;
-            k0 = rem * BK;
-            break;
-          }
-          rem -= kn;
+      } else {  // Dw: the types' row ranges, walked forward as kt grows
+        while (kt >= w_k0 + w_kn && w_n + 1 < nseg) {
+          w_k0 += w_kn;
+          ++w_n;
+          const int t = law_member(tb_b, tb_b ^ tb_j, w_n, a.L);
+          w_lo = offsets[t];
+          w_len = offsets[t + 1] - w_lo;
+          w_kn = (w_len + BK - 1) / BK;
         }
+        krows_s = rows + w_lo;
+        seg_len = w_len;
+        k0 = (kt - w_k0) * BK;
       }
     }
 #pragma unroll
@@ -451,21 +460,51 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
   };
 
   // ---------------- main loop ----------------
-  if (nk > 0) {
-    load_step(0);
+  // (dW with a split contraction: this workgroup's contiguous range of k-steps)
+  int k_lo = 0, k_hi = nk;
+  if constexpr (OP == Op::Dw) {
+    const int chunk = (nk + a.splits - 1) / a.splits;
+    k_lo = min(nk, split * chunk);
+    k_hi = min(nk, k_lo + chunk);
+  }
+  if (k_hi > k_lo) {
+    load_step(k_lo);
     store_step(0);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const bool more = kt + 1 < nk;
+    for (int kt = k_lo; kt < k_hi; ++kt) {
+      const bool more = kt + 1 < k_hi;
       if (more) load_step(kt + 1);
-      compute_step(kt & 1);
-      if (more) store_step((kt + 1) & 1);
+      compute_step((kt - k_lo) & 1);
+      if (more) store_step((kt - k_lo + 1) & 1);
       __syncthreads();
     }
   }
 
   // ---------------- epilogue: one RNE rounding per output ----------------
   const int64_t ldc = (OP == Op::Fwd) ? a.N : (OP == Op::Dx ? a.K : a.N);
+  if constexpr (OP == Op::Dw) {
+    if (a.splits > 1) {
+      // fp32 partial tile; the reduction sums the splits in order and rounds once
+      float* prow0 = a.part + int64_t(split) * a.K * a.N;
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) {
+        const int ml = wm * C::WTM + fm * 32 + l32;
+        if (ml >= m_cnt) continue;
+        float* prow = prow0 + int64_t(out_first + ml) * a.N + n0;
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int nl = wn * C::WTN + fn * 32 + g * 8 + lhi * 4;
+            if (nl < n_cnt) {
+              const f32x16& v = acc[fm][fn];
+              *reinterpret_cast<float4*>(prow + nl) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+            }
+          }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
     const int ml = wm * C::WTM + fm * 32 + l32;
@@ -619,8 +658,32 @@ __global__ __launch_bounds__(F_T) void tiled_f32_kernel(Args a, const float* A32
 
 inline int cdiv(int64_t a, int64_t b) { return int((a + b - 1) / b); }
 
+// dW = bf16(sum over splits of the fp32 partial tiles), in split order: one
+// rounding per element, the same bits on every run.  4 elements per thread.
+__global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict__ part, int splits, int64_t n,
+                                                        uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  float4 acc = *reinterpret_cast<const float4*>(part + i);
+  for (int p = 1; p < splits; ++p) {
+    const float4 v = *reinterpret_cast<const float4*>(part + int64_t(p) * n + i);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  *reinterpret_cast<u32x2*>(out + i) = pack4_bf16(acc.x, acc.y, acc.z, acc.w);
+}
+
+hipError_t launch_dw_reduce(const float* part, int splits, int64_t n, uint16_t* out, hipStream_t s) {
+  const int64_t threads = n / 4;
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, part, splits, n, out);
+  return hipGetLastError();
+}
+
 Args make_args(const ProblemDesc& p, int bm, int bn) {
   Args a{};
+  a.splits = 1;
   a.A = static_cast<const uint16_t*>(p.A);
   a.B = static_cast<const uint16_t*>(p.B);
   a.C = static_cast<uint16_t*>(p.C);
@@ -653,7 +716,7 @@ Args make_args(const ProblemDesc& p, int bm, int bn) {
 }
 
 dim3 grid_for(const ProblemDesc& p, const Args& a, int bm) {
-  if (p.op == Op::Dw) return dim3(unsigned(p.q * p.q * a.tm_dw * a.tn_dw), unsigned(p.E));
+  if (p.op == Op::Dw) return dim3(unsigned(p.q * p.q * a.tm_dw * a.tn_dw * (a.splits > 1 ? a.splits : 1)), unsigned(p.E));
   // worst case over all type splits: sum_i ceil(M_i / BM) <= ceil(M / BM) + q - 1
   const int64_t rt = (p.M + bm - 1) / bm + p.q - 1;
   return dim3(unsigned(rt * a.n_ct), unsigned(p.E));
@@ -664,16 +727,29 @@ hipError_t launch_cfg(const ProblemDesc& p, hipStream_t s, bool skip_cyclic) {
   Args a = make_args(p, C::BM, C::BN);
   a.skip_cyclic = skip_cyclic ? 1 : 0;
   a.L = p.law_L;
+  // (not beside the persistent kernel: there this launch may return at once)
+  if (OP == Op::Dw && p.dw_part != nullptr && p.E == 1 && !skip_cyclic) {
+    // enough workgroups to cover the CUs about four times, at most kDwMaxSplits per tile
+    const int64_t tiles = int64_t(p.q) * p.q * a.tm_dw * a.tn_dw;
+    int64_t sp = (4 * 256 + tiles - 1) / tiles;
+    sp = sp < 1 ? 1 : (sp > kDwMaxSplits ? kDwMaxSplits : sp);
+    a.splits = int(sp);
+    a.part = static_cast<float*>(p.dw_part);
+  }
   const dim3 g = grid_for(p, a, C::BM);
   if (g.x == 0) return hipSuccess;
   if constexpr (OP != Op::Fwd) {
     if (p.law_L > 0) {
       hipLaunchKernelGGL((tiled_bf16_kernel<OP, C, true>), g, dim3(C::THREADS), 0, s, a);
-      return hipGetLastError();
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess || a.splits == 1) return e;
+      return launch_dw_reduce(a.part, a.splits, p.K * p.N, static_cast<uint16_t*>(p.C), s);
     }
   }
   hipLaunchKernelGGL((tiled_bf16_kernel<OP, C>), g, dim3(C::THREADS), 0, s, a);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  return launch_dw_reduce(a.part, a.splits, p.K * p.N, static_cast<uint16_t*>(p.C), s);
 }
 
 using Cfg128 = TileCfg<128, 128, 64, 2, 2>;

@@ -133,6 +133,18 @@ int qalg_version(void);
 size_t qalg_workspace_bytes(int32_t q, int64_t M);
 
 /*
+ * Workspace that also lets qalg_backward_dw split the contraction of each
+ * output tile over several workgroups on its register-staged path (listed
+ * schedules, the recursive law, shapes the persistent gradient kernel does
+ * not take): qalg_workspace_bytes(q, M) plus fp32 scratch for up to 16
+ * partial sums of the K x N gradient, summed in a fixed order afterwards
+ * (bitwise reproducible, one rounding).  A smaller workspace (at least
+ * qalg_workspace_bytes(q, M)) gives the same result without the split.
+ * Returns 0 for invalid sizes.
+ */
+size_t qalg_workspace_bytes_dw(int32_t q, int64_t M, int64_t K, int64_t N);
+
+/*
  * Type schedule (section 4: a token at position p selects row i = tau(p) by a
  * fixed deterministic schedule; appendix D.5 for the interval form).
  * positions: device int64[M], each >= 0 (a negative position yields type -1,

@@ -44,6 +44,14 @@ def test_version_and_status_strings(lib):
     assert "unknown" in Q.qalg_status_string(99)
 
 
+def test_dw_workspace_size(lib):
+    for q, M, K, N in ((4, 3072, 768, 1536), (1, 10, 64, 64)):
+        base = Q.qalg_workspace_bytes(q, M)
+        assert Q.qalg_workspace_bytes_dw(q, M, K, N) == base + 16 * K * N * 4
+    assert Q.qalg_workspace_bytes_dw(0, 10, 64, 64) == 0
+    assert Q.qalg_workspace_bytes_dw(4, 10, 0, 64) == 0
+
+
 def test_workspace_layout(lib):
     for q, M in ((1, 0), (2, 64), (8, 16384), (512, 1000)):
         n = Q.qalg_workspace_bytes(q, M)

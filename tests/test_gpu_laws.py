@@ -195,3 +195,43 @@ def test_pilot_gated_training_step_matches_oracle():
     for name, got, ref in (("dW_gate", dWg, dWgr), ("dW_up", dWu, dWur), ("dW_down", dWd, dWdr)):
         e[name] = assert_groups(rel_frob_blocks(to_f64(got), ref, q), GATED_STEP_TOL, name)
     say("    " + ", ".join(f"{k} {v:.2e}" for k, v in e.items()))
+
+
+SPLIT_SHAPES = [
+    # M, K, N, L (0: Q_q), q, tau kind
+    (3072, 768, 1536, 2, 4, "interval"),   # the pilot's up dW under Q_2^(x)2
+    (3072, 1536, 768, 0, 4, "interval"),   # Q_4 on the interval schedule (register-staged dW)
+    (1000, 512, 1024, 0, 4, "random"),
+    (512, 256, 512, 3, 8, "cyclic"),       # the recursive law on a cyclic schedule
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=[f"M{s[0]}K{s[1]}N{s[2]}L{s[3]}q{s[4]}{s[5]}" for s in SPLIT_SHAPES])
+def test_dw_split_contraction_matches_oracle(shape):
+    """dW with a workspace of qalg_workspace_bytes_dw: the register-staged path splits each tile's
+    contraction and sums the fp32 partials in a fixed order (bitwise reproducible)."""
+    torch = torch_cuda()
+    M, K, N, L, q, kind = shape
+    say(f"[dw split] M={M} K={K} N={N} L={L} q={q} tau={kind}")
+    X = synth.normal_operand(9320 + M, (M, K), 1.0, "bf16")
+    dY = synth.normal_operand(9520 + M, (M, N), 1.0, "bf16")
+    if kind == "interval":
+        td, tau = _interval_tau(M)
+    else:
+        tau = make_tau(kind, M, q, seed=M + 17, bad=5 if kind == "random" else 0)
+        td = tau_dev(tau)
+    Xd, dYd = to_dev(X), to_dev(dY)
+    ws = Q.workspace(q, M, dw_shape=(K, N))
+    assert ws.numel() == Q.qalg_workspace_bytes_dw(q, M, K, N)
+    Q.qalg_build_index(td, q, ws=ws)
+    fl = (T if L else 0) | Q.QALG_FLAG_INDEX_READY
+    dW = Q.qalg_backward_dw(Xd, dYd, td, q, ws=ws, flags=fl)
+    dW2 = Q.qalg_backward_dw(Xd, dYd, td, q, ws=ws, flags=fl)
+    dW1 = Q.qalg_backward_dw(Xd, dYd, td, q, flags=fl & ~Q.QALG_FLAG_INDEX_READY)  # small workspace: no split
+    torch.cuda.synchronize()
+    assert torch.equal(dW, dW2), "split dW is not bitwise reproducible"
+    table = O.tensor_power_table(L) if L else None
+    _, dWr = O.row_typed_backward(X.f64, np.zeros((K, N)), dY.f64, tau, q, table=table)
+    e = assert_groups(rel_frob_blocks(to_f64(dW), dWr, q), BF16_TOL, "dW (split)")
+    e1 = assert_groups(rel_frob_blocks(to_f64(dW1), dWr, q), BF16_TOL, "dW")
+    say(f"    max rel err split {e:.2e}, unsplit {e1:.2e}")
