@@ -6,7 +6,7 @@ the current stream.  There is no CPU fallback: if libqalg.so is missing or a
 tensor is not on the GPU, the call raises.
 
 Functions carry the C names:
-    qalg_forward, qalg_backward_dx, qalg_backward_dw, qalg_forward_batched,
+    qalg_forward, qalg_forward_graph, qalg_backward_dx, qalg_backward_dw, qalg_forward_batched,
     qalg_gated_forward, qalg_merge_gate_up, qalg_split_gate_up, qalg_swiglu_forward, qalg_swiglu_backward,
     qalg_attention_forward,
     qalg_type_schedule, qalg_build_index, qalg_build_index_batched,
@@ -25,7 +25,7 @@ __all__ = [
     "QALG_FLAG_TILE_M64", "QALG_FLAG_TILE_M128", "QALG_FLAG_TILE_M256", "QALG_SCHEDULE_CYCLIC", "QALG_SCHEDULE_INTERVAL", "QALG_MAX_Q",
     "qalg_version", "qalg_status_string", "qalg_workspace_bytes", "qalg_workspace_bytes_dw", "qalg_index_layout",
     "qalg_type_schedule", "qalg_build_index", "qalg_build_index_batched",
-    "qalg_forward", "qalg_backward_dx", "qalg_backward_dw", "qalg_forward_batched",
+    "qalg_forward", "qalg_forward_graph", "qalg_backward_dx", "qalg_backward_dw", "qalg_forward_batched",
     "qalg_gated_forward", "qalg_merge_gate_up", "qalg_split_gate_up", "qalg_swiglu_forward",
     "qalg_swiglu_backward", "qalg_attention_forward", "qalg_read_status", "workspace",
 ]
@@ -63,6 +63,8 @@ _SIGS = {
     "qalg_build_index": (ctypes.c_int, [_vp, _c_i32, _c_i64, _vp, _c_size, _vp]),
     "qalg_build_index_batched": (ctypes.c_int, [_c_i32, _vp, _c_i32, _c_i64, _vp, _c_size, _vp]),
     "qalg_forward": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
+    "qalg_forward_graph": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size,
+                                          _c_u32, _vp]),
     "qalg_backward_dx": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
     "qalg_backward_dw": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
     "qalg_forward_batched": (ctypes.c_int, [_c_i32, _vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
@@ -233,6 +235,27 @@ def qalg_forward(X, W, tau, q: int, Y=None, ws=None, flags: int = 0, stream=None
     if K2 != K:
         raise ValueError("X and W inner sizes differ")
     return _proj("qalg_forward", X, W, tau, q, Y, (M, N), ws, flags, stream, M, K, N)
+
+
+def qalg_forward_graph(X, W, tau, q: int, adjacency, Y=None, ws=None, flags: int = 0, stream=None):
+    """Y = X *_{Q_G} W under a graph law: adjacency is an int64 device tensor of q out-edge masks."""
+    torch = _torch()
+    M, K = X.shape
+    K2, N = W.shape
+    if K2 != K:
+        raise ValueError("X and W inner sizes differ")
+    if adjacency.dtype != torch.int64 or adjacency.numel() != q:
+        raise ValueError("adjacency must be int64 with q elements")
+    _tau_check(tau, M)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    if ws is None:
+        ws = workspace(q, M, device=X.device)
+    _check("qalg_forward_graph", lib().qalg_forward_graph(
+        _dev_ptr(X, "X"), _dev_ptr(W, "W"), _dev_ptr(tau, "tau"), q, _dev_ptr(adjacency, "adjacency"), M, K, N,
+        _dev_ptr(Y, "Y"), _dtype_code(X), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags,
+        _stream(stream)))
+    return Y
 
 
 def qalg_backward_dx(dY, W, tau, q: int, dX=None, ws=None, flags: int = 0, stream=None):

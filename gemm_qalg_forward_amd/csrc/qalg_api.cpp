@@ -266,6 +266,47 @@ qalg_status qalg_forward(const void* X, const void* W, const int32_t* tau, int32
   return run_projection(Op::Fwd, 1, X, W, tau, q, M, K, N, Y, dtype, ws, ws_bytes, flags, stream);
 }
 
+qalg_status qalg_forward_graph(const void* X, const void* W, const int32_t* tau, int32_t q,
+                               const uint64_t* adjacency, int64_t M, int64_t K, int64_t N, void* Y,
+                               int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags, void* stream) {
+  if (dtype != QALG_BF16) return QALG_ERR_DTYPE;
+  if (flags & ~uint32_t(QALG_FLAG_INDEX_READY)) return QALG_ERR_ARG;
+  if (M < 0 || K <= 0 || N <= 0 || M > INT32_MAX / 2 || K > INT32_MAX / 2 || N > INT32_MAX / 2) return QALG_ERR_DIM;
+  if (q < 1 || q > 64 || K % q || N % q) return QALG_ERR_Q;
+  if (M == 0) return QALG_OK;
+  if (X == nullptr || W == nullptr || tau == nullptr || adjacency == nullptr || Y == nullptr) return QALG_ERR_NULL;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y) || (reinterpret_cast<uintptr_t>(tau) & 3u) ||
+      (reinterpret_cast<uintptr_t>(adjacency) & 7u))
+    return QALG_ERR_ALIGN;
+  qalg_status st = check_ws(1, q, M, ws, ws_bytes);
+  if (st != QALG_OK) return st;
+  ProblemDesc p{};
+  p.op = Op::Fwd;
+  p.A = X;
+  p.B = W;
+  p.C = Y;
+  p.tau = tau;
+  p.q = q;
+  p.M = M;
+  p.K = K;
+  p.N = N;
+  p.E = 1;
+  p.graph_adj = adjacency;
+  if (!qalg::fwd_persistent_shape_ok(p)) {
+    const int64_t lim = int64_t(1) << 31;
+    return (M * K >= lim || K * N >= lim || M * N >= lim) ? QALG_ERR_DIM : QALG_ERR_ALIGN;
+  }
+  int32_t* wsi = static_cast<int32_t*>(ws);
+  p.ws = wsi;
+  p.ws_stride = ws_stride_ints(q, M);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!(flags & QALG_FLAG_INDEX_READY)) {
+    if (qalg::launch_build_index(tau, q, M, 1, wsi, p.ws_stride, s) != hipSuccess) return QALG_ERR_HIP;
+  }
+  if (qalg::launch_graph_zero_bf16(tau, adjacency, q, M, N, Y, s) != hipSuccess) return QALG_ERR_HIP;
+  return hip_status(qalg::launch_fwd_persistent_bf16(p, s));
+}
+
 qalg_status qalg_backward_dx(const void* dY, const void* W, const int32_t* tau, int32_t q,
                              int64_t M, int64_t K, int64_t N, void* dX, int32_t dtype, void* ws,
                              size_t ws_bytes, uint32_t flags, void* stream) {

@@ -135,6 +135,7 @@ struct FwdArgs {
   int kts;     // k-steps per contraction segment (s / kBK)
   int out_n;   // columns of an output row (N; N / 2 for the gated epilogue)
   int L;       // 0: the complete-graph law Q_q; L >= 1: the recursive law Q_2^(x)L (q = 2^L)
+  const uint64_t* adj;  // graph law Q_G (complete-law kernels): out-edges of each type; null for Q_q
 };
 
 // One output tile, decoded from its position in the tile order.
@@ -271,6 +272,14 @@ __device__ __forceinline__ Tile decode_tile(const FwdArgs& a, const IX& ix, int 
     t.seg0 = i * a.s;
     t.seg1 = j * a.s;
     t.nk = uni((j == i) ? a.kts : 2 * a.kts);
+    if (a.adj != nullptr && j != i) {
+      // graph law Q_G: without the edge (i, j) the output block has no term
+      // (eq 9: edge * edge and unmatched slots vanish); its zeros are written
+      // before the launch, and the tile does no work
+      const cint_ptr e = to_const(reinterpret_cast<const int32_t*>(a.adj));
+      const int word = uni(e[2 * i + (j >> 5)]);
+      if (!((word >> (j & 31)) & 1)) t.nk = 0;
+    }
   }
   return t;
 }
@@ -326,7 +335,17 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   dcomp = dcopy;
   int l_long;  // class of the copy cursor's next tile
   int l_idx;
-  if (!dcopy.next(&l_long, &l_idx)) return;
+  // the next tile with work (graph-law tiles of absent edges have none and are
+  // skipped by both cursors alike)
+  auto next_work = [&](Deal& d, int* cls, int* idx, Tile* t) -> bool {
+    for (;;) {
+      if (!d.next(cls, idx)) return false;
+      *t = decode_tile<C, TENSOR>(a, ix, n_rt, *cls, uni(*idx));
+      if (t->nk > 0) return true;
+    }
+  };
+  Tile lt0;
+  if (!next_work(dcopy, &l_long, &l_idx, &lt0)) return;
 
   const uint32_t n_bytes = uint32_t(a.N) * 2u;      // bytes per weight row
   const uint32_t y_bytes = uint32_t(a.out_n) * 2u;  // bytes per output row
@@ -375,10 +394,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
 
   // copy cursor: tile lt at k-step lk; the tile after it is decoded ahead so
   // that a listed schedule's row ids are fetched a whole tile before use
-  Tile lt = decode_tile<C, TENSOR>(a, ix, n_rt, l_long, uni(l_idx));
+  Tile lt = lt0;
   int lk = 0;
-  bool have_next = dcopy.next(&l_long, &l_idx);
-  Tile nt = have_next ? decode_tile<C, TENSOR>(a, ix, n_rt, l_long, uni(l_idx)) : lt;
+  Tile nt = lt;
+  bool have_next = next_work(dcopy, &l_long, &l_idx, &nt);
+  if (!have_next) nt = lt;
   prefetch_rows(lt);
   take_rows();
   if (have_next) prefetch_rows(nt);
@@ -432,11 +452,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
       lseg = 0;
       lcol = lt.seg0;
       take_rows();
-      have_next = dcopy.next(&l_long, &l_idx);
-      if (have_next) {
-        nt = decode_tile<C, TENSOR>(a, ix, n_rt, l_long, uni(l_idx));
-        prefetch_rows(nt);
-      }
+      have_next = next_work(dcopy, &l_long, &l_idx, &nt);
+      if (have_next) prefetch_rows(nt);
       return;
     }
     if (more && (lk = uni(lk + 1)) >= lt.nk) {
@@ -447,11 +464,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
         lt = nt;
         lk = 0;
         take_rows();
-        have_next = dcopy.next(&l_long, &l_idx);
-        if (have_next) {
-          nt = decode_tile<C, TENSOR>(a, ix, n_rt, l_long, uni(l_idx));
-          prefetch_rows(nt);
-        }
+        have_next = next_work(dcopy, &l_long, &l_idx, &nt);
+        if (have_next) prefetch_rows(nt);
       }
     }
   };
@@ -548,8 +562,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
 
   int c_long;
   int c_idx;
-  dcomp.next(&c_long, &c_idx);
-  Tile ct = decode_tile<C, TENSOR>(a, ix, n_rt, c_long, uni(c_idx));
+  Tile ct = lt0;
+  next_work(dcomp, &c_long, &c_idx, &ct);
   int stage = 0;  // LDS stage of the current k-step (k-step mod 2)
   static_assert(C::FM + C::FN <= C::FM * C::FN, "fragment reads fit a quarter step");
   // one quarter step: MFMAs on fragments (fa, fb) of quarter ks, each followed
@@ -668,8 +682,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
         }
       }
     }
-    if (!dcomp.next(&c_long, &c_idx)) break;
-    ct = decode_tile<C, TENSOR>(a, ix, n_rt, c_long, uni(c_idx));
+    if (!next_work(dcomp, &c_long, &c_idx, &ct)) break;
   }
   // the repeated copies past the last k-step land in LDS: drain them before
   // the workgroup's LDS can be handed to another workgroup
@@ -746,6 +759,7 @@ hipError_t launch_fwd(const ProblemDesc& p, hipStream_t s) {
   a.kts = a.s / kBK;
   a.out_n = C::GATED ? a.N / 2 : a.N;
   a.L = p.law_L;
+  a.adj = p.graph_adj;
   a.cpg = a.r / C::BN;
   a.n_ct = p.q * a.cpg;
   const int64_t max_tiles = ((p.M + C::BM - 1) / C::BM + p.q - 1) * int64_t(a.n_ct);
@@ -814,6 +828,37 @@ __global__ void merge_gate_up_kernel(const uint16_t* Wg, const uint16_t* Wu, uin
 }
 
 }  // namespace
+
+namespace {
+
+// Graph law: zero the output blocks (rows of type i, columns of group j != i)
+// that no edge (i, j) reaches.  One thread per 16-byte piece of an output row.
+__global__ __launch_bounds__(256) void graph_zero_kernel(const int32_t* __restrict__ tau,
+                                                         const uint64_t* __restrict__ adj, int q, int64_t M,
+                                                         int out_n, int r, uint16_t* __restrict__ Y) {
+  const int pc = blockIdx.x * 256 + threadIdx.x;
+  if (pc * 8 >= out_n) return;
+  const int j = (pc * 8) / r;
+  for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+    const int i = tau[m];
+    if (i < 0 || i >= q || i == j || ((adj[i] >> j) & 1ull)) continue;
+    *reinterpret_cast<u32x4*>(Y + m * out_n + pc * 8) = (u32x4){0u, 0u, 0u, 0u};
+  }
+}
+
+}  // namespace
+
+hipError_t launch_graph_zero_bf16(const int32_t* tau, const uint64_t* adj, int q, int64_t M, int64_t out_n,
+                                  void* Y, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int64_t bx = (out_n / 8 + 255) / 256;
+  int64_t by = (2048 + bx - 1) / bx;
+  if (by > M) by = M;
+  if (by > 65535) by = 65535;
+  hipLaunchKernelGGL(graph_zero_kernel, dim3(unsigned(bx), unsigned(by)), dim3(256), 0, s, tau, adj, q, M,
+                     int(out_n), int(out_n / q), static_cast<uint16_t*>(Y));
+  return hipGetLastError();
+}
 
 hipError_t launch_merge_gate_up_bf16(const void* Wg, const void* Wu, void* Wgu, int64_t K, int64_t F, int q,
                                      hipStream_t s) {

@@ -77,6 +77,7 @@ struct ProblemDesc {
   int E;              // problems (experts); operands packed back to back
   int law_L = 0;      // 0: the complete-graph law Q_q; L >= 1: the recursive law Q_2^(x)L, q = 2^L
   void* dw_part = nullptr;  // dW on the register-staged path: fp32 scratch for a split contraction
+  const uint64_t* graph_adj = nullptr;  // graph law Q_G: per-type out-edge masks (device; q <= 64)
 };
 
 // dW's split contraction (register-staged path): at most this many partial tiles per output tile
@@ -99,6 +100,9 @@ int fwd_tile_height(const ProblemDesc& p, int forced_bm);
 // Gated (SwiGLU gate/up) forward over a merged bank; p.N is the merged width 2F.
 bool fwd_gated_supported(const ProblemDesc& p);
 hipError_t launch_fwd_gated_bf16(const ProblemDesc& p, hipStream_t s);
+// graph law: zero the output blocks of absent edges (before the forward)
+hipError_t launch_graph_zero_bf16(const int32_t* tau, const uint64_t* adj, int q, int64_t M, int64_t out_n,
+                                  void* Y, hipStream_t s);
 hipError_t launch_merge_gate_up_bf16(const void* Wg, const void* Wu, void* Wgu, int64_t K, int64_t F, int q,
                                      hipStream_t s);
 // pointwise SwiGLU pieces on the merged gate/up layout (qalg_act.hip)

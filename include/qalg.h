@@ -194,6 +194,24 @@ qalg_status qalg_forward(const void* X, const void* W, const int32_t* tau, int32
                          uint32_t flags, void* stream);
 
 /*
+ * Forward projection under a graph law Q_G (section 3.1, eq 9-12): the slots
+ * of the algebra are the vertices (i, i) and the directed edges (i, j) of a
+ * graph on the q groups; a product of two slots vanishes unless the inner
+ * indices meet and one factor is a vertex.  A row of type i then gets
+ * y_i = x_i W_ii, y_j = x_i W_ij + x_j W_jj for every edge (i, j), and y_j = 0
+ * for every other j (eq 27 with B(i, j) = {i, j} on edges, empty off them).
+ * The complete graph is Q_q (qalg_forward).  adjacency: q device uint64 masks,
+ * caller-owned; bit j of adjacency[i] set iff the edge (i, j) exists (bit i
+ * ignored).  q <= 64 (QALG_ERR_Q).  bf16, the persistent forward's shapes:
+ * K / q a multiple of 64, N / q of 128 (QALG_ERR_ALIGN).  Flags:
+ * QALG_FLAG_INDEX_READY only.  The output blocks of absent edges are zeroed
+ * by a pass before the projection.
+ */
+qalg_status qalg_forward_graph(const void* X, const void* W, const int32_t* tau, int32_t q,
+                               const uint64_t* adjacency, int64_t M, int64_t K, int64_t N, void* Y,
+                               int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags, void* stream);
+
+/*
  * Activation gradient (appendix B, eq 31-32): for a row of type i,
  *   dx_i = sum_j dy_j W_ij^T  and  dx_j = dy_j W_jj^T  (j != i).
  * dY: M x N, W: K x N, dX: M x K (overwritten).

@@ -323,6 +323,27 @@ def pin_masked_dense(O, seed=19):
             np.testing.assert_allclose(Y[m], want, rtol=1e-12, atol=1e-13)
 
 
+def pin_graph_masked_dense(O, seed=41):
+    """Q_G rows by plain matmul (section 3.1, eq 10-11): a type-i row sees block (i, i), and for
+    each edge (i, b) the blocks (i, b) and (b, b); every other block of W is masked to zero."""
+    g = _rng(seed)
+    for q, M, s, r in ((3, 11, 2, 3), (4, 15, 3, 2), (5, 12, 1, 2)):
+        X = g.standard_normal((M, q * s))
+        W = g.standard_normal((q * s, q * r))
+        tau = g.integers(0, q, size=M)
+        edges = [(a, b) for a in range(q) for b in range(q) if a != b and g.random() < 0.5]
+        Y = O.row_typed_forward(X, W, tau, q, edges=edges)
+        for m in range(M):
+            i = int(tau[m])
+            T = np.zeros_like(W)
+            T[i * s:(i + 1) * s, i * r:(i + 1) * r] = W[i * s:(i + 1) * s, i * r:(i + 1) * r]
+            for b in range(q):
+                if (i, b) in edges:
+                    T[i * s:(i + 1) * s, b * r:(b + 1) * r] = W[i * s:(i + 1) * s, b * r:(b + 1) * r]
+                    T[b * s:(b + 1) * s, b * r:(b + 1) * r] = W[b * s:(b + 1) * s, b * r:(b + 1) * r]
+            np.testing.assert_allclose(Y[m], X[m] @ T, rtol=1e-12, atol=1e-13)
+
+
 def pin_row_typed_is_square_rows(O, seed=20):
     """Rows grouped by type form the square form's block rows (section 1: one row of the table per token)."""
     g = _rng(seed)
@@ -830,7 +851,7 @@ ALL_PINS = [
     pin_q2_table, pin_q2_scalar_example, pin_eq3_rectangular_blocks, pin_eq13_14,
     pin_product_counts, pin_graph_counts, pin_appendix_a, pin_associativity,
     pin_row_typed_composition, pin_unit_laws, pin_brute_force, pin_teaching_matrix,
-    pin_masked_dense, pin_row_typed_is_square_rows, pin_q1_is_matmul, pin_block_diagonal,
+    pin_masked_dense, pin_graph_masked_dense, pin_row_typed_is_square_rows, pin_q1_is_matmul, pin_block_diagonal,
     pin_coverage, pin_vjp_scalar_eq31_35, pin_vjp_autograd, pin_vjp_adjoint,
     pin_mac_count, pin_type_index, pin_type_schedule, pin_silu_values, pin_gated_masked_dense,
     pin_silu_grad, pin_gated_ffn_autograd, pin_tensor_counts, pin_tensor_support,

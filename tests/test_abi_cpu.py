@@ -240,3 +240,17 @@ def test_attention_argument_errors_are_synchronous(lib):
     assert at(Qp=None) == 1
     assert at(O=FAKE + 4) == 4
     assert at(S=0, Qp=None) == 0   # no positions: nothing to do
+
+
+def test_graph_forward_argument_errors_are_synchronous(lib):
+    g = lambda **k: lib.qalg_forward_graph(FAKE, FAKE, FAKE, k.get("q", 4), k.get("adj", FAKE), k.get("M", 64),  # noqa: E731
+                                           k.get("K", 256), k.get("N", 512), k.get("Y", FAKE), k.get("dt", 1),
+                                           FAKE, 1 << 20, k.get("flags", 0), None)
+    assert g(dt=0) == 5
+    assert g(flags=Q.QALG_FLAG_LAW_TENSOR) == 8
+    assert g(q=65, K=65 * 64, N=65 * 128) == 3     # at most 64 groups (one mask word per type)
+    assert g(q=3) == 3                            # 3 divides neither 256 nor 512
+    assert g(adj=None) == 1
+    assert g(adj=FAKE + 4) == 4                   # masks are 8-byte words
+    assert g(K=128) == 4                          # K / q = 32: not a multiple of 64
+    assert g(M=0, adj=None) == 0
