@@ -18,8 +18,11 @@ Reported (one JSON line):
   roofline         the forward GEMM kernel against the bf16 MFMA peak, its
                    launch time taken with HIP events on the launch stream
   cpu_baseline     the fp64 CPU oracle on the host cores (a bounded sample)
-  extra            training leg (forward + dX + dW at the same shape) and the
-                   small-M decode leg (64 experts), each timed separately
+  extra            further legs, each timed separately: training (forward + dX +
+                   dW at the same shape), small-M decode (64 experts), gated
+                   SwiGLU FFN (forward and training step), the pilot FFN under
+                   Q_2^(x)2 / Q_4 / q = 1, few rows per type (q = 32), algebraic
+                   attention, and the graph law Q_G (forward, dX, dW)
 """
 from __future__ import annotations
 
@@ -174,6 +177,7 @@ def main() -> int:
         extra["pilot_ffn"] = pilot_leg(Q, torch, np, synth, dev, stream)
         extra["few_rows"] = few_rows_leg(Q, torch, np, synth, dev, stream)
         extra["attention"] = attention_leg(Q, torch, np, synth, dev, stream)
+        extra["graph_law"] = graph_leg(Q, torch, np, synth, dev, stream)
 
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib << 20
@@ -282,6 +286,56 @@ def training_leg(Q, torch, np, synth, dev, stream):
     res["step_ms"] = round(tot, 4)
     res["step_tflops"] = round(3 * flop / (tot * 1e-3) / 1e12, 1)
     log(f"[bench] training leg: {res}")
+    return res
+
+
+def graph_leg(Q, torch, np, synth, dev, stream):
+    """Graph law Q_G (section 3.1) at (4096, 12288), q = 8, M = 16384: forward, dX and dW on a seeded
+    random digraph (each of the 56 edges kept with probability 1/2)."""
+    c = 9
+    X = synth.normal_operand(1000 * c + 1, (M, D), 1.0, "bf16")
+    W = synth.normal_operand(1000 * c + 2, (D, F), D ** -0.5, "bf16")
+    dY = synth.normal_operand(1000 * c + 3, (M, F), 1.0, "bf16")
+    g = np.random.Generator(np.random.PCG64(1000 * c + 4))
+    edges = [(a, b) for a in range(QQ) for b in range(QQ) if a != b and g.random() < 0.5]
+    masks = [0] * QQ
+    for a, b in edges:
+        masks[a] |= 1 << b
+    adj = torch.tensor(masks, dtype=torch.int64, device=dev)
+    to = lambda op: torch.from_numpy(op.bits.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    Xd, Wd, dYd = to(X), to(W), to(dY)
+    tau = torch.from_numpy((np.arange(M) % QQ).astype(np.int32)).to(dev)
+    ws = Q.workspace(QQ, M, device=dev, dw_shape=(D, F))
+    Y = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    dW = torch.empty(D, F, dtype=torch.bfloat16, device=dev)
+    Q.qalg_build_index(tau, QQ, ws=ws, stream=stream)
+    r = Q.QALG_FLAG_INDEX_READY
+    ops = {
+        "fwd": lambda: Q.qalg_forward_graph(Xd, Wd, tau, QQ, adj, Y=Y, ws=ws, flags=r, stream=stream),
+        "dx": lambda: Q.qalg_backward_dx_graph(dYd, Wd, tau, QQ, adj, dX=dX, ws=ws, flags=r, stream=stream),
+        "dw": lambda: Q.qalg_backward_dw_graph(Xd, dYd, tau, QQ, adj, dW=dW, ws=ws, flags=r, stream=stream),
+    }
+    # a type-i row multiplies 1 + 2 outdeg(i) blocks of s x r (eq 10-11)
+    blocks = sum(1 + 2 * bin(masks[i]).count("1") for i in range(QQ))
+    flop = 2.0 * (M // QQ) * (D // QQ) * (F // QQ) * blocks
+    res = {"workload": "graph_law_D4096_F12288_q8_M16384_random_half", "edges": len(edges),
+           "per_op_flop": flop, "fraction_of_dense": round(blocks / QQ ** 3, 4)}
+    for name, fn in ops.items():
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 5
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n
+        res[f"{name}_ms"] = round(ms, 4)
+        res[f"{name}_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+    log(f"[bench] graph-law leg: {res}")
     return res
 
 

@@ -7,6 +7,7 @@ tensor is not on the GPU, the call raises.
 
 Functions carry the C names:
     qalg_forward, qalg_forward_graph, qalg_backward_dx, qalg_backward_dw, qalg_forward_batched,
+    qalg_backward_dx_graph, qalg_backward_dw_graph,
     qalg_gated_forward, qalg_merge_gate_up, qalg_split_gate_up, qalg_swiglu_forward, qalg_swiglu_backward,
     qalg_attention_forward,
     qalg_type_schedule, qalg_build_index, qalg_build_index_batched,
@@ -26,6 +27,7 @@ __all__ = [
     "qalg_version", "qalg_status_string", "qalg_workspace_bytes", "qalg_workspace_bytes_dw", "qalg_index_layout",
     "qalg_type_schedule", "qalg_build_index", "qalg_build_index_batched",
     "qalg_forward", "qalg_forward_graph", "qalg_backward_dx", "qalg_backward_dw", "qalg_forward_batched",
+    "qalg_backward_dx_graph", "qalg_backward_dw_graph",
     "qalg_gated_forward", "qalg_merge_gate_up", "qalg_split_gate_up", "qalg_swiglu_forward",
     "qalg_swiglu_backward", "qalg_attention_forward", "qalg_read_status", "workspace",
 ]
@@ -65,6 +67,10 @@ _SIGS = {
     "qalg_forward": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
     "qalg_forward_graph": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size,
                                           _c_u32, _vp]),
+    "qalg_backward_dx_graph": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size,
+                                              _c_u32, _vp]),
+    "qalg_backward_dw_graph": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size,
+                                              _c_u32, _vp]),
     "qalg_backward_dx": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
     "qalg_backward_dw": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
     "qalg_forward_batched": (ctypes.c_int, [_c_i32, _vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
@@ -237,6 +243,12 @@ def qalg_forward(X, W, tau, q: int, Y=None, ws=None, flags: int = 0, stream=None
     return _proj("qalg_forward", X, W, tau, q, Y, (M, N), ws, flags, stream, M, K, N)
 
 
+def _adjacency_check(adjacency, q: int) -> None:
+    torch = _torch()
+    if adjacency.dtype != torch.int64 or adjacency.numel() != q:
+        raise ValueError("adjacency must be int64 with q elements")
+
+
 def qalg_forward_graph(X, W, tau, q: int, adjacency, Y=None, ws=None, flags: int = 0, stream=None):
     """Y = X *_{Q_G} W under a graph law: adjacency is an int64 device tensor of q out-edge masks."""
     torch = _torch()
@@ -244,8 +256,7 @@ def qalg_forward_graph(X, W, tau, q: int, adjacency, Y=None, ws=None, flags: int
     K2, N = W.shape
     if K2 != K:
         raise ValueError("X and W inner sizes differ")
-    if adjacency.dtype != torch.int64 or adjacency.numel() != q:
-        raise ValueError("adjacency must be int64 with q elements")
+    _adjacency_check(adjacency, q)
     _tau_check(tau, M)
     if Y is None:
         Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
@@ -256,6 +267,46 @@ def qalg_forward_graph(X, W, tau, q: int, adjacency, Y=None, ws=None, flags: int
         _dev_ptr(Y, "Y"), _dtype_code(X), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags,
         _stream(stream)))
     return Y
+
+
+def qalg_backward_dx_graph(dY, W, tau, q: int, adjacency, dX=None, ws=None, flags: int = 0, stream=None):
+    """dX of the graph-law projection: dY [M, N], W [K, N] -> dX [M, K]."""
+    torch = _torch()
+    M, N = dY.shape
+    K, N2 = W.shape
+    if N2 != N:
+        raise ValueError("dY and W widths differ")
+    _adjacency_check(adjacency, q)
+    _tau_check(tau, M)
+    if dX is None:
+        dX = torch.empty((M, K), dtype=dY.dtype, device=dY.device)
+    if ws is None:
+        ws = workspace(q, M, device=dY.device)
+    _check("qalg_backward_dx_graph", lib().qalg_backward_dx_graph(
+        _dev_ptr(dY, "dY"), _dev_ptr(W, "W"), _dev_ptr(tau, "tau"), q, _dev_ptr(adjacency, "adjacency"), M, K, N,
+        _dev_ptr(dX, "dX"), _dtype_code(dY), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags,
+        _stream(stream)))
+    return dX
+
+
+def qalg_backward_dw_graph(X, dY, tau, q: int, adjacency, dW=None, ws=None, flags: int = 0, stream=None):
+    """dW of the graph-law projection: X [M, K], dY [M, N] -> dW [K, N]."""
+    torch = _torch()
+    M, K = X.shape
+    M2, N = dY.shape
+    if M2 != M:
+        raise ValueError("X and dY row counts differ")
+    _adjacency_check(adjacency, q)
+    _tau_check(tau, M)
+    if dW is None:
+        dW = torch.empty((K, N), dtype=X.dtype, device=X.device)
+    if ws is None:
+        ws = workspace(q, M, device=X.device)
+    _check("qalg_backward_dw_graph", lib().qalg_backward_dw_graph(
+        _dev_ptr(X, "X"), _dev_ptr(dY, "dY"), _dev_ptr(tau, "tau"), q, _dev_ptr(adjacency, "adjacency"), M, K, N,
+        _dev_ptr(dW, "dW"), _dtype_code(X), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags,
+        _stream(stream)))
+    return dW
 
 
 def qalg_backward_dx(dY, W, tau, q: int, dX=None, ws=None, flags: int = 0, stream=None):

@@ -184,6 +184,70 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
   return hip_status(e);
 }
 
+// Shared driver of the graph-law entry points (bf16, q <= 64, one 64-bit
+// out-edge mask per type).  The forward takes the persistent kernel where its
+// shapes allow (absent-edge blocks zeroed by a pass first); every other case
+// runs the register-staged kernels, whose tiles of absent edges store zeros.
+qalg_status run_graph(Op op, const void* A, const void* B, const int32_t* tau, int32_t q, const uint64_t* adj,
+                      int64_t M, int64_t K, int64_t N, void* C, int32_t dtype, void* ws, size_t ws_bytes,
+                      uint32_t flags, void* stream) {
+  if (dtype != QALG_BF16) return QALG_ERR_DTYPE;
+  if (flags & ~uint32_t(QALG_FLAG_INDEX_READY)) return QALG_ERR_ARG;
+  if (M < 0 || K <= 0 || N <= 0 || M > INT32_MAX / 2 || K > INT32_MAX / 2 || N > INT32_MAX / 2) return QALG_ERR_DIM;
+  const int64_t lim = int64_t(1) << 31;
+  if (M * K >= lim || K * N >= lim || M * N >= lim) return QALG_ERR_DIM;
+  if (q < 1 || q > 64 || K % q || N % q) return QALG_ERR_Q;
+  if ((K / q) % 8 || (N / q) % 8) return QALG_ERR_ALIGN;
+  if (M > 0 && (A == nullptr || B == nullptr || C == nullptr || tau == nullptr || adj == nullptr))
+    return QALG_ERR_NULL;
+  if (M == 0 && op == Op::Dw && C == nullptr) return QALG_ERR_NULL;
+  if ((A && !aligned16(A)) || (B && !aligned16(B)) || (C && !aligned16(C)) ||
+      (tau && (reinterpret_cast<uintptr_t>(tau) & 3u)) || (adj && (reinterpret_cast<uintptr_t>(adj) & 7u)))
+    return QALG_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M == 0) {
+    if (op != Op::Dw) return QALG_OK;
+    return hip_status(qalg::launch_fill_zero(C, size_t(K) * size_t(N) * 2, s));
+  }
+  qalg_status st = check_ws(1, q, M, ws, ws_bytes);
+  if (st != QALG_OK) return st;
+  ProblemDesc p{};
+  p.op = op;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.tau = tau;
+  p.q = q;
+  p.M = M;
+  p.K = K;
+  p.N = N;
+  p.E = 1;
+  p.graph_adj = adj;
+  if (op == Op::Dw && ws_bytes >= qalg_workspace_bytes_dw(q, M, K, N))
+    p.dw_part = static_cast<char*>(ws) + qalg_workspace_bytes(q, M);
+  int32_t* wsi = static_cast<int32_t*>(ws);
+  p.ws = wsi;
+  p.ws_stride = ws_stride_ints(q, M);
+  const bool ready = (flags & QALG_FLAG_INDEX_READY) != 0;
+  if (op == Op::Fwd && qalg::fwd_persistent_shape_ok(p)) {
+    if (!ready && qalg::launch_build_index(tau, q, M, 1, wsi, p.ws_stride, s) != hipSuccess) return QALG_ERR_HIP;
+    if (qalg::launch_graph_zero_bf16(tau, adj, q, M, N, C, s) != hipSuccess) return QALG_ERR_HIP;
+    return hip_status(qalg::launch_fwd_persistent_bf16(p, s));
+  }
+  // rows of an out-of-range type get zero Y / dX rows; dW ignores them
+  void* zero_out = op == Op::Dw ? nullptr : C;
+  const int64_t zero_ld = op == Op::Fwd ? N : K;
+  hipError_t e;
+  if (!ready)
+    e = qalg::launch_build_index_zeroing(tau, q, M, 1, wsi, p.ws_stride, zero_out, zero_ld, 2, M * zero_ld * 2, s);
+  else if (zero_out != nullptr)
+    e = qalg::launch_zero_bad_rows(wsi, q, M, 1, p.ws_stride, zero_out, zero_ld, 2, M * zero_ld * 2, s);
+  else
+    e = hipSuccess;
+  if (e != hipSuccess) return QALG_ERR_HIP;
+  return hip_status(qalg::launch_tiled_bf16(p, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -269,42 +333,19 @@ qalg_status qalg_forward(const void* X, const void* W, const int32_t* tau, int32
 qalg_status qalg_forward_graph(const void* X, const void* W, const int32_t* tau, int32_t q,
                                const uint64_t* adjacency, int64_t M, int64_t K, int64_t N, void* Y,
                                int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags, void* stream) {
-  if (dtype != QALG_BF16) return QALG_ERR_DTYPE;
-  if (flags & ~uint32_t(QALG_FLAG_INDEX_READY)) return QALG_ERR_ARG;
-  if (M < 0 || K <= 0 || N <= 0 || M > INT32_MAX / 2 || K > INT32_MAX / 2 || N > INT32_MAX / 2) return QALG_ERR_DIM;
-  if (q < 1 || q > 64 || K % q || N % q) return QALG_ERR_Q;
-  if (M == 0) return QALG_OK;
-  if (X == nullptr || W == nullptr || tau == nullptr || adjacency == nullptr || Y == nullptr) return QALG_ERR_NULL;
-  if (!aligned16(X) || !aligned16(W) || !aligned16(Y) || (reinterpret_cast<uintptr_t>(tau) & 3u) ||
-      (reinterpret_cast<uintptr_t>(adjacency) & 7u))
-    return QALG_ERR_ALIGN;
-  qalg_status st = check_ws(1, q, M, ws, ws_bytes);
-  if (st != QALG_OK) return st;
-  ProblemDesc p{};
-  p.op = Op::Fwd;
-  p.A = X;
-  p.B = W;
-  p.C = Y;
-  p.tau = tau;
-  p.q = q;
-  p.M = M;
-  p.K = K;
-  p.N = N;
-  p.E = 1;
-  p.graph_adj = adjacency;
-  if (!qalg::fwd_persistent_shape_ok(p)) {
-    const int64_t lim = int64_t(1) << 31;
-    return (M * K >= lim || K * N >= lim || M * N >= lim) ? QALG_ERR_DIM : QALG_ERR_ALIGN;
-  }
-  int32_t* wsi = static_cast<int32_t*>(ws);
-  p.ws = wsi;
-  p.ws_stride = ws_stride_ints(q, M);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!(flags & QALG_FLAG_INDEX_READY)) {
-    if (qalg::launch_build_index(tau, q, M, 1, wsi, p.ws_stride, s) != hipSuccess) return QALG_ERR_HIP;
-  }
-  if (qalg::launch_graph_zero_bf16(tau, adjacency, q, M, N, Y, s) != hipSuccess) return QALG_ERR_HIP;
-  return hip_status(qalg::launch_fwd_persistent_bf16(p, s));
+  return run_graph(Op::Fwd, X, W, tau, q, adjacency, M, K, N, Y, dtype, ws, ws_bytes, flags, stream);
+}
+
+qalg_status qalg_backward_dx_graph(const void* dY, const void* W, const int32_t* tau, int32_t q,
+                                   const uint64_t* adjacency, int64_t M, int64_t K, int64_t N, void* dX,
+                                   int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags, void* stream) {
+  return run_graph(Op::Dx, dY, W, tau, q, adjacency, M, K, N, dX, dtype, ws, ws_bytes, flags, stream);
+}
+
+qalg_status qalg_backward_dw_graph(const void* X, const void* dY, const int32_t* tau, int32_t q,
+                                   const uint64_t* adjacency, int64_t M, int64_t K, int64_t N, void* dW,
+                                   int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags, void* stream) {
+  return run_graph(Op::Dw, X, dY, tau, q, adjacency, M, K, N, dW, dtype, ws, ws_bytes, flags, stream);
 }
 
 qalg_status qalg_backward_dx(const void* dY, const void* W, const int32_t* tau, int32_t q,

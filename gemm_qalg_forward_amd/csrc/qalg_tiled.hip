@@ -72,6 +72,7 @@ struct Args {
   int tm_dw, tn_dw;                  // dW: tiles per block along rows / columns
   int skip_cyclic;                   // return at once when the index says the schedule is cyclic
   int L;                             // recursive law Q_2^(x)L (TENSOR kernels); 0 otherwise
+  const uint64_t* adj;               // graph law Q_G (GRAPH kernels): out-edge mask of each type
   float* part;                       // dW split contraction: fp32 partial tiles [splits][K][N]
   int splits;                        // dW: workgroups per output tile (1: no split)
 };
@@ -92,6 +93,20 @@ __device__ __forceinline__ int law_member(int fixed_from, int fixed_mask, int n,
       n >>= 1;
     }
   return g;
+}
+
+// Graph law Q_G (section 3.1, eq 9-12): B(i, i) = {i}, B(i, j) = {i, j} when
+// (i, j) is an edge and empty otherwise.  Transposed for the VJPs:
+//   dX[I_i, g_i] sums over the output groups {i} and the out-neighbours of i;
+//   dX[I_i, g_k] (k != i) is dY[I_i, g_k] W_kk^T on an edge (i, k), else 0;
+//   dW[g_j, g_j] sums over the rows of type j and of the in-neighbours of j;
+//   dW[g_b, g_j] (b != j) sums over the rows of type b on an edge (b, j), else 0.
+__device__ __forceinline__ bool graph_edge(const uint64_t* adj, int i, int j) { return (adj[i] >> j) & 1ull; }
+
+__device__ __forceinline__ uint64_t graph_in_mask(const uint64_t* adj, int q, int j) {
+  uint64_t m = 1ull << j;
+  for (int i = 0; i < q; ++i) m |= ((adj[i] >> j) & 1ull) << i;
+  return m;
 }
 
 __device__ __forceinline__ int swz(int row, int chunk, int kch) {
@@ -133,8 +148,11 @@ __device__ __forceinline__ int find_type(const int32_t* tile_off, int q, int rt)
   return lo;
 }
 
-template <Op OP, class C, bool TENSOR = false>
+constexpr int kLawComplete = 0, kLawTensor = 1, kLawGraph = 2;
+
+template <Op OP, class C, int LAW = kLawComplete>
 __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
+  constexpr bool TENSOR = LAW == kLawTensor, GRAPH = LAW == kLawGraph;
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, KCH = C::KCH, T = C::THREADS;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
 
@@ -192,9 +210,12 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
     seg_len = k_last - k_first;
     segA0 = b * a.s + rm * BM;  // X column of output row 0
     segB0 = n0;                 // dY column of output column 0
-    if constexpr (TENSOR) {
+    if constexpr (TENSOR || GRAPH) {
       tb_b = b;
       tb_j = j;
+    }
+    if constexpr (GRAPH) {
+      if (b != j && !graph_edge(a.adj, b, j)) nseg = 0;  // absent edge: a zero block
     }
   } else {
     const int32_t* tile_off = ws + a.off_tiles + tile_height_slot(BM) * (q + 1);
@@ -213,6 +234,20 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
       nseg = (j == i) ? 1 : 2;
       segA0 = segB0 = i * a.s;   // X columns / W rows of group i
       segA1 = segB1 = j * a.s;   // X columns / W rows of group j
+      if constexpr (GRAPH) {
+        if (j != i && !graph_edge(a.adj, i, j)) nseg = 0;  // absent edge: zero output block
+      }
+    } else if constexpr (GRAPH) {
+      seg_len = a.r;
+      tb_b = j;
+      tb_j = i;
+      if (j == i) {
+        // contraction over the output groups {i} and the out-neighbours of i
+        nseg = __builtin_popcountll(a.adj[i] | (1ull << i));
+      } else {
+        nseg = graph_edge(a.adj, i, j) ? 1 : 0;
+        segA0 = j * a.r;
+      }
     } else if constexpr (TENSOR) {
       // dX column group j of a type-i row: contraction over the output groups
       // agreeing with j where j differs from i, r columns each
@@ -245,6 +280,36 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
     w_lo = offsets[t0];
     w_len = offsets[t0 + 1] - w_lo;
     w_kn = (w_len + BK - 1) / BK;
+  }
+  // graph-law walkers: the member (type for dW, output group for dX) of the
+  // segment the copy steps are in, and the members still to come
+  uint64_t g_rest = 0;
+  int g_cur = 0;
+  if constexpr (GRAPH && OP == Op::Dw) {
+    if (tb_b == tb_j) {
+      // dW block (j, j): the rows of type j and of its in-neighbours
+      const uint64_t mem = graph_in_mask(a.adj, q, tb_j);
+      nseg = __builtin_popcountll(mem);
+      nk = 0;
+      for (uint64_t m = mem; m != 0; m &= m - 1) {
+        const int t = __builtin_ctzll(m);
+        nk += (offsets[t + 1] - offsets[t] + BK - 1) / BK;
+      }
+      g_cur = __builtin_ctzll(mem);
+      g_rest = mem & (mem - 1);
+      w_lo = offsets[g_cur];
+      w_len = offsets[g_cur + 1] - w_lo;
+      w_kn = (w_len + BK - 1) / BK;
+    } else if (nseg > 0) {
+      nk = kts;  // the rows of type b: one segment (krows, seg_len above)
+    }
+  }
+  if constexpr (GRAPH && OP == Op::Dx) {
+    if (tb_b == tb_j) {
+      const uint64_t mem = a.adj[tb_j] | (1ull << tb_j);
+      g_cur = __builtin_ctzll(mem);
+      g_rest = mem & (mem - 1);
+    }
   }
 
   // ---------------- loaders ----------------
@@ -312,6 +377,35 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
     int seg_len = this_seg_len;     // this segment's length
     const int32_t* krows_s = krows;
     int segA0_s = segA0;
+    if constexpr (GRAPH) {
+      if constexpr (OP == Op::Dx) {
+        if (tb_b == tb_j) {  // member groups visited in increasing order as kt grows
+          const int n = kt / kts;
+          while (w_n < n) {
+            g_cur = __builtin_ctzll(g_rest);
+            g_rest &= g_rest - 1;
+            ++w_n;
+          }
+          k0 = (kt - n * kts) * BK;
+          segA0_s = g_cur * a.r;
+          sg = 0;
+        }
+      } else if constexpr (OP == Op::Dw) {
+        if (tb_b == tb_j) {  // diagonal block: the member types' row ranges
+          while (kt >= w_k0 + w_kn && g_rest != 0) {
+            w_k0 += w_kn;
+            g_cur = __builtin_ctzll(g_rest);
+            g_rest &= g_rest - 1;
+            w_lo = offsets[g_cur];
+            w_len = offsets[g_cur + 1] - w_lo;
+            w_kn = (w_len + BK - 1) / BK;
+          }
+          krows_s = rows + w_lo;
+          seg_len = w_len;
+          k0 = (kt - w_k0) * BK;
+        }
+      }
+    }
     if constexpr (TENSOR) {
       if constexpr (OP == Op::Dx) {
         const int n = kt / kts;
@@ -736,15 +830,22 @@ hipError_t launch_cfg(const ProblemDesc& p, hipStream_t s, bool skip_cyclic) {
     a.splits = int(sp);
     a.part = static_cast<float*>(p.dw_part);
   }
+  a.adj = p.graph_adj;
   const dim3 g = grid_for(p, a, C::BM);
   if (g.x == 0) return hipSuccess;
   if constexpr (OP != Op::Fwd) {
     if (p.law_L > 0) {
-      hipLaunchKernelGGL((tiled_bf16_kernel<OP, C, true>), g, dim3(C::THREADS), 0, s, a);
+      hipLaunchKernelGGL((tiled_bf16_kernel<OP, C, kLawTensor>), g, dim3(C::THREADS), 0, s, a);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess || a.splits == 1) return e;
       return launch_dw_reduce(a.part, a.splits, p.K * p.N, static_cast<uint16_t*>(p.C), s);
     }
+  }
+  if (p.graph_adj != nullptr) {
+    hipLaunchKernelGGL((tiled_bf16_kernel<OP, C, kLawGraph>), g, dim3(C::THREADS), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.splits == 1) return e;
+    return launch_dw_reduce(a.part, a.splits, p.K * p.N, static_cast<uint16_t*>(p.C), s);
   }
   hipLaunchKernelGGL((tiled_bf16_kernel<OP, C>), g, dim3(C::THREADS), 0, s, a);
   const hipError_t e = hipGetLastError();

@@ -201,15 +201,38 @@ qalg_status qalg_forward(const void* X, const void* W, const int32_t* tau, int32
  * y_i = x_i W_ii, y_j = x_i W_ij + x_j W_jj for every edge (i, j), and y_j = 0
  * for every other j (eq 27 with B(i, j) = {i, j} on edges, empty off them).
  * The complete graph is Q_q (qalg_forward).  adjacency: q device uint64 masks,
- * caller-owned; bit j of adjacency[i] set iff the edge (i, j) exists (bit i
- * ignored).  q <= 64 (QALG_ERR_Q).  bf16, the persistent forward's shapes:
- * K / q a multiple of 64, N / q of 128 (QALG_ERR_ALIGN).  Flags:
- * QALG_FLAG_INDEX_READY only.  The output blocks of absent edges are zeroed
- * by a pass before the projection.
+ * caller-owned, 8-byte aligned; bit j of adjacency[i] set iff the edge (i, j)
+ * exists (bit i ignored).  q <= 64 (QALG_ERR_Q).  bf16 only (QALG_ERR_DTYPE);
+ * K / q and N / q multiples of 8 (QALG_ERR_ALIGN); M K, K N and M N below
+ * 2^31 (QALG_ERR_DIM).  Flags: QALG_FLAG_INDEX_READY only (QALG_ERR_ARG).
+ * Rows of an out-of-range type get zero rows; output blocks of absent edges
+ * are written as zeros.  Shapes of the persistent forward (K / q a multiple
+ * of 64, N / q of 128) run it; the others run the register-staged kernel.
  */
 qalg_status qalg_forward_graph(const void* X, const void* W, const int32_t* tau, int32_t q,
                                const uint64_t* adjacency, int64_t M, int64_t K, int64_t N, void* Y,
                                int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags, void* stream);
+
+/*
+ * Gradients of the graph-law projection (appendix B's VJPs with the Q_G
+ * supports of section 3.1 transposed).  For a row of type i:
+ *   dx_i = dy_i W_ii^T + sum over edges (i, j) of dy_j W_ij^T,
+ *   dx_k = dy_k W_kk^T on an edge (i, k), and 0 for every other k != i;
+ *   dW_jj sums x_j^T dy_j over the rows of type j and of every type i with an
+ *         edge (i, j); dW_bj (b != j) sums x_b^T dy_j over the rows of type b
+ *         on an edge (b, j), and is 0 off the edges.
+ * Operands, adjacency, errors and flags as in qalg_forward_graph, and as in
+ * qalg_backward_dx / qalg_backward_dw (dX and dW overwritten; rows of an
+ * out-of-range type get zero dX rows and add nothing to dW; a workspace of
+ * qalg_workspace_bytes_dw bytes lets dW split its contraction).  Register-
+ * staged kernels; each output element has one owner (bitwise reproducible).
+ */
+qalg_status qalg_backward_dx_graph(const void* dY, const void* W, const int32_t* tau, int32_t q,
+                                   const uint64_t* adjacency, int64_t M, int64_t K, int64_t N, void* dX,
+                                   int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags, void* stream);
+qalg_status qalg_backward_dw_graph(const void* X, const void* dY, const int32_t* tau, int32_t q,
+                                   const uint64_t* adjacency, int64_t M, int64_t K, int64_t N, void* dW,
+                                   int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags, void* stream);
 
 /*
  * Activation gradient (appendix B, eq 31-32): for a row of type i,

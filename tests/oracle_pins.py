@@ -457,6 +457,37 @@ def pin_vjp_autograd(O, seed=25):
         np.testing.assert_allclose(O.row_typed_forward(Xn, Wn, tau, q), Y.detach().numpy(), rtol=1e-12, atol=1e-12)
 
 
+def _graph_mask(q, s, r, i, edges):
+    """Ones where a type-i row reads W under Q_G (section 3.1, eq 10-11), zeros elsewhere."""
+    T = np.zeros((q * s, q * r))
+    T[i * s:(i + 1) * s, i * r:(i + 1) * r] = 1.0
+    for b in range(q):
+        if (i, b) in edges:
+            T[i * s:(i + 1) * s, b * r:(b + 1) * r] = 1.0
+            T[b * s:(b + 1) * s, b * r:(b + 1) * r] = 1.0
+    return T
+
+
+def pin_graph_vjp_autograd(O, seed=42):
+    """float64 torch autograd of the Q_G masked-dense rows equals the oracle's graph dX and dW."""
+    import torch
+    g = _rng(seed)
+    for q, M, s, r in ((3, 14, 2, 3), (4, 17, 3, 2), (5, 11, 1, 2)):
+        Xn = g.standard_normal((M, q * s))
+        Wn = g.standard_normal((q * s, q * r))
+        dYn = g.standard_normal((M, q * r))
+        tau = g.integers(0, q, size=M)
+        edges = [(a, b) for a in range(q) for b in range(q) if a != b and g.random() < 0.5]
+        X = torch.tensor(Xn, requires_grad=True)
+        W = torch.tensor(Wn, requires_grad=True)
+        Y = torch.cat([X[m:m + 1] @ (W * torch.tensor(_graph_mask(q, s, r, int(tau[m]), edges)))
+                       for m in range(M)])
+        (Y * torch.tensor(dYn)).sum().backward()
+        dX, dW = O.row_typed_backward(Xn, Wn, dYn, tau, q, edges=edges)
+        np.testing.assert_allclose(dX, X.grad.numpy(), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dW, W.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
 def pin_vjp_adjoint(O, seed=26):
     """Bilinearity: <dY, Y> = <dX, X> = <dW, W>; dW blocks with no contributing rows are zero."""
     g = _rng(seed)
@@ -852,7 +883,7 @@ ALL_PINS = [
     pin_product_counts, pin_graph_counts, pin_appendix_a, pin_associativity,
     pin_row_typed_composition, pin_unit_laws, pin_brute_force, pin_teaching_matrix,
     pin_masked_dense, pin_graph_masked_dense, pin_row_typed_is_square_rows, pin_q1_is_matmul, pin_block_diagonal,
-    pin_coverage, pin_vjp_scalar_eq31_35, pin_vjp_autograd, pin_vjp_adjoint,
+    pin_coverage, pin_vjp_scalar_eq31_35, pin_vjp_autograd, pin_graph_vjp_autograd, pin_vjp_adjoint,
     pin_mac_count, pin_type_index, pin_type_schedule, pin_silu_values, pin_gated_masked_dense,
     pin_silu_grad, pin_gated_ffn_autograd, pin_tensor_counts, pin_tensor_support,
     pin_tensor_associativity, pin_tensor_masked_dense, pin_tensor_cost, pin_tensor_vjp_autograd,

@@ -242,15 +242,26 @@ def test_attention_argument_errors_are_synchronous(lib):
     assert at(S=0, Qp=None) == 0   # no positions: nothing to do
 
 
-def test_graph_forward_argument_errors_are_synchronous(lib):
-    g = lambda **k: lib.qalg_forward_graph(FAKE, FAKE, FAKE, k.get("q", 4), k.get("adj", FAKE), k.get("M", 64),  # noqa: E731
-                                           k.get("K", 256), k.get("N", 512), k.get("Y", FAKE), k.get("dt", 1),
-                                           FAKE, 1 << 20, k.get("flags", 0), None)
-    assert g(dt=0) == 5
-    assert g(flags=Q.QALG_FLAG_LAW_TENSOR) == 8
-    assert g(q=65, K=65 * 64, N=65 * 128) == 3     # at most 64 groups (one mask word per type)
-    assert g(q=3) == 3                            # 3 divides neither 256 nor 512
-    assert g(adj=None) == 1
-    assert g(adj=FAKE + 4) == 4                   # masks are 8-byte words
-    assert g(K=128) == 4                          # K / q = 32: not a multiple of 64
-    assert g(M=0, adj=None) == 0
+def test_graph_argument_errors_are_synchronous(lib):
+    """Every graph-law entry point rejects bad arguments before any launch (the pointers are fake)."""
+    for fn in ("qalg_forward_graph", "qalg_backward_dx_graph", "qalg_backward_dw_graph"):
+        f = getattr(lib, fn)
+        g = lambda **k: f(FAKE, FAKE, FAKE, k.get("q", 4), k.get("adj", FAKE), k.get("M", 64),  # noqa: E731
+                          k.get("K", 256), k.get("N", 512), k.get("Y", FAKE), k.get("dt", 1),
+                          k.get("ws", FAKE), k.get("wsb", 1 << 20), k.get("flags", 0), None)
+        assert g(dt=0) == 5, fn
+        assert g(flags=Q.QALG_FLAG_LAW_TENSOR) == 8, fn
+        assert g(flags=Q.QALG_FLAG_FORCE_TILED) == 8, fn
+        assert g(q=65, K=65 * 64, N=65 * 128) == 3, fn   # at most 64 groups (one mask word per type)
+        assert g(q=3) == 3, fn                          # 3 divides neither 256 nor 512
+        assert g(adj=None) == 1, fn
+        assert g(Y=None) == 1, fn
+        assert g(adj=FAKE + 4) == 4, fn                 # masks are 8-byte words
+        assert g(K=48) == 4, fn                         # K / q = 12: not a multiple of 8
+        assert g(M=1 << 20, K=1 << 12) == 2, fn         # M K >= 2^31
+        assert g(ws=None) == 1, fn
+        assert g(wsb=16) == 6, fn
+        assert g(M=-1) == 2, fn
+    assert lib.qalg_forward_graph(FAKE, FAKE, FAKE, 4, None, 0, 256, 512, FAKE, 1, FAKE, 0, 0, None) == 0
+    assert lib.qalg_backward_dx_graph(FAKE, FAKE, FAKE, 4, None, 0, 256, 512, FAKE, 1, FAKE, 0, 0, None) == 0
+    assert lib.qalg_backward_dw_graph(FAKE, FAKE, FAKE, 4, None, 0, 256, 512, None, 1, FAKE, 0, 0, None) == 1
