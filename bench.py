@@ -22,7 +22,8 @@ Reported (one JSON line):
                    dW at the same shape), small-M decode (64 experts), gated
                    SwiGLU FFN (forward and training step), the pilot FFN under
                    Q_2^(x)2 / Q_4 / q = 1, few rows per type (q = 32), algebraic
-                   attention, and the graph law Q_G (forward, dX, dW)
+                   attention, the graph law Q_G and unequal group widths (forward,
+                   dX, dW each)
 """
 from __future__ import annotations
 
@@ -178,6 +179,7 @@ def main() -> int:
         extra["few_rows"] = few_rows_leg(Q, torch, np, synth, dev, stream)
         extra["attention"] = attention_leg(Q, torch, np, synth, dev, stream)
         extra["graph_law"] = graph_leg(Q, torch, np, synth, dev, stream)
+        extra["unequal_widths"] = widths_leg(Q, torch, np, synth, dev, stream)
 
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib << 20
@@ -336,6 +338,53 @@ def graph_leg(Q, torch, np, synth, dev, stream):
         res[f"{name}_ms"] = round(ms, 4)
         res[f"{name}_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
     log(f"[bench] graph-law leg: {res}")
+    return res
+
+
+def widths_leg(Q, torch, np, synth, dev, stream):
+    """Unequal group widths (eq 18) at D = 4096 -> F = 12288, q = 4, M = 16384 (cyclic types): input
+    widths 512 / 768 / 1024 / 1792, output widths three times those; forward, dX and dW."""
+    c = 10
+    kw = [512, 768, 1024, 1792]
+    nw = [3 * w for w in kw]
+    q = len(kw)
+    X = synth.normal_operand(1000 * c + 1, (M, D), 1.0, "bf16")
+    W = synth.normal_operand(1000 * c + 2, (D, F), D ** -0.5, "bf16")
+    dY = synth.normal_operand(1000 * c + 3, (M, F), 1.0, "bf16")
+    to = lambda op: torch.from_numpy(op.bits.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    Xd, Wd, dYd = to(X), to(W), to(dY)
+    tau = torch.from_numpy((np.arange(M) % q).astype(np.int32)).to(dev)
+    ws = Q.workspace(q, M, device=dev, dw_shape=(D, F))
+    Y = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    dW = torch.empty(D, F, dtype=torch.bfloat16, device=dev)
+    Q.qalg_build_index(tau, q, ws=ws, stream=stream)
+    r = Q.QALG_FLAG_INDEX_READY
+    ops = {
+        "fwd": lambda: Q.qalg_forward_widths(Xd, Wd, tau, q, kw, nw, Y=Y, ws=ws, flags=r, stream=stream),
+        "dx": lambda: Q.qalg_backward_dx_widths(dYd, Wd, tau, q, kw, nw, dX=dX, ws=ws, flags=r, stream=stream),
+        "dw": lambda: Q.qalg_backward_dw_widths(Xd, dYd, tau, q, kw, nw, dW=dW, ws=ws, flags=r, stream=stream),
+    }
+    # a type-i row: s_i N (its strip) + sum over j != i of s_j r_j (the diagonal blocks), eq 18
+    macs_per_type = [kw[i] * F + sum(kw[j] * nw[j] for j in range(q) if j != i) for i in range(q)]
+    flop = 2.0 * (M // q) * sum(macs_per_type)
+    res = {"workload": "widths_D4096_F12288_q4_M16384_w512_768_1024_1792", "per_op_flop": flop,
+           "fraction_of_dense": round(flop / (2.0 * M * D * F), 4)}
+    for name, fn in ops.items():
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 5
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n
+        res[f"{name}_ms"] = round(ms, 4)
+        res[f"{name}_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+    log(f"[bench] unequal-widths leg: {res}")
     return res
 
 

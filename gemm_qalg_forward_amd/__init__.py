@@ -7,7 +7,8 @@ tensor is not on the GPU, the call raises.
 
 Functions carry the C names:
     qalg_forward, qalg_forward_graph, qalg_backward_dx, qalg_backward_dw, qalg_forward_batched,
-    qalg_backward_dx_graph, qalg_backward_dw_graph,
+    qalg_backward_dx_graph, qalg_backward_dw_graph, qalg_forward_widths, qalg_backward_dx_widths,
+    qalg_backward_dw_widths,
     qalg_gated_forward, qalg_merge_gate_up, qalg_split_gate_up, qalg_swiglu_forward, qalg_swiglu_backward,
     qalg_attention_forward,
     qalg_type_schedule, qalg_build_index, qalg_build_index_batched,
@@ -27,7 +28,8 @@ __all__ = [
     "qalg_version", "qalg_status_string", "qalg_workspace_bytes", "qalg_workspace_bytes_dw", "qalg_index_layout",
     "qalg_type_schedule", "qalg_build_index", "qalg_build_index_batched",
     "qalg_forward", "qalg_forward_graph", "qalg_backward_dx", "qalg_backward_dw", "qalg_forward_batched",
-    "qalg_backward_dx_graph", "qalg_backward_dw_graph",
+    "qalg_backward_dx_graph", "qalg_backward_dw_graph", "qalg_forward_widths", "qalg_backward_dx_widths",
+    "qalg_backward_dw_widths",
     "qalg_gated_forward", "qalg_merge_gate_up", "qalg_split_gate_up", "qalg_swiglu_forward",
     "qalg_swiglu_backward", "qalg_attention_forward", "qalg_read_status", "workspace",
 ]
@@ -71,6 +73,12 @@ _SIGS = {
                                               _c_u32, _vp]),
     "qalg_backward_dw_graph": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size,
                                               _c_u32, _vp]),
+    "qalg_forward_widths": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i64),
+                                           _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
+    "qalg_backward_dx_widths": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i64),
+                                               _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
+    "qalg_backward_dw_widths": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i64),
+                                               _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
     "qalg_backward_dx": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
     "qalg_backward_dw": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
     "qalg_forward_batched": (ctypes.c_int, [_c_i32, _vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
@@ -325,6 +333,72 @@ def qalg_backward_dw(X, dY, tau, q: int, dW=None, ws=None, flags: int = 0, strea
     if M2 != M:
         raise ValueError("X and dY row counts differ")
     return _proj("qalg_backward_dw", X, dY, tau, q, dW, (K, N), ws, flags, stream, M, K, N)
+
+
+def _widths_arg(widths, q: int, total: int, what: str):
+    w = [int(x) for x in widths]
+    if len(w) != q or sum(w) != total:
+        raise ValueError(f"{what} must hold q = {q} widths summing to {total}")
+    return (_c_i64 * q)(*w)
+
+
+def qalg_forward_widths(X, W, tau, q: int, in_widths, out_widths, Y=None, ws=None, flags: int = 0, stream=None):
+    """Y = X *_{Q_q} W on groups of unequal widths (in_widths over K, out_widths over N; host ints)."""
+    torch = _torch()
+    M, K = X.shape
+    K2, N = W.shape
+    if K2 != K:
+        raise ValueError("X and W inner sizes differ")
+    kw, nw = _widths_arg(in_widths, q, K, "in_widths"), _widths_arg(out_widths, q, N, "out_widths")
+    _tau_check(tau, M)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    if ws is None:
+        ws = workspace(q, M, device=X.device)
+    _check("qalg_forward_widths", lib().qalg_forward_widths(
+        _dev_ptr(X, "X"), _dev_ptr(W, "W"), _dev_ptr(tau, "tau"), q, kw, nw, M, K, N, _dev_ptr(Y, "Y"),
+        _dtype_code(X), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags, _stream(stream)))
+    return Y
+
+
+def qalg_backward_dx_widths(dY, W, tau, q: int, in_widths, out_widths, dX=None, ws=None, flags: int = 0,
+                            stream=None):
+    """dX of the unequal-width projection: dY [M, N], W [K, N] -> dX [M, K]."""
+    torch = _torch()
+    M, N = dY.shape
+    K, N2 = W.shape
+    if N2 != N:
+        raise ValueError("dY and W widths differ")
+    kw, nw = _widths_arg(in_widths, q, K, "in_widths"), _widths_arg(out_widths, q, N, "out_widths")
+    _tau_check(tau, M)
+    if dX is None:
+        dX = torch.empty((M, K), dtype=dY.dtype, device=dY.device)
+    if ws is None:
+        ws = workspace(q, M, device=dY.device)
+    _check("qalg_backward_dx_widths", lib().qalg_backward_dx_widths(
+        _dev_ptr(dY, "dY"), _dev_ptr(W, "W"), _dev_ptr(tau, "tau"), q, kw, nw, M, K, N, _dev_ptr(dX, "dX"),
+        _dtype_code(dY), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags, _stream(stream)))
+    return dX
+
+
+def qalg_backward_dw_widths(X, dY, tau, q: int, in_widths, out_widths, dW=None, ws=None, flags: int = 0,
+                            stream=None):
+    """dW of the unequal-width projection: X [M, K], dY [M, N] -> dW [K, N]."""
+    torch = _torch()
+    M, K = X.shape
+    M2, N = dY.shape
+    if M2 != M:
+        raise ValueError("X and dY row counts differ")
+    kw, nw = _widths_arg(in_widths, q, K, "in_widths"), _widths_arg(out_widths, q, N, "out_widths")
+    _tau_check(tau, M)
+    if dW is None:
+        dW = torch.empty((K, N), dtype=X.dtype, device=X.device)
+    if ws is None:
+        ws = workspace(q, M, device=X.device)
+    _check("qalg_backward_dw_widths", lib().qalg_backward_dw_widths(
+        _dev_ptr(X, "X"), _dev_ptr(dY, "dY"), _dev_ptr(tau, "tau"), q, kw, nw, M, K, N, _dev_ptr(dW, "dW"),
+        _dtype_code(X), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags, _stream(stream)))
+    return dW
 
 
 def qalg_merge_gate_up(Wg, Wu, q: int, Wgu=None, stream=None):

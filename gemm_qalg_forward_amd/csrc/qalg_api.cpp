@@ -248,6 +248,70 @@ qalg_status run_graph(Op op, const void* A, const void* B, const int32_t* tau, i
   return hip_status(qalg::launch_tiled_bf16(p, s));
 }
 
+// Shared driver of the unequal-width entry points (the complete-graph law on
+// groups of widths in_widths / out_widths, eq 18; bf16, q <= 64): index, zero
+// rows of out-of-range types, then the register-staged kernels.
+qalg_status run_widths(Op op, const void* A, const void* B, const int32_t* tau, int32_t q, const int64_t* in_w,
+                       const int64_t* out_w, int64_t M, int64_t K, int64_t N, void* C, int32_t dtype, void* ws,
+                       size_t ws_bytes, uint32_t flags, void* stream) {
+  if (dtype != QALG_BF16) return QALG_ERR_DTYPE;
+  if (flags & ~uint32_t(QALG_FLAG_INDEX_READY)) return QALG_ERR_ARG;
+  if (M < 0 || K <= 0 || N <= 0 || M > INT32_MAX / 2 || K > INT32_MAX / 2 || N > INT32_MAX / 2) return QALG_ERR_DIM;
+  const int64_t lim = int64_t(1) << 31;
+  if (M * K >= lim || K * N >= lim || M * N >= lim) return QALG_ERR_DIM;
+  if (q < 1 || q > qalg::kMaxWidthGroups) return QALG_ERR_Q;
+  if (in_w == nullptr || out_w == nullptr) return QALG_ERR_NULL;
+  int64_t sk = 0, sn = 0;
+  for (int g = 0; g < q; ++g) {
+    if (in_w[g] <= 0 || out_w[g] <= 0) return QALG_ERR_DIM;
+    if (in_w[g] % 8 || out_w[g] % 8) return QALG_ERR_ALIGN;
+    sk += in_w[g];
+    sn += out_w[g];
+  }
+  if (sk != K || sn != N) return QALG_ERR_DIM;
+  if (M > 0 && (A == nullptr || B == nullptr || C == nullptr || tau == nullptr)) return QALG_ERR_NULL;
+  if (M == 0 && op == Op::Dw && C == nullptr) return QALG_ERR_NULL;
+  if ((A && !aligned16(A)) || (B && !aligned16(B)) || (C && !aligned16(C)) ||
+      (tau && (reinterpret_cast<uintptr_t>(tau) & 3u)))
+    return QALG_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M == 0) {
+    if (op != Op::Dw) return QALG_OK;
+    return hip_status(qalg::launch_fill_zero(C, size_t(K) * size_t(N) * 2, s));
+  }
+  qalg_status st = check_ws(1, q, M, ws, ws_bytes);
+  if (st != QALG_OK) return st;
+  ProblemDesc p{};
+  p.op = op;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.tau = tau;
+  p.q = q;
+  p.M = M;
+  p.K = K;
+  p.N = N;
+  p.E = 1;
+  p.in_widths = in_w;
+  p.out_widths = out_w;
+  if (op == Op::Dw && ws_bytes >= qalg_workspace_bytes_dw(q, M, K, N))
+    p.dw_part = static_cast<char*>(ws) + qalg_workspace_bytes(q, M);
+  int32_t* wsi = static_cast<int32_t*>(ws);
+  p.ws = wsi;
+  p.ws_stride = ws_stride_ints(q, M);
+  void* zero_out = op == Op::Dw ? nullptr : C;
+  const int64_t zero_ld = op == Op::Fwd ? N : K;
+  hipError_t e;
+  if (!(flags & QALG_FLAG_INDEX_READY))
+    e = qalg::launch_build_index_zeroing(tau, q, M, 1, wsi, p.ws_stride, zero_out, zero_ld, 2, M * zero_ld * 2, s);
+  else if (zero_out != nullptr)
+    e = qalg::launch_zero_bad_rows(wsi, q, M, 1, p.ws_stride, zero_out, zero_ld, 2, M * zero_ld * 2, s);
+  else
+    e = hipSuccess;
+  if (e != hipSuccess) return QALG_ERR_HIP;
+  return hip_status(qalg::launch_tiled_bf16(p, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -346,6 +410,27 @@ qalg_status qalg_backward_dw_graph(const void* X, const void* dY, const int32_t*
                                    const uint64_t* adjacency, int64_t M, int64_t K, int64_t N, void* dW,
                                    int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags, void* stream) {
   return run_graph(Op::Dw, X, dY, tau, q, adjacency, M, K, N, dW, dtype, ws, ws_bytes, flags, stream);
+}
+
+qalg_status qalg_forward_widths(const void* X, const void* W, const int32_t* tau, int32_t q,
+                                const int64_t* in_widths, const int64_t* out_widths, int64_t M, int64_t K,
+                                int64_t N, void* Y, int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags,
+                                void* stream) {
+  return run_widths(Op::Fwd, X, W, tau, q, in_widths, out_widths, M, K, N, Y, dtype, ws, ws_bytes, flags, stream);
+}
+
+qalg_status qalg_backward_dx_widths(const void* dY, const void* W, const int32_t* tau, int32_t q,
+                                    const int64_t* in_widths, const int64_t* out_widths, int64_t M, int64_t K,
+                                    int64_t N, void* dX, int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags,
+                                    void* stream) {
+  return run_widths(Op::Dx, dY, W, tau, q, in_widths, out_widths, M, K, N, dX, dtype, ws, ws_bytes, flags, stream);
+}
+
+qalg_status qalg_backward_dw_widths(const void* X, const void* dY, const int32_t* tau, int32_t q,
+                                    const int64_t* in_widths, const int64_t* out_widths, int64_t M, int64_t K,
+                                    int64_t N, void* dW, int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags,
+                                    void* stream) {
+  return run_widths(Op::Dw, X, dY, tau, q, in_widths, out_widths, M, K, N, dW, dtype, ws, ws_bytes, flags, stream);
 }
 
 qalg_status qalg_backward_dx(const void* dY, const void* W, const int32_t* tau, int32_t q,

@@ -78,10 +78,14 @@ struct ProblemDesc {
   int law_L = 0;      // 0: the complete-graph law Q_q; L >= 1: the recursive law Q_2^(x)L, q = 2^L
   void* dw_part = nullptr;  // dW on the register-staged path: fp32 scratch for a split contraction
   const uint64_t* graph_adj = nullptr;  // graph law Q_G: per-type out-edge masks (device; q <= 64)
+  const int64_t* in_widths = nullptr;   // unequal group widths (host arrays of q; sums K and N)
+  const int64_t* out_widths = nullptr;
 };
 
 // dW's split contraction (register-staged path): at most this many partial tiles per output tile
 constexpr int kDwMaxSplits = 16;
+// unequal group widths: at most this many groups (the tables ride in the kernel arguments)
+constexpr int kMaxWidthGroups = 64;
 
 // skip_cyclic: the kernel returns at once when the index says the schedule is
 // cyclic (a persistent kernel launched beside it covers that case).

@@ -73,6 +73,11 @@ struct Args {
   int skip_cyclic;                   // return at once when the index says the schedule is cyclic
   int L;                             // recursive law Q_2^(x)L (TENSOR kernels); 0 otherwise
   const uint64_t* adj;               // graph law Q_G (GRAPH kernels): out-edge mask of each type
+  // unequal group widths (WIDTHS kernels, q <= kMaxWidthGroups): group starts
+  // along K (gk) and N (gn), and prefix counts of the tiles of each group along
+  // the tiled output axes (rows of dW: tk; columns of Y, dW: tn; columns of dX: tk)
+  int gk[kMaxWidthGroups + 1], gn[kMaxWidthGroups + 1];
+  int tk[kMaxWidthGroups + 1], tn[kMaxWidthGroups + 1];
   float* part;                       // dW split contraction: fp32 partial tiles [splits][K][N]
   int splits;                        // dW: workgroups per output tile (1: no split)
 };
@@ -148,11 +153,12 @@ __device__ __forceinline__ int find_type(const int32_t* tile_off, int q, int rt)
   return lo;
 }
 
-constexpr int kLawComplete = 0, kLawTensor = 1, kLawGraph = 2;
+// kLawWidths: the complete-graph law Q_q on groups of unequal widths (eq 18)
+constexpr int kLawComplete = 0, kLawTensor = 1, kLawGraph = 2, kLawWidths = 3;
 
 template <Op OP, class C, int LAW = kLawComplete>
 __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
-  constexpr bool TENSOR = LAW == kLawTensor, GRAPH = LAW == kLawGraph;
+  constexpr bool TENSOR = LAW == kLawTensor, GRAPH = LAW == kLawGraph, WIDTHS = LAW == kLawWidths;
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, KCH = C::KCH, T = C::THREADS;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
 
@@ -182,8 +188,27 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
   int tb_b = 0, tb_j = 0;  // recursive law: the tile's (dX: column group, row type; dW: b, j)
   const int32_t* krows = nullptr;  // dw: contraction rows
 
+  int seg_len1 = 0;  // unequal widths: the second forward segment's length
   int split = 0;  // dW: this workgroup's share of the tile's contraction
-  if constexpr (OP == Op::Dw) {
+  if constexpr (OP == Op::Dw && WIDTHS) {
+    // tiles: (row tile over all K features) x (column tile over all N columns)
+    const int tix = blockIdx.x / a.splits;
+    split = blockIdx.x - tix * a.splits;
+    const int n_tn = a.tn[q];
+    const int rt = tix / n_tn, ct = tix - rt * n_tn;
+    const int b = find_type(a.tk, q, rt), j = find_type(a.tn, q, ct);
+    out_first = a.gk[b] + (rt - a.tk[b]) * BM;
+    m_cnt = min(BM, a.gk[b + 1] - out_first);
+    n0 = a.gn[j] + (ct - a.tn[j]) * BN;
+    n_cnt = min(BN, a.gn[j + 1] - n0);
+    const int k_first = (b == j) ? 0 : offsets[b];
+    const int k_last = (b == j) ? offsets[q] : offsets[b + 1];
+    krows = rows + k_first;
+    nseg = 1;
+    seg_len = k_last - k_first;
+    segA0 = out_first;
+    segB0 = n0;
+  } else if constexpr (OP == Op::Dw) {
     const int per_block = a.tm_dw * a.tn_dw;
     const int tix = blockIdx.x / a.splits;
     split = blockIdx.x - tix * a.splits;
@@ -225,6 +250,27 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
     const int i = find_type(tile_off, q, rt);
     out_first = offsets[i] + (rt - tile_off[i]) * BM;
     m_cnt = min(BM, offsets[i + 1] - out_first);
+    if constexpr (WIDTHS) {
+      if constexpr (OP == Op::Fwd) {
+        // output group j of widths r_j; segments X[., g_i] W[g_i, .] (s_i) and X[., g_j] W[g_j, .] (s_j)
+        const int j = find_type(a.tn, q, ct);
+        n0 = a.gn[j] + (ct - a.tn[j]) * BN;
+        n_cnt = min(BN, a.gn[j + 1] - n0);
+        nseg = (j == i) ? 1 : 2;
+        seg_len = a.gk[i + 1] - a.gk[i];
+        seg_len1 = a.gk[j + 1] - a.gk[j];
+        segA0 = segB0 = a.gk[i];
+        segA1 = segB1 = a.gk[j];
+      } else {
+        // dX column group k of width s_k; contraction all N (k == i) or output group k (r_k)
+        const int k = find_type(a.tk, q, ct);
+        n0 = a.gk[k] + (ct - a.tk[k]) * BN;
+        n_cnt = min(BN, a.gk[k + 1] - n0);
+        nseg = 1;
+        seg_len = (k == i) ? a.N : a.gn[k + 1] - a.gn[k];
+        segA0 = (k == i) ? 0 : a.gn[k];
+      }
+    } else {
     const int j = ct / a.ct_per_group, cc = ct - j * a.ct_per_group;
     const int gw = (OP == Op::Fwd) ? a.r : a.s;
     n0 = j * gw + cc * BN;
@@ -260,10 +306,15 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
       seg_len = (j == i) ? a.N : a.r;
       segA0 = (j == i) ? 0 : j * a.r;  // dY columns (= W columns) of the contraction
     }
+    }
   }
-  const int kts = (seg_len + BK - 1) / BK;  // k-steps per segment
+  const int kts = (seg_len + BK - 1) / BK;  // k-steps per segment (the first, for unequal widths)
   const int this_seg_len = seg_len;
+  const int this_seg_len1 = WIDTHS ? seg_len1 : seg_len;
   int nk = nseg * kts;
+  if constexpr (WIDTHS && OP == Op::Fwd) {
+    if (nseg == 2) nk = kts + (seg_len1 + BK - 1) / BK;
+  }
   // recursive-law dW: the segment (type) the copy steps are in, its first
   // k-step, row range and k-steps (loads call it with increasing k-steps)
   int w_n = 0, w_k0 = 0, w_lo = 0, w_len = 0, w_kn = 0;
@@ -374,7 +425,7 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
   auto load_step = [&](int kt) {
     int sg = kt >= kts ? 1 : 0;
     int k0 = (kt - sg * kts) * BK;  // offset inside the segment
-    int seg_len = this_seg_len;     // this segment's length
+    int seg_len = sg ? this_seg_len1 : this_seg_len;  // this segment's length
     const int32_t* krows_s = krows;
     int segA0_s = segA0;
     if constexpr (GRAPH) {
@@ -806,11 +857,28 @@ Args make_args(const ProblemDesc& p, int bm, int bn) {
     a.tn_dw = cdiv(a.r, bn);
   }
   a.n_ct = p.q * a.ct_per_group;
+  if (p.in_widths != nullptr) {
+    // group starts, and per-group tile counts along the tiled output axes
+    const int tile_k = p.op == Op::Dw ? bm : bn;  // dW rows / dX columns run along K
+    a.gk[0] = a.gn[0] = a.tk[0] = a.tn[0] = 0;
+    for (int g = 0; g < p.q; ++g) {
+      a.gk[g + 1] = a.gk[g] + int(p.in_widths[g]);
+      a.gn[g + 1] = a.gn[g] + int(p.out_widths[g]);
+      a.tk[g + 1] = a.tk[g] + cdiv(p.in_widths[g], tile_k);
+      a.tn[g + 1] = a.tn[g] + cdiv(p.out_widths[g], bn);
+    }
+    a.n_ct = p.op == Op::Fwd ? a.tn[p.q] : a.tk[p.q];
+  }
   return a;
 }
 
+// dW tiles of a launch
+int64_t dw_tiles(const ProblemDesc& p, const Args& a) {
+  return p.in_widths != nullptr ? int64_t(a.tk[p.q]) * a.tn[p.q] : int64_t(p.q) * p.q * a.tm_dw * a.tn_dw;
+}
+
 dim3 grid_for(const ProblemDesc& p, const Args& a, int bm) {
-  if (p.op == Op::Dw) return dim3(unsigned(p.q * p.q * a.tm_dw * a.tn_dw * (a.splits > 1 ? a.splits : 1)), unsigned(p.E));
+  if (p.op == Op::Dw) return dim3(unsigned(dw_tiles(p, a) * (a.splits > 1 ? a.splits : 1)), unsigned(p.E));
   // worst case over all type splits: sum_i ceil(M_i / BM) <= ceil(M / BM) + q - 1
   const int64_t rt = (p.M + bm - 1) / bm + p.q - 1;
   return dim3(unsigned(rt * a.n_ct), unsigned(p.E));
@@ -824,7 +892,7 @@ hipError_t launch_cfg(const ProblemDesc& p, hipStream_t s, bool skip_cyclic) {
   // (not beside the persistent kernel: there this launch may return at once)
   if (OP == Op::Dw && p.dw_part != nullptr && p.E == 1 && !skip_cyclic) {
     // enough workgroups to cover the CUs about four times, at most kDwMaxSplits per tile
-    const int64_t tiles = int64_t(p.q) * p.q * a.tm_dw * a.tn_dw;
+    const int64_t tiles = dw_tiles(p, a);
     int64_t sp = (4 * 256 + tiles - 1) / tiles;
     sp = sp < 1 ? 1 : (sp > kDwMaxSplits ? kDwMaxSplits : sp);
     a.splits = int(sp);
@@ -840,6 +908,12 @@ hipError_t launch_cfg(const ProblemDesc& p, hipStream_t s, bool skip_cyclic) {
       if (e != hipSuccess || a.splits == 1) return e;
       return launch_dw_reduce(a.part, a.splits, p.K * p.N, static_cast<uint16_t*>(p.C), s);
     }
+  }
+  if (p.in_widths != nullptr) {
+    hipLaunchKernelGGL((tiled_bf16_kernel<OP, C, kLawWidths>), g, dim3(C::THREADS), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.splits == 1) return e;
+    return launch_dw_reduce(a.part, a.splits, p.K * p.N, static_cast<uint16_t*>(p.C), s);
   }
   if (p.graph_adj != nullptr) {
     hipLaunchKernelGGL((tiled_bf16_kernel<OP, C, kLawGraph>), g, dim3(C::THREADS), 0, s, a);

@@ -235,6 +235,33 @@ qalg_status qalg_backward_dw_graph(const void* X, const void* dY, const int32_t*
                                    int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags, void* stream);
 
 /*
+ * The complete-graph law Q_q on groups of unequal widths (eq 18): input group
+ * g spans in_widths[g] columns of X (rows of W), output group g spans
+ * out_widths[g] columns of Y and W; a row of type i gets y_i = x_i W_ii and
+ * y_j = x_i W_ij + x_j W_jj, the blocks now rectangular.  Forward, dX and dW
+ * with the operands, overwrite and zero-row rules of qalg_forward,
+ * qalg_backward_dx and qalg_backward_dw.  in_widths, out_widths: host arrays
+ * of q int64, read during the call only; every width a positive multiple of
+ * 8 (QALG_ERR_DIM / QALG_ERR_ALIGN), summing to K and N (QALG_ERR_DIM).
+ * q <= 64 (QALG_ERR_Q); bf16 only (QALG_ERR_DTYPE); M K, K N and M N below
+ * 2^31 (QALG_ERR_DIM); flags: QALG_FLAG_INDEX_READY only (QALG_ERR_ARG).  A
+ * workspace of qalg_workspace_bytes_dw bytes lets dW split its contraction.
+ * Register-staged kernels; each output element has one owner.
+ */
+qalg_status qalg_forward_widths(const void* X, const void* W, const int32_t* tau, int32_t q,
+                                const int64_t* in_widths, const int64_t* out_widths, int64_t M, int64_t K,
+                                int64_t N, void* Y, int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags,
+                                void* stream);
+qalg_status qalg_backward_dx_widths(const void* dY, const void* W, const int32_t* tau, int32_t q,
+                                    const int64_t* in_widths, const int64_t* out_widths, int64_t M, int64_t K,
+                                    int64_t N, void* dX, int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags,
+                                    void* stream);
+qalg_status qalg_backward_dw_widths(const void* X, const void* dY, const int32_t* tau, int32_t q,
+                                    const int64_t* in_widths, const int64_t* out_widths, int64_t M, int64_t K,
+                                    int64_t N, void* dW, int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags,
+                                    void* stream);
+
+/*
  * Activation gradient (appendix B, eq 31-32): for a row of type i,
  *   dx_i = sum_j dy_j W_ij^T  and  dx_j = dy_j W_jj^T  (j != i).
  * dY: M x N, W: K x N, dX: M x K (overwritten).

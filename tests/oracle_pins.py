@@ -488,6 +488,34 @@ def pin_graph_vjp_autograd(O, seed=42):
         np.testing.assert_allclose(dW, W.grad.numpy(), rtol=1e-12, atol=1e-12)
 
 
+def pin_widths_vjp_autograd(O, seed=43):
+    """Unequal widths (eq 18): float64 autograd of the masked-dense rows equals the oracle's dX, dW."""
+    import torch
+    g = _rng(seed)
+    for kw, nw, M in (([2, 5, 1], [3, 1, 4], 13), ([4, 1], [2, 6], 9), ([1, 3, 2, 2], [2, 2, 5, 1], 15)):
+        q = len(kw)
+        kb, nb = _bounds(kw), _bounds(nw)
+        Xn = g.standard_normal((M, sum(kw)))
+        Wn = g.standard_normal((sum(kw), sum(nw)))
+        dYn = g.standard_normal((M, sum(nw)))
+        tau = g.integers(0, q, size=M)
+        X = torch.tensor(Xn, requires_grad=True)
+        W = torch.tensor(Wn, requires_grad=True)
+        rows = []
+        for m in range(M):
+            i = int(tau[m])
+            T = np.zeros_like(Wn)
+            for a in range(q):
+                for b in range(q):
+                    if a == i or a == b:
+                        T[kb[a][0]:kb[a][1], nb[b][0]:nb[b][1]] = 1.0
+            rows.append(X[m:m + 1] @ (W * torch.tensor(T)))
+        (torch.cat(rows) * torch.tensor(dYn)).sum().backward()
+        dX, dW = O.row_typed_backward(Xn, Wn, dYn, tau, q, in_widths=kw, out_widths=nw)
+        np.testing.assert_allclose(dX, X.grad.numpy(), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dW, W.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
 def pin_vjp_adjoint(O, seed=26):
     """Bilinearity: <dY, Y> = <dX, X> = <dW, W>; dW blocks with no contributing rows are zero."""
     g = _rng(seed)
@@ -883,7 +911,7 @@ ALL_PINS = [
     pin_product_counts, pin_graph_counts, pin_appendix_a, pin_associativity,
     pin_row_typed_composition, pin_unit_laws, pin_brute_force, pin_teaching_matrix,
     pin_masked_dense, pin_graph_masked_dense, pin_row_typed_is_square_rows, pin_q1_is_matmul, pin_block_diagonal,
-    pin_coverage, pin_vjp_scalar_eq31_35, pin_vjp_autograd, pin_graph_vjp_autograd, pin_vjp_adjoint,
+    pin_coverage, pin_vjp_scalar_eq31_35, pin_vjp_autograd, pin_graph_vjp_autograd, pin_widths_vjp_autograd, pin_vjp_adjoint,
     pin_mac_count, pin_type_index, pin_type_schedule, pin_silu_values, pin_gated_masked_dense,
     pin_silu_grad, pin_gated_ffn_autograd, pin_tensor_counts, pin_tensor_support,
     pin_tensor_associativity, pin_tensor_masked_dense, pin_tensor_cost, pin_tensor_vjp_autograd,

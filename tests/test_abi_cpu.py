@@ -265,3 +265,32 @@ def test_graph_argument_errors_are_synchronous(lib):
     assert lib.qalg_forward_graph(FAKE, FAKE, FAKE, 4, None, 0, 256, 512, FAKE, 1, FAKE, 0, 0, None) == 0
     assert lib.qalg_backward_dx_graph(FAKE, FAKE, FAKE, 4, None, 0, 256, 512, FAKE, 1, FAKE, 0, 0, None) == 0
     assert lib.qalg_backward_dw_graph(FAKE, FAKE, FAKE, 4, None, 0, 256, 512, None, 1, FAKE, 0, 0, None) == 1
+
+
+def test_widths_argument_errors_are_synchronous(lib):
+    """The unequal-width entry points reject bad arguments before any launch (the pointers are fake)."""
+    import ctypes
+    arr = lambda *v: (ctypes.c_int64 * len(v))(*v)  # noqa: E731
+    for fn in ("qalg_forward_widths", "qalg_backward_dx_widths", "qalg_backward_dw_widths"):
+        f = getattr(lib, fn)
+        g = lambda **k: f(FAKE, FAKE, FAKE, k.get("q", 3), k.get("kw", arr(64, 128, 64)),  # noqa: E731
+                          k.get("nw", arr(256, 128, 128)), k.get("M", 64), k.get("K", 256), k.get("N", 512),
+                          k.get("Y", FAKE), k.get("dt", 1), k.get("ws", FAKE), k.get("wsb", 1 << 20),
+                          k.get("flags", 0), None)
+        assert g(dt=0) == 5, fn
+        assert g(flags=Q.QALG_FLAG_LAW_TENSOR) == 8, fn
+        assert g(q=65) == 3, fn
+        assert g(kw=None) == 1, fn
+        assert g(nw=None) == 1, fn
+        assert g(kw=arr(64, 132, 60)) == 4, fn           # widths are multiples of 8
+        assert g(kw=arr(64, 192, 0)) == 2, fn            # and positive
+        assert g(kw=arr(64, 128, 72)) == 2, fn           # summing to K
+        assert g(nw=arr(256, 128, 120)) == 2, fn         # and to N
+        assert g(Y=None) == 1, fn
+        assert g(ws=None) == 1, fn
+        assert g(wsb=16) == 6, fn
+        assert g(M=1 << 24) == 2, fn                     # M K >= 2^31
+    assert lib.qalg_forward_widths(FAKE, FAKE, FAKE, 3, arr(64, 128, 64), arr(256, 128, 128), 0, 256, 512,
+                                   FAKE, 1, FAKE, 0, 0, None) == 0
+    assert lib.qalg_backward_dw_widths(FAKE, FAKE, FAKE, 3, arr(64, 128, 64), arr(256, 128, 128), 0, 256, 512,
+                                       None, 1, FAKE, 0, 0, None) == 1
