@@ -371,6 +371,11 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
   constexpr int B_PER = B_KMAJOR ? (C::B_CHUNKS + T - 1) / T : (C::B_BLOCKS + T - 1) / T;
   constexpr int A_REGS = A_KMAJOR ? 1 : 8;
   constexpr int B_REGS = B_KMAJOR ? 1 : 8;
+  // dW with both operands' 8x8 blocks fitting the workgroup once: the X blocks
+  // go to the first threads and the dY blocks to the last, so that each thread
+  // gathers 8 rows of one operand, and the row ids are fetched a k-step ahead
+  constexpr bool DW_SPLIT = OP == Op::Dw && C::A_BLOCKS + C::B_BLOCKS <= T;
+  constexpr int B_BASE = DW_SPLIT ? T - C::B_BLOCKS : 0;  // first thread of the dY blocks
 
   const uint16_t* a_ptr[A_PER];  // K-major: row base (contraction offset added per step)
   int a_kc[A_PER];               // K-major: chunk; MN-major: block's k-chunk
@@ -411,8 +416,9 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
       b_kc[u] = kc;
       b_ptr[u] = Bg + int64_t(n0 + min(nl, n_cnt - 1)) * a.N;  // W row = dX column
     } else {
-      b_on[u] = c < C::B_BLOCKS;
-      const int kb = c % KCH, nb = c / KCH;
+      const int cb = c - B_BASE;
+      b_on[u] = cb >= 0 && cb < C::B_BLOCKS;
+      const int kb = max(cb, 0) % KCH, nb = max(cb, 0) / KCH;
       b_kc[u] = kb;
       b_mn[u] = nb * 8;
       b_ptr[u] = Bg + n0 + nb * 8;
@@ -422,12 +428,17 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
   u32x4 ra[A_PER][A_REGS];
   u32x4 rb[B_PER][B_REGS];
 
-  auto load_step = [&](int kt) {
-    int sg = kt >= kts ? 1 : 0;
-    int k0 = (kt - sg * kts) * BK;  // offset inside the segment
-    int seg_len = sg ? this_seg_len1 : this_seg_len;  // this segment's length
-    const int32_t* krows_s = krows;
-    int segA0_s = segA0;
+  // segment of k-step kt: segment index sg (0/1, two-segment forwards), offset
+  // k0 inside it, its length, dW's contraction rows and the A column offset.
+  // The walks of the recursive and graph laws only move forward: calls come
+  // with increasing kt.
+  auto seg_at = [&](int kt, int& sg, int& k0, int& seg_len, const int32_t*& krows_s,
+                    int& segA0_s) __attribute__((always_inline)) {
+    sg = kt >= kts ? 1 : 0;
+    k0 = (kt - sg * kts) * BK;
+    seg_len = sg ? this_seg_len1 : this_seg_len;
+    krows_s = krows;
+    segA0_s = segA0;
     if constexpr (GRAPH) {
       if constexpr (OP == Op::Dx) {
         if (tb_b == tb_j) {  // member groups visited in increasing order as kt grows
@@ -477,6 +488,12 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
         k0 = (kt - w_k0) * BK;
       }
     }
+  };
+
+  auto load_step = [&](int kt) __attribute__((always_inline)) {
+    int sg, k0, seg_len, segA0_s;
+    const int32_t* krows_s;
+    seg_at(kt, sg, k0, seg_len, krows_s, segA0_s);
 #pragma unroll
     for (int u = 0; u < A_PER; ++u) {
       if constexpr (A_KMAJOR) {
@@ -532,6 +549,35 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
           }
         }
       }
+    }
+  };
+
+  // DW_SPLIT: this thread's block (X features or dY columns: 8 of them, at
+  // contraction chunk dw_kc), computed from scalars so that no selection
+  // between the per-operand arrays is needed, and the row ids of the block's
+  // 8 contraction rows for the next gathered load (-1: padding)
+  const bool dw_isA = tid < C::A_BLOCKS;
+  const int dw_c = dw_isA ? tid : max(tid - B_BASE, 0);
+  const int dw_kc = dw_c % KCH, dw_mn = (dw_c / KCH) * 8;
+  const bool dw_on = dw_isA ? dw_mn < m_cnt : (tid >= B_BASE && dw_mn < n_cnt);
+  const uint16_t* dw_ptr = dw_isA ? Ag + segA0 + dw_mn : Bg + n0 + dw_mn;
+  const int64_t dw_ld = dw_isA ? a.K : a.N;
+  int nid[8];
+  auto fetch_ids = [&](int kt) __attribute__((always_inline)) {
+    int sg, k0, seg_len, segA0_s;
+    const int32_t* krows_s;
+    seg_at(kt, sg, k0, seg_len, krows_s, segA0_s);
+    const int kk = k0 + dw_kc * 8;
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) nid[rr] = (dw_on && kk + rr < seg_len) ? krows_s[kk + rr] : -1;
+  };
+  auto load_ids = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+      if (nid[rr] >= 0) v = *reinterpret_cast<const u32x4*>(dw_ptr + int64_t(nid[rr]) * dw_ld);
+      ra[0][rr] = v;  // store_step takes ra on the X threads, rb on the dY threads
+      rb[0][rr] = v;
     }
   };
 
@@ -612,7 +658,25 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
     k_lo = min(nk, split * chunk);
     k_hi = min(nk, k_lo + chunk);
   }
-  if (k_hi > k_lo) {
+  if constexpr (DW_SPLIT) {
+    if (k_hi > k_lo) {
+      fetch_ids(k_lo);
+      load_ids();
+      if (k_lo + 1 < k_hi) fetch_ids(k_lo + 1);
+      store_step(0);
+      __syncthreads();
+      for (int kt = k_lo; kt < k_hi; ++kt) {
+        const bool more = kt + 1 < k_hi;
+        if (more) {
+          load_ids();                            // k-step kt + 1 (ids fetched a step ago)
+          if (kt + 2 < k_hi) fetch_ids(kt + 2);  // in flight during this k-step's MFMAs
+        }
+        compute_step((kt - k_lo) & 1);
+        if (more) store_step((kt - k_lo + 1) & 1);
+        __syncthreads();
+      }
+    }
+  } else if (k_hi > k_lo) {
     load_step(k_lo);
     store_step(0);
     __syncthreads();
