@@ -11,6 +11,7 @@ Workloads:
   * dense FFN (4096, 12288), bf16, q=8, M=16384: up and down projections
   * narrow expert shapes, bf16, 64 experts: (7168,2048) q=4, (2048,768) q=4 and q=8
   * training gradients at (4096, 12288), q=8, M=16384: forward, dX and dW
+  * the graph law Q_G and unequal group widths at (4096, 12288), M=16384: forward, dX, dW
 """
 import numpy as np
 import pytest
@@ -323,3 +324,72 @@ def test_attention_bench_shape_sampled_heads(law):
     errs = [float(np.linalg.norm(got[k] - Or[k]) / np.linalg.norm(Or[k])) for k in range(len(heads))]
     say(f"    max rel err over heads {heads}: {max(errs):.2e}")
     assert max(errs) <= BF16_TOL, errs
+
+
+def test_graph_law_bench_shape_sampled():
+    """The benchmark's graph-law leg: the same seeds, graph and calls (forward, dX, split dW)."""
+    torch = torch_cuda()
+    c, M, K, N, q = 9, 16384, 4096, 12288, 8
+    g = np.random.Generator(np.random.PCG64(1000 * c + 4))
+    edges = [(a, b) for a in range(q) for b in range(q) if a != b and g.random() < 0.5]
+    say(f"[workload] graph law q={q} M={M} {K}->{N}, {len(edges)} edges: forward, dX, dW")
+    masks = [0] * q
+    for a, b in edges:
+        masks[a] |= 1 << b
+    X = synth.normal_operand(1000 * c + 1, (M, K), 1.0, "bf16")
+    W = synth.normal_operand(1000 * c + 2, (K, N), K ** -0.5, "bf16")
+    dY = synth.normal_operand(1000 * c + 3, (M, N), 1.0, "bf16")
+    tau = (np.arange(M) % q).astype(np.int32)
+    Xd, Wd, dYd, td = to_dev(X), to_dev(W), to_dev(dY), tau_dev(tau)
+    adj = torch.tensor(masks, dtype=torch.int64, device="cuda")
+    ws = Q.workspace(q, M, dw_shape=(K, N))
+    Q.qalg_build_index(td, q, ws=ws)
+    r = Q.QALG_FLAG_INDEX_READY
+    Y = Q.qalg_forward_graph(Xd, Wd, td, q, adj, ws=ws, flags=r)
+    dX = Q.qalg_backward_dx_graph(dYd, Wd, td, q, adj, ws=ws, flags=r)
+    dW = Q.qalg_backward_dw_graph(Xd, dYd, td, q, adj, ws=ws, flags=r)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M, q, 512, 9)
+    Yr = O.row_typed_forward(X.f64[rows], W.f64, tau[rows], q, edges=edges)
+    assert_groups(rel_frob_col_groups(to_f64(Y[rows]), Yr, q), BF16_TOL, "Y")
+    dXr_s, _ = O.row_typed_backward(X.f64[rows], W.f64, dY.f64[rows], tau[rows], q, edges=edges)
+    assert_groups(rel_frob_col_groups(to_f64(dX[rows]), dXr_s, q), BF16_TOL, "dX")
+    _, dWr = O.row_typed_backward(X.f64, W.f64, dY.f64, tau, q, edges=edges)
+    e = assert_groups(rel_frob_blocks(to_f64(dW), dWr, q), BF16_TOL, "dW")
+    say(f"    dW max rel err {e:.2e}")
+
+
+def test_unequal_widths_bench_shape_sampled():
+    """The benchmark's unequal-widths leg: the same seeds, widths and calls (forward, dX, split dW)."""
+    torch = torch_cuda()
+    c, M, K, N = 10, 16384, 4096, 12288
+    kw = [512, 768, 1024, 1792]
+    nw = [3 * w for w in kw]
+    q = len(kw)
+    say(f"[workload] unequal widths q={q} M={M} {K}->{N} {kw}: forward, dX, dW")
+    X = synth.normal_operand(1000 * c + 1, (M, K), 1.0, "bf16")
+    W = synth.normal_operand(1000 * c + 2, (K, N), K ** -0.5, "bf16")
+    dY = synth.normal_operand(1000 * c + 3, (M, N), 1.0, "bf16")
+    tau = (np.arange(M) % q).astype(np.int32)
+    Xd, Wd, dYd, td = to_dev(X), to_dev(W), to_dev(dY), tau_dev(tau)
+    ws = Q.workspace(q, M, dw_shape=(K, N))
+    Q.qalg_build_index(td, q, ws=ws)
+    r = Q.QALG_FLAG_INDEX_READY
+    Y = Q.qalg_forward_widths(Xd, Wd, td, q, kw, nw, ws=ws, flags=r)
+    dX = Q.qalg_backward_dx_widths(dYd, Wd, td, q, kw, nw, ws=ws, flags=r)
+    dW = Q.qalg_backward_dw_widths(Xd, dYd, td, q, kw, nw, ws=ws, flags=r)
+    torch.cuda.synchronize()
+    kb = np.concatenate([[0], np.cumsum(kw)])
+    nb = np.concatenate([[0], np.cumsum(nw)])
+    rows = _sample_rows(M, q, 512, 10)
+    Yr = O.row_typed_forward(X.f64[rows], W.f64, tau[rows], q, in_widths=kw, out_widths=nw)
+    dXr_s, _ = O.row_typed_backward(X.f64[rows], W.f64, dY.f64[rows], tau[rows], q, in_widths=kw, out_widths=nw)
+    _, dWr = O.row_typed_backward(X.f64, W.f64, dY.f64, tau, q, in_widths=kw, out_widths=nw)
+    gy, gx, gw = to_f64(Y[rows]), to_f64(dX[rows]), to_f64(dW)
+    from qalg_check import _rel
+    ey = max(_rel(gy[:, nb[j]:nb[j + 1]], Yr[:, nb[j]:nb[j + 1]]) for j in range(q))
+    ex = max(_rel(gx[:, kb[j]:kb[j + 1]], dXr_s[:, kb[j]:kb[j + 1]]) for j in range(q))
+    ew = max(_rel(gw[kb[b]:kb[b + 1], nb[j]:nb[j + 1]], dWr[kb[b]:kb[b + 1], nb[j]:nb[j + 1]])
+             for b in range(q) for j in range(q))
+    say(f"    max rel err Y {ey:.2e}, dX {ex:.2e}, dW {ew:.2e}")
+    assert ey <= BF16_TOL and ex <= BF16_TOL and ew <= BF16_TOL
