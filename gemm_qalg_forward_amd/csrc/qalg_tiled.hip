@@ -140,6 +140,20 @@ __device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) 
   return (u32x2){__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
 }
 
+// XCD-aware order: workgroup w runs on XCD w mod 8.  Logical tiles come in
+// groups of gs that share operand rows (the column tiles of one row tile, or
+// the tiles of one dW block); each group goes whole to one XCD, and the groups
+// go round robin over the XCDs, so that a group's tiles share an L2 while the
+// costly and the cheap groups still spread over all XCDs.  Workgroups past
+// the last whole round of 8 groups keep their index.
+__device__ __forceinline__ int xcd_remap(int w, int G, int gs) {
+  const int span = 8 * gs;
+  if (gs < 1 || w >= (G / span) * span) return w;
+  const int x = w % 8, i = w / 8;
+  const int gi = i / gs, o = i - gi * gs;
+  return (gi * 8 + x) * gs + o;
+}
+
 // Position of a row tile among the per-type row tiles: largest i with tile_off[i] <= rt.
 __device__ __forceinline__ int find_type(const int32_t* tile_off, int q, int rt) {
   int lo = 0, hi = q;
@@ -191,10 +205,13 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
   int seg_len1 = 0;  // unequal widths: the second forward segment's length
   int split = 0;  // dW: this workgroup's share of the tile's contraction
   if constexpr (OP == Op::Dw && WIDTHS) {
-    // tiles: (row tile over all K features) x (column tile over all N columns)
+    // tiles: (row tile over all K features) x (column tile over all N columns).
+    // dW tiles differ widely in cost (diagonal blocks contract over all rows),
+    // so consecutive workgroups, which the hardware deals round robin over the
+    // XCDs, take the splits of one tile: each tile's work spreads over all XCDs.
+    const int n_tn = a.tn[q];
     const int tix = blockIdx.x / a.splits;
     split = blockIdx.x - tix * a.splits;
-    const int n_tn = a.tn[q];
     const int rt = tix / n_tn, ct = tix - rt * n_tn;
     const int b = find_type(a.tk, q, rt), j = find_type(a.tn, q, ct);
     out_first = a.gk[b] + (rt - a.tk[b]) * BM;
@@ -210,6 +227,7 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
     segB0 = n0;
   } else if constexpr (OP == Op::Dw) {
     const int per_block = a.tm_dw * a.tn_dw;
+    // consecutive workgroups take the splits of one tile (see the widths case)
     const int tix = blockIdx.x / a.splits;
     split = blockIdx.x - tix * a.splits;
     const int bid = tix / per_block;
@@ -244,8 +262,9 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
     }
   } else {
     const int32_t* tile_off = ws + a.off_tiles + tile_height_slot(BM) * (q + 1);
-    const int rt = blockIdx.x / a.n_ct;
-    const int ct = blockIdx.x - rt * a.n_ct;
+    const int w = xcd_remap(blockIdx.x, gridDim.x, a.n_ct);
+    const int rt = w / a.n_ct;
+    const int ct = w - rt * a.n_ct;
     if (rt >= tile_off[q]) return;
     const int i = find_type(tile_off, q, rt);
     out_first = offsets[i] + (rt - tile_off[i]) * BM;
@@ -994,6 +1013,22 @@ hipError_t launch_cfg(const ProblemDesc& p, hipStream_t s, bool skip_cyclic) {
 using Cfg128 = TileCfg<128, 128, 64, 2, 2>;
 using Cfg64 = TileCfg<64, 64, 64, 2, 2>;
 using Cfg32 = TileCfg<32, 64, 64, 1, 2>;
+// dW on wide groups: 256- or 192-feature tiles with 32-deep k-steps (twice the
+// MFMA work per loaded byte of the 128 x 128 tile, whose loads saturate the
+// vector-memory path)
+using CfgW256 = TileCfg<256, 256, 32, 2, 4>;
+using CfgW192 = TileCfg<192, 256, 32, 2, 4>;
+using CfgW192n = TileCfg<192, 192, 32, 2, 2>;
+
+// whether every feature group (rows of dW) and output group (its columns) is a whole number of bm x bn tiles
+bool dw_tiles_exact(const ProblemDesc& p, int bm, int bn) {
+  for (int g = 0; g < p.q; ++g) {
+    const int64_t s = p.in_widths ? p.in_widths[g] : p.K / p.q;
+    const int64_t r = p.out_widths ? p.out_widths[g] : p.N / p.q;
+    if (s % bm || r % bn) return false;
+  }
+  return true;
+}
 
 }  // namespace
 
@@ -1010,6 +1045,9 @@ hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s, bool skip_cycl
       if (per_type >= 48) return launch_cfg<Op::Dx, Cfg64>(p, s, skip_cyclic);
       return launch_cfg<Op::Dx, Cfg32>(p, s, skip_cyclic);
     case Op::Dw:
+      if (dw_tiles_exact(p, 256, 256)) return launch_cfg<Op::Dw, CfgW256>(p, s, skip_cyclic);
+      if (dw_tiles_exact(p, 192, 256)) return launch_cfg<Op::Dw, CfgW192>(p, s, skip_cyclic);
+      if (dw_tiles_exact(p, 192, 192)) return launch_cfg<Op::Dw, CfgW192n>(p, s, skip_cyclic);
       if (per_type >= 128) return launch_cfg<Op::Dw, Cfg128>(p, s, skip_cyclic);
       return launch_cfg<Op::Dw, Cfg64>(p, s, skip_cyclic);
   }
