@@ -1020,6 +1020,17 @@ using CfgW256 = TileCfg<256, 256, 32, 2, 4>;
 using CfgW192 = TileCfg<192, 256, 32, 2, 4>;
 using CfgW192n = TileCfg<192, 192, 32, 2, 2>;
 
+// whether every group along the output columns of Y (out widths) or dX (in widths) is a whole
+// number of bn-wide tiles
+bool cols_exact(const ProblemDesc& p, int bn) {
+  for (int g = 0; g < p.q; ++g) {
+    const int64_t w = p.op == Op::Fwd ? (p.out_widths ? p.out_widths[g] : p.N / p.q)
+                                      : (p.in_widths ? p.in_widths[g] : p.K / p.q);
+    if (w % bn) return false;
+  }
+  return true;
+}
+
 // whether every feature group (rows of dW) and output group (its columns) is a whole number of bm x bn tiles
 bool dw_tiles_exact(const ProblemDesc& p, int bm, int bn) {
   for (int g = 0; g < p.q; ++g) {
@@ -1037,10 +1048,16 @@ hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s, bool skip_cycl
   const int64_t per_type = p.op == Op::Dw ? p.K / p.q : (p.M + p.q - 1) / p.q;
   switch (p.op) {
     case Op::Fwd:
+      // wide tiles where every type has rows for several and the output groups divide evenly
+      if (per_type >= 512 && cols_exact(p, 256)) return launch_cfg<Op::Fwd, CfgW256>(p, s, skip_cyclic);
       if (per_type >= 128) return launch_cfg<Op::Fwd, Cfg128>(p, s, skip_cyclic);
       if (per_type >= 48) return launch_cfg<Op::Fwd, Cfg64>(p, s, skip_cyclic);
       return launch_cfg<Op::Fwd, Cfg32>(p, s, skip_cyclic);
     case Op::Dx:
+      // (not for graph laws: their dX tiles range from no work to q segments, and the
+      // smaller tiles balance that better)
+      if (per_type >= 512 && cols_exact(p, 256) && p.graph_adj == nullptr)
+        return launch_cfg<Op::Dx, CfgW256>(p, s, skip_cyclic);
       if (per_type >= 128) return launch_cfg<Op::Dx, Cfg128>(p, s, skip_cyclic);
       if (per_type >= 48) return launch_cfg<Op::Dx, Cfg64>(p, s, skip_cyclic);
       return launch_cfg<Op::Dx, Cfg32>(p, s, skip_cyclic);
