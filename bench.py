@@ -7,7 +7,9 @@ with q = 8 (512 x 1536 weight blocks), M = 16384 token rows at positions
     X_up [M, 4096] x W_up [4096, 12288] and the down projection
     X_dn [M, 12288] x W_dn [12288, 4096], both forward, fp32 accumulation.
 Inputs are seeded synthetic N(0,1) activations and N(0,1/K) weights, resident
-in HBM before timing starts.
+in HBM before timing starts.  Before the W warm-up steps the step runs untimed
+for --prewarm-s seconds (the clock ramp from idle takes about 25 ms of load);
+then exactly K steps are timed with HIP events on the launch stream.
 
 Reported (one JSON line):
   value            algebra TFLOP/s of the step: 2 * rho_q * M*K*N per projection
@@ -60,6 +62,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--prewarm-s", type=float, default=0.3,
+                    help="untimed steps run for this wall time before the warm-up steps (clock ramp from idle)")
     ap.add_argument("--cpu-rows", type=int, default=16384,
                     help="rows of each projection the CPU oracle leg evaluates")
     ap.add_argument("--no-extra", action="store_true", help="skip the training and decode legs")
@@ -127,7 +131,20 @@ def main() -> int:
         if ev is not None:
             ev[2].record(stream)
 
-    def timed(q, tau_t, ws_t, steps, warmup):
+    def prewarm(q, tau_t, ws_t, seconds):
+        # From idle the GPU needs about 25 ms of sustained load before its clock
+        # settles (per-launch times fall from 0.8 to 0.36 ms over the first
+        # ~50 launches, then stay flat), which a handful of warm-up steps does
+        # not cover: run the untimed step for a fixed wall time first.
+        t_end = time.time() + seconds
+        while time.time() < t_end:
+            for _ in range(10):
+                step(q, tau_t, ws_t)
+            torch.cuda.synchronize()
+
+    def timed(q, tau_t, ws_t, steps, warmup, prewarm_s=0.0):
+        if prewarm_s > 0:
+            prewarm(q, tau_t, ws_t, prewarm_s)
         for _ in range(warmup):
             step(q, tau_t, ws_t)
         torch.cuda.synchronize()
@@ -146,7 +163,7 @@ def main() -> int:
         return total_ms, up, dn
 
     # ---------------- the step at q = 8 ----------------
-    total_ms, up_ms, dn_ms = timed(QQ, tau, ws, args.steps, args.warmup)
+    total_ms, up_ms, dn_ms = timed(QQ, tau, ws, args.steps, args.warmup, args.prewarm_s)
     ms_step = total_ms / args.steps
     alg_flop_proj = 2.0 * rho(QQ) * M * D * F
     dense_flop_proj = 2.0 * M * D * F
