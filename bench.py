@@ -273,7 +273,8 @@ def training_leg(Q, torch, np, synth, dev, stream):
     to = lambda op: torch.from_numpy(op.bits.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
     Xd, Wd, dYd = to(X), to(W), to(dY)
     tau = torch.from_numpy((np.arange(M) % QQ).astype(np.int32)).to(dev)
-    ws = Q.workspace(QQ, M, device=dev)
+    # with the dW scratch, dW splits the contraction of its diagonal tiles
+    ws = Q.workspace(QQ, M, device=dev, dw_shape=(D, F))
     Y = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
     dX = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
     dW = torch.empty(D, F, dtype=torch.bfloat16, device=dev)
@@ -416,7 +417,7 @@ def gated_leg(Q, torch, np, synth, dev, stream):
     Xd, Wdd = to(X), to(Wd)
     Wgu = Q.qalg_merge_gate_up(to(Wg), to(Wu), QQ, stream=stream)  # weight layout, once
     tau = torch.from_numpy((np.arange(M) % QQ).astype(np.int32)).to(dev)
-    ws = Q.workspace(QQ, M, device=dev)
+    ws = Q.workspace(QQ, M, device=dev, dw_shape=(D, 2 * F))  # dW scratch for the training step
     H = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
     Y = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
     Q.qalg_build_index(tau, QQ, ws=ws, stream=stream)

@@ -33,7 +33,12 @@
 // are dealt to its workgroups round robin, longs first; workgroups that got
 // one long tile fewer then take up to q short tiles each before the remaining
 // short tiles are dealt round robin, so every workgroup ends with nearly the
-// same number of k-steps.
+// same number of k-steps.  A dW long tile (a diagonal block, contracted over
+// all M rows) can still exceed the average load of a workgroup by far (at
+// q = 8: 512 k-steps against an average of 360); given fp32 scratch, its
+// contraction is cut into `splits` equal pieces dealt as separate long tiles,
+// each writing an fp32 partial tile, and a reduction sums the pieces in order
+// and rounds once (bitwise reproducible).
 //
 // Rows of type i are the arithmetic progression (i - o) mod q + k q of a
 // cyclic schedule (detected by the index); a launch on any other schedule
@@ -102,6 +107,9 @@ struct GradArgs {
   int n_rt;        // dX: row tiles over all types (from the index; read on device)
   int cpg;         // dX: column tiles per input group (s / BN); dW: per output group (r / BN)
   int rpb;         // dW: row tiles per feature group (s / BM)
+  int splits;      // dW: pieces of each long tile's contraction (1: none)
+  float* part;     // dW, splits > 1: fp32 partial tiles [splits][K][N] (diagonal blocks only)
+  int64_t part_stride;  // floats per piece (K * N)
 };
 
 // One output tile.
@@ -110,8 +118,9 @@ struct GTile {
   int type;        // dX: row type;  dW: type whose rows are contracted (-1: all rows)
   int m_cnt;       // valid output rows (dX ragged row tiles)
   int n0;          // first output column
-  int c0;          // dX: first contraction column (in N)
+  int c0;          // dX: first contraction column (in N);  dW: first k-step of a split piece
   int nk;          // k-steps
+  int piece;       // dW: piece of a split long tile (fp32 partial output); -1 otherwise
 };
 
 
@@ -145,9 +154,17 @@ __device__ __forceinline__ GTile decode(const GradArgs& a, const CycIndex& ix, b
     }
     t.n0 = k * a.s + cc * C::BN;
     t.c0 = is_long ? 0 : k * a.r;
+    t.piece = -1;
     t.nk = uni((is_long ? a.N : a.r) / C::BK);
   } else {
     const int tpb = a.rpb * a.cpg;
+    // split long tiles: consecutive indices are the pieces of one tile
+    int piece = -1;
+    if (is_long && a.splits > 1) {
+      const int tix = idx / a.splits;
+      piece = idx - tix * a.splits;
+      idx = tix;
+    }
     const int blk = idx / tpb, w = idx - blk * tpb;
     int b, j;
     if (is_long) {
@@ -162,8 +179,9 @@ __device__ __forceinline__ GTile decode(const GradArgs& a, const CycIndex& ix, b
     t.m_cnt = C::BM;
     t.n0 = j * a.r + ct * C::BN;
     t.type = is_long ? -1 : b;
-    t.c0 = 0;
-    t.nk = uni((is_long ? a.M : a.M / a.q) / C::BK);
+    t.nk = uni((is_long ? a.M / a.splits : a.M / a.q) / C::BK);
+    t.c0 = piece > 0 ? piece * t.nk : 0;
+    t.piece = piece;
   }
   return t;
 }
@@ -194,9 +212,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
     t_short = g.r / C::BK;
   } else {
     const int tpb = g.rpb * g.cpg;
-    n_long = q * tpb;
+    n_long = q * tpb * g.splits;  // pieces of the split long tiles
     n_short = q * (q - 1) * tpb;
-    t_long = g.M / C::BK;
+    t_long = g.M / g.splits / C::BK;
     t_short = g.M / q / C::BK;
   }
 
@@ -253,7 +271,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
       cp_kc = lt.c0 + lk * C::BK;
       cp_start = type_start(lt.type);
     } else {
-      const int k0 = lk * C::BK;
+      const int k0 = (lt.c0 + lk) * C::BK;  // c0: a split piece's first k-step
       cp_rbase = lt.type < 0 ? k0 : type_start(lt.type) + k0 * q;
       cp_rstep = lt.type < 0 ? 1 : q;
     }
@@ -460,10 +478,32 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
       advance_copies();
     }
 
-    // epilogue: one rounding of each fp32 sum, restaged through the wave's
-    // share of the LDS behind the stages so that each store instruction
-    // writes whole 16-byte pieces of a few rows
-    {
+    bool partial = false;
+    if constexpr (OP == Op::Dw) partial = ct.piece >= 0;
+    if (partial) {
+      // a piece of a split long tile: its fp32 sums go to the piece's partial
+      // tile (lane (l32, lhi) holds 4 consecutive columns of one row per
+      // group gg, i.e. one 16-byte piece); the reduction rounds them
+      float* P = g.part + size_t(ct.piece) * size_t(g.part_stride);
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) {
+        const size_t row = size_t(ct.out_row0 + wm * C::WTM + fm * 32 + l32);
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            const f32x16& v = acc[fm][fn];
+            const int col = ct.n0 + wn * C::WTN + fn * 32 + gg * 8 + lhi * 4;
+            const u32x4 val = {__float_as_uint(v[4 * gg]), __float_as_uint(v[4 * gg + 1]),
+                               __float_as_uint(v[4 * gg + 2]), __float_as_uint(v[4 * gg + 3])};
+            *reinterpret_cast<u32x4*>(P + row * size_t(g.N) + size_t(col)) = val;
+          }
+        }
+      }
+    } else {
+      // epilogue: one rounding of each fp32 sum, restaged through the wave's
+      // share of the LDS behind the stages so that each store instruction
+      // writes whole 16-byte pieces of a few rows
       char* ebuf = smem + C::E_OFF + wid * C::E_BYTES;
       const uint32_t col0 = uint32_t(ct.n0 + wn * C::WTN) * 2u;
       const int ostart = OP == Op::Dx ? type_start(ct.type) : 0;
@@ -500,6 +540,36 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   // the repeated copies past the last k-step land in LDS: drain them before
   // the workgroup's LDS can be handed to another workgroup
   wait_vmcnt<0>();
+}
+
+// dW of a split launch: dW[diagonal block] = bf16(sum over pieces of the fp32
+// partial tiles), pieces in order, one rounding.  One thread per 4 consecutive
+// elements of the q diagonal blocks (s x r each).  Like the persistent kernel
+// it does nothing unless the index holds a cyclic schedule of this problem
+// (on other schedules the register-staged kernel writes all of dW).
+__global__ __launch_bounds__(256) void dw_diag_reduce_kernel(const int32_t* __restrict__ ws, int q, int M,
+                                                             const float* __restrict__ part, int splits,
+                                                             int64_t stride, int N, int s, int r,
+                                                             uint16_t* __restrict__ dW) {
+  if (ws[1] != kIndexMagic || ws[2] != q || ws[3] != M || ws[4] < 0) return;
+  const int64_t r4 = r / 4;
+  const int64_t per_blk = int64_t(s) * r4;
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= q * per_blk) return;
+  const int b = int(i / per_blk);
+  const int64_t w = i - b * per_blk;
+  const int64_t f = w / r4, c4 = w - f * r4;
+  const int64_t off = (int64_t(b) * s + f) * N + int64_t(b) * r + c4 * 4;
+  u32x4 x = *reinterpret_cast<const u32x4*>(part + off);
+  float v0 = __uint_as_float(x[0]), v1 = __uint_as_float(x[1]), v2 = __uint_as_float(x[2]), v3 = __uint_as_float(x[3]);
+  for (int p = 1; p < splits; ++p) {
+    x = *reinterpret_cast<const u32x4*>(part + p * stride + off);
+    v0 += __uint_as_float(x[0]);
+    v1 += __uint_as_float(x[1]);
+    v2 += __uint_as_float(x[2]);
+    v3 += __uint_as_float(x[3]);
+  }
+  *reinterpret_cast<u32x2*>(dW + off) = pack4_bf16(v0, v1, v2, v3);
 }
 
 template <int BN>
@@ -551,8 +621,29 @@ hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
   }
   int grid = cu_count();
   grid = grid >= 8 ? grid / 8 * 8 : grid;
+  a.splits = 1;
+  a.part = nullptr;
+  a.part_stride = 0;
+  if (OP == Op::Dw && p.dw_part != nullptr) {
+    // split the long (diagonal) tiles until a piece is no longer than the
+    // average k-steps per workgroup
+    const int64_t tpb = int64_t(a.rpb) * a.cpg;
+    const int64_t t_long = p.M / C::BK, t_short = p.M / p.q / C::BK;
+    const int64_t total = p.q * tpb * t_long + p.q * (p.q - 1) * tpb * t_short;
+    const int64_t avg = (total + grid - 1) / grid;
+    int sp = 1;
+    while (sp * 2 <= kDwMaxSplits && t_long % (sp * 2) == 0 && t_long / sp > avg) sp *= 2;
+    a.splits = sp;
+    a.part = static_cast<float*>(p.dw_part);
+    a.part_stride = p.K * p.N;
+  }
   const size_t shm = C::LDS_BYTES;
   hipLaunchKernelGGL((grad_persistent_kernel<C, OP>), dim3(grid), dim3(C::THREADS), shm, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  const int64_t threads = p.q * int64_t(a.s) * (a.r / 4);
+  hipLaunchKernelGGL(dw_diag_reduce_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, p.ws, a.q, a.M,
+                     a.part, a.splits, a.part_stride, a.N, a.s, a.r, static_cast<uint16_t*>(p.C));
   return hipGetLastError();
 }
 

@@ -133,14 +133,17 @@ int qalg_version(void);
 size_t qalg_workspace_bytes(int32_t q, int64_t M);
 
 /*
- * Workspace that also lets qalg_backward_dw split the contraction of each
- * output tile over several workgroups on its register-staged path (listed
- * schedules, the recursive law, shapes the persistent gradient kernel does
- * not take): qalg_workspace_bytes(q, M) plus fp32 scratch for up to 16
+ * Workspace that also lets qalg_backward_dw split contractions over several
+ * workgroups: qalg_workspace_bytes(q, M) plus fp32 scratch for up to 16
  * partial sums of the K x N gradient, summed in a fixed order afterwards
- * (bitwise reproducible, one rounding).  A smaller workspace (at least
- * qalg_workspace_bytes(q, M)) gives the same result without the split.
- * Returns 0 for invalid sizes.
+ * (bitwise reproducible, one rounding).  On the register-staged path (listed
+ * schedules, the recursive law, shapes the persistent gradient kernel does
+ * not take) every output tile may be split; on the persistent path (cyclic
+ * schedules) the diagonal blocks W_jj, whose tiles contract over all M rows
+ * against M/q for the others, are cut into pieces no longer than a
+ * workgroup's average share.  A smaller workspace (at least
+ * qalg_workspace_bytes(q, M)) gives the result without the split (equal
+ * within the fp32 summation order).  Returns 0 for invalid sizes.
  */
 size_t qalg_workspace_bytes_dw(int32_t q, int64_t M, int64_t K, int64_t N);
 

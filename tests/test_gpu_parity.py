@@ -294,3 +294,40 @@ def test_gated_forward_matches_oracle(shape):
     if bad:
         rows = np.where((tau < 0) | (tau >= q))[0]
         assert np.all(to_f64(H)[rows] == 0.0)
+
+
+DW_SPLIT_SHAPES = [
+    # M, K, N, q, tau kind, offset: persistent dW shapes (cyclic) whose diagonal
+    # tiles get split over several workgroups when the dW scratch is given
+    (4096, 2048, 2048, 8, "cyclic", 3),   # 16 pieces of 8 k-steps per diagonal tile
+    (2048, 1024, 1536, 4, "cyclic", 1),   # 256x192 tiles, 16 pieces
+    (2048, 512, 512, 1, "zeros", 0),      # q = 1: every tile is diagonal
+    (2048, 1024, 1536, 4, "random", 0),   # listed schedule: no split, the reduction must not touch dW
+]
+
+
+@pytest.mark.parametrize("shape", DW_SPLIT_SHAPES, ids=[f"M{s[0]}K{s[1]}N{s[2]}q{s[3]}{s[4]}" for s in DW_SPLIT_SHAPES])
+def test_dw_split_contraction_matches_oracle(shape):
+    """dW with the split-contraction scratch (App B eq 33-35): diagonal blocks summed from fp32
+    pieces in a fixed order; against the oracle, bitwise the same on a second call, and within the
+    bar of the unsplit launch."""
+    torch = torch_cuda()
+    M, K, N, q, kind, off = shape
+    say(f"[dw split] M={M} K={K} N={N} q={q} tau={kind} offset={off}")
+    X, _, dY = _inputs(M, K, N, "bf16", 7300 + M)
+    tau = make_tau(kind, M, q, seed=M, offset=off)
+    Xd, dYd, td = to_dev(X), to_dev(dY), tau_dev(tau)
+    ws_split = Q.workspace(q, M, dw_shape=(K, N))
+    ws_plain = Q.workspace(q, M)
+    # the scratch holds stale partials of an earlier call: fill it with garbage first
+    ws_split[Q.qalg_workspace_bytes(q, M):].fill_(0x7f)
+    dW1 = torch.full((K, N), 3.0, dtype=torch.bfloat16, device="cuda")
+    Q.qalg_backward_dw(Xd, dYd, td, q, dW=dW1, ws=ws_split)
+    dW2 = Q.qalg_backward_dw(Xd, dYd, td, q, ws=ws_split, flags=Q.QALG_FLAG_INDEX_READY)
+    dW0 = Q.qalg_backward_dw(Xd, dYd, td, q, ws=ws_plain)
+    torch.cuda.synchronize()
+    assert torch.equal(dW1, dW2), "split dW is not reproducible"
+    _, dWr = O.row_typed_backward(X.f64, np.zeros((K, N)), dY.f64, tau, q)
+    e1 = assert_groups(rel_frob_blocks(to_f64(dW1), dWr, q), BF16_TOL, "dW split")
+    e0 = assert_groups(rel_frob_blocks(to_f64(dW0), dWr, q), BF16_TOL, "dW unsplit")
+    say(f"    max rel err  dW split {e1:.2e}  unsplit {e0:.2e}")
