@@ -103,13 +103,25 @@ __global__ __launch_bounds__(kIdxThreads) void build_index_kernel(
   if (tid == 0) s_cyclic = (M > 0 && t0 >= 0 && t0 < q) ? 1 : 0;
   __syncthreads();
   if (s_cyclic) {
+    // kBatch independent loads per thread before any comparison, so that a
+    // thread waits for one memory latency per batch instead of one per row
     const int step = kIdxThreads % q;
     int want = (t0 + tid) % q;  // (t0 + m) mod q for m = tid + kIdxThreads k
     bool ok = true;
-    for (int m = tid; m < M; m += kIdxThreads) {
-      ok = ok && tau[m] == want;
-      want += step;
-      if (want >= q) want -= q;
+    for (int m0 = tid; m0 < M; m0 += kIdxThreads * kBatch) {
+      int tv[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int m = m0 + b * kIdxThreads;
+        tv[b] = m < M ? tau[m] : 0;
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int m = m0 + b * kIdxThreads;
+        ok &= m >= M || tv[b] == want;
+        want += step;
+        if (want >= q) want -= q;
+      }
     }
     if (!ok) s_cyclic = 0;
   }

@@ -152,6 +152,24 @@ def test_index_edge_cases_bit_exact(M, q, kind, bad):
     assert Q.qalg_read_status(ws, q, M) == bad
 
 
+@pytest.mark.parametrize("M,q,off,swap", [(16384, 8, 0, None), (20000, 8, 3, None), (4099, 3, 2, None),
+                                          (16384, 8, 0, (0, 1)), (16384, 8, 0, (9000, 9001)),
+                                          (20000, 8, 3, (19998, 19999)), (3000, 4, 1, (1500, 2999))])
+def test_cyclic_detection_bit_exact(M, q, off, swap):
+    """The index recognises (o + m) mod q at any offset o (its rows are then computed, not listed) and
+    rejects a schedule that breaks it anywhere: two rows of different types swapped (same counts)."""
+    torch = torch_cuda()
+    tau = make_tau("cyclic", M, q, offset=off)
+    if swap is not None:
+        a, b = swap
+        tau[a], tau[b] = tau[b], tau[a]
+    ws = Q.qalg_build_index(tau_dev(tau), q)
+    torch.cuda.synchronize()
+    _check_index(ws, tau, q)
+    w = ws.view(dtype=torch.int32).cpu().numpy()
+    assert w[4] == (off if swap is None else -1)
+
+
 def test_unit_law_is_bitwise():
     """A diagonal bank of identity maps is the identity projection (section 4): Y == X exactly."""
     torch = torch_cuda()
