@@ -22,7 +22,8 @@ Reported (one JSON line):
   cpu_baseline     the fp64 CPU oracle on the host cores (a bounded sample)
   extra            further legs, each timed separately: training (forward + dX +
                    dW at the same shape), small-M decode (64 experts), gated
-                   SwiGLU FFN (forward and training step), the pilot FFN under
+                   SwiGLU FFN (forward and training step), the 64-expert shapes at
+                   M = 1..1024 against q = 1, the pilot FFN under
                    Q_2^(x)2 / Q_4 / q = 1, few rows per type (q = 32), algebraic
                    attention, the graph law Q_G and unequal group widths (forward,
                    dX, dW each)
@@ -191,6 +192,7 @@ def main() -> int:
     if not args.no_extra:
         extra["training"] = training_leg(Q, torch, np, synth, dev, stream)
         extra["decode"] = decode_leg(Q, torch, np, synth, dev, stream)
+        extra["experts"] = experts_leg(Q, torch, np, synth, dev, stream)
         extra["gated_ffn"] = gated_leg(Q, torch, np, synth, dev, stream)
         extra["pilot_ffn"] = pilot_leg(Q, torch, np, synth, dev, stream)
         extra["few_rows"] = few_rows_leg(Q, torch, np, synth, dev, stream)
@@ -712,6 +714,64 @@ def decode_leg(Q, torch, np, synth, dev, stream):
            "algorithmic_bytes": byts, "GBs": round(byts / (ms * 1e-3) / 1e9, 1),
            "frac_hbm": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "protocol": "flushed (1 GiB written, then read)"}
     log(f"[bench] decode leg: {res}")
+    return res
+
+
+def experts_leg(Q, torch, np, synth, dev, stream):
+    """Narrow MoE expert shapes (section 7.1's expert projections): 64 experts, each with its own
+    bank, M in {1, 8, 64, 256, 1024} tokens per expert at random absolute positions (tau = p mod q),
+    (7168 -> 2048, q = 4), (2048 -> 768, q = 4 and q = 8).  Each launch is timed alone after a
+    1 GiB cache flush (the 64 banks of 2048 x 768 would otherwise sit in the MALL), against the
+    same kernels at q = 1.  X and positions of M rows are the first M rows of the 1024-row draws
+    (the seeded streams are prefix-consistent), as in the parity test of this workload."""
+    c, E, MS = 4, 64, (1, 8, 64, 256, 1024)
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def flushed(fn, reps=8):
+        times = []
+        for k in range(reps + 2):
+            flush.fill_(k & 0xFF)
+            flush.view(torch.float32).sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        return float(np.median(times[2:]))
+
+    res = {"workload": "experts_64_bf16", "protocol": "flushed (1 GiB written, then read), median of 8"}
+    pos_all = np.stack([synth.random_positions(1000 * c + 200 + e, MS[-1]) for e in range(E)])
+    for K, N in ((7168, 2048), (2048, 768)):
+        with ThreadPoolExecutor(max_workers=8) as ex:
+            Wb = list(ex.map(lambda e: synth.normal_operand(1000 * c + 100 + e, (K, N), K ** -0.5, "bf16").bits,
+                             range(E)))
+            Xb = list(ex.map(lambda e: synth.normal_operand(1000 * c + 300 + e, (MS[-1], K), 1.0, "bf16").bits,
+                             range(E)))
+        W = to(np.stack(Wb))
+        X_all = to(np.stack(Xb))
+        del Wb, Xb
+        for q in ((4,) if K == 7168 else (4, 8)):
+            s, r = K // q, N // q
+            for Mx in MS:
+                X = X_all[:, :Mx].contiguous()
+                taus = (pos_all[:, :Mx] % q).astype(np.int32)
+                tau = torch.from_numpy(taus).to(dev)
+                tau1 = torch.zeros_like(tau)
+                Y = torch.empty(E, Mx, N, dtype=torch.bfloat16, device=dev)
+                ws, ws1 = Q.workspace(q, Mx, E, device=dev), Q.workspace(1, Mx, E, device=dev)
+                t_q = flushed(lambda: Q.qalg_forward_batched(X, W, tau, q, Y=Y, ws=ws, stream=stream))
+                t_1 = flushed(lambda: Q.qalg_forward_batched(X, W, tau1, 1, Y=Y, ws=ws1, stream=stream))
+                flop = 2.0 * rho(q) * E * Mx * K * N
+                wblocks = sum(q + (q - 1) * len(set(int(t) for t in taus[e])) for e in range(E))
+                byts = wblocks * s * r * 2 + E * Mx * (K + N) * 2
+                res[f"{K}x{N}_q{q}_M{Mx}"] = {
+                    "ms": round(t_q, 4), "q1_ms": round(t_1, 4), "speedup_vs_q1": round(t_1 / t_q, 3),
+                    "algebra_tflops": round(flop / (t_q * 1e-3) / 1e12, 1),
+                    "GBs": round(byts / (t_q * 1e-3) / 1e9, 1)}
+        del W, X_all
+    log(f"[bench] experts leg: {res}")
     return res
 
 

@@ -1013,6 +1013,14 @@ hipError_t launch_cfg(const ProblemDesc& p, hipStream_t s, bool skip_cyclic) {
 using Cfg128 = TileCfg<128, 128, 64, 2, 2>;
 using Cfg64 = TileCfg<64, 64, 64, 2, 2>;
 using Cfg32 = TileCfg<32, 64, 64, 1, 2>;
+// few rows per type, wider column tiles: each weight row is read as 256 or 512
+// contiguous bytes instead of 128, and a launch has 2-4x fewer tiles, each
+// re-reading the diagonal block W_jj (measured on 64 experts, 7168 -> 2048,
+// q = 4: M = 64 0.59 -> 0.48 ms, M = 256 0.99 -> 0.74 ms)
+using CfgN32 = TileCfg<32, 256, 64, 1, 4>;
+using CfgN64 = TileCfg<64, 256, 64, 1, 4>;
+using CfgM32 = TileCfg<32, 128, 64, 1, 2>;
+using CfgM64 = TileCfg<64, 128, 64, 2, 2>;
 // dW on wide groups: 256- or 192-feature tiles with 32-deep k-steps (twice the
 // MFMA work per loaded byte of the 128 x 128 tile, whose loads saturate the
 // vector-memory path)
@@ -1041,6 +1049,21 @@ bool dw_tiles_exact(const ProblemDesc& p, int bm, int bn) {
   return true;
 }
 
+// Column-tile width of the forward's few-rows tiles (64, 128 or 256) for output
+// groups of width r: the share of each tile's columns inside the group, times
+// the relative streaming efficiency of the width (1, 0.9, 0.75: wider weight
+// rows stream better), largest wins, ties to the wider tile
+int fwd_small_bn(int64_t r) {
+  int best = 64;
+  double best_v = -1.0;
+  for (int bn : {256, 128, 64}) {
+    const double fill = double(r) / double(((r + bn - 1) / bn) * bn);
+    const double v = fill * (bn == 256 ? 1.0 : bn == 128 ? 0.9 : 0.75);
+    if (v > best_v + 1e-9) best = bn, best_v = v;
+  }
+  return best;
+}
+
 }  // namespace
 
 hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s, bool skip_cyclic) {
@@ -1051,6 +1074,15 @@ hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s, bool skip_cycl
       // wide tiles where every type has rows for several and the output groups divide evenly
       if (per_type >= 512 && cols_exact(p, 256)) return launch_cfg<Op::Fwd, CfgW256>(p, s, skip_cyclic);
       if (per_type >= 128) return launch_cfg<Op::Fwd, Cfg128>(p, s, skip_cyclic);
+      if (p.in_widths == nullptr) {
+        const int bn = fwd_small_bn(p.N / p.q);
+        if (bn == 256)
+          return per_type >= 48 ? launch_cfg<Op::Fwd, CfgN64>(p, s, skip_cyclic)
+                                : launch_cfg<Op::Fwd, CfgN32>(p, s, skip_cyclic);
+        if (bn == 128)
+          return per_type >= 48 ? launch_cfg<Op::Fwd, CfgM64>(p, s, skip_cyclic)
+                                : launch_cfg<Op::Fwd, CfgM32>(p, s, skip_cyclic);
+      }
       if (per_type >= 48) return launch_cfg<Op::Fwd, Cfg64>(p, s, skip_cyclic);
       return launch_cfg<Op::Fwd, Cfg32>(p, s, skip_cyclic);
     case Op::Dx:

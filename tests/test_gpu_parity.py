@@ -349,3 +349,42 @@ def test_dw_split_contraction_matches_oracle(shape):
     e1 = assert_groups(rel_frob_blocks(to_f64(dW1), dWr, q), BF16_TOL, "dW split")
     e0 = assert_groups(rel_frob_blocks(to_f64(dW0), dWr, q), BF16_TOL, "dW unsplit")
     say(f"    max rel err  dW split {e1:.2e}  unsplit {e0:.2e}")
+
+
+FEW_ROWS_SHAPES = [
+    # M, K, N, q, tau kind, offset, bad rows: forward tiles of 32 / 64 rows and 256 / 128
+    # columns (few rows per type), every output element against the oracle
+    (200, 512, 1024, 4, "random", 0, 0),   # 64 x 256 tiles (r = 256)
+    (100, 768, 2048, 4, "random", 0, 5),   # 32 x 256 tiles (r = 512), rows without a type
+    (150, 512, 768, 8, "random", 0, 0),    # 32 x 128 tiles (r = 96: one ragged tile per group)
+    (400, 256, 768, 8, "cyclic", 3, 0),    # 64 x 128 tiles, type offset
+    (120, 1024, 1536, 4, "random", 0, 0),  # 32 x 128 tiles (r = 384)
+    (90, 512, 832, 4, "random", 0, 3),     # 32 x 256 tiles, ragged (r = 208)
+]
+
+
+@pytest.mark.parametrize("shape", FEW_ROWS_SHAPES, ids=[f"M{s[0]}K{s[1]}N{s[2]}q{s[3]}" for s in FEW_ROWS_SHAPES])
+def test_few_rows_wide_tiles_match_oracle(shape):
+    """The register-staged forward's few-rows tiles (eq 16-17), forced on one problem and as three
+    experts of a batched call, every output group against the oracle; rows without a type are zero."""
+    torch = torch_cuda()
+    M, K, N, q, kind, off, bad = shape
+    say(f"[few rows] M={M} K={K} N={N} q={q} tau={kind} bad={bad}")
+    X, W, _ = _inputs(M, K, N, "bf16", 7700 + M)
+    tau = make_tau(kind, M, q, seed=M + 1, offset=off, bad=bad)
+    Y = Q.qalg_forward(to_dev(X), to_dev(W), tau_dev(tau), q, flags=Q.QALG_FLAG_FORCE_TILED)
+    torch.cuda.synchronize()
+    Yr = O.row_typed_forward(X.f64, W.f64, tau, q)
+    e = assert_groups(rel_frob_col_groups(to_f64(Y), Yr, q), BF16_TOL, "Y")
+    badrows = (tau < 0) | (tau >= q)
+    assert not to_f64(Y)[badrows].any()
+    # three experts: the same bank for all, types shifted per expert
+    taus = np.stack([make_tau(kind, M, q, seed=M + 1 + x, offset=off, bad=bad) for x in range(3)])
+    Xd = torch.stack([to_dev(X)] * 3)
+    Wd = torch.stack([to_dev(W)] * 3)
+    Yb = Q.qalg_forward_batched(Xd, Wd, tau_dev(taus), q)
+    torch.cuda.synchronize()
+    for x in range(3):
+        Ybr = O.row_typed_forward(X.f64, W.f64, taus[x], q)
+        assert_groups(rel_frob_col_groups(to_f64(Yb[x]), Ybr, q), BF16_TOL, f"Y expert {x}")
+    say(f"    max rel err {e:.2e}")

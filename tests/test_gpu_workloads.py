@@ -221,7 +221,7 @@ def test_gated_ffn_training_q8_sampled():
     dY = synth.normal_operand(1000 * c + 5, (M, D), 1.0, "bf16")
     pos = torch.from_numpy(synth.cyclic_positions(M)).to("cuda")
     td = Q.qalg_type_schedule(pos, q)
-    ws = Q.workspace(q, M)
+    ws = Q.workspace(q, M, dw_shape=(D, 2 * F))  # as the benchmark: dW may split its diagonal tiles
     Q.qalg_build_index(td, q, ws=ws)
     r = Q.QALG_FLAG_INDEX_READY
     Xd, Wdd, dYd = to_dev(X), to_dev(Wd), to_dev(dY)
