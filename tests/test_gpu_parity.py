@@ -321,6 +321,7 @@ DW_SPLIT_SHAPES = [
     (2048, 1024, 1536, 4, "cyclic", 1),   # 256x192 tiles, 16 pieces
     (2048, 512, 512, 1, "zeros", 0),      # q = 1: every tile is diagonal
     (2048, 1024, 1536, 4, "random", 0),   # listed schedule: no split, the reduction must not touch dW
+    (3072, 768, 768, 3, "cyclic", 2),     # odd q: 16 pieces of 6 k-steps
 ]
 
 
@@ -388,3 +389,19 @@ def test_few_rows_wide_tiles_match_oracle(shape):
         Ybr = O.row_typed_forward(X.f64, W.f64, taus[x], q)
         assert_groups(rel_frob_col_groups(to_f64(Yb[x]), Ybr, q), BF16_TOL, f"Y expert {x}")
     say(f"    max rel err {e:.2e}")
+
+
+def test_dw_split_then_smaller_problem_on_one_workspace():
+    """Two split dW calls in a row on one workspace, the second smaller (fewer rows and types): the
+    second result must not depend on the first call's partials left in the scratch."""
+    torch = torch_cuda()
+    big, small = (4096, 2048, 2048, 8), (2048, 1024, 1024, 4)
+    ws = Q.workspace(big[3], big[0], dw_shape=(big[1], big[2]))
+    for (M, K, N, q) in (big, small):
+        say(f"[dw split reuse] M={M} K={K} N={N} q={q}")
+        X, _, dY = _inputs(M, K, N, "bf16", 7400 + M)
+        tau = make_tau("cyclic", M, q, offset=1)
+        dW = Q.qalg_backward_dw(to_dev(X), to_dev(dY), tau_dev(tau), q, ws=ws)
+        torch.cuda.synchronize()
+        _, dWr = O.row_typed_backward(X.f64, np.zeros((K, N)), dY.f64, tau, q)
+        assert_groups(rel_frob_blocks(to_f64(dW), dWr, q), BF16_TOL, "dW")
