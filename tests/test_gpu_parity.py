@@ -28,6 +28,7 @@ SHAPES = [
     (2600, 1024, 2304, 4, "cyclic", 0, 0),   # persistent 256x192 tiles (r = 576 = 3 x 192)
     (2048, 1024, 1536, 4, "cyclic", 1, 0),   # persistent dX and dW (dW tiles 256x192)
     (4096, 2048, 2048, 8, "cyclic", 3, 0),   # persistent dX and dW (256x256), long/short balance
+    (2100, 768, 512, 4, "random", 0, 7),     # listed types, 525 rows per type: register-staged dX and dW
 ]
 
 
