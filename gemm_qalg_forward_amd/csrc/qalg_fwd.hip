@@ -114,7 +114,8 @@ struct FwdCfg {
   static_assert(!GATED || FN % 2 == 0, "gate and up halves of a wave tile");
   static constexpr int E_PITCH = OUT_WTN * 2;      // bytes per restaged row
   static constexpr int E_NP = OUT_WTN / 8;         // 16-byte pieces per row
-  static constexpr int E_BYTES = 32 * E_PITCH;
+  // gated: a 32-row slice of one half (gate or up) of the wave's columns in fp32
+  static constexpr int E_BYTES = GATED ? 32 * OUT_WTN * 4 : 32 * E_PITCH;
   static constexpr int E_MASK = E_NP == 12 ? 3 : E_NP - 1;  // piece swizzle: p ^ (row & E_MASK)
   static_assert(E_NP % 2 == 0 && (E_NP == 12 || (E_NP & E_MASK) == 0), "epilogue buffer");
   static constexpr int E_OFF = kStages * STAGE;
@@ -631,35 +632,79 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
       const uint32_t col0 = uint32_t((C::GATED ? ct.n0 / 2 : ct.n0) + wn * C::OUT_WTN) * 2u;
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm) {
-        // lane (l32, lhi) holds row l32, columns fn*32 + g*8 + lhi*4 .. +3
-        constexpr int FO = C::GATED ? C::FN / 2 : C::FN;  // 32-column output blocks per wave
+        if constexpr (C::GATED) {
+          // h = silu(gate) * up in fp32, one rounding.  Gate column c sits in
+          // block fn, its up column in block fn + FN/2 (same lane and
+          // register).  Reading the two blocks together makes the register
+          // allocator spill the accumulators, so each half goes through the
+          // wave's LDS share in fp32 on its own: the gate half is written and
+          // read back row-contiguous, then the up half at the same positions.
+          // Slice layout: row l32 of 64 fp32 in 16-byte pieces, piece p kept
+          // at p ^ (row & 15) (conflict-free for both the writes and the reads).
+          constexpr int HN = C::FN / 2;  // 32-column blocks per half
+          static_assert(HN * 32 == C::OUT_WTN && C::OUT_WTN == 64, "gated slice layout");
+          auto write_half = [&](int fb) {
 #pragma unroll
-        for (int fn = 0; fn < FO; ++fn) {
+            for (int fn = 0; fn < HN; ++fn)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const f32x16& v = acc[fm][fb + fn];
+                const int pc = (fn * 8 + g * 2 + lhi) ^ (l32 & 15);
+                *reinterpret_cast<u32x4*>(ebuf + l32 * 256 + pc * 16) =
+                    (u32x4){__float_as_uint(v[4 * g]), __float_as_uint(v[4 * g + 1]),
+                            __float_as_uint(v[4 * g + 2]), __float_as_uint(v[4 * g + 3])};
+              }
+          };
+          // lane: row it * 8 + lane / 8, output piece lane % 8 (8 columns)
+          auto read_piece = [&](int it, float (&x)[8]) {
+            const int row = it * 8 + (lane >> 3), p8 = lane & 7;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const u32x4 w = *reinterpret_cast<const u32x4*>(ebuf + row * 256 + (((2 * p8 + h2) ^ (row & 15)) << 4));
+#pragma unroll
+              for (int e = 0; e < 4; ++e) x[4 * h2 + e] = __uint_as_float(w[e]);
+            }
+          };
+          float gate[4][8];
+          write_half(0);
+#pragma unroll
+          for (int it = 0; it < 4; ++it) read_piece(it, gate[it]);
+          write_half(HN);
+#pragma unroll
+          for (int it = 0; it < 4; ++it) {
+            float up[8], h[8];
+            read_piece(it, up);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float gv = gate[it][e];
+              // sigmoid through the hardware reciprocal (about 1 ulp; the
+              // result is rounded to bf16 next)
+              h[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * up[e];
+            }
+            const u32x2 lo = pack4_bf16(h[0], h[1], h[2], h[3]), hi = pack4_bf16(h[4], h[5], h[6], h[7]);
+            const u32x4 val = {lo[0], lo[1], hi[0], hi[1]};
+            const int row = it * 8 + (lane >> 3), p8 = lane & 7;
+            const int ml = wm * C::WTM + fm * 32 + row;
+            int orow;
+            if constexpr (CYC)
+              orow = row_of(ct, ml);
+            else
+              orow = __shfl(out_row[fm], row);
+            // a store instruction writes 8 whole 128-byte output rows
+            if (ml < ct.m_cnt)
+              __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(a.Y + (uint32_t(orow) * y_bytes + col0 + uint32_t(p8) * 16u)));
+          }
+          continue;
+        }
+        // lane (l32, lhi) holds row l32, columns fn*32 + g*8 + lhi*4 .. +3
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const f32x16& v = acc[fm][fn];
             const int pc = (fn * 4 + g) ^ (l32 & C::E_MASK);
-            u32x2 packed;
-            if constexpr (C::GATED) {
-              // gate column c sits in block fn, its up column in block fn + FN/2,
-              // same lane and register: h = silu(gate) * up in fp32, one rounding
-              const f32x16& u = acc[fm][fn + C::FN / 2];
-              float h[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float gv = v[4 * g + e];
-                // sigmoid through the hardware reciprocal (about 1 ulp; the
-                // result is rounded to bf16 next)
-                h[e] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * u[4 * g + e];
-              }
-              packed = pack4_bf16(h[0], h[1], h[2], h[3]);
-            } else {
-              packed = pack4_bf16(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
-            }
+            const u32x2 packed = pack4_bf16(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
             *reinterpret_cast<u32x2*>(ebuf + l32 * C::E_PITCH + pc * 16 + lhi * 8) = packed;
-            // gated: keep one group's values live at a time (else the
-            // activation work of a whole block is interleaved and spills)
-            if constexpr (C::GATED) __builtin_amdgcn_sched_barrier(0);
           }
         }
         // read back: 64 lanes take 64 consecutive (row, piece) slots per instruction
