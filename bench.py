@@ -452,8 +452,9 @@ def gated_leg(Q, torch, np, synth, dev, stream):
 
 
 def gated_train(Q, torch, np, synth, dev, stream, Xd, Wgu, Wdd, tau, ws, H, Y, flop):
-    """Training step of the gated FFN on the merged layout: merged forward, pointwise SwiGLU, down
-    forward; down dX and dW, pointwise SwiGLU VJP, merged dX and dW.  9 projections (section 6.2)."""
+    """Training step of the gated FFN on the merged layout: merged forward keeping the pre-activations
+    with H computed in the same launch, down forward; down dX and dW, pointwise SwiGLU VJP, merged dX
+    and dW.  9 projections (section 6.2)."""
     r = Q.QALG_FLAG_INDEX_READY
     dY = torch.from_numpy(synth.normal_operand(6005, (M, D), 1.0, "bf16").bits.view(np.int16)).view(
         torch.bfloat16).to(dev)
@@ -464,8 +465,9 @@ def gated_train(Q, torch, np, synth, dev, stream, Xd, Wgu, Wdd, tau, ws, H, Y, f
     dWd = torch.empty(F, D, dtype=torch.bfloat16, device=dev)
     dWgu = torch.empty(D, 2 * F, dtype=torch.bfloat16, device=dev)
     ops = [
-        ("fwd_gate_up", lambda: Q.qalg_forward(Xd, Wgu, tau, QQ, Y=GU, ws=ws, flags=r, stream=stream)),
-        ("swiglu_fwd", lambda: Q.qalg_swiglu_forward(GU, QQ, H=H, stream=stream)),
+        # gate/up products kept in bf16 for the VJP, and H from them, in one launch
+        ("fwd_gate_up", lambda: Q.qalg_gated_forward_keep(Xd, Wgu, tau, QQ, H=H, GU=GU, ws=ws, flags=r,
+                                                          stream=stream)),
         ("fwd_down", lambda: Q.qalg_forward(H, Wdd, tau, QQ, Y=Y, ws=ws, flags=r, stream=stream)),
         ("dx_down", lambda: Q.qalg_backward_dx(dY, Wdd, tau, QQ, dX=dH, ws=ws, flags=r, stream=stream)),
         ("dw_down", lambda: Q.qalg_backward_dw(H, dY, tau, QQ, dW=dWd, ws=ws, flags=r, stream=stream)),
@@ -493,7 +495,6 @@ def gated_train(Q, torch, np, synth, dev, stream, Xd, Wgu, Wdd, tau, ws, H, Y, f
     out = {f"{k}_ms": round(v, 4) for k, v in ms.items()}
     out["step_ms"] = round(step, 4)
     out["step_tflops"] = round(9 * flop / (step * 1e-3) / 1e12, 1)  # 9 projection-shaped products
-    out["swiglu_fwd_GBs"] = round(6.0 * M * F / (ms["swiglu_fwd"] * 1e-3) / 1e9, 1)   # gate, up in; H out
     out["swiglu_bwd_GBs"] = round(10.0 * M * F / (ms["swiglu_bwd"] * 1e-3) / 1e9, 1)  # gate, up, dH in; 2 out
     return out
 

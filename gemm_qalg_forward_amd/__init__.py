@@ -9,7 +9,7 @@ Functions carry the C names:
     qalg_forward, qalg_forward_graph, qalg_backward_dx, qalg_backward_dw, qalg_forward_batched,
     qalg_backward_dx_graph, qalg_backward_dw_graph, qalg_forward_widths, qalg_backward_dx_widths,
     qalg_backward_dw_widths,
-    qalg_gated_forward, qalg_merge_gate_up, qalg_split_gate_up, qalg_swiglu_forward, qalg_swiglu_backward,
+    qalg_gated_forward, qalg_gated_forward_keep, qalg_merge_gate_up, qalg_split_gate_up, qalg_swiglu_forward, qalg_swiglu_backward,
     qalg_attention_forward,
     qalg_type_schedule, qalg_build_index, qalg_build_index_batched,
     qalg_read_status, qalg_workspace_bytes, qalg_index_layout,
@@ -30,7 +30,7 @@ __all__ = [
     "qalg_forward", "qalg_forward_graph", "qalg_backward_dx", "qalg_backward_dw", "qalg_forward_batched",
     "qalg_backward_dx_graph", "qalg_backward_dw_graph", "qalg_forward_widths", "qalg_backward_dx_widths",
     "qalg_backward_dw_widths",
-    "qalg_gated_forward", "qalg_merge_gate_up", "qalg_split_gate_up", "qalg_swiglu_forward",
+    "qalg_gated_forward", "qalg_gated_forward_keep", "qalg_merge_gate_up", "qalg_split_gate_up", "qalg_swiglu_forward",
     "qalg_swiglu_backward", "qalg_attention_forward", "qalg_read_status", "workspace",
 ]
 
@@ -83,6 +83,8 @@ _SIGS = {
     "qalg_backward_dw": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
     "qalg_forward_batched": (ctypes.c_int, [_c_i32, _vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
     "qalg_gated_forward": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
+    "qalg_gated_forward_keep": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i32, _vp,
+                                               _c_size, _c_u32, _vp]),
     "qalg_merge_gate_up": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i64, _vp, _c_i32, _vp]),
     "qalg_split_gate_up": (ctypes.c_int, [_vp, _c_i32, _c_i64, _c_i64, _vp, _vp, _c_i32, _vp]),
     "qalg_swiglu_forward": (ctypes.c_int, [_vp, _c_i32, _c_i64, _c_i64, _vp, _c_i32, _vp]),
@@ -485,6 +487,30 @@ def qalg_gated_forward(X, Wgu, tau, q: int, H=None, ws=None, flags: int = 0, str
     if K2 != K or F2 % 2:
         raise ValueError("X and Wgu shapes differ (Wgu is K x 2F)")
     return _proj("qalg_gated_forward", X, Wgu, tau, q, H, (M, F2 // 2), ws, flags, stream, M, K, F2 // 2)
+
+
+def qalg_gated_forward_keep(X, Wgu, tau, q: int, H=None, GU=None, ws=None, flags: int = 0, stream=None):
+    """The training step's gated forward: GU = bf16 merged pre-activations [M, 2F] and
+    H = silu(gate) * up [M, F] from those rounded values, one launch; returns (H, GU)."""
+    torch = _torch()
+    M, K = X.shape
+    K2, F2 = Wgu.shape
+    if K2 != K or F2 % 2:
+        raise ValueError("X and Wgu shapes differ (Wgu is K x 2F)")
+    if X.dtype != Wgu.dtype:
+        raise TypeError("operands must share a dtype")
+    _tau_check(tau, M)
+    if H is None:
+        H = torch.empty((M, F2 // 2), dtype=X.dtype, device=X.device)
+    if GU is None:
+        GU = torch.empty((M, F2), dtype=X.dtype, device=X.device)
+    if ws is None:
+        ws = workspace(q, M, device=X.device)
+    _check("qalg_gated_forward_keep", lib().qalg_gated_forward_keep(
+        _dev_ptr(X, "X"), _dev_ptr(Wgu, "Wgu"), _dev_ptr(tau, "tau"), q, M, K, F2 // 2, _dev_ptr(H, "H"),
+        _dev_ptr(GU, "GU"), _dtype_code(X), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags,
+        _stream(stream)))
+    return H, GU
 
 
 def qalg_forward_batched(X, W, tau, q: int, Y=None, ws=None, flags: int = 0, stream=None):

@@ -454,9 +454,31 @@ qalg_status qalg_forward_batched(int32_t E, const void* X, const void* W, const 
   return run_projection(Op::Fwd, E, X, W, tau, q, M, K, N, Y, dtype, ws, ws_bytes, flags, stream);
 }
 
+namespace {
+// shared by the gated forward and its variant that keeps the pre-activations (GU may be null)
+qalg_status run_gated(const void* X, const void* Wgu, const int32_t* tau, int32_t q, int64_t M, int64_t K,
+                      int64_t F, void* H, void* GU, int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags,
+                      void* stream);
+}  // namespace
+
 qalg_status qalg_gated_forward(const void* X, const void* Wgu, const int32_t* tau, int32_t q, int64_t M,
                                int64_t K, int64_t F, void* H, int32_t dtype, void* ws, size_t ws_bytes,
                                uint32_t flags, void* stream) {
+  return run_gated(X, Wgu, tau, q, M, K, F, H, nullptr, dtype, ws, ws_bytes, flags, stream);
+}
+
+qalg_status qalg_gated_forward_keep(const void* X, const void* Wgu, const int32_t* tau, int32_t q, int64_t M,
+                                    int64_t K, int64_t F, void* H, void* GU, int32_t dtype, void* ws,
+                                    size_t ws_bytes, uint32_t flags, void* stream) {
+  if (M > 0 && GU == nullptr) return QALG_ERR_NULL;
+  if (GU != nullptr && !aligned16(GU)) return QALG_ERR_ALIGN;
+  return run_gated(X, Wgu, tau, q, M, K, F, H, GU, dtype, ws, ws_bytes, flags, stream);
+}
+
+namespace {
+qalg_status run_gated(const void* X, const void* Wgu, const int32_t* tau, int32_t q, int64_t M, int64_t K,
+                      int64_t F, void* H, void* GU, int32_t dtype, void* ws, size_t ws_bytes, uint32_t flags,
+                      void* stream) {
   if (dtype != QALG_BF16) return QALG_ERR_DTYPE;
   if (flags & ~uint32_t(QALG_FLAG_INDEX_READY | QALG_FLAG_LAW_TENSOR)) return QALG_ERR_ARG;
   if (M < 0 || K <= 0 || F <= 0 || M > INT32_MAX / 2 || K > INT32_MAX / 2 || F > INT32_MAX / 4)
@@ -487,12 +509,14 @@ qalg_status qalg_gated_forward(const void* X, const void* Wgu, const int32_t* ta
   p.ws = wsi;
   p.ws_stride = ws_stride_ints(q, M);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  p.gu = GU;
   if (!(flags & QALG_FLAG_INDEX_READY)) {
     const hipError_t e = qalg::launch_build_index(tau, q, M, 1, wsi, p.ws_stride, s);
     if (e != hipSuccess) return QALG_ERR_HIP;
   }
   return hip_status(qalg::launch_fwd_gated_bf16(p, s));
 }
+}  // namespace
 
 qalg_status qalg_merge_gate_up(const void* Wg, const void* Wu, int32_t q, int64_t K, int64_t F, void* Wgu,
                                int32_t dtype, void* stream) {

@@ -86,11 +86,15 @@ constexpr int kQ = kBK / 16;  // MFMA quarter steps per k-step
 // and the matching 64 up columns, and the epilogue writes silu(gate) * up.
 // WGM x WGN waves per workgroup; the low tile heights (for few rows per type)
 // use 1 x 4 or 2 x 2 so that every wave still has at least 2 x 2 MFMA blocks.
-template <int BM_, int BN_, bool GATED_ = false, int WGM_ = 2, int WGN_ = 2>
+// KEEP_ (gated only): also store the merged pre-activations GU in bf16 and
+// compute H from those rounded values (the training step keeps GU for the VJP).
+template <int BM_, int BN_, bool GATED_ = false, int WGM_ = 2, int WGN_ = 2, bool KEEP_ = false>
 struct FwdCfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
   static_assert(WGM * WGN == 4, "four waves");
   static constexpr bool GATED = GATED_;
+  static constexpr bool KEEP = KEEP_;
+  static_assert(!KEEP || GATED, "pre-activations are kept by the gated forward only");
   static constexpr int THREADS = 256;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -137,6 +141,7 @@ struct FwdArgs {
   int out_n;   // columns of an output row (N; N / 2 for the gated epilogue)
   int L;       // 0: the complete-graph law Q_q; L >= 1: the recursive law Q_2^(x)L (q = 2^L)
   const uint64_t* adj;  // graph law Q_G (complete-law kernels): out-edges of each type; null for Q_q
+  char* GU;             // gated forward with kept pre-activations: M x N merged GU (bf16); else null
 };
 
 // One output tile, decoded from its position in the tile order.
@@ -315,6 +320,10 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
     for (int b = blockIdx.x; b < nbad; b += gridDim.x) {
       u32x4* yr = reinterpret_cast<u32x4*>(a.Y + int64_t(rows[typed + b]) * a.out_n * 2);
       for (int x = tid; x < row_u4; x += T) yr[x] = (u32x4){0u, 0u, 0u, 0u};
+      if constexpr (C::KEEP) {
+        u32x4* gr = reinterpret_cast<u32x4*>(a.GU + int64_t(rows[typed + b]) * a.N * 2);
+        for (int x = tid; x < a.N / 8; x += T) gr[x] = (u32x4){0u, 0u, 0u, 0u};
+      }
     }
   }
 
@@ -674,6 +683,33 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
           for (int it = 0; it < 4; ++it) {
             float up[8], h[8];
             read_piece(it, up);
+            const int row = it * 8 + (lane >> 3), p8 = lane & 7;
+            const int ml = wm * C::WTM + fm * 32 + row;
+            int orow;
+            if constexpr (CYC)
+              orow = row_of(ct, ml);
+            else
+              orow = __shfl(out_row[fm], row);
+            if constexpr (C::KEEP) {
+              // the pre-activations in bf16 (the wave's 128 merged columns are
+              // 64 gate then the matching 64 up), and H from those rounded values
+              const u32x2 g0 = pack4_bf16(gate[it][0], gate[it][1], gate[it][2], gate[it][3]);
+              const u32x2 g1 = pack4_bf16(gate[it][4], gate[it][5], gate[it][6], gate[it][7]);
+              const u32x2 u0 = pack4_bf16(up[0], up[1], up[2], up[3]), u1 = pack4_bf16(up[4], up[5], up[6], up[7]);
+              const u32x4 gq = {g0[0], g0[1], g1[0], g1[1]}, uq = {u0[0], u0[1], u1[0], u1[1]};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                gate[it][2 * e] = __uint_as_float(gq[e] << 16);
+                gate[it][2 * e + 1] = __uint_as_float(gq[e] & 0xffff0000u);
+                up[2 * e] = __uint_as_float(uq[e] << 16);
+                up[2 * e + 1] = __uint_as_float(uq[e] & 0xffff0000u);
+              }
+              if (ml < ct.m_cnt) {
+                char* gr = a.GU + (uint32_t(orow) * n_bytes + uint32_t(ct.n0 + wn * 128 + p8 * 8) * 2u);
+                __builtin_nontemporal_store(gq, reinterpret_cast<u32x4*>(gr));
+                __builtin_nontemporal_store(uq, reinterpret_cast<u32x4*>(gr + 128));
+              }
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const float gv = gate[it][e];
@@ -683,13 +719,6 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
             }
             const u32x2 lo = pack4_bf16(h[0], h[1], h[2], h[3]), hi = pack4_bf16(h[4], h[5], h[6], h[7]);
             const u32x4 val = {lo[0], lo[1], hi[0], hi[1]};
-            const int row = it * 8 + (lane >> 3), p8 = lane & 7;
-            const int ml = wm * C::WTM + fm * 32 + row;
-            int orow;
-            if constexpr (CYC)
-              orow = row_of(ct, ml);
-            else
-              orow = __shfl(out_row[fm], row);
             // a store instruction writes 8 whole 128-byte output rows
             if (ml < ct.m_cnt)
               __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(a.Y + (uint32_t(orow) * y_bytes + col0 + uint32_t(p8) * 16u)));
@@ -751,6 +780,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void fwd_persistent_kernel(FwdArgs a
 
 using Fwd256x256 = FwdCfg<256, 256>;
 using Fwd256x256Gated = FwdCfg<256, 256, true>;
+using Fwd256x256GatedKeep = FwdCfg<256, 256, true, 2, 2, true>;
 using Fwd256x192 = FwdCfg<256, 192>;
 using Fwd256x128 = FwdCfg<256, 128>;
 // few rows per type: 128- and 64-row tiles (64 x 64 and 64 x 128 wave tiles)
@@ -805,6 +835,7 @@ hipError_t launch_fwd(const ProblemDesc& p, hipStream_t s) {
   a.out_n = C::GATED ? a.N / 2 : a.N;
   a.L = p.law_L;
   a.adj = p.graph_adj;
+  a.GU = static_cast<char*>(p.gu);
   a.cpg = a.r / C::BN;
   a.n_ct = p.q * a.cpg;
   const int64_t max_tiles = ((p.M + C::BM - 1) / C::BM + p.q - 1) * int64_t(a.n_ct);
@@ -849,7 +880,9 @@ bool fwd_gated_supported(const ProblemDesc& p) {
   return s % kBK == 0 && r2 % 256 == 0;
 }
 
-hipError_t launch_fwd_gated_bf16(const ProblemDesc& p, hipStream_t s) { return launch_fwd<Fwd256x256Gated>(p, s); }
+hipError_t launch_fwd_gated_bf16(const ProblemDesc& p, hipStream_t s) {
+  return p.gu != nullptr ? launch_fwd<Fwd256x256GatedKeep>(p, s) : launch_fwd<Fwd256x256Gated>(p, s);
+}
 
 namespace {
 

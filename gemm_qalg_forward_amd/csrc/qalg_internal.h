@@ -80,6 +80,7 @@ struct ProblemDesc {
   const uint64_t* graph_adj = nullptr;  // graph law Q_G: per-type out-edge masks (device; q <= 64)
   const int64_t* in_widths = nullptr;   // unequal group widths (host arrays of q; sums K and N)
   const int64_t* out_widths = nullptr;
+  void* gu = nullptr;                   // gated forward: also store the merged pre-activations here
 };
 
 // dW's split contraction (register-staged path): at most this many partial tiles per output tile

@@ -318,6 +318,22 @@ qalg_status qalg_gated_forward(const void* X, const void* Wgu, const int32_t* ta
                                uint32_t flags, void* stream);
 
 /*
+ * The gated forward of a training step, which needs the pre-activations again
+ * for the SwiGLU VJP (section 6.2 counts the training step's products; the
+ * activation keeps its usual definition): GU (M x 2F, the merged layout of
+ * qalg_merge_gate_up) receives the gate and up products rounded once to bf16,
+ * and H = silu(gate) * up is computed from those rounded values, i.e. exactly
+ * what qalg_forward on the merged bank followed by qalg_swiglu_forward gives,
+ * in one launch.  Arguments, requirements and flags as qalg_gated_forward;
+ * GU is caller-owned device memory (non-null when M > 0, 16-byte aligned,
+ * overwritten; rows of an out-of-range type are written as zero).
+ */
+qalg_status qalg_gated_forward_keep(const void* X, const void* Wgu, const int32_t* tau, int32_t q,
+                                    int64_t M, int64_t K, int64_t F, void* H, void* GU,
+                                    int32_t dtype, void* ws, size_t ws_bytes,
+                                    uint32_t flags, void* stream);
+
+/*
  * Merged gate/up bank for qalg_gated_forward (a layout copy, done once per
  * weight update): Wg, Wu: K x F; Wgu: K x 2F.  Output group j's columns
  * j*2r .. j*2r + 2r - 1 (r = F / q) come in pieces of 256: piece t holds, for

@@ -135,3 +135,53 @@ def test_gated_ffn_training_step_matches_oracle(shape):
     if bad:
         rows = np.where((tau < 0) | (tau >= q))[0]
         assert np.all(to_f64(Y)[rows] == 0.0) and np.all(to_f64(dX)[rows] == 0.0)
+
+
+KEEP_SHAPES = [
+    # M, K, F, q, tau kind, offset, bad rows, law
+    (2048, 512, 1024, 4, "cyclic", 0, 0, "complete"),
+    (1000, 768, 3072, 4, "cyclic", 3, 0, "complete"),   # ragged rows, type offset
+    (700, 256, 1024, 2, "random", 0, 7, "complete"),    # listed schedule, out-of-range types
+    (1536, 768, 1536, 4, "interval", 0, 0, "tensor"),   # the pilot's law and schedule (Q_2^(x)2)
+]
+
+
+@pytest.mark.parametrize("shape", KEEP_SHAPES, ids=[f"M{s[0]}K{s[1]}F{s[2]}q{s[3]}{s[4]}{s[7]}" for s in KEEP_SHAPES])
+def test_gated_forward_keep_is_unfused_path_bitwise(shape):
+    """qalg_gated_forward_keep's GU and H are bit for bit the merged forward followed by the pointwise
+    SwiGLU (same tiles, same fp32 sums, H from the rounded pre-activations)."""
+    torch = torch_cuda()
+    M, K, F, q, kind, off, bad, law = shape
+    say(f"[gated keep] M={M} K={K} F={F} q={q} tau={kind} law={law} bad={bad}")
+    X = synth.normal_operand(9450 + M, (M, K), 1.0, "bf16")
+    Wg = synth.normal_operand(9550 + M, (K, F), K ** -0.5, "bf16")
+    Wu = synth.normal_operand(9650 + M, (K, F), K ** -0.5, "bf16")
+    if kind == "interval":
+        pos = torch.arange(M, dtype=torch.int64, device="cuda") % 1536
+        td = Q.qalg_type_schedule(pos, q, Q.QALG_SCHEDULE_INTERVAL, 768)
+        tau = td.cpu().numpy()
+    else:
+        tau = make_tau(kind, M, q, seed=M + 5, offset=off, bad=bad)
+        td = tau_dev(tau)
+    fl = Q.QALG_FLAG_LAW_TENSOR if law == "tensor" else 0
+    Xd = to_dev(X)
+    Wgu = Q.qalg_merge_gate_up(to_dev(Wg), to_dev(Wu), q)
+    ws = Q.workspace(q, M)
+    # garbage in the outputs first: every element must be written
+    H = torch.full((M, F), 7.0, dtype=torch.bfloat16, device="cuda")
+    GU = torch.full((M, 2 * F), -3.0, dtype=torch.bfloat16, device="cuda")
+    Q.qalg_gated_forward_keep(Xd, Wgu, td, q, H=H, GU=GU, ws=ws, flags=fl)
+    GU0 = Q.qalg_forward(Xd, Wgu, td, q, ws=ws, flags=fl | Q.QALG_FLAG_INDEX_READY)
+    H0 = Q.qalg_swiglu_forward(GU0, q)
+    torch.cuda.synchronize()
+    assert torch.equal(GU, GU0), "pre-activations differ from the merged forward"
+    assert torch.equal(H, H0), "H differs from the pointwise SwiGLU of the pre-activations"
+    if bad:
+        rows = np.where((tau < 0) | (tau >= q))[0]
+        assert np.all(to_f64(H)[rows] == 0.0) and np.all(to_f64(GU)[rows] == 0.0)
+    # and against the oracle: H (rounded pre-activations, then H: the gated step's bar) per group
+    table = O.tensor_power_table(int(np.log2(q))) if law == "tensor" else None
+    Gr = O.row_typed_forward(X.f64, Wg.f64, tau, q, table=table)
+    Ur = O.row_typed_forward(X.f64, Wu.f64, tau, q, table=table)
+    e = assert_groups(rel_frob_col_groups(to_f64(H), O.swiglu(Gr, Ur), q), STEP_TOL, "H")
+    say(f"    bitwise equal to the unfused path; H max rel err {e:.2e}")
