@@ -554,8 +554,7 @@ def pilot_leg(Q, torch, np, synth, dev, stream):
         fl = law | Q.QALG_FLAG_INDEX_READY
 
         def train():
-            Q.qalg_forward(X, Wgu, tau, q, Y=GU, ws=ws, flags=fl, stream=stream)
-            Q.qalg_swiglu_forward(GU, q, H=H, stream=stream)
+            Q.qalg_gated_forward_keep(X, Wgu, tau, q, H=H, GU=GU, ws=ws, flags=fl, stream=stream)
             Q.qalg_forward(H, Wd, tau, q, Y=Y, ws=ws, flags=fl, stream=stream)
             Q.qalg_backward_dx(dY, Wd, tau, q, dX=dH, ws=ws, flags=fl, stream=stream)
             Q.qalg_backward_dw(H, dY, tau, q, dW=dWd, ws=ws, flags=fl, stream=stream)

@@ -178,8 +178,7 @@ def test_pilot_gated_training_step_matches_oracle():
     fl = T | Q.QALG_FLAG_INDEX_READY
     Xd, Wdd, dYd = to_dev(X), to_dev(Wdn), to_dev(dY)
     Wgu = Q.qalg_merge_gate_up(to_dev(Wg), to_dev(Wu), q)
-    GU = Q.qalg_forward(Xd, Wgu, td, q, ws=ws, flags=fl)
-    H = Q.qalg_swiglu_forward(GU, q)
+    H, GU = Q.qalg_gated_forward_keep(Xd, Wgu, td, q, ws=ws, flags=fl)   # as the benchmark's pilot step
     Y = Q.qalg_forward(H, Wdd, td, q, ws=ws, flags=fl)
     dH = Q.qalg_backward_dx(dYd, Wdd, td, q, ws=ws, flags=fl)
     dWd = Q.qalg_backward_dw(H, dYd, td, q, ws=ws, flags=fl)
