@@ -313,10 +313,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
       const int ga = 2 * (ks & 1);
       const u32x2 pa = pack4_bf16(sc[nb][4 * ga], sc[nb][4 * ga + 1], sc[nb][4 * ga + 2], sc[nb][4 * ga + 3]);
       const u32x2 pb = pack4_bf16(sc[nb][4 * ga + 4], sc[nb][4 * ga + 5], sc[nb][4 * ga + 6], sc[nb][4 * ga + 7]);
-      const u32x2 own = lhi ? pb : pa;
-      const u32x2 snd = lhi ? pa : pb;
-      const unsigned r0 = __shfl_xor(snd[0], 32), r1 = __shfl_xor(snd[1], 32);
-      const u32x4 pw = lhi == 0 ? (u32x4){own[0], own[1], r0, r1} : (u32x4){r0, r1, own[0], own[1]};
+      // v_permlane32_swap exchanges lanes 32-63 of its first operand with
+      // lanes 0-31 of its second: on (pa, pb) half 0 ends with its own
+      // group-ga piece and the partner's, half 1 with the partner's group-ga+1
+      // piece and its own, in key order in both, with no per-lane selects
+      const auto s0 = __builtin_amdgcn_permlane32_swap(pa[0], pb[0], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(pa[1], pb[1], false, false);
+      const u32x4 pw = {s0[0], s1[0], s0[1], s1[1]};
       const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
