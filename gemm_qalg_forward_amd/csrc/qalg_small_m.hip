@@ -42,8 +42,6 @@ struct SmallArgs {
   int chunks_per_group;
 };
 
-__device__ __forceinline__ float lo_bf16(unsigned u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float hi_bf16(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
 
 // COLS output columns per workgroup: each weight row is read as COLS * 2
 // contiguous bytes, 16 per lane (wider rows stream better; narrower ones give
@@ -54,9 +52,15 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
   constexpr int kSmColLanes = kSmCols / 8;             // lanes per weight row (16 bytes each)
   constexpr int kSmKLanes = kSmThreads / kSmColLanes;  // weight rows in flight per step
   static_assert(kSmColLanes <= 64 && 64 % kSmColLanes == 0, "a weight row within one wave");
+  // contraction rows kk and kk + KL (KL = kSmKLanes) are the two weight rows a
+  // lane applies together: the activations are staged as those pairs, u32
+  // (x[kk], x[kk + KL]), and the group width is padded to whole pairs with zeros
+  constexpr int KL = kSmKLanes;
+  const int s_pad = (a.s + 2 * KL - 1) / (2 * KL) * (2 * KL);
   extern __shared__ __attribute__((aligned(16))) unsigned char sm_raw[];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(sm_raw);               // [s][R]
-  float* red = reinterpret_cast<float*>(sm_raw + size_t(a.s) * R * 2 + 16);  // [4][R][64]
+  uint16_t* xs16 = reinterpret_cast<uint16_t*>(sm_raw);              // [s_pad / 2][R] pairs of bf16
+  const unsigned* xs2 = reinterpret_cast<const unsigned*>(sm_raw);
+  float* red = reinterpret_cast<float*>(sm_raw + size_t(s_pad) * R * 2 + 16);  // [4][R][64]
   __shared__ int s_type[R];
   __shared__ int s_blocks[R + 1];
   __shared__ int s_nblk;
@@ -108,9 +112,12 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
   const int nblk = s_nblk;
   for (int bi = 0; bi < nblk; ++bi) {
     const int b = s_blocks[bi];
-    // stage x[m, g_b] transposed (xs[k][m]), 8 contraction values (16 bytes)
-    // per load; zero for rows that do not use block (b, j)
+    // stage x[m, g_b] as the pairs (k, k + KL) of each row m, 8 contraction
+    // values (16 bytes) per load; zero for rows that do not use block (b, j)
+    // and past the group width.  Value k sits in pair (k / 2KL) KL + k % KL,
+    // half (k / KL) & 1.
     const int s8 = s >> 3;
+    auto xs_at = [&](int k, int m) { return ((k / (2 * KL)) * KL + (k % KL)) * (R * 2) + m * 2 + ((k / KL) & 1); };
     for (int x = tid; x < s8 * R; x += kSmThreads) {
       const int m = x / s8, k8 = x - m * s8;
       const int t = s_type[m];
@@ -119,10 +126,11 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
                            : (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        xs[(k8 * 8 + 2 * d) * R + m] = uint16_t(v[d] & 0xffffu);
-        xs[(k8 * 8 + 2 * d + 1) * R + m] = uint16_t(v[d] >> 16);
+        xs16[xs_at(k8 * 8 + 2 * d, m)] = uint16_t(v[d] & 0xffffu);
+        xs16[xs_at(k8 * 8 + 2 * d + 1, m)] = uint16_t(v[d] >> 16);
       }
     }
+    for (int x = tid; x < (s_pad - s) * R; x += kSmThreads) xs16[xs_at(s + x / R, x % R)] = 0;
     __syncthreads();
     // weight rows of the block: batches of kSmUnroll rows per thread, the next
     // batch's loads issued before the current batch is applied, so that two
@@ -137,23 +145,28 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
                                    : (u32x4){0u, 0u, 0u, 0u};
       }
     };
+    // weight rows kk (piece 2v) and kk + KL (piece 2v + 1) are applied together:
+    // their columns interleaved into bf16 pairs, one v_dot2c_f32_bf16 per
+    // row and column (a weight past the group width is loaded as zero, and so
+    // is its activation)
     auto apply_batch = [&](int k0, const u32x4 (&wv)[kSmUnroll]) {
 #pragma unroll
-      for (int u = 0; u < kSmUnroll; ++u) {
-        const int kk = k0 + u * kSmKLanes;
+      for (int v = 0; v < kSmUnroll / 2; ++v) {
+        const int kk = k0 + 2 * v * KL;
         if (kk >= s) break;
-        float w8[8];
+        unsigned wp[8];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          w8[2 * d] = lo_bf16(wv[u][d]);
-          w8[2 * d + 1] = hi_bf16(wv[u][d]);
+          wp[2 * d] = __builtin_amdgcn_perm(wv[2 * v + 1][d], wv[2 * v][d], 0x05040100u);      // column 2d
+          wp[2 * d + 1] = __builtin_amdgcn_perm(wv[2 * v + 1][d], wv[2 * v][d], 0x07060302u);  // column 2d + 1
         }
-        const uint16_t* xr = xs + kk * R;
+        const unsigned* xr = xs2 + ((kk / (2 * KL)) * KL + (kk % KL)) * R;
 #pragma unroll
         for (int m = 0; m < R; ++m) {
-          const float xv = __uint_as_float(unsigned(xr[m]) << 16);
+          const bf16x2 xp = __builtin_bit_cast(bf16x2, xr[m]);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) acc[m][c] = fmaf(xv, w8[c], acc[m][c]);
+          for (int c = 0; c < 8; ++c)
+            acc[m][c] = __builtin_amdgcn_fdot2_f32_bf16(xp, __builtin_bit_cast(bf16x2, wp[c]), acc[m][c], false);
         }
       }
     };
@@ -201,7 +214,9 @@ template <int R, int COLS>
 hipError_t launch_rc(SmallArgs a, int E, hipStream_t st) {
   a.chunks_per_group = (a.r + COLS - 1) / COLS;
   const dim3 grid(unsigned(a.q * a.chunks_per_group), unsigned(E));
-  const size_t shm = size_t(a.s) * R * 2 + 16 + sizeof(float) * 4 * R * COLS;
+  constexpr int KL = kSmThreads / (COLS / 8);  // weight rows per step (the pair distance)
+  const size_t s_pad = size_t(a.s + 2 * KL - 1) / (2 * KL) * (2 * KL);
+  const size_t shm = s_pad * R * 2 + 16 + sizeof(float) * 4 * R * COLS;
   static bool attr_set = false;  // allow more than the default 64 KB of dynamic LDS
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&small_m_kernel<R, COLS>),
@@ -233,7 +248,8 @@ bool small_m_supported(const ProblemDesc& p) {
   if (p.op != Op::Fwd || p.M < 1 || p.M > kSmMaxRows) return false;
   int R = 1;
   while (R < p.M) R <<= 1;
-  return (p.K / p.q) * R <= kSmMaxXs;
+  // the staged group width padded to whole row pairs (at most 64 rows apart)
+  return ((p.K / p.q + 63) / 64 * 64) * R <= kSmMaxXs;
 }
 
 hipError_t launch_small_m_bf16(const ProblemDesc& p, hipStream_t st) {

@@ -70,7 +70,7 @@ def test_forward_dx_dw_match_oracle(shape, dtype):
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
-@pytest.mark.parametrize("q,K,N", [(4, 512, 768), (8, 256, 768), (2, 1024, 64)])
+@pytest.mark.parametrize("q,K,N", [(4, 512, 768), (8, 256, 768), (2, 1024, 64), (8, 192, 320)])
 def test_small_m_paths_match_oracle(M, q, K, N):
     """The weight-streaming path and the tiled path at decode sizes, both against the oracle."""
     torch = torch_cuda()
