@@ -31,7 +31,8 @@ constexpr int kSmThreads = 256;
 
 constexpr int kSmMaxRows = 8;
 constexpr int kSmUnroll = 8;          // weight loads per thread per batch; two batches in flight
-constexpr int kSmMaxXs = 16384;        // bf16 elements of staged activations (32 KB)
+constexpr int kSmMaxXs = 16384;        // bf16 elements of one block's staged activations (32 KB)
+constexpr int kSmStageAll = 32768;     // bf16 elements for staging every needed block at once (64 KB)
 
 struct SmallArgs {
   const uint16_t* X;
@@ -40,6 +41,7 @@ struct SmallArgs {
   uint16_t* Y;
   int q, M, K, N, s, r;
   int chunks_per_group;
+  int x_regions;   // staged activation regions: 1 (one block at a time) or the most blocks a chunk needs
 };
 
 
@@ -60,7 +62,8 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char sm_raw[];
   uint16_t* xs16 = reinterpret_cast<uint16_t*>(sm_raw);              // [s_pad / 2][R] pairs of bf16
   const unsigned* xs2 = reinterpret_cast<const unsigned*>(sm_raw);
-  float* red = reinterpret_cast<float*>(sm_raw + size_t(s_pad) * R * 2 + 16);  // [4][R][64]
+  const size_t x_region = size_t(s_pad) * R;  // bf16 elements of one block's staged activations
+  float* red = reinterpret_cast<float*>(sm_raw + x_region * a.x_regions * 2 + 16);  // [4][R][64]
   __shared__ int s_type[R];
   __shared__ int s_blocks[R + 1];
   __shared__ int s_nblk;
@@ -110,14 +113,14 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
     for (int c = 0; c < 8; ++c) acc[m][c] = 0.f;
 
   const int nblk = s_nblk;
-  for (int bi = 0; bi < nblk; ++bi) {
-    const int b = s_blocks[bi];
-    // stage x[m, g_b] as the pairs (k, k + KL) of each row m, 8 contraction
-    // values (16 bytes) per load; zero for rows that do not use block (b, j)
-    // and past the group width.  Value k sits in pair (k / 2KL) KL + k % KL,
-    // half (k / KL) & 1.
-    const int s8 = s >> 3;
-    auto xs_at = [&](int k, int m) { return ((k / (2 * KL)) * KL + (k % KL)) * (R * 2) + m * 2 + ((k / KL) & 1); };
+  // stage x[m, g_b] of block b into region rg as the pairs (k, k + KL) of each
+  // row m, 8 contraction values (16 bytes) per load; zero for rows that do not
+  // use block (b, j) and past the group width.  Value k sits in pair
+  // (k / 2KL) KL + k % KL, half (k / KL) & 1.
+  const int s8 = s >> 3;
+  auto xs_at = [&](int k, int m) { return ((k / (2 * KL)) * KL + (k % KL)) * (R * 2) + m * 2 + ((k / KL) & 1); };
+  auto stage = [&](int b, int rg) {
+    uint16_t* xr16 = xs16 + rg * x_region;
     for (int x = tid; x < s8 * R; x += kSmThreads) {
       const int m = x / s8, k8 = x - m * s8;
       const int t = s_type[m];
@@ -126,12 +129,27 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
                            : (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        xs16[xs_at(k8 * 8 + 2 * d, m)] = uint16_t(v[d] & 0xffffu);
-        xs16[xs_at(k8 * 8 + 2 * d + 1, m)] = uint16_t(v[d] >> 16);
+        xr16[xs_at(k8 * 8 + 2 * d, m)] = uint16_t(v[d] & 0xffffu);
+        xr16[xs_at(k8 * 8 + 2 * d + 1, m)] = uint16_t(v[d] >> 16);
       }
     }
-    for (int x = tid; x < (s_pad - s) * R; x += kSmThreads) xs16[xs_at(s + x / R, x % R)] = 0;
+    for (int x = tid; x < (s_pad - s) * R; x += kSmThreads) xr16[xs_at(s + x / R, x % R)] = 0;
+  };
+  // with room for every block the chunk needs, all activations are staged up
+  // front behind one barrier and the weight stream runs through the blocks
+  // back to back; otherwise one block at a time
+  const bool all = a.x_regions > 1;
+  if (all) {
+    for (int bi = 0; bi < nblk; ++bi) stage(s_blocks[bi], bi);
     __syncthreads();
+  }
+  for (int bi = 0; bi < nblk; ++bi) {
+    const int b = s_blocks[bi];
+    if (!all) {
+      stage(b, 0);
+      __syncthreads();
+    }
+    const unsigned* xsb = xs2 + (all ? bi : 0) * (x_region / 2);
     // weight rows of the block: batches of kSmUnroll rows per thread, the next
     // batch's loads issued before the current batch is applied, so that two
     // batches (2 x 8 x 16 bytes per thread) are in flight
@@ -160,7 +178,7 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
           wp[2 * d] = __builtin_amdgcn_perm(wv[2 * v + 1][d], wv[2 * v][d], 0x05040100u);      // column 2d
           wp[2 * d + 1] = __builtin_amdgcn_perm(wv[2 * v + 1][d], wv[2 * v][d], 0x07060302u);  // column 2d + 1
         }
-        const unsigned* xr = xs2 + ((kk / (2 * KL)) * KL + (kk % KL)) * R;
+        const unsigned* xr = xsb + ((kk / (2 * KL)) * KL + (kk % KL)) * R;
 #pragma unroll
         for (int m = 0; m < R; ++m) {
           const bf16x2 xp = __builtin_bit_cast(bf16x2, xr[m]);
@@ -178,7 +196,7 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
       load_batch(k + 2 * kStep, wa);
       apply_batch(k + kStep, wb);
     }
-    __syncthreads();  // xs is restaged for the next block
+    if (!all) __syncthreads();  // the region is restaged for the next block
   }
 
   // reduce the weight-row lanes: those of a wave by a fixed shuffle tree, then
@@ -216,12 +234,16 @@ hipError_t launch_rc(SmallArgs a, int E, hipStream_t st) {
   const dim3 grid(unsigned(a.q * a.chunks_per_group), unsigned(E));
   constexpr int KL = kSmThreads / (COLS / 8);  // weight rows per step (the pair distance)
   const size_t s_pad = size_t(a.s + 2 * KL - 1) / (2 * KL) * (2 * KL);
-  const size_t shm = s_pad * R * 2 + 16 + sizeof(float) * 4 * R * COLS;
+  // a chunk of output group j needs W_jj and W_tj for the other types among the
+  // rows: at most min(q, 1 + R) blocks; stage them all when they fit kSmStageAll
+  const int nb_max = a.q < 1 + R ? a.q : 1 + R;
+  a.x_regions = (nb_max > 1 && s_pad * R * nb_max <= size_t(kSmStageAll)) ? nb_max : 1;
+  const size_t shm = s_pad * R * 2 * a.x_regions + 16 + sizeof(float) * 4 * R * COLS;
   static bool attr_set = false;  // allow more than the default 64 KB of dynamic LDS
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&small_m_kernel<R, COLS>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             int(kSmMaxXs * 2 + 16 + sizeof(float) * 4 * R * COLS));
+                                             int(kSmStageAll * 2 + 16 + sizeof(float) * 4 * R * COLS));
     if (e != hipSuccess) return e;
     attr_set = true;
   }

@@ -150,6 +150,22 @@ def test_gated_argument_errors_are_synchronous(lib):
     assert call_gated(lib, M=0, X=None, H=None) == 0  # no rows: nothing to do, no launch
 
 
+def call_gated_keep(lib, X=FAKE, W=FAKE, tau=FAKE, q=2, M=64, K=256, F=512, H=FAKE, GU=FAKE, dt=1, ws=FAKE,
+                    wsb=1 << 20, flags=0):
+    return lib.qalg_gated_forward_keep(X, W, tau, q, M, K, F, H, GU, dt, ws, wsb, flags, None)
+
+
+def test_gated_keep_argument_errors_are_synchronous(lib):
+    """The gated forward that keeps the pre-activations: the gated forward's checks plus its GU."""
+    assert call_gated_keep(lib, GU=None) == 1                 # GU is required when there are rows
+    assert call_gated_keep(lib, GU=FAKE + 8) == 4             # 16-byte aligned
+    assert call_gated_keep(lib, dt=0) == 5
+    assert call_gated_keep(lib, F=384) == 4                   # F / q = 192: not a multiple of 128
+    assert call_gated_keep(lib, H=None) == 1
+    assert call_gated_keep(lib, wsb=16) == 6
+    assert call_gated_keep(lib, M=0, X=None, H=None, GU=None) == 0  # no rows: nothing to do, no launch
+
+
 def test_merge_argument_errors_are_synchronous(lib):
     m = lambda **k: lib.qalg_merge_gate_up(k.get("Wg", FAKE), k.get("Wu", FAKE), k.get("q", 2), k.get("K", 64),  # noqa: E731
                                            k.get("F", 512), k.get("Wgu", FAKE), k.get("dt", 1), None)
