@@ -743,15 +743,23 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
     else
       grow = rows[out_first + ml];
     uint16_t* crow = Cg + grow * ldc + n0;
+    // lane (l32, lhi) holds columns g*8 + lhi*4 .. +3 of each 32-column block;
+    // v_permlane32_swap on the packed pieces of groups 2gp and 2gp + 1 (lanes
+    // 32-63 of the first exchanged with lanes 0-31 of the second; both lanes of
+    // a pair hold the same row) leaves half 0 with columns 16gp + 0..7 and half
+    // 1 with 16gp + 8..15: one 16-byte store per lane (column counts are whole
+    // 8-column pieces)
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int nl = wn * C::WTN + fn * 32 + g * 8 + lhi * 4;
-        if (nl < n_cnt) {
-          const f32x16& v = acc[fm][fn];
-          *reinterpret_cast<u32x2*>(crow + nl) = pack4_bf16(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
-        }
+      for (int gp = 0; gp < 2; ++gp) {
+        const f32x16& v = acc[fm][fn];
+        const u32x2 x = pack4_bf16(v[8 * gp], v[8 * gp + 1], v[8 * gp + 2], v[8 * gp + 3]);
+        const u32x2 y = pack4_bf16(v[8 * gp + 4], v[8 * gp + 5], v[8 * gp + 6], v[8 * gp + 7]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
+        const int nl = wn * C::WTN + fn * 32 + gp * 16 + lhi * 8;
+        if (nl < n_cnt) *reinterpret_cast<u32x4*>(crow + nl) = (u32x4){s0[0], s1[0], s0[1], s1[1]};
       }
     }
   }
