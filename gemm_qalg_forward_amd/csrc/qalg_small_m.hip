@@ -7,8 +7,8 @@
 // that the decode kernel performs vector reductions; section 6.3 and appendix G
 // that single-token work is bounded by weight bandwidth.
 //
-// Design: weight-stationary.  A workgroup owns a 64-column chunk of one output
-// group j of one problem.  The weight blocks that chunk needs are W_jj (every
+// Design: weight-stationary.  A workgroup owns a chunk of 64 to 512 columns of
+// one output group j of one problem.  The weight blocks that chunk needs are W_jj (every
 // typed row uses it, eq 17) and W_tj for each type t != j present among the
 // rows (eq 17's x_t W_tj term; W_jj alone when t == j, eq 16).  Each needed
 // block is streamed from HBM exactly once, in 16-byte row pieces, and applied
@@ -16,7 +16,10 @@
 // (staged in LDS), so the inner loop has no branches.  Blocks are visited in a
 // fixed order and partial sums are reduced in a fixed tree: the result is
 // bitwise reproducible.  No type index is needed: the <= 8 types are read
-// directly.
+// directly.  The two weight rows a lane loads per step are applied together
+// with bf16 dot-2 instructions on interleaved columns, against activations
+// staged in LDS as the same row pairs (all needed blocks at once when they
+// fit in 64 KB, else one block at a time).
 #include "qalg_internal.h"
 
 namespace qalg {

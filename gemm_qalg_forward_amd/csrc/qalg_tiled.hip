@@ -28,7 +28,8 @@
 // dY in dW) are loaded as 8x8 blocks and transposed in registers on the way
 // into LDS.  The MFMA is v_mfma_f32_32x32x16_bf16 with the operands swapped
 // (the weight-side tile as the first operand) so that each lane ends with
-// four consecutive output columns of one row: one 8-byte store per group.
+// four consecutive output columns of one row; the lane halves exchange pieces
+// (v_permlane32_swap) so that each lane stores 16 contiguous bytes.
 #include "qalg_internal.h"
 
 namespace qalg {
