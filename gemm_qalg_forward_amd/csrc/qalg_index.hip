@@ -13,7 +13,9 @@
 // by type with ballots (one round per distinct type present), so both passes
 // cost O(M / 64 * distinct types per step) wave instructions.  The scatter
 // keeps rows of a type in ascending order because slices, steps and lanes
-// are visited in row order.
+// are visited in row order.  The type offsets and the row-tile prefix sums
+// (one per tile height) are scans over q + 1 values: shuffles within one wave
+// when q < 64, block-wide scans otherwise.
 #include "qalg_internal.h"
 
 namespace qalg {
@@ -70,6 +72,17 @@ __device__ int block_exclusive_scan(int v, int* tmp, int* total) {
   return before + x - v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (no shared memory).
+__device__ int wave_inclusive_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
 // One workgroup per problem (blockIdx.x = problem).  Optional `zero_out`: the
 // rows of an out-of-range type are zeroed there (row length zero_ld elements of
 // zero_elem_bytes bytes), so the projection that follows need not visit them.
@@ -90,7 +103,6 @@ __global__ __launch_bounds__(kIdxThreads) void build_index_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
   for (int x = tid; x < kIdxWaves * Q1; x += kIdxThreads) tab[x] = 0;
-  __syncthreads();
 
   const int slice = (M + kIdxWaves * 64 - 1) / (kIdxWaves * 64) * 64;
   const int r0 = min(w * slice, M), r1 = min(r0 + slice, M);
@@ -101,7 +113,7 @@ __global__ __launch_bounds__(kIdxThreads) void build_index_kernel(
   __shared__ int s_cyclic;
   const int t0 = M > 0 ? tau[0] : 0;
   if (tid == 0) s_cyclic = (M > 0 && t0 >= 0 && t0 < q) ? 1 : 0;
-  __syncthreads();
+  __syncthreads();  // also orders the zeroing of tab before pass 1
   if (s_cyclic) {
     // kBatch independent loads per thread before any comparison, so that a
     // thread waits for one memory latency per batch instead of one per row
@@ -156,10 +168,13 @@ __global__ __launch_bounds__(kIdxThreads) void build_index_kernel(
       }
     }
   }
-  __syncthreads();
+  if (!cyclic) __syncthreads();
 
-  // per type: exclusive prefix over waves (in place), total per type
-  for (int t = tid; t < Q1; t += kIdxThreads) {
+  // per type: exclusive prefix over waves (in place), total per type.  With
+  // q < 64 types the scans below run in one wave, and a cyclic schedule's
+  // totals are formed there too.
+  const bool wave_scans = Q1 <= 64;
+  for (int t = tid; t < Q1 && (!cyclic || !wave_scans); t += kIdxThreads) {
     if (cyclic) {
       // rows of type t are (t - t0) mod q + k q
       const int start = (t - t0 + q) % q;
@@ -174,48 +189,87 @@ __global__ __launch_bounds__(kIdxThreads) void build_index_kernel(
     }
     tot[t] = run;
   }
-  __syncthreads();
+  if (!cyclic || !wave_scans) __syncthreads();
 
   int32_t* counts = ws + off_counts;
   int32_t* offsets = ws + off_offsets;
   int32_t* tiles = ws + off_tiles;
   int32_t* rows = ws + off_rows;
 
-  // offsets over types 0..q-1; the out-of-range rows follow all valid rows
-  // (q <= QALG_MAX_Q < kIdxThreads: one value per thread)
-  {
-    const int t = tid;
-    const int cnt = (t < q) ? tot[t] : 0;
-    int valid_rows;
-    const int ex = block_exclusive_scan(cnt, tmp, &valid_rows);
-    if (t < q) {
-      counts[t] = cnt;
-      offsets[t] = ex;
-    }
-    if (tid == 0) {
-      offsets[q] = valid_rows;
-      ws[0] = tot[q];  // rows with an out-of-range type
+  if (wave_scans) {
+    // lane t holds type t (lane q: the out-of-range rows); the same offsets
+    // and tile prefix sums as the block-wide scans below, without barriers
+    if (w == 0) {
+      const int t = lane;
+      int cnt = 0;
+      if (cyclic) {
+        const int start = (t - t0 + q) % q;
+        cnt = (t < q && start < M) ? (M - 1 - start) / q + 1 : 0;
+      } else if (t < Q1) {
+        cnt = tot[t];
+      }
+      const int c = t < q ? cnt : 0;
+      const int inc = wave_inclusive_scan(c);
+      const int valid_rows = __shfl(inc, 63, 64);
+      const int nbad = __shfl(cnt, q, 64);
+      if (t < q) {
+        counts[t] = c;
+        offsets[t] = inc - c;
+      }
+      if (t == 0) {
+        offsets[q] = valid_rows;
+        ws[0] = nbad;
+      }
+      if (t < Q1) tot[t] = (t < q) ? inc - c : valid_rows;
+      for (int h = 0; h < kNumTileHeights; ++h) {
+        const int bm = kTileHeights[h];
+        const int nt = (c + bm - 1) / bm;
+        const int ti = wave_inclusive_scan(nt);
+        const int sum = __shfl(ti, 63, 64);
+        if (t < q) tiles[h * Q1 + t] = ti - nt;
+        if (t == 0) tiles[h * Q1 + q] = sum;
+      }
     }
     __syncthreads();
-    if (t < Q1) tot[t] = (t < q) ? ex : valid_rows;  // first slot of each type
+  } else {
+    // offsets over types 0..q-1; the out-of-range rows follow all valid rows
+    // (q <= QALG_MAX_Q < kIdxThreads: one value per thread)
+    {
+      const int t = tid;
+      const int cnt = (t < q) ? tot[t] : 0;
+      int valid_rows;
+      const int ex = block_exclusive_scan(cnt, tmp, &valid_rows);
+      if (t < q) {
+        counts[t] = cnt;
+        offsets[t] = ex;
+      }
+      if (tid == 0) {
+        offsets[q] = valid_rows;
+        ws[0] = tot[q];  // rows with an out-of-range type
+      }
+      __syncthreads();
+      if (t < Q1) tot[t] = (t < q) ? ex : valid_rows;  // first slot of each type
+      __syncthreads();
+    }
+
+    // row-tile prefix sums for each tile height
+    for (int h = 0; h < kNumTileHeights; ++h) {
+      const int bm = kTileHeights[h];
+      const int t = tid;
+      const int c = (t < q) ? counts[t] : 0;  // same thread wrote counts[t]
+      const int nt = (c + bm - 1) / bm;
+      int sum;
+      const int ex = block_exclusive_scan(nt, tmp, &sum);
+      if (t < q) tiles[h * Q1 + t] = ex;
+      if (tid == 0) tiles[h * Q1 + q] = sum;
+    }
+  }
+
+  // bases: first output slot of each (wave, type); a cyclic index has no scatter
+  if (!cyclic) {
+    for (int x = tid; x < kIdxWaves * Q1; x += kIdxThreads) tab[x] += tot[x % Q1];
     __syncthreads();
   }
-
-  // row-tile prefix sums for each tile height
-  for (int h = 0; h < kNumTileHeights; ++h) {
-    const int bm = kTileHeights[h];
-    const int t = tid;
-    const int c = (t < q) ? counts[t] : 0;  // same thread wrote counts[t]
-    const int nt = (c + bm - 1) / bm;
-    int sum;
-    const int ex = block_exclusive_scan(nt, tmp, &sum);
-    if (t < q) tiles[h * Q1 + t] = ex;
-    if (tid == 0) tiles[h * Q1 + q] = sum;
-  }
-
-  // bases: first output slot of each (wave, type)
-  for (int x = tid; x < kIdxWaves * Q1; x += kIdxThreads) tab[x] += tot[x % Q1];
-  __syncthreads();
 
   if (cyclic) {
     // closed-form row list: slot offsets[i] + k holds (i - t0) mod q + k q

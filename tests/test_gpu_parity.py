@@ -22,6 +22,8 @@ SHAPES = [
     (777, 192, 320, 8, "random", 0, 13),     # s = 24, r = 40: groups narrower than a tile; bad types
     (513, 1024, 512, 1, "zeros", 0, 0),      # q = 1: the dense product
     (300, 128, 128, 16, "cyclic", 5, 0),     # s = r = 8
+    (2000, 504, 504, 63, "random", 0, 5),    # q = 63: the largest q whose index scans run in one wave
+    (1500, 512, 512, 64, "cyclic", 3, 0),    # q = 64: the smallest with block-wide index scans
     (2048, 256, 512, 4, "random", 0, 0),     # some types with many row tiles
     (5000, 512, 1024, 4, "random", 0, 37),   # persistent 256x256 path: ragged row tiles, bad types
     (4099, 768, 768, 3, "cyclic", 2, 0),     # persistent path, odd q, type offset
@@ -143,7 +145,9 @@ def _check_index(ws, tau, q):
 
 @pytest.mark.parametrize("M,q,kind,bad", [(1, 1, "zeros", 0), (1, 4, "random", 1), (63, 2, "cyclic", 0),
                                           (64, 4, "cyclic", 0), (65, 4, "random", 3), (4096, 8, "random", 0),
-                                          (20000, 7, "random", 111), (3000, 512, "random", 0)])
+                                          (20000, 7, "random", 111), (3000, 512, "random", 0),
+                                          (5000, 63, "random", 9), (5000, 63, "cyclic", 0),
+                                          (5000, 64, "random", 2), (5000, 64, "cyclic", 0)])
 def test_index_edge_cases_bit_exact(M, q, kind, bad):
     torch = torch_cuda()
     tau = make_tau(kind, M, q, seed=M, bad=bad)
@@ -155,7 +159,8 @@ def test_index_edge_cases_bit_exact(M, q, kind, bad):
 
 @pytest.mark.parametrize("M,q,off,swap", [(16384, 8, 0, None), (20000, 8, 3, None), (4099, 3, 2, None),
                                           (16384, 8, 0, (0, 1)), (16384, 8, 0, (9000, 9001)),
-                                          (20000, 8, 3, (19998, 19999)), (3000, 4, 1, (1500, 2999))])
+                                          (20000, 8, 3, (19998, 19999)), (3000, 4, 1, (1500, 2999)),
+                                          (4099, 63, 5, None), (4099, 64, 60, None)])
 def test_cyclic_detection_bit_exact(M, q, off, swap):
     """The index recognises (o + m) mod q at any offset o (its rows are then computed, not listed) and
     rejects a schedule that breaks it anywhere: two rows of different types swapped (same counts)."""
