@@ -190,10 +190,50 @@ def workspace(q: int, M: int, E: int = 1, device="cuda", dw_shape=None):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def _tau_check(tau, M: int, E: int = 1):
+def _tau_check(tau, M: int, E: int = 1, like=None):
     torch = _torch()
     if tau.dtype != torch.int32 or tau.numel() != M * E:
         raise ValueError(f"tau must be int32 with {M * E} elements")
+    if like is not None:
+        _same_device(tau, like, "tau")
+
+
+def _same_device(t, like, name: str) -> None:
+    if t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, the operands on {like.device}")
+
+
+def _check_out(t, shape, like, name: str):
+    """A caller-supplied output must have exactly the shape, dtype and device the
+    kernels write: the library trusts the sizes it is given, so an undersized or
+    mistyped buffer would be written out of bounds on the device.  Checked before
+    any pointer is taken, so the error is raised without touching the GPU."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != like.dtype:
+        raise TypeError(f"{name} must have dtype {like.dtype}, got {t.dtype}")
+    _same_device(t, like, name)
+    return t
+
+
+def _same_operand(t, like, name: str) -> None:
+    if t.dtype != like.dtype:
+        raise TypeError("operands must share a dtype")
+    _same_device(t, like, name)
+
+
+def _new_or_check(t, shape, like, name: str):
+    torch = _torch()
+    if t is None:
+        return torch.empty(tuple(shape), dtype=like.dtype, device=like.device)
+    return _check_out(t, shape, like, name)
+
+
+def _ws_or_new(ws, q: int, M: int, like, E: int = 1, dw_shape=None):
+    if ws is None:
+        return workspace(q, M, E, device=like.device, dw_shape=dw_shape)
+    _same_device(ws, like, "ws")
+    return ws
 
 
 def qalg_type_schedule(positions, q: int, kind: int = QALG_SCHEDULE_CYCLIC, period: int = 0,
@@ -205,6 +245,10 @@ def qalg_type_schedule(positions, q: int, kind: int = QALG_SCHEDULE_CYCLIC, peri
     M = positions.numel()
     if tau is None:
         tau = torch.empty(M, dtype=torch.int32, device=positions.device)
+    elif tau.dtype != torch.int32 or tau.numel() != M:
+        raise ValueError(f"tau must be int32 with {M} elements")
+    else:
+        _same_device(tau, positions, "tau")
     _check("qalg_type_schedule", lib().qalg_type_schedule(
         _dev_ptr(positions, "positions"), M, q, kind, period, _dev_ptr(tau, "tau"), _stream(stream)))
     return tau
@@ -212,8 +256,7 @@ def qalg_type_schedule(positions, q: int, kind: int = QALG_SCHEDULE_CYCLIC, peri
 
 def qalg_build_index(tau, q: int, ws=None, stream=None):
     M = tau.numel()
-    if ws is None:
-        ws = workspace(q, M, device=tau.device)
+    ws = _ws_or_new(ws, q, M, tau)
     _check("qalg_build_index", lib().qalg_build_index(
         _dev_ptr(tau, "tau"), q, M, _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
     return ws
@@ -221,23 +264,20 @@ def qalg_build_index(tau, q: int, ws=None, stream=None):
 
 def qalg_build_index_batched(tau, q: int, ws=None, stream=None):
     E, M = tau.shape
-    if ws is None:
-        ws = workspace(q, M, E, device=tau.device)
+    ws = _ws_or_new(ws, q, M, tau, E)
     _check("qalg_build_index_batched", lib().qalg_build_index_batched(
         E, _dev_ptr(tau, "tau"), q, M, _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
     return ws
 
 
 def _proj(fn: str, A, B, tau, q: int, out, out_shape, ws, flags: int, stream, M: int, K: int, N: int):
-    torch = _torch()
     if A.dtype != B.dtype:
         raise TypeError("operands must share a dtype")
     dt = _dtype_code(A)
-    _tau_check(tau, M)
-    if out is None:
-        out = torch.empty(out_shape, dtype=A.dtype, device=A.device)
-    if ws is None:
-        ws = workspace(q, M, device=A.device)
+    _same_device(B, A, "B")
+    _tau_check(tau, M, like=A)
+    out = _new_or_check(out, out_shape, A, "out")
+    ws = _ws_or_new(ws, q, M, A)
     _check(fn, getattr(lib(), fn)(
         _dev_ptr(A, "A"), _dev_ptr(B, "B"), _dev_ptr(tau, "tau"), q, M, K, N, _dev_ptr(out, "out"),
         dt, _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags, _stream(stream)))
@@ -253,10 +293,12 @@ def qalg_forward(X, W, tau, q: int, Y=None, ws=None, flags: int = 0, stream=None
     return _proj("qalg_forward", X, W, tau, q, Y, (M, N), ws, flags, stream, M, K, N)
 
 
-def _adjacency_check(adjacency, q: int) -> None:
+def _adjacency_check(adjacency, q: int, like=None) -> None:
     torch = _torch()
     if adjacency.dtype != torch.int64 or adjacency.numel() != q:
         raise ValueError("adjacency must be int64 with q elements")
+    if like is not None:
+        _same_device(adjacency, like, "adjacency")
 
 
 def qalg_forward_graph(X, W, tau, q: int, adjacency, Y=None, ws=None, flags: int = 0, stream=None):
@@ -266,12 +308,11 @@ def qalg_forward_graph(X, W, tau, q: int, adjacency, Y=None, ws=None, flags: int
     K2, N = W.shape
     if K2 != K:
         raise ValueError("X and W inner sizes differ")
-    _adjacency_check(adjacency, q)
-    _tau_check(tau, M)
-    if Y is None:
-        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
-    if ws is None:
-        ws = workspace(q, M, device=X.device)
+    _adjacency_check(adjacency, q, like=X)
+    _same_operand(W, X, "W")
+    _tau_check(tau, M, like=X)
+    Y = _new_or_check(Y, (M, N), X, "Y")
+    ws = _ws_or_new(ws, q, M, X)
     _check("qalg_forward_graph", lib().qalg_forward_graph(
         _dev_ptr(X, "X"), _dev_ptr(W, "W"), _dev_ptr(tau, "tau"), q, _dev_ptr(adjacency, "adjacency"), M, K, N,
         _dev_ptr(Y, "Y"), _dtype_code(X), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags,
@@ -286,12 +327,11 @@ def qalg_backward_dx_graph(dY, W, tau, q: int, adjacency, dX=None, ws=None, flag
     K, N2 = W.shape
     if N2 != N:
         raise ValueError("dY and W widths differ")
-    _adjacency_check(adjacency, q)
-    _tau_check(tau, M)
-    if dX is None:
-        dX = torch.empty((M, K), dtype=dY.dtype, device=dY.device)
-    if ws is None:
-        ws = workspace(q, M, device=dY.device)
+    _adjacency_check(adjacency, q, like=dY)
+    _same_operand(W, dY, "W")
+    _tau_check(tau, M, like=dY)
+    dX = _new_or_check(dX, (M, K), dY, "dX")
+    ws = _ws_or_new(ws, q, M, dY)
     _check("qalg_backward_dx_graph", lib().qalg_backward_dx_graph(
         _dev_ptr(dY, "dY"), _dev_ptr(W, "W"), _dev_ptr(tau, "tau"), q, _dev_ptr(adjacency, "adjacency"), M, K, N,
         _dev_ptr(dX, "dX"), _dtype_code(dY), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags,
@@ -306,12 +346,11 @@ def qalg_backward_dw_graph(X, dY, tau, q: int, adjacency, dW=None, ws=None, flag
     M2, N = dY.shape
     if M2 != M:
         raise ValueError("X and dY row counts differ")
-    _adjacency_check(adjacency, q)
-    _tau_check(tau, M)
-    if dW is None:
-        dW = torch.empty((K, N), dtype=X.dtype, device=X.device)
-    if ws is None:
-        ws = workspace(q, M, device=X.device)
+    _adjacency_check(adjacency, q, like=X)
+    _same_operand(dY, X, "dY")
+    _tau_check(tau, M, like=X)
+    dW = _new_or_check(dW, (K, N), X, "dW")
+    ws = _ws_or_new(ws, q, M, X)
     _check("qalg_backward_dw_graph", lib().qalg_backward_dw_graph(
         _dev_ptr(X, "X"), _dev_ptr(dY, "dY"), _dev_ptr(tau, "tau"), q, _dev_ptr(adjacency, "adjacency"), M, K, N,
         _dev_ptr(dW, "dW"), _dtype_code(X), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags,
@@ -352,11 +391,10 @@ def qalg_forward_widths(X, W, tau, q: int, in_widths, out_widths, Y=None, ws=Non
     if K2 != K:
         raise ValueError("X and W inner sizes differ")
     kw, nw = _widths_arg(in_widths, q, K, "in_widths"), _widths_arg(out_widths, q, N, "out_widths")
-    _tau_check(tau, M)
-    if Y is None:
-        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
-    if ws is None:
-        ws = workspace(q, M, device=X.device)
+    _same_operand(W, X, "W")
+    _tau_check(tau, M, like=X)
+    Y = _new_or_check(Y, (M, N), X, "Y")
+    ws = _ws_or_new(ws, q, M, X)
     _check("qalg_forward_widths", lib().qalg_forward_widths(
         _dev_ptr(X, "X"), _dev_ptr(W, "W"), _dev_ptr(tau, "tau"), q, kw, nw, M, K, N, _dev_ptr(Y, "Y"),
         _dtype_code(X), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags, _stream(stream)))
@@ -372,11 +410,10 @@ def qalg_backward_dx_widths(dY, W, tau, q: int, in_widths, out_widths, dX=None, 
     if N2 != N:
         raise ValueError("dY and W widths differ")
     kw, nw = _widths_arg(in_widths, q, K, "in_widths"), _widths_arg(out_widths, q, N, "out_widths")
-    _tau_check(tau, M)
-    if dX is None:
-        dX = torch.empty((M, K), dtype=dY.dtype, device=dY.device)
-    if ws is None:
-        ws = workspace(q, M, device=dY.device)
+    _same_operand(W, dY, "W")
+    _tau_check(tau, M, like=dY)
+    dX = _new_or_check(dX, (M, K), dY, "dX")
+    ws = _ws_or_new(ws, q, M, dY)
     _check("qalg_backward_dx_widths", lib().qalg_backward_dx_widths(
         _dev_ptr(dY, "dY"), _dev_ptr(W, "W"), _dev_ptr(tau, "tau"), q, kw, nw, M, K, N, _dev_ptr(dX, "dX"),
         _dtype_code(dY), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags, _stream(stream)))
@@ -392,11 +429,10 @@ def qalg_backward_dw_widths(X, dY, tau, q: int, in_widths, out_widths, dW=None, 
     if M2 != M:
         raise ValueError("X and dY row counts differ")
     kw, nw = _widths_arg(in_widths, q, K, "in_widths"), _widths_arg(out_widths, q, N, "out_widths")
-    _tau_check(tau, M)
-    if dW is None:
-        dW = torch.empty((K, N), dtype=X.dtype, device=X.device)
-    if ws is None:
-        ws = workspace(q, M, device=X.device)
+    _same_operand(dY, X, "dY")
+    _tau_check(tau, M, like=X)
+    dW = _new_or_check(dW, (K, N), X, "dW")
+    ws = _ws_or_new(ws, q, M, X)
     _check("qalg_backward_dw_widths", lib().qalg_backward_dw_widths(
         _dev_ptr(X, "X"), _dev_ptr(dY, "dY"), _dev_ptr(tau, "tau"), q, kw, nw, M, K, N, _dev_ptr(dW, "dW"),
         _dtype_code(X), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags, _stream(stream)))
@@ -409,8 +445,8 @@ def qalg_merge_gate_up(Wg, Wu, q: int, Wgu=None, stream=None):
     K, F = Wg.shape
     if tuple(Wu.shape) != (K, F) or Wu.dtype != Wg.dtype:
         raise ValueError("gate and up weights must have the same shape and dtype")
-    if Wgu is None:
-        Wgu = torch.empty((K, 2 * F), dtype=Wg.dtype, device=Wg.device)
+    _same_device(Wu, Wg, "Wu")
+    Wgu = _new_or_check(Wgu, (K, 2 * F), Wg, "Wgu")
     _check("qalg_merge_gate_up", lib().qalg_merge_gate_up(
         _dev_ptr(Wg, "Wg"), _dev_ptr(Wu, "Wu"), q, K, F, _dev_ptr(Wgu, "Wgu"), _dtype_code(Wg), _stream(stream)))
     return Wgu
@@ -423,10 +459,8 @@ def qalg_split_gate_up(Wgu, q: int, Wg=None, Wu=None, stream=None):
     if F2 % 2:
         raise ValueError("Wgu must have an even number of columns")
     F = F2 // 2
-    if Wg is None:
-        Wg = torch.empty((K, F), dtype=Wgu.dtype, device=Wgu.device)
-    if Wu is None:
-        Wu = torch.empty((K, F), dtype=Wgu.dtype, device=Wgu.device)
+    Wg = _new_or_check(Wg, (K, F), Wgu, "Wg")
+    Wu = _new_or_check(Wu, (K, F), Wgu, "Wu")
     _check("qalg_split_gate_up", lib().qalg_split_gate_up(
         _dev_ptr(Wgu, "Wgu"), q, K, F, _dev_ptr(Wg, "Wg"), _dev_ptr(Wu, "Wu"), _dtype_code(Wgu), _stream(stream)))
     return Wg, Wu
@@ -438,10 +472,7 @@ def qalg_swiglu_forward(GU, q: int, H=None, stream=None):
     M, F2 = GU.shape
     if F2 % 2:
         raise ValueError("GU must have an even number of columns")
-    if H is None:
-        H = torch.empty((M, F2 // 2), dtype=GU.dtype, device=GU.device)
-    elif tuple(H.shape) != (M, F2 // 2) or H.dtype != GU.dtype:
-        raise ValueError("H must be [M, F] with the dtype of GU")
+    H = _new_or_check(H, (M, F2 // 2), GU, "H")
     _check("qalg_swiglu_forward", lib().qalg_swiglu_forward(
         _dev_ptr(GU, "GU"), q, M, F2 // 2, _dev_ptr(H, "H"), _dtype_code(GU), _stream(stream)))
     return H
@@ -453,10 +484,8 @@ def qalg_swiglu_backward(GU, dH, q: int, dGU=None, stream=None):
     M, F2 = GU.shape
     if F2 % 2 or tuple(dH.shape) != (M, F2 // 2) or dH.dtype != GU.dtype:
         raise ValueError("GU must be [M, 2F] and dH [M, F] of the same dtype")
-    if dGU is None:
-        dGU = torch.empty((M, F2), dtype=GU.dtype, device=GU.device)
-    elif tuple(dGU.shape) != (M, F2) or dGU.dtype != GU.dtype:
-        raise ValueError("dGU must be [M, 2F] with the dtype of GU")
+    _same_device(dH, GU, "dH")
+    dGU = _new_or_check(dGU, (M, F2), GU, "dGU")
     _check("qalg_swiglu_backward", lib().qalg_swiglu_backward(
         _dev_ptr(GU, "GU"), _dev_ptr(dH, "dH"), q, M, F2 // 2, _dev_ptr(dGU, "dGU"), _dtype_code(GU),
         _stream(stream)))
@@ -472,8 +501,9 @@ def qalg_attention_forward(Qh, Kh, Vh, q: int, O=None, flags: int = 0, stream=No
         raise ValueError("K and V must be [Hkv, S, d] with the S and d of Q")
     if Kh.dtype != Qh.dtype or Vh.dtype != Qh.dtype:
         raise TypeError("Q, K and V must share a dtype")
-    if O is None:
-        O = torch.empty_like(Qh)
+    _same_device(Kh, Qh, "K")
+    _same_device(Vh, Qh, "V")
+    O = _new_or_check(O, (Hq, S, d), Qh, "O")
     _check("qalg_attention_forward", lib().qalg_attention_forward(
         _dev_ptr(Qh, "Q"), _dev_ptr(Kh, "K"), _dev_ptr(Vh, "V"), Hq, Hkv, S, d, q, _dev_ptr(O, "O"),
         _dtype_code(Qh), flags, _stream(stream)))
@@ -499,13 +529,11 @@ def qalg_gated_forward_keep(X, Wgu, tau, q: int, H=None, GU=None, ws=None, flags
         raise ValueError("X and Wgu shapes differ (Wgu is K x 2F)")
     if X.dtype != Wgu.dtype:
         raise TypeError("operands must share a dtype")
-    _tau_check(tau, M)
-    if H is None:
-        H = torch.empty((M, F2 // 2), dtype=X.dtype, device=X.device)
-    if GU is None:
-        GU = torch.empty((M, F2), dtype=X.dtype, device=X.device)
-    if ws is None:
-        ws = workspace(q, M, device=X.device)
+    _same_device(Wgu, X, "Wgu")
+    _tau_check(tau, M, like=X)
+    H = _new_or_check(H, (M, F2 // 2), X, "H")
+    GU = _new_or_check(GU, (M, F2), X, "GU")
+    ws = _ws_or_new(ws, q, M, X)
     _check("qalg_gated_forward_keep", lib().qalg_gated_forward_keep(
         _dev_ptr(X, "X"), _dev_ptr(Wgu, "Wgu"), _dev_ptr(tau, "tau"), q, M, K, F2 // 2, _dev_ptr(H, "H"),
         _dev_ptr(GU, "GU"), _dtype_code(X), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags,
@@ -522,11 +550,10 @@ def qalg_forward_batched(X, W, tau, q: int, Y=None, ws=None, flags: int = 0, str
         raise ValueError("X and W shapes differ")
     if X.dtype != W.dtype:
         raise TypeError("operands must share a dtype")
-    _tau_check(tau, M, E)
-    if Y is None:
-        Y = torch.empty((E, M, N), dtype=X.dtype, device=X.device)
-    if ws is None:
-        ws = workspace(q, M, E, device=X.device)
+    _same_device(W, X, "W")
+    _tau_check(tau, M, E, like=X)
+    Y = _new_or_check(Y, (E, M, N), X, "Y")
+    ws = _ws_or_new(ws, q, M, X, E)
     _check("qalg_forward_batched", lib().qalg_forward_batched(
         E, _dev_ptr(X, "X"), _dev_ptr(W, "W"), _dev_ptr(tau, "tau"), q, M, K, N, _dev_ptr(Y, "Y"),
         _dtype_code(X), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags, _stream(stream)))

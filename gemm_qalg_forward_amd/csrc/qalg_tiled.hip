@@ -897,8 +897,13 @@ inline int cdiv(int64_t a, int64_t b) { return int((a + b - 1) / b); }
 
 // dW = bf16(sum over splits of the fp32 partial tiles), in split order: one
 // rounding per element, the same bits on every run.  4 elements per thread.
+// It checks the index like the tile kernel that wrote the partials: when that
+// kernel returned at once (an index of another q or M), dW is left untouched
+// instead of being overwritten from stale partials.
 __global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict__ part, int splits, int64_t n,
-                                                        uint16_t* __restrict__ out) {
+                                                        uint16_t* __restrict__ out, const int32_t* __restrict__ ws,
+                                                        int q, int M) {
+  if (ws[1] != kIndexMagic || ws[2] != q || ws[3] != M) return;
   const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
   if (i >= n) return;
   float4 acc = *reinterpret_cast<const float4*>(part + i);
@@ -912,9 +917,10 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict_
   *reinterpret_cast<u32x2*>(out + i) = pack4_bf16(acc.x, acc.y, acc.z, acc.w);
 }
 
-hipError_t launch_dw_reduce(const float* part, int splits, int64_t n, uint16_t* out, hipStream_t s) {
+hipError_t launch_dw_reduce(const Args& a, int64_t n, uint16_t* out, hipStream_t s) {
   const int64_t threads = n / 4;
-  hipLaunchKernelGGL(dw_reduce_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, part, splits, n, out);
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, a.part, a.splits, n,
+                     out, a.ws, a.q, a.M);
   return hipGetLastError();
 }
 
@@ -998,25 +1004,25 @@ hipError_t launch_cfg(const ProblemDesc& p, hipStream_t s, bool skip_cyclic) {
       hipLaunchKernelGGL((tiled_bf16_kernel<OP, C, kLawTensor>), g, dim3(C::THREADS), 0, s, a);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess || a.splits == 1) return e;
-      return launch_dw_reduce(a.part, a.splits, p.K * p.N, static_cast<uint16_t*>(p.C), s);
+      return launch_dw_reduce(a, p.K * p.N, static_cast<uint16_t*>(p.C), s);
     }
   }
   if (p.in_widths != nullptr) {
     hipLaunchKernelGGL((tiled_bf16_kernel<OP, C, kLawWidths>), g, dim3(C::THREADS), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
-    return launch_dw_reduce(a.part, a.splits, p.K * p.N, static_cast<uint16_t*>(p.C), s);
+    return launch_dw_reduce(a, p.K * p.N, static_cast<uint16_t*>(p.C), s);
   }
   if (p.graph_adj != nullptr) {
     hipLaunchKernelGGL((tiled_bf16_kernel<OP, C, kLawGraph>), g, dim3(C::THREADS), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
-    return launch_dw_reduce(a.part, a.splits, p.K * p.N, static_cast<uint16_t*>(p.C), s);
+    return launch_dw_reduce(a, p.K * p.N, static_cast<uint16_t*>(p.C), s);
   }
   hipLaunchKernelGGL((tiled_bf16_kernel<OP, C>), g, dim3(C::THREADS), 0, s, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  return launch_dw_reduce(a.part, a.splits, p.K * p.N, static_cast<uint16_t*>(p.C), s);
+  return launch_dw_reduce(a, p.K * p.N, static_cast<uint16_t*>(p.C), s);
 }
 
 using Cfg128 = TileCfg<128, 128, 64, 2, 2>;

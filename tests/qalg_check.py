@@ -1,8 +1,23 @@
-"""Comparison helpers for parity tests: relative Frobenius error per output group.
+"""Comparison helpers for parity tests.
 
-The bar (per output group, max over groups): 5e-3 for bf16 operands with fp32
-accumulation, 1e-5 for the fp32 path.  A group whose reference is exactly zero
-must be exactly zero.
+Two bars, both required of every projection output (Y, dX, dW):
+
+* relative Frobenius error per output group (max over groups): 5e-3 for bf16
+  operands with fp32 accumulation, 1e-5 for the fp32 path; a group whose
+  reference is exactly zero must be exactly zero;
+* a per-element bound, so that a localized error (one wrong element, piece or
+  row, which moves a group's norm by far less than its bar) cannot hide:
+      |got - ref| <= u_out |ref| + (1 + u_out) lam sqrt(n) u_acc mag
+  where ref is the fp64 oracle on the same inputs, mag the oracle evaluated on
+  the absolute values of the inputs (the sum of |term| over the support of that
+  output), n the number of terms, u_acc = 2^-24 (fp32 accumulation; bf16
+  products are exact in fp32), u_out = 2^-8 for the single RNE rounding to
+  bf16 (8 significant bits) and 0 for the fp32 path.  The accumulation term is
+  the probabilistic inner-product bound of Higham and Mary ("A new approach to
+  probabilistic rounding error analysis", SIAM J. Sci. Comput. 41(5), 2019):
+  with mean-independent rounding errors it fails with probability at most
+  2 n exp(-lam^2 (1 - u)^2 / 2) per output; lam = 8 makes that below 5e-10
+  for n <= 16384.
 """
 from __future__ import annotations
 
@@ -14,9 +29,13 @@ F32_TOL = 1e-5
 # The gated FFN's composed training step rounds to bf16 up to five times along
 # the path of any output (GU, H or dH, dGU, the output itself), each rounding
 # adding about 1.5e-3 relative error (the level one projection shows): about
-# sqrt(5) x 1.5e-3 = 3.4e-3 expected, 3.4-3.6e-3 measured.  Its bar is 1e-2 per
-# group, about 3x that; each projection given its bf16 inputs meets BF16_TOL.
-GATED_STEP_TOL = 1e-2
+# sqrt(5) x 1.5e-3 = 3.4e-3 expected, 3.4-4.1e-3 measured.  It is held to the
+# same 5e-3 per group as a single projection.
+GATED_STEP_TOL = 5e-3
+
+U_BF16 = 2.0 ** -8    # unit roundoff of bf16 round-to-nearest-even
+U_F32 = 2.0 ** -24    # unit roundoff of fp32
+LAMBDA = 8.0
 
 
 def _rel(got: np.ndarray, ref: np.ndarray) -> float:
@@ -46,3 +65,50 @@ def assert_groups(errs: list[float], tol: float, what: str) -> float:
     worst = max(errs) if errs else 0.0
     assert worst <= tol, f"{what}: max relative Frobenius error {worst:.3e} > {tol:.1e} (per group: {np.round(errs, 6)})"
     return worst
+
+
+def elementwise_bound(ref: np.ndarray, mag: np.ndarray, n: int, dtype: str) -> np.ndarray:
+    """Per-element error bound (module docstring) for an output of n fp32-accumulated terms."""
+    if dtype == "bf16":
+        return U_BF16 * np.abs(ref) + (1 + U_BF16) * LAMBDA * np.sqrt(n) * U_F32 * mag
+    # fp32 operands: the products are rounded too, 2n rounding errors in all
+    return LAMBDA * np.sqrt(2 * n) * U_F32 * mag
+
+
+def assert_elementwise(got: np.ndarray, ref: np.ndarray, mag: np.ndarray, n: int, dtype: str, what: str) -> float:
+    """Every element within elementwise_bound; returns the largest |got - ref| / bound (0/0 = 0)."""
+    assert got.shape == ref.shape == mag.shape
+    err = np.abs(got - ref)
+    bound = elementwise_bound(ref, mag, n, dtype)
+    bad = err > bound
+    if bad.any():
+        idx = np.unravel_index(int(np.argmax(np.where(bad, err - bound, -np.inf))), err.shape)
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {err.size} elements outside the per-element bound; worst at {idx}: "
+            f"got {got[idx]!r} ref {ref[idx]!r} bound {bound[idx]:.3e} (n = {n}, {dtype})")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), 0.0)
+    return float(r.max()) if r.size else 0.0
+
+
+def forward_elementwise(got: np.ndarray, ref: np.ndarray, X64: np.ndarray, W64: np.ndarray, tau, q: int,
+                        dtype: str, what: str, **law) -> float:
+    """Per-element bound on a projection output: mag is the oracle forward of |X| and |W| under the
+    same law (keyword arguments of row_typed_forward); n = K bounds the terms of any output."""
+    from oracle import qalg_oracle as O
+    mag = O.row_typed_forward(np.abs(X64), np.abs(W64), tau, q, **law)
+    return assert_elementwise(got, ref, mag, X64.shape[1], dtype, what)
+
+
+def backward_elementwise(got_dX, ref_dX, got_dW, ref_dW, X64, W64, dY64, tau, q: int, dtype: str,
+                         what: str = "", **law) -> tuple[float, float]:
+    """Per-element bounds on dX (n = N terms) and dW (n = M terms); either may be None (skipped).
+    For dX on sampled rows pass those rows of X and dY (a dX row depends on its own rows only)."""
+    from oracle import qalg_oracle as O
+    mdX, mdW = O.row_typed_backward(np.abs(X64), np.abs(W64), np.abs(dY64), tau, q, **law)
+    ex = ew = 0.0
+    if got_dX is not None:
+        ex = assert_elementwise(got_dX, ref_dX, mdX, W64.shape[1], dtype, f"dX{what}")
+    if got_dW is not None:
+        ew = assert_elementwise(got_dW, ref_dW, mdW, X64.shape[0], dtype, f"dW{what}")
+    return ex, ew

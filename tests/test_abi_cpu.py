@@ -129,6 +129,55 @@ def test_binding_refuses_cpu_tensors(lib):
         Q.qalg_forward(X, W, tau, 2, Y=torch.empty(4, 16, dtype=torch.bfloat16), ws=torch.empty(4096, dtype=torch.uint8))
 
 
+def test_binding_checks_caller_outputs_before_any_launch(lib):
+    """A caller-supplied output of the wrong shape, dtype or device is refused in
+    Python (the library trusts the sizes it is given and would write out of
+    bounds); the checks run before any pointer is taken, so CPU tensors suffice."""
+    torch = pytest.importorskip("torch")
+    bf = torch.bfloat16
+    M, K, N, q, F = 4, 16, 16, 2, 256
+    X, W, dY = torch.zeros(M, K, dtype=bf), torch.zeros(K, N, dtype=bf), torch.zeros(M, N, dtype=bf)
+    tau = torch.zeros(M, dtype=torch.int32)
+    ws = torch.empty(4096, dtype=torch.uint8)
+    adj = torch.zeros(q, dtype=torch.int64)
+    wid = [K // q] * q
+    cases = [
+        (lambda o: Q.qalg_forward(X, W, tau, q, Y=o, ws=ws), (M, N)),
+        (lambda o: Q.qalg_backward_dx(dY, W, tau, q, dX=o, ws=ws), (M, K)),
+        (lambda o: Q.qalg_backward_dw(X, dY, tau, q, dW=o, ws=ws), (K, N)),
+        (lambda o: Q.qalg_forward_graph(X, W, tau, q, adj, Y=o, ws=ws), (M, N)),
+        (lambda o: Q.qalg_backward_dx_graph(dY, W, tau, q, adj, dX=o, ws=ws), (M, K)),
+        (lambda o: Q.qalg_backward_dw_graph(X, dY, tau, q, adj, dW=o, ws=ws), (K, N)),
+        (lambda o: Q.qalg_forward_widths(X, W, tau, q, wid, wid, Y=o, ws=ws), (M, N)),
+        (lambda o: Q.qalg_backward_dx_widths(dY, W, tau, q, wid, wid, dX=o, ws=ws), (M, K)),
+        (lambda o: Q.qalg_backward_dw_widths(X, dY, tau, q, wid, wid, dW=o, ws=ws), (K, N)),
+        (lambda o: Q.qalg_forward_batched(X[None], W[None], tau[None], q, Y=o, ws=ws), (1, M, N)),
+        (lambda o: Q.qalg_gated_forward(X, torch.zeros(K, 2 * F, dtype=bf), tau, q, H=o, ws=ws), (M, F)),
+        (lambda o: Q.qalg_gated_forward_keep(X, torch.zeros(K, 2 * F, dtype=bf), tau, q, H=o, ws=ws), (M, F)),
+        (lambda o: Q.qalg_gated_forward_keep(X, torch.zeros(K, 2 * F, dtype=bf), tau, q, GU=o, ws=ws), (M, 2 * F)),
+        (lambda o: Q.qalg_merge_gate_up(torch.zeros(K, F, dtype=bf), torch.zeros(K, F, dtype=bf), q, Wgu=o), (K, 2 * F)),
+        (lambda o: Q.qalg_split_gate_up(torch.zeros(K, 2 * F, dtype=bf), q, Wg=o), (K, F)),
+        (lambda o: Q.qalg_swiglu_forward(torch.zeros(M, 2 * F, dtype=bf), q, H=o), (M, F)),
+        (lambda o: Q.qalg_swiglu_backward(torch.zeros(M, 2 * F, dtype=bf), torch.zeros(M, F, dtype=bf), q, dGU=o),
+         (M, 2 * F)),
+        (lambda o: Q.qalg_attention_forward(torch.zeros(2, 8, 64, dtype=bf), torch.zeros(1, 8, 64, dtype=bf),
+                                            torch.zeros(1, 8, 64, dtype=bf), 2, O=o), (2, 8, 64)),
+    ]
+    for call, shape in cases:
+        short = (shape[0] - 1,) + tuple(shape[1:])
+        with pytest.raises(ValueError, match="shape"):
+            call(torch.empty(short, dtype=bf))
+        with pytest.raises(TypeError, match="dtype"):
+            call(torch.empty(shape, dtype=torch.float32))
+        # the right output gets as far as the device check of the inputs
+        with pytest.raises(ValueError, match="GPU"):
+            call(torch.empty(shape, dtype=bf))
+    with pytest.raises(ValueError, match="tau must be int32"):
+        Q.qalg_type_schedule(torch.zeros(M, dtype=torch.int64), q, tau=torch.empty(M - 1, dtype=torch.int32))
+    with pytest.raises(TypeError, match="share a dtype"):
+        Q.qalg_forward_graph(X, W.float(), tau, q, adj, ws=ws)
+
+
 def call_gated(lib, X=FAKE, W=FAKE, tau=FAKE, q=2, M=64, K=256, F=512, H=FAKE, dt=1, ws=FAKE,
                wsb=1 << 20, flags=0):
     return lib.qalg_gated_forward(X, W, tau, q, M, K, F, H, dt, ws, wsb, flags, None)

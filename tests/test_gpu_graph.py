@@ -12,7 +12,8 @@ import gemm_qalg_forward_amd as Q
 import synth
 from gpu_common import make_tau, say, tau_dev, to_dev, to_f64, torch_cuda
 from oracle import qalg_oracle as O
-from qalg_check import BF16_TOL, assert_groups, rel_frob_blocks, rel_frob_col_groups
+from qalg_check import (BF16_TOL, assert_groups, backward_elementwise, forward_elementwise, rel_frob_blocks,
+                        rel_frob_col_groups)
 
 pytestmark = pytest.mark.gpu
 
@@ -71,6 +72,7 @@ def test_graph_forward_matches_oracle(case):
     got = to_f64(Y)
     r = N // q
     e = assert_groups(rel_frob_col_groups(got, Yr, q), BF16_TOL, "Y")
+    forward_elementwise(got, Yr, X.f64, W.f64, tau, q, "bf16", "Y", edges=edges)
     for i in range(q):
         rows = np.where(tau == i)[0]
         for j in range(q):
@@ -133,6 +135,7 @@ def test_graph_gradients_match_oracle(case):
     gx, gw = to_f64(dX), to_f64(dW)
     e1 = assert_groups(rel_frob_col_groups(gx, dXr, q), BF16_TOL, "dX")
     e2 = assert_groups(rel_frob_blocks(gw, dWr, q), BF16_TOL, "dW")
+    backward_elementwise(gx, dXr, gw, dWr, X.f64, W.f64, dY.f64, tau, q, "bf16", edges=edges)
     s_, r_ = K // q, N // q
     for i in range(q):
         rows = np.where(tau == i)[0]

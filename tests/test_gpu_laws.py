@@ -13,7 +13,8 @@ import gemm_qalg_forward_amd as Q
 import synth
 from gpu_common import make_tau, say, tau_dev, to_dev, to_f64, torch_cuda
 from oracle import qalg_oracle as O
-from qalg_check import BF16_TOL, assert_groups, rel_frob_blocks, rel_frob_col_groups
+from qalg_check import (BF16_TOL, assert_groups, backward_elementwise, forward_elementwise, rel_frob_blocks,
+                        rel_frob_col_groups)
 
 pytestmark = pytest.mark.gpu
 
@@ -62,6 +63,7 @@ def test_tensor_law_forward_matches_oracle(shape):
     assert torch.equal(Y, Y2), "forward is not bitwise reproducible"
     Yr = O.row_typed_forward(X.f64, W.f64, tau, q, table=O.tensor_power_table(L))
     e = assert_groups(rel_frob_col_groups(to_f64(Y), Yr, q), BF16_TOL, "Y")
+    forward_elementwise(to_f64(Y), Yr, X.f64, W.f64, tau, q, "bf16", "Y", table=O.tensor_power_table(L))
     say(f"    max rel err {e:.2e}")
     if bad:
         rows = np.where((tau < 0) | (tau >= q))[0]
@@ -154,6 +156,8 @@ def test_tensor_law_gradients_match_oracle(shape):
     dXr, dWr = O.row_typed_backward(X.f64, W.f64, dY.f64, tau, q, table=O.tensor_power_table(L))
     e1 = assert_groups(rel_frob_col_groups(to_f64(dX), dXr, q), BF16_TOL, "dX")
     e2 = assert_groups(rel_frob_blocks(to_f64(dW), dWr, q), BF16_TOL, "dW")
+    backward_elementwise(to_f64(dX), dXr, to_f64(dW), dWr, X.f64, W.f64, dY.f64, tau, q, "bf16",
+                         table=O.tensor_power_table(L))
     say(f"    max rel err dX {e1:.2e}, dW {e2:.2e}")
     if bad:
         rows = np.where((tau < 0) | (tau >= q))[0]

@@ -10,7 +10,8 @@ import gemm_qalg_forward_amd as Q
 import synth
 from gpu_common import make_tau, say, tau_dev, to_dev, to_f64, torch_cuda
 from oracle import qalg_oracle as O
-from qalg_check import BF16_TOL, F32_TOL, assert_groups, rel_frob_blocks, rel_frob_col_groups
+from qalg_check import (BF16_TOL, F32_TOL, assert_groups, backward_elementwise, forward_elementwise, rel_frob_blocks,
+                        rel_frob_col_groups)
 
 pytestmark = pytest.mark.gpu
 
@@ -65,6 +66,9 @@ def test_forward_dx_dw_match_oracle(shape, dtype):
     ex = assert_groups(rel_frob_col_groups(to_f64(dX), dXr, q), tol, "dX")
     ew = assert_groups(rel_frob_blocks(to_f64(dW), dWr, q), tol, "dW")
     say(f"    max rel err  Y {ey:.2e}  dX {ex:.2e}  dW {ew:.2e}")
+    ry = forward_elementwise(to_f64(Y), Yr, X.f64, W.f64, tau, q, dtype, "Y")
+    rx, rw = backward_elementwise(to_f64(dX), dXr, to_f64(dW), dWr, X.f64, W.f64, dY.f64, tau, q, dtype)
+    say(f"    per-element error / bound  Y {ry:.2f}  dX {rx:.2f}  dW {rw:.2f}")
     # rows of an out-of-range type are exactly zero in Y and dX
     badrows = (tau < 0) | (tau >= q)
     if badrows.any():
@@ -88,6 +92,8 @@ def test_small_m_paths_match_oracle(M, q, K, N):
     Yr = O.row_typed_forward(X.f64, W.f64, tau, q)
     assert_groups(rel_frob_col_groups(to_f64(Ys), Yr, q), BF16_TOL, "Y small-M")
     assert_groups(rel_frob_col_groups(to_f64(Yt), Yr, q), BF16_TOL, "Y tiled")
+    forward_elementwise(to_f64(Ys), Yr, X.f64, W.f64, tau, q, "bf16", "Y small-M")
+    forward_elementwise(to_f64(Yt), Yr, X.f64, W.f64, tau, q, "bf16", "Y tiled")
     Ys2 = Q.qalg_forward(Xd, Wd, td, q, ws=ws, flags=Q.QALG_FLAG_FORCE_SMALL_M)
     torch.cuda.synchronize()
     assert torch.equal(Ys, Ys2), "small-M path is not bitwise reproducible"
@@ -114,6 +120,7 @@ def test_batched_experts_match_oracle(E, M, q, K, N):
     for e in range(E):
         Yr = O.row_typed_forward(Xs[e].f64, Ws[e].f64, taus[e], q)
         assert_groups(rel_frob_col_groups(Yh[e], Yr, q), BF16_TOL, f"expert {e}")
+        forward_elementwise(Yh[e], Yr, Xs[e].f64, Ws[e].f64, taus[e], q, "bf16", f"expert {e}")
 
 
 @pytest.mark.parametrize("kind,q,M,period", [("cyclic", 8, 16384, 0), ("cyclic", 3, 1001, 0),

@@ -11,7 +11,7 @@ import gemm_qalg_forward_amd as Q
 import synth
 from gpu_common import make_tau, say, tau_dev, to_dev, to_f64, torch_cuda
 from oracle import qalg_oracle as O
-from qalg_check import BF16_TOL, assert_groups, rel_frob_col_groups
+from qalg_check import BF16_TOL, assert_groups, forward_elementwise, rel_frob_col_groups
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +53,7 @@ def test_tile_heights_match_oracle(shape):
         torch.cuda.synchronize()
         assert torch.equal(Y, Y2), f"{name}: not bitwise reproducible"
         e = assert_groups(rel_frob_col_groups(to_f64(Y), Yr, q), BF16_TOL, f"Y ({name})")
+        forward_elementwise(to_f64(Y), Yr, X.f64, W.f64, tau, q, "bf16", f"Y ({name})", table=table)
         if bad:
             rows = np.where((tau < 0) | (tau >= q))[0]
             assert np.all(to_f64(Y)[rows] == 0.0)

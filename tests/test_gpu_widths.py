@@ -11,7 +11,7 @@ import gemm_qalg_forward_amd as Q
 import synth
 from gpu_common import make_tau, say, tau_dev, to_dev, to_f64, torch_cuda
 from oracle import qalg_oracle as O
-from qalg_check import BF16_TOL, _rel
+from qalg_check import BF16_TOL, _rel, backward_elementwise, forward_elementwise
 
 pytestmark = pytest.mark.gpu
 
@@ -67,6 +67,9 @@ def test_widths_forward_and_gradients_match_oracle(case):
     e2 = max(_block_errs(to_f64(dW), dWr, kw, nw))
     say(f"    max rel err Y {e0:.2e}, dX {e1:.2e}, dW {e2:.2e}")
     assert e0 <= BF16_TOL and e1 <= BF16_TOL and e2 <= BF16_TOL
+    law = {"in_widths": kw, "out_widths": nw}
+    forward_elementwise(to_f64(Y), Yr, X.f64, W.f64, tau, q, "bf16", "Y", **law)
+    backward_elementwise(to_f64(dX), dXr, to_f64(dW), dWr, X.f64, W.f64, dY.f64, tau, q, "bf16", **law)
     if bad:
         rows = np.where((tau < 0) | (tau >= q))[0]
         assert np.all(to_f64(Y)[rows] == 0.0) and np.all(to_f64(dX)[rows] == 0.0)

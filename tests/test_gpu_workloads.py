@@ -20,7 +20,8 @@ import gemm_qalg_forward_amd as Q
 import synth
 from gpu_common import say, tau_dev, to_dev, to_f64, torch_cuda
 from oracle import qalg_oracle as O
-from qalg_check import BF16_TOL, F32_TOL, GATED_STEP_TOL as STEP_TOL, assert_groups, rel_frob_blocks, rel_frob_col_groups
+from qalg_check import (BF16_TOL, F32_TOL, GATED_STEP_TOL as STEP_TOL, assert_groups, backward_elementwise,
+                        forward_elementwise, rel_frob_blocks, rel_frob_col_groups)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +36,7 @@ def _sample_rows(M, q, n, seed):
 def _sampled_forward_check(X, W, tau, q, Yd, rows, what):
     Yr = O.row_typed_forward(X.f64[rows], W.f64, tau[rows], q)
     got = to_f64(Yd[rows])
+    forward_elementwise(got, Yr, X.f64[rows], W.f64, tau[rows], q, "bf16", what)
     return assert_groups(rel_frob_col_groups(got, Yr, q), BF16_TOL, what)
 
 
@@ -59,6 +61,8 @@ def test_q2_fp32_whole_output():
     assert_groups(rel_frob_col_groups(to_f64(Y), Yr, q), F32_TOL, "Y")
     assert_groups(rel_frob_col_groups(to_f64(dX), dXr, q), F32_TOL, "dX")
     assert_groups(rel_frob_blocks(to_f64(dW), dWr, q), F32_TOL, "dW")
+    forward_elementwise(to_f64(Y), Yr, X.f64, W.f64, tau, q, "f32", "Y")
+    backward_elementwise(to_f64(dX), dXr, to_f64(dW), dWr, X.f64, W.f64, dY.f64, tau, q, "f32")
     # 6 of the 8 block products of the square form are used by the two row types
     assert O.mac_count(tau, q, K, N)[0] == 6
 
@@ -78,7 +82,8 @@ def test_lm_ffn_q4_whole_output(K, N):
     torch.cuda.synchronize()
     Yr = O.row_typed_forward(X.f64, W.f64, tau, q)
     e = assert_groups(rel_frob_col_groups(to_f64(Y), Yr, q), BF16_TOL, "Y")
-    say(f"    max rel err {e:.2e}")
+    r = forward_elementwise(to_f64(Y), Yr, X.f64, W.f64, tau, q, "bf16", "Y")
+    say(f"    max rel err {e:.2e}; per-element error / bound {r:.2f}")
 
 
 @pytest.mark.parametrize("proj", ["up", "down"])
@@ -172,10 +177,15 @@ def test_training_grads_q8():
     # dX rows depend on their own dY rows only
     dXr_s, _ = O.row_typed_backward(X.f64[rows], W.f64, dY.f64[rows], tau[rows], q)
     assert_groups(rel_frob_col_groups(to_f64(dX[rows]), dXr_s, q), BF16_TOL, "dX")
+    backward_elementwise(to_f64(dX[rows]), dXr_s, None, None, X.f64[rows], W.f64, dY.f64[rows], tau[rows], q, "bf16")
     # dW is a sum over all rows: the whole oracle gradient (fp64 block GEMMs)
     _, dWr = O.row_typed_backward(X.f64, W.f64, dY.f64, tau, q)
     e = assert_groups(rel_frob_blocks(to_f64(dW), dWr, q), BF16_TOL, "dW")
     e0 = assert_groups(rel_frob_blocks(to_f64(dW0), dWr, q), BF16_TOL, "dW unsplit")
+    _, mdW = O.row_typed_backward(np.abs(X.f64), np.abs(W.f64), np.abs(dY.f64), tau, q)
+    from qalg_check import assert_elementwise
+    assert_elementwise(to_f64(dW), dWr, mdW, M, "bf16", "dW")
+    assert_elementwise(to_f64(dW0), dWr, mdW, M, "bf16", "dW unsplit")
     say(f"    dW max rel err {e:.2e} (unsplit {e0:.2e})")
 
 
