@@ -10,7 +10,7 @@ Functions carry the C names:
     qalg_backward_dx_graph, qalg_backward_dw_graph, qalg_forward_widths, qalg_backward_dx_widths,
     qalg_backward_dw_widths,
     qalg_gated_forward, qalg_gated_forward_keep, qalg_merge_gate_up, qalg_split_gate_up, qalg_swiglu_forward, qalg_swiglu_backward,
-    qalg_attention_forward,
+    qalg_attention_forward, qalg_forward_noalloc,
     qalg_type_schedule, qalg_build_index, qalg_build_index_batched,
     qalg_read_status, qalg_workspace_bytes, qalg_index_layout,
     qalg_status_string, qalg_version.
@@ -32,6 +32,7 @@ __all__ = [
     "qalg_backward_dw_widths",
     "qalg_gated_forward", "qalg_gated_forward_keep", "qalg_merge_gate_up", "qalg_split_gate_up", "qalg_swiglu_forward",
     "qalg_swiglu_backward", "qalg_attention_forward", "qalg_read_status", "workspace",
+    "qalg_forward_noalloc", "QALG_NOALLOC_SCRATCH_BYTES",
 ]
 
 QALG_F32 = 0
@@ -46,6 +47,7 @@ QALG_FLAG_TILE_M256 = 64
 QALG_SCHEDULE_CYCLIC = 0
 QALG_SCHEDULE_INTERVAL = 1
 QALG_MAX_Q = 512
+QALG_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 _PKG = pathlib.Path(__file__).resolve().parent
 lib_path = _PKG / "libqalg.so"
@@ -92,6 +94,7 @@ _SIGS = {
     "qalg_attention_forward": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _vp, _c_i32,
                                               _c_u32, _vp]),
     "qalg_read_status": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i64, _vp, ctypes.POINTER(_c_i64)]),
+    "qalg_forward_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _c_u32, _vp]),
 }
 
 
@@ -557,6 +560,24 @@ def qalg_forward_batched(X, W, tau, q: int, Y=None, ws=None, flags: int = 0, str
     _check("qalg_forward_batched", lib().qalg_forward_batched(
         E, _dev_ptr(X, "X"), _dev_ptr(W, "W"), _dev_ptr(tau, "tau"), q, M, K, N, _dev_ptr(Y, "Y"),
         _dtype_code(X), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags, _stream(stream)))
+    return Y
+
+
+def qalg_forward_noalloc(X, W, tau, q: int, Y, flags: int = 0, stream=None):
+    """Y = X *_{Q_q} W with the index in the library's own device array (no workspace, no
+    allocation by the library or here: Y is the caller's).  X [M, K], W [K, N], tau int32 [M]."""
+    M, K = X.shape
+    K2, N = W.shape
+    if K2 != K:
+        raise ValueError("X and W inner sizes differ")
+    if X.dtype != W.dtype:
+        raise TypeError("operands must share a dtype")
+    _same_device(W, X, "W")
+    _tau_check(tau, M, like=X)
+    _check_out(Y, (M, N), X, "Y")
+    _check("qalg_forward_noalloc", lib().qalg_forward_noalloc(
+        _dev_ptr(X, "X"), _dev_ptr(W, "W"), _dev_ptr(tau, "tau"), q, M, K, N, _dev_ptr(Y, "Y"), _dtype_code(X),
+        flags, _stream(stream)))
     return Y
 
 

@@ -17,7 +17,7 @@ CSRC = PKG / "csrc"
 OBJ = PKG / "_build"
 LIB = PKG / "libqalg.so"
 
-SOURCES = ["qalg_api.cpp", "qalg_index.hip", "qalg_tiled.hip", "qalg_small_m.hip", "qalg_fwd.hip", "qalg_grad.hip", "qalg_act.hip", "qalg_attn.hip"]
+SOURCES = ["qalg_api.cpp", "qalg_index.hip", "qalg_tiled.hip", "qalg_small_m.hip", "qalg_fwd.hip", "qalg_grad.hip", "qalg_act.hip", "qalg_attn.hip", "qalg_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

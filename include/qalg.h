@@ -29,7 +29,9 @@
  *  - Ownership: every pointer is device memory owned by the caller (for
  *    example allocated by PyTorch).  The library allocates nothing, keeps no
  *    pointer after a call returns, and holds no state: calls are reentrant,
- *    but concurrent calls need separate workspaces.
+ *    but concurrent calls need separate workspaces.  (qalg_forward_noalloc,
+ *    for callers that cannot allocate, is the one exception: it uses a device
+ *    array of the library's own and keeps that array's address per GPU.)
  *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the
  *    default stream) and the call returns without waiting.  Buffers must
  *    stay valid until the stream has run the work.
@@ -399,6 +401,26 @@ qalg_status qalg_swiglu_backward(const void* GU, const void* dH, int32_t q, int6
 qalg_status qalg_attention_forward(const void* Q, const void* K, const void* V, int32_t Hq, int32_t Hkv,
                                    int64_t S, int32_t d, int32_t q, void* O, int32_t dtype, uint32_t flags,
                                    void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * qalg_forward with no workspace argument.  The type index it builds goes to
+ * a device array owned by the library, QALG_NOALLOC_SCRATCH_BYTES on each GPU
+ * it runs on, reserved with the library's code object and held until the
+ * process ends; the call allocates and frees nothing.  Arguments, results and
+ * errors as qalg_forward, plus: qalg_workspace_bytes(q, M) must not exceed
+ * QALG_NOALLOC_SCRATCH_BYTES (QALG_ERR_WORKSPACE; about 1.04 M rows at small
+ * q), and QALG_FLAG_INDEX_READY is refused (QALG_ERR_ARG): every call on a GPU
+ * shares that GPU's array, so the index is rebuilt by each call.  Calls that
+ * overlap on one GPU (two streams, or two host threads) race on the array and
+ * must be ordered by the caller; calls on one stream are ordered already.
+ * The GPU is the stream's device (the current device for the NULL stream).
+ */
+#define QALG_NOALLOC_SCRATCH_BYTES (4u << 20)
+qalg_status qalg_forward_noalloc(const void* X, const void* W, const int32_t* tau, int32_t q,
+                                 int64_t M, int64_t K, int64_t N, void* Y,
+                                 int32_t dtype, uint32_t flags, void* stream);
 
 /*
  * Number of rows with an out-of-range type seen by the last index build in
