@@ -20,7 +20,13 @@ Reported (one JSON line):
   roofline         the forward GEMM kernel against the bf16 MFMA peak, its
                    launch time taken with HIP events on the launch stream
   cpu_baseline     the fp64 CPU oracle on the host cores (a bounded sample)
-  extra            further legs, each timed separately: training (forward + dX +
+  protocol         the pages' timing protocol on the two forwards: graph replays of at
+                   least 2 ms per trial, 12 trials alternating q = 8 and its q = 1 control,
+                   medians and interquartile ranges, and a flushed (cold-cache) run
+  clock            the shader clock sampled during back-to-back replays of the up forward,
+                   and the bf16 MFMA peak at that clock (256 CU x f x 4096 FLOP)
+  extra            further legs, each timed separately: the ~110M-LM FFN (768 <-> 3072,
+                   q = 4, M = 8192, both roofline fractions), training (forward + dX +
                    dW at the same shape), small-M decode (64 experts), gated
                    SwiGLU FFN (forward and training step), the 64-expert shapes at
                    M = 1..1024 against q = 1, the pilot FFN under
@@ -57,6 +63,135 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+class Protocol:
+    """The pages' timing protocol (App E, App F), adapted: each operation is captured in a HIP
+    graph and replayed until a timed trial lasts at least 2 ms (warm caches); trials alternate
+    between the algebra and its q = 1 control of the same template, 12 of each, reported as
+    median and interquartile range; a flushed run writes then reads a 1 GiB buffer before each
+    single replay (outside the timed interval), so that neither L2 nor the 256 MB MALL holds
+    the operands and no dirty lines of the flush are written back inside it."""
+
+    def __init__(self, torch, np, dev):
+        self.torch, self.np = torch, np
+        self.flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        self.side = torch.cuda.Stream()   # default priority
+
+    def capture(self, fn):
+        """fn(stream) enqueues the operation; it is run once eagerly (first-call set-up), then captured."""
+        torch = self.torch
+        self.side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(self.side):
+            fn(self.side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.side):
+            fn(self.side)
+        torch.cuda.synchronize()
+        return g
+
+    def _events(self):
+        E = self.torch.cuda.Event
+        return E(enable_timing=True), E(enable_timing=True)
+
+    def replay_ms(self, g, reps):
+        a, b = self._events()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        self.torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def flushed_ms(self, g, n=8):
+        np, out = self.np, []
+        for k in range(n + 2):
+            self.flush.fill_(k & 0xFF)
+            self.flush.view(self.torch.float32).sum()
+            out.append(self.replay_ms(g, 1))
+        return float(np.median(out[2:]))
+
+    def stats(self, xs):
+        np = self.np
+        q25, q50, q75 = np.percentile(xs, [25, 50, 75])
+        return {"median_ms": round(float(q50), 5), "iqr_ms": [round(float(q25), 5), round(float(q75), 5)]}
+
+    def compare(self, g_q, g_1, trials=12, min_ms=2.0, flushed=True):
+        """Alternating warm trials of the algebra (g_q) and its q = 1 control (g_1), then flushed runs."""
+        np = self.np
+        for g in (g_q, g_1):      # settle the clock on this operation
+            self.replay_ms(g, 20)
+        reps = {id(g): max(1, int(np.ceil(min_ms / self.replay_ms(g, 3)))) for g in (g_q, g_1)}
+        tq, t1 = [], []
+        for _ in range(trials):
+            tq.append(self.replay_ms(g_q, reps[id(g_q)]))
+            t1.append(self.replay_ms(g_1, reps[id(g_1)]))
+        res = {"warm": self.stats(tq), "warm_q1": self.stats(t1), "replays_per_trial": [reps[id(g_q)], reps[id(g_1)]],
+               "trials": trials}
+        res["speedup_vs_q1"] = round(float(np.median(t1) / np.median(tq)), 3)
+        if flushed:
+            fq, f1 = self.flushed_ms(g_q), self.flushed_ms(g_1)
+            res["flushed_ms"], res["flushed_q1_ms"] = round(fq, 5), round(f1, 5)
+            res["flushed_speedup_vs_q1"] = round(f1 / fq, 3)
+        return res
+
+
+def sclk_sampler(torch):
+    """A function returning the shader clock (MHz) of GPU 0 from its hwmon node, or None when the
+    node is not visible.  The card is found by its PCI address."""
+    import glob
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        dom, bus, devn = (getattr(pr, "pci_domain_id", 0), getattr(pr, "pci_bus_id", None),
+                          getattr(pr, "pci_device_id", 0))
+        if bus is None:
+            return None
+        paths = glob.glob(f"/sys/bus/pci/devices/{dom:04x}:{bus:02x}:{devn:02x}.0/hwmon/hwmon*/freq1_input")
+        if not paths:
+            return None
+        path = paths[0]
+
+        def read():
+            try:
+                with open(path) as f:
+                    return int(f.read().strip()) / 1e6
+            except (OSError, ValueError):
+                return None
+        return read if read() is not None else None
+    except Exception:  # informational only
+        return None
+
+
+def sustained_clock(torch, np, g, seconds=0.4):
+    """Median shader clock sampled every ~5 ms while graph g is replayed back to back for `seconds`."""
+    import threading
+    read = sclk_sampler(torch)
+    if read is None:
+        return None
+    vals, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            v = read()
+            if v:
+                vals.append(v)
+            time.sleep(0.005)
+    th = threading.Thread(target=sample)
+    t_end = time.time() + seconds
+    th.start()
+    while time.time() < t_end:
+        for _ in range(10):
+            g.replay()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not vals:
+        return None
+    f = float(np.median(vals))
+    return {"sclk_mhz_median": round(f, 1), "samples": len(vals),
+            "peak_at_clock_tflops": round(256 * f * 1e6 * 4096 / 1e12, 1),
+            "source": "hwmon freq1_input of the GPU's PCI device, sampled during back-to-back replays"}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -67,8 +202,11 @@ def parse():
                     help="untimed steps run for this wall time before the warm-up steps (clock ramp from idle)")
     ap.add_argument("--cpu-rows", type=int, default=16384,
                     help="rows of each projection the CPU oracle leg evaluates")
+    ap.add_argument("--cpu-rows-1t", type=int, default=1024,
+                    help="rows of each projection the one-thread CPU oracle run evaluates")
     ap.add_argument("--no-extra", action="store_true", help="skip the training and decode legs")
-    ap.add_argument("--no-dense", action="store_true", help="skip the q = 1 dense-control leg")
+    ap.add_argument("--no-dense", action="store_true", help="skip the protocol's q = 1 control trials")
+    ap.add_argument("--legs", default="all", help="comma-separated extra legs to run (default: all)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (scales HBM counters)")
     return ap.parse_args()
@@ -175,30 +313,57 @@ def main() -> int:
     log(f"[bench] q=8 step {ms_step:.3f} ms; forward launch up {np.median(up_ms):.3f} ms "
         f"down {np.median(dn_ms):.3f} ms; {value:.1f} algebra TFLOP/s")
 
-    # ---------------- dense control: the same kernel template at q = 1 ----------------
+    # ---------------- the pages' protocol: graph replays, alternating q = 8 / q = 1 trials ----------------
+    # (the dense control is the same kernel template at q = 1, where Q_1 is the plain product)
+    proto = Protocol(torch, np, dev)
+    tau1 = torch.zeros(M, dtype=torch.int32, device=dev)
+    ws1 = Q.workspace(1, M, device=dev)
+    Q.qalg_build_index(tau1, 1, ws=ws1, stream=stream)
+    torch.cuda.synchronize()
+    graphs = {
+        (proj, q): proto.capture(lambda st, X=X, W=W, Y=Y, q=q, t=t, w=w: Q.qalg_forward(
+            X, W, t, q, Y=Y, ws=w, flags=ready, stream=st))
+        for proj, X, W, Y in (("up", d["Xu"], d["Wu"], Yu), ("down", d["Xd"], d["Wd"], Yd))
+        for q, t, w in ((QQ, tau, ws), (1, tau1, ws1))
+    }
+    protocol = {}
     speedup = dense_tflops = None
     if not args.no_dense:
-        tau1 = torch.empty(M, dtype=torch.int32, device=dev)
-        ws1 = Q.workspace(1, M, device=dev)
-        dsteps = max(3, args.steps // 4)
-        dtotal, dup, ddn = timed(1, tau1, ws1, dsteps, 2)
-        dense_fwd_ms = (sum(dup) + sum(ddn)) / (len(dup) + len(ddn))
-        speedup = round(dense_fwd_ms / fwd_launch_ms, 3)
-        dense_tflops = round(dense_flop_proj / (dense_fwd_ms * 1e-3) / 1e12, 1)
-        log(f"[bench] q=1 dense template: forward launch {dense_fwd_ms:.3f} ms ({dense_tflops:.1f} TFLOP/s); "
-            f"speedup {speedup:.2f}x")
+        protocol = {proj: proto.compare(graphs[(proj, QQ)], graphs[(proj, 1)]) for proj in ("up", "down")}
+        t8 = sum(protocol[p_]["warm"]["median_ms"] for p_ in ("up", "down"))
+        t1 = sum(protocol[p_]["warm_q1"]["median_ms"] for p_ in ("up", "down"))
+        speedup = round(t1 / t8, 3)
+        dense_tflops = round(2 * dense_flop_proj / (t1 * 1e-3) / 1e12, 1)
+        for p_ in ("up", "down"):
+            r_ = protocol[p_]
+            r_["algebra_tflops_warm"] = round(alg_flop_proj / (r_["warm"]["median_ms"] * 1e-3) / 1e12, 1)
+            r_["algebra_tflops_flushed"] = round(alg_flop_proj / (r_["flushed_ms"] * 1e-3) / 1e12, 1)
+            r_["dense_tflops_q1_warm"] = round(dense_flop_proj / (r_["warm_q1"]["median_ms"] * 1e-3) / 1e12, 1)
+        log(f"[bench] protocol (12 alternating trials, graph replays >= 2 ms): {protocol}")
+        log(f"[bench] q=1 dense template: {dense_tflops:.1f} TFLOP/s; speedup {speedup:.2f}x")
+    clock = sustained_clock(torch, np, graphs[("up", QQ)])
+    if clock is not None:
+        clock["frac_of_peak_at_clock"] = round(achieved / clock["peak_at_clock_tflops"], 4)
+    log(f"[bench] sustained clock during the up forward: {clock}")
 
     extra = {}
-    if not args.no_extra:
-        extra["training"] = training_leg(Q, torch, np, synth, dev, stream)
-        extra["decode"] = decode_leg(Q, torch, np, synth, dev, stream)
-        extra["experts"] = experts_leg(Q, torch, np, synth, dev, stream)
-        extra["gated_ffn"] = gated_leg(Q, torch, np, synth, dev, stream)
-        extra["pilot_ffn"] = pilot_leg(Q, torch, np, synth, dev, stream)
-        extra["few_rows"] = few_rows_leg(Q, torch, np, synth, dev, stream)
-        extra["attention"] = attention_leg(Q, torch, np, synth, dev, stream)
-        extra["graph_law"] = graph_leg(Q, torch, np, synth, dev, stream)
-        extra["unequal_widths"] = widths_leg(Q, torch, np, synth, dev, stream)
+    legs = {
+        "lm_ffn_q4": lambda: lm_ffn_leg(Q, torch, np, synth, dev, proto),
+        "training": lambda: training_leg(Q, torch, np, synth, dev, stream),
+        "decode": lambda: decode_leg(Q, torch, np, synth, dev, stream),
+        "experts": lambda: experts_leg(Q, torch, np, synth, dev, stream),
+        "gated_ffn": lambda: gated_leg(Q, torch, np, synth, dev, stream),
+        "pilot_ffn": lambda: pilot_leg(Q, torch, np, synth, dev, stream),
+        "few_rows": lambda: few_rows_leg(Q, torch, np, synth, dev, stream),
+        "attention": lambda: attention_leg(Q, torch, np, synth, dev, stream),
+        "graph_law": lambda: graph_leg(Q, torch, np, synth, dev, stream),
+        "unequal_widths": lambda: widths_leg(Q, torch, np, synth, dev, stream),
+    }
+    chosen = [] if args.no_extra else (list(legs) if args.legs == "all" else args.legs.split(","))
+    for name in chosen:
+        if name not in legs:
+            raise SystemExit(f"unknown leg {name!r}; choose from {', '.join(legs)}")
+        extra[name] = legs[name]()
 
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib << 20
@@ -212,6 +377,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_leg(np, host, args.cpu_rows)
+        cpu["one_thread"] = cpu_leg(np, host, args.cpu_rows_1t, threads=1)
 
     out = {
         "metric": "algebra TFLOP/s + % bf16 MFMA peak; speedup vs same-shape dense GEMM",
@@ -233,6 +399,8 @@ def main() -> int:
         "dense_equiv_tflops": round(2 * dense_flop_proj / (ms_step * 1e-3) / 1e12, 1),
         "speedup_vs_dense": speedup,
         "dense_template_tflops": dense_tflops,
+        "protocol": protocol,
+        "clock": clock,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": profiled_traffic(),
                      "kernel": "fwd_persistent_kernel (forward GEMM, 256x256 tiles)",
@@ -264,6 +432,46 @@ def profiled_traffic():
         return int(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def lm_ffn_leg(Q, torch, np, synth, dev, proto):
+    """The ~110M-LM FFN shapes in bf16 with q = 4: up 768 -> 3072 and down 3072 -> 768, M = 8192
+    (8 sequences x 1024 positions, tau = (m mod 1024) mod 4), forward.  At these sizes a launch
+    lasts about 10 us, so each projection is timed with the graph-replay protocol (warm, and
+    flushed), against the q = 1 control.  The arithmetic intensity (about 250 FLOP per algorithmic
+    byte) sits just under the ridge of the MFMA and HBM roofs, so both fractions are reported."""
+    c, Mx, q = 2, 8192, 4
+    to = lambda op: torch.from_numpy(op.bits.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    pos = synth.cyclic_positions(Mx, seq_len=1024)
+    tau = Q.qalg_type_schedule(torch.from_numpy(pos).to(dev), q)
+    tau1 = torch.zeros(Mx, dtype=torch.int32, device=dev)
+    ws, ws1 = Q.workspace(q, Mx, device=dev), Q.workspace(1, Mx, device=dev)
+    Q.qalg_build_index(tau, q, ws=ws)
+    Q.qalg_build_index(tau1, 1, ws=ws1)
+    r = Q.QALG_FLAG_INDEX_READY
+    res = {"workload": "lm_ffn_q4_M8192_bf16_fwd", "tau": "(m mod 1024) mod 4"}
+    for proj, K, N, off in (("up", 768, 3072, 0), ("down", 3072, 768, 10)):
+        X = to(synth.normal_operand(1000 * c + 1 + off, (Mx, K), 1.0, "bf16"))
+        W = to(synth.normal_operand(1000 * c + 2 + off, (K, N), K ** -0.5, "bf16"))
+        Y = torch.empty(Mx, N, dtype=torch.bfloat16, device=dev)
+        g_q = proto.capture(lambda st: Q.qalg_forward(X, W, tau, q, Y=Y, ws=ws, flags=r, stream=st))
+        g_1 = proto.capture(lambda st: Q.qalg_forward(X, W, tau1, 1, Y=Y, ws=ws1, flags=r, stream=st))
+        cmp_ = proto.compare(g_q, g_1)
+        flop = 2.0 * rho(q) * Mx * K * N
+        byts = 2 * (Mx * K + K * N + Mx * N)
+        for key, t in (("warm", cmp_["warm"]["median_ms"]), ("flushed", cmp_["flushed_ms"])):
+            tf = flop / (t * 1e-3) / 1e12
+            gbs = byts / (t * 1e-3) / 1e9
+            cmp_[f"{key}_algebra_tflops"] = round(tf, 1)
+            cmp_[f"{key}_frac_mfma"] = round(tf / PEAK_BF16_TFLOPS, 4)
+            cmp_[f"{key}_GBs"] = round(gbs, 1)
+            cmp_[f"{key}_frac_hbm"] = round(gbs / PEAK_HBM_GBS, 4)
+        cmp_["algebra_flop"] = flop
+        cmp_["algorithmic_bytes"] = byts
+        res[proj] = cmp_
+        del X, W, Y, g_q, g_1
+    log(f"[bench] 110M-LM FFN leg: {res}")
+    return res
 
 
 def training_leg(Q, torch, np, synth, dev, stream):
@@ -775,25 +983,32 @@ def experts_leg(Q, torch, np, synth, dev, stream):
     return res
 
 
-def cpu_leg(np, host, rows):
-    """The fp64 oracle (NumPy/OpenBLAS) on the first `rows` rows of both projections."""
+def cpu_leg(np, host, rows, threads=None):
+    """The fp64 oracle (NumPy/OpenBLAS) on the first `rows` rows of both projections, on all host
+    cores (threads=None) or on `threads` BLAS threads."""
+    import contextlib
     from oracle import qalg_oracle as O
     try:
         import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 0) for i in info if i.get("internal_api") in ("openblas", "mkl", "blis")] or [0])
+        limit = threadpoolctl.threadpool_limits(limits=threads, user_api="blas") if threads else contextlib.nullcontext()
     except Exception:  # pragma: no cover - informational only
-        threads = 0
+        threadpoolctl, limit = None, contextlib.nullcontext()
     rows = min(rows, M)
     tau = (np.arange(rows) % QQ).astype(np.int32)
     Xu = host["Xu"].f64[:rows]
     Xd = host["Xd"].f64[:rows]
     Wu = host["Wu"].f64
     Wd = host["Wd"].f64
-    t0 = time.perf_counter()
-    O.row_typed_forward(Xu, Wu, tau, QQ)
-    O.row_typed_forward(Xd, Wd, tau, QQ)
-    dt = time.perf_counter() - t0
+    with limit:
+        used = 0
+        if threadpoolctl is not None:
+            info = threadpoolctl.threadpool_info()
+            used = max([i.get("num_threads", 0) for i in info if i.get("user_api") == "blas"] or [0])
+        t0 = time.perf_counter()
+        O.row_typed_forward(Xu, Wu, tau, QQ)
+        O.row_typed_forward(Xd, Wd, tau, QQ)
+        dt = time.perf_counter() - t0
+    threads = used
     flop = 2 * 2.0 * rho(QQ) * rows * D * F
     res = {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads or len(os.sched_getaffinity(0)),
            "kind": "oracle", "seconds": round(dt, 2),

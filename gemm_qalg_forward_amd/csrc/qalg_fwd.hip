@@ -786,6 +786,7 @@ using Fwd256x128 = FwdCfg<256, 128>;
 // few rows per type: 128- and 64-row tiles (64 x 64 and 64 x 128 wave tiles)
 using Fwd128x256 = FwdCfg<128, 256>;
 using Fwd128x128 = FwdCfg<128, 128>;
+using Fwd128x192 = FwdCfg<128, 192>;
 using Fwd64x256 = FwdCfg<64, 256, false, 1, 4>;
 
 int cu_count() {
@@ -951,14 +952,15 @@ hipError_t launch_merge_gate_up_bf16(const void* Wg, const void* Wu, void* Wgu, 
 }
 
 // Tile height from a cost model calibrated with the sweep of calibrate.py on
-// 4096 <-> 12288 at M = 2048 .. 16384, q = 8 .. 64: (waves of tiles over the
+// 4096 <-> 12288 at M = 2048 .. 16384, q = 8 .. 64 (128-row tiles are 256,
+// 192 or 128 columns wide, whichever the group width takes first): (waves of tiles over the
 // CUs) x (tile area) / (relative per-area efficiency of the height: 1, 0.85
 // and 0.6 for 256, 128 and 64 rows).  Few rows per type favour low tiles (a
 // 256-row tile of a 64-row type is 3/4 padding); few tiles in all favour low
 // tiles too (more workgroups busy); many rows favour the most efficient tile.
 int fwd_tile_height(const ProblemDesc& p, int forced) {
   const int64_t r = p.N / p.q;
-  const bool ok64 = r % 256 == 0, ok128 = r % 128 == 0;
+  const bool ok64 = r % 256 == 0, ok128 = r % 128 == 0 || r % 192 == 0;
   if (forced) {
     if (forced == 256) return 256;
     if (forced == 128 && ok128) return 128;
@@ -974,7 +976,7 @@ int fwd_tile_height(const ProblemDesc& p, int forced) {
   int best = 256;
   double c_best = cost(256, r % 256 == 0 ? 256 : (r % 192 == 0 ? 192 : 128), 1.0);
   if (ok128) {
-    const double c = cost(128, ok64 ? 256 : 128, 0.85);
+    const double c = cost(128, ok64 ? 256 : (r % 192 == 0 ? 192 : 128), 0.85);
     if (c < c_best) best = 128, c_best = c;
   }
   if (ok64) {
@@ -988,7 +990,11 @@ hipError_t launch_fwd_persistent_bf16(const ProblemDesc& p, hipStream_t s, int f
   const int64_t r = p.N / p.q;
   const int bm = fwd_tile_height(p, forced_bm);
   if (bm == 64) return launch_fwd<Fwd64x256>(p, s);
-  if (bm == 128) return r % 256 == 0 ? launch_fwd<Fwd128x256>(p, s) : launch_fwd<Fwd128x128>(p, s);
+  if (bm == 128) {
+    if (r % 256 == 0) return launch_fwd<Fwd128x256>(p, s);
+    if (r % 192 == 0) return launch_fwd<Fwd128x192>(p, s);
+    return launch_fwd<Fwd128x128>(p, s);
+  }
   if (bm != 256) return hipErrorInvalidValue;
   if (r % 256 == 0) return launch_fwd<Fwd256x256>(p, s);
   if (r % 192 == 0) return launch_fwd<Fwd256x192>(p, s);

@@ -108,8 +108,8 @@ enum {
     /* Tile calibration (qalg_forward, bf16, one bank): run the persistent
      * forward with 64-, 128- or 256-row output tiles instead of the height
      * chosen from the rows per type (at most one; QALG_ERR_ARG if the shape
-     * cannot use it: 64 needs N / q a multiple of 256, 128 a multiple of 128,
-     * and every persistent shape K / q a multiple of 64). */
+     * cannot use it: 64 needs N / q a multiple of 256, 128 a multiple of 128
+     * or of 192, and every persistent shape K / q a multiple of 64). */
     QALG_FLAG_TILE_M64 = 16,
     QALG_FLAG_TILE_M128 = 32,
     QALG_FLAG_TILE_M256 = 64

@@ -22,6 +22,8 @@ TILE_SHAPES = [
     (600, 256, 1024, 4, "cyclic", 3, 0, 0),      # 150 rows per type, type offset
     (700, 512, 1024, 8, "cyclic", 0, 0, 0),      # N / q = 128: 128- and 256-row tiles only
     (512, 512, 2048, 8, "cyclic", 1, 0, 3),      # the recursive law at 64 rows per type
+    (1500, 768, 768, 4, "cyclic", 1, 0, 0),      # N / q = 192: 128 x 192 and 256 x 192 tiles
+    (900, 512, 2304, 4, "random", 0, 5, 0),      # N / q = 576 = 3 x 192, listed types, out-of-range rows
 ]
 FLAGS = [("default", 0), ("m64", Q.QALG_FLAG_TILE_M64), ("m128", Q.QALG_FLAG_TILE_M128),
          ("m256", Q.QALG_FLAG_TILE_M256)]
