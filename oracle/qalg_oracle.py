@@ -39,6 +39,11 @@ What is computed, plainly:
   F(i, j) ({i} or {i, j}, eq 38; eq 42 for the recursive law), scaled by
   1 / sqrt(|F| m) (eq 41), then the causal softmax and a dense PV (eq 43-44);
   `attention_score_macs` counts its score and value MACs (eq 45).
+* `algebraic_attention_decode` is appendix G's cached decoding (Algorithm 3,
+  the loop over cached positions and the softmax / value sum): one new query
+  row per sequence against that sequence's full-key cache, each key's type
+  recovered from its absolute position (G.2); `attention_decode_macs` counts
+  its score and value MACs (eq 57-58 for Q_q, eq 61 for the recursive law).
 * `gated_forward` is the gate/up half of a gated (SwiGLU) FFN: both D x F
   projections are row-typed exactly like any other projection, while gates
   and pointwise activations are left as they are (section 4), combined as silu(X *_{Q_q} W_gate) * (X *_{Q_q} W_up), silu
@@ -93,6 +98,8 @@ __all__ = [
     "score_support",
     "algebraic_attention",
     "attention_score_macs",
+    "algebraic_attention_decode",
+    "attention_decode_macs",
 ]
 
 
@@ -540,3 +547,70 @@ def attention_score_macs(tau: np.ndarray, q: int, d: int, L: int = 0,
                 pairs += 1
                 score += len(score_support(int(tau[p]), int(tau[u]), q, L)) * m
     return score, pairs * d
+
+
+def algebraic_attention_decode(Qn: np.ndarray, Kc: np.ndarray, Vc: np.ndarray, q_pos: np.ndarray,
+                               key_pos: np.ndarray, q: int, L: int = 0, kind: str = "cyclic",
+                               period: int = 0) -> np.ndarray:
+    """Cached decoding with the algebraic score (appendix G, Algorithm 3: the loop over the
+    allowed cached positions, then the softmax and the value sum; G.2 for the cache).
+
+    Qn: [B, Hq, d], the new row's queries of each of B sequences; Kc, Vc: [B, Hkv, N, d], each
+    sequence's cache of N slots (full keys and values, Hkv dividing Hq: query head h reads
+    key/value head h // (Hq / Hkv)); q_pos: [B] absolute position p of the new row; key_pos:
+    [B, N] absolute position u of each cached slot, negative for an empty slot.  The query's type
+    is i = tau(p), a cached key's j = tau(u), tau the position schedule (`type_schedule`).  For
+    every slot with 0 <= u <= p:
+        r_pu = sum over a in F(i, j) of <Q_p^(a), K_u^(a)>        (eq 39)
+        s_pu = r_pu / sqrt(|F(i, j)| m),  m = d / q                 (eq 41)
+    P_p = softmax over those slots, O_p = sum_u P_pu V_u (dense).  A row with no allowed slot
+    is written as zeros (the softmax of an empty set is not defined).
+    """
+    Qn = np.asarray(Qn, dtype=np.float64)
+    Kc = np.asarray(Kc, dtype=np.float64)
+    Vc = np.asarray(Vc, dtype=np.float64)
+    B, Hq, d = Qn.shape
+    Hkv, N = Kc.shape[1], Kc.shape[2]
+    if Kc.shape != (B, Hkv, N, d) or Vc.shape != Kc.shape or Hq % Hkv or d % q:
+        raise ValueError("shapes")
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    key_pos = np.asarray(key_pos, dtype=np.int64)
+    m = d // q
+    O = np.zeros((B, Hq, d))
+    for b in range(B):
+        p = int(q_pos[b])
+        i = int(type_schedule(np.array([p]), q, kind, period)[0])
+        slots = np.where((key_pos[b] >= 0) & (key_pos[b] <= p))[0]
+        if slots.size == 0:
+            continue
+        js = type_schedule(key_pos[b][slots], q, kind, period)
+        # sel[a, k]: group a is compared for the k-th allowed slot
+        sel = np.zeros((q, slots.size), dtype=bool)
+        for k, j in enumerate(js):
+            sel[score_support(i, int(j), q, L), k] = True
+        k_pair = sel.sum(axis=0) * m
+        for h in range(Hq):
+            kv = h // (Hq // Hkv)
+            K = Kc[b, kv][slots]
+            r = np.zeros(slots.size)
+            for a in range(q):
+                r += np.where(sel[a], K[:, a * m:(a + 1) * m] @ Qn[b, h, a * m:(a + 1) * m], 0.0)
+            s = r / np.sqrt(k_pair)
+            w = np.exp(s - s.max())
+            O[b, h] = (w / w.sum()) @ Vc[b, kv][slots]
+    return O
+
+
+def attention_decode_macs(p: int, key_pos: np.ndarray, q: int, d: int, L: int = 0, kind: str = "cyclic",
+                          period: int = 0) -> tuple[int, int]:
+    """(score MACs, value MACs) of one query head decoding position p against one cache
+    (appendix G.2): each allowed key of type j costs |F(tau(p), j)| m score MACs, so for Q_q with
+    n_j allowed keys of type j the score cost is m (2 N_p - n_i) (eq 57), and for the recursive
+    law m sum_j 2^h(i, j) n_j (eq 61); the dense value sum costs N_p d."""
+    key_pos = np.asarray(key_pos, dtype=np.int64)
+    allowed = key_pos[(key_pos >= 0) & (key_pos <= p)]
+    i = int(type_schedule(np.array([p]), q, kind, period)[0])
+    js = type_schedule(allowed, q, kind, period)
+    m = d // q
+    score = sum(len(score_support(i, int(j), q, L)) * m for j in js)
+    return score, allowed.size * d

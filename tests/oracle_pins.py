@@ -906,6 +906,123 @@ def pin_attention_laws_and_counts(O):
         assert sm == (2 * Mp - Meq) * (d // q) and vm == Mp * d
 
 
+def pin_attention_type_offset(O, seed=55):
+    """A sequence chunk starting at absolute position p0 has types (p0 + s) mod q: its scores are
+    Q *_{Q_q} K^T under those types (the typed-product closed form of the block S_ij, with the
+    key columns sorted by type), and for p0 not a multiple of q they differ from p0 = 0 (the
+    offset changes which F(i, j) each pair uses)."""
+    g = _rng(seed)
+    for q, S, d, p0 in ((4, 12, 8, 5), (3, 9, 6, 7), (2, 10, 4, 3)):
+        Q = g.standard_normal((1, S, d))
+        K = g.standard_normal((1, S, d))
+        V = g.standard_normal((1, S, d))
+        pos = p0 + np.arange(S)
+        tau = pos % q
+        perm = np.argsort(tau, kind="stable")
+        Z = O.row_typed_forward(Q[0], K[0][perm].T, tau, q)
+        r = np.empty_like(Z)
+        r[:, perm] = Z
+        m = d // q
+        k = np.where(tau[:, None] == tau[None, :], m, 2 * m)
+        s_ = np.where(pos[None, :] <= pos[:, None], r / np.sqrt(k), -np.inf)
+        want = _softmax_rows(s_) @ V[0]
+        got = O.algebraic_attention(Q, K, V, tau, q, positions=pos)
+        np.testing.assert_allclose(got[0], want, rtol=1e-12, atol=1e-12)
+        assert not np.allclose(got, O.algebraic_attention(Q, K, V, np.arange(S) % q, q))
+
+
+def pin_decode_is_prefill_row(O, seed=56):
+    """Algorithm 3 gives the row Algorithm 2 gives (appendix G: each pair score depends only on the
+    query, one key and their types, so a cached key serves every later query): decoding row t of a
+    chunk at positions p0 .. p0 + S - 1 against the whole cache (later keys masked by position)
+    equals row t of the parallel computation; the cache's slot order and empty slots do not
+    matter.  Q_q and the recursive law, cyclic and interval schedules, GQA."""
+    g = _rng(seed)
+    for q, L, S, d, p0, kind, period in ((4, 0, 11, 8, 5, "cyclic", 0), (3, 0, 9, 6, 4, "cyclic", 0),
+                                         (4, 2, 10, 8, 2, "cyclic", 0), (4, 0, 13, 8, 1, "interval", 8)):
+        Hq, Hkv = 4, 2
+        Q = g.standard_normal((Hq, S, d))
+        K = g.standard_normal((Hkv, S, d))
+        V = g.standard_normal((Hkv, S, d))
+        pos = p0 + np.arange(S)
+        tau = O.type_schedule(pos, q, kind, period)
+        want = O.algebraic_attention(Q, K, V, tau, q, L, positions=pos)
+        # the cache: the S keys in a shuffled slot order, with two empty slots
+        order = g.permutation(S)
+        slot_pos = np.concatenate([pos[order], [-1, -1]])
+        Kc = np.concatenate([K[:, order], g.standard_normal((Hkv, 2, d))], axis=1)
+        Vc = np.concatenate([V[:, order], g.standard_normal((Hkv, 2, d))], axis=1)
+        B = S
+        got = O.algebraic_attention_decode(Q.transpose(1, 0, 2), np.repeat(Kc[None], B, 0), np.repeat(Vc[None], B, 0),
+                                           pos, np.repeat(slot_pos[None], B, 0), q, L, kind, period)
+        np.testing.assert_allclose(got, want.transpose(1, 0, 2), rtol=1e-12, atol=1e-12)
+
+
+def pin_decode_q1_is_sdpa(O, seed=57):
+    """q = 1: one query row against its whole cache is ordinary attention with 1/sqrt(d)
+    (fp64 torch scaled_dot_product_attention, no mask: every cached key is at or before p)."""
+    import torch
+    g = _rng(seed)
+    B, Hq, Hkv, N, d = 3, 4, 2, 9, 8
+    Qn = g.standard_normal((B, Hq, d))
+    Kc = g.standard_normal((B, Hkv, N, d))
+    Vc = g.standard_normal((B, Hkv, N, d))
+    kp = np.tile(np.arange(N), (B, 1))
+    got = O.algebraic_attention_decode(Qn, Kc, Vc, np.full(B, N - 1), kp, 1)
+    Kx = torch.tensor(np.repeat(Kc, 2, axis=1))
+    Vx = torch.tensor(np.repeat(Vc, 2, axis=1))
+    want = torch.nn.functional.scaled_dot_product_attention(torch.tensor(Qn)[:, :, None], Kx, Vx)[:, :, 0].numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def pin_decode_cached_key_groups(O):
+    """G.2's example, q = 4: a type-3 query reads group 3 of a cached type-3 key and groups {3, 1}
+    of a cached type-1 key; a later type-2 query reads groups {2, 1} of that same type-1 key.  With
+    Q all ones and key group a holding the constant c_a, r = m sum over F of c_a; V = I reads the
+    softmax weights back, exp(r / sqrt(|F| m)) normalised.  Empty slots and keys after p get 0."""
+    q, d = 4, 8
+    m = d // q
+    c = np.array([0.3, -0.2, 0.5, 0.1])
+    keyvec = lambda: np.repeat(c, m)  # noqa: E731
+    N = 5
+    key_pos = np.array([[1, 3, -1, 6, 9]])      # types 1, 3, (empty), 2, 1 (position 9 > p for both queries)
+    Kc = np.tile(keyvec(), (1, 1, N, 1))
+    Vc = np.eye(N)[None, None, :, :N].repeat(1, 0)
+    Vc = np.pad(Vc, ((0, 0), (0, 0), (0, 0), (0, d - N)))
+    ones = np.ones((1, 1, d))
+    # type-3 query at p = 3: keys at 1 (groups {3, 1}) and 3 (group {3})
+    P3 = O.algebraic_attention_decode(ones, Kc, Vc, np.array([3]), key_pos, q)[0, 0, :N]
+    w = np.array([np.exp(m * (c[3] + c[1]) / np.sqrt(2 * m)), np.exp(m * c[3] / np.sqrt(m)), 0, 0, 0])
+    np.testing.assert_allclose(P3, w / w.sum(), rtol=1e-13, atol=1e-15)
+    # type-2 query at p = 6: keys at 1 (groups {2, 1}), 3 (groups {2, 3}) and 6 (group {2})
+    P2 = O.algebraic_attention_decode(ones, Kc, Vc, np.array([6]), key_pos, q)[0, 0, :N]
+    w = np.array([np.exp(m * (c[2] + c[1]) / np.sqrt(2 * m)), np.exp(m * (c[2] + c[3]) / np.sqrt(2 * m)), 0,
+                  np.exp(m * c[2] / np.sqrt(m)), 0])
+    np.testing.assert_allclose(P2, w / w.sum(), rtol=1e-13, atol=1e-15)
+    # no allowed key: a zero row
+    assert not O.algebraic_attention_decode(ones, Kc, Vc, np.array([0]), key_pos, q).any()
+
+
+def pin_decode_macs(O):
+    """eq 57: a type-i query over N_p allowed keys, n_i of its own type, costs m (2 N_p - n_i) score
+    MACs; eq 58: a balanced cache gives the fraction rho_q = (2q - 1) / q^2 (7/16 at q = 4); eq 61:
+    the recursive law costs m sum_j 2^h(i, j) n_j, 9/16 of dense for a balanced Q_2^(x)2 cache;
+    the value sum is N_p d in every case."""
+    for q, d, Np, p in ((4, 8, 64, 70), (3, 6, 30, 40), (8, 16, 64, 100)):
+        key_pos = np.concatenate([np.arange(Np), [p + 1, -1]])   # one future key, one empty slot
+        sm, vm = O.attention_decode_macs(p, key_pos, q, d)
+        i = p % q
+        n_i = sum(1 for u in range(Np) if u % q == i)
+        assert sm == (d // q) * (2 * Np - n_i) and vm == Np * d
+        if Np % q == 0:
+            assert sm * q * q == (2 * q - 1) * Np * d
+    sm, vm = O.attention_decode_macs(63, np.arange(64), 4, 8, L=2)
+    assert sm * 16 == 9 * 64 * 8 and vm == 64 * 8
+    i = 63 % 4
+    want = sum(2 ** bin(i ^ (u % 4)).count("1") for u in range(64)) * 2
+    assert sm == want
+
+
 ALL_PINS = [
     pin_q2_table, pin_q2_scalar_example, pin_eq3_rectangular_blocks, pin_eq13_14,
     pin_product_counts, pin_graph_counts, pin_appendix_a, pin_associativity,
@@ -916,5 +1033,6 @@ ALL_PINS = [
     pin_silu_grad, pin_gated_ffn_autograd, pin_tensor_counts, pin_tensor_support,
     pin_tensor_associativity, pin_tensor_masked_dense, pin_tensor_cost, pin_tensor_vjp_autograd,
     pin_attention_q1_is_sdpa, pin_attention_scores_are_typed_product, pin_attention_scale_and_mask,
-    pin_attention_causality, pin_attention_gqa, pin_attention_laws_and_counts,
+    pin_attention_causality, pin_attention_gqa, pin_attention_laws_and_counts, pin_attention_type_offset,
+    pin_decode_is_prefill_row, pin_decode_q1_is_sdpa, pin_decode_cached_key_groups, pin_decode_macs,
 ]

@@ -22,6 +22,8 @@ _real_tensor = O.tensor_power_table
 _real_attn = O.algebraic_attention
 _real_support = O.score_support
 _real_swiglu_bwd = O.swiglu_backward
+_real_decode = O.algebraic_attention_decode
+_real_decode_macs = O.attention_decode_macs
 
 
 def table_with_edge_edge(q, edges=None):
@@ -230,6 +232,57 @@ def attn_anticausal(Q, K, V, tau, q, L=0, positions=None):
     return _real_attn(Q, K, V, tau, q, L, -pos)
 
 
+def _decode_variant(Qn, Kc, Vc, q_pos, key_pos, q, L, kind, period, key_types, allowed):
+    """Algorithm 3 with the key types and the allowed slots supplied by a mutant."""
+    Qn, Kc, Vc = (np.asarray(a, float) for a in (Qn, Kc, Vc))
+    B, Hq, d = Qn.shape
+    Hkv = Kc.shape[1]
+    m = d // q
+    out = np.zeros(Qn.shape)
+    for b in range(B):
+        i = int(O.type_schedule(np.array([q_pos[b]]), q, kind, period)[0])
+        slots = np.where(allowed(b))[0]
+        if slots.size == 0:
+            continue
+        js = key_types(b)[slots]
+        for h in range(Hq):
+            kv = h // (Hq // Hkv)
+            s_ = np.array([sum(Kc[b, kv, u, a * m:(a + 1) * m] @ Qn[b, h, a * m:(a + 1) * m]
+                               for a in O.score_support(i, int(j), q, L)) / np.sqrt(len(O.score_support(i, int(j), q, L)) * m)
+                           for u, j in zip(slots, js)])
+            w = np.exp(s_ - s_.max())
+            out[b, h] = (w / w.sum()) @ Vc[b, kv][slots]
+    return out
+
+
+def decode_type_from_slot(Qn, Kc, Vc, q_pos, key_pos, q, L=0, kind="cyclic", period=0):
+    """Mistake: a cached key's type is taken from its slot index, not from its position."""
+    kp = np.asarray(key_pos)
+    return _decode_variant(Qn, Kc, Vc, q_pos, key_pos, q, L, kind, period,
+                           key_types=lambda b: O.type_schedule(np.arange(kp.shape[1]), q, kind, period),
+                           allowed=lambda b: (kp[b] >= 0) & (kp[b] <= q_pos[b]))
+
+
+def decode_admits_future(Qn, Kc, Vc, q_pos, key_pos, q, L=0, kind="cyclic", period=0):
+    """Mistake: every non-empty slot is attended, including keys after the query's position."""
+    kp = np.asarray(key_pos)
+    return _decode_variant(Qn, Kc, Vc, q_pos, key_pos, q, L, kind, period,
+                           key_types=lambda b: O.type_schedule(np.maximum(kp[b], 0), q, kind, period),
+                           allowed=lambda b: kp[b] >= 0)
+
+
+def decode_dense_scale(Qn, Kc, Vc, q_pos, key_pos, q, L=0, kind="cyclic", period=0):
+    """Mistake: scores scaled by 1/sqrt(d) as in dense attention instead of 1/sqrt(|F| m)."""
+    d = np.asarray(Qn).shape[2]
+    return _real_decode(np.asarray(Qn, float) * np.sqrt((d // q) / d), Kc, Vc, q_pos, key_pos, q, L, kind, period)
+
+
+def decode_macs_full_keys(p, key_pos, q, d, L=0, kind="cyclic", period=0):
+    """Mistake: every cached key costs d score MACs (the dense count)."""
+    sm, vm = _real_decode_macs(p, key_pos, q, d, L, kind, period)
+    return vm, vm
+
+
 MUTANTS = [
     ("structure_table", table_with_edge_edge),
     ("structure_table", table_without_right_vertex),
@@ -255,6 +308,10 @@ MUTANTS = [
     ("score_support", support_own_group_only),
     ("algebraic_attention", attn_kv_head_modulo),
     ("algebraic_attention", attn_anticausal),
+    ("algebraic_attention_decode", decode_type_from_slot),
+    ("algebraic_attention_decode", decode_admits_future),
+    ("algebraic_attention_decode", decode_dense_scale),
+    ("attention_decode_macs", decode_macs_full_keys),
 ]
 
 
