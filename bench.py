@@ -31,7 +31,8 @@ Reported (one JSON line):
                    SwiGLU FFN (forward and training step), the 64-expert shapes at
                    M = 1..1024 against q = 1, the pilot FFN under
                    Q_2^(x)2 / Q_4 / q = 1, few rows per type (q = 32), algebraic
-                   attention, the graph law Q_G and unequal group widths (forward,
+                   attention (prefill, and cached decoding against a 4096-slot cache),
+                   the graph law Q_G and unequal group widths (forward,
                    dX, dW each)
 """
 from __future__ import annotations
@@ -356,6 +357,7 @@ def main() -> int:
         "pilot_ffn": lambda: pilot_leg(Q, torch, np, synth, dev, stream),
         "few_rows": lambda: few_rows_leg(Q, torch, np, synth, dev, stream),
         "attention": lambda: attention_leg(Q, torch, np, synth, dev, stream),
+        "attention_decode": lambda: attention_decode_leg(Q, torch, np, synth, dev, proto),
         "graph_law": lambda: graph_leg(Q, torch, np, synth, dev, stream),
         "unequal_widths": lambda: widths_leg(Q, torch, np, synth, dev, stream),
     }
@@ -879,6 +881,53 @@ def attention_leg(Q, torch, np, synth, dev, stream):
         out[name]["ceiling"] = round(2 / (1 + rho), 3)   # eq 46
     log(f"[bench] attention leg: {out}")
     return out
+
+
+def attention_decode_leg(Q, torch, np, synth, dev, proto):
+    """Cached decoding with the algebraic score (appendix G, Algorithm 3): 32 sequences, one new
+    row each, 32 query heads over 8 key/value heads (GQA), d = 128, caches of 4096 slots where
+    sequence b holds positions 0 .. 4095 - b (the rest empty), q = 4 and its q = 1 control (the
+    same kernel, ordinary attention).  HBM-bound: the algorithmic bytes are each allowed slot's
+    value row, the F(i, j) groups of its key row (eq 57: m or 2m of the d features), the slot
+    positions, Q and O."""
+    c, B, Hq, Hkv, N, d, q = 11, 32, 32, 8, 4096, 128, 4
+    to = lambda op: torch.from_numpy(op.bits.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    Qn = to(synth.normal_operand(1000 * c + 1, (B, Hq, d), 1.0, "bf16"))
+    Kc = to(synth.normal_operand(1000 * c + 2, (B, Hkv, N, d), 1.0, "bf16"))
+    Vc = to(synth.normal_operand(1000 * c + 3, (B, Hkv, N, d), 1.0, "bf16"))
+    lens = N - np.arange(B)
+    key_pos = np.full((B, N), -1, np.int64)
+    for b in range(B):
+        key_pos[b, :lens[b]] = np.arange(lens[b])
+    q_pos = (lens - 1).astype(np.int64)
+    qp, kp = torch.from_numpy(q_pos).to(dev), torch.from_numpy(key_pos).to(dev)
+    O = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(Q.qalg_attention_decode_workspace_bytes(B, Hq, N, d), dtype=torch.uint8, device=dev)
+    res = {"workload": "attn_decode_B32_Hq32_Hkv8_N4096_d128_q4_bf16", "cache": "sequence b: positions 0..4095-b"}
+    per_q = {}
+    for qq in (q, 1):
+        m = d // qq
+        kbytes = 0
+        for b in range(B):
+            i = int(q_pos[b]) % qq
+            js = np.arange(lens[b]) % qq
+            kbytes += int(np.where(js == i, m, 2 * m).sum()) * 2 * Hkv
+        vbytes = int(lens.sum()) * d * 2 * Hkv
+        per_q[qq] = kbytes + vbytes + B * N * 8 + 2 * B * Hq * d * 2
+    g_q = proto.capture(lambda st: Q.qalg_attention_decode(Qn, Kc, Vc, qp, kp, q, O=O, ws=ws, stream=st))
+    g_1 = proto.capture(lambda st: Q.qalg_attention_decode(Qn, Kc, Vc, qp, kp, 1, O=O, ws=ws, stream=st))
+    cmp_ = proto.compare(g_q, g_1)
+    for key, t, t1 in (("warm", cmp_["warm"]["median_ms"], cmp_["warm_q1"]["median_ms"]),
+                       ("flushed", cmp_["flushed_ms"], cmp_["flushed_q1_ms"])):
+        cmp_[f"{key}_GBs"] = round(per_q[q] / (t * 1e-3) / 1e9, 1)
+        cmp_[f"{key}_frac_hbm"] = round(per_q[q] / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        cmp_[f"{key}_q1_GBs"] = round(per_q[1] / (t1 * 1e-3) / 1e9, 1)
+    cmp_["algorithmic_bytes"] = per_q[q]
+    cmp_["algorithmic_bytes_q1"] = per_q[1]
+    cmp_["byte_ratio_q1_over_q"] = round(per_q[1] / per_q[q], 3)   # the ceiling the byte cut allows
+    res.update(cmp_)
+    log(f"[bench] attention decode leg: {res}")
+    return res
 
 
 def decode_leg(Q, torch, np, synth, dev, stream):

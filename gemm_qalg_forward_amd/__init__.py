@@ -10,7 +10,8 @@ Functions carry the C names:
     qalg_backward_dx_graph, qalg_backward_dw_graph, qalg_forward_widths, qalg_backward_dx_widths,
     qalg_backward_dw_widths,
     qalg_gated_forward, qalg_gated_forward_keep, qalg_merge_gate_up, qalg_split_gate_up, qalg_swiglu_forward, qalg_swiglu_backward,
-    qalg_attention_forward, qalg_forward_noalloc,
+    qalg_attention_forward, qalg_attention_forward_at, qalg_attention_decode,
+    qalg_attention_decode_workspace_bytes, qalg_forward_noalloc,
     qalg_type_schedule, qalg_build_index, qalg_build_index_batched,
     qalg_read_status, qalg_workspace_bytes, qalg_index_layout,
     qalg_status_string, qalg_version.
@@ -32,7 +33,8 @@ __all__ = [
     "qalg_backward_dw_widths",
     "qalg_gated_forward", "qalg_gated_forward_keep", "qalg_merge_gate_up", "qalg_split_gate_up", "qalg_swiglu_forward",
     "qalg_swiglu_backward", "qalg_attention_forward", "qalg_read_status", "workspace",
-    "qalg_forward_noalloc", "QALG_NOALLOC_SCRATCH_BYTES",
+    "qalg_forward_noalloc", "QALG_NOALLOC_SCRATCH_BYTES", "qalg_attention_forward_at", "qalg_attention_decode",
+    "qalg_attention_decode_workspace_bytes",
 ]
 
 QALG_F32 = 0
@@ -95,6 +97,11 @@ _SIGS = {
                                               _c_u32, _vp]),
     "qalg_read_status": (ctypes.c_int, [_vp, _c_i32, _c_i32, _c_i64, _vp, ctypes.POINTER(_c_i64)]),
     "qalg_forward_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i64, _c_i64, _c_i64, _vp, _c_i32, _c_u32, _vp]),
+    "qalg_attention_forward_at": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_i64, _vp,
+                                                 _c_i32, _c_u32, _vp]),
+    "qalg_attention_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i64, _c_i32]),
+    "qalg_attention_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32,
+                                             _c_i32, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
 }
 
 
@@ -510,6 +517,58 @@ def qalg_attention_forward(Qh, Kh, Vh, q: int, O=None, flags: int = 0, stream=No
     _check("qalg_attention_forward", lib().qalg_attention_forward(
         _dev_ptr(Qh, "Q"), _dev_ptr(Kh, "K"), _dev_ptr(Vh, "V"), Hq, Hkv, S, d, q, _dev_ptr(O, "O"),
         _dtype_code(Qh), flags, _stream(stream)))
+    return O
+
+
+def qalg_attention_forward_at(Qh, Kh, Vh, q: int, first_position: int, O=None, flags: int = 0, stream=None):
+    """qalg_attention_forward for a chunk whose row 0 sits at absolute position first_position
+    (row s: position first_position + s, type (first_position + s) mod q)."""
+    Hq, S, d = Qh.shape
+    Hkv = Kh.shape[0]
+    if tuple(Kh.shape) != (Hkv, S, d) or tuple(Vh.shape) != (Hkv, S, d):
+        raise ValueError("K and V must be [Hkv, S, d] with the S and d of Q")
+    if Kh.dtype != Qh.dtype or Vh.dtype != Qh.dtype:
+        raise TypeError("Q, K and V must share a dtype")
+    _same_device(Kh, Qh, "K")
+    _same_device(Vh, Qh, "V")
+    O = _new_or_check(O, (Hq, S, d), Qh, "O")
+    _check("qalg_attention_forward_at", lib().qalg_attention_forward_at(
+        _dev_ptr(Qh, "Q"), _dev_ptr(Kh, "K"), _dev_ptr(Vh, "V"), Hq, Hkv, S, d, q, int(first_position),
+        _dev_ptr(O, "O"), _dtype_code(Qh), flags, _stream(stream)))
+    return O
+
+
+def qalg_attention_decode_workspace_bytes(B: int, Hq: int, N: int, d: int) -> int:
+    return lib().qalg_attention_decode_workspace_bytes(B, Hq, N, d)
+
+
+def qalg_attention_decode(Qn, Kc, Vc, q_pos, key_pos, q: int, kind: int = QALG_SCHEDULE_CYCLIC, period: int = 0,
+                          O=None, ws=None, flags: int = 0, stream=None):
+    """Cached decoding (Algorithm 3): Qn [B, Hq, d] new rows at positions q_pos (int64 [B]) against
+    caches Kc, Vc [B, Hkv, N, d] with slot positions key_pos (int64 [B, N], negative: empty) -> O [B, Hq, d]."""
+    torch = _torch()
+    B, Hq, d = Qn.shape
+    B2, Hkv, N, d2 = Kc.shape
+    if B2 != B or d2 != d or tuple(Vc.shape) != tuple(Kc.shape):
+        raise ValueError("Kc and Vc must be [B, Hkv, N, d] with the B and d of Qn")
+    if Kc.dtype != Qn.dtype or Vc.dtype != Qn.dtype:
+        raise TypeError("Qn, Kc and Vc must share a dtype")
+    if q_pos.dtype != torch.int64 or tuple(q_pos.shape) != (B,):
+        raise ValueError(f"q_pos must be int64 [{B}]")
+    if key_pos.dtype != torch.int64 or tuple(key_pos.shape) != (B, N):
+        raise ValueError(f"key_pos must be int64 [{B}, {N}]")
+    for t, n in ((Kc, "Kc"), (Vc, "Vc"), (q_pos, "q_pos"), (key_pos, "key_pos")):
+        _same_device(t, Qn, n)
+    O = _new_or_check(O, (B, Hq, d), Qn, "O")
+    need = qalg_attention_decode_workspace_bytes(B, Hq, N, d)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=Qn.device)
+    else:
+        _same_device(ws, Qn, "ws")
+    _check("qalg_attention_decode", lib().qalg_attention_decode(
+        _dev_ptr(Qn, "Qn"), _dev_ptr(Kc, "Kc"), _dev_ptr(Vc, "Vc"), _dev_ptr(q_pos, "q_pos"), _dev_ptr(key_pos, "key_pos"),
+        B, Hq, Hkv, N, d, q, kind, period, _dev_ptr(O, "O"), _dtype_code(Qn), _dev_ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), flags, _stream(stream)))
     return O
 
 

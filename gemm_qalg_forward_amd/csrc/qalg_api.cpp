@@ -570,6 +570,13 @@ qalg_status qalg_swiglu_backward(const void* GU, const void* dH, int32_t q, int6
 qalg_status qalg_attention_forward(const void* Q, const void* K, const void* V, int32_t Hq, int32_t Hkv,
                                    int64_t S, int32_t d, int32_t q, void* O, int32_t dtype, uint32_t flags,
                                    void* stream) {
+  return qalg_attention_forward_at(Q, K, V, Hq, Hkv, S, d, q, 0, O, dtype, flags, stream);
+}
+
+qalg_status qalg_attention_forward_at(const void* Q, const void* K, const void* V, int32_t Hq, int32_t Hkv,
+                                      int64_t S, int32_t d, int32_t q, int64_t first_position, void* O,
+                                      int32_t dtype, uint32_t flags, void* stream) {
+  if (first_position < 0) return QALG_ERR_DIM;
   if (dtype != QALG_BF16) return QALG_ERR_DTYPE;
   if (flags & ~uint32_t(QALG_FLAG_LAW_TENSOR)) return QALG_ERR_ARG;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv || S < 0 || (d != 64 && d != 128)) return QALG_ERR_DIM;
@@ -581,7 +588,40 @@ qalg_status qalg_attention_forward(const void* Q, const void* K, const void* V, 
   if (S == 0) return QALG_OK;
   if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr) return QALG_ERR_NULL;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return QALG_ERR_ALIGN;
-  return hip_status(qalg::launch_attn_fwd_bf16(Q, K, V, O, Hq, Hkv, S, d, q, L, static_cast<hipStream_t>(stream)));
+  return hip_status(
+      qalg::launch_attn_fwd_bf16(Q, K, V, O, Hq, Hkv, S, d, q, L, first_position, static_cast<hipStream_t>(stream)));
+}
+
+size_t qalg_attention_decode_workspace_bytes(int32_t B, int32_t Hq, int64_t N, int32_t d) {
+  if (B < 0 || Hq < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  const size_t n = qalg::attn_decode_part_bytes(B, Hq, N, d);
+  return (n + 255) / 256 * 256;
+}
+
+qalg_status qalg_attention_decode(const void* Qn, const void* Kc, const void* Vc, const int64_t* q_pos,
+                                  const int64_t* key_pos, int32_t B, int32_t Hq, int32_t Hkv, int64_t N, int32_t d,
+                                  int32_t q, int32_t kind, int64_t period, void* O, int32_t dtype, void* ws,
+                                  size_t ws_bytes, uint32_t flags, void* stream) {
+  if (dtype != QALG_BF16) return QALG_ERR_DTYPE;
+  if (flags & ~uint32_t(QALG_FLAG_LAW_TENSOR)) return QALG_ERR_ARG;
+  if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || Hq / Hkv > 8 || N < 1 || (d != 64 && d != 128)) return QALG_ERR_DIM;
+  if (B > 65535 || Hkv > 65535 || int64_t(B) * Hq > INT32_MAX || N > qalg::attn_decode_max_slots()) return QALG_ERR_DIM;
+  if (q < 1 || q > QALG_MAX_Q || d % q) return QALG_ERR_Q;
+  const int L = (flags & QALG_FLAG_LAW_TENSOR) ? tensor_levels(q) : 0;
+  if (L < 0) return QALG_ERR_Q;
+  if (!qalg::attn_decode_supported(d, q)) return QALG_ERR_ALIGN;
+  if (kind != QALG_SCHEDULE_CYCLIC && kind != QALG_SCHEDULE_INTERVAL) return QALG_ERR_ARG;
+  if (kind == QALG_SCHEDULE_INTERVAL && (period <= 0 || period % q)) return QALG_ERR_ARG;
+  if (B == 0) return QALG_OK;
+  if (Qn == nullptr || Kc == nullptr || Vc == nullptr || q_pos == nullptr || key_pos == nullptr || O == nullptr)
+    return QALG_ERR_NULL;
+  if (!aligned16(Qn) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(O) ||
+      (reinterpret_cast<uintptr_t>(q_pos) & 7u) || (reinterpret_cast<uintptr_t>(key_pos) & 7u))
+    return QALG_ERR_ALIGN;
+  if (ws == nullptr) return QALG_ERR_NULL;
+  if (!aligned16(ws) || ws_bytes < qalg_attention_decode_workspace_bytes(B, Hq, N, d)) return QALG_ERR_WORKSPACE;
+  return hip_status(qalg::launch_attn_decode_bf16(Qn, Kc, Vc, q_pos, key_pos, O, B, Hq, Hkv, N, d, q, L, kind, period,
+                                                  ws, static_cast<hipStream_t>(stream)));
 }
 
 qalg_status qalg_read_status(const void* ws, int32_t E, int32_t q, int64_t M, void* stream,

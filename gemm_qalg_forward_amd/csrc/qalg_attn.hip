@@ -1,16 +1,17 @@
 // Causal attention with the algebraic score (arXiv 2609.32814, appendix G),
 // forward, bf16 in and out, fp32 softmax statistics and accumulation.
 //
-// A query at position p (type i = p mod q) and a key at u (type j) compare only
+// A query at position p (type i = p mod q; rows s of a chunk whose first row
+// sits at absolute position p0 have p = p0 + s) and a key at u (type j) compare only
 // the feature groups F(i, j) of the head: {i} if i == j, else {i, j} (eq 38;
 // eq 42 for the recursive law Q_2^(x)L: every group whose bits each come from i
 // or j).  The score r_pu (eq 39) is scaled by 1/sqrt(|F| m), m = d / q (eq 41),
 // masked to u <= p (eq 43), softmaxed, and the values are aggregated densely
 // (eq 44).  Algorithm 2, steps 3-7, for one sequence per head.
 //
-// Work.  A workgroup owns 128 queries of one type i of one head (positions
-// i + q t for 128 consecutive t), 32 per wave, and walks the keys type by type:
-// keys of type j are the positions j + q t', so a block of 64 of them shares
+// Work.  A workgroup owns 128 queries of one type i of one head (rows
+// s_i + q t for 128 consecutive t, s_i = (i - p0) mod q), 32 per wave, and walks
+// the keys type by type: keys of type j are the rows s_j + q t', so a block of 64 of them shares
 // one support F(i, j), i.e. one contraction of |F| m features instead of d.
 // Per key block: S = Q K^T over the support's groups (MFMA 32x32x16, K read
 // row-major from LDS), the causal mask on the actual positions, an online
@@ -31,6 +32,7 @@ namespace qalg {
 namespace {
 
 using dev::bf16x8;
+using dev::bf16x2;
 using dev::f32x16;
 using dev::s16x4;
 using dev::u32x2;
@@ -53,6 +55,7 @@ struct AttnArgs {
   int Hq, Hkv, S, q, L;
   int m;          // features per group (d / q)
   int n_qblk;     // query blocks per (head, type)
+  int o;          // type of row 0: rows s have positions p0 + s and types (o + s) mod q, o = p0 mod q
 };
 
 // groups compared by types (i, j): count, and the b-th one
@@ -106,12 +109,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
   const int h = bid / a.q;
   const int kvh = h / (a.Hq / a.Hkv);
   const int q = a.q, S = a.S;
-  const int n_i = S > i ? (S - i + q - 1) / q : 0;  // queries of type i
+  // rows of type t are first_row(t) + q k (the type offset o shifts them)
+  auto first_row = [&](int t) -> int { return t >= a.o ? t - a.o : t - a.o + q; };
+  const int si = first_row(i);
+  const int n_i = S > si ? (S - si + q - 1) / q : 0;  // queries of type i
   const int t0 = qb * kAttnQ;
   if (t0 >= n_i) return;
   const int t_last = min(t0 + kAttnQ, n_i) - 1;
-  const int p_last = i + q * t_last;                // latest query position in the block
-  const int p_wave0 = i + q * min(t0 + 32 * wid, n_i - 1);  // earliest query position of the wave
+  const int p_last = si + q * t_last;                // latest query row in the block
+  const int p_wave0 = si + q * min(t0 + 32 * wid, n_i - 1);  // earliest query row of the wave
 
   const char* Qh = a.Q + int64_t(h) * S * ROWB;
   const char* Kh = a.K + int64_t(kvh) * S * ROWB;
@@ -121,7 +127,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
   // this lane's query row (row l32 of the wave's 32): its fragments stay in registers
   const int tq = t0 + wid * 32 + l32;
   const bool q_ok = tq < n_i;
-  const int pq = i + q * min(tq, n_i - 1);
+  const int pq = si + q * min(tq, n_i - 1);
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
@@ -161,8 +167,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
   // key blocks, type by type; the cursor (cj, ct) names the next block to copy
   int cj = 0, ct = 0;
   auto keys_of = [&](int j) -> int {
-    // keys of type j that some query of the block may see: u = j + q t' <= p_last < S
-    return p_last >= j ? (p_last - j) / q + 1 : 0;
+    // keys of type j that some query of the block may see: u = first_row(j) + q t' <= p_last < S
+    const int sj = first_row(j);
+    return p_last >= sj ? (p_last - sj) / q + 1 : 0;
   };
   auto skip_empty = [&]() {
     while (cj < q && ct >= keys_of(cj)) {
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
     const uint32_t base = lds0 + uint32_t(stage * 2 * BLK) + uint32_t(wid * LOADS * 1024);
 #pragma unroll
     for (int x = 0; x < LOADS; ++x) {
-      const uint32_t u = uint32_t(cj + q * min(ct + k_row[x], nk - 1));
+      const uint32_t u = uint32_t(first_row(cj) + q * min(ct + k_row[x], nk - 1));
       copy16_to_lds(Kh, u * ROWB + k_pc[x], base + uint32_t(x * 1024));
       copy16_to_lds(Vh, u * ROWB + v_pc[x], base + uint32_t(BLK + x * 1024));
     }
@@ -258,14 +265,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
     const int nf = tot / (a.m / 16);
     // causal mask (only blocks that reach past the wave's earliest query, or past the type's keys)
     const int nk_j = keys_of(j);
-    const bool full = tb + kAttnK <= nk_j && j + q * (tb + kAttnK - 1) <= p_wave0;
+    const int sj = first_row(j);
+    const bool full = tb + kAttnK <= nk_j && sj + q * (tb + kAttnK - 1) <= p_wave0;
     if (!full) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int tk = tb + nb * 32 + 8 * (e >> 2) + 4 * lhi + (e & 3);
-          if (!(tk < nk_j && j + q * tk <= pq)) sc[nb][e] = -INFINITY;
+          if (!(tk < nk_j && sj + q * tk <= pq)) sc[nb][e] = -INFINITY;
         }
     }
     // online softmax in the log2 domain: scale folded into the exponent
@@ -350,12 +358,320 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Cached decoding (appendix G, Algorithm 3; G.2): one new query row per
+// sequence against that sequence's full-key cache.
+//
+// The cache is HBM-bound work: every allowed slot's value row is read once,
+// and of its key row only the feature groups F(i, j) that the query's type i
+// and the key's type j compare (m or 2m of the d features for Q_q), so the key
+// bytes shrink with the score arithmetic (eq 57).  A key's type comes from its
+// absolute position (G.2), through the same schedule as the projections.
+//
+// Split over the cache: a workgroup takes a chunk of kDecCh slots of one
+// (sequence, key/value head) and serves all G = Hq / Hkv query heads that read
+// that head (GQA), so each slot is read once for all of them.  It writes, per
+// query head, the chunk's max score, the sum of exp(score - max) and the
+// unnormalised value sum in fp32; a second kernel combines the chunks in a
+// fixed order (the result does not depend on scheduling).
+//
+// Lanes map to features: in a group of D / 8 lanes (16 for d = 128) lane p
+// owns the 16-byte piece p (features 8p .. 8p + 7) of a row, and holds the G
+// query heads' values of those features in registers.  A wave covers 64 / (D / 8)
+// slots at a time.  Scores: each lane loads its key piece only when the piece's
+// group is in F(i, j) (so only the compared groups are read), multiplies it
+// with its query features, and the group's lanes sum the G partial dot
+// products with a butterfly; all key pieces of the chunk are in flight before
+// the first is used.  Then one wave per query head takes the chunk max and the
+// exponentials.  Values: the same lane/piece map over the value rows of the
+// allowed slots, fp32 sums per head, reduced across the lane groups of a wave
+// and then across waves in a fixed order.
+// ---------------------------------------------------------------------------
+
+constexpr int kDecCh = 128;       // cache slots per workgroup
+constexpr int kDecThreads = 256;
+constexpr int kDecMaxG = 8;       // query heads per key/value head
+constexpr int kDecMaxChunks = 2048;  // chunks the combination takes (N <= kDecCh * kDecMaxChunks)
+
+struct DecArgs {
+  const char* Q;       // B x Hq x d
+  const char* K;       // B x Hkv x N x d
+  const char* V;
+  const int64_t* q_pos;    // B
+  const int64_t* key_pos;  // B x N
+  float* part;         // B x Hq x chunks x (d + 4)
+  char* O;             // B x Hq x d
+  int B, Hq, Hkv, G, q, L, m, kind, chunks;
+  int64_t N, period;
+};
+
+static_assert(kDecCh <= kDecThreads, "one slot per thread at most");
+
+// the position schedule (section 4; appendix D.5): -1 for a negative position
+__device__ __forceinline__ int dec_type(int64_t pos, int q, int kind, int64_t period) {
+  if (pos < 0) return -1;
+  if (kind == 0) return int(pos % q);
+  return int((pos % period) / (period / q));
+}
+
+// is group a one of F(i, j)?  Q_q: a = i or a = j (eq 38); the recursive law:
+// each bit of a equals i's or j's (eq 42)
+__device__ __forceinline__ bool in_support(int a, int i, int j, int L) {
+  if (L == 0) return a == i || a == j;
+  return ((a ^ i) & (a ^ j)) == 0;
+}
+
+// Cross-lane sums on the VALU (no LDS traffic).  row_tail_sum: the lane at
+// position n - 1 of each group of n consecutive lanes (n = 8 or 16, groups
+// inside a 16-lane row) receives the group's sum, through DPP row shifts that
+// read 0 past the row start (bound_ctrl).
+template <int k>
+__device__ __forceinline__ float add_row_shr(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + k, 0xf, 0xf, true));
+}
+template <int n>
+__device__ __forceinline__ float row_tail_sum(float x) {
+  static_assert(n == 8 || n == 16, "groups of 8 or 16 lanes");
+  x = add_row_shr<1>(x);
+  x = add_row_shr<2>(x);
+  x = add_row_shr<4>(x);
+  if constexpr (n == 16) x = add_row_shr<8>(x);
+  return x;
+}
+// every lane receives the sum over the lanes with its position in the 16-lane
+// row (the four rows), by v_permlane16_swap then v_permlane32_swap
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// the sum of lane l and lane l ^ 8 (the two halves of a 16-lane row), by a row rotation
+__device__ __forceinline__ float half_rows_sum(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ void unpack8(const u32x4 v, float (&f)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = __uint_as_float(v[e] << 16);
+    f[2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+  }
+}
+
+// GM: the query heads per key/value head rounded up to a power of two (register arrays)
+template <int D, int GM>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))) void attn_decode_kernel(DecArgs a) {
+  constexpr int NP = D / 8;                    // lanes (16-byte pieces) per row
+  constexpr int SPW = 64 / NP;                 // slots per wave step
+  constexpr int SPB = kDecThreads / NP;        // slots per workgroup step
+  constexpr int STEPS = kDecCh / SPB;          // steps over the chunk
+  __shared__ float ssc[kDecCh][GM];      // scores, then exp(score - max)
+  __shared__ int styp[kDecThreads];            // key type of each slot, -1: not allowed (slots past the chunk: -1)
+  __shared__ float smax[GM], ssum[GM];
+  __shared__ float sred[4][GM][D];       // per-wave value sums
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int G = a.G, q = a.q, m = a.m;
+  const int64_t p = a.q_pos[b];
+  const int i = dec_type(p, q, a.kind, a.period);
+  const int64_t slot0 = int64_t(c) * kDecCh;
+  const int nslot = int(min<int64_t>(kDecCh, a.N - slot0));
+  const int pc = lane % NP;                    // this lane's piece of a row
+  const int sub = tid / NP;                    // slot of this lane within a step
+  const int grp = (pc * 8) / m;                // the feature group of the piece
+
+  // allowed slots and their key types
+  {
+    int t = -1;
+    if (tid < nslot && tid < kDecCh && i >= 0) {
+      const int64_t u = a.key_pos[int64_t(b) * a.N + slot0 + tid];
+      if (u >= 0 && u <= p) t = dec_type(u, q, a.kind, a.period);
+    }
+    styp[tid] = t;
+  }
+  // the G query heads' features of this lane's piece, as bf16 pairs
+  u32x4 qv[GM];
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    qv[g] = (u32x4){0u, 0u, 0u, 0u};
+    if (g < G) qv[g] = *reinterpret_cast<const u32x4*>(a.Q + ((int64_t(b) * a.Hq + kvh * G + g) * D + pc * 8) * 2);
+  }
+  __syncthreads();
+
+  const int64_t row0 = (int64_t(b) * a.Hkv + kvh) * a.N + slot0;  // first slot's row in K / V
+  // every needed key piece and every allowed value piece of the chunk is
+  // requested before the first is used: one memory round trip per workgroup
+  u32x4 kreg[STEPS], vreg[STEPS];
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const int sl = st * SPB + sub;
+    const int j = styp[sl];
+    kreg[st] = (u32x4){0u, 0u, 0u, 0u};
+    if (j >= 0 && in_support(grp, i, j, a.L))
+      kreg[st] = *reinterpret_cast<const u32x4*>(a.K + ((row0 + sl) * D + pc * 8) * 2);
+  }
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const int sl = st * SPB + sub;
+    vreg[st] = (u32x4){0u, 0u, 0u, 0u};
+    if (styp[sl] >= 0) vreg[st] = *reinterpret_cast<const u32x4*>(a.V + ((row0 + sl) * D + pc * 8) * 2);
+  }
+  // scores
+  {
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const int sl = st * SPB + sub;
+      const int j = styp[sl];
+      float r[GM];
+      // (plain arrays: a bit cast of a vector-type element subscript loses the subscript in this compiler)
+      const unsigned kw[4] = {kreg[st].x, kreg[st].y, kreg[st].z, kreg[st].w};
+#pragma unroll
+      for (int g = 0; g < GM; ++g) {
+        const unsigned qw[4] = {qv[g].x, qv[g].y, qv[g].z, qv[g].w};
+        r[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          r[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw[e]), __builtin_bit_cast(bf16x2, qw[e]),
+                                                 r[g], false);
+        // the row's pieces sit in NP consecutive lanes: their sum lands in the last one
+        r[g] = row_tail_sum<NP>(r[g]);
+      }
+      if (pc == NP - 1) {
+        const float scl = j >= 0 ? __builtin_amdgcn_rsqf(float(support_count(i, j, a.L) * m)) : 0.f;
+#pragma unroll
+        for (int g = 0; g < GM; ++g) ssc[sl][g] = g >= G ? 0.f : (j >= 0 ? r[g] * scl : -INFINITY);
+      }
+    }
+  }
+  __syncthreads();
+
+  // per query head: chunk max, exponentials, their sum (one wave per head)
+  for (int g = wid; g < G; g += 4) {
+    float mx = -INFINITY;
+    for (int sl = lane; sl < kDecCh; sl += 64) mx = fmaxf(mx, ssc[sl][g]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float sum = 0.f;
+    for (int sl = lane; sl < kDecCh; sl += 64) {
+      const float e = mx == -INFINITY ? 0.f : __expf(ssc[sl][g] - mx);
+      ssc[sl][g] = e;
+      sum += e;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+    if (lane == 0) {
+      smax[g] = mx;
+      ssum[g] = sum;
+    }
+  }
+  __syncthreads();
+
+  // value sums over the allowed slots: this lane's 8 features, per head
+  float acc[GM][8];
+#pragma unroll
+  for (int g = 0; g < GM; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+  {
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const int sl = st * SPB + sub;
+      float vf[8];
+      unpack8(vreg[st], vf);
+      float w[GM];
+#pragma unroll
+      for (int g = 0; g < GM; ++g) w[g] = ssc[sl][g];
+#pragma unroll
+      for (int g = 0; g < GM; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = __builtin_fmaf(w[g], vf[e], acc[g][e]);
+    }
+  }
+  // lane groups of a wave (same piece) in a fixed tree, then the waves in order
+#pragma unroll
+  for (int g = 0; g < GM; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (NP == 8) acc[g][e] = half_rows_sum(acc[g][e]);
+      acc[g][e] = rows_sum(acc[g][e]);
+    }
+  if (lane < NP) {
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+      if (g < G)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sred[wid][g][pc * 8 + e] = acc[g][e];
+  }
+  __syncthreads();
+  float* part = a.part + ((int64_t(b) * a.Hq + kvh * G) * a.chunks + c) * (D + 4);
+  for (int x = tid; x < G * D; x += kDecThreads) {
+    const int g = x / D, f = x - g * D;
+    const float v = ((sred[0][g][f] + sred[1][g][f]) + sred[2][g][f]) + sred[3][g][f];
+    part[int64_t(g) * a.chunks * (D + 4) + f] = v;
+  }
+  if (tid < G) {
+    float* pg = part + int64_t(tid) * a.chunks * (D + 4);
+    pg[D] = smax[tid];
+    pg[D + 1] = ssum[tid];
+  }
+}
+
+// O = sum_c e^(M_c - M) O_c / sum_c e^(M_c - M) L_c over the chunks c with
+// L_c > 0; one workgroup of D threads per (sequence, query head).  The chunk
+// weights are formed once (thread t takes chunks t, t + D, ...; block max and
+// sum in a fixed tree), then thread f sums its feature over the chunks in
+// order.  Rows with no allowed slot (every L_c = 0) are written as zeros.
+template <int D>
+__global__ __launch_bounds__(D) void attn_decode_combine_kernel(const float* __restrict__ part, int chunks,
+                                                                char* __restrict__ O) {
+  constexpr int W = D / 64;
+  __shared__ float sw[kDecMaxChunks];  // chunk weights
+  __shared__ float sr[W];
+  const int64_t row = blockIdx.x;
+  const int f = threadIdx.x, lane = f & 63, wv = f >> 6;
+  const float* pr = part + row * chunks * (D + 4);
+  auto block_reduce = [&](float x, bool is_max) -> float {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float y = __shfl_xor(x, o);
+      x = is_max ? fmaxf(x, y) : x + y;
+    }
+    __syncthreads();
+    if (lane == 0) sr[wv] = x;
+    __syncthreads();
+    float t = sr[0];
+    for (int w = 1; w < W; ++w) t = is_max ? fmaxf(t, sr[w]) : t + sr[w];
+    return t;
+  };
+  float mloc = -INFINITY;
+  for (int cc = f; cc < chunks; cc += D) {
+    const float* pc = pr + int64_t(cc) * (D + 4);
+    if (pc[D + 1] > 0.f) mloc = fmaxf(mloc, pc[D]);
+  }
+  const float M = block_reduce(mloc, true);
+  float lloc = 0.f;
+  for (int cc = f; cc < chunks; cc += D) {
+    const float* pc = pr + int64_t(cc) * (D + 4);
+    const float w = (M != -INFINITY && pc[D + 1] > 0.f) ? __expf(pc[D] - M) : 0.f;
+    sw[cc] = w;
+    lloc = __builtin_fmaf(w, pc[D + 1], lloc);
+  }
+  const float Lsum = block_reduce(lloc, false);  // its barriers also publish sw
+  float acc = 0.f;
+  for (int cc = 0; cc < chunks; ++cc) acc = __builtin_fmaf(sw[cc], pr[int64_t(cc) * (D + 4) + f], acc);
+  const float v = Lsum > 0.f ? acc / Lsum : 0.f;
+  const bf16x2 h = __builtin_convertvector((dev::f32x2){v, 0.f}, bf16x2);
+  reinterpret_cast<uint16_t*>(O)[row * D + f] = uint16_t(__builtin_bit_cast(uint32_t, h) & 0xffffu);
+}
+
 }  // namespace
 
 bool attn_supported(int d, int q) { return (d == 64 || d == 128) && q >= 1 && d % q == 0 && (d / q) % 16 == 0; }
 
 hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, void* O, int Hq, int Hkv, int64_t S,
-                                int d, int q, int L, hipStream_t s) {
+                                int d, int q, int L, int64_t first_pos, hipStream_t s) {
   AttnArgs a;
   a.Q = static_cast<const char*>(Q);
   a.K = static_cast<const char*>(K);
@@ -367,6 +683,7 @@ hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, voi
   a.q = q;
   a.L = L;
   a.m = d / q;
+  a.o = int(first_pos % q);
   const int64_t n0 = (S + q - 1) / q;  // queries of type 0, the most of any type
   a.n_qblk = int((n0 + kAttnQ - 1) / kAttnQ);
   const int64_t blocks = int64_t(Hq) * q * a.n_qblk;
@@ -376,6 +693,64 @@ hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, voi
   else
     hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(unsigned(blocks)), dim3(kAttnThreads), 0, s, a);
   return hipGetLastError();
+}
+
+bool attn_decode_supported(int d, int q) { return (d == 64 || d == 128) && q >= 1 && d % q == 0 && (d / q) % 8 == 0; }
+
+int64_t attn_decode_max_slots() { return int64_t(kDecCh) * kDecMaxChunks; }
+
+size_t attn_decode_part_bytes(int64_t B, int64_t Hq, int64_t N, int d) {
+  const int64_t chunks = (N + kDecCh - 1) / kDecCh;
+  return size_t(B * Hq * chunks * (d + 4)) * sizeof(float);
+}
+
+hipError_t launch_attn_decode_bf16(const void* Q, const void* K, const void* V, const int64_t* q_pos,
+                                   const int64_t* key_pos, void* O, int B, int Hq, int Hkv, int64_t N, int d, int q,
+                                   int L, int kind, int64_t period, void* part, hipStream_t s) {
+  DecArgs a;
+  a.Q = static_cast<const char*>(Q);
+  a.K = static_cast<const char*>(K);
+  a.V = static_cast<const char*>(V);
+  a.q_pos = q_pos;
+  a.key_pos = key_pos;
+  a.part = static_cast<float*>(part);
+  a.O = static_cast<char*>(O);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.q = q;
+  a.L = L;
+  a.m = d / q;
+  a.kind = kind;
+  a.period = period;
+  a.N = N;
+  a.chunks = int((N + kDecCh - 1) / kDecCh);
+  const dim3 grid(unsigned(a.chunks), unsigned(Hkv), unsigned(B));
+  const int gm = a.G <= 1 ? 1 : a.G <= 2 ? 2 : a.G <= 4 ? 4 : 8;
+  auto run = [&](auto d_c, auto g_c) {
+    constexpr int DD = decltype(d_c)::value, GG = decltype(g_c)::value;
+    hipLaunchKernelGGL((attn_decode_kernel<DD, GG>), grid, dim3(kDecThreads), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL(attn_decode_combine_kernel<DD>, dim3(unsigned(B * Hq)), dim3(DD), 0, s, a.part, a.chunks, a.O);
+    return hipGetLastError();
+  };
+  using I128 = std::integral_constant<int, 128>;
+  using I64 = std::integral_constant<int, 64>;
+  using G1 = std::integral_constant<int, 1>;
+  using G2 = std::integral_constant<int, 2>;
+  using G4 = std::integral_constant<int, 4>;
+  using G8 = std::integral_constant<int, 8>;
+  if (d == 128) {
+    if (gm == 1) return run(I128{}, G1{});
+    if (gm == 2) return run(I128{}, G2{});
+    if (gm == 4) return run(I128{}, G4{});
+    return run(I128{}, G8{});
+  }
+  if (gm == 1) return run(I64{}, G1{});
+  if (gm == 2) return run(I64{}, G2{});
+  if (gm == 4) return run(I64{}, G4{});
+  return run(I64{}, G8{});
 }
 
 }  // namespace qalg

@@ -120,7 +120,14 @@ hipError_t launch_split_gate_up_bf16(const void* Wgu, void* Wg, void* Wu, int64_
 // causal attention with the algebraic score, forward (qalg_attn.hip)
 bool attn_supported(int d, int q);
 hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, void* O, int Hq, int Hkv, int64_t S,
-                                int d, int q, int L, hipStream_t s);
+                                int d, int q, int L, int64_t first_pos, hipStream_t s);
+// cached decoding (Algorithm 3): per-chunk partials in `part`, then their ordered combination into O
+bool attn_decode_supported(int d, int q);
+int64_t attn_decode_max_slots();  // cache slots per sequence the decode kernels take
+size_t attn_decode_part_bytes(int64_t B, int64_t Hq, int64_t N, int d);
+hipError_t launch_attn_decode_bf16(const void* Q, const void* K, const void* V, const int64_t* q_pos,
+                                   const int64_t* key_pos, void* O, int B, int Hq, int Hkv, int64_t N, int d, int q,
+                                   int L, int kind, int64_t period, void* part, hipStream_t s);
 // Persistent 256-row-tile dX / dW (bf16, one problem) for cyclic schedules; a
 // launch on any other schedule returns at once.
 bool grad_persistent_supported(const ProblemDesc& p);

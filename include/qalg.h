@@ -403,6 +403,51 @@ qalg_status qalg_attention_forward(const void* Q, const void* K, const void* V, 
                                    void* stream);
 
 /*
+ * The same for a chunk of S rows whose first row sits at absolute position
+ * first_position (>= 0, QALG_ERR_DIM otherwise): row s has position
+ * first_position + s and type (first_position + s) mod q (section 4's cyclic
+ * schedule at that offset, so the type of row 0 is first_position mod q and
+ * the pairs F(i, j) move with it); the mask is the chunk's own causal order.
+ * Everything else as qalg_attention_forward (which is first_position = 0).
+ */
+qalg_status qalg_attention_forward_at(const void* Q, const void* K, const void* V, int32_t Hq, int32_t Hkv,
+                                      int64_t S, int32_t d, int32_t q, int64_t first_position, void* O,
+                                      int32_t dtype, uint32_t flags, void* stream);
+
+/*
+ * Cached decoding with the algebraic score (appendix G, Algorithm 3; G.2's
+ * cache): one new query row per sequence against that sequence's full-key
+ * cache.  B sequences; Qn: B x Hq x d, the new rows' queries; Kc, Vc:
+ * B x Hkv x N x d, each sequence's cache of N slots holding full keys and
+ * values (query head h reads key/value head h / (Hq / Hkv), GQA); q_pos:
+ * int64[B], the absolute position p of each new row; key_pos: int64[B x N],
+ * the absolute position u of each cached slot, negative for an empty slot.
+ * All device memory, caller-owned, bf16 / int64, packed; Qn, Kc, Vc, O 16-byte
+ * and the positions 8-byte aligned.  Types come from positions through the
+ * schedule `kind` (a qalg_schedule; `period` for the interval form, as in
+ * qalg_type_schedule): i = tau(p), j = tau(u).  For each slot with
+ * 0 <= u <= p the score sums <Q^(a), K_u^(a)> over the groups a of F(i, j)
+ * (eq 38-39; eq 42 with QALG_FLAG_LAW_TENSOR) scaled by 1 / sqrt(|F| d / q)
+ * (eq 41); O (B x Hq x d, overwritten) is the softmax-weighted sum of those
+ * slots' values over all d features (Algorithm 3's last step).  A row with no
+ * such slot (or p < 0) is written as zeros.  Only the F(i, j) groups of each
+ * cached key are read (eq 57's cost).  fp32 scores, softmax and sums; O rounded
+ * once.  ws: caller-owned device memory of at least
+ * qalg_attention_decode_workspace_bytes(B, Hq, N, d) bytes, 16-byte aligned
+ * (fp32 partial results of slot chunks, combined in a fixed order: bitwise
+ * reproducible).  Errors: d not 64 or 128, Hkv not dividing Hq, Hq / Hkv > 8,
+ * N < 1 or N > 262144, B or Hkv > 65535 (QALG_ERR_DIM); q not dividing d or the
+ * recursive law with q not a power of two (QALG_ERR_Q); d / q not a multiple of
+ * 8 or misaligned pointers (QALG_ERR_ALIGN); an unknown schedule or flag
+ * (QALG_ERR_ARG); a small workspace (QALG_ERR_WORKSPACE).  B = 0 enqueues nothing.
+ */
+size_t qalg_attention_decode_workspace_bytes(int32_t B, int32_t Hq, int64_t N, int32_t d);
+qalg_status qalg_attention_decode(const void* Qn, const void* Kc, const void* Vc, const int64_t* q_pos,
+                                  const int64_t* key_pos, int32_t B, int32_t Hq, int32_t Hkv, int64_t N, int32_t d,
+                                  int32_t q, int32_t kind, int64_t period, void* O, int32_t dtype, void* ws,
+                                  size_t ws_bytes, uint32_t flags, void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * qalg_forward with no workspace argument.  The type index it builds goes to

@@ -359,3 +359,30 @@ def test_widths_argument_errors_are_synchronous(lib):
                                    FAKE, 1, FAKE, 0, 0, None) == 0
     assert lib.qalg_backward_dw_widths(FAKE, FAKE, FAKE, 3, arr(64, 128, 64), arr(256, 128, 128), 0, 256, 512,
                                        None, 1, FAKE, 0, 0, None) == 1
+
+
+def test_attention_decode_argument_errors_are_synchronous(lib):
+    def dec(B=2, Hq=4, Hkv=2, N=16, d=128, q=4, kind=0, period=0, dt=1, ws=FAKE, wsb=1 << 20, flags=0,
+            Qn=FAKE, qp=FAKE, kp=FAKE):
+        return lib.qalg_attention_decode(Qn, FAKE, FAKE, qp, kp, B, Hq, Hkv, N, d, q, kind, period, FAKE, dt, ws, wsb,
+                                         flags, None)
+    assert dec(dt=0) == 5
+    assert dec(flags=1) == 8
+    assert dec(Hkv=3) == 2                 # Hkv does not divide Hq
+    assert dec(Hq=18, Hkv=2) == 2          # more than 8 query heads per key/value head
+    assert dec(d=96) == 2
+    assert dec(N=0) == 2
+    assert dec(q=3) == 3
+    assert dec(q=32) == 4                  # d / q = 4 is not a multiple of 8
+    assert dec(q=4, kind=1, period=6) == 8
+    assert dec(q=4, kind=7) == 8
+    assert dec(Qn=None) == 1
+    assert dec(qp=FAKE + 4) == 4
+    assert dec(wsb=16) == 6
+    assert dec(ws=None) == 1
+    assert dec(B=0, Qn=None, qp=None, kp=None, ws=None) == 0
+    need = Q.qalg_attention_decode_workspace_bytes(2, 4, 16, 128)
+    assert need >= 2 * 4 * 1 * 132 * 4 and need % 256 == 0
+    assert Q.qalg_attention_decode_workspace_bytes(2, 4, 0, 128) == 0
+    # the offset prefill: a negative first position is refused
+    assert lib.qalg_attention_forward_at(FAKE, FAKE, FAKE, 2, 1, 8, 64, 2, -1, FAKE, 1, 0, None) == 2

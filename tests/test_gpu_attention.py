@@ -52,3 +52,118 @@ def test_attention_forward_matches_oracle(shape):
     errs = [_rel(got[h], Or[h]) for h in range(Hq)]
     say(f"    max rel err over heads {max(errs):.2e}")
     assert max(errs) <= BF16_TOL, errs
+
+
+OFFSET_SHAPES = [
+    # Hq, Hkv, S, d, q, L, first position
+    (4, 2, 300, 128, 4, 0, 5),
+    (2, 2, 257, 64, 4, 0, 4099),
+    (2, 1, 200, 128, 4, 2, 3),     # the recursive law at an offset
+    (2, 2, 37, 128, 4, 0, 2),
+    (2, 2, 100, 128, 1, 0, 7),     # q = 1: the offset changes nothing
+]
+
+
+@pytest.mark.parametrize("shape", OFFSET_SHAPES, ids=[f"H{s[0]}kv{s[1]}S{s[2]}d{s[3]}q{s[4]}L{s[5]}p{s[6]}" for s in OFFSET_SHAPES])
+def test_attention_forward_at_offset_matches_oracle(shape):
+    """A prefill chunk whose first row sits at absolute position p0: types (p0 + s) mod q."""
+    torch = torch_cuda()
+    Hq, Hkv, S, d, q, L, p0 = shape
+    say(f"[attn offset] Hq={Hq} Hkv={Hkv} S={S} d={d} q={q} L={L} p0={p0}")
+    Qo = synth.normal_operand(9610 + S, (Hq, S, d), 1.0, "bf16")
+    Ko = synth.normal_operand(9710 + S, (Hkv, S, d), 1.0, "bf16")
+    Vo = synth.normal_operand(9810 + S, (Hkv, S, d), 1.0, "bf16")
+    flags = Q.QALG_FLAG_LAW_TENSOR if L else 0
+    Qd, Kd, Vd = to_dev(Qo), to_dev(Ko), to_dev(Vo)
+    Og = Q.qalg_attention_forward_at(Qd, Kd, Vd, q, p0, flags=flags)
+    Og2 = Q.qalg_attention_forward_at(Qd, Kd, Vd, q, p0, flags=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(Og, Og2), "not bitwise reproducible"
+    pos = p0 + np.arange(S)
+    Or = O.algebraic_attention(Qo.f64, Ko.f64, Vo.f64, pos % q, q, L, positions=pos)
+    got = to_f64(Og)
+    errs = [_rel(got[h], Or[h]) for h in range(Hq)]
+    say(f"    max rel err over heads {max(errs):.2e}")
+    assert max(errs) <= BF16_TOL, errs
+    if q > 1 and p0 % q:
+        # the offset changes the pairs: not the zero-offset result
+        O0 = to_f64(Q.qalg_attention_forward(Qd, Kd, Vd, q, flags=flags))
+        assert not np.allclose(O0, got)
+
+
+def _decode_case(B, Hq, Hkv, N, d, q, L, kind, period, lens, p0s, seed, holes=0, future=0):
+    """Caches of N slots: sequence b holds positions p0s[b] .. p0s[b] + lens[b] - 1 in a shuffled slot
+    order, `holes` of them emptied (-1) and `future` positions after the query added; the new row
+    sits at the last position p0s[b] + lens[b] - 1."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    key_pos = np.full((B, N), -1, np.int64)
+    q_pos = np.zeros(B, np.int64)
+    for b in range(B):
+        n = lens[b]
+        pos = p0s[b] + np.arange(n)
+        q_pos[b] = pos[-1]
+        slots = g.permutation(N)[:n]
+        key_pos[b, slots] = pos
+        free = np.setdiff1d(np.arange(N), slots)
+        if holes and n > 1:
+            key_pos[b, g.choice(slots, size=min(holes, n - 1), replace=False)] = -1
+        if future and free.size:
+            key_pos[b, free[:future]] = q_pos[b] + 1 + np.arange(min(future, free.size))
+    Qo = synth.normal_operand(seed + 1, (B, Hq, d), 1.0, "bf16")
+    Ko = synth.normal_operand(seed + 2, (B, Hkv, N, d), 1.0, "bf16")
+    Vo = synth.normal_operand(seed + 3, (B, Hkv, N, d), 1.0, "bf16")
+    return Qo, Ko, Vo, q_pos, key_pos
+
+
+DECODE_CASES = [
+    # B, Hq, Hkv, N, d, q, L, kind, period, lens, first positions, holes, future keys
+    (2, 4, 1, 1, 128, 4, 0, 0, 0, [1, 1], [3, 6], 0, 0),                 # S = 1: one cached key
+    (3, 8, 2, 37, 128, 4, 0, 0, 0, [37, 20, 5], [5, 0, 101], 3, 2),     # S = 37, offsets, holes, future keys
+    (2, 32, 8, 4096, 128, 4, 0, 0, 0, [4096, 3000], [3, 17], 0, 0),     # S = 4096 (several chunks), GQA 4
+    (2, 8, 1, 700, 64, 8, 0, 0, 0, [700, 513], [1, 9], 5, 3),           # d = 64, q = 8, GQA 8
+    (2, 4, 2, 300, 128, 4, 2, 0, 0, [300, 299], [2, 7], 4, 0),          # the recursive law
+    (2, 4, 4, 600, 128, 4, 0, 1, 768, [600, 450], [100, 700], 0, 1),    # the interval schedule
+    (1, 4, 4, 512, 128, 1, 0, 0, 0, [512], [0], 0, 0),                  # q = 1: ordinary decode
+    (2, 2, 2, 260, 128, 16, 0, 0, 0, [260, 3], [1, 2], 2, 0),           # q = 16 (groups of 8 features)
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[f"B{c[0]}H{c[1]}kv{c[2]}N{c[3]}d{c[4]}q{c[5]}L{c[6]}k{c[7]}"
+                                                    for c in DECODE_CASES])
+def test_attention_decode_matches_oracle(case):
+    torch = torch_cuda()
+    B, Hq, Hkv, N, d, q, L, kind, period, lens, p0s, holes, future = case
+    say(f"[decode] B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} q={q} L={L} kind={kind} lens={lens} p0={p0s}")
+    Qo, Ko, Vo, q_pos, key_pos = _decode_case(B, Hq, Hkv, N, d, q, L, kind, period, lens, p0s, 9950 + N + q,
+                                              holes, future)
+    Qd, Kd, Vd = to_dev(Qo), to_dev(Ko), to_dev(Vo)
+    qp, kp = torch.from_numpy(q_pos).to("cuda"), torch.from_numpy(key_pos).to("cuda")
+    flags = Q.QALG_FLAG_LAW_TENSOR if L else 0
+    Og = Q.qalg_attention_decode(Qd, Kd, Vd, qp, kp, q, kind, period, flags=flags)
+    Og2 = Q.qalg_attention_decode(Qd, Kd, Vd, qp, kp, q, kind, period, flags=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(Og, Og2), "not bitwise reproducible"
+    sched = "cyclic" if kind == 0 else "interval"
+    Or = O.algebraic_attention_decode(Qo.f64, Ko.f64, Vo.f64, q_pos, key_pos, q, L, sched, period)
+    got = to_f64(Og)
+    errs = [_rel(got[b, h], Or[b, h]) for b in range(B) for h in range(Hq)]
+    say(f"    max rel err over rows {max(errs):.2e}")
+    assert max(errs) <= BF16_TOL, errs
+
+
+def test_attention_decode_empty_rows_are_zero():
+    """A new row with no allowed cached slot (all empty, or all after it) gets a zero output."""
+    torch = torch_cuda()
+    B, Hq, Hkv, N, d, q = 3, 4, 2, 300, 128, 4
+    Qo, Ko, Vo, _, _ = _decode_case(B, Hq, Hkv, N, d, q, 0, 0, 0, [1, 1, 1], [0, 0, 0], 9990)
+    key_pos = np.full((B, N), -1, np.int64)
+    key_pos[1, 10:20] = 50 + np.arange(10)   # every key after the query
+    key_pos[2, 5] = 7                        # one allowed key
+    q_pos = np.array([9, 9, 9], np.int64)
+    Og = Q.qalg_attention_decode(to_dev(Qo), to_dev(Ko), to_dev(Vo), torch.from_numpy(q_pos).to("cuda"),
+                                 torch.from_numpy(key_pos).to("cuda"), q)
+    torch.cuda.synchronize()
+    got = to_f64(Og)
+    assert not got[0].any() and not got[1].any()
+    Or = O.algebraic_attention_decode(Qo.f64, Ko.f64, Vo.f64, q_pos, key_pos, q)
+    assert _rel(got[2], Or[2]) <= BF16_TOL

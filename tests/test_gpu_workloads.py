@@ -408,3 +408,30 @@ def test_unequal_widths_bench_shape_sampled():
              for b in range(q) for j in range(q))
     say(f"    max rel err Y {ey:.2e}, dX {ex:.2e}, dW {ew:.2e}")
     assert ey <= BF16_TOL and ex <= BF16_TOL and ew <= BF16_TOL
+
+
+def test_attention_decode_bench_shape_sampled():
+    """The benchmark's cached-decoding leg: 32 sequences, 32 query heads over 8 key/value heads,
+    d = 128, 4096-slot caches (sequence b holds positions 0..4095-b), q = 4; same seeds and call.
+    Four sequences (all query heads) against the oracle."""
+    torch = torch_cuda()
+    c, B, Hq, Hkv, N, d, q = 11, 32, 32, 8, 4096, 128, 4
+    say(f"[workload] attention decode B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} q={q}")
+    Qo = synth.normal_operand(1000 * c + 1, (B, Hq, d), 1.0, "bf16")
+    Ko = synth.normal_operand(1000 * c + 2, (B, Hkv, N, d), 1.0, "bf16")
+    Vo = synth.normal_operand(1000 * c + 3, (B, Hkv, N, d), 1.0, "bf16")
+    lens = N - np.arange(B)
+    key_pos = np.full((B, N), -1, np.int64)
+    for b in range(B):
+        key_pos[b, :lens[b]] = np.arange(lens[b])
+    q_pos = (lens - 1).astype(np.int64)
+    Og = Q.qalg_attention_decode(to_dev(Qo), to_dev(Ko), to_dev(Vo), torch.from_numpy(q_pos).to("cuda"),
+                                 torch.from_numpy(key_pos).to("cuda"), q)
+    torch.cuda.synchronize()
+    got = to_f64(Og)
+    seqs = [0, 1, 2, 31]   # query types 3, 2, 1, 0
+    Or = O.algebraic_attention_decode(Qo.f64[seqs], Ko.f64[seqs], Vo.f64[seqs], q_pos[seqs], key_pos[seqs], q)
+    errs = [float(np.linalg.norm(got[b, h] - Or[k, h]) / np.linalg.norm(Or[k, h]))
+            for k, b in enumerate(seqs) for h in range(Hq)]
+    say(f"    max rel err over {len(errs)} rows {max(errs):.2e}")
+    assert max(errs) <= BF16_TOL, max(errs)
