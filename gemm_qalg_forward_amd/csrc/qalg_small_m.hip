@@ -32,6 +32,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kSmThreads = 256;
 
+// wave-uniform integer quotient (both operands uniform): kept on the scalar unit
+__device__ __forceinline__ int uni_div(int x, int y) {
+  return __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readfirstlane(x) / __builtin_amdgcn_readfirstlane(y));
+}
+
 constexpr int kSmMaxRows = 8;
 constexpr int kSmUnroll = 8;          // weight loads per thread per batch; two batches in flight
 constexpr int kSmMaxXs = 16384;        // bf16 elements of one block's staged activations (32 KB)
@@ -61,7 +66,9 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
   // lane applies together: the activations are staged as those pairs, u32
   // (x[kk], x[kk + KL]), and the group width is padded to whole pairs with zeros
   constexpr int KL = kSmKLanes;
-  const int s_pad = (a.s + 2 * KL - 1) / (2 * KL) * (2 * KL);
+  constexpr int kStep = kSmKLanes * kSmUnroll;  // weight rows of one batch (all threads)
+  // the group width padded to whole batches: a batch never straddles two blocks
+  const int s_pad = (a.s + kStep - 1) / kStep * kStep;
   extern __shared__ __attribute__((aligned(16))) unsigned char sm_raw[];
   uint16_t* xs16 = reinterpret_cast<uint16_t*>(sm_raw);              // [s_pad / 2][R] pairs of bf16
   const unsigned* xs2 = reinterpret_cast<const unsigned*>(sm_raw);
@@ -138,43 +145,40 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
     }
     for (int x = tid; x < (s_pad - s) * R; x += kSmThreads) xr16[xs_at(s + x / R, x % R)] = 0;
   };
-  // with room for every block the chunk needs, all activations are staged up
-  // front behind one barrier and the weight stream runs through the blocks
-  // back to back; otherwise one block at a time
-  const bool all = a.x_regions > 1;
-  if (all) {
-    for (int bi = 0; bi < nblk; ++bi) stage(s_blocks[bi], bi);
-    __syncthreads();
-  }
-  for (int bi = 0; bi < nblk; ++bi) {
-    const int b = s_blocks[bi];
-    if (!all) {
-      stage(b, 0);
-      __syncthreads();
-    }
-    const unsigned* xsb = xs2 + (all ? bi : 0) * (x_region / 2);
-    // weight rows of the block: batches of kSmUnroll rows per thread, the next
-    // batch's loads issued before the current batch is applied, so that two
-    // batches (2 x 8 x 16 bytes per thread) are in flight
-    const uint16_t* wp = W + int64_t(b) * s * N + col0 + l8 * 8;
-    constexpr int kStep = kSmKLanes * kSmUnroll;
-    auto load_batch = [&](int k0, u32x4 (&wv)[kSmUnroll]) {
+  // The weight rows of the chunk's blocks form one stream of batches: block
+  // bi's rows are stream rows bi * s_pad + k, and batch n (kStep rows, 8 per
+  // thread: rows n kStep + kr + u KL) lies inside block n kStep / s_pad.  The
+  // two-batch pipeline therefore keeps 2 x 8 16-byte loads per thread in
+  // flight across block boundaries, not only inside a block (a 256-row block
+  // is a single batch).  Rows past s load nothing and meet zero activations.
+  // With room for every block the chunk needs, all activations are staged up
+  // front, behind the first two batches' loads, and one stream runs through
+  // all blocks; otherwise one block at a time, restaged in between.
+  auto run_stream = [&](int bi0, int nbat, int x_base, bool stage_first) {
+    auto load_batch = [&](int n, u32x4 (&wv)[kSmUnroll]) {
+      const int bl = uni_div(n * kStep, s_pad);
+      const int k0 = n * kStep - bl * s_pad + kr;
+      const uint16_t* wp = n < nbat ? W + (int64_t(s_blocks[bi0 + bl]) * s + k0) * N + col0 + l8 * 8 : W;
 #pragma unroll
       for (int u = 0; u < kSmUnroll; ++u) {
         const int kk = k0 + u * kSmKLanes;
-        wv[u] = (kk < s && col_on) ? *reinterpret_cast<const u32x4*>(wp + int64_t(kk) * N)
-                                   : (u32x4){0u, 0u, 0u, 0u};
+        wv[u] = (n < nbat && kk < s && col_on) ? *reinterpret_cast<const u32x4*>(wp + int64_t(u) * kSmKLanes * N)
+                                               : (u32x4){0u, 0u, 0u, 0u};
       }
     };
     // weight rows kk (piece 2v) and kk + KL (piece 2v + 1) are applied together:
     // their columns interleaved into bf16 pairs, one v_dot2c_f32_bf16 per
     // row and column (a weight past the group width is loaded as zero, and so
     // is its activation)
-    auto apply_batch = [&](int k0, const u32x4 (&wv)[kSmUnroll]) {
+    auto apply_batch = [&](int n, const u32x4 (&wv)[kSmUnroll]) {
+      if (n >= nbat) return;
+      const int bl = uni_div(n * kStep, s_pad);
+      const int k0 = n * kStep - bl * s_pad + kr;
+      if (k0 - kr >= s) return;  // a batch of padding rows only
+      const unsigned* xsb = xs2 + (x_base + bl) * (x_region / 2);
 #pragma unroll
       for (int v = 0; v < kSmUnroll / 2; ++v) {
         const int kk = k0 + 2 * v * KL;
-        if (kk >= s) break;
         unsigned wp[8];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -192,14 +196,29 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
       }
     };
     u32x4 wa[kSmUnroll], wb[kSmUnroll];
-    load_batch(kr, wa);
-    for (int k = kr; k < s; k += 2 * kStep) {
-      load_batch(k + kStep, wb);
-      apply_batch(k, wa);
-      load_batch(k + 2 * kStep, wa);
-      apply_batch(k + kStep, wb);
+    load_batch(0, wa);
+    load_batch(1, wb);
+    if (stage_first) {
+      for (int bi = 0; bi < nblk; ++bi) stage(s_blocks[bi], bi);
+      __syncthreads();
     }
-    if (!all) __syncthreads();  // the region is restaged for the next block
+    for (int n = 0; n < nbat; n += 2) {
+      apply_batch(n, wa);
+      load_batch(n + 2, wa);
+      apply_batch(n + 1, wb);
+      load_batch(n + 3, wb);
+    }
+  };
+  const int bat_per_block = s_pad / kStep;
+  if (a.x_regions > 1) {
+    run_stream(0, nblk * bat_per_block, 0, true);
+  } else {
+    for (int bi = 0; bi < nblk; ++bi) {
+      stage(s_blocks[bi], 0);
+      __syncthreads();
+      run_stream(bi, bat_per_block, 0, false);
+      __syncthreads();  // the region is restaged for the next block
+    }
   }
 
   // reduce the weight-row lanes: those of a wave by a fixed shuffle tree, then
@@ -236,7 +255,8 @@ hipError_t launch_rc(SmallArgs a, int E, hipStream_t st) {
   a.chunks_per_group = (a.r + COLS - 1) / COLS;
   const dim3 grid(unsigned(a.q * a.chunks_per_group), unsigned(E));
   constexpr int KL = kSmThreads / (COLS / 8);  // weight rows per step (the pair distance)
-  const size_t s_pad = size_t(a.s + 2 * KL - 1) / (2 * KL) * (2 * KL);
+  constexpr int kStep = KL * kSmUnroll;          // weight rows per batch
+  const size_t s_pad = size_t(a.s + kStep - 1) / kStep * kStep;
   // a chunk of output group j needs W_jj and W_tj for the other types among the
   // rows: at most min(q, 1 + R) blocks; stage them all when they fit kSmStageAll
   const int nb_max = a.q < 1 + R ? a.q : 1 + R;
@@ -273,8 +293,8 @@ bool small_m_supported(const ProblemDesc& p) {
   if (p.op != Op::Fwd || p.M < 1 || p.M > kSmMaxRows) return false;
   int R = 1;
   while (R < p.M) R <<= 1;
-  // the staged group width padded to whole row pairs (at most 64 rows apart)
-  return ((p.K / p.q + 63) / 64 * 64) * R <= kSmMaxXs;
+  // the staged group width padded to whole batches (at most 256 rows: 64-column chunks)
+  return ((p.K / p.q + 255) / 256 * 256) * R <= kSmMaxXs;
 }
 
 hipError_t launch_small_m_bf16(const ProblemDesc& p, hipStream_t st) {
