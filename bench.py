@@ -1020,11 +1020,24 @@ def experts_leg(Q, torch, np, synth, dev, stream):
                 ws, ws1 = Q.workspace(q, Mx, E, device=dev), Q.workspace(1, Mx, E, device=dev)
                 t_q = flushed(lambda: Q.qalg_forward_batched(X, W, tau, q, Y=Y, ws=ws, stream=stream))
                 t_1 = flushed(lambda: Q.qalg_forward_batched(X, W, tau1, 1, Y=Y, ws=ws1, stream=stream))
+                t_2s = t_mk = None
+                if Mx >= 8:
+                    # section 5.3's second schedule (diagonal maps over all rows, then the strips)
+                    ws2 = Q.workspace(q, Mx, E, device=dev, two_stage_N=N)
+                    t_2s = flushed(lambda: Q.qalg_forward_batched(X, W, tau, q, Y=Y, ws=ws2, stream=stream,
+                                                                  flags=Q.QALG_FLAG_TWO_STAGE))
+                    del ws2
+                    t_mk = flushed(lambda: Q.qalg_forward_batched(X, W, tau, q, Y=Y, ws=ws, stream=stream,
+                                                                  flags=Q.QALG_FLAG_MASKED))
                 flop = 2.0 * rho(q) * E * Mx * K * N
                 wblocks = sum(q + (q - 1) * len(set(int(t) for t in taus[e])) for e in range(E))
                 byts = wblocks * s * r * 2 + E * Mx * (K + N) * 2
                 res[f"{K}x{N}_q{q}_M{Mx}"] = {
                     "ms": round(t_q, 4), "q1_ms": round(t_1, 4), "speedup_vs_q1": round(t_1 / t_q, 3),
+                    "two_stage_ms": round(t_2s, 4) if t_2s else None,
+                    "two_stage_speedup_vs_q1": round(t_1 / t_2s, 3) if t_2s else None,
+                    "masked_ms": round(t_mk, 4) if t_mk else None,
+                    "masked_speedup_vs_q1": round(t_1 / t_mk, 3) if t_mk else None,
                     "algebra_tflops": round(flop / (t_q * 1e-3) / 1e12, 1),
                     "GBs": round(byts / (t_q * 1e-3) / 1e9, 1)}
         del W, X_all

@@ -25,7 +25,8 @@ __all__ = [
     "QalgError", "lib", "lib_path",
     "QALG_F32", "QALG_BF16", "QALG_FLAG_INDEX_READY", "QALG_FLAG_FORCE_TILED",
     "QALG_FLAG_FORCE_SMALL_M", "QALG_FLAG_LAW_TENSOR",
-    "QALG_FLAG_TILE_M64", "QALG_FLAG_TILE_M128", "QALG_FLAG_TILE_M256", "QALG_SCHEDULE_CYCLIC", "QALG_SCHEDULE_INTERVAL", "QALG_MAX_Q",
+    "QALG_FLAG_TILE_M64", "QALG_FLAG_TILE_M128", "QALG_FLAG_TILE_M256", "QALG_FLAG_TWO_STAGE", "QALG_FLAG_MASKED",
+    "qalg_workspace_bytes_two_stage", "QALG_SCHEDULE_CYCLIC", "QALG_SCHEDULE_INTERVAL", "QALG_MAX_Q",
     "qalg_version", "qalg_status_string", "qalg_workspace_bytes", "qalg_workspace_bytes_dw", "qalg_index_layout",
     "qalg_type_schedule", "qalg_build_index", "qalg_build_index_batched",
     "qalg_forward", "qalg_forward_graph", "qalg_backward_dx", "qalg_backward_dw", "qalg_forward_batched",
@@ -46,6 +47,8 @@ QALG_FLAG_LAW_TENSOR = 8
 QALG_FLAG_TILE_M64 = 16
 QALG_FLAG_TILE_M128 = 32
 QALG_FLAG_TILE_M256 = 64
+QALG_FLAG_TWO_STAGE = 128
+QALG_FLAG_MASKED = 256
 QALG_SCHEDULE_CYCLIC = 0
 QALG_SCHEDULE_INTERVAL = 1
 QALG_MAX_Q = 512
@@ -66,6 +69,7 @@ _SIGS = {
     "qalg_version": (ctypes.c_int, []),
     "qalg_workspace_bytes": (_c_size, [_c_i32, _c_i64]),
     "qalg_workspace_bytes_dw": (_c_size, [_c_i32, _c_i64, _c_i64, _c_i64]),
+    "qalg_workspace_bytes_two_stage": (_c_size, [_c_i32, _c_i64, _c_i64]),
     "qalg_index_layout": (ctypes.c_int, [_c_i32, _c_i64, ctypes.POINTER(_c_i64)]),
     "qalg_type_schedule": (ctypes.c_int, [_vp, _c_i64, _c_i32, _c_i32, _c_i64, _vp, _vp]),
     "qalg_build_index": (ctypes.c_int, [_vp, _c_i32, _c_i64, _vp, _c_size, _vp]),
@@ -147,6 +151,10 @@ def qalg_workspace_bytes_dw(q: int, M: int, K: int, N: int) -> int:
     return lib().qalg_workspace_bytes_dw(q, M, K, N)
 
 
+def qalg_workspace_bytes_two_stage(q: int, M: int, N: int) -> int:
+    return lib().qalg_workspace_bytes_two_stage(q, M, N)
+
+
 def qalg_index_layout(q: int, M: int) -> tuple[int, int, int, int]:
     out = (_c_i64 * 4)()
     _check("qalg_index_layout", lib().qalg_index_layout(q, M, out))
@@ -189,11 +197,14 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def workspace(q: int, M: int, E: int = 1, device="cuda", dw_shape=None):
+def workspace(q: int, M: int, E: int = 1, device="cuda", dw_shape=None, two_stage_N=None):
     """A device workspace of the size the projections need (uint8 tensor); with dw_shape = (K, N)
-    large enough for qalg_backward_dw to split its contraction (qalg_workspace_bytes_dw)."""
+    large enough for qalg_backward_dw to split its contraction (qalg_workspace_bytes_dw); with
+    two_stage_N = N large enough for the two-stage forward (qalg_workspace_bytes_two_stage)."""
     torch = _torch()
-    if dw_shape is not None and E == 1:
+    if two_stage_N is not None:
+        n = qalg_workspace_bytes_two_stage(q, M, two_stage_N) * E
+    elif dw_shape is not None and E == 1:
         n = qalg_workspace_bytes_dw(q, M, dw_shape[0], dw_shape[1])
     else:
         n = qalg_workspace_bytes(q, M) * E

@@ -2,10 +2,12 @@
 
 Times qalg_forward on one shape with every output-tile height the persistent
 forward offers (QALG_FLAG_TILE_M64 / M128 / M256), the register-staged tiled
-kernel (QALG_FLAG_FORCE_TILED) and the default choice, on seeded synthetic
-bf16 operands, and prints the times.  Section 5.3 and appendix F of arXiv
-2609.32814 calibrate tiles per shape the same way (a short sweep, then the
-chosen configuration).
+kernel (QALG_FLAG_FORCE_TILED), both few-rows schedules (section 5.3's
+two-stage schedule, QALG_FLAG_TWO_STAGE, and the masked tile over all rows,
+QALG_FLAG_MASKED) and the default choice, on seeded synthetic bf16 operands,
+and prints the times.  Section 5.3 and appendix F of arXiv 2609.32814
+calibrate tiles and both schedules per shape the same way (a short sweep,
+then the chosen configuration).
 
     python -m gemm_qalg_forward_amd.calibrate --M 2048 --K 4096 --N 12288 --q 32
 """
@@ -22,6 +24,8 @@ CANDIDATES = [
     ("persistent_m128", Q.QALG_FLAG_TILE_M128),
     ("persistent_m256", Q.QALG_FLAG_TILE_M256),
     ("tiled", Q.QALG_FLAG_FORCE_TILED),
+    ("two_stage", Q.QALG_FLAG_TWO_STAGE),
+    ("masked", Q.QALG_FLAG_MASKED),
 ]
 
 
@@ -36,10 +40,11 @@ def sweep(M: int, K: int, N: int, q: int, law: int = 0, reps: int = 20, warmup: 
     W = (torch.randn(K, N, device="cuda", generator=g) * K ** -0.5).to(torch.bfloat16)
     tau = (torch.arange(M, device="cuda") % q).to(torch.int32)
     Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    ws = Q.qalg_build_index(tau, q, stream=stream)
+    ws = Q.workspace(q, M, two_stage_N=N)   # room for the two-stage schedule's diagonal maps
+    Q.qalg_build_index(tau, q, ws=ws, stream=stream)
     runs = {}
     for name, flag in CANDIDATES:
-        if law and flag == Q.QALG_FLAG_FORCE_TILED:
+        if law and flag in (Q.QALG_FLAG_FORCE_TILED, Q.QALG_FLAG_TWO_STAGE, Q.QALG_FLAG_MASKED):
             continue
         fl = flag | law | Q.QALG_FLAG_INDEX_READY
 

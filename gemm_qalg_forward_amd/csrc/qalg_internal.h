@@ -81,6 +81,7 @@ struct ProblemDesc {
   const int64_t* in_widths = nullptr;   // unequal group widths (host arrays of q; sums K and N)
   const int64_t* out_widths = nullptr;
   void* gu = nullptr;                   // gated forward: also store the merged pre-activations here
+  void* fwd_diag = nullptr;             // two-stage forward: fp32 diagonal maps, M x N per problem
 };
 
 // dW's split contraction (register-staged path): at most this many partial tiles per output tile
@@ -92,6 +93,10 @@ constexpr int kMaxWidthGroups = 64;
 // cyclic (a persistent kernel launched beside it covers that case).
 hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s, bool skip_cyclic = false);
 hipError_t launch_tiled_f32(const ProblemDesc& p, hipStream_t s);
+// the two-stage forward (diagonal maps over all rows into p.fwd_diag, then the strips); bf16, complete law
+hipError_t launch_tiled_two_stage_bf16(const ProblemDesc& p, hipStream_t s);
+// the masked forward (one tile over all rows, every block once, masked per row); bf16, complete law
+hipError_t launch_tiled_masked_bf16(const ProblemDesc& p, hipStream_t s);
 hipError_t launch_small_m_bf16(const ProblemDesc& p, hipStream_t s);
 bool small_m_supported(const ProblemDesc& p);
 // Persistent 256x256-tile forward (bf16, one problem); zeroes rows of out-of-range type itself.

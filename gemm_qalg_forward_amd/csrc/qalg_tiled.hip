@@ -30,6 +30,8 @@
 // (the weight-side tile as the first operand) so that each lane ends with
 // four consecutive output columns of one row; the lane halves exchange pieces
 // (v_permlane32_swap) so that each lane stores 16 contiguous bytes.
+#include <type_traits>
+
 #include "qalg_internal.h"
 
 namespace qalg {
@@ -81,6 +83,9 @@ struct Args {
   int tk[kMaxWidthGroups + 1], tn[kMaxWidthGroups + 1];
   float* part;                       // dW split contraction: fp32 partial tiles [splits][K][N]
   int splits;                        // dW: workgroups per output tile (1: no split)
+  float* D;                          // two-stage forward: the diagonal maps of every row, fp32 [M][N]
+  const int32_t* tau;                // kMasked forward: the row types (E x M)
+  int64_t strideD;                   // elements between problems' D
 };
 
 // Recursive law Q_2^(x)L (appendix C, eq 36): b is in the support of (i, j)
@@ -171,9 +176,26 @@ __device__ __forceinline__ int find_type(const int32_t* tile_off, int q, int rt)
 // kLawWidths: the complete-graph law Q_q on groups of unequal widths (eq 18)
 constexpr int kLawComplete = 0, kLawTensor = 1, kLawGraph = 2, kLawWidths = 3;
 
-template <Op OP, class C, int LAW = kLawComplete>
+// Forward schedules (section 5.3): kFused sums both endpoint products of an
+// output tile in registers.  The two-stage schedule computes the diagonal maps
+// over all rows first (kDiag: D[m, g_j] = X[m, g_j] W_jj for every typed row m,
+// row tiles across types, so each W_jj tile is read once for all rows; fp32
+// into D), then the type-dependent maps (kStrip: for a type-i row tile and
+// output group j != i, X[I_i, g_i] W_ij; each off-diagonal block is read once,
+// by the one type that uses it), whose epilogue adds D and rounds once.
+//
+// kMasked (few rows per type): one tile over all M rows in their own order and
+// the whole contraction, the weight column tile read once, block by block; the
+// activations of block b reach only the rows that use it (type b, or all rows
+// when b is the output group j: eq 17's x_i W_ij + x_j W_jj), the others are
+// zeroed in registers.  Every weight block is read once per column tile, as in
+// the plain product, and nothing is re-read per type.
+constexpr int kFused = 0, kDiag = 1, kStrip = 2, kMasked = 3;
+
+template <Op OP, class C, int LAW = kLawComplete, int SCHED = kFused>
 __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
   constexpr bool TENSOR = LAW == kLawTensor, GRAPH = LAW == kLawGraph, WIDTHS = LAW == kLawWidths;
+  static_assert(SCHED == kFused || (OP == Op::Fwd && LAW == kLawComplete), "two-stage: complete-law forward");
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, KCH = C::KCH, T = C::THREADS;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
 
@@ -266,10 +288,25 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
     const int w = xcd_remap(blockIdx.x, gridDim.x, a.n_ct);
     const int rt = w / a.n_ct;
     const int ct = w - rt * a.n_ct;
-    if (rt >= tile_off[q]) return;
-    const int i = find_type(tile_off, q, rt);
-    out_first = offsets[i] + (rt - tile_off[i]) * BM;
-    m_cnt = min(BM, offsets[i + 1] - out_first);
+    int i;
+    if constexpr (SCHED == kMasked) {
+      // row tiles over all M rows in order (no index gather)
+      out_first = rt * BM;
+      if (out_first >= a.M) return;
+      m_cnt = min(BM, a.M - out_first);
+      i = 0;
+    } else if constexpr (SCHED == kDiag) {
+      // row tiles over all typed rows (the index lists them type by type)
+      out_first = rt * BM;
+      if (out_first >= offsets[q]) return;
+      m_cnt = min(BM, offsets[q] - out_first);
+      i = 0;
+    } else {
+      if (rt >= tile_off[q]) return;
+      i = find_type(tile_off, q, rt);
+      out_first = offsets[i] + (rt - tile_off[i]) * BM;
+      m_cnt = min(BM, offsets[i + 1] - out_first);
+    }
     if constexpr (WIDTHS) {
       if constexpr (OP == Op::Fwd) {
         // output group j of widths r_j; segments X[., g_i] W[g_i, .] (s_i) and X[., g_j] W[g_j, .] (s_j)
@@ -300,6 +337,15 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
       nseg = (j == i) ? 1 : 2;
       segA0 = segB0 = i * a.s;   // X columns / W rows of group i
       segA1 = segB1 = j * a.s;   // X columns / W rows of group j
+      if constexpr (SCHED == kMasked) {
+        nseg = q;                // every block b = 0 .. q-1, masked per row
+        tb_j = j;
+      } else if constexpr (SCHED == kDiag) {
+        nseg = 1;                // X[., g_j] W_jj
+        segA0 = segB0 = j * a.s;
+      } else if constexpr (SCHED == kStrip) {
+        nseg = (j == i) ? 0 : 1; // X[I_i, g_i] W_ij (the diagonal term is in D)
+      }
       if constexpr (GRAPH) {
         if (j != i && !graph_edge(a.adj, i, j)) nseg = 0;  // absent edge: zero output block
       }
@@ -398,6 +444,8 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
   constexpr int B_BASE = DW_SPLIT ? T - C::B_BLOCKS : 0;  // first thread of the dY blocks
 
   const uint16_t* a_ptr[A_PER];  // K-major: row base (contraction offset added per step)
+  int a_typ[A_PER];              // kMasked: the row's type (-1: padding row or out of range)
+  bool a_use[A_PER];             // kMasked: whether the loaded step reaches the row
   int a_kc[A_PER];               // K-major: chunk; MN-major: block's k-chunk
   int a_mn[A_PER];               // K-major: local row; MN-major: local first column (x8)
   bool a_on[A_PER];
@@ -415,7 +463,11 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
       a_mn[u] = rl;
       a_kc[u] = kc;
       const int slot = out_first + min(rl, m_cnt - 1);
-      const int grow = rows[slot];
+      const int grow = SCHED == kMasked ? slot : rows[slot];
+      if constexpr (SCHED == kMasked) {
+        const int t = (rl < m_cnt) ? a.tau[int64_t(e) * a.M + grow] : -1;
+        a_typ[u] = (t >= 0 && t < q) ? t : -1;  // an out-of-range row takes no block: a zero output row
+      }
       const int64_t ld = (OP == Op::Fwd) ? a.K : a.N;
       a_ptr[u] = Ag + int64_t(grow) * ld;  // + segment column + k offset per step
     } else {
@@ -459,6 +511,12 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
     seg_len = sg ? this_seg_len1 : this_seg_len;
     krows_s = krows;
     segA0_s = segA0;
+    if constexpr (SCHED == kMasked) {
+      // block n = kt / kts; sg carries n (the segment column is n s)
+      sg = kt / kts;
+      k0 = (kt - sg * kts) * BK;
+      segA0_s = sg * a.s;
+    }
     if constexpr (GRAPH) {
       if constexpr (OP == Op::Dx) {
         if (tb_b == tb_j) {  // member groups visited in increasing order as kt grows
@@ -518,11 +576,17 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
     for (int u = 0; u < A_PER; ++u) {
       if constexpr (A_KMAJOR) {
         const int kk = k0 + a_kc[u] * 8;
-        const int col = (sg ? segA1 : segA0_s) + kk;
+        const int col = SCHED == kMasked ? segA0_s + kk : (sg ? segA1 : segA0_s) + kk;
         if (a_on[u] && kk < seg_len)
           ra[u][0] = *reinterpret_cast<const u32x4*>(a_ptr[u] + col);
         else
           ra[u][0] = (u32x4){0u, 0u, 0u, 0u};
+        if constexpr (SCHED == kMasked) {
+          // block sg reaches rows of type sg, and every row when sg is the output
+          // group; the others are zeroed when the step is stored to LDS (using
+          // the loaded value here would wait for the load at once)
+          a_use[u] = a_typ[u] >= 0 && (a_typ[u] == sg || sg == tb_j);
+        }
       } else {  // dW: 8 gathered contraction rows x 8 output rows
         const int kk = k0 + a_kc[u] * 8;
         const bool on = a_on[u] && a_mn[u] < m_cnt;
@@ -547,7 +611,7 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
           rb[u][0] = (u32x4){0u, 0u, 0u, 0u};
       } else if constexpr (OP == Op::Fwd) {  // W rows of the segment, 8 output columns
         const int kk = k0 + b_kc[u] * 8;
-        const int wrow = (sg ? segB1 : segB0) + kk;
+        const int wrow = SCHED == kMasked ? sg * a.s + kk : (sg ? segB1 : segB0) + kk;
         const bool on = b_on[u] && b_mn[u] < n_cnt;
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) {
@@ -609,7 +673,9 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
       if (!a_on[u]) continue;
       if constexpr (A_KMAJOR) {
         const int rl = a_mn[u];
-        *reinterpret_cast<u32x4*>(As + rl * BK + swz(rl, a_kc[u], KCH) * 8) = ra[u][0];
+        u32x4 v = ra[u][0];
+        if constexpr (SCHED == kMasked) v = a_use[u] ? v : (u32x4){0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(As + rl * BK + swz(rl, a_kc[u], KCH) * 8) = v;
       } else {
         u32x4 t8[8];
         transpose8x8(ra[u], t8);
@@ -734,16 +800,55 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
       return;
     }
   }
+  if constexpr (SCHED == kDiag) {
+    // fp32 diagonal maps into D (rows at their own positions)
+    float* Dg = a.D + int64_t(e) * a.strideD;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int ml = wm * C::WTM + fm * 32 + l32;
+      if (ml >= m_cnt) continue;
+      float* drow = Dg + int64_t(rows[out_first + ml]) * a.N + n0;
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int nl = wn * C::WTN + fn * 32 + g * 8 + lhi * 4;
+          if (nl < n_cnt) {
+            const f32x16& v = acc[fm][fn];
+            *reinterpret_cast<float4*>(drow + nl) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+          }
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
     const int ml = wm * C::WTM + fm * 32 + l32;
     if (ml >= m_cnt) continue;
     int64_t grow;
-    if constexpr (OP == Op::Dw)
+    if constexpr (OP == Op::Dw || SCHED == kMasked)
       grow = out_first + ml;
     else
       grow = rows[out_first + ml];
     uint16_t* crow = Cg + grow * ldc + n0;
+    if constexpr (SCHED == kStrip) {
+      // add the row's diagonal map from D: the output is the sum of both
+      // endpoint products, rounded once below
+      const float* drow = a.D + int64_t(e) * a.strideD + grow * a.N + n0;
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int nl = wn * C::WTN + fn * 32 + g * 8 + lhi * 4;
+          if (nl < n_cnt) {
+            const float4 d = *reinterpret_cast<const float4*>(drow + nl);
+            acc[fm][fn][4 * g] += d.x;
+            acc[fm][fn][4 * g + 1] += d.y;
+            acc[fm][fn][4 * g + 2] += d.z;
+            acc[fm][fn][4 * g + 3] += d.w;
+          }
+        }
+    }
     // lane (l32, lhi) holds columns g*8 + lhi*4 .. +3 of each 32-column block;
     // v_permlane32_swap on the packed pieces of groups 2gp and 2gp + 1 (lanes
     // 32-63 of the first exchanged with lanes 0-31 of the second; both lanes of
@@ -975,14 +1080,17 @@ int64_t dw_tiles(const ProblemDesc& p, const Args& a) {
   return p.in_widths != nullptr ? int64_t(a.tk[p.q]) * a.tn[p.q] : int64_t(p.q) * p.q * a.tm_dw * a.tn_dw;
 }
 
-dim3 grid_for(const ProblemDesc& p, const Args& a, int bm) {
+dim3 grid_for(const ProblemDesc& p, const Args& a, int bm, int sched = kFused) {
   if (p.op == Op::Dw) return dim3(unsigned(dw_tiles(p, a) * (a.splits > 1 ? a.splits : 1)), unsigned(p.E));
-  // worst case over all type splits: sum_i ceil(M_i / BM) <= ceil(M / BM) + q - 1
-  const int64_t rt = (p.M + bm - 1) / bm + p.q - 1;
+  // row tiles over all rows (masked and diagonal schedules): exactly ceil(M / BM);
+  // tiles of one type each: at most sum_i ceil(M_i / BM) <= ceil(M / BM) + q - 1.
+  // (Sizing the former like the latter would leave most workgroups idle, and
+  // the XCD remap would put all the busy ones on one XCD.)
+  const int64_t rt = (p.M + bm - 1) / bm + (sched == kMasked || sched == kDiag ? 0 : p.q - 1);
   return dim3(unsigned(rt * a.n_ct), unsigned(p.E));
 }
 
-template <Op OP, class C>
+template <Op OP, class C, int SCHED = kFused>
 hipError_t launch_cfg(const ProblemDesc& p, hipStream_t s, bool skip_cyclic) {
   Args a = make_args(p, C::BM, C::BN);
   a.skip_cyclic = skip_cyclic ? 1 : 0;
@@ -997,8 +1105,15 @@ hipError_t launch_cfg(const ProblemDesc& p, hipStream_t s, bool skip_cyclic) {
     a.part = static_cast<float*>(p.dw_part);
   }
   a.adj = p.graph_adj;
-  const dim3 g = grid_for(p, a, C::BM);
+  const dim3 g = grid_for(p, a, C::BM, SCHED);
   if (g.x == 0) return hipSuccess;
+  if constexpr (SCHED != kFused) {
+    a.D = static_cast<float*>(p.fwd_diag);
+    a.strideD = p.M * p.N;
+    a.tau = p.tau;
+    hipLaunchKernelGGL((tiled_bf16_kernel<Op::Fwd, C, kLawComplete, SCHED>), g, dim3(C::THREADS), 0, s, a);
+    return hipGetLastError();
+  }
   if constexpr (OP != Op::Fwd) {
     if (p.law_L > 0) {
       hipLaunchKernelGGL((tiled_bf16_kernel<OP, C, kLawTensor>), g, dim3(C::THREADS), 0, s, a);
@@ -1116,6 +1231,42 @@ hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s, bool skip_cycl
       return launch_cfg<Op::Dw, Cfg64>(p, s, skip_cyclic);
   }
   return hipErrorInvalidValue;
+}
+
+// The two-stage forward (section 5.3's second schedule): the diagonal maps
+// over all typed rows into p.fwd_diag (fp32, M x N per problem), then the
+// type-dependent maps with the diagonal added in the epilogue.  Row tiles of
+// the first stage span all rows (its height from M), the second stage's from
+// the rows per type, each as in the fused forward.
+hipError_t launch_tiled_two_stage_bf16(const ProblemDesc& p, hipStream_t s) {
+  const int64_t per_type = (p.M + p.q - 1) / p.q;
+  const int bn = fwd_small_bn(p.N / p.q);
+  auto pick = [&](int64_t rows, auto sched) -> hipError_t {
+    constexpr int SC = decltype(sched)::value;
+    if (rows >= 128) return launch_cfg<Op::Fwd, Cfg128, SC>(p, s, false);
+    if (bn == 256) return rows >= 48 ? launch_cfg<Op::Fwd, CfgN64, SC>(p, s, false)
+                                     : launch_cfg<Op::Fwd, CfgN32, SC>(p, s, false);
+    if (bn == 128) return rows >= 48 ? launch_cfg<Op::Fwd, CfgM64, SC>(p, s, false)
+                                     : launch_cfg<Op::Fwd, CfgM32, SC>(p, s, false);
+    return rows >= 48 ? launch_cfg<Op::Fwd, Cfg64, SC>(p, s, false) : launch_cfg<Op::Fwd, Cfg32, SC>(p, s, false);
+  };
+  const hipError_t e = pick(p.M, std::integral_constant<int, kDiag>{});
+  if (e != hipSuccess) return e;
+  return pick(per_type, std::integral_constant<int, kStrip>{});
+}
+
+// The masked forward for few rows per type (kMasked): one tile per (row tile
+// of all rows, column tile), the whole contraction, blocks masked per row.
+hipError_t launch_tiled_masked_bf16(const ProblemDesc& p, hipStream_t s) {
+  const int bn = fwd_small_bn(p.N / p.q);
+  const int64_t rows = p.M;
+  constexpr int SC = kMasked;
+  if (rows >= 128) return launch_cfg<Op::Fwd, Cfg128, SC>(p, s, false);
+  if (bn == 256) return rows >= 48 ? launch_cfg<Op::Fwd, CfgN64, SC>(p, s, false)
+                                   : launch_cfg<Op::Fwd, CfgN32, SC>(p, s, false);
+  if (bn == 128) return rows >= 48 ? launch_cfg<Op::Fwd, CfgM64, SC>(p, s, false)
+                                   : launch_cfg<Op::Fwd, CfgM32, SC>(p, s, false);
+  return rows >= 48 ? launch_cfg<Op::Fwd, Cfg64, SC>(p, s, false) : launch_cfg<Op::Fwd, Cfg32, SC>(p, s, false);
 }
 
 hipError_t launch_tiled_f32(const ProblemDesc& p, hipStream_t s) {

@@ -112,7 +112,32 @@ enum {
      * or of 192, and every persistent shape K / q a multiple of 64). */
     QALG_FLAG_TILE_M64 = 16,
     QALG_FLAG_TILE_M128 = 32,
-    QALG_FLAG_TILE_M256 = 64
+    QALG_FLAG_TILE_M256 = 64,
+    /* Section 5.3's second forward schedule (qalg_forward, qalg_forward_batched;
+     * bf16, the complete law Q_q): the diagonal maps over all rows first,
+     * D[m, g_j] = x_j W_jj for every typed row m and group j, with row tiles
+     * that span the types, so that each diagonal block is read once for all
+     * rows; then the type-dependent maps, X[I_i, g_i] W_ij for j != i, whose
+     * epilogue adds D and rounds once (the same one-rounding result as the
+     * fused schedule, up to the fp32 summation order).  Pays off when each
+     * type has few rows (the fused schedule reads W_jj once per type).  D is
+     * fp32 in the workspace, which must hold qalg_workspace_bytes_two_stage
+     * bytes per problem (QALG_ERR_WORKSPACE otherwise); M N below 2^31
+     * (QALG_ERR_DIM); with QALG_FLAG_LAW_TENSOR, the forced paths or a tile
+     * flag: QALG_ERR_ARG. */
+    QALG_FLAG_TWO_STAGE = 128,
+    /* The few-rows forward (qalg_forward, qalg_forward_batched; bf16, the
+     * complete law): one output tile spans all M rows of a problem in their
+     * own order and runs the whole contraction, weight block by weight block,
+     * each block's activations reaching only the rows that use it (rows of
+     * type b for block b, every row for the output group's own block j,
+     * eq 17); the others are zero.  Each weight column tile is read once, as
+     * in the plain product, where the fused schedule re-reads W_jj once per
+     * type.  For a handful of rows per type (the few-rows regime of section
+     * 5.2 and 5.3); the matrix-core work is that of the dense product.  With
+     * QALG_FLAG_LAW_TENSOR, QALG_FLAG_TWO_STAGE, the forced paths or a tile
+     * flag: QALG_ERR_ARG. */
+    QALG_FLAG_MASKED = 256
 };
 
 /* Position-type schedules for qalg_type_schedule. */
@@ -148,6 +173,14 @@ size_t qalg_workspace_bytes(int32_t q, int64_t M);
  * within the fp32 summation order).  Returns 0 for invalid sizes.
  */
 size_t qalg_workspace_bytes_dw(int32_t q, int64_t M, int64_t K, int64_t N);
+
+/*
+ * Workspace per problem that the two-stage forward (QALG_FLAG_TWO_STAGE) needs:
+ * qalg_workspace_bytes(q, M) plus the fp32 diagonal maps (M x N).  A batched
+ * call of E problems needs E times this (the E indices first, then the E
+ * diagonal buffers).  0 for invalid sizes.
+ */
+size_t qalg_workspace_bytes_two_stage(int32_t q, int64_t M, int64_t N);
 
 /*
  * Type schedule (section 4: a token at position p selects row i = tau(p) by a

@@ -268,7 +268,7 @@ def test_tensor_law_flag_errors_are_synchronous(lib):
     assert fwd(flags=T | Q.QALG_FLAG_FORCE_SMALL_M) == 8
     assert fwd(K=128) == 4                         # K / q = 32: not a multiple of 64
     assert fwd(N=320) == 4                         # N / q = 80: no tile width divides it
-    assert fwd(flags=128) == 8                     # unknown flag
+    assert fwd(flags=512) == 8                     # unknown flag
     # dX and dW accept the law (bf16, one bank); the checks still come first
     dx = lib.qalg_backward_dx(FAKE, FAKE, FAKE, 6, 64, 384, 768, FAKE, 1, FAKE, 1 << 20, T, None)
     dw = lib.qalg_backward_dw(FAKE, FAKE, FAKE, 4, 64, 256, 512, FAKE, 0, FAKE, 1 << 20, T, None)
@@ -386,3 +386,19 @@ def test_attention_decode_argument_errors_are_synchronous(lib):
     assert Q.qalg_attention_decode_workspace_bytes(2, 4, 0, 128) == 0
     # the offset prefill: a negative first position is refused
     assert lib.qalg_attention_forward_at(FAKE, FAKE, FAKE, 2, 1, 8, 64, 2, -1, FAKE, 1, 0, None) == 2
+
+
+def test_two_stage_flag_errors_are_synchronous(lib):
+    ts = 128
+    q, M, K, N = 2, 64, 16, 16
+    need = Q.qalg_workspace_bytes_two_stage(q, M, N)
+    assert need == Q.qalg_workspace_bytes(q, M) + (M * N * 4 + 255) // 256 * 256
+    assert Q.qalg_workspace_bytes_two_stage(0, M, N) == 0 and Q.qalg_workspace_bytes_two_stage(q, M, 0) == 0
+    base = Q.qalg_workspace_bytes(q, M)
+    assert call_fwd(lib, flags=ts, wsb=base) == 6                      # no room for the diagonal maps
+    assert call_fwd(lib, flags=ts, dt=0, wsb=need) == 8                 # bf16 only
+    assert call_fwd(lib, flags=ts | 8, wsb=need) == 8                   # not with the recursive law
+    assert call_fwd(lib, flags=ts | 2, wsb=need) == 8                   # not with a forced path
+    assert call_fwd(lib, flags=ts | 16, wsb=need) == 8                  # not with a tile flag
+    assert call_fwd(lib, flags=ts, fn="qalg_backward_dx", wsb=need) == 8
+    assert lib.qalg_forward_batched(2, FAKE, FAKE, FAKE, q, M, K, N, FAKE, 1, FAKE, need, ts, None) == 6
