@@ -229,12 +229,10 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
   }
   if (e != hipSuccess) return QALG_ERR_HIP;
 
-  if (dtype == QALG_BF16 && p.law_L == 0 && qalg::grad_persistent_supported(p)) {
-    // which of the two runs depends on the index (cyclic schedule or not),
-    // known only on the device: both are enqueued, the other returns at once
-    e = qalg::launch_grad_persistent_bf16(p, s);
-    if (e != hipSuccess) return QALG_ERR_HIP;
-    return hip_status(qalg::launch_tiled_bf16(p, s, /*skip_cyclic=*/true));
+  if (dtype == QALG_BF16 && qalg::grad_persistent_supported(p)) {
+    // the persistent gradients read the index on the device: closed-form rows
+    // for a cyclic schedule, the row list otherwise
+    return hip_status(qalg::launch_grad_persistent_bf16(p, s));
   }
   e = dtype == QALG_BF16 ? qalg::launch_tiled_bf16(p, s) : qalg::launch_tiled_f32(p, s);
   return hip_status(e);

@@ -41,6 +41,26 @@ __device__ __forceinline__ void copy16_to_lds(const char* gbase, uint32_t voff, 
                : "memory", "m0");
 }
 
+// The same copy through a buffer resource (gfx950 buffer_load_dwordx4 with
+// lds): a lane whose offset lies at or past the resource's byte count reads
+// nothing from memory and writes zeros into its LDS piece.  The resource is
+// wave-uniform (four scalar registers, see buffer_rsrc).
+__device__ __forceinline__ void copy16_to_lds_buf(u32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+// Raw buffer resource over `bytes` bytes at base (no stride, no swizzle): the
+// hardware range check returns zeros for offsets at or past `bytes`.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return (u32x4){uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a)))),
+                 uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffffu))),
+                 uint32_t(__builtin_amdgcn_readfirstlane(int(bytes))), 0x00020000u};
+}
+
 // Workgroup barrier ordering LDS only (the stage copies are waited for
 // explicitly; global stores need no ordering here).
 __device__ __forceinline__ void lds_barrier() {
@@ -91,6 +111,32 @@ __device__ __forceinline__ int find_group(P tile_off, int q, int rt) {
       hi = mid;
   }
   return lo;
+}
+
+// Recursive law Q_2^(x)L (appendix C, eq 36): types and groups are L-bit
+// strings.  binom_small(L, d) counts the masks with d of L bits set,
+// unrank_mask(jj, d, L) is the jj-th of them in ascending order, and
+// law_member(from, mask, n, L) is the L-bit string equal to `from` on the bits
+// of `mask` and to the bits of n, in order, on the others (the n-th member of a
+// segment list whose fixed bits are `mask`).
+__device__ __forceinline__ int binom_small(int L, int d) {
+  int c = 1;
+  for (int k = 0; k < d; ++k) c = c * (L - k) / (k + 1);
+  return c;
+}
+__device__ __forceinline__ int unrank_mask(int jj, int d, int L) {
+  for (int m = 0; m < (1 << L); ++m)
+    if (__builtin_popcount(m) == d && jj-- == 0) return m;
+  return 0;
+}
+__device__ __forceinline__ int law_member(int fixed_from, int fixed_mask, int n, int L) {
+  int g = fixed_from & fixed_mask;
+  for (int k = 0; k < L; ++k)
+    if (!((fixed_mask >> k) & 1)) {
+      if (n & 1) g |= 1 << k;
+      n >>= 1;
+    }
+  return g;
 }
 
 // Type index of a cyclic schedule (tau[m] = (o + m) mod q for every row m),

@@ -161,18 +161,8 @@ struct Tile {
 // and output group j of a type-i row sums x_b W_bj over every b whose bits each
 // equal i's or j's (eq 36), i.e. b = (i & ~m) | (any subset of m), m = i ^ j:
 // 2^popcount(m) segments.  Tiles fall in L + 1 classes by d = popcount(m), with
-// C(L, d) output groups per type and 2^d segments each.
-__device__ __forceinline__ int binom_small(int L, int d) {
-  int c = 1;
-  for (int k = 0; k < d; ++k) c = c * (L - k) / (k + 1);
-  return c;
-}
-// the jj-th L-bit mask (ascending) with d bits set
-__device__ __forceinline__ int unrank_mask(int jj, int d, int L) {
-  for (int m = 0; m < (1 << L); ++m)
-    if (__builtin_popcount(m) == d && jj-- == 0) return m;
-  return 0;
-}
+// C(L, d) output groups per type and 2^d segments each (binom_small and
+// unrank_mask enumerate them).
 // scatter the low bits of n into the set bits of m
 __device__ __forceinline__ int deposit_bits(int n, int m, int L) {
   int b = 0;

@@ -1,48 +1,59 @@
-// Persistent matrix-core gradients of the row-typed Q_q projection (bf16 in,
-// fp32 accumulate, bf16 out) for gfx950, cyclic schedules.
+// Persistent matrix-core gradients of the row-typed projection (bf16 in, fp32
+// accumulate, bf16 out) for gfx950: the complete law Q_q and the recursive law
+// Q_2^(x)L, on any schedule.
 //
-// Paper: arXiv 2609.32814, appendix B (eq 31-35).  For a row of type i:
+// Paper: arXiv 2609.32814, appendix B (eq 31-35) and appendix C (eq 36).  For
+// the complete law and a row of type i:
 //   dx_i = sum_j dy_j W_ij^T,   dx_k = dy_k W_kk^T (k != i)             (eq 31-32)
 //   dW_jj += x_j^T dy_j (every row),  dW_ij += x_i^T dy_j (rows of type i)  (eq 33-35)
+// Under the recursive law, b feeds output group j of a type-i row when every
+// bit of b equals i's or j's; transposed, dX[I_i, g_k] sums over the output
+// groups agreeing with k wherever k differs from i, and dW[g_b, g_j] over the
+// rows of the types agreeing with b wherever b differs from j.
 // Section 5.3: separate gradient kernels with one owner per output element,
 // so every dW / dX element is written once and the result does not depend on
 // scheduling.
 //
-// Output tiles are GEMM tiles of 256 x BN (BN = 256, 192 or 128):
-//   dX  tile (256 rows of type i, BN columns of input group k):
-//         k == i: dY[rows, :] W[cols, :]^T     (contraction N: a "long" tile)
-//         k != i: dY[rows, g_k] W[cols, g_k]^T (contraction r)
-//   dW  tile (256 features of group b, BN columns of output group j):
-//         b == j: X[:, f]^T dY[:, cols] over all M rows   ("long")
-//         b != j: the same over the rows of type b         (M / q rows)
-// The dX operands are both contraction-contiguous (dY rows; W rows, i.e. the
-// transpose of the weight block is read in place); the dW operands are both
-// row-major over the contraction (token rows of X and dY), read into LDS as is
-// and turned into MFMA fragments with the transposing LDS read.
+// Output tiles are GEMM tiles of BM x BN:
+//   dX  tile (256 rows of type i, BN columns of input group k), both operands
+//       contraction-contiguous (dY rows; W rows, the transposed weight block
+//       read in place).  Contraction: complete law, k == i: all N columns (a
+//       "long" tile); k != i: group k's r columns.  Recursive law: the
+//       2^(L - |i ^ k|) output groups above, r columns each.
+//   dW  tile (BM = 256 or 192 features of group b, BN columns of output group
+//       j), both operands row-major over the contraction (token rows of X and
+//       dY, read into LDS as is, turned into MFMA fragments by the transposing
+//       LDS read).  Contraction: complete law, b == j: every typed row
+//       ("long"); b != j: the rows of type b.  Recursive law: the rows of the
+//       2^(L - |b ^ j|) types above (all typed rows when b == j).
+// Rows of a type: for a cyclic schedule (detected by the index) the
+// progression (i - o) mod q + m q in closed form; otherwise the index's row
+// list.  dX tiles gather their rows (clamped into the type's rows; extra rows
+// are not stored).  dW contractions walk their types' rows 32 per k-step: each
+// wave looks up the 8 rows its copies carry as scalars and copies through a
+// buffer resource, so that the rows past a type's last one read as zeros.
 //
-// Pipeline (as in the forward): one workgroup per CU, operands copied
-// global -> LDS directly (global_load_lds_dwordx4); dX in two 64-deep stages
-// (contraction-major rows are whole 128-byte lines; the publishing barrier
-// after the third of four MFMA quarter steps), dW in four 32-deep stages
-// (copies three k-steps ahead; the barrier mid-step); MFMAs interleaved one by one with fragment reads (in the
-// order the MFMAs use them) and copies, v_mfma_f32_32x32x16_bf16 on 128x128
-// wave tiles, one RNE rounding, output restaged through LDS into whole pieces.
+// Pipeline: one workgroup per CU, operands copied global -> LDS directly; dX
+// in two 64-deep stages (contraction-major rows are whole 128-byte lines; the
+// publishing barrier after the third of four MFMA quarter steps), dW in four
+// 32-deep stages (copies three k-steps ahead; the barrier mid-step); MFMAs
+// interleaved one by one with fragment reads (in the order the MFMAs use them)
+// and copies, v_mfma_f32_32x32x16_bf16 on wave tiles of BM/2 x BN/2, one RNE
+// rounding, output restaged through LDS into whole pieces.
 //
-// Work balance.  Long tiles carry q times the contraction of short ones.  The
-// tiles of each XCD (a contiguous share of the long and of the short tiles)
-// are dealt to its workgroups round robin, longs first; workgroups that got
-// one long tile fewer then take up to q short tiles each before the remaining
-// short tiles are dealt round robin, so every workgroup ends with nearly the
-// same number of k-steps.  A dW long tile (a diagonal block, contracted over
-// all M rows) can still exceed the average load of a workgroup by far (at
-// q = 8: 512 k-steps against an average of 360); given fp32 scratch, its
-// contraction is cut into `splits` equal pieces dealt as separate long tiles,
-// each writing an fp32 partial tile, and a reduction sums the pieces in order
-// and rounds once (bitwise reproducible).
-//
-// Rows of type i are the arithmetic progression (i - o) mod q + k q of a
-// cyclic schedule (detected by the index); a launch on any other schedule
-// returns at once and the register-staged gradient kernels run instead.
+// Work balance.  Tiles fall in classes by contraction length: long and short
+// (complete law), or d = |i ^ k| (dX) and d = |b ^ j| (dW) under the
+// recursive law, 2^(L - d) segments each.  A dW tile's contraction runs over
+// many rows, and there are few dW tiles: each class's tiles are cut into
+// `np` pieces of nearly equal k-steps, each writing an fp32 partial tile that
+// a reduction sums in piece order and rounds once (bitwise reproducible).  The
+// units (tiles or pieces) of each XCD are a contiguous share of every class.
+// Complete law: its workgroups are dealt the long units round robin, then the
+// workgroups that got one long unit fewer take up to t_long / t_short short
+// units each before the rest are dealt round robin.  Recursive law: the
+// concatenation of the classes, longest first, round robin.
+#include <type_traits>
+
 #include "qalg.h"
 #include "qalg_device.h"
 #include "qalg_internal.h"
@@ -58,6 +69,7 @@ using namespace dev;
 // dW reads token rows that are whole lines already, and keeps 32-deep
 // k-steps in four stages (copies three k-steps ahead), measured faster there.
 constexpr int kBKDx = 64, kBKDw = 32;
+constexpr int kMaxClasses = 8;  // recursive law: d = 0 .. L, L <= 6
 
 template <int BM_, int BN_, bool A_KM_, bool B_KM_, int BK_, int STAGES_>
 struct GradCfg {
@@ -81,6 +93,9 @@ struct GradCfg {
   static constexpr int A_DMA = A_BYTES / 4096, B_DMA = B_BYTES / 4096;
   static constexpr int DMA = A_DMA + B_DMA;
   static_assert(STAGES * DMA < 64, "vmcnt range");
+  // row-major operands: wave w's copies carry contraction rows 8 w .. 8 w + 7
+  static_assert(A_KM || A_DMA * 64 == 8 * A_NCH, "8 contraction rows per wave (A)");
+  static_assert(B_KM || B_DMA * 64 == 8 * B_NCH, "8 contraction rows per wave (B)");
   // epilogue: each wave restages 32 rows x WTN columns of bf16 at a time in
   // its own share of a buffer behind the stages
   static constexpr int E_PITCH = WTN * 2;          // bytes per restaged row
@@ -97,145 +112,306 @@ struct GradCfg {
 template <int BK>
 __device__ __forceinline__ int swz_km(int row) { return BK == 64 ? swz_x128(row) : swz_x(row); }
 
+// Row id of the copy slot's contraction row, picked per lane from the 8
+// wave-uniform ids of the wave's rows: copy u of a row-major operand with NCH
+// pieces per row carries rows (64 u + lane) / NCH of the wave's 8.
+template <int NCH>
+__device__ __forceinline__ int pick_row(const int (&o)[8], int u, int lane) {
+  const int lo = (64 * u) / NCH, hi = (64 * u + 63) / NCH;
+  int v = o[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e)
+    if (e == lo) v = o[e];
+#pragma unroll
+  for (int e = 1; e < 8; ++e)
+    if (e > lo && e <= hi) v = lane >= e * NCH - 64 * u ? o[e] : v;
+  return v;
+}
+
+// offset that fails the buffer range check (resources never exceed 2 GiB)
+constexpr uint32_t kNoRow = 0x80000000u;
+
 struct GradArgs {
   const char* A;   // dX: dY;  dW: X
   const char* B;   // dX: W;   dW: dY
   char* C;         // dX: dX;  dW: dW
   const int32_t* ws;
-  int64_t off_offsets, off_tiles;
+  int64_t off_offsets, off_tiles, off_rows;
   int q, M, K, N, s, r;
-  int n_rt;        // dX: row tiles over all types (from the index; read on device)
+  int L;           // recursive law Q_2^(x)L; 0: the complete law
   int cpg;         // dX: column tiles per input group (s / BN); dW: per output group (r / BN)
-  int rpb;         // dW: row tiles per feature group (s / BM)
-  int splits;      // dW: pieces of each long tile's contraction (1: none)
-  float* part;     // dW, splits > 1: fp32 partial tiles [splits][K][N] (diagonal blocks only)
+  int rpb;         // dW: feature tiles per input group (s / BM)
+  int np[kMaxClasses];  // dW: pieces per tile of each class (1: not split)
+  int t_unit[2];   // dW, complete law: k-steps per unit of a short / long tile
+  float* part;     // dW: fp32 partial tiles [piece][K][N] of split tiles
   int64_t part_stride;  // floats per piece (K * N)
+  uint32_t a_bytes, b_bytes;  // dW: bytes of X and dY (buffer ranges)
 };
 
-// One output tile.
+// One unit of work: an output tile, or a piece of a split dW tile.
 struct GTile {
+  int cls;         // class (complete law: 1 long, 0 short; recursive law: d)
+  int type;        // dX: row type
   int out_row0;    // dX: rank of the first row within its type;  dW: first feature
-  int type;        // dX: row type;  dW: type whose rows are contracted (-1: all rows)
-  int m_cnt;       // valid output rows (dX ragged row tiles)
+  int first;       // dX: slot of the first row in the index's row list
+  int m_cnt;       // dX: valid output rows
   int n0;          // first output column
-  int c0;          // dX: first contraction column (in N);  dW: first k-step of a split piece
-  int nk;          // k-steps
-  int piece;       // dW: piece of a split long tile (fp32 partial output); -1 otherwise
+  int nk;          // k-steps of this unit
+  int c0;          // dW: first k-step of this piece within its tile's contraction
+  int piece;       // dW: piece of a split tile (fp32 partial output); -1 otherwise
+  int seg_from, seg_mask;  // segments: the n-th is law_member(seg_from, seg_mask, n, L)
+  int nseg;        // dX: 0 for one contiguous range from col0; dW: segments (0: all typed rows)
+  int col0;        // dX: first contraction column of a contiguous range
 };
 
-
-// Tile decode.  dX long tiles: (row tile, column tile of the row's own group);
-// short: (row tile, other group, column tile); both in groups of 4 row tiles
-// by all columns, row tile fastest.  dW long tiles: (block b == j, row tile,
-// column tile); short: (b, j != b, row tile, column tile), b slowest.
-template <class C, Op OP>
-__device__ __forceinline__ GTile decode(const GradArgs& a, const CycIndex& ix, bool is_long, int idx) {
-  GTile t;
-  if constexpr (OP == Op::Dx) {
-    constexpr int G = 4;
-    const int ncol = is_long ? a.cpg : (a.q - 1) * a.cpg;
-    const int span = G * ncol;
-    const int grp = idx / span, w = idx - grp * span;
-    const int first_rt = grp * G;
-    const int gm = min(a.n_rt - first_rt, G);
-    const int rt = first_rt + w % gm, ct = w / gm;
-    const int i = ix.group_of_tile(rt);
-    t.type = i;
-    t.out_row0 = (rt - ix.tiles_before(i)) * C::BM;
-    t.m_cnt = min(C::BM, ix.count(i) - t.out_row0);
-    int k, cc;
-    if (is_long) {
-      k = i;
-      cc = ct;
-    } else {
-      const int kk = ct / a.cpg;
-      cc = ct - kk * a.cpg;
-      k = kk < i ? kk : kk + 1;
-    }
-    t.n0 = k * a.s + cc * C::BN;
-    t.c0 = is_long ? 0 : k * a.r;
-    t.piece = -1;
-    t.nk = uni((is_long ? a.N : a.r) / C::BK);
-  } else {
-    const int tpb = a.rpb * a.cpg;
-    // split long tiles: consecutive indices are the pieces of one tile
-    int piece = -1;
-    if (is_long && a.splits > 1) {
-      const int tix = idx / a.splits;
-      piece = idx - tix * a.splits;
-      idx = tix;
-    }
-    const int blk = idx / tpb, w = idx - blk * tpb;
-    int b, j;
-    if (is_long) {
-      b = j = blk;
-    } else {
-      b = blk / (a.q - 1);
-      const int jj = blk - b * (a.q - 1);
-      j = jj < b ? jj : jj + 1;
-    }
-    const int rt = w % a.rpb, ct = w / a.rpb;
-    t.out_row0 = b * a.s + rt * C::BM;
-    t.m_cnt = C::BM;
-    t.n0 = j * a.r + ct * C::BN;
-    t.type = is_long ? -1 : b;
-    t.nk = uni((is_long ? a.M / a.splits : a.M / a.q) / C::BK);
-    t.c0 = piece > 0 ? piece * t.nk : 0;
-    t.piece = piece;
+// The u-th unit of a workgroup (slot g of the G on XCD xcd of nx), in closed
+// form from a few per-workgroup constants, so that a cursor carries nothing
+// but u through the pipeline and a lookup costs a handful of scalar ops.
+// Complete law: each XCD takes a contiguous share of the long and of the
+// short units; its workgroups take the longs round robin; those left one long
+// unit short then take up to t_long / t_short short units each, and the rest
+// of the shorts are dealt round robin (k-steps per workgroup end within one
+// unit of each other).  cls 1: long, 0: short.
+struct Deal2 {
+  int lx0, c0, sx0, sx1, g, G, light, lg, G_light, E, base;
+  __device__ void init(int n_long, int n_short, int t_long, int t_short, int xcd, int nx, int g_, int G_) {
+    g = g_;
+    G = G_;
+    lx0 = uni(int(int64_t(n_long) * xcd / nx));
+    const int lx1 = uni(int(int64_t(n_long) * (xcd + 1) / nx));
+    sx0 = uni(int(int64_t(n_short) * xcd / nx));
+    sx1 = uni(int(int64_t(n_short) * (xcd + 1) / nx));
+    const int nl = lx1 - lx0, ns = sx1 - sx0;
+    c0 = uni(g < nl ? (nl - g + G - 1) / G : 0);  // longs of this workgroup
+    const int rem = nl % G;
+    G_light = rem != 0 ? G - rem : 0;
+    const int e = t_short > 0 ? t_long / t_short : 0;
+    E = uni(rem != 0 ? min(e, ns / G_light) : 0);
+    base = uni(G_light * E);
+    light = rem != 0 && g >= rem;
+    lg = g - rem;
   }
-  return t;
-}
+  template <class A>
+  __device__ bool at(const A&, int u, int* cls, int* idx) const {
+    if (u < c0) {
+      *cls = 1;
+      *idx = lx0 + g + u * G;
+      return true;
+    }
+    u -= c0;
+    *cls = 0;
+    if (light) {
+      if (u < E) {
+        *idx = sx0 + lg + u * G_light;
+        return true;
+      }
+      u -= E;
+    }
+    *idx = sx0 + base + g + u * G;
+    return *idx < sx1;
+  }
+};
 
-template <class C, Op OP>
-__global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs a) {
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
+// Recursive law: each XCD takes a contiguous share of every class; its
+// workgroups take the concatenation, class 0 (the longest) first, round robin.
+// Class c holds mul * C(L, c) tiles (times np[c] pieces each for dW).
+struct DealC {
+  int L, mul, xcd, sh, g, G;
+  bool pieces;
+  template <class A>
+  __device__ void init(const A& a, int mul_, bool pieces_, int xcd_, int nx, int g_, int G_) {
+    L = a.L;
+    mul = mul_;
+    pieces = pieces_;
+    xcd = xcd_;
+    sh = nx == 8 ? 3 : 0;  // shares of 1/nx: nx is 8 or 1
+    g = g_;
+    G = G_;
+  }
+  template <class A>
+  __device__ bool at(const A& a, int u, int* cls, int* idx) const {
+    int p = g + u * G;
+    int bn = 1;  // C(L, c)
+    for (int c = 0; c <= L; ++c) {
+      if (c > 0) bn = bn * (L - c + 1) / c;
+      const int T = mul * bn * (pieces ? a.np[c] : 1);
+      const int x0 = (T * xcd) >> sh, x1 = (T * (xcd + 1)) >> sh;
+      if (p < x1 - x0) {
+        *cls = c;
+        *idx = x0 + p;
+        return true;
+      }
+      p -= x1 - x0;
+    }
+    return false;
+  }
+};
+
+template <class C, Op OP, bool LISTED, bool TENSOR>
+__device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
   const int32_t* ws = a.ws;
-  if (ws[1] != kIndexMagic || ws[2] != a.q || ws[3] != a.M) return;
-  const int cyc = ws[4];
-  if (cyc < 0) return;  // listed schedule: the register-staged kernel handles it
+  const int32_t* rows = ws + a.off_rows;
+  const cint_ptr s_off = to_const(ws + a.off_offsets);
+  const cint_ptr s_rows = to_const(rows);
   const int q = a.q;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // the type index of the cyclic schedule, in closed form
-  const CycIndex ix = CycIndex::make(q, uni(cyc), a.M, C::BM);
-  // first row of each type in the cyclic schedule
+  // the type index: closed form for a cyclic schedule, the tables otherwise
+  // (row tiles of 256 rows; dW decodes no row tiles)
+  using IX = std::conditional_t<LISTED, MemIndex, CycIndex>;
+  IX ix;
+  const int cyc = LISTED ? -1 : uni(ws[4]);
+  if constexpr (LISTED)
+    ix = MemIndex{s_off, to_const(ws + a.off_tiles + tile_height_slot(256) * (q + 1)), q};
+  else
+    ix = CycIndex::make(q, cyc, a.M, 256);
+  // first row of type i in a cyclic schedule
   auto type_start = [&](int i) { return i >= cyc ? i - cyc : i - cyc + q; };
+  const int typed = LISTED ? uni(s_off[q]) : a.M;  // rows with a type in range
 
-  GradArgs g = a;
-  int n_long, n_short, t_long, t_short;
-  if constexpr (OP == Op::Dx) {
-    g.n_rt = ix.tiles_before(q);
-    n_long = g.n_rt * g.cpg;
-    n_short = g.n_rt * (q - 1) * g.cpg;
-    t_long = g.N / C::BK;
-    t_short = g.r / C::BK;
-  } else {
-    const int tpb = g.rpb * g.cpg;
-    n_long = q * tpb * g.splits;  // pieces of the split long tiles
-    n_short = q * (q - 1) * tpb;
-    t_long = g.M / g.splits / C::BK;
-    t_short = g.M / q / C::BK;
-  }
+  // rows of dW segment n of unit t: count, start (cyclic) or list slot, and
+  // how rows are found (0: rows 0.. in order; 1: start + m q; 2: row list)
+  auto seg_rows = [&](const GTile& t, int n, int& cnt, int& base, int& mode) {
+    if (t.nseg == 0) {
+      cnt = typed;
+      base = 0;
+      mode = typed == a.M ? 0 : 2;
+      return;
+    }
+    const int ty = TENSOR ? law_member(t.seg_from, t.seg_mask, n, a.L) : t.seg_from;
+    cnt = ix.count(ty);
+    base = LISTED ? ix.offset(ty) : type_start(ty);
+    mode = LISTED ? 2 : 1;
+  };
 
+  const int n_rt = OP == Op::Dx ? ix.tiles_before(q) : 0;
+  const int tpb = a.rpb * a.cpg;
+  auto decode = [&](int cls, int idx) -> GTile {
+    GTile t;
+    t.cls = cls;
+    t.c0 = 0;
+    t.piece = -1;
+    if constexpr (OP == Op::Dx) {
+      constexpr int G = 4;
+      const int ngrp = TENSOR ? binom_small(a.L, cls) : (cls ? 1 : q - 1);
+      const int span = G * ngrp * a.cpg;
+      const int grp = idx / span, w = idx - grp * span;
+      const int first_rt = grp * G;
+      const int gm = min(n_rt - first_rt, G);
+      const int rt = first_rt + w % gm, c2 = w / gm;
+      const int jj = c2 / a.cpg, cc = c2 - jj * a.cpg;
+      const int i = ix.group_of_tile(rt);
+      t.type = i;
+      t.out_row0 = (rt - ix.tiles_before(i)) * C::BM;
+      t.m_cnt = min(C::BM, ix.count(i) - t.out_row0);
+      t.first = ix.offset(i) + t.out_row0;
+      int k;
+      const int kts = a.r / C::BK;
+      if constexpr (TENSOR) {
+        const int m = unrank_mask(jj, cls, a.L);
+        k = i ^ m;
+        // output groups agreeing with k where k differs from i (all when k == i)
+        t.seg_from = k;
+        t.seg_mask = m;
+        t.nseg = cls > 0 ? 1 << (a.L - cls) : 0;
+        t.col0 = 0;
+        t.nk = (1 << (a.L - cls)) * kts;
+      } else {
+        k = cls ? i : (jj < i ? jj : jj + 1);
+        t.seg_from = t.seg_mask = 0;
+        t.nseg = 0;
+        t.col0 = cls ? 0 : k * a.r;
+        t.nk = cls ? a.N / C::BK : kts;
+      }
+      t.n0 = k * a.s + cc * C::BN;
+    } else {
+      const int npc = a.np[cls];
+      const int tix = idx / npc;
+      const int piece = idx - tix * npc;
+      const int blk = tix / tpb, w = tix - blk * tpb;
+      int b, j;
+      if constexpr (TENSOR) {
+        const int nb = binom_small(a.L, cls);
+        b = blk / nb;
+        const int m = unrank_mask(blk - b * nb, cls, a.L);
+        j = b ^ m;
+        // rows of the types agreeing with b where b differs from j
+        t.seg_from = b;
+        t.seg_mask = m;
+        t.nseg = cls > 0 ? 1 << (a.L - cls) : 0;
+      } else if (cls) {
+        b = j = blk;
+        t.seg_from = b;
+        t.seg_mask = 0;
+        t.nseg = 0;
+      } else {
+        b = blk / (q - 1);
+        const int jj = blk - b * (q - 1);
+        j = jj < b ? jj : jj + 1;
+        t.seg_from = b;
+        t.seg_mask = 0;
+        t.nseg = 1;
+      }
+      const int rt = w % a.rpb, ct = w / a.rpb;
+      t.out_row0 = b * a.s + rt * C::BM;
+      t.n0 = j * a.r + ct * C::BN;
+      t.type = -1;
+      t.first = 0;
+      t.m_cnt = C::BM;
+      t.col0 = 0;
+      // k-steps of the whole contraction: each segment rounded up to whole k-steps
+      int nk_all = 0;
+      const int ns = t.nseg == 0 ? 1 : t.nseg;
+      for (int n = 0; n < ns; ++n) {
+        int cnt, base, mode;
+        seg_rows(t, n, cnt, base, mode);
+        nk_all += (cnt + C::BK - 1) / C::BK;
+      }
+      const int per = (nk_all + npc - 1) / npc;
+      t.c0 = uni(piece * per);
+      t.nk = uni(max(0, min(per, nk_all - t.c0)));
+      t.piece = npc > 1 ? piece : -1;
+    }
+    return t;
+  };
+
+  // this XCD's units
   const int nx = gridDim.x >= 8 ? 8 : 1;
   const int per_x = gridDim.x / nx;
   const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx;
   if (slot >= per_x) return;
+  std::conditional_t<TENSOR, DealC, Deal2> deal;
+  if constexpr (TENSOR)
+    deal.init(a, OP == Op::Dx ? n_rt * a.cpg : q * tpb, OP == Op::Dw, xcd, nx, slot, per_x);
+  else if constexpr (OP == Op::Dx)
+    deal.init(n_rt * a.cpg, n_rt * (q - 1) * a.cpg, a.N / C::BK, a.r / C::BK, xcd, nx, slot, per_x);
+  else
+    deal.init(q * tpb * a.np[1], q * (q - 1) * tpb * a.np[0], a.t_unit[1], a.t_unit[0], xcd, nx, slot, per_x);
+  auto unit_at = [&](int u, int* cls, int* idx) -> bool {
+    const bool ok = deal.at(a, u, cls, idx);
+    *cls = uni(*cls);
+    *idx = uni(*idx);
+    return ok;
+  };
+  // cursors over the units: the copy cursor's next unit, the compute cursor's
+  int u_copy = 0, u_comp = 0;
+  // the next unit with k-steps (dW pieces and tiles of types without rows
+  // can have none: the compute cursor writes their zeros, the copy cursor
+  // skips them)
+  auto next_work = [&](GTile* t) -> bool {
+    for (;;) {
+      int cls, idx;
+      if (!unit_at(u_copy, &cls, &idx)) return false;
+      u_copy = uni(u_copy + 1);
+      *t = decode(cls, idx);
+      if (t->nk > 0) return true;
+    }
+  };
 
-  const uint32_t a_ld = uint32_t(OP == Op::Dx ? g.N : g.K) * 2u;   // bytes per row of A
-  const uint32_t b_ld = uint32_t(g.N) * 2u;                         // bytes per row of B (W or dY)
-  const uint32_t c_ld = uint32_t(OP == Op::Dx ? g.K : g.N) * 2u;    // bytes per row of C
-
-  // ---------------- copy cursor ----------------
-  TileDeal dcopy;
-  dcopy.init(n_long, n_short, t_long, t_short, xcd, nx, slot, per_x);
-  bool l_long;
-  int l_idx;
-  if (!dcopy.next(&l_long, &l_idx)) return;
-  GTile lt = decode<C, OP>(g, ix, l_long, l_idx);
-  int lk = 0;
-  bool more = true;  // the copy cursor has not passed the last k-step
+  const uint32_t a_ld = uint32_t(OP == Op::Dx ? a.N : a.K) * 2u;   // bytes per row of A
+  const uint32_t b_ld = uint32_t(a.N) * 2u;                         // bytes per row of B (W or dY)
+  const uint32_t c_ld = uint32_t(OP == Op::Dx ? a.K : a.N) * 2u;    // bytes per row of C
 
   // per-lane copy slots: KM operand -> (tile row, swizzled piece); RM operand -> (contraction row, piece)
   int a_r[C::A_DMA], a_c[C::A_DMA], b_r[C::B_DMA], b_c[C::B_DMA];
@@ -262,56 +438,230 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
     }
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(smem)));
+  const u32x4 rs_a = buffer_rsrc(a.A, a.a_bytes), rs_b = buffer_rsrc(a.B, a.b_bytes);
 
-  // copy cursor in three parts (per-step offsets, one copy, advance) so that
-  // the copies can be interleaved with MFMAs
-  int cp_kc = 0, cp_start = 0, cp_rbase = 0, cp_rstep = 1;
-  auto prep_copies = [&]() {
+  // ---------------- copy cursor ----------------
+  GTile lt;
+  bool more = next_work(&lt);  // the copy cursor has not passed the last k-step
+  int lk = 0;
+
+  // dX: byte offsets of the lane's A rows (dY rows of the tile's type), and,
+  // for a listed schedule, the row ids of the next tile, loaded a tile ahead
+  // and taken after the wait that closes a k-step's copies (the wait for them
+  // then costs nothing)
+  uint32_t a_roff[OP == Op::Dx ? C::A_DMA : 1];
+  int pre_row[(OP == Op::Dx && LISTED) ? C::A_DMA : 1];
+  bool rows_pending = false;
+  GTile nt = lt;   // dX, listed: the unit after lt (its rows prefetched)
+  bool have_nt = false;
+  auto prefetch_rows = [&](const GTile& t) {
+    if constexpr (OP == Op::Dx && LISTED) {
+#pragma unroll
+      for (int u = 0; u < C::A_DMA; ++u) pre_row[u] = rows[t.first + min(a_r[u], t.m_cnt - 1)];
+    }
+  };
+  auto set_rows = [&](const GTile& t) {
     if constexpr (OP == Op::Dx) {
-      cp_kc = lt.c0 + lk * C::BK;
-      cp_start = type_start(lt.type);
-    } else {
-      const int k0 = (lt.c0 + lk) * C::BK;  // c0: a split piece's first k-step
-      cp_rbase = lt.type < 0 ? k0 : type_start(lt.type) + k0 * q;
-      cp_rstep = lt.type < 0 ? 1 : q;
+#pragma unroll
+      for (int u = 0; u < C::A_DMA; ++u) {
+        int row;
+        if constexpr (LISTED)
+          row = pre_row[u];
+        else
+          row = type_start(t.type) + (t.out_row0 + min(a_r[u], t.m_cnt - 1)) * q;
+        a_roff[u] = uint32_t(row) * a_ld;
+      }
+    }
+  };
+  // dX contraction cursor: column of the current k-step (segment walk for the recursive law)
+  int cx_n = 0, cx_kk = 0, cx_col = 0;
+  // dW contraction cursor: segment w_n of the unit's contraction covers
+  // k-steps [w_k0, w_k0 + w_kn) with w_cnt rows from w_base (mode as seg_rows)
+  int w_n = 0, w_k0 = 0, w_kn = 0, w_cnt = 0, w_base = 0, w_mode = 0;
+  // dW, cyclic schedule: rows in closed form, row r0 + e st for the wave's
+  // row e, with stride st = 1 (all rows in order) or q (the rows of one type);
+  // each copy's offset is a per-lane part at that stride (p1, pq, fixed for the
+  // kernel) plus a wave-uniform part per k-step
+  constexpr bool CYC_DW = OP == Op::Dw && !LISTED;
+  // the complete law on a cyclic schedule: one segment per unit, no walk
+  constexpr bool SIMPLE = CYC_DW && !TENSOR;
+  uint32_t p1[CYC_DW ? C::DMA : 1], pq[CYC_DW ? C::DMA : 1];
+  if constexpr (CYC_DW) {
+#pragma unroll
+    for (int u = 0; u < C::A_DMA; ++u) {
+      const int e = a_r[u] - 8 * wid;
+      p1[u] = uint32_t(e) * a_ld + uint32_t(a_c[u]) * 16u;
+      pq[u] = uint32_t(e * q) * a_ld + uint32_t(a_c[u]) * 16u;
+    }
+#pragma unroll
+    for (int v = 0; v < C::B_DMA; ++v) {
+      const int e = b_r[v] - 8 * wid;
+      p1[C::A_DMA + v] = uint32_t(e) * b_ld + uint32_t(b_c[v]) * 16u;
+      pq[C::A_DMA + v] = uint32_t(e * q) * b_ld + uint32_t(b_c[v]) * 16u;
+    }
+  }
+  int w_rbase = 0, w_rstep = 1;  // cyclic: row of the segment's rank j is w_rbase + j w_rstep
+  auto seg_enter = [&](int n) {
+    w_n = n;
+    seg_rows(lt, n, w_cnt, w_base, w_mode);
+    w_kn = (w_cnt + C::BK - 1) / C::BK;
+    if constexpr (!LISTED) {
+      w_rstep = uni(w_mode == 0 ? 1 : q);
+      w_rbase = uni(w_mode == 0 ? 0 : w_base);
+    }
+  };
+  auto seg_walk = [&](int kabs) {
+    if constexpr (!SIMPLE) {
+      const int ns = lt.nseg == 0 ? 1 : lt.nseg;
+      while (kabs >= w_k0 + w_kn && w_n + 1 < ns) {
+        w_k0 += w_kn;
+        seg_enter(w_n + 1);
+      }
+    }
+  };
+  // start of a unit: contraction cursors at its first k-step
+  auto unit_start = [&]() {
+    if constexpr (OP == Op::Dx) {
+      cx_n = 0;
+      cx_kk = 0;
+      cx_col = lt.nseg ? law_member(lt.seg_from, lt.seg_mask, 0, a.L) * a.r : lt.col0;
+    } else if constexpr (!SIMPLE) {
+      w_k0 = 0;
+      seg_enter(0);
+      seg_walk(lt.c0);
+    }
+  };
+  // dW: ids of the 8 rows this wave copies at the cursor's k-step, and how
+  // many of them lie inside the segment (w_rem; the others read as zeros)
+  int w_id[8];
+  int w_rem = 0;
+  uint32_t w_ua = 0, w_ub = 0;  // cyclic: wave-uniform offset parts of the A and B copies
+  auto prep_rows = [&]() {
+    if constexpr (CYC_DW) {
+      // rows past a type's last one (or past M) lie past the end of X and dY:
+      // the buffer range check reads them as zeros, no test needed
+      int r0;
+      if constexpr (SIMPLE) {
+        // long units: every row in order; short ones: the rows of type seg_from
+        const int j0 = uni((lt.c0 + lk) * C::BK + 8 * wid);
+        w_rstep = lt.nseg == 0 ? 1 : q;
+        r0 = lt.nseg == 0 ? j0 : type_start(lt.seg_from) + j0 * q;
+      } else {
+        const int j0 = uni((lt.c0 + lk - w_k0) * C::BK + 8 * wid);
+        r0 = w_rbase + j0 * w_rstep;
+      }
+      w_ua = uint32_t(uni(int(uint32_t(r0) * a_ld + uint32_t(lt.out_row0) * 2u)));
+      w_ub = uint32_t(uni(int(uint32_t(r0) * b_ld + uint32_t(lt.n0) * 2u)));
+    } else if constexpr (OP == Op::Dw) {
+      const int j0 = (lt.c0 + lk - w_k0) * C::BK + 8 * wid;  // segment rank of the wave's first row
+      w_rem = uni(w_cnt - j0);
+      if (w_mode == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w_id[e] = uni(s_rows[w_base + j0 + e]);  // may read the spare tail
+      } else {
+        const int r0 = w_mode == 0 ? j0 : w_base + j0 * q, st = w_mode == 0 ? 1 : q;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w_id[e] = uni(r0 + e * st);
+      }
+    }
+  };
+  // dW: byte offset of a copy's row (local row e of the wave's 8), or one that
+  // fails the range check past the segment's rows
+  auto row_off = [&](int id, int e, uint32_t ld, uint32_t col_bytes) -> uint32_t {
+    const uint32_t ro = __umul24(uint32_t(id), ld);
+    return (e < w_rem ? ro : kNoRow) + col_bytes;
+  };
+  // dW: source offsets of the wave's copies for the cursor's k-step, worked
+  // out in the first quarter step (rows after its first MFMA, offsets in the
+  // MFMA slots that carry no fragment read), off the slots that issue the copies
+  uint32_t c_off[OP == Op::Dw ? C::DMA : 1];
+  auto off_u = [&](int u) {
+    if constexpr (CYC_DW) {
+      c_off[u] = (w_rstep == 1 ? p1[u] : pq[u]) + (u < C::A_DMA ? w_ua : w_ub);
+    } else if constexpr (OP == Op::Dw) {
+      if (u < C::A_DMA) {
+        c_off[u] = row_off(pick_row<C::A_NCH>(w_id, u, lane), a_r[u] - 8 * wid, a_ld,
+                           uint32_t(lt.out_row0 + a_c[u] * 8) * 2u);
+      } else {
+        const int v = u - C::A_DMA;
+        c_off[u] = row_off(pick_row<C::B_NCH>(w_id, v, lane), b_r[v] - 8 * wid, b_ld,
+                           uint32_t(lt.n0 + b_c[v] * 8) * 2u);
+      }
     }
   };
   auto copy_u = [&](int stage, int u) {
     const uint32_t S = lds0 + uint32_t(stage * C::STAGE);
     if constexpr (OP == Op::Dx) {
       // A = dY rows of type lt.type (tile rows), B = W rows n0.. (tile rows);
-      // contraction columns cp_kc..
+      // contraction columns cx_col..
       if (u < C::A_DMA) {
-        const int row = cp_start + (lt.out_row0 + min(a_r[u], lt.m_cnt - 1)) * q;
-        copy16_to_lds(g.A, uint32_t(row) * a_ld + uint32_t(cp_kc + a_c[u] * 8) * 2u,
+        copy16_to_lds(a.A, a_roff[u] + uint32_t(cx_col + a_c[u] * 8) * 2u,
                       S + uint32_t((wid * C::A_DMA + u) * 1024));
       } else {
         const int v = u - C::A_DMA;
-        copy16_to_lds(g.B, uint32_t(lt.n0 + b_r[v]) * b_ld + uint32_t(cp_kc + b_c[v] * 8) * 2u,
+        copy16_to_lds(a.B, uint32_t(lt.n0 + b_r[v]) * b_ld + uint32_t(cx_col + b_c[v] * 8) * 2u,
                       S + uint32_t(C::A_BYTES + (wid * C::B_DMA + v) * 1024));
       }
     } else {
-      // contraction rows: all rows (long tiles) or the rows of type lt.type
-      if (u < C::A_DMA) {
-        const int row = cp_rbase + a_r[u] * cp_rstep;
-        copy16_to_lds(g.A, uint32_t(row) * a_ld + uint32_t(lt.out_row0 + a_c[u] * 8) * 2u,
-                      S + uint32_t((wid * C::A_DMA + u) * 1024));
-      } else {
-        const int v = u - C::A_DMA;
-        const int row = cp_rbase + b_r[v] * cp_rstep;
-        copy16_to_lds(g.B, uint32_t(row) * b_ld + uint32_t(lt.n0 + b_c[v] * 8) * 2u,
-                      S + uint32_t(C::A_BYTES + (wid * C::B_DMA + v) * 1024));
+      // contraction rows of the k-step; output features / columns along the rows
+      if (u < C::A_DMA)
+        copy16_to_lds_buf(rs_a, c_off[u], S + uint32_t((wid * C::A_DMA + u) * 1024));
+      else
+        copy16_to_lds_buf(rs_b, c_off[u], S + uint32_t(C::A_BYTES + (wid * C::B_DMA + (u - C::A_DMA)) * 1024));
+    }
+  };
+  // called after the wait that ends a k-step's outstanding copies (and in the
+  // prologue): a new dX tile's rows are taken here
+  auto prep_copies = [&]() {
+    if constexpr (OP == Op::Dx) {
+      if (rows_pending) {
+        rows_pending = false;
+        set_rows(lt);
+        if constexpr (LISTED) {
+          have_nt = next_work(&nt);
+          if (have_nt) prefetch_rows(nt);
+        }
       }
     }
   };
-  // After the last k-step the cursor stays on it: the copies issued for the
-  // k-steps past the end repeat it into stages that are never read (drained
-  // before exit), so that the pipeline needs no conditions.
+  // next k-step of the copy cursor.  After the last k-step the cursor stays
+  // on it: the copies issued for the k-steps past the end repeat it into
+  // stages that are never read (drained before exit), so that the pipeline
+  // needs no conditions.
   auto advance_copies = [&]() {
-    if (more && (lk = uni(lk + 1)) >= lt.nk) {
-      if (dcopy.next(&l_long, &l_idx)) {
-        lt = decode<C, OP>(g, ix, l_long, uni(l_idx));
+    if (!more) return;
+    lk = uni(lk + 1);
+    if (lk < lt.nk) {
+      if constexpr (OP == Op::Dx) {
+        if (lt.nseg) {
+          cx_kk = uni(cx_kk + 1);
+          if (cx_kk == a.r / C::BK) {
+            cx_kk = 0;
+            cx_n = uni(cx_n + 1);
+            cx_col = law_member(lt.seg_from, lt.seg_mask, cx_n, a.L) * a.r;
+          } else {
+            cx_col = uni(cx_col + C::BK);
+          }
+        } else {
+          cx_col = uni(cx_col + C::BK);
+        }
+      } else {
+        seg_walk(lt.c0 + lk);
+      }
+    } else {
+      bool got;
+      GTile t2;
+      if constexpr (OP == Op::Dx && LISTED) {
+        got = have_nt;
+        t2 = nt;
+      } else {
+        got = next_work(&t2);
+      }
+      if (got) {
+        lt = t2;
         lk = 0;
+        unit_start();
+        rows_pending = true;
       } else {
         more = false;
         lk = uni(lt.nk - 1);
@@ -320,8 +670,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   };
   auto issue_copies = [&](int stage) {
     prep_copies();
+    prep_rows();
 #pragma unroll
-    for (int u = 0; u < C::DMA; ++u) copy_u(stage, u);
+    for (int u = 0; u < C::DMA; ++u) {
+      off_u(u);
+      copy_u(stage, u);
+    }
     advance_copies();
   };
 
@@ -397,29 +751,41 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
   // ---------------- pipeline (as in the forward) ----------------
   static_assert(C::FM + C::FN <= C::FM * C::FN, "fragment reads fit a quarter step");
   constexpr int S = C::STAGES;
+  if (more) {
+    unit_start();
+    if constexpr (OP == Op::Dx) {
+      // the first unit's rows are taken by the first prep_copies (which also
+      // finds the unit after it and prefetches its rows)
+      prefetch_rows(lt);
+      rows_pending = true;
+    }
 #pragma unroll
-  for (int st = 0; st < S - 1 + (S == 2 ? 1 : 0); ++st) issue_copies(st);
-  // two stages: step 1 may be in flight; four: steps 1 and 2
-  wait_vmcnt<(S == 2 ? 1 : 2) * C::DMA>();
-  lds_barrier();
-  load_frags(0, 0, fa0, fb0);
+    for (int st = 0; st < S - 1 + (S == 2 ? 1 : 0); ++st) issue_copies(st);
+    // two stages: step 1 may be in flight; four: steps 1 and 2
+    wait_vmcnt<(S == 2 ? 1 : 2) * C::DMA>();
+    lds_barrier();
+    load_frags(0, 0, fa0, fb0);
+  }
 
-  TileDeal dcomp;
-  dcomp.init(n_long, n_short, t_long, t_short, xcd, nx, slot, per_x);
-  bool c_long;
-  int c_idx;
-  dcomp.next(&c_long, &c_idx);
-  GTile ct = decode<C, OP>(g, ix, c_long, uni(c_idx));
   int stage = 0;  // LDS stage of the current k-step
   // one quarter step: MFMAs on fragments (fa, fb) of quarter ks, each followed
   // by one read of quarter ks + 1's fragments into (ga, gb)
   auto quarter = [&](int ks, const bf16x8 (&fa)[C::FM], const bf16x8 (&fb)[C::FN], bf16x8 (&ga)[C::FM],
                      bf16x8 (&gb)[C::FN]) {
+    // dW, first quarter: the slots past the reads work out the copy offsets
+    constexpr int R = C::FM + C::FN, F = C::FM * C::FN - R;
+    static_assert(OP != Op::Dw || F >= 1, "a free slot for the copy offsets");
 #pragma unroll
     for (int x = 0; x < C::FM * C::FN; ++x) {
       const int fm = x / C::FN, fn = x % C::FN;
       acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fn], fa[fm], acc[fm][fn], 0, 0, 0);
-      if (x < C::FM + C::FN) read_slot(x, stage, ks + 1, ga, gb);
+      if (x < R) read_slot(x, stage, ks + 1, ga, gb);
+      if (OP == Op::Dw && ks == 0 && x == 0) prep_rows();
+      if (OP == Op::Dw && ks == 0 && x >= R) {
+        const int f = x - R;
+#pragma unroll
+        for (int u = f * C::DMA / (F > 0 ? F : 1); u < (f + 1) * C::DMA / (F > 0 ? F : 1); ++u) off_u(u);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -445,6 +811,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
     }
   };
   for (;;) {
+    int c_cls, c_idx;
+    if (!unit_at(u_comp, &c_cls, &c_idx)) break;
+    u_comp = uni(u_comp + 1);
+    const GTile ct = decode(c_cls, c_idx);
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
@@ -481,10 +851,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
     bool partial = false;
     if constexpr (OP == Op::Dw) partial = ct.piece >= 0;
     if (partial) {
-      // a piece of a split long tile: its fp32 sums go to the piece's partial
-      // tile (lane (l32, lhi) holds 4 consecutive columns of one row per
-      // group gg, i.e. one 16-byte piece); the reduction rounds them
-      float* P = g.part + size_t(ct.piece) * size_t(g.part_stride);
+      // a piece of a split tile: its fp32 sums go to the piece's partial tile
+      // (lane (l32, lhi) holds 4 consecutive columns of one row per group gg,
+      // i.e. one 16-byte piece); the reduction rounds them
+      float* P = a.part + size_t(ct.piece) * size_t(a.part_stride);
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm) {
         const size_t row = size_t(ct.out_row0 + wm * C::WTM + fm * 32 + l32);
@@ -496,7 +866,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
             const int col = ct.n0 + wn * C::WTN + fn * 32 + gg * 8 + lhi * 4;
             const u32x4 val = {__float_as_uint(v[4 * gg]), __float_as_uint(v[4 * gg + 1]),
                                __float_as_uint(v[4 * gg + 2]), __float_as_uint(v[4 * gg + 3])};
-            *reinterpret_cast<u32x4*>(P + row * size_t(g.N) + size_t(col)) = val;
+            *reinterpret_cast<u32x4*>(P + row * size_t(a.N) + size_t(col)) = val;
           }
         }
       }
@@ -506,7 +876,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
       // writes whole 16-byte pieces of a few rows
       char* ebuf = smem + C::E_OFF + wid * C::E_BYTES;
       const uint32_t col0 = uint32_t(ct.n0 + wn * C::WTN) * 2u;
-      const int ostart = OP == Op::Dx ? type_start(ct.type) : 0;
+      const int ostart = (OP == Op::Dx && !LISTED) ? type_start(ct.type) : 0;
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm) {
         // lane (l32, lhi) holds row l32, columns fn*32 + g*8 + lhi*4 .. +3
@@ -527,55 +897,90 @@ __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs
           const int row = sl / C::E_NP, pc = sl - row * C::E_NP;
           const u32x4 val = *reinterpret_cast<const u32x4*>(ebuf + row * C::E_PITCH + ((pc ^ (row & C::E_MASK)) << 4));
           const int ml = wm * C::WTM + fm * 32 + row;
-          const int orow = OP == Op::Dx ? ostart + (ct.out_row0 + ml) * q : ct.out_row0 + ml;
           // non-temporal whole-line stores keep the output out of L2 (as in the forward)
-          if (ml < ct.m_cnt)
-            __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(g.C + (uint32_t(orow) * c_ld + col0 + uint32_t(pc) * 16u)));
+          if (ml < ct.m_cnt) {
+            int orow;
+            if constexpr (OP == Op::Dx)
+              orow = LISTED ? rows[ct.first + ml] : ostart + (ct.out_row0 + ml) * q;
+            else
+              orow = ct.out_row0 + ml;
+            __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(a.C + (uint32_t(orow) * c_ld + col0 + uint32_t(pc) * 16u)));
+          }
         }
       }
     }
-    if (!dcomp.next(&c_long, &c_idx)) break;
-    ct = decode<C, OP>(g, ix, c_long, uni(c_idx));
   }
   // the repeated copies past the last k-step land in LDS: drain them before
   // the workgroup's LDS can be handed to another workgroup
   wait_vmcnt<0>();
 }
 
-// dW of a split launch: dW[diagonal block] = bf16(sum over pieces of the fp32
-// partial tiles), pieces in order, one rounding.  One thread per 4 consecutive
-// elements of the q diagonal blocks (s x r each).  Like the persistent kernel
-// it does nothing unless the index holds a cyclic schedule of this problem
-// (on other schedules the register-staged kernel writes all of dW).
-__global__ __launch_bounds__(256) void dw_diag_reduce_kernel(const int32_t* __restrict__ ws, int q, int M,
-                                                             const float* __restrict__ part, int splits,
-                                                             int64_t stride, int N, int s, int r,
-                                                             uint16_t* __restrict__ dW) {
-  if (ws[1] != kIndexMagic || ws[2] != q || ws[3] != M || ws[4] < 0) return;
-  const int64_t r4 = r / 4;
-  const int64_t per_blk = int64_t(s) * r4;
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= q * per_blk) return;
-  const int b = int(i / per_blk);
-  const int64_t w = i - b * per_blk;
-  const int64_t f = w / r4, c4 = w - f * r4;
-  const int64_t off = (int64_t(b) * s + f) * N + int64_t(b) * r + c4 * 4;
-  u32x4 x = *reinterpret_cast<const u32x4*>(part + off);
+template <class C, Op OP, bool TENSOR>
+__global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int32_t* ws = a.ws;
+  if (ws[1] != kIndexMagic || ws[2] != a.q || ws[3] != a.M) return;
+  // two bodies: the cyclic one never reads the row list
+  if (ws[4] >= 0)
+    grad_body<C, OP, false, TENSOR>(a, smem);
+  else
+    grad_body<C, OP, true, TENSOR>(a, smem);
+}
+
+// dW of split tiles: dW = bf16(sum over pieces of the fp32 partial tiles),
+// pieces in order, one rounding.  Workgroups cover the blocks (b, j) of the
+// split classes in class order, wpb workgroups of 1024 elements per block.
+struct ReduceArgs {
+  const int32_t* ws;
+  int q, M, L;
+  const float* part;
+  int64_t stride;  // floats per piece
+  int N, s, r, wpb;
+  int np[kMaxClasses];
+  int first[kMaxClasses + 1];  // first workgroup of each class (classes not split have none)
+  uint16_t* dW;
+};
+
+__global__ __launch_bounds__(256) void dw_piece_reduce_kernel(ReduceArgs a) {
+  const int32_t* ws = a.ws;
+  if (ws[1] != kIndexMagic || ws[2] != a.q || ws[3] != a.M) return;
+  const int bid = blockIdx.x;
+  int c = 0;
+  while (c + 1 < kMaxClasses && bid >= a.first[c + 1]) ++c;
+  const int local = bid - a.first[c];
+  const int blk = local / a.wpb, w = local - blk * a.wpb;
+  int b, j;
+  if (a.L > 0) {
+    const int nb = binom_small(a.L, c);
+    b = blk / nb;
+    j = b ^ unrank_mask(blk - b * nb, c, a.L);
+  } else if (c == 1) {
+    b = j = blk;
+  } else {
+    b = blk / (a.q - 1);
+    const int jj = blk - b * (a.q - 1);
+    j = jj < b ? jj : jj + 1;
+  }
+  const int64_t e = (int64_t(w) * 256 + threadIdx.x) * 4;
+  if (e >= int64_t(a.s) * a.r) return;
+  const int64_t f = e / a.r, cc = e - f * a.r;
+  const int64_t off = (int64_t(b) * a.s + f) * a.N + int64_t(j) * a.r + cc;
+  u32x4 x = *reinterpret_cast<const u32x4*>(a.part + off);
   float v0 = __uint_as_float(x[0]), v1 = __uint_as_float(x[1]), v2 = __uint_as_float(x[2]), v3 = __uint_as_float(x[3]);
-  for (int p = 1; p < splits; ++p) {
-    x = *reinterpret_cast<const u32x4*>(part + p * stride + off);
+  for (int p = 1; p < a.np[c]; ++p) {
+    x = *reinterpret_cast<const u32x4*>(a.part + p * a.stride + off);
     v0 += __uint_as_float(x[0]);
     v1 += __uint_as_float(x[1]);
     v2 += __uint_as_float(x[2]);
     v3 += __uint_as_float(x[3]);
   }
-  *reinterpret_cast<u32x2*>(dW + off) = pack4_bf16(v0, v1, v2, v3);
+  *reinterpret_cast<u32x2*>(a.dW + off) = pack4_bf16(v0, v1, v2, v3);
 }
 
 template <int BN>
 using DxCfg = GradCfg<256, BN, true, true, kBKDx, 2>;
-template <int BN>
-using DwCfg = GradCfg<256, BN, false, false, kBKDw, 4>;
+template <int BM, int BN>
+using DwCfg = GradCfg<BM, BN, false, false, kBKDw, 4>;
 
 int cu_count() {
   static int n = 0;
@@ -588,12 +993,24 @@ int cu_count() {
   return n;
 }
 
-template <class C, Op OP>
+int binom_host(int L, int d) {
+  int c = 1;
+  for (int k = 0; k < d; ++k) c = c * (L - k) / (k + 1);
+  return c;
+}
+
+int tensor_levels_of(int q) {
+  int L = 0;
+  while ((1 << L) < q) ++L;
+  return L;
+}
+
+template <class C, Op OP, bool TENSOR>
 hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
   static bool attr_set = false;
   const int lds = C::LDS_BYTES;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grad_persistent_kernel<C, OP>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grad_persistent_kernel<C, OP, TENSOR>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -603,15 +1020,19 @@ hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
   a.B = static_cast<const char*>(p.B);
   a.C = static_cast<char*>(p.C);
   a.ws = p.ws;
-  const WsLayout L = ws_layout(p.q, p.M);
-  a.off_offsets = L.offsets;
-  a.off_tiles = L.tile_off;
+  const WsLayout Lw = ws_layout(p.q, p.M);
+  a.off_offsets = Lw.offsets;
+  a.off_tiles = Lw.tile_off;
+  a.off_rows = Lw.rows;
   a.q = p.q;
   a.M = int(p.M);
   a.K = int(p.K);
   a.N = int(p.N);
   a.s = int(p.K / p.q);
   a.r = int(p.N / p.q);
+  a.L = TENSOR ? tensor_levels_of(p.q) : 0;
+  a.a_bytes = uint32_t(p.M * p.K * 2);
+  a.b_bytes = uint32_t(p.M * p.N * 2);
   if (OP == Op::Dx) {
     a.cpg = a.s / C::BN;
     a.rpb = 0;
@@ -621,61 +1042,123 @@ hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
   }
   int grid = cu_count();
   grid = grid >= 8 ? grid / 8 * 8 : grid;
-  a.splits = 1;
+  for (int c = 0; c < kMaxClasses; ++c) a.np[c] = 1;
+  a.t_unit[0] = a.t_unit[1] = 1;
   a.part = nullptr;
   a.part_stride = 0;
-  if (OP == Op::Dw && p.dw_part != nullptr) {
-    // split the long (diagonal) tiles until a piece is no longer than the
-    // average k-steps per workgroup
+  int ncls = 0;
+  int64_t nblk[kMaxClasses] = {};  // dW blocks of each class
+  if (OP == Op::Dw) {
+    // contraction k-steps of each class's tiles, from M / q rows per type
+    const int64_t kd = C::BK;
+    const int64_t per_type = (p.M + p.q - 1) / p.q;
+    int64_t nk[kMaxClasses] = {};
+    if (TENSOR) {
+      ncls = a.L + 1;
+      for (int d = 0; d <= a.L; ++d) {
+        nblk[d] = int64_t(p.q) * binom_host(a.L, d);
+        nk[d] = d == 0 ? (p.M + kd - 1) / kd : (int64_t(1) << (a.L - d)) * ((per_type + kd - 1) / kd);
+      }
+    } else {
+      ncls = 2;
+      nblk[1] = p.q;
+      nblk[0] = int64_t(p.q) * (p.q - 1);
+      nk[1] = (p.M + kd - 1) / kd;
+      nk[0] = (per_type + kd - 1) / kd;
+    }
     const int64_t tpb = int64_t(a.rpb) * a.cpg;
-    const int64_t t_long = p.M / C::BK, t_short = p.M / p.q / C::BK;
-    const int64_t total = p.q * tpb * t_long + p.q * (p.q - 1) * tpb * t_short;
+    int64_t total = 0;
+    for (int c = 0; c < ncls; ++c) total += nblk[c] * tpb * nk[c];
     const int64_t avg = (total + grid - 1) / grid;
-    int sp = 1;
-    while (sp * 2 <= kDwMaxSplits && t_long % (sp * 2) == 0 && t_long / sp > avg) sp *= 2;
-    a.splits = sp;
-    a.part = static_cast<float*>(p.dw_part);
-    a.part_stride = p.K * p.N;
+    if (p.dw_part != nullptr) {
+      // cut a class's tiles until a piece is no longer than the average
+      // k-steps per workgroup (powers of two, at most kDwMaxSplits pieces)
+      for (int c = 0; c < ncls; ++c) {
+        int sp = 1;
+        while (sp * 2 <= kDwMaxSplits && (nk[c] + sp - 1) / sp > avg && nk[c] / (sp * 2) >= 1) sp *= 2;
+        a.np[c] = sp;
+      }
+      a.part = static_cast<float*>(p.dw_part);
+      a.part_stride = p.K * p.N;
+    }
+    if (!TENSOR) {
+      a.t_unit[0] = int((nk[0] + a.np[0] - 1) / a.np[0]);
+      a.t_unit[1] = int((nk[1] + a.np[1] - 1) / a.np[1]);
+    }
   }
   const size_t shm = C::LDS_BYTES;
-  hipLaunchKernelGGL((grad_persistent_kernel<C, OP>), dim3(grid), dim3(C::THREADS), shm, s, a);
+  hipLaunchKernelGGL((grad_persistent_kernel<C, OP, TENSOR>), dim3(grid), dim3(C::THREADS), shm, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.splits == 1) return e;
-  const int64_t threads = p.q * int64_t(a.s) * (a.r / 4);
-  hipLaunchKernelGGL(dw_diag_reduce_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, p.ws, a.q, a.M,
-                     a.part, a.splits, a.part_stride, a.N, a.s, a.r, static_cast<uint16_t*>(p.C));
+  if (e != hipSuccess || OP != Op::Dw) return e;
+  // reduce the split classes
+  ReduceArgs ra{};
+  ra.ws = p.ws;
+  ra.q = a.q;
+  ra.M = a.M;
+  ra.L = a.L;
+  ra.part = a.part;
+  ra.stride = a.part_stride;
+  ra.N = a.N;
+  ra.s = a.s;
+  ra.r = a.r;
+  ra.wpb = int((int64_t(a.s) * a.r / 4 + 255) / 256);
+  ra.dW = static_cast<uint16_t*>(p.C);
+  int64_t wgs = 0;
+  for (int c = 0; c < kMaxClasses; ++c) {
+    ra.np[c] = a.np[c];
+    ra.first[c] = int(wgs);
+    if (c < ncls && a.np[c] > 1) wgs += nblk[c] * ra.wpb;
+  }
+  ra.first[kMaxClasses] = int(wgs);
+  if (wgs == 0) return hipSuccess;
+  hipLaunchKernelGGL(dw_piece_reduce_kernel, dim3(unsigned(wgs)), dim3(256), 0, s, ra);
   return hipGetLastError();
 }
 
 int pick_bn(int64_t w) { return w % 256 == 0 ? 256 : w % 192 == 0 ? 192 : w % 128 == 0 ? 128 : 0; }
+int pick_bm_dw(int64_t w) { return w % 256 == 0 ? 256 : w % 192 == 0 ? 192 : 0; }
+
+template <Op OP, bool TENSOR>
+hipError_t launch_op(const ProblemDesc& p, hipStream_t s) {
+  if (OP == Op::Dx) {
+    const int bn = pick_bn(p.K / p.q);
+    if (bn == 256) return launch_grad<DxCfg<256>, Op::Dx, TENSOR>(p, s);
+    if (bn == 192) return launch_grad<DxCfg<192>, Op::Dx, TENSOR>(p, s);
+    return launch_grad<DxCfg<128>, Op::Dx, TENSOR>(p, s);
+  }
+  const int bm = pick_bm_dw(p.K / p.q), bn = pick_bn(p.N / p.q);
+  if (bm == 256) {
+    if (bn == 256) return launch_grad<DwCfg<256, 256>, Op::Dw, TENSOR>(p, s);
+    if (bn == 192) return launch_grad<DwCfg<256, 192>, Op::Dw, TENSOR>(p, s);
+    return launch_grad<DwCfg<256, 128>, Op::Dw, TENSOR>(p, s);
+  }
+  if (bn == 256) return launch_grad<DwCfg<192, 256>, Op::Dw, TENSOR>(p, s);
+  if (bn == 192) return launch_grad<DwCfg<192, 192>, Op::Dw, TENSOR>(p, s);
+  return launch_grad<DwCfg<192, 128>, Op::Dw, TENSOR>(p, s);
+}
 
 }  // namespace
 
 bool grad_persistent_supported(const ProblemDesc& p) {
   if (p.E != 1 || (p.op != Op::Dx && p.op != Op::Dw)) return false;
+  if (p.law_L > 6) return false;
   const int64_t s = p.K / p.q, r = p.N / p.q;
-  const int64_t lim = int64_t(1) << 31;
+  // 32-bit offsets; dW's buffer ranges stay below 2 GiB
+  const int64_t lim = int64_t(1) << 30;
   if (p.M * p.K >= lim || p.K * p.N >= lim || p.M * p.N >= lim) return false;
   if (p.op == Op::Dx) {
     // rows of a type in 256-row tiles; columns of an input group in BN tiles;
     // contraction lengths N and r in whole k-steps
     return (p.M + p.q - 1) / p.q >= 128 && pick_bn(s) != 0 && r % kBKDx == 0;
   }
-  // features of a group in 256-row tiles, output group columns in BN tiles,
-  // every type's rows (M / q of a cyclic schedule) in whole k-steps
-  return s % 256 == 0 && pick_bn(r) != 0 && p.M % (int64_t(kBKDw) * p.q) == 0 && p.M >= int64_t(kBKDw) * p.q;
+  // features of a group in 256- or 192-row tiles, output group columns in BN
+  // tiles; rows in 32-row k-steps (a type's last k-step reads zeros past its rows)
+  return pick_bm_dw(s) != 0 && pick_bn(r) != 0 && p.M >= int64_t(kBKDw) * p.q;
 }
 
 hipError_t launch_grad_persistent_bf16(const ProblemDesc& p, hipStream_t s) {
-  const int bn = pick_bn(p.op == Op::Dx ? p.K / p.q : p.N / p.q);
-  if (p.op == Op::Dx) {
-    if (bn == 256) return launch_grad<DxCfg<256>, Op::Dx>(p, s);
-    if (bn == 192) return launch_grad<DxCfg<192>, Op::Dx>(p, s);
-    return launch_grad<DxCfg<128>, Op::Dx>(p, s);
-  }
-  if (bn == 256) return launch_grad<DwCfg<256>, Op::Dw>(p, s);
-  if (bn == 192) return launch_grad<DwCfg<192>, Op::Dw>(p, s);
-  return launch_grad<DwCfg<128>, Op::Dw>(p, s);
+  if (p.op == Op::Dx) return p.law_L > 0 ? launch_op<Op::Dx, true>(p, s) : launch_op<Op::Dx, false>(p, s);
+  return p.law_L > 0 ? launch_op<Op::Dw, true>(p, s) : launch_op<Op::Dw, false>(p, s);
 }
 
 }  // namespace qalg

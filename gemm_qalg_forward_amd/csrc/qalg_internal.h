@@ -26,6 +26,8 @@ constexpr int tile_height_slot(int bm) {
 //   [.., +q+1)     offsets[q+1]              (running sums of counts)
 //   [.., +5(q+1))  tile_off[5][q+1]          (running sums of ceil(M_i / BM))
 //   [rows, +M)     rows[M]                   (rows of type 0, 1, ..., then bad rows)
+//   then at least 64 spare ints, so that kernels may read row ids in whole
+//   groups of up to 64 past the end of the list (the extra ids are never used)
 constexpr int32_t kIndexMagic = 0x51414c47;  // "QALG"
 
 struct WsLayout {
@@ -39,7 +41,7 @@ inline WsLayout ws_layout(int q, int64_t M) {
   L.tile_off = L.offsets + (q + 1);
   int64_t end = L.tile_off + int64_t(kNumTileHeights) * (q + 1);
   L.rows = (end + 15) / 16 * 16;
-  L.total_ints = (L.rows + M + 63) / 64 * 64;
+  L.total_ints = (L.rows + M + 64 + 63) / 64 * 64;
   return L;
 }
 
@@ -89,9 +91,7 @@ constexpr int kDwMaxSplits = 16;
 // unequal group widths: at most this many groups (the tables ride in the kernel arguments)
 constexpr int kMaxWidthGroups = 64;
 
-// skip_cyclic: the kernel returns at once when the index says the schedule is
-// cyclic (a persistent kernel launched beside it covers that case).
-hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s, bool skip_cyclic = false);
+hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s);
 hipError_t launch_tiled_f32(const ProblemDesc& p, hipStream_t s);
 // the two-stage forward (diagonal maps over all rows into p.fwd_diag, then the strips); bf16, complete law
 hipError_t launch_tiled_two_stage_bf16(const ProblemDesc& p, hipStream_t s);

@@ -32,11 +32,14 @@
 // (v_permlane32_swap) so that each lane stores 16 contiguous bytes.
 #include <type_traits>
 
+#include "qalg_device.h"
 #include "qalg_internal.h"
 
 namespace qalg {
 
 namespace {
+
+using dev::law_member;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -73,7 +76,6 @@ struct Args {
   int ct_per_group;                  // column tiles per output group
   int n_ct;                          // all column tiles (q * ct_per_group)
   int tm_dw, tn_dw;                  // dW: tiles per block along rows / columns
-  int skip_cyclic;                   // return at once when the index says the schedule is cyclic
   int L;                             // recursive law Q_2^(x)L (TENSOR kernels); 0 otherwise
   const uint64_t* adj;               // graph law Q_G (GRAPH kernels): out-edge mask of each type
   // unequal group widths (WIDTHS kernels, q <= kMaxWidthGroups): group starts
@@ -95,16 +97,7 @@ struct Args {
 //   dW[g_b, g_j] sums over the rows of the types i that agree with b wherever
 //     b differs from j (2^(L - |b ^ j|) types).
 // In both, segment n fixes the free bits (the bits where the two given indices
-// agree) to n's bits in order.
-__device__ __forceinline__ int law_member(int fixed_from, int fixed_mask, int n, int L) {
-  int g = fixed_from & fixed_mask;
-  for (int k = 0; k < L; ++k)
-    if (!((fixed_mask >> k) & 1)) {
-      if (n & 1) g |= 1 << k;
-      n >>= 1;
-    }
-  return g;
-}
+// agree) to n's bits in order (law_member).
 
 // Graph law Q_G (section 3.1, eq 9-12): B(i, i) = {i}, B(i, j) = {i, j} when
 // (i, j) is an edge and empty otherwise.  Transposed for the VJPs:
@@ -211,7 +204,6 @@ __global__ __launch_bounds__(C::THREADS) void tiled_bf16_kernel(Args a) {
   // an index of another (q, M) is never trusted: no row id is read from it
   if (ws[1] != kIndexMagic || ws[2] != q || ws[3] != a.M) return;
   // cyclic schedules are handled by the persistent kernel launched beside this one
-  if (a.skip_cyclic && ws[4] >= 0) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / C::WGN, wn = wid % C::WGN;
@@ -1091,12 +1083,11 @@ dim3 grid_for(const ProblemDesc& p, const Args& a, int bm, int sched = kFused) {
 }
 
 template <Op OP, class C, int SCHED = kFused>
-hipError_t launch_cfg(const ProblemDesc& p, hipStream_t s, bool skip_cyclic) {
+hipError_t launch_cfg(const ProblemDesc& p, hipStream_t s) {
   Args a = make_args(p, C::BM, C::BN);
-  a.skip_cyclic = skip_cyclic ? 1 : 0;
   a.L = p.law_L;
   // (not beside the persistent kernel: there this launch may return at once)
-  if (OP == Op::Dw && p.dw_part != nullptr && p.E == 1 && !skip_cyclic) {
+  if (OP == Op::Dw && p.dw_part != nullptr && p.E == 1) {
     // enough workgroups to cover the CUs about four times, at most kDwMaxSplits per tile
     const int64_t tiles = dw_tiles(p, a);
     int64_t sp = (4 * 256 + tiles - 1) / tiles;
@@ -1196,39 +1187,39 @@ int fwd_small_bn(int64_t r) {
 
 }  // namespace
 
-hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s, bool skip_cyclic) {
+hipError_t launch_tiled_bf16(const ProblemDesc& p, hipStream_t s) {
   // Row-tile height from the rows per type (tiles never straddle types).
   const int64_t per_type = p.op == Op::Dw ? p.K / p.q : (p.M + p.q - 1) / p.q;
   switch (p.op) {
     case Op::Fwd:
       // wide tiles where every type has rows for several and the output groups divide evenly
-      if (per_type >= 512 && cols_exact(p, 256)) return launch_cfg<Op::Fwd, CfgW256>(p, s, skip_cyclic);
-      if (per_type >= 128) return launch_cfg<Op::Fwd, Cfg128>(p, s, skip_cyclic);
+      if (per_type >= 512 && cols_exact(p, 256)) return launch_cfg<Op::Fwd, CfgW256>(p, s);
+      if (per_type >= 128) return launch_cfg<Op::Fwd, Cfg128>(p, s);
       if (p.in_widths == nullptr) {
         const int bn = fwd_small_bn(p.N / p.q);
         if (bn == 256)
-          return per_type >= 48 ? launch_cfg<Op::Fwd, CfgN64>(p, s, skip_cyclic)
-                                : launch_cfg<Op::Fwd, CfgN32>(p, s, skip_cyclic);
+          return per_type >= 48 ? launch_cfg<Op::Fwd, CfgN64>(p, s)
+                                : launch_cfg<Op::Fwd, CfgN32>(p, s);
         if (bn == 128)
-          return per_type >= 48 ? launch_cfg<Op::Fwd, CfgM64>(p, s, skip_cyclic)
-                                : launch_cfg<Op::Fwd, CfgM32>(p, s, skip_cyclic);
+          return per_type >= 48 ? launch_cfg<Op::Fwd, CfgM64>(p, s)
+                                : launch_cfg<Op::Fwd, CfgM32>(p, s);
       }
-      if (per_type >= 48) return launch_cfg<Op::Fwd, Cfg64>(p, s, skip_cyclic);
-      return launch_cfg<Op::Fwd, Cfg32>(p, s, skip_cyclic);
+      if (per_type >= 48) return launch_cfg<Op::Fwd, Cfg64>(p, s);
+      return launch_cfg<Op::Fwd, Cfg32>(p, s);
     case Op::Dx:
       // (not for graph laws: their dX tiles range from no work to q segments, and the
       // smaller tiles balance that better)
       if (per_type >= 512 && cols_exact(p, 256) && p.graph_adj == nullptr)
-        return launch_cfg<Op::Dx, CfgW256>(p, s, skip_cyclic);
-      if (per_type >= 128) return launch_cfg<Op::Dx, Cfg128>(p, s, skip_cyclic);
-      if (per_type >= 48) return launch_cfg<Op::Dx, Cfg64>(p, s, skip_cyclic);
-      return launch_cfg<Op::Dx, Cfg32>(p, s, skip_cyclic);
+        return launch_cfg<Op::Dx, CfgW256>(p, s);
+      if (per_type >= 128) return launch_cfg<Op::Dx, Cfg128>(p, s);
+      if (per_type >= 48) return launch_cfg<Op::Dx, Cfg64>(p, s);
+      return launch_cfg<Op::Dx, Cfg32>(p, s);
     case Op::Dw:
-      if (dw_tiles_exact(p, 256, 256)) return launch_cfg<Op::Dw, CfgW256>(p, s, skip_cyclic);
-      if (dw_tiles_exact(p, 192, 256)) return launch_cfg<Op::Dw, CfgW192>(p, s, skip_cyclic);
-      if (dw_tiles_exact(p, 192, 192)) return launch_cfg<Op::Dw, CfgW192n>(p, s, skip_cyclic);
-      if (per_type >= 128) return launch_cfg<Op::Dw, Cfg128>(p, s, skip_cyclic);
-      return launch_cfg<Op::Dw, Cfg64>(p, s, skip_cyclic);
+      if (dw_tiles_exact(p, 256, 256)) return launch_cfg<Op::Dw, CfgW256>(p, s);
+      if (dw_tiles_exact(p, 192, 256)) return launch_cfg<Op::Dw, CfgW192>(p, s);
+      if (dw_tiles_exact(p, 192, 192)) return launch_cfg<Op::Dw, CfgW192n>(p, s);
+      if (per_type >= 128) return launch_cfg<Op::Dw, Cfg128>(p, s);
+      return launch_cfg<Op::Dw, Cfg64>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1243,12 +1234,12 @@ hipError_t launch_tiled_two_stage_bf16(const ProblemDesc& p, hipStream_t s) {
   const int bn = fwd_small_bn(p.N / p.q);
   auto pick = [&](int64_t rows, auto sched) -> hipError_t {
     constexpr int SC = decltype(sched)::value;
-    if (rows >= 128) return launch_cfg<Op::Fwd, Cfg128, SC>(p, s, false);
-    if (bn == 256) return rows >= 48 ? launch_cfg<Op::Fwd, CfgN64, SC>(p, s, false)
-                                     : launch_cfg<Op::Fwd, CfgN32, SC>(p, s, false);
-    if (bn == 128) return rows >= 48 ? launch_cfg<Op::Fwd, CfgM64, SC>(p, s, false)
-                                     : launch_cfg<Op::Fwd, CfgM32, SC>(p, s, false);
-    return rows >= 48 ? launch_cfg<Op::Fwd, Cfg64, SC>(p, s, false) : launch_cfg<Op::Fwd, Cfg32, SC>(p, s, false);
+    if (rows >= 128) return launch_cfg<Op::Fwd, Cfg128, SC>(p, s);
+    if (bn == 256) return rows >= 48 ? launch_cfg<Op::Fwd, CfgN64, SC>(p, s)
+                                     : launch_cfg<Op::Fwd, CfgN32, SC>(p, s);
+    if (bn == 128) return rows >= 48 ? launch_cfg<Op::Fwd, CfgM64, SC>(p, s)
+                                     : launch_cfg<Op::Fwd, CfgM32, SC>(p, s);
+    return rows >= 48 ? launch_cfg<Op::Fwd, Cfg64, SC>(p, s) : launch_cfg<Op::Fwd, Cfg32, SC>(p, s);
   };
   const hipError_t e = pick(p.M, std::integral_constant<int, kDiag>{});
   if (e != hipSuccess) return e;
@@ -1261,12 +1252,12 @@ hipError_t launch_tiled_masked_bf16(const ProblemDesc& p, hipStream_t s) {
   const int bn = fwd_small_bn(p.N / p.q);
   const int64_t rows = p.M;
   constexpr int SC = kMasked;
-  if (rows >= 128) return launch_cfg<Op::Fwd, Cfg128, SC>(p, s, false);
-  if (bn == 256) return rows >= 48 ? launch_cfg<Op::Fwd, CfgN64, SC>(p, s, false)
-                                   : launch_cfg<Op::Fwd, CfgN32, SC>(p, s, false);
-  if (bn == 128) return rows >= 48 ? launch_cfg<Op::Fwd, CfgM64, SC>(p, s, false)
-                                   : launch_cfg<Op::Fwd, CfgM32, SC>(p, s, false);
-  return rows >= 48 ? launch_cfg<Op::Fwd, Cfg64, SC>(p, s, false) : launch_cfg<Op::Fwd, Cfg32, SC>(p, s, false);
+  if (rows >= 128) return launch_cfg<Op::Fwd, Cfg128, SC>(p, s);
+  if (bn == 256) return rows >= 48 ? launch_cfg<Op::Fwd, CfgN64, SC>(p, s)
+                                   : launch_cfg<Op::Fwd, CfgN32, SC>(p, s);
+  if (bn == 128) return rows >= 48 ? launch_cfg<Op::Fwd, CfgM64, SC>(p, s)
+                                   : launch_cfg<Op::Fwd, CfgM32, SC>(p, s);
+  return rows >= 48 ? launch_cfg<Op::Fwd, Cfg64, SC>(p, s) : launch_cfg<Op::Fwd, Cfg32, SC>(p, s);
 }
 
 hipError_t launch_tiled_f32(const ProblemDesc& p, hipStream_t s) {

@@ -31,12 +31,17 @@ def tau_dev(tau: np.ndarray):
 
 
 def make_tau(kind: str, M: int, q: int, seed: int = 0, offset: int = 0, bad: int = 0) -> np.ndarray:
-    """Types for a test: 'cyclic' ((m + offset) mod q) or 'random'; `bad` rows get out-of-range types."""
+    """Types for a test: 'cyclic' ((m + offset) mod q), 'random', or 'absent' (random without type 1);
+    `bad` rows get out-of-range types."""
     if kind == "cyclic":
         tau = ((np.arange(M) + offset) % q).astype(np.int32)
     elif kind == "random":
         g = np.random.Generator(np.random.PCG64(seed))
         tau = g.integers(0, q, size=M).astype(np.int32)
+    elif kind == "absent":
+        g = np.random.Generator(np.random.PCG64(seed))
+        tau = g.integers(0, q - 1, size=M).astype(np.int32)
+        tau[tau >= 1] += 1
     elif kind == "zeros":
         tau = np.zeros(M, np.int32)
     else:

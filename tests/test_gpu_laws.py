@@ -125,6 +125,11 @@ LAW_GRAD_SHAPES = [
     (1000, 512, 1024, 2, "random", 9),      # listed types, out-of-range rows
     (512, 256, 512, 3, "cyclic", 0),
     (777, 256, 512, 1, "cyclic", 0),        # L = 1 is Q_2
+    # persistent dX / dW: 256- and 192-feature tiles, listed rows, ragged types, every class
+    (1000, 1024, 1024, 2, "random", 9),     # ragged row counts (dW's last k-step of a type partly empty)
+    (2050, 2048, 2048, 3, "cyclic", 0),     # L = 3, cyclic with M / q not a whole k-step
+    (3000, 1536, 1536, 3, "random", 11),    # L = 3 on listed rows, 192 x 192 dW tiles
+    (2000, 1024, 2048, 2, "absent", 4),     # a type without rows
 ]
 
 
@@ -203,16 +208,18 @@ def test_pilot_gated_training_step_matches_oracle():
 SPLIT_SHAPES = [
     # M, K, N, L (0: Q_q), q, tau kind
     (3072, 768, 1536, 2, 4, "interval"),   # the pilot's up dW under Q_2^(x)2
-    (3072, 1536, 768, 0, 4, "interval"),   # Q_4 on the interval schedule (register-staged dW)
+    (3072, 1536, 768, 0, 4, "interval"),   # Q_4 on the interval schedule (listed rows)
     (1000, 512, 1024, 0, 4, "random"),
     (512, 256, 512, 3, 8, "cyclic"),       # the recursive law on a cyclic schedule
+    (1000, 1024, 1024, 2, 4, "random"),    # persistent pieces of every class on listed rows
+    (2050, 2048, 2048, 3, 8, "cyclic"),    # L = 3, all four classes split
 ]
 
 
 @pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=[f"M{s[0]}K{s[1]}N{s[2]}L{s[3]}q{s[4]}{s[5]}" for s in SPLIT_SHAPES])
 def test_dw_split_contraction_matches_oracle(shape):
-    """dW with a workspace of qalg_workspace_bytes_dw: the register-staged path splits each tile's
-    contraction and sums the fp32 partials in a fixed order (bitwise reproducible)."""
+    """dW with a workspace of qalg_workspace_bytes_dw: each tile's contraction is split into pieces
+    whose fp32 partials are summed in a fixed order (bitwise reproducible)."""
     torch = torch_cuda()
     M, K, N, L, q, kind = shape
     say(f"[dw split] M={M} K={K} N={N} L={L} q={q} tau={kind}")

@@ -31,7 +31,9 @@ SHAPES = [
     (2600, 1024, 2304, 4, "cyclic", 0, 0),   # persistent 256x192 tiles (r = 576 = 3 x 192)
     (2048, 1024, 1536, 4, "cyclic", 1, 0),   # persistent dX and dW (dW tiles 256x192)
     (4096, 2048, 2048, 8, "cyclic", 3, 0),   # persistent dX and dW (256x256), long/short balance
-    (2100, 768, 512, 4, "random", 0, 7),     # listed types, 525 rows per type: register-staged dX and dW
+    (2100, 768, 512, 4, "random", 0, 7),     # listed types, ~525 rows per type: persistent dX, dW 192x128
+    (3000, 1024, 1024, 4, "random", 0, 11),  # listed, ragged row counts: dW's last k-step of a type half empty
+    (2500, 1536, 768, 3, "absent", 0, 6),    # listed, one type without rows: zero dW blocks, no dX tiles
 ]
 
 
@@ -333,8 +335,9 @@ DW_SPLIT_SHAPES = [
     (4096, 2048, 2048, 8, "cyclic", 3),   # 16 pieces of 8 k-steps per diagonal tile
     (2048, 1024, 1536, 4, "cyclic", 1),   # 256x192 tiles, 16 pieces
     (2048, 512, 512, 1, "zeros", 0),      # q = 1: every tile is diagonal
-    (2048, 1024, 1536, 4, "random", 0),   # listed schedule: no split, the reduction must not touch dW
+    (2048, 1024, 1536, 4, "random", 0),   # listed schedule: row ids from the index, split
     (3072, 768, 768, 3, "cyclic", 2),     # odd q: 16 pieces of 6 k-steps
+    (3000, 768, 1536, 4, "random", 0),    # listed, 192-feature tiles, ragged types, short tiles split too
 ]
 
 
