@@ -70,17 +70,28 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // LDS piece swizzles.  A contraction-major tile (rows of 32 contraction
-// values, 64 bytes) keeps row r's 16-byte piece c at c ^ ((r >> 1) & 3); a
-// row-major tile (32 contraction rows of R values) keeps row k's piece c at
-// c ^ 2 (k & 3).  Both make 8 consecutive lanes of the fragment reads and of
-// the 1 KB direct-to-LDS copies touch distinct bank groups.
+// values, 64 bytes) keeps row r's 16-byte piece c at c ^ ((r >> 1) & 3), so
+// that 8 consecutive lanes of the fragment reads and of the 1 KB
+// direct-to-LDS copies touch distinct bank groups.
 __device__ __forceinline__ int swz_x(int row) { return (row >> 1) & 3; }
 // Contraction-major tile with rows of 64 contraction values (128 bytes): row
 // r keeps its piece c at c ^ ((r >> 1) & 7), so that the 16 rows a
 // quarter-wave reads, and the 8 rows a 1 KB copy writes, fall in distinct
 // bank groups.
 __device__ __forceinline__ int swz_x128(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int swz_w(int k) { return 2 * (k & 3); }
+// Row-major tile (contraction rows of ROWB bytes, read with the transposing
+// ds_read_b64_tr_b16): row k keeps its 64-byte group g (the 32 columns of one
+// MFMA fragment) at g ^ s(k).  Half a wave of such a read takes 64 bytes from
+// each of 4 consecutive rows, and the LDS serves 256 bytes (64 banks) per
+// pass: s(k) = k & 3 when rows are a multiple of 256 bytes long, and
+// (k >> 1) & 1 when they are 128 bytes past one, put the 4 groups in the 4
+// distinct quarters of the bank window.  Returned as a mask on the 16-byte
+// piece index.
+template <int ROWB>
+__device__ __forceinline__ int swz_rm(int k) {
+  static_assert(ROWB % 128 == 0 && ROWB >= 256, "row-major tile rows");
+  return ROWB % 256 == 0 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+}
 
 __device__ __forceinline__ u32x2 pack4_bf16(float a, float b, float c, float d) {
   const bf16x2 lo = __builtin_convertvector((f32x2){a, b}, bf16x2);

@@ -43,12 +43,14 @@
 // the matrix cores see a steady stream instead of bursts of other
 // instructions.
 //
-// LDS layouts (both bank-conflict free for the patterns used):
+// LDS layouts (the LDS serves 256 bytes, 64 banks, per pass; both layouts
+// keep every pass of the reads used here on distinct banks):
 //  * X tile: row r of the tile keeps its eight 16-byte pieces (8 contraction
 //    values each) at piece c ^ ((r >> 1) & 7).  MFMA fragments are plain
 //    128-bit reads (lane: row l % 32, piece 2*ks + l / 32 for quarter ks).
-//  * W tile: contraction row k keeps the tile's BN columns in 16-byte pieces
-//    at piece c ^ 2*(k & 3), i.e. the weight bank's own row-major layout.  The
+//  * W tile: contraction row k keeps the tile's BN columns in the weight
+//    bank's own row-major order, its 64-byte groups (32 columns) permuted by
+//    g ^ s(k) (swz_rm: k & 3 for BN 256 and 128, (k >> 1) & 1 for BN 192).  The
 //    MFMA needs 8 consecutive contraction values per lane, so the fragment is
 //    read with two ds_read_b64_tr_b16 (gfx950 transposing LDS read): in a
 //    16-lane group, lane t's element e comes from element t % 4 of the
@@ -368,7 +370,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   for (int u = 0; u < C::B_DMA; ++u) {
     const int sl = (wid * C::B_DMA + u) * 64 + lane;
     const int k = sl / C::NCH, p = sl - (sl / C::NCH) * C::NCH;
-    const int c = p ^ swz_w(k);
+    const int c = p ^ swz_rm<C::ROWB>(k);
     b_src[u] = uint32_t(k) * n_bytes + uint32_t(c) * 16u;
   }
   int a_row[C::A_DMA];   // tile-local row of each X copy slot, and its swizzled piece
@@ -487,18 +489,18 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   // W fragment (32 columns x 16 contraction) as two transposing 8-byte reads per lane:
   // in a 16-lane group (g = lane / 16, t = lane % 16) lane t reads row 8*(g/2) + t/4 (+4),
   // columns 16*(g%2) + 4*(t%4) of the fragment; the transpose hands lane t column t, 4 rows.
-  int b_rd[2];  // by parity of the fragment's 32-column block index
+  // b_rd[fn]: the lane's offset for the wave's fragment fn (32-column block m0 + fn,
+  // stored as group (m0 + fn) ^ s(row)); a row 4 or 16 further has the same s.
+  const int m0 = wn * (C::WTN / 32);  // block index of the wave's first 32-column block
+  int b_rd[C::FN];
   {
     const int g = lane >> 4, t = lane & 15;
     const int k_l = 8 * (g >> 1) + (t >> 2);
-    const int f = swz_w(k_l);
     const int r2 = 2 * (g & 1) + ((t & 3) >> 1);
-    const int lo = ((r2 ^ (f & 2)) << 4) + 8 * (t & 1) + k_l * C::ROWB;
-    const int dm = (f >> 2) ? 64 : 0;  // block-index bit flipped by the swizzle
-    b_rd[0] = C::A_BYTES + lo + dm;
-    b_rd[1] = C::A_BYTES + lo - dm;
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+      b_rd[fn] = C::A_BYTES + k_l * C::ROWB + ((((m0 + fn) * 4) ^ swz_rm<C::ROWB>(k_l)) + r2) * 16 + 8 * (t & 1);
   }
-  const int m0 = wn * (C::WTN / 32);  // block index of the wave's first 32-column block
 
   f32x16 acc[C::FM][C::FN];
   // fragments of the two 16-wide halves of a k-step (registers double buffered)
@@ -507,8 +509,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
     return *reinterpret_cast<const bf16x8*>(smem + stage * C::STAGE + a_rd[ks] + fm * 32 * C::AROWB);
   };
   auto read_b = [&](int stage, int ks, int fn) -> bf16x8 {
-    const int m = m0 + fn;
-    const char* p = smem + stage * C::STAGE + b_rd[m & 1] + 64 * m + 16 * ks * C::ROWB;
+    const char* p = smem + stage * C::STAGE + b_rd[fn] + 16 * ks * C::ROWB;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * C::ROWB));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -530,8 +531,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
       fa[fm] = *reinterpret_cast<const bf16x8*>(S + a_rd[ks] + fm * 32 * C::AROWB);
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
-      const int m = m0 + fn;
-      const char* p = S + b_rd[m & 1] + 64 * m + 16 * ks * C::ROWB;
+      const char* p = S + b_rd[fn] + 16 * ks * C::ROWB;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * C::ROWB));
       fb[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));

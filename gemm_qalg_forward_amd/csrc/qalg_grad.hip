@@ -423,7 +423,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
       a_c[u] = (sl % C::KPC) ^ swz_km<C::BK>(sl / C::KPC);
     } else {
       a_r[u] = sl / C::A_NCH;
-      a_c[u] = (sl - (sl / C::A_NCH) * C::A_NCH) ^ swz_w(sl / C::A_NCH);
+      a_c[u] = (sl - (sl / C::A_NCH) * C::A_NCH) ^ swz_rm<C::A_ROWB>(sl / C::A_NCH);
     }
   }
 #pragma unroll
@@ -434,7 +434,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
       b_c[u] = (sl % C::KPC) ^ swz_km<C::BK>(sl / C::KPC);
     } else {
       b_r[u] = sl / C::B_NCH;
-      b_c[u] = (sl - (sl / C::B_NCH) * C::B_NCH) ^ swz_w(sl / C::B_NCH);
+      b_c[u] = (sl - (sl / C::B_NCH) * C::B_NCH) ^ swz_rm<C::B_ROWB>(sl / C::B_NCH);
     }
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(smem)));
@@ -684,26 +684,36 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
   const int l32 = lane & 31, lhi = lane >> 5;
   // contraction-major operand: 128-bit read of row l32, piece 2*ks + lhi
   auto km_rd = [&](int w0, int ks) { return (w0 + l32) * C::KROWB + (((2 * ks + lhi) ^ swz_km<C::BK>(l32)) << 4); };
-  // row-major operand with rows of rowb bytes: per-lane offsets of the two
-  // transposing reads, by parity of the fragment's 32-column block index
-  auto rm_rd = [&](int rowb, int par) {
-    const int gq = lane >> 4, t = lane & 15;
-    const int k_l = 8 * (gq >> 1) + (t >> 2);
-    const int f = swz_w(k_l);
-    const int r2 = 2 * (gq & 1) + ((t & 3) >> 1);
-    const int lo = ((r2 ^ (f & 2)) << 4) + 8 * (t & 1) + k_l * rowb;
-    const int dm = (f >> 2) ? 64 : 0;
-    return par == 0 ? lo + dm : lo - dm;
-  };
-  // contraction-major: one offset per quarter step; row-major: one per
-  // parity of the 32-column block index (entries 2, 3 unused)
+  // contraction-major operands: one offset per quarter step
   int a_rd[C::Q], b_rd[C::Q];
 #pragma unroll
   for (int x = 0; x < C::Q; ++x) {
-    a_rd[x] = C::A_KM ? km_rd(wm * C::WTM, x) : rm_rd(C::A_ROWB, x & 1);
-    b_rd[x] = C::A_BYTES + (C::B_KM ? km_rd(wn * C::WTN, x) : rm_rd(C::B_ROWB, x & 1));
+    a_rd[x] = C::A_KM ? km_rd(wm * C::WTM, x) : 0;
+    b_rd[x] = C::A_BYTES + (C::B_KM ? km_rd(wn * C::WTN, x) : 0);
   }
   const int am0 = wm * (C::WTM / 32), bm0 = wn * (C::WTN / 32);
+  // row-major operands, read with the transposing LDS read: in a 16-lane group
+  // (gq = lane / 16, t = lane % 16) lane t reads row 8*(gq/2) + t/4 (+4),
+  // columns 16*(gq%2) + 4*(t%4) of the 32-column block; the lane's offset for
+  // each of the wave's fragments (block am0 + fm or bm0 + fn, stored as group
+  // block ^ s(row); rows 4 and 16 further have the same s)
+  int a_rm[C::A_KM ? 1 : C::FM], b_rm[C::B_KM ? 1 : C::FN];
+  {
+    const int gq = lane >> 4, t = lane & 15;
+    const int k_l = 8 * (gq >> 1) + (t >> 2);
+    const int r2 = 2 * (gq & 1) + ((t & 3) >> 1);
+    if constexpr (!C::A_KM) {
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+        a_rm[fm] = k_l * C::A_ROWB + ((((am0 + fm) * 4) ^ swz_rm<C::A_ROWB>(k_l)) + r2) * 16 + 8 * (t & 1);
+    }
+    if constexpr (!C::B_KM) {
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+        b_rm[fn] = C::A_BYTES + k_l * C::B_ROWB + ((((bm0 + fn) * 4) ^ swz_rm<C::B_ROWB>(k_l)) + r2) * 16 +
+                   8 * (t & 1);
+    }
+  }
 
   f32x16 acc[C::FM][C::FN];
   bf16x8 fa0[C::FM], fb0[C::FN], fa1[C::FM], fb1[C::FN];
@@ -712,8 +722,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
     if constexpr (C::A_KM) {
       return *reinterpret_cast<const bf16x8*>(S + a_rd[ks] + fm * 32 * C::KROWB);
     } else {
-      const int m = am0 + fm;
-      const char* p = S + a_rd[m & 1] + 64 * m + 16 * ks * C::A_ROWB;
+      const char* p = S + a_rm[fm] + 16 * ks * C::A_ROWB;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * C::A_ROWB));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -724,8 +733,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
     if constexpr (C::B_KM) {
       return *reinterpret_cast<const bf16x8*>(S + b_rd[ks] + fn * 32 * C::KROWB);
     } else {
-      const int m = bm0 + fn;
-      const char* p = S + b_rd[m & 1] + 64 * m + 16 * ks * C::B_ROWB;
+      const char* p = S + b_rm[fn] + 16 * ks * C::B_ROWB;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p));
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * C::B_ROWB));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
