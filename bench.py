@@ -137,27 +137,43 @@ class Protocol:
 
 
 def sclk_sampler(torch):
-    """A function returning the shader clock (MHz) of GPU 0 from its hwmon node, or None when the
-    node is not visible.  The card is found by its PCI address."""
+    """A function returning the shader clock (MHz) of GPU 0, or None when no source is visible:
+    the hwmon node of the GPU's PCI device, else its pp_dpm_sclk table (the entry marked '*' is
+    the current clock).  The card is found by its PCI address."""
     import glob
+    import re
     try:
         pr = torch.cuda.get_device_properties(0)
         dom, bus, devn = (getattr(pr, "pci_domain_id", 0), getattr(pr, "pci_bus_id", None),
                           getattr(pr, "pci_device_id", 0))
         if bus is None:
             return None
-        paths = glob.glob(f"/sys/bus/pci/devices/{dom:04x}:{bus:02x}:{devn:02x}.0/hwmon/hwmon*/freq1_input")
-        if not paths:
-            return None
-        path = paths[0]
+        node = f"/sys/bus/pci/devices/{dom:04x}:{bus:02x}:{devn:02x}.0"
+        hw = glob.glob(f"{node}/hwmon/hwmon*/freq1_input")
+        dpm = glob.glob(f"{node}/pp_dpm_sclk")
 
-        def read():
+        def read_hwmon():
             try:
-                with open(path) as f:
+                with open(hw[0]) as f:
                     return int(f.read().strip()) / 1e6
             except (OSError, ValueError):
                 return None
-        return read if read() is not None else None
+
+        def read_dpm():
+            try:
+                with open(dpm[0]) as f:
+                    for line in f:
+                        if line.rstrip().endswith("*"):
+                            m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                            return float(m.group(1)) if m else None
+            except OSError:
+                return None
+            return None
+        for read in ((read_hwmon,) if hw else ()) + ((read_dpm,) if dpm else ()):
+            if read() is not None:
+                read.source = "hwmon freq1_input" if read is read_hwmon else "pp_dpm_sclk (current entry)"
+                return read
+        return None
     except Exception:  # informational only
         return None
 
@@ -190,7 +206,7 @@ def sustained_clock(torch, np, g, seconds=0.4):
     f = float(np.median(vals))
     return {"sclk_mhz_median": round(f, 1), "samples": len(vals),
             "peak_at_clock_tflops": round(256 * f * 1e6 * 4096 / 1e12, 1),
-            "source": "hwmon freq1_input of the GPU's PCI device, sampled during back-to-back replays"}
+            "source": f"{read.source} of the GPU's PCI device, sampled during back-to-back replays"}
 
 
 def parse():
