@@ -380,8 +380,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
 // query heads' values of those features in registers.  A wave covers 64 / (D / 8)
 // slots at a time.  Scores: each lane loads its key piece only when the piece's
 // group is in F(i, j) (so only the compared groups are read), multiplies it
-// with its query features, and the group's lanes sum the G partial dot
-// products with a butterfly; all key pieces of the chunk are in flight before
+// with its query features (v_dot2_f32_bf16), and the group's lanes sum the G
+// partial dot products with DPP row shifts (and a permlane exchange across
+// rows for 32-lane groups); all key pieces of the chunk are in flight before
 // the first is used.  Then one wave per query head takes the chunk max and the
 // exponentials.  Values: the same lane/piece map over the value rows of the
 // allowed slots, fp32 sums per head, reduced across the lane groups of a wave
