@@ -38,7 +38,10 @@ What is computed, plainly:
   score: a query of type i and a key of type j compare only the feature groups
   F(i, j) ({i} or {i, j}, eq 38; eq 42 for the recursive law), scaled by
   1 / sqrt(|F| m) (eq 41), then the causal softmax and a dense PV (eq 43-44);
-  `attention_score_macs` counts its score and value MACs (eq 45).
+  `attention_score_macs` counts its score and value MACs (eq 45);
+  `algebraic_attention_backward` gives its gradients (Algorithm 2, step 9):
+  the softmax and value-sum VJPs, and the score's gradient routed to the
+  compared groups only.
 * `algebraic_attention_decode` is appendix G's cached decoding (Algorithm 3,
   the loop over cached positions and the softmax / value sum): one new query
   row per sequence against that sequence's full-key cache, each key's type
@@ -97,6 +100,7 @@ __all__ = [
     "gated_forward",
     "score_support",
     "algebraic_attention",
+    "algebraic_attention_backward",
     "attention_score_macs",
     "algebraic_attention_decode",
     "attention_decode_macs",
@@ -529,6 +533,69 @@ def algebraic_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, tau: np.nda
         P /= P.sum(axis=1, keepdims=True)
         O[h] = P @ V[kv]
     return O
+
+
+
+def algebraic_attention_backward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray,
+                                 tau: np.ndarray, q: int, L: int = 0,
+                                 positions: np.ndarray | None = None):
+    """Gradients of `algebraic_attention` (Algorithm 2, step 9: backpropagation through steps
+    3-7), returned as (dQ, dK, dV) with the shapes of Q, K, V.
+
+    With r, s, P as in the forward (eq 39-44) and the incoming gradient dO of the outputs, per
+    query head (chain rule through each step, last step first):
+        dV_u     = sum_p P_pu dO_p                                (the dense PV, transposed)
+        dP_pu    = <dO_p, V_u>
+        dS_pu    = P_pu (dP_pu - sum_u' P_pu' dP_pu')             (the row softmax)
+        dR_pu    = dS_pu / sqrt(|F(i, j)| m)                      (eq 41's scale)
+        dQ_p^(a) = sum_u dR_pu K_u^(a),  dK_u^(a) = sum_p dR_pu Q_p^(a),  for a in F(i, j) only
+                                                                  (eq 39: r is bilinear in the
+                                                                   compared groups)
+    Masked pairs (eq 43) have P = 0 and contribute nothing.  A key/value head's dK and dV sum
+    over the query heads that read it (GQA).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    Hq, S, d = Q.shape
+    Hkv = K.shape[0]
+    if d % q or Hq % Hkv or K.shape[1:] != (S, d) or V.shape != K.shape or dO.shape != Q.shape:
+        raise ValueError("shapes")
+    m = d // q
+    tau = np.asarray(tau)
+    pos = np.arange(S) if positions is None else np.asarray(positions)
+    allowed = pos[None, :] <= pos[:, None]
+    sel = np.zeros((q, S, S), dtype=bool)
+    for i in range(q):
+        for j in range(q):
+            for a in score_support(i, j, q, L):
+                sel[a][np.ix_(tau == i, tau == j)] = True
+    k_pair = np.maximum(sel.sum(axis=0) * m, 1)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for h in range(Hq):
+        kv = h // (Hq // Hkv)
+        # forward again: scores over the compared groups, scale, causal softmax
+        r = np.zeros((S, S))
+        for a in range(q):
+            g = Q[h][:, a * m:(a + 1) * m] @ K[kv][:, a * m:(a + 1) * m].T
+            r += np.where(sel[a], g, 0.0)
+        s = np.where(allowed, r / np.sqrt(k_pair), -np.inf)
+        P = np.exp(s - s.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        # backward, step by step
+        dV[kv] += P.T @ dO[h]
+        dP = dO[h] @ V[kv].T
+        dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+        dR = dS / np.sqrt(k_pair)
+        for a in range(q):
+            ga = slice(a * m, (a + 1) * m)
+            dRa = np.where(sel[a], dR, 0.0)
+            dQ[h][:, ga] += dRa @ K[kv][:, ga]
+            dK[kv][:, ga] += dRa.T @ Q[h][:, ga]
+    return dQ, dK, dV
 
 
 def attention_score_macs(tau: np.ndarray, q: int, d: int, L: int = 0,

@@ -1023,6 +1023,98 @@ def pin_decode_macs(O):
     assert sm == want
 
 
+
+def _torch_algebraic_attention(Qt, Kt, Vt, tau, q, L, pos):
+    """A second, differentiable statement of appendix G's forward (fp64 torch): the compared
+    groups written out by hand (Q_q: the query's and the key's own groups; the recursive law:
+    the groups whose every bit is the query's or the key's), per pair scale 1/sqrt(|F| m),
+    causal mask on positions, softmax, dense PV."""
+    import torch
+    Hq, S, d = Qt.shape
+    Hkv = Kt.shape[0]
+    m = d // q
+    use = np.zeros((q, S, S))
+    for p_ in range(S):
+        for u in range(S):
+            i, j = int(tau[p_]), int(tau[u])
+            if L == 0:
+                groups = {i, j}
+            else:
+                groups = {a for a in range(q) if all((a >> k) & 1 in ((i >> k) & 1, (j >> k) & 1) for k in range(L))}
+            for a in groups:
+                use[a, p_, u] = 1.0
+    use_t = torch.tensor(use, dtype=torch.float64)
+    k = use_t.sum(0) * m
+    causal = torch.tensor(np.asarray(pos)[None, :] <= np.asarray(pos)[:, None])
+    outs = []
+    for h in range(Hq):
+        kv = h // (Hq // Hkv)
+        r = sum(use_t[a] * (Qt[h, :, a * m:(a + 1) * m] @ Kt[kv, :, a * m:(a + 1) * m].T) for a in range(q))
+        sc = torch.where(causal, r / torch.sqrt(k), torch.tensor(-float("inf"), dtype=torch.float64))
+        outs.append(torch.softmax(sc, dim=1) @ Vt[kv])
+    return torch.stack(outs)
+
+
+def pin_attention_backward_autograd(O, seed=58):
+    """Algorithm 2, step 9: the oracle's explicit gradients equal fp64 torch autograd of the
+    differentiable statement above, for Q_q with GQA at a position offset, the recursive law,
+    and q = 3 with one key/value head."""
+    import torch
+    g = _rng(seed)
+    for Hq, Hkv, S, d, q, L, p0 in ((4, 2, 11, 8, 4, 0, 5), (2, 2, 10, 8, 4, 2, 0), (2, 1, 9, 6, 3, 0, 2)):
+        Q = g.standard_normal((Hq, S, d))
+        K = g.standard_normal((Hkv, S, d))
+        V = g.standard_normal((Hkv, S, d))
+        dO = g.standard_normal((Hq, S, d))
+        pos = p0 + np.arange(S)
+        tau = pos % q
+        Qt, Kt, Vt = (torch.tensor(x, requires_grad=True) for x in (Q, K, V))
+        out = _torch_algebraic_attention(Qt, Kt, Vt, tau, q, L, pos)
+        (out * torch.tensor(dO)).sum().backward()
+        got = O.algebraic_attention_backward(Q, K, V, dO, tau, q, L, positions=pos)
+        for gg, want in zip(got, (Qt.grad, Kt.grad, Vt.grad)):
+            np.testing.assert_allclose(gg, want.numpy(), rtol=1e-11, atol=1e-11)
+
+
+def pin_attention_backward_q1_is_sdpa(O, seed=59):
+    """q = 1: the gradients of ordinary causal attention (fp64 torch autograd through
+    scaled_dot_product_attention; GQA by repeating the key/value heads, whose gradients then sum)."""
+    import torch
+    g = _rng(seed)
+    Hq, Hkv, S, d = 4, 2, 13, 8
+    Q = g.standard_normal((Hq, S, d))
+    K = g.standard_normal((Hkv, S, d))
+    V = g.standard_normal((Hkv, S, d))
+    dO = g.standard_normal((Hq, S, d))
+    Qt, Kt, Vt = (torch.tensor(x, requires_grad=True) for x in (Q, K, V))
+    out = torch.nn.functional.scaled_dot_product_attention(Qt, Kt.repeat_interleave(2, 0), Vt.repeat_interleave(2, 0),
+                                                           is_causal=True)
+    (out * torch.tensor(dO)).sum().backward()
+    got = O.algebraic_attention_backward(Q, K, V, dO, np.zeros(S, int), 1)
+    for gg, want in zip(got, (Qt.grad, Kt.grad, Vt.grad)):
+        np.testing.assert_allclose(gg, want.numpy(), rtol=1e-11, atol=1e-11)
+
+
+def pin_attention_backward_finite_differences(O, seed=60):
+    """The gradients are the derivative of f = <dO, attention(Q, K, V)>: along a random direction
+    (E_Q, E_K, E_V) the central difference of f (the oracle's own forward, eps = 1e-5) equals
+    <dQ, E_Q> + <dK, E_K> + <dV, E_V>; Q_q and the recursive law, GQA."""
+    g = _rng(seed)
+    for Hq, Hkv, S, d, q, L in ((4, 2, 9, 8, 4, 0), (2, 1, 8, 8, 4, 2)):
+        Q = g.standard_normal((Hq, S, d))
+        K = g.standard_normal((Hkv, S, d))
+        V = g.standard_normal((Hkv, S, d))
+        dO = g.standard_normal((Hq, S, d))
+        E = [g.standard_normal(x.shape) for x in (Q, K, V)]
+        tau = np.arange(S) % q
+        f = lambda t: float((dO * O.algebraic_attention(Q + t * E[0], K + t * E[1], V + t * E[2], tau, q, L)).sum())  # noqa: E731
+        eps = 1e-5
+        fd = (f(eps) - f(-eps)) / (2 * eps)
+        dQ, dK, dV = O.algebraic_attention_backward(Q, K, V, dO, tau, q, L)
+        an = float((dQ * E[0]).sum() + (dK * E[1]).sum() + (dV * E[2]).sum())
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (fd, an)
+
+
 ALL_PINS = [
     pin_q2_table, pin_q2_scalar_example, pin_eq3_rectangular_blocks, pin_eq13_14,
     pin_product_counts, pin_graph_counts, pin_appendix_a, pin_associativity,
@@ -1035,4 +1127,5 @@ ALL_PINS = [
     pin_attention_q1_is_sdpa, pin_attention_scores_are_typed_product, pin_attention_scale_and_mask,
     pin_attention_causality, pin_attention_gqa, pin_attention_laws_and_counts, pin_attention_type_offset,
     pin_decode_is_prefill_row, pin_decode_q1_is_sdpa, pin_decode_cached_key_groups, pin_decode_macs,
+    pin_attention_backward_autograd, pin_attention_backward_q1_is_sdpa, pin_attention_backward_finite_differences,
 ]

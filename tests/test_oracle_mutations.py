@@ -24,6 +24,7 @@ _real_support = O.score_support
 _real_swiglu_bwd = O.swiglu_backward
 _real_decode = O.algebraic_attention_decode
 _real_decode_macs = O.attention_decode_macs
+_real_attn_bwd = O.algebraic_attention_backward
 
 
 def table_with_edge_edge(q, edges=None):
@@ -283,6 +284,65 @@ def decode_macs_full_keys(p, key_pos, q, d, L=0, kind="cyclic", period=0):
     return vm, vm
 
 
+
+def _attn_bwd_variant(Q, K, V, dO, tau, q, L, positions, row_term=True, all_groups=False, assign_heads=False):
+    """The attention gradients with one step replaced by a mutant's choice."""
+    Q, K, V, dO = (np.asarray(a, float) for a in (Q, K, V, dO))
+    Hq, S, d = Q.shape
+    Hkv = K.shape[0]
+    m = d // q
+    tau = np.asarray(tau)
+    pos = np.arange(S) if positions is None else np.asarray(positions)
+    sel = np.zeros((q, S, S), dtype=bool)
+    for i in range(q):
+        for j in range(q):
+            for a in O.score_support(i, j, q, L):
+                sel[a][np.ix_(tau == i, tau == j)] = True
+    k_pair = np.maximum(sel.sum(axis=0) * m, 1)
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    for h in range(Hq):
+        kv = h // (Hq // Hkv)
+        r = sum(np.where(sel[a], Q[h][:, a * m:(a + 1) * m] @ K[kv][:, a * m:(a + 1) * m].T, 0.0) for a in range(q))
+        sc = np.where(pos[None, :] <= pos[:, None], r / np.sqrt(k_pair), -np.inf)
+        P = np.exp(sc - sc.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        dP = dO[h] @ V[kv].T
+        dS = P * (dP - (P * dP).sum(axis=1, keepdims=True)) if row_term else P * dP
+        dR = dS / np.sqrt(k_pair)
+        if assign_heads:
+            dV[kv] = P.T @ dO[h]
+            dK[kv] = 0.0
+        else:
+            dV[kv] += P.T @ dO[h]
+        for a in range(q):
+            ga = slice(a * m, (a + 1) * m)
+            dRa = dR if all_groups else np.where(sel[a], dR, 0.0)
+            dQ[h][:, ga] += dRa @ K[kv][:, ga]
+            dK[kv][:, ga] += dRa.T @ Q[h][:, ga]
+    return dQ, dK, dV
+
+
+def attn_bwd_drops_row_term(Q, K, V, dO, tau, q, L=0, positions=None):
+    """Mistake: the softmax VJP without its row term (dS = P dP)."""
+    return _attn_bwd_variant(Q, K, V, dO, tau, q, L, positions, row_term=False)
+
+
+def attn_bwd_all_groups(Q, K, V, dO, tau, q, L=0, positions=None):
+    """Mistake: the score gradient reaches every feature group, not only the compared ones."""
+    return _attn_bwd_variant(Q, K, V, dO, tau, q, L, positions, all_groups=True)
+
+
+def attn_bwd_last_head_wins(Q, K, V, dO, tau, q, L=0, positions=None):
+    """Mistake: a key/value head keeps the gradient of its last query head only (no GQA sum)."""
+    return _attn_bwd_variant(Q, K, V, dO, tau, q, L, positions, assign_heads=True)
+
+
+def attn_bwd_swaps_dk_dv(Q, K, V, dO, tau, q, L=0, positions=None):
+    """Mistake: dK and dV returned in each other's place."""
+    dQ, dK, dV = _real_attn_bwd(Q, K, V, dO, tau, q, L, positions)
+    return dQ, dV, dK
+
+
 MUTANTS = [
     ("structure_table", table_with_edge_edge),
     ("structure_table", table_without_right_vertex),
@@ -312,6 +372,10 @@ MUTANTS = [
     ("algebraic_attention_decode", decode_admits_future),
     ("algebraic_attention_decode", decode_dense_scale),
     ("attention_decode_macs", decode_macs_full_keys),
+    ("algebraic_attention_backward", attn_bwd_drops_row_term),
+    ("algebraic_attention_backward", attn_bwd_all_groups),
+    ("algebraic_attention_backward", attn_bwd_last_head_wins),
+    ("algebraic_attention_backward", attn_bwd_swaps_dk_dv),
 ]
 
 
