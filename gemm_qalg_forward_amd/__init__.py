@@ -11,7 +11,8 @@ Functions carry the C names:
     qalg_backward_dw_widths,
     qalg_gated_forward, qalg_gated_forward_keep, qalg_merge_gate_up, qalg_split_gate_up, qalg_swiglu_forward, qalg_swiglu_backward,
     qalg_attention_forward, qalg_attention_forward_at, qalg_attention_decode,
-    qalg_attention_decode_workspace_bytes, qalg_forward_noalloc,
+    qalg_attention_decode_workspace_bytes, qalg_attention_forward_train, qalg_attention_backward,
+    qalg_attention_backward_workspace_bytes, qalg_forward_noalloc,
     qalg_type_schedule, qalg_build_index, qalg_build_index_batched,
     qalg_read_status, qalg_workspace_bytes, qalg_index_layout,
     qalg_status_string, qalg_version.
@@ -35,7 +36,8 @@ __all__ = [
     "qalg_gated_forward", "qalg_gated_forward_keep", "qalg_merge_gate_up", "qalg_split_gate_up", "qalg_swiglu_forward",
     "qalg_swiglu_backward", "qalg_attention_forward", "qalg_read_status", "workspace",
     "qalg_forward_noalloc", "QALG_NOALLOC_SCRATCH_BYTES", "qalg_attention_forward_at", "qalg_attention_decode",
-    "qalg_attention_decode_workspace_bytes",
+    "qalg_attention_decode_workspace_bytes", "qalg_attention_forward_train", "qalg_attention_backward",
+    "qalg_attention_backward_workspace_bytes",
 ]
 
 QALG_F32 = 0
@@ -106,6 +108,11 @@ _SIGS = {
     "qalg_attention_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i64, _c_i32]),
     "qalg_attention_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32,
                                              _c_i32, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
+    "qalg_attention_forward_train": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_i64,
+                                                    _vp, _vp, _c_i32, _c_u32, _vp]),
+    "qalg_attention_backward_workspace_bytes": (_c_size, [_c_i32, _c_i64, _c_i32]),
+    "qalg_attention_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32,
+                                               _c_i64, _vp, _vp, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
 }
 
 
@@ -548,6 +555,68 @@ def qalg_attention_forward_at(Qh, Kh, Vh, q: int, first_position: int, O=None, f
         _dev_ptr(O, "O"), _dtype_code(Qh), flags, _stream(stream)))
     return O
 
+
+
+def _attn_operands(Qh, Kh, Vh):
+    Hq, S, d = Qh.shape
+    Hkv = Kh.shape[0]
+    if tuple(Kh.shape) != (Hkv, S, d) or tuple(Vh.shape) != (Hkv, S, d):
+        raise ValueError("K and V must be [Hkv, S, d] with the S and d of Q")
+    if Kh.dtype != Qh.dtype or Vh.dtype != Qh.dtype:
+        raise TypeError("Q, K and V must share a dtype")
+    _same_device(Kh, Qh, "K")
+    _same_device(Vh, Qh, "V")
+    return Hq, Hkv, S, d
+
+
+def qalg_attention_forward_train(Qh, Kh, Vh, q: int, first_position: int = 0, O=None, lse=None, flags: int = 0,
+                                 stream=None):
+    """The forward for training: O [Hq, S, d] and lse [Hq, S] (fp32, natural log of each query's
+    softmax denominator), for qalg_attention_backward; returns (O, lse)."""
+    torch = _torch()
+    Hq, Hkv, S, d = _attn_operands(Qh, Kh, Vh)
+    O = _new_or_check(O, (Hq, S, d), Qh, "O")
+    if lse is None:
+        lse = torch.empty((Hq, S), dtype=torch.float32, device=Qh.device)
+    elif tuple(lse.shape) != (Hq, S) or lse.dtype != torch.float32:
+        raise ValueError(f"lse must be float32 [{Hq}, {S}]")
+    else:
+        _same_device(lse, Qh, "lse")
+    _check("qalg_attention_forward_train", lib().qalg_attention_forward_train(
+        _dev_ptr(Qh, "Q"), _dev_ptr(Kh, "K"), _dev_ptr(Vh, "V"), Hq, Hkv, S, d, q, int(first_position),
+        _dev_ptr(O, "O"), _dev_ptr(lse, "lse"), _dtype_code(Qh), flags, _stream(stream)))
+    return O, lse
+
+
+def qalg_attention_backward_workspace_bytes(Hq: int, S: int, q: int) -> int:
+    return lib().qalg_attention_backward_workspace_bytes(Hq, S, q)
+
+
+def qalg_attention_backward(Qh, Kh, Vh, Oh, dOh, lse, q: int, first_position: int = 0, dQ=None, dK=None, dV=None,
+                            ws=None, flags: int = 0, stream=None):
+    """Gradients of the algebraic-score attention (Algorithm 2, step 9) from the forward's O and lse
+    and the output gradient dO [Hq, S, d]; returns (dQ [Hq, S, d], dK, dV [Hkv, S, d])."""
+    torch = _torch()
+    Hq, Hkv, S, d = _attn_operands(Qh, Kh, Vh)
+    for t, n in ((Oh, "O"), (dOh, "dO")):
+        _check_out(t, (Hq, S, d), Qh, n)
+    if tuple(lse.shape) != (Hq, S) or lse.dtype != torch.float32:
+        raise ValueError(f"lse must be float32 [{Hq}, {S}]")
+    _same_device(lse, Qh, "lse")
+    dQ = _new_or_check(dQ, (Hq, S, d), Qh, "dQ")
+    dK = _new_or_check(dK, (Hkv, S, d), Qh, "dK")
+    dV = _new_or_check(dV, (Hkv, S, d), Qh, "dV")
+    need = qalg_attention_backward_workspace_bytes(Hq, S, q)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=Qh.device)
+    else:
+        _same_device(ws, Qh, "ws")
+    _check("qalg_attention_backward", lib().qalg_attention_backward(
+        _dev_ptr(Qh, "Q"), _dev_ptr(Kh, "K"), _dev_ptr(Vh, "V"), _dev_ptr(Oh, "O"), _dev_ptr(dOh, "dO"),
+        _dev_ptr(lse, "lse"), Hq, Hkv, S, d, q, int(first_position), _dev_ptr(dQ, "dQ"), _dev_ptr(dK, "dK"),
+        _dev_ptr(dV, "dV"), _dtype_code(Qh), _dev_ptr(ws, "ws"), ws.numel() * ws.element_size(), flags,
+        _stream(stream)))
+    return dQ, dK, dV
 
 def qalg_attention_decode_workspace_bytes(B: int, Hq: int, N: int, d: int) -> int:
     return lib().qalg_attention_decode_workspace_bytes(B, Hq, N, d)

@@ -652,6 +652,60 @@ qalg_status qalg_attention_forward_at(const void* Q, const void* K, const void* 
       qalg::launch_attn_fwd_bf16(Q, K, V, O, Hq, Hkv, S, d, q, L, first_position, static_cast<hipStream_t>(stream)));
 }
 
+// the checks every attention entry shares; L receives the law's level count
+static qalg_status attn_check(int32_t Hq, int32_t Hkv, int64_t S, int32_t d, int32_t q, int64_t first_position,
+                              int32_t dtype, uint32_t flags, int* L) {
+  if (first_position < 0) return QALG_ERR_DIM;
+  if (dtype != QALG_BF16) return QALG_ERR_DTYPE;
+  if (flags & ~uint32_t(QALG_FLAG_LAW_TENSOR)) return QALG_ERR_ARG;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv || S < 0 || (d != 64 && d != 128)) return QALG_ERR_DIM;
+  if (S * int64_t(d) * 2 >= (int64_t(1) << 31)) return QALG_ERR_DIM;  // a head's rows: 32-bit byte offsets
+  if (q < 1 || q > QALG_MAX_Q || d % q) return QALG_ERR_Q;
+  *L = (flags & QALG_FLAG_LAW_TENSOR) ? tensor_levels(q) : 0;
+  if (*L < 0) return QALG_ERR_Q;
+  if (!qalg::attn_supported(d, q)) return QALG_ERR_ALIGN;
+  return QALG_OK;
+}
+
+qalg_status qalg_attention_forward_train(const void* Q, const void* K, const void* V, int32_t Hq, int32_t Hkv,
+                                         int64_t S, int32_t d, int32_t q, int64_t first_position, void* O, float* lse,
+                                         int32_t dtype, uint32_t flags, void* stream) {
+  int L = 0;
+  const qalg_status st = attn_check(Hq, Hkv, S, d, q, first_position, dtype, flags, &L);
+  if (st != QALG_OK) return st;
+  if (S == 0) return QALG_OK;
+  if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr || lse == nullptr) return QALG_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || reinterpret_cast<uintptr_t>(lse) % 4)
+    return QALG_ERR_ALIGN;
+  return hip_status(qalg::launch_attn_fwd_lse_bf16(Q, K, V, O, lse, Hq, Hkv, S, d, q, L, first_position,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t qalg_attention_backward_workspace_bytes(int32_t Hq, int64_t S, int32_t q) {
+  if (Hq < 1 || S < 0 || q < 1 || q > QALG_MAX_Q) return 0;
+  const size_t n = qalg::attn_bwd_stat_bytes(Hq, S, q);
+  return (n + 255) / 256 * 256;
+}
+
+qalg_status qalg_attention_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                                    const float* lse, int32_t Hq, int32_t Hkv, int64_t S, int32_t d, int32_t q,
+                                    int64_t first_position, void* dQ, void* dK, void* dV, int32_t dtype, void* ws,
+                                    size_t ws_bytes, uint32_t flags, void* stream) {
+  int L = 0;
+  const qalg_status st = attn_check(Hq, Hkv, S, d, q, first_position, dtype, flags, &L);
+  if (st != QALG_OK) return st;
+  if (S == 0) return QALG_OK;
+  if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr || dO == nullptr || lse == nullptr ||
+      dQ == nullptr || dK == nullptr || dV == nullptr || ws == nullptr)
+    return QALG_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(dQ) ||
+      !aligned16(dK) || !aligned16(dV) || reinterpret_cast<uintptr_t>(lse) % 4)
+    return QALG_ERR_ALIGN;
+  if (!aligned16(ws) || ws_bytes < qalg_attention_backward_workspace_bytes(Hq, S, q)) return QALG_ERR_WORKSPACE;
+  return hip_status(qalg::launch_attn_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, ws, Hq, Hkv, S, d, q, L,
+                                               first_position, static_cast<hipStream_t>(stream)));
+}
+
 size_t qalg_attention_decode_workspace_bytes(int32_t B, int32_t Hq, int64_t N, int32_t d) {
   if (B < 0 || Hq < 1 || N < 1 || (d != 64 && d != 128)) return 0;
   const size_t n = qalg::attn_decode_part_bytes(B, Hq, N, d);

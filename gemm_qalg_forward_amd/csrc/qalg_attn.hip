@@ -56,6 +56,7 @@ struct AttnArgs {
   int m;          // features per group (d / q)
   int n_qblk;     // query blocks per (head, type)
   int o;          // type of row 0: rows s have positions p0 + s and types (o + s) mod q, o = p0 mod q
+  float* lse;     // Hq x S natural-log sums of exp(score) per query (for the backward), or null
 };
 
 // groups compared by types (i, j): count, and the b-th one
@@ -355,6 +356,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
                                    acc[db][4 * g + 3] * inv);
         *reinterpret_cast<u32x2*>(orow + (32 * db + 8 * g + 4 * lhi) * 2) = v;
       }
+    // log of the softmax denominator in the scores' own units: the running
+    // max and sum live in the log2 domain of the scaled scores
+    if (a.lse != nullptr && lhi == 0) a.lse[int64_t(h) * S + pq] = (m_run + __log2f(l_run)) * 0.6931471805599453f;
   }
 }
 
@@ -667,12 +671,524 @@ __global__ __launch_bounds__(D) void attn_decode_combine_kernel(const float* __r
   reinterpret_cast<uint16_t*>(O)[row * D + f] = uint16_t(__builtin_bit_cast(uint32_t, h) & 0xffffu);
 }
 
+
+// ---------------------------------------------------------------------------
+// Backward (Algorithm 2, step 9): gradients of the algebraic-score attention.
+// With P the softmax rows (recomputed from the scores and the forward's
+// log-sum-exp), dP_pu = <dO_p, V_u> and D_p = <dO_p, O_p> (= sum_u P_pu dP_pu):
+//   dS_pu = P_pu (dP_pu - D_p) / sqrt(|F(i, j)| m)      (softmax, then eq 41's scale)
+//   dQ_p^(a) = sum_u dS_pu K_u^(a),  dK_u^(a) = sum_p dS_pu Q_p^(a)   (a in F(i, j) only, eq 39)
+//   dV_u = sum_p P_pu dO_p
+// attn_bwd_dq_kernel takes the forward's work split (128 queries of one type
+// of one head) and its walk over the key blocks, type by type: scores over
+// the support, P, dP = dO V^T over all d, dS, then dQ^T += K^T dS over the
+// feature blocks that meet the support (K read transposed from LDS, features
+// outside F(i, j) zeroed in the fragment).  It also stores each query's
+// (log2-domain log-sum-exp, D) pair, grouped by type, for the second kernel.
+// attn_bwd_dkdv_kernel owns 128 keys of one type of one key/value head (32 per
+// wave, K and V rows in registers) and walks, for every query head that reads
+// that head (GQA), the 64-query blocks of every type at or after its first key:
+// S^T = Q K^T over the support, P^T, dP^T = dO V^T, dS^T, then dV^T += dO^T P
+// and dK^T += Q^T dS (Q and dO read transposed).  Each key's dK and dV come
+// from one workgroup, so no atomics and bitwise reproducible.  P and dS enter
+// the MFMAs in bf16; everything else stays fp32 until the one rounding of dQ,
+// dK and dV.  Rows live in LDS in the K layout above (swk); the transposing
+// reads compute each lane's address through the same swizzle.
+// ---------------------------------------------------------------------------
+
+struct AttnBwdArgs {
+  const char* Q;
+  const char* K;
+  const char* V;
+  const char* O;
+  const char* dO;
+  const float* lse;   // Hq x S, natural log of each query's softmax denominator
+  float* stat;        // (head, query type): n_pad pairs (log2-domain lse, D), then 64 spare pairs
+  char* dQ;
+  char* dK;
+  char* dV;
+  int Hq, Hkv, S, q, L, m, o;
+  int n_qblk;         // 128-query blocks per (head, type)
+  int n_kblk;         // 128-key blocks per (key/value head, type)
+  int n_pad;          // pairs per (head, type): ceil(S / q) rounded up to 64
+};
+
+// Transposing-read offsets for a 16-row step of swk rows: lane (g = lane / 16,
+// t = lane % 16) reads 8 bytes of rows k_l and k_l + 4 of the step, k_l =
+// 8 (g / 2) + t / 4, logical piece 4 db + 2 (g % 2) + (t % 4) / 2, half t % 2
+// (the forward's V read, with the K layout's swizzle, which within a step of
+// 16 rows does not depend on the step).
+template <int D>
+__device__ __forceinline__ void tr_offsets(int lane, int (&lo)[D / 32], int (&hi)[D / 32]) {
+  constexpr int ROWB = D * 2;
+  const int g = lane >> 4, t = lane & 15;
+  const int k_l = 8 * (g >> 1) + (t >> 2);
+  const int r2 = 2 * (g & 1) + ((t & 3) >> 1);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    lo[db] = k_l * ROWB + (((4 * db + r2) ^ swk<D>(k_l)) << 4) + 8 * (t & 1);
+    hi[db] = (k_l + 4) * ROWB + (((4 * db + r2) ^ swk<D>(k_l + 4)) << 4) + 8 * (t & 1);
+  }
+}
+
+// A operand (32 features x 16 rows) of feature block db, row step st, from swk rows
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr(const char* base, int st, int lo, int hi) {
+  const char* p = base + st * 16 * (D * 2);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + lo));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + hi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// A operand (32 rows x 16 features) from swk rows: row r, logical piece pc
+template <int D>
+__device__ __forceinline__ bf16x8 read_row(const char* base, int r, int pc) {
+  return *reinterpret_cast<const bf16x8*>(base + r * (D * 2) + ((pc ^ swk<D>(r)) << 4));
+}
+
+// rows 16 ks .. 16 ks + 15 of a 64-row tile of fp32 results (two 32x32 MFMA
+// outputs, rows in registers) as a bf16 B operand with those rows as the
+// contraction: the forward's probability exchange (v_permlane32_swap)
+template <int KS4>
+__device__ __forceinline__ bf16x8 pack_rows(const f32x16 (&x)[2]) {
+  constexpr int nb = KS4 >> 1, ga = 2 * (KS4 & 1);
+  const u32x2 pa = pack4_bf16(x[nb][4 * ga], x[nb][4 * ga + 1], x[nb][4 * ga + 2], x[nb][4 * ga + 3]);
+  const u32x2 pb = pack4_bf16(x[nb][4 * ga + 4], x[nb][4 * ga + 5], x[nb][4 * ga + 6], x[nb][4 * ga + 7]);
+  const auto s0 = __builtin_amdgcn_permlane32_swap(pa[0], pb[0], false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(pa[1], pb[1], false, false);
+  const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// the support of types (i, j) as MFMA slots: slot x is the x-th 16-feature
+// step of F(i, j) (piece 2 step of a row; the B fragment f[step]); per
+// 32-feature block, whether it meets F(i, j) (uniform) and whether this lane's
+// feature (32 db + l32) lies in it
+template <int D>
+struct BwdSupport {
+  int tot, nf;
+  int kp[D / 16];
+  bf16x8 sl[D / 16];
+  bool blk[D / 32], lane_in[D / 32];
+  __device__ __forceinline__ void set(int i, int j, int L, int m, int l32, const bf16x8 (&f)[D / 16]) {
+    constexpr int KS = D / 16;
+    const int ms = m / 16;
+    nf = uni(support_count(i, j, L));
+    tot = uni(nf * ms);
+#pragma unroll
+    for (int x = 0; x < KS; ++x) {
+      const int step = x < tot ? support_group(i, j, L, x / ms) * ms + x % ms : 0;
+      kp[x] = uni(2 * step);
+      bf16x8 v = f[0];
+#pragma unroll
+      for (int z = 1; z < KS; ++z)
+        if (z == step) v = f[z];
+      sl[x] = v;
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      blk[db] = in_support(32 * db / m, i, j, L) || in_support((32 * db + 31) / m, i, j, L);
+      lane_in[db] = in_support((32 * db + l32) / m, i, j, L);
+    }
+  }
+};
+
+// sc[nb] (rows nb * 32 + 8 (e / 4) + 4 lhi + e % 4, column = lane) = rows of
+// `base` times the support slots
+template <int D, int T>
+__device__ __forceinline__ void support_scores(f32x16 (&sc)[2], const char* base, const BwdSupport<D>& sp, int l32,
+                                               int lhi) {
+  sc[0] = (f32x16){};
+  sc[1] = (f32x16){};
+#pragma unroll
+  for (int x = 0; x < T; ++x)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(base, nb * 32 + l32, sp.kp[x] + lhi), sp.sl[x],
+                                                       sc[nb], 0, 0, 0);
+}
+template <int D>
+__device__ __forceinline__ void support_scores_any(f32x16 (&sc)[2], const char* base, const BwdSupport<D>& sp,
+                                                   int l32, int lhi) {
+  switch (sp.tot) {
+    case 1: support_scores<D, 1>(sc, base, sp, l32, lhi); break;
+    case 2: support_scores<D, 2>(sc, base, sp, l32, lhi); break;
+    case 3: support_scores<D, 3>(sc, base, sp, l32, lhi); break;
+    case 4: support_scores<D, 4>(sc, base, sp, l32, lhi); break;
+    case 5: support_scores<D, 5>(sc, base, sp, l32, lhi); break;
+    case 6: support_scores<D, 6>(sc, base, sp, l32, lhi); break;
+    case 7: support_scores<D, 7>(sc, base, sp, l32, lhi); break;
+    default: support_scores<D, D / 16>(sc, base, sp, l32, lhi); break;
+  }
+}
+
+// dp[nb] = rows of `base` (all d features) times the lane's fragments f
+template <int D>
+__device__ __forceinline__ void full_scores(f32x16 (&dp)[2], const char* base, const bf16x8 (&f)[D / 16], int l32,
+                                            int lhi) {
+  dp[0] = (f32x16){};
+  dp[1] = (f32x16){};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      dp[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(base, nb * 32 + l32, 2 * ks + lhi), f[ks], dp[nb],
+                                                       0, 0, 0);
+}
+
+// acc[db] += (feature block db of the 64 swk rows at `base`, transposed) x
+// (x's rows as the contraction); with MASK only the blocks and lanes of F
+template <int D, bool MASK>
+__device__ __forceinline__ void accumulate_tr(f32x16 (&acc)[D / 32], const char* base, const f32x16 (&x)[2],
+                                              const int (&lo)[D / 32], const int (&hi)[D / 32],
+                                              const BwdSupport<D>& sp) {
+  auto step = [&](auto ks_c) {
+    constexpr int KS4 = decltype(ks_c)::value;
+    const bf16x8 b = pack_rows<KS4>(x);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      if (MASK && !sp.blk[db]) continue;
+      bf16x8 a = read_tr<D>(base, KS4, lo[db], hi[db]);
+      if (MASK && !sp.lane_in[db]) a = (bf16x8){};
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[db], 0, 0, 0);
+    }
+  };
+  step(std::integral_constant<int, 0>{});
+  step(std::integral_constant<int, 1>{});
+  step(std::integral_constant<int, 2>{});
+  step(std::integral_constant<int, 3>{});
+}
+
+// a lane's row of a 32-row result: features 32 db + 8 g + 4 lhi + 0..3 of row `row`
+template <int D>
+__device__ __forceinline__ void store_row(char* row, const f32x16 (&acc)[D / 32], int lhi) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<u32x2*>(row + (32 * db + 8 * g + 4 * lhi) * 2) =
+          pack4_bf16(acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]);
+}
+
+template <int D>
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArgs a) {
+  constexpr int ROWB = D * 2;
+  constexpr int NP = D / 8;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int BLK = kAttnK * ROWB;
+  constexpr int LOADS = BLK / (4 * 1024);
+  static_assert(BLK % 4096 == 0, "whole 1 KB copies per wave");
+  // two stages of [K block | V block], both in the swk layout
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * BLK];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, lhi = lane >> 5;
+  int bid = blockIdx.x;
+  const int qb = a.n_qblk - 1 - bid % a.n_qblk;  // late (heavy) query blocks first
+  bid /= a.n_qblk;
+  const int i = bid % a.q;
+  const int h = bid / a.q;
+  const int kvh = h / (a.Hq / a.Hkv);
+  const int q = a.q, S = a.S;
+  auto first_row = [&](int t) -> int { return t >= a.o ? t - a.o : t - a.o + q; };
+  const int si = first_row(i);
+  const int n_i = S > si ? (S - si + q - 1) / q : 0;
+  const int t0 = qb * kAttnQ;
+  if (t0 >= n_i) return;
+  const int t_last = min(t0 + kAttnQ, n_i) - 1;
+  const int p_last = si + q * t_last;
+  const int p_wave0 = si + q * min(t0 + 32 * wid, n_i - 1);
+
+  const int64_t hoff = int64_t(h) * S * ROWB;
+  const char* Kh = a.K + int64_t(kvh) * S * ROWB;
+  const char* Vh = a.V + int64_t(kvh) * S * ROWB;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(smem)));
+
+  // this lane's query row: Q and dO fragments in registers; D = <dO, O> in fp32
+  const int tq = t0 + wid * 32 + l32;
+  const bool q_ok = tq < n_i;
+  const int pq = si + q * min(tq, n_i - 1);
+  bf16x8 qf[KS], df[KS];
+  float dsum = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int64_t off = hoff + int64_t(pq) * ROWB + (2 * ks + lhi) * 16;
+    qf[ks] = *reinterpret_cast<const bf16x8*>(a.Q + off);
+    df[ks] = *reinterpret_cast<const bf16x8*>(a.dO + off);
+    const bf16x8 of = *reinterpret_cast<const bf16x8*>(a.O + off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf(float(df[ks][e]), float(of[e]), dsum);
+  }
+  dsum += __shfl_xor(dsum, 32);
+  const float log2e = 1.4426950408889634f;
+  const float lse2 = a.lse[int64_t(h) * S + pq] * log2e;
+  if (q_ok && lhi == 0) {
+    float* st = a.stat + 2 * (int64_t(h * q + i) * a.n_pad + tq);
+    st[0] = lse2;
+    st[1] = dsum;
+  }
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = (f32x16){};
+  int tlo[DB], thi[DB];
+  tr_offsets<D>(lane, tlo, thi);
+  int k_row[LOADS];
+  uint32_t k_pc[LOADS];
+#pragma unroll
+  for (int x = 0; x < LOADS; ++x) {
+    const int sl = (wid * LOADS + x) * 64 + lane;
+    k_row[x] = sl / NP;
+    k_pc[x] = uint32_t((sl % NP) ^ swk<D>(k_row[x])) * 16u;
+  }
+
+  // key blocks, type by type (the forward's walk)
+  int cj = 0, ct = 0;
+  auto keys_of = [&](int j) -> int {
+    const int sj = first_row(j);
+    return p_last >= sj ? (p_last - sj) / q + 1 : 0;
+  };
+  auto skip_empty = [&]() {
+    while (cj < q && ct >= keys_of(cj)) {
+      cj = uni(cj + 1);
+      ct = 0;
+    }
+  };
+  auto issue = [&](int stage) {
+    const int nk = keys_of(cj);
+    const uint32_t base = lds0 + uint32_t(stage * 2 * BLK) + uint32_t(wid * LOADS * 1024);
+#pragma unroll
+    for (int x = 0; x < LOADS; ++x) {
+      const uint32_t u = uint32_t(first_row(cj) + q * min(ct + k_row[x], nk - 1));
+      copy16_to_lds(Kh, u * ROWB + k_pc[x], base + uint32_t(x * 1024));
+      copy16_to_lds(Vh, u * ROWB + k_pc[x], base + uint32_t(BLK + x * 1024));
+    }
+  };
+
+  BwdSupport<D> sp;
+  int cur_j = -1;
+  skip_empty();
+  int stage = 0;
+  int bj = cj, btb = ct;
+  issue(0);
+  ct = uni(ct + kAttnK);
+  skip_empty();
+  for (;;) {
+    wait_vmcnt<0>();
+    lds_barrier();
+    const int j = bj, tb = btb;
+    const bool more = cj < q;
+    if (more) {
+      bj = cj;
+      btb = ct;
+      issue(stage ^ 1);
+      ct = uni(ct + kAttnK);
+      skip_empty();
+    }
+    const char* sK = smem + stage * 2 * BLK;
+    const char* sV = sK + BLK;
+    if (j != cur_j) {
+      cur_j = j;
+      sp.set(i, j, a.L, a.m, l32, qf);
+    }
+    f32x16 sc[2], dp[2];
+    support_scores_any<D>(sc, sK, sp, l32, lhi);
+    full_scores<D>(dp, sV, df, l32, lhi);
+    const float c = __builtin_amdgcn_rsqf(float(sp.nf * a.m));
+    const float scl = log2e * c;
+    const int nk_j = keys_of(j);
+    const int sj = first_row(j);
+    const bool full = tb + kAttnK <= nk_j && sj + q * (tb + kAttnK - 1) <= p_wave0;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int tk = tb + nb * 32 + 8 * (e >> 2) + 4 * lhi + (e & 3);
+        const bool ok = full || (tk < nk_j && sj + q * tk <= pq);
+        const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nb][e], scl, -lse2)) : 0.f;
+        dp[nb][e] = ok ? p * (dp[nb][e] - dsum) * c : 0.f;
+      }
+    accumulate_tr<D, true>(acc, sK, dp, tlo, thi, sp);
+    if (!more) break;
+    stage ^= 1;
+  }
+  if (q_ok) store_row<D>(a.dQ + hoff + int64_t(pq) * ROWB, acc, lhi);
+}
+
+template <int D>
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+  constexpr int ROWB = D * 2;
+  constexpr int NP = D / 8;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int BLK = kAttnK * ROWB;     // 64 query rows
+  constexpr int LOADS = BLK / (4 * 1024);
+  constexpr int STG = 2 * BLK + 1024;    // [Q block | dO block | 64 (lse, D) pairs + pad]
+  static_assert(BLK % 4096 == 0, "whole 1 KB copies per wave");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STG];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, lhi = lane >> 5;
+  const int q = a.q, S = a.S;
+  // block -> (key block, key type, key/value head), early (heavy) key blocks first
+  int bid = blockIdx.x;
+  const int kb = bid / (q * a.Hkv);
+  bid -= kb * q * a.Hkv;
+  const int j = bid % q;
+  const int hk = bid / q;
+  const int G = a.Hq / a.Hkv;
+  auto first_row = [&](int t) -> int { return t >= a.o ? t - a.o : t - a.o + q; };
+  auto n_of = [&](int t) -> int {
+    const int s_ = first_row(t);
+    return S > s_ ? (S - s_ + q - 1) / q : 0;
+  };
+  const int sj = first_row(j);
+  const int n_j = n_of(j);
+  const int t0 = kb * kAttnQ;
+  if (t0 >= n_j) return;
+  const int p_first = sj + q * t0;
+  const int p_wave_last = sj + q * min(t0 + 32 * wid + 31, n_j - 1);
+
+  // this lane's key: K and V fragments in registers
+  const int tk = t0 + wid * 32 + l32;
+  const bool k_ok = tk < n_j;
+  const int pk = sj + q * min(tk, n_j - 1);
+  const int64_t koff = int64_t(hk) * S * ROWB + int64_t(pk) * ROWB;
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = *reinterpret_cast<const bf16x8*>(a.K + koff + (2 * ks + lhi) * 16);
+    vf[ks] = *reinterpret_cast<const bf16x8*>(a.V + koff + (2 * ks + lhi) * 16);
+  }
+  f32x16 accK[DB], accV[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    accK[db] = (f32x16){};
+    accV[db] = (f32x16){};
+  }
+  int tlo[DB], thi[DB];
+  tr_offsets<D>(lane, tlo, thi);
+  int r_row[LOADS];
+  uint32_t r_pc[LOADS];
+#pragma unroll
+  for (int x = 0; x < LOADS; ++x) {
+    const int sl = (wid * LOADS + x) * 64 + lane;
+    r_row[x] = sl / NP;
+    r_pc[x] = uint32_t((sl % NP) ^ swk<D>(r_row[x])) * 16u;
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(smem)));
+
+  // query blocks: for each query head of the group and each query type, the
+  // queries from the first one at or after p_first (an even index, so that the
+  // block's (lse, D) pairs start 16-byte aligned), 64 at a time
+  auto q_first = [&](int t) -> int {
+    const int s_ = first_row(t);
+    return (p_first > s_ ? (p_first - s_ + q - 1) / q : 0) & ~1;
+  };
+  int cg = 0, ci = 0, ct = q_first(0);
+  auto skip_empty = [&]() {
+    while (cg < G && ct >= n_of(ci)) {
+      ci = uni(ci + 1);
+      if (ci == q) {
+        ci = 0;
+        cg = uni(cg + 1);
+      }
+      ct = uni(q_first(ci));
+    }
+  };
+  auto issue = [&](int stage) {
+    const int h = hk * G + cg;
+    const int n = n_of(ci), s_ = first_row(ci);
+    const char* Qh = a.Q + int64_t(h) * S * ROWB;
+    const char* dOh = a.dO + int64_t(h) * S * ROWB;
+    const uint32_t base = lds0 + uint32_t(stage * STG) + uint32_t(wid * LOADS * 1024);
+#pragma unroll
+    for (int x = 0; x < LOADS; ++x) {
+      const uint32_t u = uint32_t(s_ + q * min(ct + r_row[x], n - 1));
+      copy16_to_lds(Qh, u * ROWB + r_pc[x], base + uint32_t(x * 1024));
+      copy16_to_lds(dOh, u * ROWB + r_pc[x], base + uint32_t(BLK + x * 1024));
+    }
+    if (wid == 0) {
+      // 64 pairs = 512 bytes: lanes 0-31; lanes 32-63 repeat them into the pad
+      const char* st = reinterpret_cast<const char*>(a.stat + 2 * (int64_t(h * q + ci) * a.n_pad + ct));
+      copy16_to_lds(st, uint32_t(lane & 31) * 16u, lds0 + uint32_t(stage * STG + 2 * BLK));
+    }
+  };
+
+  const float log2e = 1.4426950408889634f;
+  BwdSupport<D> sp;
+  int cur_i = -1;
+  skip_empty();
+  int stage = 0;
+  int bi = ci, btb = ct;
+  issue(0);
+  ct = uni(ct + kAttnK);
+  skip_empty();
+  for (;;) {
+    wait_vmcnt<0>();
+    lds_barrier();
+    const int i = bi, tb = btb;
+    const bool more = cg < G;
+    if (more) {
+      bi = ci;
+      btb = ct;
+      issue(stage ^ 1);
+      ct = uni(ct + kAttnK);
+      skip_empty();
+    }
+    const char* sQ = smem + stage * STG;
+    const char* sdO = sQ + BLK;
+    const char* sst = sdO + BLK;
+    if (i != cur_i) {
+      cur_i = i;
+      sp.set(i, j, a.L, a.m, l32, kf);
+    }
+    f32x16 sc[2], dp[2];
+    support_scores_any<D>(sc, sQ, sp, l32, lhi);
+    full_scores<D>(dp, sdO, vf, l32, lhi);
+    const float c = __builtin_amdgcn_rsqf(float(sp.nf * a.m));
+    const float scl = log2e * c;
+    const int n_i = n_of(i), s_i = first_row(i);
+    const bool full = tb + kAttnK <= n_i && s_i + q * tb >= p_wave_last;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r0 = nb * 32 + 8 * g4 + 4 * lhi;  // the lane's 4 consecutive queries
+        const float4 w0 = *reinterpret_cast<const float4*>(sst + 8 * r0);
+        const float4 w1 = *reinterpret_cast<const float4*>(sst + 8 * r0 + 16);
+        const float ls[4] = {w0.x, w0.z, w1.x, w1.z};
+        const float dd[4] = {w0.y, w0.w, w1.y, w1.w};
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int e = 4 * g4 + e4;
+          const int tq = tb + r0 + e4;
+          const bool ok = full || (tq < n_i && s_i + q * tq >= pk);
+          const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nb][e], scl, -ls[e4])) : 0.f;
+          dp[nb][e] = ok ? p * (dp[nb][e] - dd[e4]) * c : 0.f;
+          sc[nb][e] = p;
+        }
+      }
+    accumulate_tr<D, false>(accV, sdO, sc, tlo, thi, sp);
+    accumulate_tr<D, true>(accK, sQ, dp, tlo, thi, sp);
+    if (!more) break;
+    stage ^= 1;
+  }
+  if (k_ok) {
+    store_row<D>(a.dK + koff, accK, lhi);
+    store_row<D>(a.dV + koff, accV, lhi);
+  }
+}
+
 }  // namespace
 
 bool attn_supported(int d, int q) { return (d == 64 || d == 128) && q >= 1 && d % q == 0 && (d / q) % 16 == 0; }
 
-hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, void* O, int Hq, int Hkv, int64_t S,
-                                int d, int q, int L, int64_t first_pos, hipStream_t s) {
+hipError_t launch_attn_fwd_lse_bf16(const void* Q, const void* K, const void* V, void* O, float* lse, int Hq,
+                                    int Hkv, int64_t S, int d, int q, int L, int64_t first_pos, hipStream_t s) {
   AttnArgs a;
   a.Q = static_cast<const char*>(Q);
   a.K = static_cast<const char*>(K);
@@ -685,7 +1201,8 @@ hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, voi
   a.L = L;
   a.m = d / q;
   a.o = int(first_pos % q);
-  const int64_t n0 = (S + q - 1) / q;  // queries of type 0, the most of any type
+  a.lse = lse;
+  const int64_t n0 = (S + q - 1) / q;  // queries of the most frequent type
   a.n_qblk = int((n0 + kAttnQ - 1) / kAttnQ);
   const int64_t blocks = int64_t(Hq) * q * a.n_qblk;
   if (blocks == 0) return hipSuccess;
@@ -693,6 +1210,58 @@ hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, voi
     hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(unsigned(blocks)), dim3(kAttnThreads), 0, s, a);
   else
     hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(unsigned(blocks)), dim3(kAttnThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, void* O, int Hq, int Hkv, int64_t S,
+                                int d, int q, int L, int64_t first_pos, hipStream_t s) {
+  return launch_attn_fwd_lse_bf16(Q, K, V, O, nullptr, Hq, Hkv, S, d, q, L, first_pos, s);
+}
+
+size_t attn_bwd_stat_bytes(int64_t Hq, int64_t S, int q) {
+  const int64_t n0 = (S + q - 1) / q;
+  const int64_t n_pad = (n0 + 63) / 64 * 64;
+  return size_t((Hq * q * n_pad + 64) * 2) * sizeof(float);
+}
+
+hipError_t launch_attn_bwd_bf16(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                                const float* lse, void* dQ, void* dK, void* dV, void* stat, int Hq, int Hkv,
+                                int64_t S, int d, int q, int L, int64_t first_pos, hipStream_t s) {
+  AttnBwdArgs a;
+  a.Q = static_cast<const char*>(Q);
+  a.K = static_cast<const char*>(K);
+  a.V = static_cast<const char*>(V);
+  a.O = static_cast<const char*>(O);
+  a.dO = static_cast<const char*>(dO);
+  a.lse = lse;
+  a.stat = static_cast<float*>(stat);
+  a.dQ = static_cast<char*>(dQ);
+  a.dK = static_cast<char*>(dK);
+  a.dV = static_cast<char*>(dV);
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.S = int(S);
+  a.q = q;
+  a.L = L;
+  a.m = d / q;
+  a.o = int(first_pos % q);
+  const int64_t n0 = (S + q - 1) / q;
+  a.n_qblk = int((n0 + kAttnQ - 1) / kAttnQ);
+  a.n_kblk = a.n_qblk;
+  a.n_pad = int((n0 + 63) / 64 * 64);
+  const int64_t qblocks = int64_t(Hq) * q * a.n_qblk;
+  const int64_t kblocks = int64_t(Hkv) * q * a.n_kblk;
+  if (qblocks == 0) return hipSuccess;
+  // dQ first: it also writes the (lse, D) pairs the dK / dV kernel reads
+  if (d == 128) {
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(unsigned(qblocks)), dim3(kAttnThreads), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(unsigned(kblocks)), dim3(kAttnThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(unsigned(qblocks)), dim3(kAttnThreads), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, dim3(unsigned(kblocks)), dim3(kAttnThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -126,6 +126,14 @@ hipError_t launch_split_gate_up_bf16(const void* Wgu, void* Wg, void* Wu, int64_
 bool attn_supported(int d, int q);
 hipError_t launch_attn_fwd_bf16(const void* Q, const void* K, const void* V, void* O, int Hq, int Hkv, int64_t S,
                                 int d, int q, int L, int64_t first_pos, hipStream_t s);
+// the forward that also stores each query's log-sum-exp (Hq x S fp32), for the backward
+hipError_t launch_attn_fwd_lse_bf16(const void* Q, const void* K, const void* V, void* O, float* lse, int Hq,
+                                    int Hkv, int64_t S, int d, int q, int L, int64_t first_pos, hipStream_t s);
+// the backward's per-query (lse, D) scratch, and the two backward kernels
+size_t attn_bwd_stat_bytes(int64_t Hq, int64_t S, int q);
+hipError_t launch_attn_bwd_bf16(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                                const float* lse, void* dQ, void* dK, void* dV, void* stat, int Hq, int Hkv,
+                                int64_t S, int d, int q, int L, int64_t first_pos, hipStream_t s);
 // cached decoding (Algorithm 3): per-chunk partials in `part`, then their ordered combination into O
 bool attn_decode_supported(int d, int q);
 int64_t attn_decode_max_slots();  // cache slots per sequence the decode kernels take

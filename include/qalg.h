@@ -448,6 +448,47 @@ qalg_status qalg_attention_forward_at(const void* Q, const void* K, const void* 
                                       int32_t dtype, uint32_t flags, void* stream);
 
 /*
+ * The forward for training: qalg_attention_forward_at that also writes lse
+ * (Hq x S fp32, caller-owned device memory, 4-byte aligned), the natural log
+ * of each query's softmax denominator over the scaled scores (log of the sum
+ * over the allowed keys of exp(s)), which the backward reuses instead of
+ * recomputing the row statistics.  Errors as qalg_attention_forward_at, plus
+ * QALG_ERR_NULL for a null lse.
+ */
+qalg_status qalg_attention_forward_train(const void* Q, const void* K, const void* V, int32_t Hq, int32_t Hkv,
+                                         int64_t S, int32_t d, int32_t q, int64_t first_position, void* O, float* lse,
+                                         int32_t dtype, uint32_t flags, void* stream);
+
+/*
+ * Gradients of the algebraic-score attention (appendix G, Algorithm 2 step 9:
+ * backpropagation through steps 3-7).  Inputs: Q, K, V, the forward's O and
+ * lse (qalg_attention_forward_train, same first_position, q and flags), and
+ * dO (Hq x S x d), the gradient of the loss with respect to O.  With P the
+ * softmax rows, dP_pu = <dO_p, V_u> and D_p = <dO_p, O_p>:
+ *   dS_pu = P_pu (dP_pu - D_p) / sqrt(|F(i, j)| d / q)
+ *   dQ_p^(a) = sum_u dS_pu K_u^(a),  dK_u^(a) = sum_p dS_pu Q_p^(a)
+ *     over the groups a of F(i, j) only (the score reads only those, eq 39),
+ *   dV_u = sum_p P_pu dO_p (the dense value sum).
+ * A key/value head's dK and dV sum over the Hq / Hkv query heads that read it.
+ * Outputs dQ (Hq x S x d), dK, dV (Hkv x S x d), bf16, overwritten.  All
+ * tensors bf16 (lse fp32), packed, 16-byte aligned (lse 4-byte), caller-owned
+ * device memory.  fp32 scores, statistics and sums; P and dS are rounded to
+ * bf16 for the matrix products, each output once at the end; every output
+ * element is written by one workgroup (no atomics): bitwise reproducible.
+ * ws: caller-owned device scratch of at least
+ * qalg_attention_backward_workspace_bytes(Hq, S, q) bytes, 16-byte aligned
+ * (per-query lse and D, grouped by type).  Errors as
+ * qalg_attention_forward_at, plus QALG_ERR_NULL for a null pointer (ws
+ * included) and QALG_ERR_WORKSPACE for a small or misaligned ws.  S = 0
+ * returns QALG_OK without a launch.
+ */
+size_t qalg_attention_backward_workspace_bytes(int32_t Hq, int64_t S, int32_t q);
+qalg_status qalg_attention_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                                    const float* lse, int32_t Hq, int32_t Hkv, int64_t S, int32_t d, int32_t q,
+                                    int64_t first_position, void* dQ, void* dK, void* dV, int32_t dtype, void* ws,
+                                    size_t ws_bytes, uint32_t flags, void* stream);
+
+/*
  * Cached decoding with the algebraic score (appendix G, Algorithm 3; G.2's
  * cache): one new query row per sequence against that sequence's full-key
  * cache.  B sequences; Qn: B x Hq x d, the new rows' queries; Kc, Vc:

@@ -388,6 +388,40 @@ def test_attention_decode_argument_errors_are_synchronous(lib):
     assert lib.qalg_attention_forward_at(FAKE, FAKE, FAKE, 2, 1, 8, 64, 2, -1, FAKE, 1, 0, None) == 2
 
 
+
+def test_attention_training_argument_errors_are_synchronous(lib):
+    def fwd(Hq=4, Hkv=2, S=64, d=128, q=4, p0=0, dt=1, flags=0, lse=FAKE, O=FAKE):
+        return lib.qalg_attention_forward_train(FAKE, FAKE, FAKE, Hq, Hkv, S, d, q, p0, O, lse, dt, flags, None)
+    assert fwd(dt=0) == 5
+    assert fwd(flags=2) == 8
+    assert fwd(Hkv=3) == 2
+    assert fwd(p0=-1) == 2
+    assert fwd(q=16) == 4
+    assert fwd(lse=None) == 1
+    assert fwd(lse=FAKE + 2) == 4
+    assert fwd(S=0, lse=None) == 0
+
+    def bwd(Hq=4, Hkv=2, S=64, d=128, q=4, p0=0, dt=1, flags=0, ws=FAKE, wsb=1 << 20, dO=FAKE, dK=FAKE, lse=FAKE):
+        return lib.qalg_attention_backward(FAKE, FAKE, FAKE, FAKE, dO, lse, Hq, Hkv, S, d, q, p0, FAKE, dK, FAKE, dt,
+                                           ws, wsb, flags, None)
+    assert bwd(dt=0) == 5
+    assert bwd(flags=4) == 8
+    assert bwd(Hkv=3) == 2
+    assert bwd(d=96) == 2
+    assert bwd(q=3) == 3
+    assert bwd(q=8, d=64) == 4
+    assert bwd(dO=None) == 1
+    assert bwd(ws=None) == 1
+    assert bwd(dK=FAKE + 8) == 4
+    assert bwd(lse=FAKE + 1) == 4
+    assert bwd(wsb=64) == 6
+    assert bwd(ws=FAKE + 8) == 6
+    assert bwd(S=0, dO=None) == 0
+    # per (head, type): ceil(S / q) rounded up to 64 pairs of fp32, plus 64 spare pairs
+    need = Q.qalg_attention_backward_workspace_bytes(4, 300, 4)
+    assert need >= (4 * 4 * 128 + 64) * 8 and need % 256 == 0
+    assert Q.qalg_attention_backward_workspace_bytes(0, 300, 4) == 0
+
 def test_two_stage_flag_errors_are_synchronous(lib):
     ts = 128
     q, M, K, N = 2, 64, 16, 16

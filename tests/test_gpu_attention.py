@@ -1,4 +1,5 @@
-"""Causal attention with the algebraic score (appendix G) on the GPU against the fp64 oracle.
+"""Causal attention with the algebraic score (appendix G) on the GPU against the fp64 oracle:
+the prefill forward, the cached decode, and the gradients.
 
 Bar: relative Frobenius error of each head's output <= 5e-3 (bf16).  The kernel
 rounds P to bf16 for the value product (<= 2^-9 relative per weight) and O once;
@@ -167,3 +168,85 @@ def test_attention_decode_empty_rows_are_zero():
     assert not got[0].any() and not got[1].any()
     Or = O.algebraic_attention_decode(Qo.f64, Ko.f64, Vo.f64, q_pos, key_pos, q)
     assert _rel(got[2], Or[2]) <= BF16_TOL
+
+
+BWD_SHAPES = [
+    # Hq, Hkv, S, d, q, L, first position
+    (4, 2, 300, 128, 4, 0, 0),     # GQA 2, ragged S (several 64-row blocks per type, a partial one)
+    (2, 2, 257, 64, 4, 0, 5),      # d = 64 at an offset
+    (2, 1, 200, 128, 4, 2, 3),     # the recursive law Q_2^(x)2 at an offset, GQA 2
+    (4, 4, 390, 128, 8, 0, 0),     # q = 8: groups of 16 features, half a 32-feature block
+    (2, 2, 160, 128, 2, 1, 1),     # L = 1 is Q_2
+    (2, 2, 100, 128, 1, 0, 0),     # q = 1: ordinary causal attention
+    (3, 3, 1, 128, 4, 0, 0),       # one position
+    (8, 2, 1100, 128, 4, 0, 2),    # GQA 4, more than one 128-key block per type
+]
+
+
+@pytest.mark.parametrize("shape", BWD_SHAPES, ids=[f"H{s[0]}kv{s[1]}S{s[2]}d{s[3]}q{s[4]}L{s[5]}p{s[6]}" for s in BWD_SHAPES])
+def test_attention_backward_matches_oracle(shape):
+    """Algorithm 2, step 9 on the GPU (the training forward's O and lse, then dQ, dK, dV) against the
+    oracle's fp64 gradients on the same bf16 inputs.  Bar: relative Frobenius error of each head's
+    gradient <= 5e-3 (BF16_TOL).  Each gradient is an fp32 sum of products in which one factor was
+    rounded to bf16 (P for dV; dS for dQ and dK, whose own error adds the rounding of O in
+    D = <dO, O>), i.e. relative errors of at most 2^-9 per term that do not line up in sign; the
+    measured errors (2.3e-3 to 2.8e-3) are printed by the test.  Where the exact gradient is zero
+    (one position: the softmax over one key is constant, so dQ = dK = 0), the bar is an absolute
+    1e-3 on the largest element (the GPU leaves the fp32 rounding of dP - D)."""
+    torch = torch_cuda()
+    Hq, Hkv, S, d, q, L, p0 = shape
+    say(f"[attn bwd] Hq={Hq} Hkv={Hkv} S={S} d={d} q={q} L={L} p0={p0}")
+    Qo = synth.normal_operand(9620 + S, (Hq, S, d), 1.0, "bf16")
+    Ko = synth.normal_operand(9720 + S, (Hkv, S, d), 1.0, "bf16")
+    Vo = synth.normal_operand(9820 + S, (Hkv, S, d), 1.0, "bf16")
+    dOo = synth.normal_operand(9920 + S, (Hq, S, d), 1.0, "bf16")
+    flags = Q.QALG_FLAG_LAW_TENSOR if L else 0
+    Qd, Kd, Vd, dOd = to_dev(Qo), to_dev(Ko), to_dev(Vo), to_dev(dOo)
+    Og, lse = Q.qalg_attention_forward_train(Qd, Kd, Vd, q, p0, flags=flags)
+    Oa = Q.qalg_attention_forward_at(Qd, Kd, Vd, q, p0, flags=flags)
+    g1 = Q.qalg_attention_backward(Qd, Kd, Vd, Og, dOd, lse, q, p0, flags=flags)
+    g2 = Q.qalg_attention_backward(Qd, Kd, Vd, Og, dOd, lse, q, p0, flags=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(Og, Oa), "the training forward's O differs from the forward's"
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b), "not bitwise reproducible"
+    pos = p0 + np.arange(S)
+    want = O.algebraic_attention_backward(Qo.f64, Ko.f64, Vo.f64, dOo.f64, pos % q, q, L, positions=pos)
+    worst = {}
+    for name, got, ref in zip(("dQ", "dK", "dV"), g1, want):
+        got = to_f64(got)
+        assert np.isfinite(got).all(), name
+        errs = []
+        for h in range(ref.shape[0]):
+            if np.linalg.norm(ref[h]) == 0.0:
+                assert np.abs(got[h]).max() <= 1e-3, (name, h, np.abs(got[h]).max())
+            else:
+                errs.append(_rel(got[h], ref[h]))
+        worst[name] = max(errs, default=0.0)
+    say("    max rel err over heads " + ", ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+    assert max(worst.values()) <= BF16_TOL, worst
+
+
+def test_attention_backward_full_size_one_group():
+    """The bench's attention shape (32 query heads over 8 key/value heads, S = 4096, d = 128, q = 4):
+    the GPU computes every head; the oracle recomputes the gradients of key/value head 0 and of the
+    4 query heads that read it (which depend on nothing else), whole, to the same bar."""
+    torch = torch_cuda()
+    Hq, Hkv, S, d, q = 32, 8, 4096, 128, 4
+    say(f"[attn bwd full] Hq={Hq} Hkv={Hkv} S={S} d={d} q={q}")
+    Qo = synth.normal_operand(9631, (Hq, S, d), 1.0, "bf16")
+    Ko = synth.normal_operand(9731, (Hkv, S, d), 1.0, "bf16")
+    Vo = synth.normal_operand(9831, (Hkv, S, d), 1.0, "bf16")
+    dOo = synth.normal_operand(9931, (Hq, S, d), 1.0, "bf16")
+    Qd, Kd, Vd, dOd = to_dev(Qo), to_dev(Ko), to_dev(Vo), to_dev(dOo)
+    Og, lse = Q.qalg_attention_forward_train(Qd, Kd, Vd, q)
+    dQ, dK, dV = Q.qalg_attention_backward(Qd, Kd, Vd, Og, dOd, lse, q)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    tau = np.arange(S) % q
+    want = O.algebraic_attention_backward(Qo.f64[:G], Ko.f64[:1], Vo.f64[:1], dOo.f64[:G], tau, q)
+    worst = {}
+    for name, got, ref in zip(("dQ", "dK", "dV"), (to_f64(dQ)[:G], to_f64(dK)[:1], to_f64(dV)[:1]), want):
+        worst[name] = max(_rel(got[h], ref[h]) for h in range(ref.shape[0]))
+    say("    max rel err over heads " + ", ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+    assert max(worst.values()) <= BF16_TOL, worst
