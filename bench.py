@@ -851,13 +851,20 @@ def few_rows_leg(Q, torch, np, synth, dev, stream):
 def attention_leg(Q, torch, np, synth, dev, stream):
     """Causal attention with the algebraic score (appendix G): 32 query heads, 8 key/value heads,
     d = 128, S = 4096 (one sequence), q = 4 under Q_4 and under Q_2^(x)2, and the same kernel at
-    q = 1 (ordinary attention).  FLOP: 2 |F| m per allowed pair for QK^T plus 2 d for PV."""
+    q = 1 (ordinary attention).  FLOP: 2 |F| m per allowed pair for QK^T plus 2 d for PV.
+    Training (Algorithm 2 with step 9): the forward that keeps the log-sum-exp, then the gradients,
+    which recompute the scores twice and form dQ and dK over the compared groups (4 score-sized
+    products) and dP twice and dV (3 d-sized products per allowed pair)."""
     c, Hq, Hkv, S, d, q = 9, 32, 8, 4096, 128, 4
     to = lambda op: torch.from_numpy(op.bits.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
     Qd = to(synth.normal_operand(1000 * c + 1, (Hq, S, d), 1.0, "bf16"))
     Kd = to(synth.normal_operand(1000 * c + 2, (Hkv, S, d), 1.0, "bf16"))
     Vd = to(synth.normal_operand(1000 * c + 3, (Hkv, S, d), 1.0, "bf16"))
     Od = torch.empty_like(Qd)
+    dOd = to(synth.normal_operand(1000 * c + 4, (Hq, S, d), 1.0, "bf16"))
+    lse = torch.empty((Hq, S), dtype=torch.float32, device=dev)
+    dQd, dKd, dVd = torch.empty_like(Qd), torch.empty_like(Kd), torch.empty_like(Vd)
+    ws_b = torch.empty(Q.qalg_attention_backward_workspace_bytes(Hq, Hkv, S, d, q), dtype=torch.uint8, device=dev)
     pairs = S * (S + 1) // 2
     same = {}  # allowed pairs with equal types, per q (cyclic types)
     for qq in (1, q):
@@ -891,8 +898,31 @@ def attention_leg(Q, torch, np, synth, dev, stream):
         flop = 2.0 * Hq * (score + pairs * d)
         out[name] = {"ms": round(ms, 4), "algebra_tflops": round(flop / (ms * 1e-3) / 1e12, 1),
                      "score_fraction": round(score / (pairs * d), 4)}
+        # training: forward with lse, then the gradients
+        fwd_t = lambda: Q.qalg_attention_forward_train(Qd, Kd, Vd, qq, 0, O=Od, lse=lse, flags=fl, stream=stream)  # noqa: E731
+        bwd = lambda: Q.qalg_attention_backward(Qd, Kd, Vd, Od, dOd, lse, qq, 0, dQ=dQd, dK=dKd, dV=dVd, ws=ws_b,  # noqa: E731
+                                                flags=fl, stream=stream)
+        for _ in range(2):
+            fwd_t()
+            bwd()
+        torch.cuda.synchronize()
+        ts = [ev() for _ in range(2 * n + 1)]
+        ts[0].record(stream)
+        for k in range(n):
+            fwd_t()
+            ts[2 * k + 1].record(stream)
+            bwd()
+            ts[2 * k + 2].record(stream)
+        torch.cuda.synchronize()
+        f_ms = sum(ts[2 * k].elapsed_time(ts[2 * k + 1]) for k in range(n)) / n
+        b_ms = sum(ts[2 * k + 1].elapsed_time(ts[2 * k + 2]) for k in range(n)) / n
+        bflop = 2.0 * Hq * (4 * score + 3 * pairs * d)
+        out[name].update({"train_fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+                          "bwd_algebra_tflops": round(bflop / (b_ms * 1e-3) / 1e12, 1),
+                          "train_step_ms": round(f_ms + b_ms, 4)})
     for name in ("complete_q4", "tensor_q4"):
         out[name]["speedup_vs_q1"] = round(out["dense_q1"]["ms"] / out[name]["ms"], 3)
+        out[name]["train_speedup_vs_q1"] = round(out["dense_q1"]["train_step_ms"] / out[name]["train_step_ms"], 3)
         rho = out[name]["score_fraction"]
         out[name]["ceiling"] = round(2 / (1 + rho), 3)   # eq 46
     log(f"[bench] attention leg: {out}")

@@ -110,7 +110,7 @@ _SIGS = {
                                              _c_i32, _c_i64, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
     "qalg_attention_forward_train": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_i64,
                                                     _vp, _vp, _c_i32, _c_u32, _vp]),
-    "qalg_attention_backward_workspace_bytes": (_c_size, [_c_i32, _c_i64, _c_i32]),
+    "qalg_attention_backward_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i64, _c_i32, _c_i32]),
     "qalg_attention_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32,
                                                _c_i64, _vp, _vp, _vp, _c_i32, _vp, _c_size, _c_u32, _vp]),
 }
@@ -588,8 +588,8 @@ def qalg_attention_forward_train(Qh, Kh, Vh, q: int, first_position: int = 0, O=
     return O, lse
 
 
-def qalg_attention_backward_workspace_bytes(Hq: int, S: int, q: int) -> int:
-    return lib().qalg_attention_backward_workspace_bytes(Hq, S, q)
+def qalg_attention_backward_workspace_bytes(Hq: int, Hkv: int, S: int, d: int, q: int) -> int:
+    return lib().qalg_attention_backward_workspace_bytes(Hq, Hkv, S, d, q)
 
 
 def qalg_attention_backward(Qh, Kh, Vh, Oh, dOh, lse, q: int, first_position: int = 0, dQ=None, dK=None, dV=None,
@@ -606,7 +606,7 @@ def qalg_attention_backward(Qh, Kh, Vh, Oh, dOh, lse, q: int, first_position: in
     dQ = _new_or_check(dQ, (Hq, S, d), Qh, "dQ")
     dK = _new_or_check(dK, (Hkv, S, d), Qh, "dK")
     dV = _new_or_check(dV, (Hkv, S, d), Qh, "dV")
-    need = qalg_attention_backward_workspace_bytes(Hq, S, q)
+    need = qalg_attention_backward_workspace_bytes(Hq, Hkv, S, d, q)
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=Qh.device)
     else:

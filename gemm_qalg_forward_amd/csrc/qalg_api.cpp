@@ -681,9 +681,9 @@ qalg_status qalg_attention_forward_train(const void* Q, const void* K, const voi
                                                    static_cast<hipStream_t>(stream)));
 }
 
-size_t qalg_attention_backward_workspace_bytes(int32_t Hq, int64_t S, int32_t q) {
-  if (Hq < 1 || S < 0 || q < 1 || q > QALG_MAX_Q) return 0;
-  const size_t n = qalg::attn_bwd_stat_bytes(Hq, S, q);
+size_t qalg_attention_backward_workspace_bytes(int32_t Hq, int32_t Hkv, int64_t S, int32_t d, int32_t q) {
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv || S < 0 || (d != 64 && d != 128) || q < 1 || q > QALG_MAX_Q) return 0;
+  const size_t n = qalg::attn_bwd_ws_bytes(Hq, Hkv, S, d, q);
   return (n + 255) / 256 * 256;
 }
 
@@ -701,7 +701,7 @@ qalg_status qalg_attention_backward(const void* Q, const void* K, const void* V,
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(dQ) ||
       !aligned16(dK) || !aligned16(dV) || reinterpret_cast<uintptr_t>(lse) % 4)
     return QALG_ERR_ALIGN;
-  if (!aligned16(ws) || ws_bytes < qalg_attention_backward_workspace_bytes(Hq, S, q)) return QALG_ERR_WORKSPACE;
+  if (!aligned16(ws) || ws_bytes < qalg_attention_backward_workspace_bytes(Hq, Hkv, S, d, q)) return QALG_ERR_WORKSPACE;
   return hip_status(qalg::launch_attn_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, ws, Hq, Hkv, S, d, q, L,
                                                first_position, static_cast<hipStream_t>(stream)));
 }

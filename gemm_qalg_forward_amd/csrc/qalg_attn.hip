@@ -707,10 +707,12 @@ struct AttnBwdArgs {
   char* dQ;
   char* dK;
   char* dV;
+  float* part;        // hsplit > 1: fp32 dK, dV of each head share, hsplit x 2 x Hkv x S x d
   int Hq, Hkv, S, q, L, m, o;
   int n_qblk;         // 128-query blocks per (head, type)
   int n_kblk;         // 128-key blocks per (key/value head, type)
   int n_pad;          // pairs per (head, type): ceil(S / q) rounded up to 64
+  int hsplit;         // workgroups sharing a key block's query heads (1 or 2)
 };
 
 // Transposing-read offsets for a 16-row step of swk rows: lane (g = lane / 16,
@@ -761,16 +763,19 @@ __device__ __forceinline__ bf16x8 pack_rows(const f32x16 (&x)[2]) {
 }
 
 // the support of types (i, j) as MFMA slots: slot x is the x-th 16-feature
-// step of F(i, j) (piece 2 step of a row; the B fragment f[step]); per
-// 32-feature block, whether it meets F(i, j) (uniform) and whether this lane's
-// feature (32 db + l32) lies in it
+// step of F(i, j) (piece 2 step + lhi of a row; its B fragment is loaded again
+// from the lane's own row in global memory when the pair of types changes,
+// which is rarer than a register select over all d / 16 fragments is cheap);
+// per 32-feature block, whether it meets F(i, j) (uniform) and whether this
+// lane's feature (32 db + l32) lies in it
 template <int D>
 struct BwdSupport {
   int tot, nf;
   int kp[D / 16];
   bf16x8 sl[D / 16];
   bool blk[D / 32], lane_in[D / 32];
-  __device__ __forceinline__ void set(int i, int j, int L, int m, int l32, const bf16x8 (&f)[D / 16]) {
+  // row: the lane's row in global memory, advanced by 16 lhi bytes
+  __device__ __forceinline__ void set(int i, int j, int L, int m, int l32, const char* row) {
     constexpr int KS = D / 16;
     const int ms = m / 16;
     nf = uni(support_count(i, j, L));
@@ -779,11 +784,7 @@ struct BwdSupport {
     for (int x = 0; x < KS; ++x) {
       const int step = x < tot ? support_group(i, j, L, x / ms) * ms + x % ms : 0;
       kp[x] = uni(2 * step);
-      bf16x8 v = f[0];
-#pragma unroll
-      for (int z = 1; z < KS; ++z)
-        if (z == step) v = f[z];
-      sl[x] = v;
+      sl[x] = *reinterpret_cast<const bf16x8*>(row + 32 * step);
     }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
@@ -871,7 +872,7 @@ __device__ __forceinline__ void store_row(char* row, const f32x16 (&acc)[D / 32]
 }
 
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   constexpr int ROWB = D * 2;
   constexpr int NP = D / 8;
   constexpr int KS = D / 16;
@@ -906,16 +907,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArg
   const char* Vh = a.V + int64_t(kvh) * S * ROWB;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(smem)));
 
-  // this lane's query row: Q and dO fragments in registers; D = <dO, O> in fp32
+  // this lane's query row: dO fragments in registers (Q's are read per key
+  // type, for the support's groups only); D = <dO, O> in fp32
   const int tq = t0 + wid * 32 + l32;
   const bool q_ok = tq < n_i;
   const int pq = si + q * min(tq, n_i - 1);
-  bf16x8 qf[KS], df[KS];
+  bf16x8 df[KS];
   float dsum = 0.f;
+  const char* q_row = a.Q + hoff + int64_t(pq) * ROWB + 16 * lhi;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int64_t off = hoff + int64_t(pq) * ROWB + (2 * ks + lhi) * 16;
-    qf[ks] = *reinterpret_cast<const bf16x8*>(a.Q + off);
     df[ks] = *reinterpret_cast<const bf16x8*>(a.dO + off);
     const bf16x8 of = *reinterpret_cast<const bf16x8*>(a.O + off);
 #pragma unroll
@@ -991,7 +993,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dq_kernel(AttnBwdArg
     const char* sV = sK + BLK;
     if (j != cur_j) {
       cur_j = j;
-      sp.set(i, j, a.L, a.m, l32, qf);
+      sp.set(i, j, a.L, a.m, l32, q_row);
     }
     f32x16 sc[2], dp[2];
     support_scores_any<D>(sc, sK, sp, l32, lhi);
@@ -1033,13 +1035,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkdv_kernel(AttnBwdA
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, lhi = lane >> 5;
   const int q = a.q, S = a.S;
-  // block -> (key block, key type, key/value head), early (heavy) key blocks first
+  // block -> (key block, key type, key/value head, share of the query heads),
+  // early (heavy) key blocks first
   int bid = blockIdx.x;
-  const int kb = bid / (q * a.Hkv);
-  bid -= kb * q * a.Hkv;
+  const int per_kb = q * a.Hkv * a.hsplit;
+  const int kb = bid / per_kb;
+  bid -= kb * per_kb;
+  const int hp = bid % a.hsplit;
+  bid /= a.hsplit;
   const int j = bid % q;
   const int hk = bid / q;
-  const int G = a.Hq / a.Hkv;
+  const int Gall = a.Hq / a.Hkv;
+  const int G = Gall / a.hsplit;      // query heads of this share: hk Gall + hp G + 0 .. G - 1
   auto first_row = [&](int t) -> int { return t >= a.o ? t - a.o : t - a.o + q; };
   auto n_of = [&](int t) -> int {
     const int s_ = first_row(t);
@@ -1052,17 +1059,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkdv_kernel(AttnBwdA
   const int p_first = sj + q * t0;
   const int p_wave_last = sj + q * min(t0 + 32 * wid + 31, n_j - 1);
 
-  // this lane's key: K and V fragments in registers
+  // this lane's key: V fragments in registers (K's are read per query type,
+  // for the support's groups only)
   const int tk = t0 + wid * 32 + l32;
   const bool k_ok = tk < n_j;
   const int pk = sj + q * min(tk, n_j - 1);
   const int64_t koff = int64_t(hk) * S * ROWB + int64_t(pk) * ROWB;
-  bf16x8 kf[KS], vf[KS];
+  bf16x8 vf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = *reinterpret_cast<const bf16x8*>(a.K + koff + (2 * ks + lhi) * 16);
-    vf[ks] = *reinterpret_cast<const bf16x8*>(a.V + koff + (2 * ks + lhi) * 16);
-  }
+  for (int ks = 0; ks < KS; ++ks) vf[ks] = *reinterpret_cast<const bf16x8*>(a.V + koff + (2 * ks + lhi) * 16);
+  const char* k_row = a.K + koff + 16 * lhi;
   f32x16 accK[DB], accV[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -1100,7 +1106,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkdv_kernel(AttnBwdA
     }
   };
   auto issue = [&](int stage) {
-    const int h = hk * G + cg;
+    const int h = hk * Gall + hp * G + cg;
     const int n = n_of(ci), s_ = first_row(ci);
     const char* Qh = a.Q + int64_t(h) * S * ROWB;
     const char* dOh = a.dO + int64_t(h) * S * ROWB;
@@ -1144,7 +1150,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkdv_kernel(AttnBwdA
     const char* sst = sdO + BLK;
     if (i != cur_i) {
       cur_i = i;
-      sp.set(i, j, a.L, a.m, l32, kf);
+      sp.set(i, j, a.L, a.m, l32, k_row);
     }
     f32x16 sc[2], dp[2];
     support_scores_any<D>(sc, sQ, sp, l32, lhi);
@@ -1177,10 +1183,56 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkdv_kernel(AttnBwdA
     if (!more) break;
     stage ^= 1;
   }
-  if (k_ok) {
+  if (!k_ok) return;
+  if (a.hsplit == 1) {
     store_row<D>(a.dK + koff, accK, lhi);
     store_row<D>(a.dV + koff, accV, lhi);
+    return;
   }
+  // this share's sums in fp32; attn_bwd_reduce_kernel adds the shares in order
+  const int64_t rows = int64_t(a.Hkv) * S;
+  float* pk_row = a.part + ((int64_t(hp) * 2) * rows + int64_t(hk) * S + pk) * D;
+  float* pv_row = pk_row + rows * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int f = 32 * db + 8 * g + 4 * lhi;
+      *reinterpret_cast<float4*>(pk_row + f) =
+          make_float4(accK[db][4 * g], accK[db][4 * g + 1], accK[db][4 * g + 2], accK[db][4 * g + 3]);
+      *reinterpret_cast<float4*>(pv_row + f) =
+          make_float4(accV[db][4 * g], accV[db][4 * g + 1], accV[db][4 * g + 2], accV[db][4 * g + 3]);
+    }
+}
+
+// dK and dV from the head shares' fp32 sums, added in share order (one
+// rounding; the result does not depend on scheduling): 8 features per thread
+__global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(const float* __restrict__ part, int hsplit,
+                                                              int64_t n, char* __restrict__ dK,
+                                                              char* __restrict__ dV) {
+  const int64_t x = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (x >= 2 * n) return;
+  const bool is_v = x >= n;
+  const int64_t e = is_v ? x - n : x;
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = 0.f;
+  for (int p = 0; p < hsplit; ++p) {
+    const float* src = part + int64_t(p) * 2 * n + x;
+    const float4 lo = *reinterpret_cast<const float4*>(src);
+    const float4 hi = *reinterpret_cast<const float4*>(src + 4);
+    v[0] += lo.x;
+    v[1] += lo.y;
+    v[2] += lo.z;
+    v[3] += lo.w;
+    v[4] += hi.x;
+    v[5] += hi.y;
+    v[6] += hi.z;
+    v[7] += hi.w;
+  }
+  const u32x2 a0 = pack4_bf16(v[0], v[1], v[2], v[3]);
+  const u32x2 a1 = pack4_bf16(v[4], v[5], v[6], v[7]);
+  *reinterpret_cast<u32x4*>((is_v ? dV : dK) + e * 2) = (u32x4){a0[0], a0[1], a1[0], a1[1]};
 }
 
 }  // namespace
@@ -1224,6 +1276,20 @@ size_t attn_bwd_stat_bytes(int64_t Hq, int64_t S, int q) {
   return size_t((Hq * q * n_pad + 64) * 2) * sizeof(float);
 }
 
+// Query heads per key/value head split over two workgroups when there are an
+// even number of them: the earliest keys of a causal sequence see every query
+// and the latest few, so with one workgroup per key block the first blocks
+// would set the kernel's length; two shares of the heads halve the longest
+// workgroups and give the scheduler twice the blocks to balance.
+int attn_bwd_hsplit(int Hq, int Hkv) { return (Hq / Hkv) % 2 == 0 ? 2 : 1; }
+
+size_t attn_bwd_ws_bytes(int64_t Hq, int64_t Hkv, int64_t S, int d, int q) {
+  const size_t stat = (attn_bwd_stat_bytes(Hq, S, q) + 255) / 256 * 256;
+  const int hs = attn_bwd_hsplit(int(Hq), int(Hkv));
+  const size_t part = hs > 1 ? size_t(hs) * 2 * size_t(Hkv) * size_t(S) * size_t(d) * sizeof(float) : 0;
+  return stat + part;
+}
+
 hipError_t launch_attn_bwd_bf16(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                                 const float* lse, void* dQ, void* dK, void* dV, void* stat, int Hq, int Hkv,
                                 int64_t S, int d, int q, int L, int64_t first_pos, hipStream_t s) {
@@ -1235,6 +1301,10 @@ hipError_t launch_attn_bwd_bf16(const void* Q, const void* K, const void* V, con
   a.dO = static_cast<const char*>(dO);
   a.lse = lse;
   a.stat = static_cast<float*>(stat);
+  a.hsplit = attn_bwd_hsplit(Hq, Hkv);
+  a.part = a.hsplit > 1 ? reinterpret_cast<float*>(static_cast<char*>(stat) +
+                                                   (attn_bwd_stat_bytes(Hq, S, q) + 255) / 256 * 256)
+                        : nullptr;
   a.dQ = static_cast<char*>(dQ);
   a.dK = static_cast<char*>(dK);
   a.dV = static_cast<char*>(dV);
@@ -1250,7 +1320,7 @@ hipError_t launch_attn_bwd_bf16(const void* Q, const void* K, const void* V, con
   a.n_kblk = a.n_qblk;
   a.n_pad = int((n0 + 63) / 64 * 64);
   const int64_t qblocks = int64_t(Hq) * q * a.n_qblk;
-  const int64_t kblocks = int64_t(Hkv) * q * a.n_kblk;
+  const int64_t kblocks = int64_t(Hkv) * q * a.n_kblk * a.hsplit;
   if (qblocks == 0) return hipSuccess;
   // dQ first: it also writes the (lse, D) pairs the dK / dV kernel reads
   if (d == 128) {
@@ -1261,6 +1331,13 @@ hipError_t launch_attn_bwd_bf16(const void* Q, const void* K, const void* V, con
     hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(unsigned(qblocks)), dim3(kAttnThreads), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, dim3(unsigned(kblocks)), dim3(kAttnThreads), 0, s, a);
+  }
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  if (a.hsplit > 1) {
+    const int64_t n = int64_t(Hkv) * S * d;  // elements of dK (and of dV)
+    const int64_t threads = 2 * n / 8;
+    hipLaunchKernelGGL(attn_bwd_reduce_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, a.part,
+                       a.hsplit, n, a.dK, a.dV);
   }
   return hipGetLastError();
 }

@@ -131,6 +131,7 @@ hipError_t launch_attn_fwd_lse_bf16(const void* Q, const void* K, const void* V,
                                     int Hkv, int64_t S, int d, int q, int L, int64_t first_pos, hipStream_t s);
 // the backward's per-query (lse, D) scratch, and the two backward kernels
 size_t attn_bwd_stat_bytes(int64_t Hq, int64_t S, int q);
+size_t attn_bwd_ws_bytes(int64_t Hq, int64_t Hkv, int64_t S, int d, int q);  // the stat pairs and the head-share sums
 hipError_t launch_attn_bwd_bf16(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                                 const float* lse, void* dQ, void* dK, void* dV, void* stat, int Hq, int Hkv,
                                 int64_t S, int d, int q, int L, int64_t first_pos, hipStream_t s);

@@ -474,15 +474,17 @@ qalg_status qalg_attention_forward_train(const void* Q, const void* K, const voi
  * tensors bf16 (lse fp32), packed, 16-byte aligned (lse 4-byte), caller-owned
  * device memory.  fp32 scores, statistics and sums; P and dS are rounded to
  * bf16 for the matrix products, each output once at the end; every output
- * element is written by one workgroup (no atomics): bitwise reproducible.
+ * element is summed in a fixed order (no atomics): bitwise reproducible.
  * ws: caller-owned device scratch of at least
- * qalg_attention_backward_workspace_bytes(Hq, S, q) bytes, 16-byte aligned
- * (per-query lse and D, grouped by type).  Errors as
+ * qalg_attention_backward_workspace_bytes(Hq, Hkv, S, d, q) bytes, 16-byte
+ * aligned (per-query lse and D, grouped by type; with an even number of query
+ * heads per key/value head, also fp32 dK and dV of two shares of those heads,
+ * added in a fixed order at the end).  Errors as
  * qalg_attention_forward_at, plus QALG_ERR_NULL for a null pointer (ws
  * included) and QALG_ERR_WORKSPACE for a small or misaligned ws.  S = 0
  * returns QALG_OK without a launch.
  */
-size_t qalg_attention_backward_workspace_bytes(int32_t Hq, int64_t S, int32_t q);
+size_t qalg_attention_backward_workspace_bytes(int32_t Hq, int32_t Hkv, int64_t S, int32_t d, int32_t q);
 qalg_status qalg_attention_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                                     const float* lse, int32_t Hq, int32_t Hkv, int64_t S, int32_t d, int32_t q,
                                     int64_t first_position, void* dQ, void* dK, void* dV, int32_t dtype, void* ws,

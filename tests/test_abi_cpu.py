@@ -417,10 +417,14 @@ def test_attention_training_argument_errors_are_synchronous(lib):
     assert bwd(wsb=64) == 6
     assert bwd(ws=FAKE + 8) == 6
     assert bwd(S=0, dO=None) == 0
-    # per (head, type): ceil(S / q) rounded up to 64 pairs of fp32, plus 64 spare pairs
-    need = Q.qalg_attention_backward_workspace_bytes(4, 300, 4)
-    assert need >= (4 * 4 * 128 + 64) * 8 and need % 256 == 0
-    assert Q.qalg_attention_backward_workspace_bytes(0, 300, 4) == 0
+    # per (head, type): ceil(S / q) rounded up to 64 pairs of fp32, plus 64 spare pairs; with an
+    # even number of query heads per key/value head also two shares of fp32 dK and dV
+    one = Q.qalg_attention_backward_workspace_bytes(3, 3, 300, 128, 4)
+    assert one >= (3 * 4 * 128 + 64) * 8 and one % 256 == 0
+    two = Q.qalg_attention_backward_workspace_bytes(4, 2, 300, 128, 4)
+    assert two >= (4 * 4 * 128 + 64) * 8 + 2 * 2 * 2 * 300 * 128 * 4 and two % 256 == 0
+    assert Q.qalg_attention_backward_workspace_bytes(0, 1, 300, 128, 4) == 0
+    assert Q.qalg_attention_backward_workspace_bytes(4, 3, 300, 128, 4) == 0
 
 def test_two_stage_flag_errors_are_synchronous(lib):
     ts = 128
