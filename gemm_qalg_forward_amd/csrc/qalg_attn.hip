@@ -1003,15 +1003,28 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bwd_dq_kernel(AttnBwdArg
     const int nk_j = keys_of(j);
     const int sj = first_row(j);
     const bool full = tb + kAttnK <= nk_j && sj + q * (tb + kAttnK - 1) <= p_wave0;
+    // dS = P (dP - D) c; a block wholly inside every query's causal range
+    // (the usual case) takes the branch without the mask
+    auto ds_pass = [&](auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int tk = tb + nb * 32 + 8 * (e >> 2) + 4 * lhi + (e & 3);
-        const bool ok = full || (tk < nk_j && sj + q * tk <= pq);
-        const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nb][e], scl, -lse2)) : 0.f;
-        dp[nb][e] = ok ? p * (dp[nb][e] - dsum) * c : 0.f;
-      }
+        for (int e = 0; e < 16; ++e) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nb][e], scl, -lse2));
+          const float v = p * (dp[nb][e] - dsum) * c;
+          if constexpr (FULL) {
+            dp[nb][e] = v;
+          } else {
+            const int tk = tb + nb * 32 + 8 * (e >> 2) + 4 * lhi + (e & 3);
+            dp[nb][e] = (tk < nk_j && sj + q * tk <= pq) ? v : 0.f;
+          }
+        }
+    };
+    if (full)
+      ds_pass(std::true_type{});
+    else
+      ds_pass(std::false_type{});
     accumulate_tr<D, true>(acc, sK, dp, tlo, thi, sp);
     if (!more) break;
     stage ^= 1;
@@ -1159,25 +1172,40 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkdv_kernel(AttnBwdA
     const float scl = log2e * c;
     const int n_i = n_of(i), s_i = first_row(i);
     const bool full = tb + kAttnK <= n_i && s_i + q * tb >= p_wave_last;
+    // P and dS = P (dP - D) c; masked pairs (and the rows past the type's
+    // last query, whose pairs hold other data) are set to 0 by selects
+    auto pds_pass = [&](auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int r0 = nb * 32 + 8 * g4 + 4 * lhi;  // the lane's 4 consecutive queries
-        const float4 w0 = *reinterpret_cast<const float4*>(sst + 8 * r0);
-        const float4 w1 = *reinterpret_cast<const float4*>(sst + 8 * r0 + 16);
-        const float ls[4] = {w0.x, w0.z, w1.x, w1.z};
-        const float dd[4] = {w0.y, w0.w, w1.y, w1.w};
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int r0 = nb * 32 + 8 * g4 + 4 * lhi;  // the lane's 4 consecutive queries
+          const float4 w0 = *reinterpret_cast<const float4*>(sst + 8 * r0);
+          const float4 w1 = *reinterpret_cast<const float4*>(sst + 8 * r0 + 16);
+          const float ls[4] = {w0.x, w0.z, w1.x, w1.z};
+          const float dd[4] = {w0.y, w0.w, w1.y, w1.w};
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int e = 4 * g4 + e4;
-          const int tq = tb + r0 + e4;
-          const bool ok = full || (tq < n_i && s_i + q * tq >= pk);
-          const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nb][e], scl, -ls[e4])) : 0.f;
-          dp[nb][e] = ok ? p * (dp[nb][e] - dd[e4]) * c : 0.f;
-          sc[nb][e] = p;
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int e = 4 * g4 + e4;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nb][e], scl, -ls[e4]));
+            const float v = p * (dp[nb][e] - dd[e4]) * c;
+            if constexpr (FULL) {
+              dp[nb][e] = v;
+              sc[nb][e] = p;
+            } else {
+              const int tq = tb + r0 + e4;
+              const bool ok = tq < n_i && s_i + q * tq >= pk;
+              dp[nb][e] = ok ? v : 0.f;
+              sc[nb][e] = ok ? p : 0.f;
+            }
+          }
         }
-      }
+    };
+    if (full)
+      pds_pass(std::true_type{});
+    else
+      pds_pass(std::false_type{});
     accumulate_tr<D, false>(accV, sdO, sc, tlo, thi, sp);
     accumulate_tr<D, true>(accK, sQ, dp, tlo, thi, sp);
     if (!more) break;
