@@ -50,6 +50,7 @@ struct SmallArgs {
   int q, M, K, N, s, r;
   int chunks_per_group;
   int x_regions;   // staged activation regions: 1 (one block at a time) or the most blocks a chunk needs
+  int xcd_order;   // 1: consecutive chunks on one XCD (column groups that are not whole cache lines)
 };
 
 
@@ -78,9 +79,22 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
   __shared__ int s_blocks[R + 1];
   __shared__ int s_nblk;
 
-  const int e = blockIdx.y;
-  const int j = blockIdx.x / a.chunks_per_group;
-  const int ch = blockIdx.x - j * a.chunks_per_group;
+  // Column groups whose rows are not whole 128-byte lines (e.g. 96 columns,
+  // 192 bytes) put chunk boundaries inside cache lines.  Then workgroups are
+  // renumbered so that consecutive chunks run on one XCD (workgroup w runs on
+  // XCD w mod 8, w the linear id, x fastest): the chunks of a weight row meet
+  // in one L2 and a line two chunks share is fetched once (2048 -> 768, q = 8,
+  // one row per expert: 1.67x -> 1.17x the needed bytes, 21.9 -> 20.0 us).
+  // Line-aligned groups keep the plain order, which measured 4 % faster on
+  // 7168 -> 2048, q = 4.
+  const int gx = gridDim.x;
+  const int total = gx * gridDim.y;
+  int lin = blockIdx.y * gx + blockIdx.x;
+  if (a.xcd_order && (total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+  const int e = lin / gx;
+  const int bx = lin - e * gx;
+  const int j = bx / a.chunks_per_group;
+  const int ch = bx - j * a.chunks_per_group;
   const int col0 = j * a.r + ch * kSmCols;
   const int ncol = min(kSmCols, a.r - ch * kSmCols);
   const int M = a.M, K = a.K, N = a.N, s = a.s, q = a.q;
@@ -253,6 +267,7 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
 template <int R, int COLS>
 hipError_t launch_rc(SmallArgs a, int E, hipStream_t st) {
   a.chunks_per_group = (a.r + COLS - 1) / COLS;
+  a.xcd_order = (2 * a.r) % 128 != 0 ? 1 : 0;
   const dim3 grid(unsigned(a.q * a.chunks_per_group), unsigned(E));
   constexpr int KL = kSmThreads / (COLS / 8);  // weight rows per step (the pair distance)
   constexpr int kStep = KL * kSmUnroll;          // weight rows per batch
