@@ -692,9 +692,24 @@ __global__ __launch_bounds__(D) void attn_decode_combine_kernel(const float* __r
 // and dK^T += Q^T dS (Q and dO read transposed).  Each key's dK and dV come
 // from one workgroup, so no atomics and bitwise reproducible.  P and dS enter
 // the MFMAs in bf16; everything else stays fp32 until the one rounding of dQ,
-// dK and dV.  Rows live in LDS in the K layout above (swk); the transposing
-// reads compute each lane's address through the same swizzle.
+// dK and dV.  Rows live in LDS in the layout swb below (good for both the
+// row and the transposing reads).
 // ---------------------------------------------------------------------------
+
+// LDS layout of the backward's row blocks: rows are read both as rows (16
+// bytes per lane, 16 consecutive rows per pass) and transposed (8 bytes per
+// lane, 4 rows x 4 pieces of one 64-byte column block per 32 lanes), so row r
+// keeps its 16-byte piece c at c ^ swb(r), which is a permutation of the
+// pieces over any 16 consecutive rows and sends the 4 rows of a transposed
+// read to 4 different 64-byte blocks: both reads are free of bank conflicts
+// (the K layout above gives the transposed read 4-way conflicts).  d = 128: a
+// row fills the 64-bank window and swb swaps the two 2-bit fields of r mod 16;
+// d = 64: two rows share a window (halves by r & 1), and swb takes the row
+// pair index k = r / 2 to (k & 1) * 4 + (k / 2) % 4.
+template <int D>
+__device__ __forceinline__ int swb(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
 
 struct AttnBwdArgs {
   const char* Q;
@@ -715,11 +730,11 @@ struct AttnBwdArgs {
   int hsplit;         // workgroups sharing a key block's query heads (1 or 2)
 };
 
-// Transposing-read offsets for a 16-row step of swk rows: lane (g = lane / 16,
+// Transposing-read offsets for a 16-row step of swb rows: lane (g = lane / 16,
 // t = lane % 16) reads 8 bytes of rows k_l and k_l + 4 of the step, k_l =
 // 8 (g / 2) + t / 4, logical piece 4 db + 2 (g % 2) + (t % 4) / 2, half t % 2
-// (the forward's V read, with the K layout's swizzle, which within a step of
-// 16 rows does not depend on the step).
+// (the forward's V read, with the swb swizzle, which within a step of 16 rows
+// does not depend on the step).
 template <int D>
 __device__ __forceinline__ void tr_offsets(int lane, int (&lo)[D / 32], int (&hi)[D / 32]) {
   constexpr int ROWB = D * 2;
@@ -728,12 +743,12 @@ __device__ __forceinline__ void tr_offsets(int lane, int (&lo)[D / 32], int (&hi
   const int r2 = 2 * (g & 1) + ((t & 3) >> 1);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
-    lo[db] = k_l * ROWB + (((4 * db + r2) ^ swk<D>(k_l)) << 4) + 8 * (t & 1);
-    hi[db] = (k_l + 4) * ROWB + (((4 * db + r2) ^ swk<D>(k_l + 4)) << 4) + 8 * (t & 1);
+    lo[db] = k_l * ROWB + (((4 * db + r2) ^ swb<D>(k_l)) << 4) + 8 * (t & 1);
+    hi[db] = (k_l + 4) * ROWB + (((4 * db + r2) ^ swb<D>(k_l + 4)) << 4) + 8 * (t & 1);
   }
 }
 
-// A operand (32 features x 16 rows) of feature block db, row step st, from swk rows
+// A operand (32 features x 16 rows) of feature block db, row step st, from swb rows
 template <int D>
 __device__ __forceinline__ bf16x8 read_tr(const char* base, int st, int lo, int hi) {
   const char* p = base + st * 16 * (D * 2);
@@ -742,10 +757,10 @@ __device__ __forceinline__ bf16x8 read_tr(const char* base, int st, int lo, int 
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// A operand (32 rows x 16 features) from swk rows: row r, logical piece pc
+// A operand (32 rows x 16 features) from swb rows: row r, logical piece pc
 template <int D>
 __device__ __forceinline__ bf16x8 read_row(const char* base, int r, int pc) {
-  return *reinterpret_cast<const bf16x8*>(base + r * (D * 2) + ((pc ^ swk<D>(r)) << 4));
+  return *reinterpret_cast<const bf16x8*>(base + r * (D * 2) + ((pc ^ swb<D>(r)) << 4));
 }
 
 // rows 16 ks .. 16 ks + 15 of a 64-row tile of fp32 results (two 32x32 MFMA
@@ -837,7 +852,7 @@ __device__ __forceinline__ void full_scores(f32x16 (&dp)[2], const char* base, c
                                                        0, 0, 0);
 }
 
-// acc[db] += (feature block db of the 64 swk rows at `base`, transposed) x
+// acc[db] += (feature block db of the 64 swb rows at `base`, transposed) x
 // (x's rows as the contraction); with MASK only the blocks and lanes of F
 template <int D, bool MASK>
 __device__ __forceinline__ void accumulate_tr(f32x16 (&acc)[D / 32], const char* base, const f32x16 (&x)[2],
@@ -880,7 +895,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bwd_dq_kernel(AttnBwdArg
   constexpr int BLK = kAttnK * ROWB;
   constexpr int LOADS = BLK / (4 * 1024);
   static_assert(BLK % 4096 == 0, "whole 1 KB copies per wave");
-  // two stages of [K block | V block], both in the swk layout
+  // two stages of [K block | V block], both in the swb layout
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * BLK];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -943,7 +958,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bwd_dq_kernel(AttnBwdArg
   for (int x = 0; x < LOADS; ++x) {
     const int sl = (wid * LOADS + x) * 64 + lane;
     k_row[x] = sl / NP;
-    k_pc[x] = uint32_t((sl % NP) ^ swk<D>(k_row[x])) * 16u;
+    k_pc[x] = uint32_t((sl % NP) ^ swb<D>(k_row[x])) * 16u;
   }
 
   // key blocks, type by type (the forward's walk)
@@ -1096,7 +1111,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkdv_kernel(AttnBwdA
   for (int x = 0; x < LOADS; ++x) {
     const int sl = (wid * LOADS + x) * 64 + lane;
     r_row[x] = sl / NP;
-    r_pc[x] = uint32_t((sl % NP) ^ swk<D>(r_row[x])) * 16u;
+    r_pc[x] = uint32_t((sl % NP) ^ swb<D>(r_row[x])) * 16u;
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(smem)));
 
