@@ -239,9 +239,11 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
 }
 
 // Shared driver of the graph-law entry points (bf16, q <= 64, one 64-bit
-// out-edge mask per type).  The forward takes the persistent kernel where its
-// shapes allow (absent-edge blocks zeroed by a pass first); every other case
-// runs the register-staged kernels, whose tiles of absent edges store zeros.
+// out-edge mask per type).  Where their shapes allow, the forward takes the
+// persistent kernel (absent-edge blocks zeroed by a pass first) and dX and dW
+// the persistent gradient kernels (tiles of absent edges have no k-steps and
+// store zeros); every other case runs the register-staged kernels, whose
+// tiles of absent edges store zeros.
 qalg_status run_graph(Op op, const void* A, const void* B, const int32_t* tau, int32_t q, const uint64_t* adj,
                       int64_t M, int64_t K, int64_t N, void* C, int32_t dtype, void* ws, size_t ws_bytes,
                       uint32_t flags, void* stream) {
@@ -299,6 +301,7 @@ qalg_status run_graph(Op op, const void* A, const void* B, const int32_t* tau, i
   else
     e = hipSuccess;
   if (e != hipSuccess) return QALG_ERR_HIP;
+  if (qalg::grad_persistent_supported(p)) return hip_status(qalg::launch_grad_persistent_bf16(p, s));
   return hip_status(qalg::launch_tiled_bf16(p, s));
 }
 

@@ -146,6 +146,7 @@ struct GradArgs {
   float* part;     // dW: fp32 partial tiles [piece][K][N] of split tiles
   int64_t part_stride;  // floats per piece (K * N)
   uint32_t a_bytes, b_bytes;  // dW: bytes of X and dY (buffer ranges)
+  const uint64_t* adj;  // graph law Q_G: per-type out-edge masks (bit j of type i: edge (i, j)); else null
 };
 
 // One unit of work: an output tile, or a piece of a split dW tile.
@@ -162,6 +163,7 @@ struct GTile {
   int seg_from, seg_mask;  // segments: the n-th is law_member(seg_from, seg_mask, n, L)
   int nseg;        // dX: 0 for one contiguous range from col0; dW: segments (0: all typed rows)
   int col0;        // dX: first contraction column of a contiguous range
+  uint64_t gmask;  // graph law: the segments' groups (dX) or row types (dW) as a bit set
 };
 
 // The u-th unit of a workgroup (slot g of the G on XCD xcd of nx), in closed
@@ -247,7 +249,14 @@ struct DealC {
   }
 };
 
-template <class C, Op OP, bool LISTED, bool TENSOR>
+// GRAPH: the graph law Q_G (section 3.1, eq 9-12) with the complete law's
+// tiles: a type-i row's dx_i sums over the output groups j of {i} and i's
+// out-neighbours (segments of the long tile), its dx_k (k != i) exists only
+// for an edge (i, k); dW_jj sums over the rows of j and of j's in-neighbours
+// (segments of the diagonal tile), dW_bj (b != j) exists only for an edge
+// (b, j).  Tiles of absent edges have no k-steps: the compute cursor writes
+// their zeros.
+template <class C, Op OP, bool LISTED, bool TENSOR, bool GRAPH>
 __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
   const int32_t* ws = a.ws;
   const int32_t* rows = ws + a.off_rows;
@@ -270,6 +279,23 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
   auto type_start = [&](int i) { return i >= cyc ? i - cyc : i - cyc + q; };
   const int typed = LISTED ? uni(s_off[q]) : a.M;  // rows with a type in range
 
+  // graph law: out-edge mask of type t (two scalar loads)
+  auto adj_of = [&](int t) -> uint64_t {
+    const cint_ptr e = to_const(reinterpret_cast<const int32_t*>(a.adj));
+    return uint64_t(uint32_t(uni(e[2 * t]))) | (uint64_t(uint32_t(uni(e[2 * t + 1]))) << 32);
+  };
+  // the n-th segment's group (dX) or row type (dW) of unit t
+  auto member = [&](const GTile& t, int n) -> int {
+    if constexpr (GRAPH) {
+      uint64_t m = t.gmask;
+      for (int k = 0; k < n; ++k) m &= m - 1;
+      return uni(int(__builtin_ctzll(m)));
+    } else if constexpr (TENSOR) {
+      return law_member(t.seg_from, t.seg_mask, n, a.L);
+    } else {
+      return t.seg_from;
+    }
+  };
   // rows of dW segment n of unit t: count, start (cyclic) or list slot, and
   // how rows are found (0: rows 0.. in order; 1: start + m q; 2: row list)
   auto seg_rows = [&](const GTile& t, int n, int& cnt, int& base, int& mode) {
@@ -279,7 +305,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
       mode = typed == a.M ? 0 : 2;
       return;
     }
-    const int ty = TENSOR ? law_member(t.seg_from, t.seg_mask, n, a.L) : t.seg_from;
+    const int ty = member(t, n);
     cnt = ix.count(ty);
     base = LISTED ? ix.offset(ty) : type_start(ty);
     mode = LISTED ? 2 : 1;
@@ -317,6 +343,26 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
         t.nseg = cls > 0 ? 1 << (a.L - cls) : 0;
         t.col0 = 0;
         t.nk = (1 << (a.L - cls)) * kts;
+      } else if constexpr (GRAPH) {
+        // bits at or past q are not types (ignored, as the forward ignores them)
+        const uint64_t valid = q >= 64 ? ~uint64_t(0) : (uint64_t(1) << q) - 1;
+        const uint64_t out = adj_of(i) & valid & ~(uint64_t(1) << i);
+        k = cls ? i : (jj < i ? jj : jj + 1);
+        t.seg_from = i;
+        t.seg_mask = 0;
+        if (cls) {
+          // dx_i: output groups i and the out-neighbours of i
+          t.gmask = out | (uint64_t(1) << i);
+          t.nseg = uni(__builtin_popcountll(t.gmask));
+          t.col0 = 0;
+          t.nk = t.nseg * kts;
+        } else {
+          // dx_k = dy_k W_kk^T only for an edge (i, k)
+          t.gmask = 0;
+          t.nseg = 0;
+          t.col0 = k * a.r;
+          t.nk = ((out >> k) & 1) ? kts : 0;
+        }
       } else {
         k = cls ? i : (jj < i ? jj : jj + 1);
         t.seg_from = t.seg_mask = 0;
@@ -345,6 +391,14 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
         t.seg_from = b;
         t.seg_mask = 0;
         t.nseg = 0;
+        if constexpr (GRAPH) {
+          // dW_jj: the rows of j and of every type with an edge into j
+          uint64_t m = uint64_t(1) << j;
+          for (int ty = 0; ty < q; ++ty)
+            if ((adj_of(ty) >> j) & 1) m |= uint64_t(1) << ty;
+          t.gmask = m;
+          t.nseg = uni(__builtin_popcountll(m));
+        }
       } else {
         b = blk / (q - 1);
         const int jj = blk - b * (q - 1);
@@ -352,6 +406,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
         t.seg_from = b;
         t.seg_mask = 0;
         t.nseg = 1;
+        if constexpr (GRAPH) t.gmask = uint64_t(1) << b;
       }
       const int rt = w % a.rpb, ct = w / a.rpb;
       t.out_row0 = b * a.s + rt * C::BM;
@@ -367,6 +422,10 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
         int cnt, base, mode;
         seg_rows(t, n, cnt, base, mode);
         nk_all += (cnt + C::BK - 1) / C::BK;
+      }
+      if constexpr (GRAPH) {
+        // dW_bj (b != j) only for an edge (b, j)
+        if (b != j && !((adj_of(b) >> j) & 1)) nk_all = 0;
       }
       const int per = (nk_all + npc - 1) / npc;
       t.c0 = uni(piece * per);
@@ -484,7 +543,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
   // kernel) plus a wave-uniform part per k-step
   constexpr bool CYC_DW = OP == Op::Dw && !LISTED;
   // the complete law on a cyclic schedule: one segment per unit, no walk
-  constexpr bool SIMPLE = CYC_DW && !TENSOR;
+  constexpr bool SIMPLE = CYC_DW && !TENSOR && !GRAPH;
   uint32_t p1[CYC_DW ? C::DMA : 1], pq[CYC_DW ? C::DMA : 1];
   if constexpr (CYC_DW) {
 #pragma unroll
@@ -524,7 +583,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
     if constexpr (OP == Op::Dx) {
       cx_n = 0;
       cx_kk = 0;
-      cx_col = lt.nseg ? law_member(lt.seg_from, lt.seg_mask, 0, a.L) * a.r : lt.col0;
+      cx_col = lt.nseg ? member(lt, 0) * a.r : lt.col0;
     } else if constexpr (!SIMPLE) {
       w_k0 = 0;
       seg_enter(0);
@@ -638,7 +697,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
           if (cx_kk == a.r / C::BK) {
             cx_kk = 0;
             cx_n = uni(cx_n + 1);
-            cx_col = law_member(lt.seg_from, lt.seg_mask, cx_n, a.L) * a.r;
+            cx_col = member(lt, cx_n) * a.r;
           } else {
             cx_col = uni(cx_col + C::BK);
           }
@@ -923,16 +982,16 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
   wait_vmcnt<0>();
 }
 
-template <class C, Op OP, bool TENSOR>
+template <class C, Op OP, bool TENSOR, bool GRAPH>
 __global__ __launch_bounds__(C::THREADS, 1) void grad_persistent_kernel(GradArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int32_t* ws = a.ws;
   if (ws[1] != kIndexMagic || ws[2] != a.q || ws[3] != a.M) return;
   // two bodies: the cyclic one never reads the row list
   if (ws[4] >= 0)
-    grad_body<C, OP, false, TENSOR>(a, smem);
+    grad_body<C, OP, false, TENSOR, GRAPH>(a, smem);
   else
-    grad_body<C, OP, true, TENSOR>(a, smem);
+    grad_body<C, OP, true, TENSOR, GRAPH>(a, smem);
 }
 
 // dW of split tiles: dW = bf16(sum over pieces of the fp32 partial tiles),
@@ -1013,12 +1072,12 @@ int tensor_levels_of(int q) {
   return L;
 }
 
-template <class C, Op OP, bool TENSOR>
+template <class C, Op OP, bool TENSOR, bool GRAPH>
 hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
   static bool attr_set = false;
   const int lds = C::LDS_BYTES;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grad_persistent_kernel<C, OP, TENSOR>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grad_persistent_kernel<C, OP, TENSOR, GRAPH>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -1039,6 +1098,7 @@ hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
   a.s = int(p.K / p.q);
   a.r = int(p.N / p.q);
   a.L = TENSOR ? tensor_levels_of(p.q) : 0;
+  a.adj = GRAPH ? p.graph_adj : nullptr;
   a.a_bytes = uint32_t(p.M * p.K * 2);
   a.b_bytes = uint32_t(p.M * p.N * 2);
   if (OP == Op::Dx) {
@@ -1095,7 +1155,7 @@ hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
     }
   }
   const size_t shm = C::LDS_BYTES;
-  hipLaunchKernelGGL((grad_persistent_kernel<C, OP, TENSOR>), dim3(grid), dim3(C::THREADS), shm, s, a);
+  hipLaunchKernelGGL((grad_persistent_kernel<C, OP, TENSOR, GRAPH>), dim3(grid), dim3(C::THREADS), shm, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || OP != Op::Dw) return e;
   // reduce the split classes
@@ -1126,23 +1186,23 @@ hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
 int pick_bn(int64_t w) { return w % 256 == 0 ? 256 : w % 192 == 0 ? 192 : w % 128 == 0 ? 128 : 0; }
 int pick_bm_dw(int64_t w) { return w % 256 == 0 ? 256 : w % 192 == 0 ? 192 : 0; }
 
-template <Op OP, bool TENSOR>
+template <Op OP, bool TENSOR, bool GRAPH>
 hipError_t launch_op(const ProblemDesc& p, hipStream_t s) {
   if (OP == Op::Dx) {
     const int bn = pick_bn(p.K / p.q);
-    if (bn == 256) return launch_grad<DxCfg<256>, Op::Dx, TENSOR>(p, s);
-    if (bn == 192) return launch_grad<DxCfg<192>, Op::Dx, TENSOR>(p, s);
-    return launch_grad<DxCfg<128>, Op::Dx, TENSOR>(p, s);
+    if (bn == 256) return launch_grad<DxCfg<256>, Op::Dx, TENSOR, GRAPH>(p, s);
+    if (bn == 192) return launch_grad<DxCfg<192>, Op::Dx, TENSOR, GRAPH>(p, s);
+    return launch_grad<DxCfg<128>, Op::Dx, TENSOR, GRAPH>(p, s);
   }
   const int bm = pick_bm_dw(p.K / p.q), bn = pick_bn(p.N / p.q);
   if (bm == 256) {
-    if (bn == 256) return launch_grad<DwCfg<256, 256>, Op::Dw, TENSOR>(p, s);
-    if (bn == 192) return launch_grad<DwCfg<256, 192>, Op::Dw, TENSOR>(p, s);
-    return launch_grad<DwCfg<256, 128>, Op::Dw, TENSOR>(p, s);
+    if (bn == 256) return launch_grad<DwCfg<256, 256>, Op::Dw, TENSOR, GRAPH>(p, s);
+    if (bn == 192) return launch_grad<DwCfg<256, 192>, Op::Dw, TENSOR, GRAPH>(p, s);
+    return launch_grad<DwCfg<256, 128>, Op::Dw, TENSOR, GRAPH>(p, s);
   }
-  if (bn == 256) return launch_grad<DwCfg<192, 256>, Op::Dw, TENSOR>(p, s);
-  if (bn == 192) return launch_grad<DwCfg<192, 192>, Op::Dw, TENSOR>(p, s);
-  return launch_grad<DwCfg<192, 128>, Op::Dw, TENSOR>(p, s);
+  if (bn == 256) return launch_grad<DwCfg<192, 256>, Op::Dw, TENSOR, GRAPH>(p, s);
+  if (bn == 192) return launch_grad<DwCfg<192, 192>, Op::Dw, TENSOR, GRAPH>(p, s);
+  return launch_grad<DwCfg<192, 128>, Op::Dw, TENSOR, GRAPH>(p, s);
 }
 
 }  // namespace
@@ -1150,6 +1210,7 @@ hipError_t launch_op(const ProblemDesc& p, hipStream_t s) {
 bool grad_persistent_supported(const ProblemDesc& p) {
   if (p.E != 1 || (p.op != Op::Dx && p.op != Op::Dw)) return false;
   if (p.law_L > 6) return false;
+  if (p.graph_adj != nullptr && (p.law_L > 0 || p.q > 64)) return false;  // one 64-bit mask per type
   const int64_t s = p.K / p.q, r = p.N / p.q;
   // 32-bit offsets; dW's buffer ranges stay below 2 GiB
   const int64_t lim = int64_t(1) << 30;
@@ -1165,8 +1226,10 @@ bool grad_persistent_supported(const ProblemDesc& p) {
 }
 
 hipError_t launch_grad_persistent_bf16(const ProblemDesc& p, hipStream_t s) {
-  if (p.op == Op::Dx) return p.law_L > 0 ? launch_op<Op::Dx, true>(p, s) : launch_op<Op::Dx, false>(p, s);
-  return p.law_L > 0 ? launch_op<Op::Dw, true>(p, s) : launch_op<Op::Dw, false>(p, s);
+  if (p.graph_adj != nullptr)
+    return p.op == Op::Dx ? launch_op<Op::Dx, false, true>(p, s) : launch_op<Op::Dw, false, true>(p, s);
+  if (p.op == Op::Dx) return p.law_L > 0 ? launch_op<Op::Dx, true, false>(p, s) : launch_op<Op::Dx, false, false>(p, s);
+  return p.law_L > 0 ? launch_op<Op::Dw, true, false>(p, s) : launch_op<Op::Dw, false, false>(p, s);
 }
 
 }  // namespace qalg

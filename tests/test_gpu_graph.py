@@ -105,6 +105,12 @@ GRAD_CASES = [
     (777, 256, 512, 2, "random", 0, "empty", False),
     (1111, 384, 2496, 3, "random", 5, "random", False),
     (1536, 512, 2048, 4, "cyclic", 0, "complete", True),
+    # persistent dW as well (input groups of 192 or 256 features)
+    (4096, 1024, 2048, 4, "cyclic", 0, "random", True),
+    (3000, 1536, 1536, 3, "random", 5, "random", False),   # listed types, unsplit dW
+    (2048, 768, 1536, 4, "cyclic", 0, "cycle", True),      # 192-feature dW tiles
+    (4096, 2048, 2048, 8, "cyclic", 0, "star", True),      # one type reaches every group
+    (1536, 1024, 1024, 4, "cyclic", 0, "empty", False),    # no edges: every off-diagonal tile is zero
 ]
 
 
