@@ -215,6 +215,17 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
     return hip_status(qalg::launch_tiled_masked_bf16(p, s));
   }
 
+  if (dtype == QALG_BF16 && qalg::grad_persistent_supported(p)) {
+    // the persistent gradients read the index on the device (closed-form rows
+    // for a cyclic schedule, the row list otherwise); dX zeroes the rows of an
+    // out-of-range type itself, dW ignores them
+    if (!(flags & QALG_FLAG_INDEX_READY)) {
+      e = qalg::launch_build_index(tau, q, M, E, wsi, stride, s);
+      if (e != hipSuccess) return QALG_ERR_HIP;
+    }
+    return hip_status(qalg::launch_grad_persistent_bf16(p, s));
+  }
+
   // rows of an out-of-range type get zero Y / dX rows; dW ignores them
   void* zero_out = op == Op::Dw ? nullptr : C;
   const int64_t zero_ld = op == Op::Fwd ? N : K;
@@ -229,11 +240,6 @@ qalg_status run_projection(Op op, int32_t E, const void* A, const void* B, const
   }
   if (e != hipSuccess) return QALG_ERR_HIP;
 
-  if (dtype == QALG_BF16 && qalg::grad_persistent_supported(p)) {
-    // the persistent gradients read the index on the device: closed-form rows
-    // for a cyclic schedule, the row list otherwise
-    return hip_status(qalg::launch_grad_persistent_bf16(p, s));
-  }
   e = dtype == QALG_BF16 ? qalg::launch_tiled_bf16(p, s) : qalg::launch_tiled_f32(p, s);
   return hip_status(e);
 }
@@ -290,10 +296,15 @@ qalg_status run_graph(Op op, const void* A, const void* B, const int32_t* tau, i
     if (qalg::launch_graph_zero_bf16(tau, adj, q, M, N, C, s) != hipSuccess) return QALG_ERR_HIP;
     return hip_status(qalg::launch_fwd_persistent_bf16(p, s));
   }
+  hipError_t e;
+  if (qalg::grad_persistent_supported(p)) {
+    // dX zeroes the rows of an out-of-range type itself
+    if (!ready && qalg::launch_build_index(tau, q, M, 1, wsi, p.ws_stride, s) != hipSuccess) return QALG_ERR_HIP;
+    return hip_status(qalg::launch_grad_persistent_bf16(p, s));
+  }
   // rows of an out-of-range type get zero Y / dX rows; dW ignores them
   void* zero_out = op == Op::Dw ? nullptr : C;
   const int64_t zero_ld = op == Op::Fwd ? N : K;
-  hipError_t e;
   if (!ready)
     e = qalg::launch_build_index_zeroing(tau, q, M, 1, wsi, p.ws_stride, zero_out, zero_ld, 2, M * zero_ld * 2, s);
   else if (zero_out != nullptr)
@@ -301,7 +312,6 @@ qalg_status run_graph(Op op, const void* A, const void* B, const int32_t* tau, i
   else
     e = hipSuccess;
   if (e != hipSuccess) return QALG_ERR_HIP;
-  if (qalg::grad_persistent_supported(p)) return hip_status(qalg::launch_grad_persistent_bf16(p, s));
   return hip_status(qalg::launch_tiled_bf16(p, s));
 }
 

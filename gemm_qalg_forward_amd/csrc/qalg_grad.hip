@@ -439,6 +439,17 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
   const int nx = gridDim.x >= 8 ? 8 : 1;
   const int per_x = gridDim.x / nx;
   const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx;
+  // dX rows of an out-of-range type (listed after the typed rows by the
+  // index; a cyclic schedule has none) are zero: written here, by every
+  // workgroup in turn, instead of by a launch of their own
+  if constexpr (OP == Op::Dx && LISTED) {
+    const int nbad = a.M - typed;
+    const int row_u4 = a.K / 8;  // 16-byte pieces per dX row
+    for (int b = blockIdx.x; b < nbad; b += gridDim.x) {
+      u32x4* xr = reinterpret_cast<u32x4*>(a.C + int64_t(rows[typed + b]) * a.K * 2);
+      for (int x = tid; x < row_u4; x += C::THREADS) xr[x] = (u32x4){0u, 0u, 0u, 0u};
+    }
+  }
   if (slot >= per_x) return;
   std::conditional_t<TENSOR, DealC, Deal2> deal;
   if constexpr (TENSOR)
