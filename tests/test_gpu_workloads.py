@@ -8,7 +8,7 @@ the relative Frobenius error per output group: 5e-3 for bf16, 1e-5 for fp32.
 Workloads:
   * Q_2 row-typed forward in fp32, M=64, K=N=256 (whole output, dX and dW too)
   * ~110M-LM FFN shapes, bf16, q=4: 768->3072 and 3072->768, M=8192
-  * dense FFN (4096, 12288), bf16, q=8, M=16384: up and down projections
+  * dense FFN (4096, 12288), bf16, q=8, M=16384: up and down projections (whole output)
   * narrow expert shapes, bf16, 64 experts: (7168,2048) q=4, (2048,768) q=4 and q=8
   * training gradients at (4096, 12288), q=8, M=16384: forward, dX and dW
   * the graph law Q_G and unequal group widths at (4096, 12288), M=16384: forward, dX, dW
@@ -87,8 +87,9 @@ def test_lm_ffn_q4_whole_output(K, N):
 
 
 @pytest.mark.parametrize("proj", ["up", "down"])
-def test_dense_ffn_q8_sampled(proj):
-    """The benchmark's workload: same seeds, same calls (schedule, index, forward with the index ready)."""
+def test_dense_ffn_q8_whole_output(proj):
+    """The benchmark's workload: same seeds, same calls (schedule, index, forward with the index
+    ready); every output element against the oracle (per group and per element)."""
     torch = torch_cuda()
     c, M, D, F, q = 3, 16384, 4096, 12288, 8
     K, N = (D, F) if proj == "up" else (F, D)
@@ -105,9 +106,12 @@ def test_dense_ffn_q8_sampled(proj):
     torch.cuda.synchronize()
     tau = td.cpu().numpy()
     np.testing.assert_array_equal(tau, np.arange(M) % q)
-    rows = _sample_rows(M, q, 768, 31 + off)
-    e = _sampled_forward_check(X, W, tau, q, Y, rows, f"Y {proj}")
-    say(f"    max rel err over {rows.size} sampled rows {e:.2e}")
+    Yr = O.row_typed_forward(X.f64, W.f64, tau, q)
+    got = to_f64(Y)
+    e = assert_groups(rel_frob_col_groups(got, Yr, q), BF16_TOL, f"Y {proj}")
+    r = forward_elementwise(got, Yr, X.f64, W.f64, tau, q, "bf16", f"Y {proj}")
+    say(f"    max rel err over all {M} rows {e:.2e}; per-element error / bound {r:.2f}")
+    del Yr, got
     # a second launch on the same inputs is bitwise identical
     Y2 = Q.qalg_forward(Xd, Wd, td, q, ws=ws, flags=Q.QALG_FLAG_INDEX_READY)
     torch.cuda.synchronize()
