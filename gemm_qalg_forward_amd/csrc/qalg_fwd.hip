@@ -58,7 +58,11 @@
 //    columns each receive one column x 4 rows.
 // The MFMA is v_mfma_f32_32x32x16_bf16 with the weight fragment as the first
 // operand, so each lane ends with four consecutive output columns of one row;
-// the wave tile is 128x128 (4x4 MFMA tiles, accumulators in AGPRs).
+// the 256x256 tile runs on 8 waves, two per SIMD, each a 128x64 wave tile
+// (4x2 MFMA tiles): the second wave's MFMAs issue while the first one reads
+// fragments or copies (measured 1-4 % faster than 4 waves of 128x128 tiles,
+// which held all 256 accumulator registers per lane); the other tile shapes
+// and the gated epilogue keep 4 waves.
 //
 // Rows.  For a cyclic schedule (tau[m] = (o + m) mod q for all m, detected by
 // the index) the rows of type i are the arithmetic progression
@@ -86,18 +90,20 @@ constexpr int kQ = kBK / 16;  // MFMA quarter steps per k-step
 // GATED: the gate/up half of a gated FFN over a merged weight bank (see the
 // gated entry point below): each wave's 128 accumulator columns are 64 gate
 // and the matching 64 up columns, and the epilogue writes silu(gate) * up.
-// WGM x WGN waves per workgroup; the low tile heights (for few rows per type)
-// use 1 x 4 or 2 x 2 so that every wave still has at least 2 x 2 MFMA blocks.
+// WGM x WGN waves per workgroup (4 or 8); the low tile heights (for few rows
+// per type) use 1 x 4 or 2 x 2 so that every wave still has at least 2 x 2
+// MFMA blocks.
 // KEEP_ (gated only): also store the merged pre-activations GU in bf16 and
 // compute H from those rounded values (the training step keeps GU for the VJP).
 template <int BM_, int BN_, bool GATED_ = false, int WGM_ = 2, int WGN_ = 2, bool KEEP_ = false>
 struct FwdCfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
-  static_assert(WGM * WGN == 4, "four waves");
+  static constexpr int NW = WGM * WGN;
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
   static constexpr bool GATED = GATED_;
   static constexpr bool KEEP = KEEP_;
   static_assert(!KEEP || GATED, "pre-activations are kept by the gated forward only");
-  static constexpr int THREADS = 256;
+  static constexpr int THREADS = 64 * NW;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0 && FM >= 1 && FN >= 1, "wave tile");
@@ -109,9 +115,9 @@ struct FwdCfg {
   static constexpr int NCH = BN / 8;                // 16-byte pieces per W row
   static constexpr int B_BYTES = kBK * ROWB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole 1 KB copies per wave");
-  static constexpr int A_DMA = A_BYTES / 4096;      // 1 KB direct-to-LDS copies per wave and k-step
-  static constexpr int B_DMA = B_BYTES / 4096;
+  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole 1 KB copies per wave");
+  static constexpr int A_DMA = A_BYTES / (1024 * NW);  // 1 KB direct-to-LDS copies per wave and k-step
+  static constexpr int B_DMA = B_BYTES / (1024 * NW);
   static constexpr int DMA = A_DMA + B_DMA;
   static_assert(kStages * DMA < 64, "vmcnt range");
   // epilogue: each wave restages 32 rows x WTN columns of bf16 at a time in
@@ -125,7 +131,7 @@ struct FwdCfg {
   static constexpr int E_MASK = E_NP == 12 ? 3 : E_NP - 1;  // piece swizzle: p ^ (row & E_MASK)
   static_assert(E_NP % 2 == 0 && (E_NP == 12 || (E_NP & E_MASK) == 0), "epilogue buffer");
   static constexpr int E_OFF = kStages * STAGE;
-  static constexpr int LDS_BYTES = E_OFF + 4 * E_BYTES;
+  static constexpr int LDS_BYTES = E_OFF + NW * E_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -768,7 +774,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void fwd_persistent_kernel(FwdArgs a
     fwd_body<C, false, TENSOR>(a, smem);
 }
 
-using Fwd256x256 = FwdCfg<256, 256>;
+using Fwd256x256 = FwdCfg<256, 256, false, 2, 4>;
 using Fwd256x256Gated = FwdCfg<256, 256, true>;
 using Fwd256x256GatedKeep = FwdCfg<256, 256, true, 2, 2, true>;
 using Fwd256x192 = FwdCfg<256, 192>;

@@ -10,7 +10,7 @@ Workloads:
   * ~110M-LM FFN shapes, bf16, q=4: 768->3072 and 3072->768, M=8192
   * dense FFN (4096, 12288), bf16, q=8, M=16384: up and down projections (whole output)
   * narrow expert shapes, bf16, 64 experts: (7168,2048) q=4, (2048,768) q=4 and q=8
-  * training gradients at (4096, 12288), q=8, M=16384: forward, dX and dW
+  * training gradients at (4096, 12288), q=8, M=16384: forward, dX and dW (whole outputs)
   * the graph law Q_G and unequal group widths at (4096, 12288), M=16384: forward, dX, dW
 """
 import numpy as np
@@ -176,21 +176,21 @@ def test_training_grads_q8():
     ws0 = Q.workspace(q, M)
     dW0 = Q.qalg_backward_dw(Xd, dYd, td, q, ws=ws0)
     torch.cuda.synchronize()
-    rows = _sample_rows(M, q, 512, 5)
-    _sampled_forward_check(X, W, tau, q, Y, rows, "Y")
-    # dX rows depend on their own dY rows only
-    dXr_s, _ = O.row_typed_backward(X.f64[rows], W.f64, dY.f64[rows], tau[rows], q)
-    assert_groups(rel_frob_col_groups(to_f64(dX[rows]), dXr_s, q), BF16_TOL, "dX")
-    backward_elementwise(to_f64(dX[rows]), dXr_s, None, None, X.f64[rows], W.f64, dY.f64[rows], tau[rows], q, "bf16")
-    # dW is a sum over all rows: the whole oracle gradient (fp64 block GEMMs)
-    _, dWr = O.row_typed_backward(X.f64, W.f64, dY.f64, tau, q)
+    # every element of Y, dX and dW against the oracle (fp64 block GEMMs)
+    Yr = O.row_typed_forward(X.f64, W.f64, tau, q)
+    ey = assert_groups(rel_frob_col_groups(to_f64(Y), Yr, q), BF16_TOL, "Y")
+    forward_elementwise(to_f64(Y), Yr, X.f64, W.f64, tau, q, "bf16", "Y")
+    del Yr
+    dXr, dWr = O.row_typed_backward(X.f64, W.f64, dY.f64, tau, q)
+    ex = assert_groups(rel_frob_col_groups(to_f64(dX), dXr, q), BF16_TOL, "dX")
     e = assert_groups(rel_frob_blocks(to_f64(dW), dWr, q), BF16_TOL, "dW")
     e0 = assert_groups(rel_frob_blocks(to_f64(dW0), dWr, q), BF16_TOL, "dW unsplit")
-    _, mdW = O.row_typed_backward(np.abs(X.f64), np.abs(W.f64), np.abs(dY.f64), tau, q)
+    mdX, mdW = O.row_typed_backward(np.abs(X.f64), np.abs(W.f64), np.abs(dY.f64), tau, q)
     from qalg_check import assert_elementwise
+    assert_elementwise(to_f64(dX), dXr, mdX, N, "bf16", "dX")
     assert_elementwise(to_f64(dW), dWr, mdW, M, "bf16", "dW")
     assert_elementwise(to_f64(dW0), dWr, mdW, M, "bf16", "dW unsplit")
-    say(f"    dW max rel err {e:.2e} (unsplit {e0:.2e})")
+    say(f"    max rel err over every element: Y {ey:.2e}, dX {ex:.2e}, dW {e:.2e} (unsplit {e0:.2e})")
 
 
 def test_gated_ffn_q8_sampled():
