@@ -61,8 +61,9 @@
 // the 256x256 tile runs on 8 waves, two per SIMD, each a 128x64 wave tile
 // (4x2 MFMA tiles): the second wave's MFMAs issue while the first one reads
 // fragments or copies (measured 1-4 % faster than 4 waves of 128x128 tiles,
-// which held all 256 accumulator registers per lane); the other tile shapes
-// and the gated epilogue keep 4 waves.
+// which held all 256 accumulator registers per lane); 128x256 tiles likewise
+// (8 waves of 64x64, 2-3 % on the 768 -> 3072 projection); the other tile
+// shapes and the gated epilogue keep 4 waves.
 //
 // Rows.  For a cyclic schedule (tau[m] = (o + m) mod q for all m, detected by
 // the index) the rows of type i are the arithmetic progression
@@ -780,7 +781,7 @@ using Fwd256x256GatedKeep = FwdCfg<256, 256, true, 2, 2, true>;
 using Fwd256x192 = FwdCfg<256, 192>;
 using Fwd256x128 = FwdCfg<256, 128>;
 // few rows per type: 128- and 64-row tiles (64 x 64 and 64 x 128 wave tiles)
-using Fwd128x256 = FwdCfg<128, 256>;
+using Fwd128x256 = FwdCfg<128, 256, false, 2, 4>;
 using Fwd128x128 = FwdCfg<128, 128>;
 using Fwd128x192 = FwdCfg<128, 192>;
 using Fwd64x256 = FwdCfg<64, 256, false, 1, 4>;
