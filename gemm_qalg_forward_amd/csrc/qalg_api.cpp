@@ -366,9 +366,15 @@ qalg_status run_widths(Op op, const void* A, const void* B, const int32_t* tau, 
   int32_t* wsi = static_cast<int32_t*>(ws);
   p.ws = wsi;
   p.ws_stride = ws_stride_ints(q, M);
+  hipError_t e;
+  if (op == Op::Fwd && qalg::fwd_widths_persistent_ok(p)) {
+    // the persistent forward zeroes the rows of an out-of-range type itself
+    if (!(flags & QALG_FLAG_INDEX_READY) && qalg::launch_build_index(tau, q, M, 1, wsi, p.ws_stride, s) != hipSuccess)
+      return QALG_ERR_HIP;
+    return hip_status(qalg::launch_fwd_widths_bf16(p, s));
+  }
   void* zero_out = op == Op::Dw ? nullptr : C;
   const int64_t zero_ld = op == Op::Fwd ? N : K;
-  hipError_t e;
   if (!(flags & QALG_FLAG_INDEX_READY))
     e = qalg::launch_build_index_zeroing(tau, q, M, 1, wsi, p.ws_stride, zero_out, zero_ld, 2, M * zero_ld * 2, s);
   else if (zero_out != nullptr)

@@ -151,6 +151,10 @@ struct FwdArgs {
   int L;       // 0: the complete-graph law Q_q; L >= 1: the recursive law Q_2^(x)L (q = 2^L)
   const uint64_t* adj;  // graph law Q_G (complete-law kernels): out-edges of each type; null for Q_q
   char* GU;             // gated forward with kept pre-activations: M x N merged GU (bf16); else null
+  // unequal group widths (eq 18), complete law: widths = 1; first K column of
+  // input group g, first N column and first column tile of output group g
+  int widths;
+  int gk[kMaxWidthGroups + 1], gn[kMaxWidthGroups + 1], tn[kMaxWidthGroups + 1];
 };
 
 // One output tile, decoded from its position in the tile order.
@@ -162,6 +166,7 @@ struct Tile {
   int n0;         // first output column
   int seg0, seg1; // K offsets of the contraction segments (group i, group j)
   int nk;         // k-steps
+  int kts0;       // k-steps of the first segment (group i)
   int fmask;      // recursive law: bits where i and j differ (free bits of the segments)
   int fbase;      // recursive law: i's bits elsewhere (segment n is fbase | pdep(n, fmask))
 };
@@ -236,6 +241,35 @@ struct TileDeal2 : TileDeal {
 template <class C, bool TENSOR, class IX>
 __device__ __forceinline__ Tile decode_tile(const FwdArgs& a, const IX& ix, int n_rt, int cls, int idx) {
   constexpr int G = 4;
+  if constexpr (!TENSOR) {
+    if (a.widths) {
+      // unequal widths: one class, groups of 4 row tiles x all n_ct column
+      // tiles (row tile fastest); the tile's output group j from the column
+      // tile starts, its contraction over groups i and j (i alone if j == i)
+      const int span = G * a.n_ct;
+      const int g = idx / span;
+      const int first_rt = g * G;
+      const int gm = min(n_rt - first_rt, G);
+      const int w = idx - g * span;
+      const int rt = first_rt + w % gm;
+      const int c2 = w / gm;
+      const int i = ix.group_of_tile(rt);
+      int j = 0;
+      while (j + 1 < a.q && c2 >= a.tn[j + 1]) j = uni(j + 1);
+      Tile t;
+      t.i = i;
+      t.rank0 = (rt - ix.tiles_before(i)) * C::BM;
+      t.first = ix.offset(i) + t.rank0;
+      t.m_cnt = min(C::BM, ix.count(i) - t.rank0);
+      t.n0 = a.gn[j] + (c2 - a.tn[j]) * C::BN;
+      t.seg0 = a.gk[i];
+      t.seg1 = a.gk[j];
+      t.kts0 = uni((a.gk[i + 1] - a.gk[i]) / kBK);
+      t.nk = uni(t.kts0 + (j == i ? 0 : (a.gk[j + 1] - a.gk[j]) / kBK));
+      t.fmask = t.fbase = 0;
+      return t;
+    }
+  }
   const bool is_long = cls != 0;
   const int ngrp = TENSOR ? binom_small(a.L, cls) : (is_long ? a.q - 1 : 1);
   const int ncol = ngrp * a.cpg;  // column tiles of the class per row tile
@@ -276,6 +310,7 @@ __device__ __forceinline__ Tile decode_tile(const FwdArgs& a, const IX& ix, int 
   } else {
     t.seg0 = i * a.s;
     t.seg1 = j * a.s;
+    t.kts0 = a.kts;
     t.nk = uni((j == i) ? a.kts : 2 * a.kts);
     if (a.adj != nullptr && j != i) {
       // graph law Q_G: without the edge (i, j) the output block has no term
@@ -339,6 +374,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
   Deal dcopy, dcomp;
   if constexpr (TENSOR)
     dcopy.init(a.L, n_rt, a.cpg, xcd, nx, slot, per_x);
+  else if (a.widths)
+    dcopy.init(n_rt * a.n_ct, 0, 2 * a.kts, a.kts, xcd, nx, slot, per_x);  // one class, all tiles
   else
     dcopy.init(n_long, n_short, 2 * a.kts, a.kts, xcd, nx, slot, per_x);
   dcomp = dcopy;
@@ -421,8 +458,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a, char* smem) {
     if constexpr (TENSOR) {
       kcol = lcol + lks * kBK;
     } else {
-      const int sg = lk >= a.kts ? 1 : 0;
-      kcol = (sg ? lt.seg1 : lt.seg0) + (lk - sg * a.kts) * kBK;
+      const int sg = lk >= lt.kts0 ? 1 : 0;
+      kcol = (sg ? lt.seg1 : lt.seg0) + (lk - sg * lt.kts0) * kBK;
     }
     cp_x = uint32_t(kcol) * 2u;
     cp_w = uint32_t(kcol) * n_bytes + uint32_t(lt.n0) * 2u;
@@ -836,6 +873,18 @@ hipError_t launch_fwd(const ProblemDesc& p, hipStream_t s) {
   a.GU = static_cast<char*>(p.gu);
   a.cpg = a.r / C::BN;
   a.n_ct = p.q * a.cpg;
+  if (p.in_widths != nullptr) {
+    // unequal widths: group starts and column-tile starts from the widths
+    a.widths = 1;
+    a.gk[0] = a.gn[0] = a.tn[0] = 0;
+    for (int g = 0; g < p.q; ++g) {
+      a.gk[g + 1] = a.gk[g] + int(p.in_widths[g]);
+      a.gn[g + 1] = a.gn[g] + int(p.out_widths[g]);
+      a.tn[g + 1] = a.tn[g] + int(p.out_widths[g] / C::BN);
+    }
+    a.n_ct = a.tn[p.q];
+    a.cpg = 0;
+  }
   const int64_t max_tiles = ((p.M + C::BM - 1) / C::BM + p.q - 1) * int64_t(a.n_ct);
   int grid = cu_count();
   if (max_tiles < grid) grid = max_tiles < 8 ? int(max_tiles) : int(max_tiles / 8 * 8);
@@ -859,6 +908,21 @@ bool fwd_persistent_shape_ok(const ProblemDesc& p) {
   if (s % kBK != 0) return false;
   return r % 256 == 0 || r % 192 == 0 || r % 128 == 0;
 }
+
+// Unequal group widths on the persistent forward (complete law): 256x256
+// tiles, so every output width a multiple of 256 and every input width of
+// 64 (whole k-steps), and at least 128 rows per type on average.
+bool fwd_widths_persistent_ok(const ProblemDesc& p) {
+  if (p.op != Op::Fwd || p.E != 1 || p.law_L != 0 || p.graph_adj != nullptr) return false;
+  if (p.in_widths == nullptr || p.out_widths == nullptr || p.q < 1 || p.q > kMaxWidthGroups) return false;
+  const int64_t lim = int64_t(1) << 31;
+  if (p.M * p.K >= lim || p.K * p.N >= lim || p.M * p.N >= lim) return false;
+  for (int g = 0; g < p.q; ++g)
+    if (p.in_widths[g] % kBK != 0 || p.out_widths[g] % 256 != 0) return false;
+  return (p.M + p.q - 1) / p.q >= 128;
+}
+
+hipError_t launch_fwd_widths_bf16(const ProblemDesc& p, hipStream_t s) { return launch_fwd<Fwd256x256>(p, s); }
 
 bool fwd_persistent_supported(const ProblemDesc& p) {
   // with only 256-row tiles available, below about 128 rows per type the

@@ -101,6 +101,9 @@ hipError_t launch_small_m_bf16(const ProblemDesc& p, hipStream_t s);
 bool small_m_supported(const ProblemDesc& p);
 // Persistent 256x256-tile forward (bf16, one problem); zeroes rows of out-of-range type itself.
 bool fwd_persistent_supported(const ProblemDesc& p);
+// unequal group widths on the persistent forward (256x256 tiles; see the shape rule there)
+bool fwd_widths_persistent_ok(const ProblemDesc& p);
+hipError_t launch_fwd_widths_bf16(const ProblemDesc& p, hipStream_t s);
 // the shapes the persistent forward can run at all (the only path of the recursive law)
 bool fwd_persistent_shape_ok(const ProblemDesc& p);
 // forced_bm: 0 picks the tile height from the rows per type; 256, 128 or 64 forces it
