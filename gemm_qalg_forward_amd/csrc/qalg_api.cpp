@@ -373,6 +373,12 @@ qalg_status run_widths(Op op, const void* A, const void* B, const int32_t* tau, 
       return QALG_ERR_HIP;
     return hip_status(qalg::launch_fwd_widths_bf16(p, s));
   }
+  if (qalg::grad_persistent_supported(p)) {
+    // dX zeroes the rows of an out-of-range type itself
+    if (!(flags & QALG_FLAG_INDEX_READY) && qalg::launch_build_index(tau, q, M, 1, wsi, p.ws_stride, s) != hipSuccess)
+      return QALG_ERR_HIP;
+    return hip_status(qalg::launch_grad_persistent_bf16(p, s));
+  }
   void* zero_out = op == Op::Dw ? nullptr : C;
   const int64_t zero_ld = op == Op::Fwd ? N : K;
   if (!(flags & QALG_FLAG_INDEX_READY))

@@ -150,6 +150,11 @@ struct GradArgs {
   int64_t part_stride;  // floats per piece (K * N)
   uint32_t a_bytes, b_bytes;  // dW: bytes of X and dY (buffer ranges)
   const uint64_t* adj;  // graph law Q_G: per-type out-edge masks (bit j of type i: edge (i, j)); else null
+  // unequal group widths (eq 18), dX of the complete law: widths = 1; first K
+  // column of input group g, first N column of output group g, first dX
+  // column tile of input group g; n_ct: dX column tiles in all
+  int widths, n_ct;
+  int gk[kMaxWidthGroups + 1], gn[kMaxWidthGroups + 1], tk[kMaxWidthGroups + 1];
 };
 
 // One unit of work: an output tile, or a piece of a split dW tile.
@@ -321,6 +326,34 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
     t.cls = cls;
     t.c0 = 0;
     t.piece = -1;
+    if constexpr (OP == Op::Dx && !TENSOR && !GRAPH) {
+      if (a.widths) {
+        // unequal widths: one class, groups of 4 row tiles x all dX column
+        // tiles (row tile fastest); column tile c2 lies in input group k; the
+        // contraction runs over all N output columns when k is the row type
+        // (eq 31-32's long sum), else over output group k alone
+        constexpr int G = 4;
+        const int span = G * a.n_ct;
+        const int grp = idx / span, w = idx - grp * span;
+        const int first_rt = grp * G;
+        const int gm = min(n_rt - first_rt, G);
+        const int rt = first_rt + w % gm, c2 = w / gm;
+        const int i = ix.group_of_tile(rt);
+        int k = 0;
+        while (k + 1 < q && c2 >= a.tk[k + 1]) k = uni(k + 1);
+        t.type = i;
+        t.out_row0 = (rt - ix.tiles_before(i)) * C::BM;
+        t.m_cnt = min(C::BM, ix.count(i) - t.out_row0);
+        t.first = ix.offset(i) + t.out_row0;
+        t.seg_from = t.seg_mask = 0;
+        t.gmask = 0;
+        t.nseg = 0;
+        t.col0 = k == i ? 0 : a.gn[k];
+        t.nk = uni(k == i ? a.N / C::BK : (a.gn[k + 1] - a.gn[k]) / C::BK);
+        t.n0 = a.gk[k] + (c2 - a.tk[k]) * C::BN;
+        return t;
+      }
+    }
     if constexpr (OP == Op::Dx) {
       constexpr int G = 4;
       const int ngrp = TENSOR ? binom_small(a.L, cls) : (cls ? 1 : q - 1);
@@ -457,8 +490,12 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
   std::conditional_t<TENSOR, DealC, Deal2> deal;
   if constexpr (TENSOR)
     deal.init(a, OP == Op::Dx ? n_rt * a.cpg : q * tpb, OP == Op::Dw, xcd, nx, slot, per_x);
-  else if constexpr (OP == Op::Dx)
-    deal.init(n_rt * a.cpg, n_rt * (q - 1) * a.cpg, a.N / C::BK, a.r / C::BK, xcd, nx, slot, per_x);
+  else if constexpr (OP == Op::Dx) {
+    if (a.widths)
+      deal.init(n_rt * a.n_ct, 0, a.N / C::BK, 1, xcd, nx, slot, per_x);  // one class, all tiles
+    else
+      deal.init(n_rt * a.cpg, n_rt * (q - 1) * a.cpg, a.N / C::BK, a.r / C::BK, xcd, nx, slot, per_x);
+  }
   else
     deal.init(q * tpb * a.np[1], q * (q - 1) * tpb * a.np[0], a.t_unit[1], a.t_unit[0], xcd, nx, slot, per_x);
   auto unit_at = [&](int u, int* cls, int* idx) -> bool {
@@ -1118,6 +1155,17 @@ hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
   if (OP == Op::Dx) {
     a.cpg = a.s / C::BN;
     a.rpb = 0;
+    if (p.in_widths != nullptr) {
+      a.widths = 1;
+      a.gk[0] = a.gn[0] = a.tk[0] = 0;
+      for (int g = 0; g < p.q; ++g) {
+        a.gk[g + 1] = a.gk[g] + int(p.in_widths[g]);
+        a.gn[g + 1] = a.gn[g] + int(p.out_widths[g]);
+        a.tk[g + 1] = a.tk[g] + int(p.in_widths[g] / C::BN);
+      }
+      a.n_ct = a.tk[p.q];
+      a.cpg = 0;
+    }
   } else {
     a.cpg = a.r / C::BN;
     a.rpb = a.s / C::BM;
@@ -1199,11 +1247,20 @@ hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
 
 int pick_bn(int64_t w) { return w % 256 == 0 ? 256 : w % 192 == 0 ? 192 : w % 128 == 0 ? 128 : 0; }
 int pick_bm_dw(int64_t w) { return w % 256 == 0 ? 256 : w % 192 == 0 ? 192 : 0; }
+// the widest dX column tile that divides every input group width
+int pick_bn_widths(const ProblemDesc& p) {
+  for (const int bn : {256, 192, 128}) {
+    bool ok = true;
+    for (int g = 0; g < p.q; ++g) ok = ok && p.in_widths[g] % bn == 0;
+    if (ok) return bn;
+  }
+  return 0;
+}
 
 template <Op OP, bool TENSOR, bool GRAPH>
 hipError_t launch_op(const ProblemDesc& p, hipStream_t s) {
   if (OP == Op::Dx) {
-    const int bn = pick_bn(p.K / p.q);
+    const int bn = p.in_widths != nullptr ? pick_bn_widths(p) : pick_bn(p.K / p.q);
     if (bn == 256) return launch_grad<DxCfg<256>, Op::Dx, TENSOR, GRAPH>(p, s);
     if (bn == 192) return launch_grad<DxCfg<192>, Op::Dx, TENSOR, GRAPH>(p, s);
     return launch_grad<DxCfg<128>, Op::Dx, TENSOR, GRAPH>(p, s);
@@ -1223,6 +1280,16 @@ hipError_t launch_op(const ProblemDesc& p, hipStream_t s) {
 
 bool grad_persistent_supported(const ProblemDesc& p) {
   if (p.E != 1 || (p.op != Op::Dx && p.op != Op::Dw)) return false;
+  if (p.in_widths != nullptr) {
+    // unequal widths: dX only (complete law), input groups in whole column
+    // tiles, output groups in whole 64-deep k-steps, 256-row tiles
+    if (p.op != Op::Dx || p.law_L != 0 || p.graph_adj != nullptr || p.q > kMaxWidthGroups) return false;
+    const int64_t lim = int64_t(1) << 30;
+    if (p.M * p.K >= lim || p.K * p.N >= lim || p.M * p.N >= lim) return false;
+    for (int g = 0; g < p.q; ++g)
+      if (p.out_widths[g] % kBKDx != 0) return false;
+    return (p.M + p.q - 1) / p.q >= 128 && pick_bn_widths(p) != 0;
+  }
   if (p.law_L > 6) return false;
   if (p.graph_adj != nullptr && (p.law_L > 0 || p.q > 64)) return false;  // one 64-bit mask per type
   const int64_t s = p.K / p.q, r = p.N / p.q;
