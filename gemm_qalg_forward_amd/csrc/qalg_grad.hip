@@ -53,6 +53,7 @@
 // workgroups that got one long unit fewer take up to t_long / t_short short
 // units each before the rest are dealt round robin.  Recursive law: the
 // concatenation of the classes, longest first, round robin.
+#include <initializer_list>
 #include <type_traits>
 
 #include "qalg.h"
@@ -150,11 +151,14 @@ struct GradArgs {
   int64_t part_stride;  // floats per piece (K * N)
   uint32_t a_bytes, b_bytes;  // dW: bytes of X and dY (buffer ranges)
   const uint64_t* adj;  // graph law Q_G: per-type out-edge masks (bit j of type i: edge (i, j)); else null
-  // unequal group widths (eq 18), dX of the complete law: widths = 1; first K
-  // column of input group g, first N column of output group g, first dX
-  // column tile of input group g; n_ct: dX column tiles in all
+  // unequal group widths (eq 18), complete law: widths = 1; first K column of
+  // input group g, first N column of output group g; first tile along K of
+  // input group g (dX: BN-column tiles, n_ct of them in all; dW: BM-row
+  // tiles); dW: first BN-column tile along N of output group g, and the first
+  // diagonal / off-diagonal tile of group g in the two classes' orders
   int widths, n_ct;
   int gk[kMaxWidthGroups + 1], gn[kMaxWidthGroups + 1], tk[kMaxWidthGroups + 1];
+  int tn[kMaxWidthGroups + 1], dpre[kMaxWidthGroups + 1], opre[kMaxWidthGroups + 1];
 };
 
 // One unit of work: an output tile, or a piece of a split dW tile.
@@ -444,9 +448,40 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
         t.nseg = 1;
         if constexpr (GRAPH) t.gmask = uint64_t(1) << b;
       }
-      const int rt = w % a.rpb, ct = w / a.rpb;
-      t.out_row0 = b * a.s + rt * C::BM;
-      t.n0 = j * a.r + ct * C::BN;
+      if (a.widths) {
+        // unequal widths (no split pieces): diagonal tiles of group j in
+        // order, feature tile fastest; off-diagonal tiles by input group b,
+        // over every column tile outside b's own output group
+        int r, c;
+        if (cls) {
+          int g = 0;
+          while (g + 1 < q && idx >= a.dpre[g + 1]) g = uni(g + 1);
+          const int local = idx - a.dpre[g];
+          const int rpb = a.tk[g + 1] - a.tk[g];
+          r = local % rpb;
+          c = a.tn[g] + local / rpb;
+          b = j = g;
+        } else {
+          int g = 0;
+          while (g + 1 < q && idx >= a.opre[g + 1]) g = uni(g + 1);
+          const int local = idx - a.opre[g];
+          const int rpb = a.tk[g + 1] - a.tk[g];
+          r = local % rpb;
+          const int cp = local / rpb;
+          c = cp < a.tn[g] ? cp : cp + (a.tn[g + 1] - a.tn[g]);
+          int jj = 0;
+          while (jj + 1 < q && c >= a.tn[jj + 1]) jj = uni(jj + 1);
+          b = g;
+          j = jj;
+          t.seg_from = b;
+        }
+        t.out_row0 = a.gk[b] + r * C::BM;
+        t.n0 = a.gn[j] + (c - a.tn[j]) * C::BN;
+      } else {
+        const int rt = w % a.rpb, ct = w / a.rpb;
+        t.out_row0 = b * a.s + rt * C::BM;
+        t.n0 = j * a.r + ct * C::BN;
+      }
       t.type = -1;
       t.first = 0;
       t.m_cnt = C::BM;
@@ -496,6 +531,8 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
     else
       deal.init(n_rt * a.cpg, n_rt * (q - 1) * a.cpg, a.N / C::BK, a.r / C::BK, xcd, nx, slot, per_x);
   }
+  else if (a.widths)
+    deal.init(a.dpre[q], a.opre[q], a.t_unit[1], a.t_unit[0], xcd, nx, slot, per_x);
   else
     deal.init(q * tpb * a.np[1], q * (q - 1) * tpb * a.np[0], a.t_unit[1], a.t_unit[0], xcd, nx, slot, per_x);
   auto unit_at = [&](int u, int* cls, int* idx) -> bool {
@@ -1169,6 +1206,23 @@ hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
   } else {
     a.cpg = a.r / C::BN;
     a.rpb = a.s / C::BM;
+    if (p.in_widths != nullptr) {
+      a.widths = 1;
+      a.gk[0] = a.gn[0] = a.tk[0] = a.tn[0] = 0;
+      for (int g = 0; g < p.q; ++g) {
+        a.gk[g + 1] = a.gk[g] + int(p.in_widths[g]);
+        a.gn[g + 1] = a.gn[g] + int(p.out_widths[g]);
+        a.tk[g + 1] = a.tk[g] + int(p.in_widths[g] / C::BM);
+        a.tn[g + 1] = a.tn[g] + int(p.out_widths[g] / C::BN);
+      }
+      a.dpre[0] = a.opre[0] = 0;
+      for (int g = 0; g < p.q; ++g) {
+        const int rpb = a.tk[g + 1] - a.tk[g], cpg = a.tn[g + 1] - a.tn[g];
+        a.dpre[g + 1] = a.dpre[g] + rpb * cpg;
+        a.opre[g + 1] = a.opre[g] + rpb * (a.tn[p.q] - cpg);
+      }
+      a.cpg = a.rpb = 1;  // unused by the widths decode; keeps its divisions defined
+    }
   }
   int grid = cu_count();
   grid = grid >= 8 ? grid / 8 * 8 : grid;
@@ -1200,7 +1254,7 @@ hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
     int64_t total = 0;
     for (int c = 0; c < ncls; ++c) total += nblk[c] * tpb * nk[c];
     const int64_t avg = (total + grid - 1) / grid;
-    if (p.dw_part != nullptr) {
+    if (p.dw_part != nullptr && p.in_widths == nullptr) {
       // cut a class's tiles until a piece is no longer than the average
       // k-steps per workgroup (powers of two, at most kDwMaxSplits pieces)
       for (int c = 0; c < ncls; ++c) {
@@ -1247,15 +1301,16 @@ hipError_t launch_grad(const ProblemDesc& p, hipStream_t s) {
 
 int pick_bn(int64_t w) { return w % 256 == 0 ? 256 : w % 192 == 0 ? 192 : w % 128 == 0 ? 128 : 0; }
 int pick_bm_dw(int64_t w) { return w % 256 == 0 ? 256 : w % 192 == 0 ? 192 : 0; }
-// the widest dX column tile that divides every input group width
-int pick_bn_widths(const ProblemDesc& p) {
-  for (const int bn : {256, 192, 128}) {
+// the widest tile extent (of those offered) that divides every group width
+int pick_widths(const int64_t* w, int q, std::initializer_list<int> sizes) {
+  for (const int t : sizes) {
     bool ok = true;
-    for (int g = 0; g < p.q; ++g) ok = ok && p.in_widths[g] % bn == 0;
-    if (ok) return bn;
+    for (int g = 0; g < q; ++g) ok = ok && w[g] % t == 0;
+    if (ok) return t;
   }
   return 0;
 }
+int pick_bn_widths(const ProblemDesc& p) { return pick_widths(p.in_widths, p.q, {256, 192, 128}); }
 
 template <Op OP, bool TENSOR, bool GRAPH>
 hipError_t launch_op(const ProblemDesc& p, hipStream_t s) {
@@ -1265,7 +1320,8 @@ hipError_t launch_op(const ProblemDesc& p, hipStream_t s) {
     if (bn == 192) return launch_grad<DxCfg<192>, Op::Dx, TENSOR, GRAPH>(p, s);
     return launch_grad<DxCfg<128>, Op::Dx, TENSOR, GRAPH>(p, s);
   }
-  const int bm = pick_bm_dw(p.K / p.q), bn = pick_bn(p.N / p.q);
+  const int bm = p.in_widths != nullptr ? pick_widths(p.in_widths, p.q, {256, 192}) : pick_bm_dw(p.K / p.q);
+  const int bn = p.in_widths != nullptr ? pick_widths(p.out_widths, p.q, {256, 192, 128}) : pick_bn(p.N / p.q);
   if (bm == 256) {
     if (bn == 256) return launch_grad<DwCfg<256, 256>, Op::Dw, TENSOR, GRAPH>(p, s);
     if (bn == 192) return launch_grad<DwCfg<256, 192>, Op::Dw, TENSOR, GRAPH>(p, s);
@@ -1281,11 +1337,15 @@ hipError_t launch_op(const ProblemDesc& p, hipStream_t s) {
 bool grad_persistent_supported(const ProblemDesc& p) {
   if (p.E != 1 || (p.op != Op::Dx && p.op != Op::Dw)) return false;
   if (p.in_widths != nullptr) {
-    // unequal widths: dX only (complete law), input groups in whole column
-    // tiles, output groups in whole 64-deep k-steps, 256-row tiles
-    if (p.op != Op::Dx || p.law_L != 0 || p.graph_adj != nullptr || p.q > kMaxWidthGroups) return false;
+    // unequal widths (complete law).  dX: input groups in whole column tiles,
+    // output groups in whole 64-deep k-steps, 256-row tiles; dW: input groups
+    // in whole 256- or 192-row tiles, output groups in whole column tiles
+    if (p.law_L != 0 || p.graph_adj != nullptr || p.q > kMaxWidthGroups) return false;
     const int64_t lim = int64_t(1) << 30;
     if (p.M * p.K >= lim || p.K * p.N >= lim || p.M * p.N >= lim) return false;
+    if (p.op == Op::Dw)
+      return pick_widths(p.in_widths, p.q, {256, 192}) != 0 && pick_widths(p.out_widths, p.q, {256, 192, 128}) != 0 &&
+             p.M >= int64_t(kBKDw) * p.q;
     for (int g = 0; g < p.q; ++g)
       if (p.out_widths[g] % kBKDx != 0) return false;
     return (p.M + p.q - 1) / p.q >= 128 && pick_bn_widths(p) != 0;

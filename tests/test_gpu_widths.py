@@ -36,6 +36,7 @@ CASES = [
     (777, [8, 120, 256, 40], [72, 8, 200, 32], "random", 0, False),
     (1536, [768, 256], [1024, 3072], "cyclic", 0, True),
     (1200, [256] * 4, [512] * 4, "random", 3, False),
+    (1100, [192, 384, 576], [384, 128, 256], "random", 2, True),
 ]
 
 
