@@ -125,14 +125,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
   const char* Vh = a.V + int64_t(kvh) * S * ROWB;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(smem)));
 
-  // this lane's query row (row l32 of the wave's 32): its fragments stay in registers
+  // this lane's query row (row l32 of the wave's 32); the fragments of the
+  // support's groups are loaded from it whenever the key type changes
   const int tq = t0 + wid * 32 + l32;
   const bool q_ok = tq < n_i;
-  const int pq = si + q * min(tq, n_i - 1);
-  bf16x8 qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    qf[ks] = *reinterpret_cast<const bf16x8*>(Qh + int64_t(pq) * ROWB + (2 * ks + lhi) * 16);
+  const int tqc = min(tq, n_i - 1);
+  const int pq = si + q * tqc;
+  const char* q_row = Qh + int64_t(pq) * ROWB + 16 * lhi;
 
   f32x16 acc[DB];
 #pragma unroll
@@ -206,6 +205,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
     lds_barrier();
     const int j = bj, tb = btb;
     const bool more = cj < q;
+    // scores of the wave's 32 queries against the 64 keys over the support's
+    // groups only.  When the key type changes, the support's k-steps are laid
+    // out as slots: slot x holds the query fragment and the K piece of the
+    // x-th 16-feature step of F(i, j); the block then runs exactly `tot`
+    // MFMA steps per 32-key tile, through a switch on tot, so that no MFMA is
+    // conditional inside straight-line code.  The slot loads are waited for
+    // here, before the next block's copies are issued: the copies then never
+    // sit behind a wait for them.
+    if (j != cur_j) {
+      cur_j = j;
+      const int ms = a.m / 16;
+      tot = uni(support_count(i, j, a.L) * ms);
+#pragma unroll
+      for (int x = 0; x < KS; ++x) {
+        const int step = x < tot ? support_group(i, j, a.L, x / ms) * ms + x % ms : 0;
+        kp[x] = uni(2 * step);
+        qsl[x] = *reinterpret_cast<const bf16x8*>(q_row + 32 * step);
+      }
+      wait_vmcnt<0>();
+    }
     if (more) {
       bj = cj;
       btb = ct;
@@ -216,42 +235,28 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
     const char* sK = smem + stage * 2 * BLK;
     const char* sV = sK + BLK;
 
-    // scores of the wave's 32 queries against the 64 keys over the support's
-    // groups only.  When the key type changes, the support's k-steps are laid
-    // out as slots: slot x holds the query fragment and the K piece of the
-    // x-th 16-feature step of F(i, j); the block then runs exactly `tot`
-    // MFMA steps per 32-key tile, through a switch on tot, so that no MFMA is
-    // conditional inside straight-line code.
-    if (j != cur_j) {
-      cur_j = j;
-      const int ms = a.m / 16;
-      tot = uni(support_count(i, j, a.L) * ms);
-#pragma unroll
-      for (int x = 0; x < KS; ++x) {
-        const int step = x < tot ? support_group(i, j, a.L, x / ms) * ms + x % ms : 0;
-        kp[x] = uni(2 * step);
-        bf16x8 v = qf[0];
-#pragma unroll
-        for (int z = 1; z < KS; ++z)
-          if (z == step) v = qf[z];
-        qsl[x] = v;
-      }
-    }
     f32x16 sc[2];
     auto scores = [&](auto tot_c) {
       constexpr int T = decltype(tot_c)::value;
       sc[0] = (f32x16){};
       sc[1] = (f32x16){};
+      // all of the block's K fragments are read before the first MFMA, so the
+      // LDS latency is paid once per block rather than once per step
+      bf16x8 kf[T][2];
 #pragma unroll
       for (int x = 0; x < T; ++x) {
         const int pc = kp[x] + lhi;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           const int row = nb * 32 + l32;
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + row * ROWB + ((pc ^ swk<D>(row)) << 4));
-          sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qsl[x], sc[nb], 0, 0, 0);
+          kf[x][nb] = *reinterpret_cast<const bf16x8*>(sK + row * ROWB + ((pc ^ swk<D>(row)) << 4));
         }
       }
+#pragma unroll
+      for (int x = 0; x < T; ++x)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[x][nb], qsl[x], sc[nb], 0, 0, 0);
     };
     switch (tot) {
       case 1: scores(std::integral_constant<int, 1>{}); break;
@@ -269,13 +274,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
     const int sj = first_row(j);
     const bool full = tb + kAttnK <= nk_j && sj + q * (tb + kAttnK - 1) <= p_wave0;
     if (!full) {
+      // key u = sj + q tk is allowed iff u <= pq = si + q tqc, i.e. (both first
+      // rows in [0, q)) iff tk <= tqc - [si < sj]; keys past the type's last
+      // allowed one fail it too (pq <= p_last).  One compare per score against
+      // the lane's limit, offset to the element's constant key index.
+      const int lim = tqc - (si < sj ? 1 : 0) - tb - 4 * lhi;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int tk = tb + nb * 32 + 8 * (e >> 2) + 4 * lhi + (e & 3);
-          if (!(tk < nk_j && sj + q * tk <= pq)) sc[nb][e] = -INFINITY;
-        }
+        for (int e = 0; e < 16; ++e)
+          if (nb * 32 + 8 * (e >> 2) + (e & 3) > lim) sc[nb][e] = -INFINITY;
     }
     // online softmax in the log2 domain: scale folded into the exponent
     const float scl = log2e * __builtin_amdgcn_rsqf(float(nf * a.m));
@@ -926,7 +934,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bwd_dq_kernel(AttnBwdArg
   // type, for the support's groups only); D = <dO, O> in fp32
   const int tq = t0 + wid * 32 + l32;
   const bool q_ok = tq < n_i;
-  const int pq = si + q * min(tq, n_i - 1);
+  const int tqc = min(tq, n_i - 1);
+  const int pq = si + q * tqc;
   bf16x8 df[KS];
   float dsum = 0.f;
   const char* q_row = a.Q + hoff + int64_t(pq) * ROWB + 16 * lhi;
@@ -952,14 +961,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bwd_dq_kernel(AttnBwdArg
   for (int db = 0; db < DB; ++db) acc[db] = (f32x16){};
   int tlo[DB], thi[DB];
   tr_offsets<D>(lane, tlo, thi);
-  int k_row[LOADS];
-  uint32_t k_pc[LOADS];
+  // copy slots: slot x is row k_row0 + x (64 / NP) of the block, at byte
+  // x of k_pcs (the piece's swizzled byte offset, < 256): two registers in
+  // all, which keeps this kernel within two workgroups' register budget
+  static_assert(LOADS <= 4 && 64 % NP == 0 && NP * 16 <= 256, "packed copy slots");
+  const int k_row0 = (wid * LOADS * 64 + lane) / NP;
+  uint32_t k_pcs = 0;
 #pragma unroll
-  for (int x = 0; x < LOADS; ++x) {
-    const int sl = (wid * LOADS + x) * 64 + lane;
-    k_row[x] = sl / NP;
-    k_pc[x] = uint32_t((sl % NP) ^ swb<D>(k_row[x])) * 16u;
-  }
+  for (int x = 0; x < LOADS; ++x)
+    k_pcs |= uint32_t(((lane % NP) ^ swb<D>(k_row0 + x * (64 / NP))) * 16) << (8 * x);
 
   // key blocks, type by type (the forward's walk)
   int cj = 0, ct = 0;
@@ -976,11 +986,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bwd_dq_kernel(AttnBwdArg
   auto issue = [&](int stage) {
     const int nk = keys_of(cj);
     const uint32_t base = lds0 + uint32_t(stage * 2 * BLK) + uint32_t(wid * LOADS * 1024);
+    // the slots are re-derived here at each block (the empty asm hides that
+    // they do not change), so the compiler cannot hoist LOADS copies of them
+    // out of the loop and spill those
+    int r0 = k_row0;
+    uint32_t pcs = k_pcs;
+    asm volatile("" : "+v"(r0), "+v"(pcs));
 #pragma unroll
     for (int x = 0; x < LOADS; ++x) {
-      const uint32_t u = uint32_t(first_row(cj) + q * min(ct + k_row[x], nk - 1));
-      copy16_to_lds(Kh, u * ROWB + k_pc[x], base + uint32_t(x * 1024));
-      copy16_to_lds(Vh, u * ROWB + k_pc[x], base + uint32_t(BLK + x * 1024));
+      const uint32_t u = uint32_t(first_row(cj) + q * min(ct + r0 + x * (64 / NP), nk - 1));
+      const uint32_t off = u * ROWB + ((pcs >> (8 * x)) & 255u);
+      copy16_to_lds(Kh, off, base + uint32_t(x * 1024));
+      copy16_to_lds(Vh, off, base + uint32_t(BLK + x * 1024));
     }
   };
 
@@ -997,6 +1014,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bwd_dq_kernel(AttnBwdArg
     lds_barrier();
     const int j = bj, tb = btb;
     const bool more = cj < q;
+    // a new key type's query slots are loaded and waited for before the next
+    // block's copies are issued, so that no later wait stalls on the copies
+    if (j != cur_j) {
+      cur_j = j;
+      sp.set(i, j, a.L, a.m, l32, q_row);
+      wait_vmcnt<0>();
+    }
     if (more) {
       bj = cj;
       btb = ct;
@@ -1006,10 +1030,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bwd_dq_kernel(AttnBwdArg
     }
     const char* sK = smem + stage * 2 * BLK;
     const char* sV = sK + BLK;
-    if (j != cur_j) {
-      cur_j = j;
-      sp.set(i, j, a.L, a.m, l32, q_row);
-    }
     f32x16 sc[2], dp[2];
     support_scores_any<D>(sc, sK, sp, l32, lhi);
     full_scores<D>(dp, sV, df, l32, lhi);
@@ -1020,6 +1040,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bwd_dq_kernel(AttnBwdArg
     const bool full = tb + kAttnK <= nk_j && sj + q * (tb + kAttnK - 1) <= p_wave0;
     // dS = P (dP - D) c; a block wholly inside every query's causal range
     // (the usual case) takes the branch without the mask
+    // allowed keys: tk <= tqc - [si < sj] (the forward's causal test)
+    const int lim = tqc - (si < sj ? 1 : 0) - tb - 4 * lhi;
     auto ds_pass = [&](auto full_c) {
       constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
@@ -1031,8 +1053,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bwd_dq_kernel(AttnBwdArg
           if constexpr (FULL) {
             dp[nb][e] = v;
           } else {
-            const int tk = tb + nb * 32 + 8 * (e >> 2) + 4 * lhi + (e & 3);
-            dp[nb][e] = (tk < nk_j && sj + q * tk <= pq) ? v : 0.f;
+            dp[nb][e] = nb * 32 + 8 * (e >> 2) + (e & 3) <= lim ? v : 0.f;
           }
         }
     };
@@ -1091,7 +1112,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkdv_kernel(AttnBwdA
   // for the support's groups only)
   const int tk = t0 + wid * 32 + l32;
   const bool k_ok = tk < n_j;
-  const int pk = sj + q * min(tk, n_j - 1);
+  const int tkc = min(tk, n_j - 1);
+  const int pk = sj + q * tkc;
   const int64_t koff = int64_t(hk) * S * ROWB + int64_t(pk) * ROWB;
   bf16x8 vf[KS];
 #pragma unroll
@@ -1166,6 +1188,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkdv_kernel(AttnBwdA
     lds_barrier();
     const int i = bi, tb = btb;
     const bool more = cg < G;
+    // a new query type's key slots: loaded and waited for before the next
+    // block's copies are issued (see the dQ kernel)
+    if (i != cur_i) {
+      cur_i = i;
+      sp.set(i, j, a.L, a.m, l32, k_row);
+      wait_vmcnt<0>();
+    }
     if (more) {
       bi = ci;
       btb = ct;
@@ -1176,10 +1205,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkdv_kernel(AttnBwdA
     const char* sQ = smem + stage * STG;
     const char* sdO = sQ + BLK;
     const char* sst = sdO + BLK;
-    if (i != cur_i) {
-      cur_i = i;
-      sp.set(i, j, a.L, a.m, l32, k_row);
-    }
     f32x16 sc[2], dp[2];
     support_scores_any<D>(sc, sQ, sp, l32, lhi);
     full_scores<D>(dp, sdO, vf, l32, lhi);
@@ -1189,6 +1214,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkdv_kernel(AttnBwdA
     const bool full = tb + kAttnK <= n_i && s_i + q * tb >= p_wave_last;
     // P and dS = P (dP - D) c; masked pairs (and the rows past the type's
     // last query, whose pairs hold other data) are set to 0 by selects
+    // allowed queries of the block: s_i + q tq >= pk = sj + q tkc, i.e. (both
+    // first rows in [0, q)) tq >= tkc + [sj > s_i], and tq < n_i; as one
+    // unsigned range test on the element's constant offset c: c - lo in [0, rg]
+    int lo = tkc + (sj > s_i ? 1 : 0) - tb - 4 * lhi, rg = n_i - 1 - tb - 4 * lhi - lo;
+    if (rg < 0) {
+      lo = 1 << 20;
+      rg = 0;
+    }
     auto pds_pass = [&](auto full_c) {
       constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
@@ -1209,8 +1242,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bwd_dkdv_kernel(AttnBwdA
               dp[nb][e] = v;
               sc[nb][e] = p;
             } else {
-              const int tq = tb + r0 + e4;
-              const bool ok = tq < n_i && s_i + q * tq >= pk;
+              const bool ok = uint32_t(nb * 32 + 8 * g4 + e4 - lo) <= uint32_t(rg);
               dp[nb][e] = ok ? v : 0.f;
               sc[nb][e] = ok ? p : 0.f;
             }
