@@ -119,6 +119,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
   const int t_last = min(t0 + kAttnQ, n_i) - 1;
   const int p_last = si + q * t_last;                // latest query row in the block
   const int p_wave0 = si + q * min(t0 + 32 * wid, n_i - 1);  // earliest query row of the wave
+  const int p_wave1 = si + q * min(t0 + 32 * wid + 31, n_i - 1);  // latest query row of the wave
 
   const char* Qh = a.Q + int64_t(h) * S * ROWB;
   const char* Kh = a.K + int64_t(kvh) * S * ROWB;
@@ -235,117 +236,121 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_fwd_kernel(AttnArgs a) {
     const char* sK = smem + stage * 2 * BLK;
     const char* sV = sK + BLK;
 
-    f32x16 sc[2];
-    auto scores = [&](auto tot_c) {
-      constexpr int T = decltype(tot_c)::value;
-      sc[0] = (f32x16){};
-      sc[1] = (f32x16){};
-      // all of the block's K fragments are read before the first MFMA, so the
-      // LDS latency is paid once per block rather than once per step
-      bf16x8 kf[T][2];
+    // a block whose first key lies past the wave's latest query adds nothing
+    // to its rows: the wave only takes part in the copies and barriers
+    if (first_row(j) + q * tb <= p_wave1) {
+      f32x16 sc[2];
+      auto scores = [&](auto tot_c) {
+        constexpr int T = decltype(tot_c)::value;
+        sc[0] = (f32x16){};
+        sc[1] = (f32x16){};
+        // the block's K fragment reads are written ahead of its MFMAs, which
+        // leaves the scheduler free to issue them as early as registers allow
+        bf16x8 kf[T][2];
 #pragma unroll
-      for (int x = 0; x < T; ++x) {
-        const int pc = kp[x] + lhi;
+        for (int x = 0; x < T; ++x) {
+          const int pc = kp[x] + lhi;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int row = nb * 32 + l32;
-          kf[x][nb] = *reinterpret_cast<const bf16x8*>(sK + row * ROWB + ((pc ^ swk<D>(row)) << 4));
+          for (int nb = 0; nb < 2; ++nb) {
+            const int row = nb * 32 + l32;
+            kf[x][nb] = *reinterpret_cast<const bf16x8*>(sK + row * ROWB + ((pc ^ swk<D>(row)) << 4));
+          }
         }
-      }
 #pragma unroll
-      for (int x = 0; x < T; ++x)
+        for (int x = 0; x < T; ++x)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[x][nb], qsl[x], sc[nb], 0, 0, 0);
+      };
+      switch (tot) {
+        case 1: scores(std::integral_constant<int, 1>{}); break;
+        case 2: scores(std::integral_constant<int, 2>{}); break;
+        case 3: scores(std::integral_constant<int, 3>{}); break;
+        case 4: scores(std::integral_constant<int, 4>{}); break;
+        case 5: scores(std::integral_constant<int, 5>{}); break;
+        case 6: scores(std::integral_constant<int, 6>{}); break;
+        case 7: scores(std::integral_constant<int, 7>{}); break;
+        default: scores(std::integral_constant<int, KS>{}); break;
+      }
+      const int nf = tot / (a.m / 16);
+      // causal mask (only blocks that reach past the wave's earliest query, or past the type's keys)
+      const int nk_j = keys_of(j);
+      const int sj = first_row(j);
+      const bool full = tb + kAttnK <= nk_j && sj + q * (tb + kAttnK - 1) <= p_wave0;
+      if (!full) {
+        // key u = sj + q tk is allowed iff u <= pq = si + q tqc, i.e. (both first
+        // rows in [0, q)) iff tk <= tqc - [si < sj]; keys past the type's last
+        // allowed one fail it too (pq <= p_last).  One compare per score against
+        // the lane's limit, offset to the element's constant key index.
+        const int lim = tqc - (si < sj ? 1 : 0) - tb - 4 * lhi;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-          sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[x][nb], qsl[x], sc[nb], 0, 0, 0);
-    };
-    switch (tot) {
-      case 1: scores(std::integral_constant<int, 1>{}); break;
-      case 2: scores(std::integral_constant<int, 2>{}); break;
-      case 3: scores(std::integral_constant<int, 3>{}); break;
-      case 4: scores(std::integral_constant<int, 4>{}); break;
-      case 5: scores(std::integral_constant<int, 5>{}); break;
-      case 6: scores(std::integral_constant<int, 6>{}); break;
-      case 7: scores(std::integral_constant<int, 7>{}); break;
-      default: scores(std::integral_constant<int, KS>{}); break;
-    }
-    const int nf = tot / (a.m / 16);
-    // causal mask (only blocks that reach past the wave's earliest query, or past the type's keys)
-    const int nk_j = keys_of(j);
-    const int sj = first_row(j);
-    const bool full = tb + kAttnK <= nk_j && sj + q * (tb + kAttnK - 1) <= p_wave0;
-    if (!full) {
-      // key u = sj + q tk is allowed iff u <= pq = si + q tqc, i.e. (both first
-      // rows in [0, q)) iff tk <= tqc - [si < sj]; keys past the type's last
-      // allowed one fail it too (pq <= p_last).  One compare per score against
-      // the lane's limit, offset to the element's constant key index.
-      const int lim = tqc - (si < sj ? 1 : 0) - tb - 4 * lhi;
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (nb * 32 + 8 * (e >> 2) + (e & 3) > lim) sc[nb][e] = -INFINITY;
+      }
+      // online softmax in the log2 domain: scale folded into the exponent
+      const float scl = log2e * __builtin_amdgcn_rsqf(float(nf * a.m));
+      float mx = -INFINITY;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (nb * 32 + 8 * (e >> 2) + (e & 3) > lim) sc[nb][e] = -INFINITY;
-    }
-    // online softmax in the log2 domain: scale folded into the exponent
-    const float scl = log2e * __builtin_amdgcn_rsqf(float(nf * a.m));
-    float mx = -INFINITY;
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[nb][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * scl;
+      // the running max moves only when some row's block max passes it by more
+      // than 8 (factors of 2): probabilities then stay below 2^8, and most blocks
+      // skip rescaling the output accumulators
+      if (__any(mx > m_run + 8.0f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[nb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scl;
-    // the running max moves only when some row's block max passes it by more
-    // than 8 (factors of 2): probabilities then stay below 2^8, and most blocks
-    // skip rescaling the output accumulators
-    if (__any(mx > m_run + 8.0f)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
-      m_run = m_new;
-    }
-    const float base = m_run == -INFINITY ? 0.f : m_run;
-    float rs = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nb][e], scl, -base));
-        sc[nb][e] = pv;
-        rs += pv;
+          for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
+        m_run = m_new;
       }
-    rs += __shfl_xor(rs, 32);
-    l_run += rs;
+      const float base = m_run == -INFINITY ? 0.f : m_run;
+      float rs = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nb][e], scl, -base));
+          sc[nb][e] = pv;
+          rs += pv;
+        }
+      rs += __shfl_xor(rs, 32);
+      l_run += rs;
 
-    // O += P V: 16 keys per step; the lane pair (l32, 0/1) exchanges half its
-    // probabilities so that each lane holds 8 consecutive keys of its row
+      // O += P V: 16 keys per step; the lane pair (l32, 0/1) exchanges half its
+      // probabilities so that each lane holds 8 consecutive keys of its row
 #pragma unroll
-    for (int ks = 0; ks < kAttnK / 16; ++ks) {
-      const int nb = ks >> 1;
-      // keys 16 ks .. +15 are groups ga = 2 (ks & 1) and ga + 1 of the score
-      // tile: lane half 0 keeps group ga and sends ga + 1, half 1 the reverse
-      // (register indices stay compile-time; only the choice is per lane)
-      const int ga = 2 * (ks & 1);
-      const u32x2 pa = pack4_bf16(sc[nb][4 * ga], sc[nb][4 * ga + 1], sc[nb][4 * ga + 2], sc[nb][4 * ga + 3]);
-      const u32x2 pb = pack4_bf16(sc[nb][4 * ga + 4], sc[nb][4 * ga + 5], sc[nb][4 * ga + 6], sc[nb][4 * ga + 7]);
-      // v_permlane32_swap exchanges lanes 32-63 of its first operand with
-      // lanes 0-31 of its second: on (pa, pb) half 0 ends with its own
-      // group-ga piece and the partner's, half 1 with the partner's group-ga+1
-      // piece and its own, in key order in both, with no per-lane selects
-      const auto s0 = __builtin_amdgcn_permlane32_swap(pa[0], pb[0], false, false);
-      const auto s1 = __builtin_amdgcn_permlane32_swap(pa[1], pb[1], false, false);
-      const u32x4 pw = {s0[0], s1[0], s0[1], s1[1]};
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+      for (int ks = 0; ks < kAttnK / 16; ++ks) {
+        const int nb = ks >> 1;
+        // keys 16 ks .. +15 are groups ga = 2 (ks & 1) and ga + 1 of the score
+        // tile: lane half 0 keeps group ga and sends ga + 1, half 1 the reverse
+        // (register indices stay compile-time; only the choice is per lane)
+        const int ga = 2 * (ks & 1);
+        const u32x2 pa = pack4_bf16(sc[nb][4 * ga], sc[nb][4 * ga + 1], sc[nb][4 * ga + 2], sc[nb][4 * ga + 3]);
+        const u32x2 pb = pack4_bf16(sc[nb][4 * ga + 4], sc[nb][4 * ga + 5], sc[nb][4 * ga + 6], sc[nb][4 * ga + 7]);
+        // v_permlane32_swap exchanges lanes 32-63 of its first operand with
+        // lanes 0-31 of its second: on (pa, pb) half 0 ends with its own
+        // group-ga piece and the partner's, half 1 with the partner's group-ga+1
+        // piece and its own, in key order in both, with no per-lane selects
+        const auto s0 = __builtin_amdgcn_permlane32_swap(pa[0], pb[0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(pa[1], pb[1], false, false);
+        const u32x4 pw = {s0[0], s1[0], s0[1], s1[1]};
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const char* pp = sV + v_rd[db] + 16 * ks * ROWB;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(pp));
-        const s16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(pp + 4 * ROWB));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[db], 0, 0, 0);
+        for (int db = 0; db < DB; ++db) {
+          const char* pp = sV + v_rd[db] + 16 * ks * ROWB;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(pp));
+          const s16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(pp + 4 * ROWB));
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[db], 0, 0, 0);
+        }
       }
     }
     if (!more) break;
