@@ -283,8 +283,15 @@ qalg_status qalg_backward_dw_graph(const void* X, const void* dY, const int32_t*
  * 8 (QALG_ERR_DIM / QALG_ERR_ALIGN), summing to K and N (QALG_ERR_DIM).
  * q <= 64 (QALG_ERR_Q); bf16 only (QALG_ERR_DTYPE); M K, K N and M N below
  * 2^31 (QALG_ERR_DIM); flags: QALG_FLAG_INDEX_READY only (QALG_ERR_ARG).  A
- * workspace of qalg_workspace_bytes_dw bytes lets dW split its contraction.
- * Register-staged kernels; each output element has one owner.
+ * workspace of qalg_workspace_bytes_dw bytes lets the register-staged dW
+ * split its contraction.  Shapes whose groups fill whole tiles run the
+ * persistent kernels: the forward when every out_widths[g] is a multiple of
+ * 256 and every in_widths[g] of 64 with at least 128 rows per type; dX when
+ * every in_widths[g] is a multiple of 128, 192 or 256 and every out_widths[g]
+ * of 64 with at least 128 rows per type; dW when every in_widths[g] is a
+ * multiple of 192 or 256 and every out_widths[g] of 128, 192 or 256 with
+ * M >= 32 q (M K, K N and M N below 2^30 for the gradients).  Other shapes
+ * run the register-staged kernels.  Each output element has one owner.
  */
 qalg_status qalg_forward_widths(const void* X, const void* W, const int32_t* tau, int32_t q,
                                 const int64_t* in_widths, const int64_t* out_widths, int64_t M, int64_t K,
