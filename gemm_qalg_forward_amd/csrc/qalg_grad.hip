@@ -97,9 +97,10 @@ struct GradCfg {
   static constexpr int A_DMA = A_BYTES / (1024 * NW), B_DMA = B_BYTES / (1024 * NW);
   static constexpr int DMA = A_DMA + B_DMA;
   static_assert(STAGES * DMA < 64, "vmcnt range");
-  // row-major operands: wave w's copies carry contraction rows 8 w .. 8 w + 7
-  static_assert(A_KM || A_DMA * 64 == 8 * A_NCH, "8 contraction rows per wave (A)");
-  static_assert(B_KM || B_DMA * 64 == 8 * B_NCH, "8 contraction rows per wave (B)");
+  // row-major operands: wave w's copies carry contraction rows RPW w .. RPW w + RPW - 1
+  static constexpr int RPW = BK / NW;
+  static_assert(A_KM || A_DMA * 64 == RPW * A_NCH, "RPW contraction rows per wave (A)");
+  static_assert(B_KM || B_DMA * 64 == RPW * B_NCH, "RPW contraction rows per wave (B)");
   // epilogue: each wave restages 32 rows x WTN columns of bf16 at a time in
   // its own share of a buffer behind the stages
   static constexpr int E_PITCH = WTN * 2;          // bytes per restaged row
@@ -116,18 +117,18 @@ struct GradCfg {
 template <int BK>
 __device__ __forceinline__ int swz_km(int row) { return BK == 64 ? swz_x128(row) : swz_x(row); }
 
-// Row id of the copy slot's contraction row, picked per lane from the 8
+// Row id of the copy slot's contraction row, picked per lane from the R
 // wave-uniform ids of the wave's rows: copy u of a row-major operand with NCH
-// pieces per row carries rows (64 u + lane) / NCH of the wave's 8.
-template <int NCH>
-__device__ __forceinline__ int pick_row(const int (&o)[8], int u, int lane) {
+// pieces per row carries rows (64 u + lane) / NCH of the wave's R.
+template <int NCH, int R>
+__device__ __forceinline__ int pick_row(const int (&o)[R], int u, int lane) {
   const int lo = (64 * u) / NCH, hi = (64 * u + 63) / NCH;
   int v = o[0];
 #pragma unroll
-  for (int e = 1; e < 8; ++e)
+  for (int e = 1; e < R; ++e)
     if (e == lo) v = o[e];
 #pragma unroll
-  for (int e = 1; e < 8; ++e)
+  for (int e = 1; e < R; ++e)
     if (e > lo && e <= hi) v = lane >= e * NCH - 64 * u ? o[e] : v;
   return v;
 }
@@ -636,13 +637,13 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
   if constexpr (CYC_DW) {
 #pragma unroll
     for (int u = 0; u < C::A_DMA; ++u) {
-      const int e = a_r[u] - 8 * wid;
+      const int e = a_r[u] - C::RPW * wid;
       p1[u] = uint32_t(e) * a_ld + uint32_t(a_c[u]) * 16u;
       pq[u] = uint32_t(e * q) * a_ld + uint32_t(a_c[u]) * 16u;
     }
 #pragma unroll
     for (int v = 0; v < C::B_DMA; ++v) {
-      const int e = b_r[v] - 8 * wid;
+      const int e = b_r[v] - C::RPW * wid;
       p1[C::A_DMA + v] = uint32_t(e) * b_ld + uint32_t(b_c[v]) * 16u;
       pq[C::A_DMA + v] = uint32_t(e * q) * b_ld + uint32_t(b_c[v]) * 16u;
     }
@@ -680,7 +681,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
   };
   // dW: ids of the 8 rows this wave copies at the cursor's k-step, and how
   // many of them lie inside the segment (w_rem; the others read as zeros)
-  int w_id[8];
+  int w_id[C::RPW];
   int w_rem = 0;
   uint32_t w_ua = 0, w_ub = 0;  // cyclic: wave-uniform offset parts of the A and B copies
   auto prep_rows = [&]() {
@@ -690,25 +691,25 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
       int r0;
       if constexpr (SIMPLE) {
         // long units: every row in order; short ones: the rows of type seg_from
-        const int j0 = uni((lt.c0 + lk) * C::BK + 8 * wid);
+        const int j0 = uni((lt.c0 + lk) * C::BK + C::RPW * wid);
         w_rstep = lt.nseg == 0 ? 1 : q;
         r0 = lt.nseg == 0 ? j0 : type_start(lt.seg_from) + j0 * q;
       } else {
-        const int j0 = uni((lt.c0 + lk - w_k0) * C::BK + 8 * wid);
+        const int j0 = uni((lt.c0 + lk - w_k0) * C::BK + C::RPW * wid);
         r0 = w_rbase + j0 * w_rstep;
       }
       w_ua = uint32_t(uni(int(uint32_t(r0) * a_ld + uint32_t(lt.out_row0) * 2u)));
       w_ub = uint32_t(uni(int(uint32_t(r0) * b_ld + uint32_t(lt.n0) * 2u)));
     } else if constexpr (OP == Op::Dw) {
-      const int j0 = (lt.c0 + lk - w_k0) * C::BK + 8 * wid;  // segment rank of the wave's first row
+      const int j0 = (lt.c0 + lk - w_k0) * C::BK + C::RPW * wid;  // segment rank of the wave's first row
       w_rem = uni(w_cnt - j0);
       if (w_mode == 2) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w_id[e] = uni(s_rows[w_base + j0 + e]);  // may read the spare tail
+        for (int e = 0; e < C::RPW; ++e) w_id[e] = uni(s_rows[w_base + j0 + e]);  // may read the spare tail
       } else {
         const int r0 = w_mode == 0 ? j0 : w_base + j0 * q, st = w_mode == 0 ? 1 : q;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w_id[e] = uni(r0 + e * st);
+        for (int e = 0; e < C::RPW; ++e) w_id[e] = uni(r0 + e * st);
       }
     }
   };
@@ -727,11 +728,11 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
       c_off[u] = (w_rstep == 1 ? p1[u] : pq[u]) + (u < C::A_DMA ? w_ua : w_ub);
     } else if constexpr (OP == Op::Dw) {
       if (u < C::A_DMA) {
-        c_off[u] = row_off(pick_row<C::A_NCH>(w_id, u, lane), a_r[u] - 8 * wid, a_ld,
+        c_off[u] = row_off(pick_row<C::A_NCH, C::RPW>(w_id, u, lane), a_r[u] - C::RPW * wid, a_ld,
                            uint32_t(lt.out_row0 + a_c[u] * 8) * 2u);
       } else {
         const int v = u - C::A_DMA;
-        c_off[u] = row_off(pick_row<C::B_NCH>(w_id, v, lane), b_r[v] - 8 * wid, b_ld,
+        c_off[u] = row_off(pick_row<C::B_NCH, C::RPW>(w_id, v, lane), b_r[v] - C::RPW * wid, b_ld,
                            uint32_t(lt.n0 + b_c[v] * 8) * 2u);
       }
     }
@@ -1135,7 +1136,7 @@ __global__ __launch_bounds__(256) void dw_piece_reduce_kernel(ReduceArgs a) {
 template <int BN>
 using DxCfg = GradCfg<256, BN, true, true, kBKDx, 2, BN == 256 ? 8 : 4>;
 template <int BM, int BN>
-using DwCfg = GradCfg<BM, BN, false, false, kBKDw, 4>;
+using DwCfg = GradCfg<BM, BN, false, false, kBKDw, 4, BM == 256 && BN == 256 ? 8 : 4>;
 
 int cu_count() {
   static int n = 0;
