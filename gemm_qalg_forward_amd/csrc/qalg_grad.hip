@@ -30,8 +30,9 @@
 // progression (i - o) mod q + m q in closed form; otherwise the index's row
 // list.  dX tiles gather their rows (clamped into the type's rows; extra rows
 // are not stored).  dW contractions walk their types' rows 32 per k-step: each
-// wave looks up the 8 rows its copies carry as scalars and copies through a
-// buffer resource, so that the rows past a type's last one read as zeros.
+// wave looks up the rows its copies carry (8 with 4 waves, 4 with 8) as
+// scalars and copies through a buffer resource, so that the rows past a
+// type's last one read as zeros.
 //
 // Pipeline: one workgroup per CU, operands copied global -> LDS directly; dX
 // in two 64-deep stages (contraction-major rows are whole 128-byte lines; the
@@ -679,7 +680,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
       seg_walk(lt.c0);
     }
   };
-  // dW: ids of the 8 rows this wave copies at the cursor's k-step, and how
+  // dW: ids of the RPW rows this wave copies at the cursor's k-step, and how
   // many of them lie inside the segment (w_rem; the others read as zeros)
   int w_id[C::RPW];
   int w_rem = 0;
@@ -713,7 +714,7 @@ __device__ __forceinline__ void grad_body(const GradArgs& a, char* smem) {
       }
     }
   };
-  // dW: byte offset of a copy's row (local row e of the wave's 8), or one that
+  // dW: byte offset of a copy's row (local row e of the wave's RPW), or one that
   // fails the range check past the segment's rows
   auto row_off = [&](int id, int e, uint32_t ld, uint32_t col_bytes) -> uint32_t {
     const uint32_t ro = __umul24(uint32_t(id), ld);
