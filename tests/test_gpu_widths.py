@@ -37,6 +37,10 @@ CASES = [
     (1536, [768, 256], [1024, 3072], "cyclic", 0, True),
     (1200, [256] * 4, [512] * 4, "random", 3, False),
     (1100, [192, 384, 576], [384, 128, 256], "random", 2, True),
+    # the persistent kernels at their edges: one group (the plain product), and
+    # two very unequal groups with barely 128 rows per type and out-of-range rows
+    (300, [512], [768], "cyclic", 0, False),
+    (265, [1792, 256], [256, 2304], "random", 4, True),
 ]
 
 
