@@ -291,10 +291,21 @@ hipError_t launch_rc(SmallArgs a, int E, hipStream_t st) {
 
 // the widest chunk that the group width fills and that still gives about two
 // workgroups per CU (measured on 64 experts, 7168 -> 2048, q = 4: 64 columns
-// 4.8 TB/s, 256 columns 6.0 TB/s)
+// 4.8 TB/s, 256 columns 6.0 TB/s).  A group whose rows are not whole 128-byte
+// lines (e.g. 96 columns) instead runs as one chunk, the narrowest that holds
+// it, when that still gives as many workgroups: no line is split between two
+// chunks, and at 8 rows (3 workgroups per CU) the grid stays in one round
+// (64 experts, 2048 -> 768, q = 8: one row 20.0 -> 17.2 us, eight rows
+// 62.4 -> 51.5 us, flushed).
 template <int R>
 hipError_t launch_r(const SmallArgs& a, int E, hipStream_t st) {
   const int64_t want = 512;
+  if ((2 * a.r) % 128 != 0 && a.r <= 512 && int64_t(E) * a.q >= want) {
+    if (a.r <= 64) return launch_rc<R, 64>(a, E, st);
+    if (a.r <= 128) return launch_rc<R, 128>(a, E, st);
+    if (a.r <= 256) return launch_rc<R, 256>(a, E, st);
+    return launch_rc<R, 512>(a, E, st);
+  }
   auto fits = [&](int cols) { return a.r >= cols && int64_t(E) * a.q * ((a.r + cols - 1) / cols) >= want; };
   if (fits(512)) return launch_rc<R, 512>(a, E, st);
   if (fits(256)) return launch_rc<R, 256>(a, E, st);
