@@ -166,13 +166,16 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
   // flight across block boundaries, not only inside a block (a 256-row block
   // is a single batch).  Rows past s load nothing and meet zero activations.
   // With room for every block the chunk needs, all activations are staged up
-  // front, behind the first two batches' loads, and one stream runs through
-  // all blocks; otherwise one block at a time, restaged in between.
-  auto run_stream = [&](int bi0, int nbat, int x_base, bool stage_first) {
+  // front, behind the first two batches' loads.  Otherwise one region is
+  // restaged at each block's first batch, between two barriers, while that
+  // batch and the next are already in flight: the weight stream does not drain
+  // at block boundaries.
+  const int bat_per_block = s_pad / kStep;
+  auto run_stream = [&](int nbat, bool restage) {
     auto load_batch = [&](int n, u32x4 (&wv)[kSmUnroll]) {
       const int bl = uni_div(n * kStep, s_pad);
       const int k0 = n * kStep - bl * s_pad + kr;
-      const uint16_t* wp = n < nbat ? W + (int64_t(s_blocks[bi0 + bl]) * s + k0) * N + col0 + l8 * 8 : W;
+      const uint16_t* wp = n < nbat ? W + (int64_t(s_blocks[bl]) * s + k0) * N + col0 + l8 * 8 : W;
 #pragma unroll
       for (int u = 0; u < kSmUnroll; ++u) {
         const int kk = k0 + u * kSmKLanes;
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
       const int bl = uni_div(n * kStep, s_pad);
       const int k0 = n * kStep - bl * s_pad + kr;
       if (k0 - kr >= s) return;  // a batch of padding rows only
-      const unsigned* xsb = xs2 + (x_base + bl) * (x_region / 2);
+      const unsigned* xsb = xs2 + (restage ? 0 : bl) * (x_region / 2);
 #pragma unroll
       for (int v = 0; v < kSmUnroll / 2; ++v) {
         const int kk = k0 + 2 * v * KL;
@@ -212,28 +215,31 @@ __global__ __launch_bounds__(kSmThreads) void small_m_kernel(SmallArgs a) {
     u32x4 wa[kSmUnroll], wb[kSmUnroll];
     load_batch(0, wa);
     load_batch(1, wb);
-    if (stage_first) {
+    if (!restage) {
       for (int bi = 0; bi < nblk; ++bi) stage(s_blocks[bi], bi);
       __syncthreads();
     }
+    // restage before batch n when it opens a block (n and the pacing counter
+    // are uniform, so every thread meets the same barriers)
+    int next_blk = 0, next_n = 0;
+    auto boundary = [&](int n) {
+      if (!restage || n >= nbat || n != next_n) return;
+      if (n > 0) __syncthreads();  // every wave is done with the previous block
+      stage(s_blocks[next_blk], 0);
+      __syncthreads();
+      ++next_blk;
+      next_n += bat_per_block;
+    };
     for (int n = 0; n < nbat; n += 2) {
+      boundary(n);
       apply_batch(n, wa);
       load_batch(n + 2, wa);
+      boundary(n + 1);
       apply_batch(n + 1, wb);
       load_batch(n + 3, wb);
     }
   };
-  const int bat_per_block = s_pad / kStep;
-  if (a.x_regions > 1) {
-    run_stream(0, nblk * bat_per_block, 0, true);
-  } else {
-    for (int bi = 0; bi < nblk; ++bi) {
-      stage(s_blocks[bi], 0);
-      __syncthreads();
-      run_stream(bi, bat_per_block, 0, false);
-      __syncthreads();  // the region is restaged for the next block
-    }
-  }
+  run_stream(nblk * bat_per_block, a.x_regions == 1);
 
   // reduce the weight-row lanes: those of a wave by a fixed shuffle tree, then
   // the 4 waves in a fixed order
@@ -307,6 +313,11 @@ hipError_t launch_r(const SmallArgs& a, int E, hipStream_t st) {
     return launch_rc<R, 512>(a, E, st);
   }
   auto fits = [&](int cols) { return a.r >= cols && int64_t(E) * a.q * ((a.r + cols - 1) / cols) >= want; };
+  // 8 rows hold 151-163 VGPRs: 3 workgroups per CU, 768 at once.  64-column
+  // chunks when they still fit that one round: more weight bytes in flight per
+  // CU than half as many wider chunks (64 experts 2048 -> 768, q = 4: 55.3 ->
+  // 51.6 us, flushed)
+  if (R == 8 && int64_t(E) * a.q * ((a.r + 63) / 64) <= 768) return launch_rc<R, 64>(a, E, st);
   if (fits(512)) return launch_rc<R, 512>(a, E, st);
   if (fits(256)) return launch_rc<R, 256>(a, E, st);
   if (fits(128)) return launch_rc<R, 128>(a, E, st);
