@@ -19,7 +19,7 @@
 // directly.  The two weight rows a lane loads per step are applied together
 // with bf16 dot-2 instructions on interleaved columns, against activations
 // staged in LDS as the same row pairs (all needed blocks at once when they
-// fit in 64 KB, else one block at a time).
+// fit in 64 KB, else each block when the weight stream reaches it).
 #include "qalg_internal.h"
 
 namespace qalg {
