@@ -313,11 +313,13 @@ hipError_t launch_r(const SmallArgs& a, int E, hipStream_t st) {
     return launch_rc<R, 512>(a, E, st);
   }
   auto fits = [&](int cols) { return a.r >= cols && int64_t(E) * a.q * ((a.r + cols - 1) / cols) >= want; };
-  // 8 rows hold 151-163 VGPRs: 3 workgroups per CU, 768 at once.  64-column
-  // chunks when they still fit that one round: more weight bytes in flight per
-  // CU than half as many wider chunks (64 experts 2048 -> 768, q = 4: 55.3 ->
-  // 51.6 us, flushed)
-  if (R == 8 && int64_t(E) * a.q * ((a.r + 63) / 64) <= 768) return launch_rc<R, 64>(a, E, st);
+  // 64-column chunks when they all fit one round of resident workgroups (8
+  // rows hold 151-163 VGPRs: 3 per CU; fewer rows at most 131 of the 64-column
+  // kernel's VGPRs: 4 per CU): more weight bytes in flight per CU than half as
+  // many wider chunks (64 experts 2048 -> 768, q = 4, flushed: 8 rows 55.3 ->
+  // 51.6 us, one row 24.6 -> 22.4 us)
+  const int64_t resident = int64_t(R == 8 ? 3 : 4) * 256;
+  if (int64_t(E) * a.q * ((a.r + 63) / 64) <= resident) return launch_rc<R, 64>(a, E, st);
   if (fits(512)) return launch_rc<R, 512>(a, E, st);
   if (fits(256)) return launch_rc<R, 256>(a, E, st);
   if (fits(128)) return launch_rc<R, 128>(a, E, st);

@@ -101,12 +101,14 @@ def test_small_m_paths_match_oracle(M, q, K, N):
     assert torch.equal(Ys, Ys2), "small-M path is not bitwise reproducible"
 
 
-# (128, 8, 4, ...) to (64, 1, 4, ...) reach the small-M kernel's 512-, 256- and
+# (128, 8, 4, ...) to (128, 1, 4, ...) reach the small-M kernel's 512-, 256- and
 # (ragged) 128-column chunks, which it picks only when there are enough
-# experts; the last three have groups that are not whole 128-byte lines (96 and
-# 160 columns), which run as one chunk wider than the group
+# experts (and more 64-column chunks than fit one round); (64, 1, 4, ...) takes
+# the 64-column chunks that do fit one round; the last three have groups that
+# are not whole 128-byte lines (96 and 160 columns), which run as one chunk
+# wider than the group
 @pytest.mark.parametrize("E,M,q,K,N", [(3, 1, 4, 512, 256), (4, 8, 8, 256, 768), (5, 64, 4, 512, 192), (2, 300, 8, 256, 256),
-                                       (128, 8, 4, 256, 2048), (64, 2, 4, 256, 2048), (64, 1, 4, 256, 768),
+                                       (128, 8, 4, 256, 2048), (64, 2, 4, 256, 2048), (128, 1, 4, 256, 768), (64, 1, 4, 256, 768),
                                        (64, 1, 8, 256, 768), (64, 5, 8, 256, 768), (64, 3, 8, 512, 1280)])
 def test_batched_experts_match_oracle(E, M, q, K, N):
     torch = torch_cuda()
